@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Benchmark of the IQ4_XS x Q8_1 matmul on one MI355X.
+
+Default run (what the driver calls): `python bench.py [--steps K] [--warmup W]`.
+One *step* is the whole hot path over the decode sweep of the attention/GDN
+input-projection shape, N=10240, K=5120: for each M in {1, 2, 4, 8, 16} one
+iq4xs_gemm call (Q8_1 quantization of X on the device, the dispatcher's
+choice of path, the matmul), with all inputs resident in HBM.  Weight copies
+are rotated (>= 640 MB in total) so the 256 MB Infinity Cache cannot serve
+them.
+
+Printed: one JSON line with
+  value      whole-step weight bandwidth = weight bytes read / step time (GB/s)
+  per_m      ms per call, weight-GB/s, int8 TOPS and % of the HBM roofline
+  roofline   for the dominant kernel (the matmul launch with the largest
+             duration): algorithmic bytes per launch / its average duration,
+             timed with HIP events on the stream the kernel runs on
+  cpu_baseline  the CPU oracle (never tuned) on a bounded sample of the same
+             sweep, in the same unit.
+`--sweep FILE` additionally times every (shape, M, path) point of the five
+workloads and writes one JSON object per point to FILE (used for the measured
+dispatch table and the results tables).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import iq4_xs_q8_amd as iq  # noqa: E402
+import synth  # noqa: E402
+
+METRIC = "IQ4_XS GEMM ms + weight-GB/s/int8-TOPS, % roofline, at M=1..512"
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
+INT8_PEAK_TOPS = 5000.0         # MI355X dense int8 MFMA, published
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
+MALL_BYTES = 256 << 20
+KERNEL_NAMES = {iq.PATH_GEMV: "k_gemv", iq.PATH_MMQ: "k_mmq", iq.PATH_DEQ_BF16: "k_gemm_bf16"}
+
+
+def algo_bytes_call(M, N, K):
+    """Algorithmic HBM bytes of one iq4xs_gemm call: the weights once, X read
+    (4 B/element), the quantized activations written and read (1.125 B/element
+    each way) and Y written."""
+    return 0.53125 * N * K + (4 + 2 * 1.125) * M * K + 4 * M * N
+
+
+def algo_bytes_kernel(M, N, K):
+    """Algorithmic bytes of one matmul launch: weights, prepared activations
+    (1 B per value + 4 B scale per 32), Y."""
+    return 0.53125 * N * K + 1.125 * M * K + 4 * M * N
+
+
+class Rotation:
+    """Copies of one weight matrix, enough to exceed twice the MALL."""
+
+    def __init__(self, W: np.ndarray, min_total=640 << 20):
+        base = torch.from_numpy(W).cuda()
+        n = max(2, math.ceil(min_total / base.numel()))
+        self.ws = [base] + [base.clone() for _ in range(n - 1)]
+        self.i = 0
+
+    def next(self):
+        w = self.ws[self.i]
+        self.i = (self.i + 1) % len(self.ws)
+        return w
+
+
+def time_events(fn, reps, stream):
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(reps):
+        fn()
+    stop.record(stream)
+    stop.synchronize()
+    return start.elapsed_time(stop) / reps      # ms
+
+
+def measure_point(rot, X, N, K, path, reps=30):
+    """ms per iq4xs_gemm call and ms per matmul-kernel launch (prepared act)."""
+    M = X.shape[0]
+    Y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    call = lambda: iq.gemm(rot.next(), X, path=path, out=Y)  # noqa: E731
+    for _ in range(3):
+        call()
+    t_call = time_events(call, reps, stream)
+    t_kern = None
+    if path != iq.PATH_DEQ_BF16:
+        act = iq.prepare_act(X)
+        kern = lambda: iq.gemm_act(rot.next(), act, M, K, path=path, out=Y)  # noqa: E731
+        for _ in range(3):
+            kern()
+        t_kern = time_events(kern, reps, stream)
+    return t_call, t_kern
+
+
+def point_record(N, K, M, path, t_call, t_kern):
+    wb = 0.53125 * N * K
+    ops = 2.0 * M * N * K
+    rec = {"N": N, "K": K, "M": M, "path": iq.path_name(path), "ms": t_call,
+           "weight_GBs": wb / (t_call * 1e-3) / 1e9,
+           "int8_TOPS": ops / (t_call * 1e-3) / 1e12,
+           "hbm_frac": algo_bytes_call(M, N, K) / (t_call * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    if t_kern is not None:
+        rec["kernel_ms"] = t_kern
+        rec["kernel_GBs"] = algo_bytes_kernel(M, N, K) / (t_kern * 1e-3) / 1e9
+        rec["kernel_hbm_frac"] = rec["kernel_GBs"] / HBM_PEAK_GBS
+        rec["kernel_mfma_frac"] = ops / (t_kern * 1e-3) / 1e12 / INT8_PEAK_TOPS
+    rec["mfma_frac"] = rec["int8_TOPS"] / INT8_PEAK_TOPS
+    # impossible-throughput flag: faster than the card can move the bytes
+    rec["impossible"] = bool(rec["hbm_frac"] > 1.0 or rec.get("kernel_hbm_frac", 0) > 1.0
+                             or rec["mfma_frac"] > 1.0)
+    return rec
+
+
+def cpu_baseline(wl, N, K, ms, target_s=12.0):
+    """The oracle (as it stands) on a sample of output columns of the same
+    sweep; returns weight-GB/s of that sample."""
+    import oracle
+    o = oracle.get()
+    W = wl.w(N, K)
+    Xs = {M: wl.x(M, K, N=N) for M in ms}
+
+    def run(ncols):
+        Ws = np.ascontiguousarray(W[:ncols])
+        t0 = time.perf_counter()
+        for M in ms:
+            o.gemm_q8_1(Ws, o.quantize_q8_1(Xs[M]), K)
+        return time.perf_counter() - t0
+
+    probe = 64
+    t = run(probe)
+    ncols = int(min(N, max(probe, probe * target_s / max(t, 1e-3))))
+    t = run(ncols)
+    wbytes = 0.53125 * ncols * K * len(ms)
+    return {"value": wbytes / t / 1e9, "unit": "weight-GB/s", "cores": o.threads(), "kind": "oracle",
+            "sample": f"{ncols} of {N} output columns, every M in {list(ms)}, quantize included; "
+                      f"{t:.1f} s"}
+
+
+def run_sweep(path_out):
+    """Every (shape, M, path) point of the five workloads -> JSONL."""
+    with open(path_out, "w") as f:
+        for wl in synth.WORKLOADS:
+            for (N, K) in wl.shapes:
+                rot = Rotation(wl.w(N, K))
+                for M in wl.ms:
+                    X = torch.from_numpy(wl.x(M, K, N=N)).cuda()
+                    paths = [iq.PATH_AUTO, iq.PATH_MMQ]
+                    if M <= 4:
+                        paths.append(iq.PATH_GEMV)
+                    if M >= 32:
+                        paths.append(iq.PATH_DEQ_BF16)
+                    for p in paths:
+                        t_call, t_kern = measure_point(rot, X, N, K, p, reps=20)
+                        rec = point_record(N, K, M, p, t_call, t_kern)
+                        rec["workload"] = wl.name
+                        if p == iq.PATH_AUTO:
+                            rec["auto"] = iq.path_name(iq.dispatch(M, N, K))
+                        f.write(json.dumps(rec) + "\n")
+                        f.flush()
+                        print(f"[sweep] {wl.cid} N={N} K={K} M={M} {rec['path']}: {rec['ms']:.4f} ms "
+                              f"{rec['weight_GBs']:.0f} GB/s", flush=True)
+                del rot
+                torch.cuda.empty_cache()
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--sweep", default=None, help="also time every workload point -> JSONL")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the matmul is built and measured on a single MI355X "
+              "(multi-GPU sharding is a design note only); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+
+    wl = synth.DECODE_ATTN
+    (N, K), ms = wl.shapes[0], wl.ms
+    rot = Rotation(wl.w(N, K))
+    Xs = {M: torch.from_numpy(wl.x(M, K, N=N)).cuda() for M in ms}
+    Ys = {M: torch.empty((M, N), dtype=torch.float32, device="cuda") for M in ms}
+    stream = torch.cuda.current_stream()
+
+    def step():
+        for M in ms:
+            iq.gemm(rot.next(), Xs[M], out=Ys[M])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = ev0.elapsed_time(ev1) / args.steps
+    wbytes = 0.53125 * N * K * len(ms)
+    value = wbytes / (step_ms * 1e-3) / 1e9
+
+    per_m = []
+    for M in ms:
+        path = iq.dispatch(M, N, K)
+        t_call, t_kern = measure_point(rot, Xs[M], N, K, path)
+        per_m.append(point_record(N, K, M, path, t_call, t_kern))
+    dom = max(per_m, key=lambda r: r["kernel_ms"])
+    achieved = algo_bytes_kernel(dom["M"], N, K) / (dom["kernel_ms"] * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                "kernel": KERNEL_NAMES[iq.PATHS[dom["path"]]], "M": dom["M"],
+                "bytes_per_launch": algo_bytes_kernel(dom["M"], N, K),
+                "avg_launch_ms": dom["kernel_ms"]}
+
+    out = {"metric": METRIC, "value": value, "unit": "weight-GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": step_ms,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+           "data": "synthetic (seeded IQ4_XS weights, N(0,1) activations with 1% outlier channels)",
+           "config": {"workload": "IQ4_XS x Q8_1 GEMM decode sweep, attention/GDN input projection "
+                                  "N=10240 K=5120, M in {1,2,4,8,16}, quantize included",
+                      "N": N, "K": K, "M": list(ms), "weight_copies": len(rot.ws)},
+           "wall_s": wall, "per_m": per_m, "roofline": roofline}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, N, K, ms)
+    if args.sweep:
+        del rot
+        torch.cuda.empty_cache()
+        run_sweep(args.sweep)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,151 @@
+/*
+ * iq4xs.h -- C ABI of libiq4xs.so: the IQ4_XS x Q8_1 quantized matmul
+ *            Y[M,N] = X[M,K] * W[N,K]^T on AMD Instinct MI355X (gfx950).
+ *
+ * Sources.  "V100TPS engine log" (agent-report.daedalus.work/V100TPS/engine.html):
+ *   - section on the batched IQ4_XS kernel: the IQ4_XS sub-block (32 weights
+ *     in four 32-bit words, low nibbles = elements 0-15, high nibbles =
+ *     16-31), the per-sub-block scale d*(ls-32), the kvalues_iq4nl lookup in
+ *     place of q-8, and the Q8_1-quantized activations;
+ *   - the M=64 kernel-launch table: quantize_q8_1 followed by the matmul; the
+ *     dequantize-then-dense-GEMM path;
+ *   - the mmvq vs dequant+GEMM table and the new-kernel vs dispatcher table:
+ *     one path per range of M, chosen by a dispatcher.
+ * "SGLang MoE port thread" (lcz.me/post/31556), section on the torch bridge:
+ *   the stream crosses the boundary as a plain integer handle and the shim
+ *   includes no framework header.
+ *
+ * Formats (GGUF; the pages name them but print no byte layout):
+ *   IQ4_XS super-block, 136 bytes, 256 weights along K:
+ *     bytes 0-1   fp16 d
+ *     bytes 2-3   u16 scales_h: bits 2b..2b+1 = high 2 bits of ls_b
+ *     bytes 4-7   u8 scales_l[4]: nibble b%2 of scales_l[b/2] = low 4 bits of ls_b
+ *     bytes 8-135 u8 qs[128]: sub-block b (elements 32b..32b+31) owns
+ *                 qs[16b..16b+15]; element 32b+t is the low nibble of
+ *                 qs[16b+t] for t < 16 and the high nibble of qs[16b+t-16]
+ *                 otherwise.
+ *     weight = d * (ls_b - 32) * kvalues_iq4nl[index].
+ *   W is [N][K/256] super-blocks: row n's blocks are contiguous.
+ *   Q8_1 block, 36 bytes, 32 activations: fp16 d, fp16 s, int8 q[32].
+ *     d = fp16(amax/127), q = round-half-away(x / (amax/127)) computed in
+ *     IEEE fp32 (q = 0 if the fp32 scale is 0), s = fp16(d * sum q).
+ *   Xq is [M][K/32] blocks, row-major.
+ *   X and Y are dense row-major fp32, [M][K] and [M][N].
+ *
+ * Conventions for every entry point:
+ *   - returns IQ4XS_OK (0) or a negative IQ4XS_E* code and never throws; the
+ *     message of the last error on the calling thread is iq4xs_last_error();
+ *   - arguments are validated on the host before any HIP call;
+ *   - device pointers are caller-owned (the library never frees them);
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream);
+ *     work is enqueued asynchronously and stream-ordered, there is no host
+ *     synchronisation; errors raised while kernels execute surface at the
+ *     caller's next synchronisation, as in HIP;
+ *   - the library is thread-safe; environment variables are read once, at
+ *     the first call.
+ */
+#ifndef IQ4XS_H
+#define IQ4XS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---- */
+#define IQ4XS_OK 0
+#define IQ4XS_EINVAL (-1)  /* null pointer, M/N < 1, K not a multiple of 256, size overflow,
+                              Y overlapping an input, unknown path                         */
+#define IQ4XS_EALIGN (-2)  /* W, X or Y not 16-byte aligned, Xq not 4-byte aligned          */
+#define IQ4XS_EDEVICE (-3) /* no HIP device, or the current device is not gfx950            */
+#define IQ4XS_ETABLE (-4)  /* dispatch table unreadable, malformed, or for another device   */
+#define IQ4XS_ELAUNCH (-5) /* a HIP runtime call or a kernel launch failed                  */
+#define IQ4XS_ENOMEM (-6)  /* stream-ordered scratch allocation failed                      */
+#define IQ4XS_EPATH (-7)   /* the requested path cannot run this shape                     */
+
+/* ---- paths ---- */
+#define IQ4XS_PATH_AUTO 0     /* the dispatcher picks from its measured table            */
+#define IQ4XS_PATH_GEMV 1     /* wavefront-per-row integer-dot kernel, 1 <= M <= 4        */
+#define IQ4XS_PATH_MMQ 2      /* int8-MFMA tile kernel, any M                             */
+#define IQ4XS_PATH_DEQ_BF16 3 /* dequantize W and X~ to bf16, bf16-MFMA GEMM (inexact:
+                                 rounds W~ and X~ to 8 significant bits)                 */
+#define IQ4XS_NUM_PATHS 4
+
+/* Sizes in bytes of an IQ4_XS matrix [N][K] and of a Q8_1 matrix [M][K].
+ * EINVAL for non-positive sizes, K % 256 != 0 (K % 32 for Q8_1), overflow. */
+int iq4xs_weight_bytes(int64_t N, int64_t K, size_t *out);
+int iq4xs_q8_1_bytes(int64_t M, int64_t K, size_t *out);
+
+/* Optional explicit initialisation: reads IQ4XS_DISPATCH_TABLE, IQ4XS_LOG and
+ * IQ4XS_ALLOW_BF16 and loads the dispatch table.  Every other entry point calls
+ * it on first use.  Does not touch the GPU. */
+int iq4xs_init(void);
+
+/* Quantize fp32 X [M][K] to Q8_1 Xq [M][K/32] (36-byte blocks), bit-exactly as
+ * described above ("V100TPS engine log", M=64 kernel-launch table:
+ * quantize_q8_1).  K % 32 == 0.  X 16-byte aligned, Xq 4-byte aligned. */
+int iq4xs_quantize_q8_1(const float *X, void *Xq, int64_t M, int64_t K, void *stream);
+
+/* Y = X * W^T with X quantized to Q8_1 on the device ("V100TPS engine log",
+ * batched IQ4_XS kernel section).  Quantization, the dispatcher's choice of
+ * path and the matmul are all enqueued on `stream`.  Y is overwritten.
+ * Stream-ordered scratch (about 1.2*M*K bytes, plus 2*(M+N)*K for the bf16
+ * path) is allocated from the device's default memory pool and released on
+ * `stream`. */
+int iq4xs_gemm(const void *W, const float *X, float *Y, int64_t M, int64_t N, int64_t K,
+               void *stream);
+
+/* As iq4xs_gemm with the path forced (IQ4XS_PATH_*; AUTO = dispatcher). */
+int iq4xs_gemm_path(const void *W, const float *X, float *Y, int64_t M, int64_t N, int64_t K,
+                    int path, void *stream);
+
+/* Y = dequant(Xq) * W^T from an already-quantized Q8_1 Xq (layout above). */
+int iq4xs_gemm_q8_1(const void *W, const void *Xq, float *Y, int64_t M, int64_t N, int64_t K,
+                    int path, void *stream);
+
+/* Prepared activations: X quantized once (bit-identical to
+ * iq4xs_quantize_q8_1) into the layout the GEMV and MMQ kernels read, so one
+ * quantization can feed several weight matrices and the matmul kernel can be
+ * launched on its own.  `act` is a caller-owned device buffer of
+ * iq4xs_act_bytes(M, K) bytes, 256-byte aligned; its contents are private to
+ * the library (int8 values reordered per 32-block plus one fp32 scale per
+ * block, rows padded to a multiple of 32).  K % 256 == 0. */
+int iq4xs_act_bytes(int64_t M, int64_t K, size_t *out);
+int iq4xs_prepare_act(const float *X, void *act, int64_t M, int64_t K, void *stream);
+/* Y = X * W^T from prepared activations; path AUTO, GEMV or MMQ (DEQ_BF16 is
+ * EPATH here).  Launches exactly one kernel. */
+int iq4xs_gemm_act(const void *W, const void *act, float *Y, int64_t M, int64_t N, int64_t K,
+                   int path, void *stream);
+
+/* Dequantize W [N][K] to bf16 Wb [N][K] (row-major): each weight
+ * d*(ls-32)*kvalues[index], computed exactly in fp32, rounded to the nearest
+ * bf16 (ties to even).  ("V100TPS engine log", M=64 kernel-launch table:
+ * dequantize_block_iq4_xs before the dense GEMM.)  Wb 16-byte aligned. */
+int iq4xs_dequantize_bf16(const void *W, void *Wb, int64_t N, int64_t K, void *stream);
+
+/* Host-only query: the path IQ4XS_PATH_AUTO resolves to for (M, N, K) under the
+ * loaded table ("V100TPS engine log", mmvq vs dequant+GEMM table: the band
+ * boundaries are measured, not hard-coded). */
+int iq4xs_dispatch(int64_t M, int64_t N, int64_t K, int *path_out);
+
+/* Replace the dispatch table with the one in `path` (NULL: the built-in
+ * default).  On ETABLE the previous table stays in force.  Format: text lines
+ *   arch <gfx name>
+ *   band <GEMV|MMQ|DEQ_BF16> <M_lo> <M_hi> <N or *> <K or *>
+ * '#' starts a comment; the first band that matches (M, N, K) wins; DEQ_BF16
+ * bands are skipped unless IQ4XS_ALLOW_BF16=1 was set at initialisation. */
+int iq4xs_load_dispatch_table(const char *path);
+
+/* Name of a path ("AUTO", "GEMV", "MMQ", "DEQ_BF16") or "?" */
+const char *iq4xs_path_name(int path);
+
+/* Message for the last error on this thread ("" if none). */
+const char *iq4xs_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IQ4XS_H */

@@ -1,0 +1,210 @@
+"""iq4_xs_q8_amd -- IQ4_XS x Q8_1 quantized matmul for AMD MI355X (gfx950).
+
+Thin ctypes binding over libiq4xs.so (C ABI in include/iq4xs.h).  This
+module only marshals arguments: tensors become device pointers, the current
+torch stream becomes the hipStream_t, and non-zero status codes become
+Iq4xsError.  Every step of the computation runs in the library's HIP
+kernels; there is no CPU or PyTorch fallback, and importing the package
+fails loudly when the library has not been built
+(``python -m iq4_xs_q8_amd.build``).
+
+Layouts (see the header): W is uint8 [N, K/256*136] (GGUF IQ4_XS super-blocks,
+row n = output row n), X fp32 [M, K], Xq uint8 [M, K/32*36] (Q8_1 blocks),
+Y fp32 [M, N].
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libiq4xs.so")
+
+OK, EINVAL, EALIGN, EDEVICE, ETABLE, ELAUNCH, ENOMEM, EPATH = 0, -1, -2, -3, -4, -5, -6, -7
+PATH_AUTO, PATH_GEMV, PATH_MMQ, PATH_DEQ_BF16 = 0, 1, 2, 3
+PATHS = {"AUTO": PATH_AUTO, "GEMV": PATH_GEMV, "MMQ": PATH_MMQ, "DEQ_BF16": PATH_DEQ_BF16}
+
+EXPORTS = ("iq4xs_weight_bytes", "iq4xs_q8_1_bytes", "iq4xs_init", "iq4xs_quantize_q8_1",
+           "iq4xs_gemm", "iq4xs_gemm_path", "iq4xs_gemm_q8_1", "iq4xs_act_bytes",
+           "iq4xs_prepare_act", "iq4xs_gemm_act", "iq4xs_dequantize_bf16",
+           "iq4xs_dispatch", "iq4xs_load_dispatch_table", "iq4xs_path_name", "iq4xs_last_error")
+
+
+class Iq4xsError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"iq4xs error {code}: {message}")
+        self.code = code
+
+
+def _load(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m iq4_xs_q8_amd.build`")
+    lib = ctypes.CDLL(path)
+    p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    sz = ctypes.POINTER(ctypes.c_size_t)
+    sig = {
+        "iq4xs_weight_bytes": [i64, i64, sz],
+        "iq4xs_q8_1_bytes": [i64, i64, sz],
+        "iq4xs_init": [],
+        "iq4xs_quantize_q8_1": [p, p, i64, i64, p],
+        "iq4xs_gemm": [p, p, p, i64, i64, i64, p],
+        "iq4xs_gemm_path": [p, p, p, i64, i64, i64, i32, p],
+        "iq4xs_gemm_q8_1": [p, p, p, i64, i64, i64, i32, p],
+        "iq4xs_act_bytes": [i64, i64, sz],
+        "iq4xs_prepare_act": [p, p, i64, i64, p],
+        "iq4xs_gemm_act": [p, p, p, i64, i64, i64, i32, p],
+        "iq4xs_dequantize_bf16": [p, p, i64, i64, p],
+        "iq4xs_dispatch": [i64, i64, i64, ctypes.POINTER(ctypes.c_int)],
+        "iq4xs_load_dispatch_table": [ctypes.c_char_p],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.iq4xs_path_name.argtypes = [ctypes.c_int]
+    lib.iq4xs_path_name.restype = ctypes.c_char_p
+    lib.iq4xs_last_error.argtypes = []
+    lib.iq4xs_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = None
+
+
+def _L() -> ctypes.CDLL:
+    """The loaded library; raises if libiq4xs.so has not been built."""
+    global _lib
+    if _lib is None:
+        _lib = _load()
+    return _lib
+
+
+def __getattr__(name):          # ``iq4_xs_q8_amd.lib`` loads on first access
+    if name == "lib":
+        return _L()
+    raise AttributeError(name)
+
+
+def check(rc: int) -> None:
+    if rc != OK:
+        raise Iq4xsError(rc, _L().iq4xs_last_error().decode())
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dev(t: torch.Tensor, dtype: torch.dtype, name: str) -> int:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def weight_bytes(N: int, K: int) -> int:
+    out = ctypes.c_size_t()
+    check(_L().iq4xs_weight_bytes(N, K, ctypes.byref(out)))
+    return out.value
+
+
+def q8_1_bytes(M: int, K: int) -> int:
+    out = ctypes.c_size_t()
+    check(_L().iq4xs_q8_1_bytes(M, K, ctypes.byref(out)))
+    return out.value
+
+
+def quantize_q8_1(X: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """fp32 [M, K] -> Q8_1 uint8 [M, K/32*36]."""
+    M, K = X.shape
+    if out is None:
+        out = torch.empty((M, (K // 32) * 36), dtype=torch.uint8, device=X.device)
+    with torch.cuda.device(X.device):
+        check(_L().iq4xs_quantize_q8_1(_dev(X, torch.float32, "X"), _dev(out, torch.uint8, "Xq"),
+                                      M, K, _stream(X)))
+    return out
+
+
+def gemm(W: torch.Tensor, X: torch.Tensor, path: int = PATH_AUTO,
+         out: torch.Tensor | None = None) -> torch.Tensor:
+    """Y[M, N] = X[M, K] * W[N, K]^T with X quantized to Q8_1 on the device."""
+    M, K = X.shape
+    N = W.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=X.device)
+    with torch.cuda.device(X.device):
+        check(_L().iq4xs_gemm_path(_dev(W, torch.uint8, "W"), _dev(X, torch.float32, "X"),
+                                  _dev(out, torch.float32, "Y"), M, N, K, path, _stream(X)))
+    return out
+
+
+def gemm_q8_1(W: torch.Tensor, Xq: torch.Tensor, K: int, path: int = PATH_AUTO,
+              out: torch.Tensor | None = None) -> torch.Tensor:
+    """Y[M, N] from already-quantized Q8_1 activations Xq [M, K/32*36]."""
+    M = Xq.shape[0]
+    N = W.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=Xq.device)
+    with torch.cuda.device(Xq.device):
+        check(_L().iq4xs_gemm_q8_1(_dev(W, torch.uint8, "W"), _dev(Xq, torch.uint8, "Xq"),
+                                  _dev(out, torch.float32, "Y"), M, N, K, path, _stream(Xq)))
+    return out
+
+
+def act_bytes(M: int, K: int) -> int:
+    out = ctypes.c_size_t()
+    check(_L().iq4xs_act_bytes(M, K, ctypes.byref(out)))
+    return out.value
+
+
+def prepare_act(X: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Quantize fp32 X [M, K] into the kernels' activation layout (opaque uint8)."""
+    M, K = X.shape
+    if out is None:
+        out = torch.empty(act_bytes(M, K), dtype=torch.uint8, device=X.device)
+    with torch.cuda.device(X.device):
+        check(_L().iq4xs_prepare_act(_dev(X, torch.float32, "X"), _dev(out, torch.uint8, "act"),
+                                    M, K, _stream(X)))
+    return out
+
+
+def gemm_act(W: torch.Tensor, act: torch.Tensor, M: int, K: int, path: int = PATH_AUTO,
+             out: torch.Tensor | None = None) -> torch.Tensor:
+    """Y[M, N] from prepared activations (one kernel launch)."""
+    N = W.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=act.device)
+    with torch.cuda.device(act.device):
+        check(_L().iq4xs_gemm_act(_dev(W, torch.uint8, "W"), _dev(act, torch.uint8, "act"),
+                                 _dev(out, torch.float32, "Y"), M, N, K, path, _stream(act)))
+    return out
+
+
+def dequantize_bf16(W: torch.Tensor, K: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """IQ4_XS [N, K/256*136] -> bf16 [N, K]."""
+    N = W.shape[0]
+    if out is None:
+        out = torch.empty((N, K), dtype=torch.bfloat16, device=W.device)
+    with torch.cuda.device(W.device):
+        check(_L().iq4xs_dequantize_bf16(_dev(W, torch.uint8, "W"), _dev(out, torch.bfloat16, "Wb"),
+                                        N, K, _stream(W)))
+    return out
+
+
+def dispatch(M: int, N: int, K: int) -> int:
+    p = ctypes.c_int()
+    check(_L().iq4xs_dispatch(M, N, K, ctypes.byref(p)))
+    return p.value
+
+
+def load_dispatch_table(path: str | None = None) -> None:
+    check(_L().iq4xs_load_dispatch_table(path.encode() if path else None))
+
+
+def path_name(p: int) -> str:
+    return _L().iq4xs_path_name(p).decode()

@@ -1,0 +1,436 @@
+// abi.hip -- the extern "C" entry points of libiq4xs.so (declared and
+// documented in include/iq4xs.h): validation, initialisation, the device
+// check, stream-ordered scratch, and the launch sequence of each path.
+//
+// "SGLang MoE port thread" (lcz.me/post/31556), section on the torch bridge:
+// the stream arrives as a plain handle and no framework header is included.
+// "V100TPS engine log" (agent-report.daedalus.work/V100TPS/engine.html),
+// section on the end-to-end concurrency test: a getenv on every matmul was
+// suspected of costing time, so the environment is read once here.
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <fstream>
+#include <mutex>
+#include <sstream>
+#include <string>
+#include <vector>
+
+#include "common.hpp"
+#include "dispatch.hpp"
+#include "iq4xs.h"
+
+using namespace iq4xs;
+
+namespace {
+
+thread_local std::string g_err;
+
+struct Config {
+    bool log = false;
+    bool allow_bf16 = false;
+    int init_status = IQ4XS_OK;
+};
+
+std::once_flag g_once;
+Config g_cfg;
+std::mutex g_mu;                       // guards g_table and g_dev_ok
+Table g_table;
+std::vector<int> g_dev_ok;             // per device: 0 unknown, 1 gfx950, -1 other
+
+int fail(int code, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    if (g_cfg.log)
+        fprintf(stderr, "[iq4xs] error %d: %s\n", code, buf);
+    return code;
+}
+
+int load_table_text(const std::string &text, const char *what)
+{
+    Table t;
+    std::string err;
+    if (!parse_table(text, &t, &err))
+        return fail(IQ4XS_ETABLE, "%s: %s", what, err.c_str());
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_table = t;
+    return IQ4XS_OK;
+}
+
+int load_table_file(const char *path)
+{
+    std::ifstream f(path);
+    if (!f)
+        return fail(IQ4XS_ETABLE, "cannot read dispatch table %s", path);
+    std::stringstream ss;
+    ss << f.rdbuf();
+    return load_table_text(ss.str(), path);
+}
+
+void do_init()
+{
+    const char *v = getenv("IQ4XS_LOG");
+    g_cfg.log = v && v[0] == '1';
+    v = getenv("IQ4XS_ALLOW_BF16");
+    g_cfg.allow_bf16 = v && v[0] == '1';
+    int st = load_table_text(default_table_text(), "built-in dispatch table");
+    const char *path = getenv("IQ4XS_DISPATCH_TABLE");
+    if (st == IQ4XS_OK && path && path[0])
+        st = load_table_file(path);
+    g_cfg.init_status = st;
+}
+
+int ensure_init()
+{
+    std::call_once(g_once, do_init);
+    return g_cfg.init_status;
+}
+
+// The current device must be a gfx950 and the table must be for it.
+int check_device()
+{
+    int dev = -1, count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || count < 1) {
+        (void)hipGetLastError();
+        return fail(IQ4XS_EDEVICE, "no HIP device");
+    }
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= count) {
+        (void)hipGetLastError();
+        return fail(IQ4XS_EDEVICE, "no current HIP device");
+    }
+    std::lock_guard<std::mutex> lk(g_mu);
+    if ((int)g_dev_ok.size() < count)
+        g_dev_ok.resize(count, 0);
+    if (g_dev_ok[dev] == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(IQ4XS_EDEVICE, "cannot query device %d", dev);
+        }
+        g_dev_ok[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+        if (g_dev_ok[dev] == 1) {
+            // keep freed scratch in the pool so steady-state calls do not
+            // return memory to the driver
+            hipMemPool_t pool;
+            if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
+                uint64_t thr = UINT64_MAX;
+                (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &thr);
+            }
+            (void)hipGetLastError();
+        }
+    }
+    if (g_dev_ok[dev] != 1)
+        return fail(IQ4XS_EDEVICE, "device %d is not gfx950", dev);
+    if (g_table.arch != "gfx950")
+        return fail(IQ4XS_ETABLE, "dispatch table is for %s, device is gfx950", g_table.arch.c_str());
+    return IQ4XS_OK;
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t *out)
+{
+    if (a < 0 || b < 0)
+        return false;
+    if (a != 0 && b > INT64_MAX / 4 / a)
+        return false;
+    *out = a * b;
+    return true;
+}
+
+// M, N >= 1, K a positive multiple of 256, and every buffer size far from overflow.
+int check_dims(int64_t M, int64_t N, int64_t K)
+{
+    int64_t t;
+    if (M < 1 || N < 1 || K < QK || K % QK)
+        return fail(IQ4XS_EINVAL, "need M >= 1, N >= 1, K a positive multiple of 256 (M=%lld N=%lld K=%lld)",
+                    (long long)M, (long long)N, (long long)K);
+    if (M > (1LL << 31) || N > (1LL << 31) || K > (1LL << 31) || !mul_ok(M, K, &t) ||
+        !mul_ok(N, K, &t) || !mul_ok(M, N, &t) || !mul_ok(t, 4, &t))
+        return fail(IQ4XS_EINVAL, "sizes overflow");
+    return IQ4XS_OK;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb)
+{
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+struct Scratch {
+    void *p = nullptr;
+    hipStream_t s = nullptr;
+    ~Scratch()
+    {
+        if (p)
+            (void)hipFreeAsync(p, s);
+    }
+};
+
+int launch_err(hipError_t e, const char *what)
+{
+    if (e == hipSuccess)
+        return IQ4XS_OK;
+    (void)hipGetLastError();
+    return fail(IQ4XS_ELAUNCH, "%s: %s", what, hipGetErrorString(e));
+}
+
+int resolve_path(int path, int64_t M, int64_t N, int64_t K, int *out)
+{
+    if (path < 0 || path >= IQ4XS_NUM_PATHS)
+        return fail(IQ4XS_EINVAL, "unknown path %d", path);
+    if (path == IQ4XS_PATH_AUTO) {
+        int st = ensure_init();
+        if (st != IQ4XS_OK)
+            return fail(st, "dispatch table not loaded: %s", g_err.c_str());
+        {
+            std::lock_guard<std::mutex> lk(g_mu);
+            path = table_lookup(g_table, M, N, K, g_cfg.allow_bf16);
+        }
+        if (!path)
+            return fail(IQ4XS_EPATH, "no dispatch band covers M=%lld N=%lld K=%lld", (long long)M,
+                        (long long)N, (long long)K);
+    }
+    if (path == IQ4XS_PATH_GEMV && M > GEMV_MAX_M)
+        return fail(IQ4XS_EPATH, "GEMV path handles M <= %d (M=%lld)", GEMV_MAX_M, (long long)M);
+    if (g_cfg.log)
+        fprintf(stderr, "[iq4xs] M=%lld N=%lld K=%lld -> %s\n", (long long)M, (long long)N,
+                (long long)K, path_name(path));
+    *out = path;
+    return IQ4XS_OK;
+}
+
+// Common tail of iq4xs_gemm_path / iq4xs_gemm_q8_1.  Exactly one of X (fp32)
+// and Xq (Q8_1 blocks) is non-null.
+int run_gemm(const void *W, const float *X, const void *Xq, float *Y, int64_t M, int64_t N, int64_t K,
+             int path, hipStream_t s)
+{
+    int st = resolve_path(path, M, N, K, &path);
+    if (st != IQ4XS_OK)
+        return st;
+    if ((st = check_device()) != IQ4XS_OK)
+        return st;
+
+    Scratch scr;
+    scr.s = s;
+    if (path == IQ4XS_PATH_GEMV || path == IQ4XS_PATH_MMQ) {
+        const size_t bytes = xplanes_bytes(M, K);
+        if (hipMallocAsync(&scr.p, bytes, s) != hipSuccess) {
+            (void)hipGetLastError();
+            scr.p = nullptr;
+            return fail(IQ4XS_ENOMEM, "scratch of %zu bytes", bytes);
+        }
+        const XPlanes xp = xplanes_at(scr.p, M, K);
+        hipError_t e = X ? launch_quantize(X, nullptr, &xp, nullptr, M, K, s)
+                         : launch_q8_1_convert(Xq, &xp, nullptr, M, K, s);
+        if ((st = launch_err(e, "quantize")) != IQ4XS_OK)
+            return st;
+        e = path == IQ4XS_PATH_GEMV ? launch_gemv(W, xp, Y, N, s) : launch_mmq(W, xp, Y, N, s);
+        return launch_err(e, path_name(path));
+    }
+    // DEQ_BF16: X~ bf16 [M][K], then W~ bf16 [N][K] (256-byte aligned)
+    const size_t xbytes = (size_t)round_up(M * K * 2, 256);
+    const size_t bytes = xbytes + (size_t)(N * K * 2);
+    if (hipMallocAsync(&scr.p, bytes, s) != hipSuccess) {
+        (void)hipGetLastError();
+        scr.p = nullptr;
+        return fail(IQ4XS_ENOMEM, "scratch of %zu bytes", bytes);
+    }
+    uint16_t *xb = (uint16_t *)scr.p;
+    uint16_t *wb = (uint16_t *)((char *)scr.p + xbytes);
+    const hipError_t e = X ? launch_quantize(X, nullptr, nullptr, xb, M, K, s)
+                           : launch_q8_1_convert(Xq, nullptr, xb, M, K, s);
+    if ((st = launch_err(e, "quantize")) != IQ4XS_OK)
+        return st;
+    if ((st = launch_err(launch_dequant_bf16(W, wb, N, K, s), "dequant_bf16")) != IQ4XS_OK)
+        return st;
+    return launch_err(launch_gemm_bf16(xb, wb, Y, M, N, K, s), "gemm_bf16");
+}
+
+}  // namespace
+
+extern "C" {
+
+int iq4xs_weight_bytes(int64_t N, int64_t K, size_t *out)
+{
+    if (!out)
+        return fail(IQ4XS_EINVAL, "null output pointer");
+    if (N < 1 || K < QK || K % QK || N > (1LL << 40) || K > (1LL << 40))
+        return fail(IQ4XS_EINVAL, "need N >= 1 and K a positive multiple of 256");
+    *out = (size_t)N * (size_t)(K / QK) * WBLK;
+    return IQ4XS_OK;
+}
+
+int iq4xs_q8_1_bytes(int64_t M, int64_t K, size_t *out)
+{
+    if (!out)
+        return fail(IQ4XS_EINVAL, "null output pointer");
+    if (M < 1 || K < SB || K % SB || M > (1LL << 40) || K > (1LL << 40))
+        return fail(IQ4XS_EINVAL, "need M >= 1 and K a positive multiple of 32");
+    *out = (size_t)M * (size_t)(K / SB) * XBLK;
+    return IQ4XS_OK;
+}
+
+int iq4xs_init(void) { return ensure_init(); }
+
+int iq4xs_quantize_q8_1(const float *X, void *Xq, int64_t M, int64_t K, void *stream)
+{
+    if (!X || !Xq)
+        return fail(IQ4XS_EINVAL, "null pointer");
+    if (M < 1 || K < SB || K % SB || M > (1LL << 31) || K > (1LL << 31) || M * K > (1LL << 60) / 4)
+        return fail(IQ4XS_EINVAL, "need M >= 1 and K a positive multiple of 32");
+    if (!aligned(X, 16) || !aligned(Xq, 4))
+        return fail(IQ4XS_EALIGN, "X must be 16-byte and Xq 4-byte aligned");
+    if (overlaps(X, (size_t)(M * K * 4), Xq, (size_t)(M * (K / SB) * XBLK)))
+        return fail(IQ4XS_EINVAL, "X and Xq overlap");
+    ensure_init();
+    int st = check_device();
+    if (st != IQ4XS_OK)
+        return st;
+    return launch_err(launch_quantize(X, Xq, nullptr, nullptr, M, K, (hipStream_t)stream), "quantize");
+}
+
+int iq4xs_gemm_path(const void *W, const float *X, float *Y, int64_t M, int64_t N, int64_t K,
+                    int path, void *stream)
+{
+    if (!W || !X || !Y)
+        return fail(IQ4XS_EINVAL, "null pointer");
+    int st = check_dims(M, N, K);
+    if (st != IQ4XS_OK)
+        return st;
+    if (!aligned(W, 16) || !aligned(X, 16) || !aligned(Y, 16))
+        return fail(IQ4XS_EALIGN, "W, X and Y must be 16-byte aligned");
+    const size_t yb = (size_t)(M * N * 4);
+    if (overlaps(Y, yb, W, (size_t)(N * (K / QK) * WBLK)) || overlaps(Y, yb, X, (size_t)(M * K * 4)))
+        return fail(IQ4XS_EINVAL, "Y overlaps an input");
+    return run_gemm(W, X, nullptr, Y, M, N, K, path, (hipStream_t)stream);
+}
+
+int iq4xs_gemm(const void *W, const float *X, float *Y, int64_t M, int64_t N, int64_t K, void *stream)
+{
+    return iq4xs_gemm_path(W, X, Y, M, N, K, IQ4XS_PATH_AUTO, stream);
+}
+
+int iq4xs_gemm_q8_1(const void *W, const void *Xq, float *Y, int64_t M, int64_t N, int64_t K,
+                    int path, void *stream)
+{
+    if (!W || !Xq || !Y)
+        return fail(IQ4XS_EINVAL, "null pointer");
+    int st = check_dims(M, N, K);
+    if (st != IQ4XS_OK)
+        return st;
+    if (!aligned(W, 16) || !aligned(Y, 16) || !aligned(Xq, 4))
+        return fail(IQ4XS_EALIGN, "W and Y must be 16-byte and Xq 4-byte aligned");
+    const size_t yb = (size_t)(M * N * 4);
+    if (overlaps(Y, yb, W, (size_t)(N * (K / QK) * WBLK)) ||
+        overlaps(Y, yb, Xq, (size_t)(M * (K / SB) * XBLK)))
+        return fail(IQ4XS_EINVAL, "Y overlaps an input");
+    return run_gemm(W, nullptr, Xq, Y, M, N, K, path, (hipStream_t)stream);
+}
+
+int iq4xs_dequantize_bf16(const void *W, void *Wb, int64_t N, int64_t K, void *stream)
+{
+    if (!W || !Wb)
+        return fail(IQ4XS_EINVAL, "null pointer");
+    int st = check_dims(1, N, K);
+    if (st != IQ4XS_OK)
+        return st;
+    if (!aligned(W, 16) || !aligned(Wb, 16))
+        return fail(IQ4XS_EALIGN, "W and Wb must be 16-byte aligned");
+    if (overlaps(Wb, (size_t)(N * K * 2), W, (size_t)(N * (K / QK) * WBLK)))
+        return fail(IQ4XS_EINVAL, "W and Wb overlap");
+    ensure_init();
+    if ((st = check_device()) != IQ4XS_OK)
+        return st;
+    return launch_err(launch_dequant_bf16(W, (uint16_t *)Wb, N, K, (hipStream_t)stream), "dequant_bf16");
+}
+
+int iq4xs_act_bytes(int64_t M, int64_t K, size_t *out)
+{
+    if (!out)
+        return fail(IQ4XS_EINVAL, "null output pointer");
+    int st = check_dims(M, 1, K);
+    if (st != IQ4XS_OK)
+        return st;
+    *out = xplanes_bytes(M, K);
+    return IQ4XS_OK;
+}
+
+int iq4xs_prepare_act(const float *X, void *act, int64_t M, int64_t K, void *stream)
+{
+    if (!X || !act)
+        return fail(IQ4XS_EINVAL, "null pointer");
+    int st = check_dims(M, 1, K);
+    if (st != IQ4XS_OK)
+        return st;
+    if (!aligned(X, 16) || !aligned(act, 256))
+        return fail(IQ4XS_EALIGN, "X must be 16-byte and act 256-byte aligned");
+    if (overlaps(X, (size_t)(M * K * 4), act, xplanes_bytes(M, K)))
+        return fail(IQ4XS_EINVAL, "X and act overlap");
+    ensure_init();
+    if ((st = check_device()) != IQ4XS_OK)
+        return st;
+    const XPlanes xp = xplanes_at(act, M, K);
+    return launch_err(launch_quantize(X, nullptr, &xp, nullptr, M, K, (hipStream_t)stream), "quantize");
+}
+
+int iq4xs_gemm_act(const void *W, const void *act, float *Y, int64_t M, int64_t N, int64_t K,
+                   int path, void *stream)
+{
+    if (!W || !act || !Y)
+        return fail(IQ4XS_EINVAL, "null pointer");
+    int st = check_dims(M, N, K);
+    if (st != IQ4XS_OK)
+        return st;
+    if (!aligned(W, 16) || !aligned(Y, 16) || !aligned(act, 256))
+        return fail(IQ4XS_EALIGN, "W and Y must be 16-byte and act 256-byte aligned");
+    const size_t yb = (size_t)(M * N * 4);
+    if (overlaps(Y, yb, W, (size_t)(N * (K / QK) * WBLK)) || overlaps(Y, yb, act, xplanes_bytes(M, K)))
+        return fail(IQ4XS_EINVAL, "Y overlaps an input");
+    if ((st = resolve_path(path, M, N, K, &path)) != IQ4XS_OK)
+        return st;
+    if (path == IQ4XS_PATH_DEQ_BF16)
+        return fail(IQ4XS_EPATH, "prepared activations feed the GEMV and MMQ paths only");
+    if ((st = check_device()) != IQ4XS_OK)
+        return st;
+    const XPlanes xp = xplanes_at((void *)act, M, K);
+    const hipStream_t s = (hipStream_t)stream;
+    return launch_err(path == IQ4XS_PATH_GEMV ? launch_gemv(W, xp, Y, N, s) : launch_mmq(W, xp, Y, N, s),
+                      path_name(path));
+}
+
+int iq4xs_dispatch(int64_t M, int64_t N, int64_t K, int *path_out)
+{
+    if (!path_out)
+        return fail(IQ4XS_EINVAL, "null output pointer");
+    int st = check_dims(M, N, K);
+    if (st != IQ4XS_OK)
+        return st;
+    int p = 0;
+    if ((st = resolve_path(IQ4XS_PATH_AUTO, M, N, K, &p)) != IQ4XS_OK)
+        return st;
+    *path_out = p;
+    return IQ4XS_OK;
+}
+
+int iq4xs_load_dispatch_table(const char *path)
+{
+    int st = ensure_init();
+    (void)st;
+    st = path ? load_table_file(path) : load_table_text(default_table_text(), "built-in dispatch table");
+    if (st == IQ4XS_OK)
+        g_cfg.init_status = IQ4XS_OK;
+    return st;
+}
+
+const char *iq4xs_path_name(int path) { return path_name(path); }
+
+const char *iq4xs_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

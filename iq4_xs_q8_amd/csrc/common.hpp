@@ -1,0 +1,131 @@
+// common.hpp -- internal definitions shared by the HIP kernels of libiq4xs.
+//
+// Format facts ("V100TPS engine log", agent-report.daedalus.work/V100TPS/engine.html,
+// section on the batched IQ4_XS kernel; byte layout and codebook from the GGUF
+// IQ4_XS / Q8_1 formats, which the pages name but do not print):
+//   IQ4_XS super-block = 256 weights in 136 bytes {fp16 d, u16 scales_h,
+//   u8 scales_l[4], u8 qs[128]}; sub-block b = 32 weights in qs[16b..16b+15],
+//   low nibbles are elements 0-15, high nibbles 16-31; scale d*(ls-32);
+//   weight = scale * kvalues_iq4nl[nibble].
+//   Q8_1 block = 32 activations in 36 bytes {fp16 d, fp16 s, int8 q[32]}.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace iq4xs {
+
+constexpr int QK = 256;         // weights per super-block
+constexpr int SB = 32;          // weights per sub-block, activations per Q8_1 block
+constexpr int SUBS = QK / SB;   // sub-blocks per super-block
+constexpr int WBLK = 136;       // bytes per IQ4_XS super-block
+constexpr int XBLK = 36;        // bytes per Q8_1 block
+constexpr int QS_OFF = 8;       // offset of qs[] inside a super-block
+static_assert(2 + 2 + 4 + QK / 2 == WBLK, "IQ4_XS super-block size");
+static_assert(QS_OFF == 2 + 2 + 4, "qs follows d, scales_h, scales_l");
+static_assert(2 + 2 + SB == XBLK, "Q8_1 block size");
+
+// Rows of the internal activation planes are padded to a multiple of this, so
+// tile kernels can read whole 32-row MFMA tiles without bounds checks.
+constexpr int MPAD = 32;
+
+// ---- kvalues_iq4nl packed for byte-permute lookups -----------------------
+constexpr int8_t KVALUES[16] = {-127, -104, -83, -65, -49, -35, -22, -10,
+                                1,    13,   25,  38,  53,  69,  89,  113};
+constexpr uint32_t kv_word(int i)
+{
+    return (uint32_t)(uint8_t)KVALUES[4 * i] | ((uint32_t)(uint8_t)KVALUES[4 * i + 1] << 8) |
+           ((uint32_t)(uint8_t)KVALUES[4 * i + 2] << 16) |
+           ((uint32_t)(uint8_t)KVALUES[4 * i + 3] << 24);
+}
+constexpr uint32_t KV0 = kv_word(0), KV1 = kv_word(1), KV2 = kv_word(2), KV3 = kv_word(3);
+static_assert(KV0 == 0xBFAD9881u && KV3 == 0x71594535u, "codebook packing");
+
+// Four 4-bit indices (one per byte, values 0..15) -> four int8 kvalues.
+// v_perm_b32 picks byte s (0..7) of {hi:lo}; indices 0-7 come from {KV1:KV0},
+// 8-15 from {KV3:KV2}, and a third permute chooses per byte by bit 3.
+__device__ __forceinline__ uint32_t lut4(uint32_t nib)
+{
+    const uint32_t s = nib & 0x07070707u;
+    const uint32_t a = __builtin_amdgcn_perm(KV1, KV0, s);
+    const uint32_t b = __builtin_amdgcn_perm(KV3, KV2, s);
+    const uint32_t sel = ((nib >> 1) & 0x04040404u) | 0x03020100u;
+    return __builtin_amdgcn_perm(b, a, sel);
+}
+
+// 8 index bytes (2 dwords of qs) -> 16 int8 weights in "chunk" order:
+// out[0..1] = low nibbles (elements j..j+7), out[2..3] = high nibbles
+// (elements 16+j..16+j+7) of the same bytes.
+__device__ __forceinline__ void expand8(uint32_t w0, uint32_t w1, uint32_t out[4])
+{
+    out[0] = lut4(w0 & 0x0F0F0F0Fu);
+    out[1] = lut4(w1 & 0x0F0F0F0Fu);
+    out[2] = lut4((w0 >> 4) & 0x0F0F0F0Fu);
+    out[3] = lut4((w1 >> 4) & 0x0F0F0F0Fu);
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t h16)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h16);
+}
+
+// Effective scale d*(ls_b - 32) of sub-block b from the first 8 header bytes
+// (h0 = bytes 0-3 = d | scales_h << 16, h1 = bytes 4-7 = scales_l).  Exact in
+// fp32 (11 + 6 significant bits).
+__device__ __forceinline__ float sub_scale(uint32_t h0, uint32_t h1, int b)
+{
+    const uint32_t lo4 = (h1 >> (4 * b)) & 15u;           // nibble b%2 of scales_l[b/2]
+    const uint32_t hi2 = (h0 >> (16 + 2 * b)) & 3u;       // bits 2b..2b+1 of scales_h
+    const int ls = (int)(lo4 | (hi2 << 4));
+    return half_bits_to_float(h0 & 0xFFFFu) * (float)(ls - 32);
+}
+
+// ---- internal activation planes ------------------------------------------
+// The matmul kernels read Q8_1 activations from two planes instead of the
+// 36-byte ABI blocks:
+//   qp  int8  [Mp][K]    sub-block b of row m at qp[m*K + 32b], stored in
+//                         "chunk" order: bytes 0-7 = elements 0-7, 8-15 =
+//                         elements 16-23, 16-23 = elements 8-15, 24-31 =
+//                         elements 24-31, so chunk h (16 bytes at 16h) holds the
+//                         elements paired with the low and high nibbles of
+//                         qs[16b+8h .. 16b+8h+7];
+//   dp  float [K/32][Mp] the block scales d (fp16 widened), m fastest.
+// Mp = M rounded up to MPAD; rows M..Mp-1 are zero.
+struct XPlanes {
+    int8_t *qp;
+    float *dp;
+    int64_t M, Mp, K;
+};
+
+inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+inline size_t xplanes_bytes(int64_t M, int64_t K)
+{
+    const int64_t Mp = round_up(M, MPAD);
+    return (size_t)(Mp * K) + (size_t)(Mp * (K / SB)) * sizeof(float);
+}
+inline XPlanes xplanes_at(void *base, int64_t M, int64_t K)
+{
+    XPlanes p;
+    p.M = M;
+    p.Mp = round_up(M, MPAD);
+    p.K = K;
+    p.qp = (int8_t *)base;
+    p.dp = (float *)((char *)base + p.Mp * K);
+    return p;
+}
+
+// ---- launchers (each defined in the .hip file that holds its kernel) -----
+// All return a hipError_t from hipGetLastError() after the launch.
+hipError_t launch_quantize(const float *X, void *Xq, const XPlanes *planes, uint16_t *Xbf,
+                           int64_t M, int64_t K, hipStream_t s);
+hipError_t launch_q8_1_convert(const void *Xq, const XPlanes *planes, uint16_t *Xbf, int64_t M,
+                              int64_t K, hipStream_t s);
+hipError_t launch_gemv(const void *W, const XPlanes &x, float *Y, int64_t N, hipStream_t s);
+hipError_t launch_mmq(const void *W, const XPlanes &x, float *Y, int64_t N, hipStream_t s);
+hipError_t launch_dequant_bf16(const void *W, uint16_t *Wb, int64_t N, int64_t K, hipStream_t s);
+hipError_t launch_gemm_bf16(const uint16_t *Xb, const uint16_t *Wb, float *Y, int64_t M,
+                            int64_t N, int64_t K, hipStream_t s);
+
+constexpr int GEMV_MAX_M = 4;
+
+}  // namespace iq4xs

@@ -1,0 +1,165 @@
+// quantize.hip -- fp32 activations -> Q8_1 ("V100TPS engine log",
+// agent-report.daedalus.work/V100TPS/engine.html, M=64 kernel-launch table:
+// quantize_q8_1 runs before every integer matmul).
+//
+// Per 32-element block: amax = max|x|; d = amax/127 (IEEE fp32 division);
+// q = round-half-away-from-zero(x/d) (IEEE fp32 division, q = 0 when d == 0),
+// clamped to [-127, 127]; stored d16 = fp16(d) (nearest even); stored
+// s16 = fp16(d16 * sum q) -- d16 * sum q is exact in fp32 (11 + 12 bits), so
+// it is rounded once.  The pages give only "Q8_1"; the rounding rule is the
+// reading stated in the ABI header.
+//
+// Layout: eight consecutive lanes own one block, four elements each, so
+// the block reductions are three butterfly steps inside an 8-lane group.
+#include "common.hpp"
+
+namespace iq4xs {
+namespace {
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
+{
+    // finite inputs only (the activations here are exact fp32 products)
+    const uint32_t u = __builtin_bit_cast(uint32_t, f);
+    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_q(int q0, int q1, int q2, int q3)
+{
+    return (uint32_t)(uint8_t)q0 | ((uint32_t)(uint8_t)q1 << 8) | ((uint32_t)(uint8_t)q2 << 16) |
+           ((uint32_t)(uint8_t)q3 << 24);
+}
+
+// Position (in bytes) of the 4-byte group holding elements 4t..4t+3 of a
+// sub-block inside the chunk-ordered plane layout: element e of 8-group
+// g = e/8 moves by +0, +8, -8, +0 for g = 0..3.
+__device__ __forceinline__ int plane_pos(int t)
+{
+    const int g = t >> 1;
+    const int delta = (g == 1) ? 8 : (g == 2) ? -8 : 0;
+    return 4 * t + delta;
+}
+
+__device__ __forceinline__ int quant1(float x, float d)
+{
+    if (d == 0.0f)
+        return 0;
+    int q = (int)roundf(x / d);   // correctly rounded fp32 division (no fast-math)
+    return q > 127 ? 127 : (q < -127 ? -127 : q);
+}
+
+// Grid: one thread per 4 activations over Mrows x K, Mrows = Mp when planes
+// are written (rows >= M are written as zero) and M otherwise.
+__global__ void __launch_bounds__(256)
+k_quantize(const float *__restrict__ X, uint8_t *__restrict__ Xq, int8_t *__restrict__ qp,
+           float *__restrict__ dp, uint16_t *__restrict__ Xbf, int64_t M, int64_t Mrows,
+           int64_t Mp, int64_t K)
+{
+    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t nblk_row = K / SB;
+    const int64_t blk = tid >> 3;                 // global Q8_1 block index
+    const int t = (int)(tid & 7);                 // lane within the block
+    if (blk >= Mrows * nblk_row)
+        return;                                   // whole 8-lane groups exit together
+    const int64_t m = blk / nblk_row, b = blk - m * nblk_row;
+
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (m < M)
+        v = *reinterpret_cast<const float4 *>(X + m * K + b * SB + 4 * t);
+
+    float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 8));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 8));
+    amax = fmaxf(amax, __shfl_xor(amax, 4, 8));
+    const float d = amax / 127.0f;                // correctly rounded fp32 division
+
+    const int q0 = quant1(v.x, d), q1 = quant1(v.y, d), q2 = quant1(v.z, d), q3 = quant1(v.w, d);
+    int sum = q0 + q1 + q2 + q3;
+    sum += __shfl_xor(sum, 1, 8);
+    sum += __shfl_xor(sum, 2, 8);
+    sum += __shfl_xor(sum, 4, 8);
+
+    const _Float16 d16 = (_Float16)d;             // v_cvt_f16_f32, round to nearest even
+    const float dst = (float)d16;
+    const uint32_t qword = pack_q(q0, q1, q2, q3);
+
+    if (Xq != nullptr && m < M) {
+        uint8_t *o = Xq + blk * XBLK;
+        const _Float16 s16 = (_Float16)(dst * (float)sum);   // exact product, one rounding
+        *reinterpret_cast<uint32_t *>(o + 4 + 4 * t) = qword;
+        if (t == 0)
+            *reinterpret_cast<uint32_t *>(o) = (uint32_t)__builtin_bit_cast(uint16_t, d16) |
+                                               ((uint32_t)__builtin_bit_cast(uint16_t, s16) << 16);
+    }
+    if (qp != nullptr) {
+        *reinterpret_cast<uint32_t *>(qp + m * K + b * SB + plane_pos(t)) = qword;
+        if (t == 0)
+            dp[b * Mp + m] = dst;
+    }
+    if (Xbf != nullptr && m < M) {
+        const uint32_t lo = f32_to_bf16_rne(dst * (float)q0) | ((uint32_t)f32_to_bf16_rne(dst * (float)q1) << 16);
+        const uint32_t hi = f32_to_bf16_rne(dst * (float)q2) | ((uint32_t)f32_to_bf16_rne(dst * (float)q3) << 16);
+        *reinterpret_cast<uint2 *>(Xbf + m * K + b * SB + 4 * t) = make_uint2(lo, hi);
+    }
+}
+
+// ABI Q8_1 blocks -> internal planes and/or bf16 X~.  Same grid shape as
+// k_quantize (Mrows = Mp when planes are written, else M).
+__global__ void __launch_bounds__(256)
+k_q8_1_convert(const uint8_t *__restrict__ Xq, int8_t *__restrict__ qp, float *__restrict__ dp,
+               uint16_t *__restrict__ Xbf, int64_t M, int64_t Mrows, int64_t Mp, int64_t K)
+{
+    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t nblk_row = K / SB;
+    const int64_t blk = tid >> 3;
+    const int t = (int)(tid & 7);
+    if (blk >= Mrows * nblk_row)
+        return;
+    const int64_t m = blk / nblk_row, b = blk - m * nblk_row;
+    uint32_t qword = 0, head = 0;
+    if (m < M) {
+        const uint8_t *src = Xq + blk * XBLK;
+        qword = *reinterpret_cast<const uint32_t *>(src + 4 + 4 * t);
+        head = *reinterpret_cast<const uint32_t *>(src);
+    }
+    const float dst = half_bits_to_float(head & 0xFFFFu);
+    if (qp != nullptr) {
+        *reinterpret_cast<uint32_t *>(qp + m * K + b * SB + plane_pos(t)) = qword;
+        if (t == 0)
+            dp[b * Mp + m] = dst;
+    }
+    if (Xbf != nullptr && m < M) {
+        const int q0 = (int8_t)(qword & 0xFF), q1 = (int8_t)((qword >> 8) & 0xFF);
+        const int q2 = (int8_t)((qword >> 16) & 0xFF), q3 = (int8_t)(qword >> 24);
+        const uint32_t lo = f32_to_bf16_rne(dst * (float)q0) | ((uint32_t)f32_to_bf16_rne(dst * (float)q1) << 16);
+        const uint32_t hi = f32_to_bf16_rne(dst * (float)q2) | ((uint32_t)f32_to_bf16_rne(dst * (float)q3) << 16);
+        *reinterpret_cast<uint2 *>(Xbf + m * K + b * SB + 4 * t) = make_uint2(lo, hi);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const float *X, void *Xq, const XPlanes *planes, uint16_t *Xbf,
+                           int64_t M, int64_t K, hipStream_t s)
+{
+    const int64_t Mrows = planes ? planes->Mp : M;
+    const int64_t threads = Mrows * (K / 4);
+    const int64_t grid = (threads + 255) / 256;
+    hipLaunchKernelGGL(k_quantize, dim3((unsigned)grid), dim3(256), 0, s, X, (uint8_t *)Xq,
+                       planes ? planes->qp : nullptr, planes ? planes->dp : nullptr, Xbf, M, Mrows,
+                       planes ? planes->Mp : M, K);
+    return hipGetLastError();
+}
+
+hipError_t launch_q8_1_convert(const void *Xq, const XPlanes *planes, uint16_t *Xbf, int64_t M,
+                              int64_t K, hipStream_t s)
+{
+    const int64_t Mrows = planes ? planes->Mp : M;
+    const int64_t threads = Mrows * (K / 4);
+    const int64_t grid = (threads + 255) / 256;
+    hipLaunchKernelGGL(k_q8_1_convert, dim3((unsigned)grid), dim3(256), 0, s, (const uint8_t *)Xq,
+                       planes ? planes->qp : nullptr, planes ? planes->dp : nullptr, Xbf, M, Mrows,
+                       planes ? planes->Mp : M, K);
+    return hipGetLastError();
+}
+
+}  // namespace iq4xs

@@ -1,0 +1,168 @@
+"""Host-side tests of the C ABI (no GPU needed).
+
+The library must load, export every function include/iq4xs.h declares, and
+validate its arguments on the host before any HIP call: argument errors come
+back as EINVAL / EALIGN even where no GPU exists, and well-formed calls on a
+machine without a gfx950 device come back as EDEVICE.
+"""
+import ctypes
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+import iq4_xs_q8_amd as iq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "iq4xs.h")
+L = iq.lib
+A = 1 << 20          # a 16-byte aligned fake address (never dereferenced)
+
+
+def _has_gpu():
+    import torch
+    return torch.cuda.is_available()
+
+
+def test_header_declarations_are_exported():
+    text = open(HEADER).read()
+    declared = set(re.findall(r"^\w[\w\s\*]*?\b(iq4xs_\w+)\s*\(", text, flags=re.M))
+    assert declared == set(iq.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", iq.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (iq4xs_\w+)$", out, flags=re.M))
+    assert declared <= exported, declared - exported
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    consts = dict((k, int(v)) for k, v in re.findall(r"#define (IQ4XS_\w+) \(?(-?\d+)\)?", text))
+    assert consts["IQ4XS_OK"] == iq.OK and consts["IQ4XS_EINVAL"] == iq.EINVAL
+    assert consts["IQ4XS_EALIGN"] == iq.EALIGN and consts["IQ4XS_EDEVICE"] == iq.EDEVICE
+    assert consts["IQ4XS_ETABLE"] == iq.ETABLE and consts["IQ4XS_ELAUNCH"] == iq.ELAUNCH
+    assert consts["IQ4XS_ENOMEM"] == iq.ENOMEM and consts["IQ4XS_EPATH"] == iq.EPATH
+    for name, v in iq.PATHS.items():
+        assert consts["IQ4XS_PATH_" + name] == v
+        assert iq.path_name(v) == name
+
+
+def test_sizes():
+    assert iq.weight_bytes(10240, 5120) == 10240 * 20 * 136
+    assert iq.q8_1_bytes(16, 5120) == 16 * 160 * 36
+    out = ctypes.c_size_t()
+    for N, K in ((0, 256), (1, 0), (1, 128), (1, 300), (-1, 256)):
+        assert L.iq4xs_weight_bytes(N, K, ctypes.byref(out)) == iq.EINVAL
+    for M, K in ((0, 32), (1, 16), (1, 33)):
+        assert L.iq4xs_q8_1_bytes(M, K, ctypes.byref(out)) == iq.EINVAL
+    assert L.iq4xs_weight_bytes(1, 256, None) == iq.EINVAL
+
+
+@pytest.mark.parametrize("M,N,K", [(0, 8, 256), (4, 0, 256), (4, 8, 0), (4, 8, 128), (4, 8, 300),
+                                   (1 << 40, 8, 256), (4, 1 << 40, 256)])
+def test_gemm_bad_sizes(M, N, K):
+    assert L.iq4xs_gemm(A, A * 2, A * 4, M, N, K, None) == iq.EINVAL
+    assert L.iq4xs_gemm_q8_1(A, A * 2, A * 4, M, N, K, 0, None) == iq.EINVAL
+
+
+def test_gemm_null_and_alignment():
+    assert L.iq4xs_gemm(None, A, A * 4, 4, 8, 256, None) == iq.EINVAL
+    assert L.iq4xs_gemm(A, None, A * 4, 4, 8, 256, None) == iq.EINVAL
+    assert L.iq4xs_gemm(A, A * 2, None, 4, 8, 256, None) == iq.EINVAL
+    assert L.iq4xs_gemm(A + 8, A * 2, A * 4, 4, 8, 256, None) == iq.EALIGN
+    assert L.iq4xs_gemm(A, A * 2 + 4, A * 4, 4, 8, 256, None) == iq.EALIGN
+    assert L.iq4xs_gemm(A, A * 2, A * 4 + 4, 4, 8, 256, None) == iq.EALIGN
+    assert L.iq4xs_gemm_q8_1(A, A * 2 + 2, A * 4, 4, 8, 256, 0, None) == iq.EALIGN
+    assert L.iq4xs_gemm_q8_1(A, A * 2 + 4, A * 4, 4, 8, 256, 0, None) != iq.EALIGN
+    assert L.iq4xs_quantize_q8_1(A + 4, A * 2, 4, 256, None) == iq.EALIGN
+    assert L.iq4xs_dequantize_bf16(A, A * 2 + 8, 8, 256, None) == iq.EALIGN
+
+
+def test_overlap_rejected():
+    # Y inside W, Y inside X
+    assert L.iq4xs_gemm(A, A * 4, A + 256, 4, 8, 256, None) == iq.EINVAL
+    assert L.iq4xs_gemm(A * 4, A, A + 256, 4, 8, 256, None) == iq.EINVAL
+    assert L.iq4xs_gemm_q8_1(A * 4, A, A + 64, 4, 8, 256, 0, None) == iq.EINVAL
+    assert L.iq4xs_quantize_q8_1(A, A + 16, 4, 256, None) == iq.EINVAL
+
+
+def test_unknown_path_and_gemv_limit():
+    assert L.iq4xs_gemm_path(A, A * 2, A * 4, 4, 8, 256, 9, None) == iq.EINVAL
+    assert L.iq4xs_gemm_path(A, A * 2, A * 4, 4, 8, 256, -1, None) == iq.EINVAL
+    assert L.iq4xs_gemm_path(A, A * 2, A * 4, 5, 8, 256, iq.PATH_GEMV, None) == iq.EPATH
+
+
+@pytest.mark.skipif(_has_gpu(), reason="checks the no-device error")
+def test_no_device_reports_edevice():
+    assert L.iq4xs_gemm(A, A * 2, A * 4, 4, 8, 256, None) == iq.EDEVICE
+    assert "device" in L.iq4xs_last_error().decode()
+    assert L.iq4xs_quantize_q8_1(A, A * 2, 4, 256, None) == iq.EDEVICE
+    assert L.iq4xs_dequantize_bf16(A, A * 2, 8, 256, None) == iq.EDEVICE
+
+
+def test_default_dispatch_table():
+    iq.load_dispatch_table(None)
+    seen = set()
+    for M in list(range(1, 130)) + [192, 256, 384, 512, 1000]:
+        for (N, K) in ((10240, 5120), (5120, 17408), (2048, 2048), (248320, 5120)):
+            p = iq.dispatch(M, N, K)
+            seen.add(p)
+            assert p in (iq.PATH_GEMV, iq.PATH_MMQ), (M, N, K, p)
+            if p == iq.PATH_GEMV:
+                assert M <= 4
+    assert iq.PATH_MMQ in seen
+
+
+def test_table_loading(tmp_path):
+    good = tmp_path / "t.txt"
+    good.write_text("arch gfx950\nband GEMV 4 4 1024 *\nband MMQ 1 7 * *\nband MMQ 8 100000 * *\n")
+    bad_gemv = tmp_path / "g.txt"
+    bad_gemv.write_text("arch gfx950\nband GEMV 1 9 * *\n")
+    garbled = tmp_path / "b.txt"
+    garbled.write_text("arch gfx950\nband MMQ one 7 * *\n")
+    noarch = tmp_path / "n.txt"
+    noarch.write_text("band MMQ 1 7 * *\n")
+    try:
+        iq.load_dispatch_table(str(good))
+        assert iq.dispatch(3, 4096, 256) == iq.PATH_MMQ
+        assert iq.dispatch(4, 1024, 256) == iq.PATH_GEMV
+        assert iq.dispatch(4, 2048, 256) == iq.PATH_MMQ
+        for f in (bad_gemv, garbled, noarch, tmp_path / "missing.txt"):
+            assert L.iq4xs_load_dispatch_table(str(f).encode()) == iq.ETABLE
+            # previous table still in force
+            assert iq.dispatch(3, 4096, 256) == iq.PATH_MMQ
+        # M outside every band
+        short = tmp_path / "s.txt"
+        short.write_text("arch gfx950\nband MMQ 1 7 * *\n")
+        iq.load_dispatch_table(str(short))
+        p = ctypes.c_int()
+        assert L.iq4xs_dispatch(8, 4096, 256, ctypes.byref(p)) == iq.EPATH
+    finally:
+        iq.load_dispatch_table(None)
+
+
+def test_bf16_bands_need_opt_in(tmp_path):
+    t = tmp_path / "t.txt"
+    t.write_text("arch gfx950\nband DEQ_BF16 64 100000 * *\nband MMQ 1 100000 * *\n")
+    code = ("import iq4_xs_q8_amd as iq, sys; iq.load_dispatch_table(sys.argv[1]); "
+            "print(iq.dispatch(128, 4096, 4096))")
+    env = dict(os.environ, PYTHONPATH=ROOT)
+    env.pop("IQ4XS_ALLOW_BF16", None)
+    off = subprocess.run([sys.executable, "-c", code, str(t)], env=env, capture_output=True,
+                         text=True, check=True).stdout.strip()
+    env["IQ4XS_ALLOW_BF16"] = "1"
+    on = subprocess.run([sys.executable, "-c", code, str(t)], env=env, capture_output=True,
+                        text=True, check=True).stdout.strip()
+    assert int(off) == iq.PATH_MMQ and int(on) == iq.PATH_DEQ_BF16
+
+
+def test_env_table_read_once_and_fail_closed(tmp_path):
+    bad = tmp_path / "bad.txt"
+    bad.write_text("garbage\n")
+    code = ("import ctypes, iq4_xs_q8_amd as iq; p = ctypes.c_int(); "
+            "print(iq.lib.iq4xs_init(), iq.lib.iq4xs_dispatch(8, 4096, 4096, ctypes.byref(p)))")
+    env = dict(os.environ, PYTHONPATH=ROOT, IQ4XS_DISPATCH_TABLE=str(bad))
+    out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                         check=True).stdout.split()
+    assert [int(v) for v in out] == [iq.ETABLE, iq.ETABLE]

@@ -1,0 +1,237 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars: Q8_1 bytes bit-exact; dequantized bf16 weights bit-exact; every GEMM
+path within max|y - y_ref| / max|y_ref| <= 1e-4 per output row against the
+oracle of its own formulation (integer dot for GEMV and MMQ, bf16 products
+for DEQ_BF16); a reference row that is exactly zero must come back exactly
+zero.  Every output buffer is poisoned first and checked to be fully written.
+"""
+import numpy as np
+import pytest
+import torch
+
+import iq4_xs_q8_amd as iq
+import oracle
+import oracle_pins
+import synth
+from gpu_util import ROW_TOL, assert_rows_close, dev, poisoned
+
+pytestmark = pytest.mark.gpu
+
+O = None
+
+
+def setup_module(_):
+    global O
+    O = oracle.get()
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+
+
+def _inputs(M, N, K, seed=0, sigma=1.0, outliers=0.0):
+    W = synth.weights((900, N, K, seed), N, K)
+    X = synth.activations((901, M, K, seed), M, K, sigma=sigma, outlier_frac=outliers)
+    return W, X
+
+
+# ------------------------------------------------------------------ Q8_1
+@pytest.mark.parametrize("M,K,sigma,outl", [(1, 256, 1.0, 0.0), (4, 2048, 1.0, 0.0),
+                                             (16, 5120, 1.0, 0.01), (7, 17408, 0.5, 0.0),
+                                             (3, 96, 1.0, 0.0)])
+def test_quantize_bit_exact(M, K, sigma, outl):
+    X = synth.activations((902, M, K), M, K, sigma=sigma, outlier_frac=outl)
+    want = O.quantize_q8_1(X)
+    got = iq.quantize_q8_1(dev(X), out=poisoned(want.shape, torch.uint8)).cpu().numpy()
+    assert np.array_equal(got, want), np.argwhere(got != want)[:5]
+
+
+def test_quantize_edge_cases_bit_exact():
+    hand, hand_bytes = oracle_pins.read_handworked_q8_1()
+    rng = np.random.default_rng(31)
+    rows = [hand.reshape(-1)]
+    d = np.float32(0.7) / np.float32(127)
+    ties = ((rng.integers(-126, 126, 160) + 0.5) * d).astype(np.float32)
+    ties[::32] = np.float32(0.7)
+    rows += [ties, np.nextafter(ties, np.float32(np.inf)), np.nextafter(ties, np.float32(-np.inf))]
+    rows.append(rng.standard_normal(160).astype(np.float32) * np.float32(1e-4))   # subnormal d
+    rows.append(np.zeros(160, np.float32))
+    X = np.stack(rows)
+    want = O.quantize_q8_1(X)
+    assert np.array_equal(want[0].reshape(-1, 36), hand_bytes)
+    got = iq.quantize_q8_1(dev(X), out=poisoned(want.shape, torch.uint8)).cpu().numpy()
+    assert np.array_equal(got, want), np.argwhere(got != want)[:5]
+
+
+# ------------------------------------------------------------------ dequant
+@pytest.mark.parametrize("N,K", [(1, 256), (37, 1280), (300, 2048)])
+def test_dequant_bf16_bit_exact(N, K):
+    W = synth.weights((903, N, K), N, K)
+    want = O.dequantize_bf16(W, K)
+    got = iq.dequantize_bf16(dev(W), K, out=poisoned((N, K), torch.bfloat16))
+    got = got.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, want)
+
+
+# ------------------------------------------------------------------ GEMM paths
+SMALL_SHAPES = [
+    # (M, N, K): several 32x32 tiles plus ragged tails in M and N
+    (1, 1, 256), (1, 257, 1024), (2, 100, 512), (3, 300, 1280), (4, 2048, 2048),
+    (5, 33, 256), (8, 129, 768), (12, 300, 1280), (16, 300, 2048), (17, 64, 512),
+    (32, 96, 1024), (33, 130, 1280), (64, 97, 768), (70, 300, 1280), (96, 200, 2048),
+    (128, 160, 512), (200, 75, 256), (300, 129, 512),
+]
+
+
+def _paths_for(M):
+    ps = [iq.PATH_MMQ, iq.PATH_DEQ_BF16, iq.PATH_AUTO]
+    if M <= 4:
+        ps.insert(0, iq.PATH_GEMV)
+    return ps
+
+
+@pytest.mark.parametrize("M,N,K", SMALL_SHAPES)
+def test_gemm_paths_match_oracle(M, N, K):
+    W, X = _inputs(M, N, K)
+    Xq = O.quantize_q8_1(X)
+    ref_int = O.gemm_q8_1(W, Xq, K)
+    ref_bf16 = O.gemm_bf16(W, Xq, K)
+    Wd, Xd = dev(W), dev(X)
+    for p in _paths_for(M):
+        y = iq.gemm(Wd, Xd, path=p, out=poisoned((M, N))).cpu().numpy()
+        ref = ref_bf16 if p == iq.PATH_DEQ_BF16 else ref_int
+        assert_rows_close(y, ref, what=f"{iq.path_name(p)} M={M} N={N} K={K}")
+        # the same through the pre-quantized entry point (oracle's Q8_1 bytes)
+        y2 = iq.gemm_q8_1(Wd, dev(Xq), K, path=p, out=poisoned((M, N))).cpu().numpy()
+        assert np.array_equal(y, y2), f"{iq.path_name(p)}: gemm and gemm_q8_1 differ"
+        if p != iq.PATH_DEQ_BF16:
+            # and through prepared activations (one quantization, one matmul launch)
+            act = iq.prepare_act(Xd)
+            y3 = iq.gemm_act(Wd, act, M, K, path=p, out=poisoned((M, N))).cpu().numpy()
+            assert np.array_equal(y, y3), f"{iq.path_name(p)}: gemm and gemm_act differ"
+
+
+@pytest.mark.parametrize("path", [iq.PATH_GEMV, iq.PATH_MMQ])
+def test_zero_scales_give_exact_zero(path):
+    # all ls = 32: every weight is zero, so every output must be exactly 0
+    rng = np.random.default_rng(41)
+    N, K, M = 70, 512, 3
+    d_bits, ls, codes = oracle_pins.random_fields(rng, N * K // 256)
+    W, _ = oracle_pins.build_matrix(d_bits, np.full_like(ls, 32), codes, N, K)
+    X = rng.standard_normal((M, K)).astype(np.float32)
+    y = iq.gemm(dev(W), dev(X), path=path, out=poisoned((M, N))).cpu().numpy()
+    assert np.all(y == 0)
+
+
+@pytest.mark.parametrize("path", [iq.PATH_GEMV, iq.PATH_MMQ])
+def test_zero_activation_row(path):
+    W, X = _inputs(4, 200, 1024, seed=3)
+    X[2] = 0
+    y = iq.gemm(dev(W), dev(X), path=path, out=poisoned((4, 200))).cpu().numpy()
+    assert np.all(y[2] == 0)
+    assert_rows_close(y, O.gemm(W, X))
+
+
+@pytest.mark.parametrize("path", [iq.PATH_GEMV, iq.PATH_MMQ])
+def test_single_nonzero_activation(path):
+    # closed form: y[n] = W~[n, k*] * d16 * 127 for x = v at k* only
+    N, K = 64, 512
+    W = synth.weights((904, N, K), N, K)
+    V = O.dequantize(W, K)
+    for kstar in (0, 15, 16, 31, 200, 511):
+        X = np.zeros((1, K), np.float32)
+        X[0, kstar] = 1.75
+        y = iq.gemm(dev(W), dev(X), path=path, out=poisoned((1, N))).cpu().numpy()[0]
+        d16 = float(np.float16(np.float32(1.75) / np.float32(127)))
+        # the kernel rounds (d_w*(ls-32)*d16) and its product with D in fp32
+        assert_rows_close(y[None, :], (V[:, kstar] * d16 * 127)[None, :], tol=1e-6)
+
+
+@pytest.mark.parametrize("path", [iq.PATH_GEMV, iq.PATH_MMQ, iq.PATH_DEQ_BF16])
+def test_deterministic_and_invariant(path):
+    M = 3 if path == iq.PATH_GEMV else 20
+    W, X = _inputs(M, 300, 1536, seed=5)
+    Wd, Xd = dev(W), dev(X)
+    y1 = iq.gemm(Wd, Xd, path=path).cpu()
+    y2 = iq.gemm(Wd, Xd, path=path).cpu()
+    assert torch.equal(y1, y2), "two runs differ"
+    assert torch.equal(iq.gemm(Wd, -Xd, path=path).cpu(), -y1)
+    assert torch.equal(iq.gemm(Wd, 2 * Xd, path=path).cpu(), 2 * y1)
+    # row m does not depend on the other rows (same path, same tile shape)
+    y_row = iq.gemm(Wd, Xd[1:2].contiguous(), path=path).cpu()
+    if path != iq.PATH_DEQ_BF16:
+        assert torch.equal(y_row[0], y1[1])
+
+
+def test_negative_control_corrupted_weight_fails():
+    # a one-byte change in W must push the affected row outside the bound
+    M, N, K = 4, 64, 1024
+    W, X = _inputs(M, N, K, seed=7)
+    ref = O.gemm(W, X)
+    Wbad = W.copy()
+    Wbad[10, 1] ^= 0x04                              # row 10, block 0: d scaled by 2 or 1/2
+    y = iq.gemm(dev(Wbad), dev(X), path=iq.PATH_MMQ).cpu().numpy()
+    with pytest.raises(AssertionError):
+        assert_rows_close(y[:, 10:11], ref[:, 10:11])
+    # and the poison check itself fires on an untouched buffer
+    with pytest.raises(AssertionError):
+        assert_rows_close(poisoned((M, N)).cpu().numpy(), ref)
+
+
+def test_large_m_grid():
+    # many 32-row tiles along M and a single column
+    W, X = _inputs(1000, 1, 512, seed=9)
+    y = iq.gemm(dev(W), dev(X), path=iq.PATH_MMQ, out=poisoned((1000, 1))).cpu().numpy()
+    assert_rows_close(y.T, O.gemm(W, X).T)
+
+
+# ------------------------------------------------------------------ full sizes
+def _sample_cols(N, n=192, seed=0):
+    rng = np.random.default_rng(seed)
+    cols = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, n)]))
+    return cols
+
+
+FULL = []
+for wl in synth.WORKLOADS:
+    for (N, K) in wl.shapes:
+        for M in wl.ms:
+            FULL.append((wl.cid, N, K, M))
+
+
+@pytest.mark.parametrize("cid,N,K,M", FULL, ids=[f"C{c}-{n}x{k}-M{m}" for c, n, k, m in FULL])
+def test_full_size_sampled(cid, N, K, M):
+    """The workloads at their real sizes, in the launch configuration the
+    benchmark times (AUTO path), checked on sampled output columns.  The
+    prefill points also run the bf16 path against its own oracle."""
+    wl = {w.cid: w for w in synth.WORKLOADS}[cid]
+    W = _weights_cached(wl, N, K)
+    X = wl.x(M, K, N=N)
+    Wd = _wdev_cached(wl, N, K, W)
+    cols = _sample_cols(N, seed=M)
+    Xq = O.quantize_q8_1(X)
+    ref = O.gemm_q8_1(W[cols], Xq, K)
+    y = iq.gemm(Wd, dev(X), out=poisoned((M, N))).cpu().numpy()
+    assert np.all(np.isfinite(y)), "outputs not written"
+    assert_rows_close(y[:, cols], ref, what=f"AUTO C{cid} M={M} N={N} K={K}")
+    if cid == 5 and M in (64, 512):
+        yb = iq.gemm(Wd, dev(X), path=iq.PATH_DEQ_BF16, out=poisoned((M, N))).cpu().numpy()
+        assert np.all(np.isfinite(yb))
+        assert_rows_close(yb[:, cols], O.gemm_bf16(W[cols], Xq, K), what="DEQ_BF16")
+
+
+_cache = {}
+
+
+def _weights_cached(wl, N, K):
+    key = ("w", wl.cid, N, K)
+    if key not in _cache:
+        _cache.clear()
+        torch.cuda.empty_cache()
+        _cache[key] = wl.w(N, K)
+    return _cache[key]
+
+
+def _wdev_cached(wl, N, K, W):
+    key = ("d", wl.cid, N, K)
+    if key not in _cache:
+        _cache[key] = dev(W)
+    return _cache[key]
