@@ -101,6 +101,16 @@ int iq4xs_gemm(const void *W, const float *X, float *Y, int64_t M, int64_t N, in
 int iq4xs_gemm_path(const void *W, const float *X, float *Y, int64_t M, int64_t N, int64_t K,
                     int path, void *stream);
 
+/* Caller-provided scratch: iq4xs_gemm_ws is iq4xs_gemm_path with the
+ * scratch supplied by the caller (`workspace`, at least
+ * iq4xs_gemm_workspace_bytes(M, N, K, path) bytes, 256-byte aligned, not
+ * overlapping W or Y).  It allocates nothing, so it can be recorded into a
+ * HIP graph; calls that share one workspace must be ordered on one stream.
+ * The size query resolves AUTO with the dispatch table in force. */
+int iq4xs_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int path, size_t *out);
+int iq4xs_gemm_ws(const void *W, const float *X, float *Y, int64_t M, int64_t N, int64_t K, int path,
+                  void *workspace, size_t workspace_bytes, void *stream);
+
 /* Y = dequant(Xq) * W^T from an already-quantized Q8_1 Xq (layout above). */
 int iq4xs_gemm_q8_1(const void *W, const void *Xq, float *Y, int64_t M, int64_t N, int64_t K,
                     int path, void *stream);
@@ -115,7 +125,9 @@ int iq4xs_gemm_q8_1(const void *W, const void *Xq, float *Y, int64_t M, int64_t 
 int iq4xs_act_bytes(int64_t M, int64_t K, size_t *out);
 int iq4xs_prepare_act(const float *X, void *act, int64_t M, int64_t K, void *stream);
 /* Y = X * W^T from prepared activations; path AUTO, GEMV or MMQ (DEQ_BF16 is
- * EPATH here).  Launches exactly one kernel. */
+ * EPATH here).  Launches the matmul kernel only -- plus, for shapes whose K is
+ * split over several workgroups (small N, long K), a fixed-order reduction
+ * kernel over a stream-ordered partial-sum workspace. */
 int iq4xs_gemm_act(const void *W, const void *act, float *Y, int64_t M, int64_t N, int64_t K,
                    int path, void *stream);
 

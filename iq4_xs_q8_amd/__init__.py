@@ -15,6 +15,7 @@ Y fp32 [M, N].
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -28,7 +29,8 @@ PATH_AUTO, PATH_GEMV, PATH_MMQ, PATH_DEQ_BF16 = 0, 1, 2, 3
 PATHS = {"AUTO": PATH_AUTO, "GEMV": PATH_GEMV, "MMQ": PATH_MMQ, "DEQ_BF16": PATH_DEQ_BF16}
 
 EXPORTS = ("iq4xs_weight_bytes", "iq4xs_q8_1_bytes", "iq4xs_init", "iq4xs_quantize_q8_1",
-           "iq4xs_gemm", "iq4xs_gemm_path", "iq4xs_gemm_q8_1", "iq4xs_act_bytes",
+           "iq4xs_gemm", "iq4xs_gemm_path", "iq4xs_gemm_workspace_bytes", "iq4xs_gemm_ws",
+           "iq4xs_gemm_q8_1", "iq4xs_act_bytes",
            "iq4xs_prepare_act", "iq4xs_gemm_act", "iq4xs_dequantize_bf16",
            "iq4xs_dispatch", "iq4xs_load_dispatch_table", "iq4xs_path_name", "iq4xs_last_error")
 
@@ -52,6 +54,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "iq4xs_quantize_q8_1": [p, p, i64, i64, p],
         "iq4xs_gemm": [p, p, p, i64, i64, i64, p],
         "iq4xs_gemm_path": [p, p, p, i64, i64, i64, i32, p],
+        "iq4xs_gemm_workspace_bytes": [i64, i64, i64, i32, sz],
+        "iq4xs_gemm_ws": [p, p, p, i64, i64, i64, i32, p, ctypes.c_size_t, p],
         "iq4xs_gemm_q8_1": [p, p, p, i64, i64, i64, i32, p],
         "iq4xs_act_bytes": [i64, i64, sz],
         "iq4xs_prepare_act": [p, p, i64, i64, p],
@@ -97,6 +101,13 @@ def _stream(t: torch.Tensor) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
+def _on(t: torch.Tensor):
+    """Make t's device current for the call (a no-op when it already is)."""
+    if t.is_cuda and t.device.index == torch.cuda.current_device():
+        return contextlib.nullcontext()
+    return torch.cuda.device(t.device)
+
+
 def _dev(t: torch.Tensor, dtype: torch.dtype, name: str) -> int:
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise TypeError(f"{name} must be a CUDA (HIP) tensor")
@@ -124,22 +135,37 @@ def quantize_q8_1(X: torch.Tensor, out: torch.Tensor | None = None) -> torch.Ten
     M, K = X.shape
     if out is None:
         out = torch.empty((M, (K // 32) * 36), dtype=torch.uint8, device=X.device)
-    with torch.cuda.device(X.device):
+    with _on(X):
         check(_L().iq4xs_quantize_q8_1(_dev(X, torch.float32, "X"), _dev(out, torch.uint8, "Xq"),
                                       M, K, _stream(X)))
     return out
 
 
+def workspace_bytes(M: int, N: int, K: int, path: int = PATH_AUTO) -> int:
+    out = ctypes.c_size_t()
+    check(_L().iq4xs_gemm_workspace_bytes(M, N, K, path, ctypes.byref(out)))
+    return out.value
+
+
 def gemm(W: torch.Tensor, X: torch.Tensor, path: int = PATH_AUTO,
-         out: torch.Tensor | None = None) -> torch.Tensor:
-    """Y[M, N] = X[M, K] * W[N, K]^T with X quantized to Q8_1 on the device."""
+         out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Y[M, N] = X[M, K] * W[N, K]^T with X quantized to Q8_1 on the device.
+
+    With `workspace` (uint8, workspace_bytes(M, N, K, path) bytes) nothing is
+    allocated inside the call, so it can be captured in a graph."""
     M, K = X.shape
     N = W.shape[0]
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=X.device)
-    with torch.cuda.device(X.device):
-        check(_L().iq4xs_gemm_path(_dev(W, torch.uint8, "W"), _dev(X, torch.float32, "X"),
-                                  _dev(out, torch.float32, "Y"), M, N, K, path, _stream(X)))
+    with _on(X):
+        if workspace is None:
+            check(_L().iq4xs_gemm_path(_dev(W, torch.uint8, "W"), _dev(X, torch.float32, "X"),
+                                      _dev(out, torch.float32, "Y"), M, N, K, path, _stream(X)))
+        else:
+            check(_L().iq4xs_gemm_ws(_dev(W, torch.uint8, "W"), _dev(X, torch.float32, "X"),
+                                    _dev(out, torch.float32, "Y"), M, N, K, path,
+                                    _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                    _stream(X)))
     return out
 
 
@@ -150,7 +176,7 @@ def gemm_q8_1(W: torch.Tensor, Xq: torch.Tensor, K: int, path: int = PATH_AUTO,
     N = W.shape[0]
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=Xq.device)
-    with torch.cuda.device(Xq.device):
+    with _on(Xq):
         check(_L().iq4xs_gemm_q8_1(_dev(W, torch.uint8, "W"), _dev(Xq, torch.uint8, "Xq"),
                                   _dev(out, torch.float32, "Y"), M, N, K, path, _stream(Xq)))
     return out
@@ -167,7 +193,7 @@ def prepare_act(X: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tenso
     M, K = X.shape
     if out is None:
         out = torch.empty(act_bytes(M, K), dtype=torch.uint8, device=X.device)
-    with torch.cuda.device(X.device):
+    with _on(X):
         check(_L().iq4xs_prepare_act(_dev(X, torch.float32, "X"), _dev(out, torch.uint8, "act"),
                                     M, K, _stream(X)))
     return out
@@ -179,7 +205,7 @@ def gemm_act(W: torch.Tensor, act: torch.Tensor, M: int, K: int, path: int = PAT
     N = W.shape[0]
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=act.device)
-    with torch.cuda.device(act.device):
+    with _on(act):
         check(_L().iq4xs_gemm_act(_dev(W, torch.uint8, "W"), _dev(act, torch.uint8, "act"),
                                  _dev(out, torch.float32, "Y"), M, N, K, path, _stream(act)))
     return out
@@ -190,7 +216,7 @@ def dequantize_bf16(W: torch.Tensor, K: int, out: torch.Tensor | None = None) ->
     N = W.shape[0]
     if out is None:
         out = torch.empty((N, K), dtype=torch.bfloat16, device=W.device)
-    with torch.cuda.device(W.device):
+    with _on(W):
         check(_L().iq4xs_dequantize_bf16(_dev(W, torch.uint8, "W"), _dev(out, torch.bfloat16, "Wb"),
                                         N, K, _stream(W)))
     return out

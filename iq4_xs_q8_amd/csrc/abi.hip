@@ -23,6 +23,18 @@
 
 using namespace iq4xs;
 
+const TuneOverride &iq4xs::tune_override()
+{
+    static const TuneOverride t = [] {
+        TuneOverride o;
+        const char *v = getenv("IQ4XS_DEC_PLAN");
+        if (v)
+            sscanf(v, "%d,%d", &o.dec_nw, &o.dec_ks);
+        return o;
+    }();
+    return t;
+}
+
 namespace {
 
 thread_local std::string g_err;
@@ -206,44 +218,64 @@ int resolve_path(int path, int64_t M, int64_t N, int64_t K, int *out)
     return IQ4XS_OK;
 }
 
-// Common tail of iq4xs_gemm_path / iq4xs_gemm_q8_1.  Exactly one of X (fp32)
-// and Xq (Q8_1 blocks) is non-null.
+// Scratch a path needs: activation planes (+ the split-K partial sums of
+// MMQ), or for DEQ_BF16 the bf16 activations and weights.
+size_t workspace_need(int path, int64_t M, int64_t N, int64_t K)
+{
+    if (path == IQ4XS_PATH_GEMV || path == IQ4XS_PATH_MMQ)
+        return (size_t)round_up((int64_t)xplanes_bytes(M, K), 256) +
+               (path == IQ4XS_PATH_MMQ ? mmq_plan(M, N, K).workspace_bytes : 0);
+    return (size_t)round_up(M * K * 2, 256) + (size_t)(N * K * 2);
+}
+
+// Common tail of the gemm entry points.  Exactly one of X (fp32) and Xq (Q8_1
+// blocks) is non-null.  With ws == nullptr the scratch comes from the
+// device's default pool, stream-ordered; otherwise ws (ws_bytes, 256-byte
+// aligned) is used and nothing is allocated.
 int run_gemm(const void *W, const float *X, const void *Xq, float *Y, int64_t M, int64_t N, int64_t K,
-             int path, hipStream_t s)
+             int path, void *ws, size_t ws_bytes, hipStream_t s)
 {
     int st = resolve_path(path, M, N, K, &path);
     if (st != IQ4XS_OK)
         return st;
+    const size_t need = workspace_need(path, M, N, K);
+    if (ws != nullptr) {
+        if (!aligned(ws, 256))
+            return fail(IQ4XS_EALIGN, "workspace must be 256-byte aligned");
+        if (ws_bytes < need)
+            return fail(IQ4XS_EINVAL, "workspace of %zu bytes, %zu needed", ws_bytes, need);
+        if (overlaps(ws, ws_bytes, Y, (size_t)(M * N * 4)) ||
+            overlaps(ws, ws_bytes, W, (size_t)(N * (K / QK) * WBLK)))
+            return fail(IQ4XS_EINVAL, "workspace overlaps W or Y");
+    }
     if ((st = check_device()) != IQ4XS_OK)
         return st;
 
     Scratch scr;
     scr.s = s;
-    if (path == IQ4XS_PATH_GEMV || path == IQ4XS_PATH_MMQ) {
-        const size_t bytes = xplanes_bytes(M, K);
-        if (hipMallocAsync(&scr.p, bytes, s) != hipSuccess) {
+    char *base = (char *)ws;
+    if (base == nullptr) {
+        if (hipMallocAsync(&scr.p, need, s) != hipSuccess) {
             (void)hipGetLastError();
             scr.p = nullptr;
-            return fail(IQ4XS_ENOMEM, "scratch of %zu bytes", bytes);
+            return fail(IQ4XS_ENOMEM, "scratch of %zu bytes", need);
         }
-        const XPlanes xp = xplanes_at(scr.p, M, K);
+        base = (char *)scr.p;
+    }
+    if (path == IQ4XS_PATH_GEMV || path == IQ4XS_PATH_MMQ) {
+        const size_t pbytes = (size_t)round_up((int64_t)xplanes_bytes(M, K), 256);
+        const XPlanes xp = xplanes_at(base, M, K);
         hipError_t e = X ? launch_quantize(X, nullptr, &xp, nullptr, M, K, s)
                          : launch_q8_1_convert(Xq, &xp, nullptr, M, K, s);
         if ((st = launch_err(e, "quantize")) != IQ4XS_OK)
             return st;
-        e = path == IQ4XS_PATH_GEMV ? launch_gemv(W, xp, Y, N, s) : launch_mmq(W, xp, Y, N, s);
+        e = path == IQ4XS_PATH_GEMV ? launch_gemv(W, xp, Y, N, s) : launch_mmq(W, xp, Y, N, base + pbytes, s);
         return launch_err(e, path_name(path));
     }
     // DEQ_BF16: X~ bf16 [M][K], then W~ bf16 [N][K] (256-byte aligned)
     const size_t xbytes = (size_t)round_up(M * K * 2, 256);
-    const size_t bytes = xbytes + (size_t)(N * K * 2);
-    if (hipMallocAsync(&scr.p, bytes, s) != hipSuccess) {
-        (void)hipGetLastError();
-        scr.p = nullptr;
-        return fail(IQ4XS_ENOMEM, "scratch of %zu bytes", bytes);
-    }
-    uint16_t *xb = (uint16_t *)scr.p;
-    uint16_t *wb = (uint16_t *)((char *)scr.p + xbytes);
+    uint16_t *xb = (uint16_t *)base;
+    uint16_t *wb = (uint16_t *)(base + xbytes);
     const hipError_t e = X ? launch_quantize(X, nullptr, nullptr, xb, M, K, s)
                            : launch_q8_1_convert(Xq, nullptr, xb, M, K, s);
     if ((st = launch_err(e, "quantize")) != IQ4XS_OK)
@@ -309,7 +341,36 @@ int iq4xs_gemm_path(const void *W, const float *X, float *Y, int64_t M, int64_t 
     const size_t yb = (size_t)(M * N * 4);
     if (overlaps(Y, yb, W, (size_t)(N * (K / QK) * WBLK)) || overlaps(Y, yb, X, (size_t)(M * K * 4)))
         return fail(IQ4XS_EINVAL, "Y overlaps an input");
-    return run_gemm(W, X, nullptr, Y, M, N, K, path, (hipStream_t)stream);
+    return run_gemm(W, X, nullptr, Y, M, N, K, path, nullptr, 0, (hipStream_t)stream);
+}
+
+int iq4xs_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int path, size_t *out)
+{
+    if (!out)
+        return fail(IQ4XS_EINVAL, "null output pointer");
+    int st = check_dims(M, N, K);
+    if (st != IQ4XS_OK)
+        return st;
+    if ((st = resolve_path(path, M, N, K, &path)) != IQ4XS_OK)
+        return st;
+    *out = workspace_need(path, M, N, K);
+    return IQ4XS_OK;
+}
+
+int iq4xs_gemm_ws(const void *W, const float *X, float *Y, int64_t M, int64_t N, int64_t K, int path,
+                  void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!W || !X || !Y || !workspace)
+        return fail(IQ4XS_EINVAL, "null pointer");
+    int st = check_dims(M, N, K);
+    if (st != IQ4XS_OK)
+        return st;
+    if (!aligned(W, 16) || !aligned(X, 16) || !aligned(Y, 16))
+        return fail(IQ4XS_EALIGN, "W, X and Y must be 16-byte aligned");
+    const size_t yb = (size_t)(M * N * 4);
+    if (overlaps(Y, yb, W, (size_t)(N * (K / QK) * WBLK)) || overlaps(Y, yb, X, (size_t)(M * K * 4)))
+        return fail(IQ4XS_EINVAL, "Y overlaps an input");
+    return run_gemm(W, X, nullptr, Y, M, N, K, path, workspace, workspace_bytes, (hipStream_t)stream);
 }
 
 int iq4xs_gemm(const void *W, const float *X, float *Y, int64_t M, int64_t N, int64_t K, void *stream)
@@ -331,7 +392,7 @@ int iq4xs_gemm_q8_1(const void *W, const void *Xq, float *Y, int64_t M, int64_t 
     if (overlaps(Y, yb, W, (size_t)(N * (K / QK) * WBLK)) ||
         overlaps(Y, yb, Xq, (size_t)(M * (K / SB) * XBLK)))
         return fail(IQ4XS_EINVAL, "Y overlaps an input");
-    return run_gemm(W, nullptr, Xq, Y, M, N, K, path, (hipStream_t)stream);
+    return run_gemm(W, nullptr, Xq, Y, M, N, K, path, nullptr, 0, (hipStream_t)stream);
 }
 
 int iq4xs_dequantize_bf16(const void *W, void *Wb, int64_t N, int64_t K, void *stream)
@@ -401,8 +462,17 @@ int iq4xs_gemm_act(const void *W, const void *act, float *Y, int64_t M, int64_t 
         return st;
     const XPlanes xp = xplanes_at((void *)act, M, K);
     const hipStream_t s = (hipStream_t)stream;
-    return launch_err(path == IQ4XS_PATH_GEMV ? launch_gemv(W, xp, Y, N, s) : launch_mmq(W, xp, Y, N, s),
-                      path_name(path));
+    if (path == IQ4XS_PATH_GEMV)
+        return launch_err(launch_gemv(W, xp, Y, N, s), path_name(path));
+    Scratch scr;   // partial-sum workspace when the shape splits K over workgroups
+    scr.s = s;
+    const size_t wbytes = mmq_plan(M, N, K).workspace_bytes;
+    if (wbytes && hipMallocAsync(&scr.p, wbytes, s) != hipSuccess) {
+        (void)hipGetLastError();
+        scr.p = nullptr;
+        return fail(IQ4XS_ENOMEM, "workspace of %zu bytes", wbytes);
+    }
+    return launch_err(launch_mmq(W, xp, Y, N, scr.p, s), path_name(path));
 }
 
 int iq4xs_dispatch(int64_t M, int64_t N, int64_t K, int *path_out)

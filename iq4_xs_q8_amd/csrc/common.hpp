@@ -25,8 +25,8 @@ static_assert(2 + 2 + 4 + QK / 2 == WBLK, "IQ4_XS super-block size");
 static_assert(QS_OFF == 2 + 2 + 4, "qs follows d, scales_h, scales_l");
 static_assert(2 + 2 + SB == XBLK, "Q8_1 block size");
 
-// Rows of the internal activation planes are padded to a multiple of this, so
-// tile kernels can read whole 32-row MFMA tiles without bounds checks.
+// Rows of the internal activation planes are allocated in multiples of this,
+// so tile kernels can read whole 32-row groups of block scales in bounds.
 constexpr int MPAD = 32;
 
 // ---- kvalues_iq4nl packed for byte-permute lookups -----------------------
@@ -90,10 +90,16 @@ __device__ __forceinline__ float sub_scale(uint32_t h0, uint32_t h1, int b)
 //                         elements paired with the low and high nibbles of
 //                         qs[16b+8h .. 16b+8h+7];
 //   dp  float [K/32][Mp] the block scales d (fp16 widened), m fastest.
-// Mp = M rounded up to MPAD; rows M..Mp-1 are zero.
+// Mp = M rounded up to MPAD; rows M..Mp-1 are allocated but never written
+// (the kernels do not use their values).
+//   cnt   uint32 [CNT_MAX] arrival counters of the split-K decode kernel,
+//                         zeroed when the planes are written and left at zero
+//                         by every matmul launch that uses them.
+constexpr int CNT_MAX = 8192;
 struct XPlanes {
     int8_t *qp;
     float *dp;
+    uint32_t *cnt;
     int64_t M, Mp, K;
 };
 
@@ -101,7 +107,7 @@ inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 inline size_t xplanes_bytes(int64_t M, int64_t K)
 {
     const int64_t Mp = round_up(M, MPAD);
-    return (size_t)(Mp * K) + (size_t)(Mp * (K / SB)) * sizeof(float);
+    return (size_t)(Mp * K) + (size_t)(Mp * (K / SB)) * sizeof(float) + CNT_MAX * sizeof(uint32_t);
 }
 inline XPlanes xplanes_at(void *base, int64_t M, int64_t K)
 {
@@ -111,6 +117,7 @@ inline XPlanes xplanes_at(void *base, int64_t M, int64_t K)
     p.K = K;
     p.qp = (int8_t *)base;
     p.dp = (float *)((char *)base + p.Mp * K);
+    p.cnt = (uint32_t *)((char *)p.dp + p.Mp * (K / SB) * sizeof(float));
     return p;
 }
 
@@ -121,11 +128,39 @@ hipError_t launch_quantize(const float *X, void *Xq, const XPlanes *planes, uint
 hipError_t launch_q8_1_convert(const void *Xq, const XPlanes *planes, uint16_t *Xbf, int64_t M,
                               int64_t K, hipStream_t s);
 hipError_t launch_gemv(const void *W, const XPlanes &x, float *Y, int64_t N, hipStream_t s);
-hipError_t launch_mmq(const void *W, const XPlanes &x, float *Y, int64_t N, hipStream_t s);
+// MMQ work split for a shape: TM 32-row subtiles per wavefront, KW
+// wavefronts per workgroup and KS workgroups along K.  With KS > 1 the launch
+// needs a workspace of workspace_bytes (KS partial [M][N] tiles).
+// Decode kernel (M <= 32): NW wavefronts x 32 columns per workgroup, KS
+// workgroups along K.
+struct DecPlan {
+    int nw = 4, ks = 1;
+    bool ok = false;
+    size_t workspace_bytes = 0;
+};
+DecPlan mmq_dec_plan(int64_t M, int64_t N, int64_t K);
+hipError_t launch_mmq_dec(const void *W, const XPlanes &x, float *Y, int64_t N, void *workspace,
+                          const DecPlan &p, hipStream_t s);
+struct MmqPlan {
+    int tm = 1, kw = 1, ks = 1;
+    bool dec = false;          // the decode kernel runs (M <= 32)
+    DecPlan dp;
+    size_t workspace_bytes = 0;
+};
+MmqPlan mmq_plan(int64_t M, int64_t N, int64_t K);
+hipError_t launch_mmq(const void *W, const XPlanes &x, float *Y, int64_t N, void *workspace,
+                      hipStream_t s);
 hipError_t launch_dequant_bf16(const void *W, uint16_t *Wb, int64_t N, int64_t K, hipStream_t s);
 hipError_t launch_gemm_bf16(const uint16_t *Xb, const uint16_t *Wb, float *Y, int64_t M,
                             int64_t N, int64_t K, hipStream_t s);
 
 constexpr int GEMV_MAX_M = 4;
+
+// Tuning override of kernel work splits, read once from IQ4XS_DEC_PLAN="nw,ks"
+// (decode kernel wavefronts per workgroup, K splits); 0 = automatic.
+struct TuneOverride {
+    int dec_nw = 0, dec_ks = 0;
+};
+const TuneOverride &tune_override();
 
 }  // namespace iq4xs

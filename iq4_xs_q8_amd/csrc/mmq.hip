@@ -22,10 +22,16 @@
 // Result layout (16 int32 per lane): column n = l%32, register r holds row
 // 8*(r/4) + 4*(l/32) + r%4.
 //
-// The weights go straight from HBM to registers (no LDS round trip): each
-// byte is needed by exactly one lane.  A workgroup is KW wavefronts over the
-// same 32 columns and 32*TM rows, each taking 1/KW of the sub-blocks; their
-// partial sums meet in LDS and are added in wave order (deterministic).
+// The weights go straight from HBM to registers (each byte is needed by one
+// lane only).  A wavefront walks whole super-blocks: the next super-block's
+// header and index bytes are loaded before the current one is computed, and
+// the activation operands of a group of G sub-blocks are loaded before their
+// MFMAs.  Work split: KW wavefronts of a workgroup share 32 columns x 32*TM
+// rows and split the workgroup's super-blocks; their partial sums meet in LDS
+// and are added in wave order.  For long K and small N the super-blocks are
+// further split over KS workgroups (grid z); each writes its partial tile to
+// a workspace and a second kernel adds the KS partials in order.  Everything
+// is deterministic: no atomics, fixed summation order.
 #include "common.hpp"
 
 namespace iq4xs {
@@ -35,28 +41,46 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
 constexpr int TILE = 32;   // MFMA tile edge (rows and columns)
+// Buffer-resource flags word for raw (stride 0) buffers on the gfx9 family.
+constexpr int BUFFER_FLAGS = 0x00020000;
 
 // TM   : 32-row activation subtiles per wavefront (weights reused TM times)
 // LIVE : result registers per subtile that can hold a real row (4: M<=8,
-//        8: M<=16, 16: M<=32) -- the rest are skipped in the epilogue
-// KW   : wavefronts per workgroup, splitting the sub-blocks
-template <int TM, int LIVE, int KW>
+//        8: M<=16, 16: M<=32); the rest are skipped in the epilogue
+// KW   : wavefronts per workgroup splitting the super-blocks
+// G    : sub-blocks whose activation operands are loaded together (1,2,4,8)
+template <int TM, int LIVE, int KW, int G>
 __global__ void __launch_bounds__(64 * KW)
 k_mmq(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, const float *__restrict__ dp,
       float *__restrict__ Y, int64_t M, int64_t N, int64_t K, int64_t Mp)
 {
     static_assert(LIVE == 4 || LIVE == 8 || LIVE == 16, "live register count");
     static_assert(TM >= 1 && TM <= 4 && KW >= 1 && KW <= 8, "tile shape");
+    static_assert(G == 1 || G == 2 || G == 4 || G == 8, "activation group");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int col = lane & 31, h = lane >> 5;
     const int64_t n0 = (int64_t)blockIdx.y * TILE;
     const int64_t m0 = (int64_t)blockIdx.x * TILE * TM;
-    const int64_t n_ld = (n0 + col < N) ? n0 + col : N - 1;   // clamp loads, mask stores
-    const int64_t nb = K / QK, nsub = K / SB;
-    const uint8_t *row = W + n_ld * nb * WBLK;
+    const int64_t nb = K / QK;
+    const uint32_t row_bytes = (uint32_t)(nb * WBLK);
+    const int ks = gridDim.z;                     // workgroups splitting K
+    const int64_t jw0 = nb * blockIdx.z / ks, jw1 = nb * (blockIdx.z + 1) / ks;
+    const int64_t j_begin = jw0 + (jw1 - jw0) * wave / KW;
+    const int64_t j_end = jw0 + (jw1 - jw0) * (wave + 1) / KW;
+    int tm_live = (int)((Mp - m0) / TILE);        // 32-row subtiles inside the padded rows
+    if (tm_live > TM)
+        tm_live = TM;
 
-    const int64_t per = nsub / KW;                // nsub is a multiple of 8, KW divides 8
-    const int64_t b_begin = wave * per, b_end = b_begin + per;
+    // Buffer descriptors: rows past N (weights) and past M (activations) lie
+    // beyond num_records, so their loads return zeros without a memory access.
+    const int64_t n_rows = (N - n0) < TILE ? (N - n0) : TILE;
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(W + n0 * (int64_t)row_bytes), (short)0, (int)(n_rows * row_bytes), BUFFER_FLAGS);
+    const int64_t m_rows = M - m0;                // > 0: the grid covers rows < Mp only
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(qp + m0 * K), (short)0,
+        (int)((m_rows < TILE * TM ? m_rows : TILE * TM) * K), BUFFER_FLAGS);
+    const uint32_t w_lane = (uint32_t)col * row_bytes;
 
     float acc[TM][LIVE];
 #pragma unroll
@@ -65,32 +89,74 @@ k_mmq(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, const float 
         for (int r = 0; r < LIVE; r++)
             acc[t][r] = 0.0f;
 
-    for (int64_t b = b_begin; b < b_end; b++) {
-        const uint8_t *blk = row + (b >> 3) * WBLK;
-        const uint2 hdr = *reinterpret_cast<const uint2 *>(blk);
-        const uint2 qs = *reinterpret_cast<const uint2 *>(blk + QS_OFF + 16 * (b & 7) + 8 * h);
-        uint32_t wv[4];
-        expand8(qs.x, qs.y, wv);
-        const v4i bw = {(int)wv[0], (int)wv[1], (int)wv[2], (int)wv[3]};
-        const float sw = sub_scale(hdr.x, hdr.y, (int)(b & 7));
+    uint2 hdr_c = make_uint2(0, 0), qs_c[SUBS];
+    uint2 hdr_n = make_uint2(0, 0), qs_n[SUBS];
 #pragma unroll
-        for (int t = 0; t < TM; t++) {
-            const int64_t mt = m0 + TILE * t;
-            if (mt >= Mp)
-                break;                            // uniform: whole subtile past the padding
-            const v4i ax = *reinterpret_cast<const v4i *>(qp + (mt + col) * K + 32 * b + 16 * h);
-            const v16i zero = {0};
-            const v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(ax, bw, zero, 0, 0, 0);
-            const float *dxp = dp + b * Mp + mt + 4 * h;
+    for (int s = 0; s < SUBS; s++)
+        qs_c[s] = qs_n[s] = make_uint2(0, 0);
+    auto load_w = [&](int64_t j, uint2 &hdr, uint2 *qs) {
+        const uint32_t o = w_lane + (uint32_t)j * WBLK;
+        hdr = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(wr, o, 0, 0));
 #pragma unroll
-            for (int j = 0; j < LIVE / 4; j++) {
-                const float4 dx = *reinterpret_cast<const float4 *>(dxp + 8 * j);
-                acc[t][4 * j + 0] += (sw * dx.x) * (float)D[4 * j + 0];
-                acc[t][4 * j + 1] += (sw * dx.y) * (float)D[4 * j + 1];
-                acc[t][4 * j + 2] += (sw * dx.z) * (float)D[4 * j + 2];
-                acc[t][4 * j + 3] += (sw * dx.w) * (float)D[4 * j + 3];
+        for (int s = 0; s < SUBS; s++)
+            qs[s] = __builtin_bit_cast(
+                uint2, __builtin_amdgcn_raw_buffer_load_b64(wr, o + QS_OFF + 16 * s + 8 * h, 0, 0));
+    };
+    if (j_begin < j_end)
+        load_w(j_begin, hdr_c, qs_c);
+
+    for (int64_t j = j_begin; j < j_end; j++) {
+#pragma unroll
+        for (int g = 0; g < SUBS; g += G) {
+            // activation operands of sub-blocks g..g+G-1 of super-block j ...
+            v4i ax[TM][G];
+            float4 dx[TM][G][LIVE / 4];
+#pragma unroll
+            for (int t = 0; t < TM; t++) {
+                if (t < tm_live) {
+                    const int64_t mt = m0 + TILE * t;
+#pragma unroll
+                    for (int s = 0; s < G; s++) {
+                        const int64_t sb = SUBS * j + g + s;
+                        ax[t][s] = __builtin_amdgcn_raw_buffer_load_b128(
+                            xr, (uint32_t)((TILE * t + col) * K + 32 * sb + 16 * h), 0, 0);
+#pragma unroll
+                        for (int q = 0; q < LIVE / 4; q++)
+                            dx[t][s][q] = *reinterpret_cast<const float4 *>(dp + sb * Mp + mt + 4 * h + 8 * q);
+                    }
+                }
+            }
+            // ... then, once the last group's activations are in flight, the
+            // next super-block's weights: loads retire in order, so waiting for
+            // the activations above never waits for this prefetch
+            if (g + G == SUBS && j + 1 < j_end)
+                load_w(j + 1, hdr_n, qs_n);
+#pragma unroll
+            for (int s = 0; s < G; s++) {
+                uint32_t wv[4];
+                expand8(qs_c[g + s].x, qs_c[g + s].y, wv);
+                const v4i bw = {(int)wv[0], (int)wv[1], (int)wv[2], (int)wv[3]};
+                const float sw = sub_scale(hdr_c.x, hdr_c.y, g + s);
+#pragma unroll
+                for (int t = 0; t < TM; t++) {
+                    if (t < tm_live) {
+                        const v16i zero = {0};
+                        const v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(ax[t][s], bw, zero, 0, 0, 0);
+#pragma unroll
+                        for (int q = 0; q < LIVE / 4; q++) {
+                            acc[t][4 * q + 0] += (sw * dx[t][s][q].x) * (float)D[4 * q + 0];
+                            acc[t][4 * q + 1] += (sw * dx[t][s][q].y) * (float)D[4 * q + 1];
+                            acc[t][4 * q + 2] += (sw * dx[t][s][q].z) * (float)D[4 * q + 2];
+                            acc[t][4 * q + 3] += (sw * dx[t][s][q].w) * (float)D[4 * q + 3];
+                        }
+                    }
+                }
             }
         }
+        hdr_c = hdr_n;
+#pragma unroll
+        for (int s = 0; s < SUBS; s++)
+            qs_c[s] = qs_n[s];
     }
 
     if constexpr (KW > 1) {
@@ -117,52 +183,109 @@ k_mmq(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, const float 
     const int64_t n = n0 + col;
     if (n >= N)
         return;
+    // with a K split, Y points at this split's slice of the [KS][M][N] workspace
+    float *out = Y + (int64_t)blockIdx.z * M * N;
 #pragma unroll
     for (int t = 0; t < TM; t++)
 #pragma unroll
         for (int r = 0; r < LIVE; r++) {
             const int64_t m = m0 + TILE * t + 8 * (r / 4) + 4 * h + (r % 4);
             if (m < M)
-                Y[m * N + n] = acc[t][r];
+                out[m * N + n] = acc[t][r];
         }
 }
 
-template <int TM, int LIVE>
-hipError_t launch_tm(const uint8_t *W, const XPlanes &x, float *Y, int64_t N, int kw,
-                     hipStream_t s)
+// Y[m,n] = sum_{z<KS} P[z][m][n], in order of z.
+__global__ void __launch_bounds__(256)
+k_sum_splits(const float *__restrict__ P, float *__restrict__ Y, int64_t MN, int ks)
 {
-    const dim3 grid((unsigned)((x.Mp + TILE * TM - 1) / (TILE * TM)), (unsigned)((N + TILE - 1) / TILE));
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= MN)
+        return;
+    float s = P[i];
+    for (int z = 1; z < ks; z++)
+        s += P[z * MN + i];
+    Y[i] = s;
+}
+
+template <int TM, int LIVE, int G>
+void launch_tm(const uint8_t *W, const XPlanes &x, float *out, int64_t N, int kw, int ks, hipStream_t s)
+{
+    const dim3 grid((unsigned)((x.Mp + TILE * TM - 1) / (TILE * TM)), (unsigned)((N + TILE - 1) / TILE),
+                    (unsigned)ks);
     switch (kw) {
-    case 1: hipLaunchKernelGGL((k_mmq<TM, LIVE, 1>), grid, dim3(64), 0, s, W, x.qp, x.dp, Y, x.M, N, x.K, x.Mp); break;
-    case 2: hipLaunchKernelGGL((k_mmq<TM, LIVE, 2>), grid, dim3(128), 0, s, W, x.qp, x.dp, Y, x.M, N, x.K, x.Mp); break;
-    case 4: hipLaunchKernelGGL((k_mmq<TM, LIVE, 4>), grid, dim3(256), 0, s, W, x.qp, x.dp, Y, x.M, N, x.K, x.Mp); break;
-    case 8: hipLaunchKernelGGL((k_mmq<TM, LIVE, 8>), grid, dim3(512), 0, s, W, x.qp, x.dp, Y, x.M, N, x.K, x.Mp); break;
-    default: return hipErrorInvalidValue;
+    case 1: hipLaunchKernelGGL((k_mmq<TM, LIVE, 1, G>), grid, dim3(64), 0, s, W, x.qp, x.dp, out, x.M, N, x.K, x.Mp); break;
+    case 2: hipLaunchKernelGGL((k_mmq<TM, LIVE, 2, G>), grid, dim3(128), 0, s, W, x.qp, x.dp, out, x.M, N, x.K, x.Mp); break;
+    case 4: hipLaunchKernelGGL((k_mmq<TM, LIVE, 4, G>), grid, dim3(256), 0, s, W, x.qp, x.dp, out, x.M, N, x.K, x.Mp); break;
+    default:
+        if constexpr (TM == 1)
+            hipLaunchKernelGGL((k_mmq<TM, LIVE, 8, G>), grid, dim3(512), 0, s, W, x.qp, x.dp, out, x.M, N, x.K, x.Mp);
+        break;
     }
-    return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_mmq(const void *Wv, const XPlanes &x, float *Y, int64_t N, hipStream_t s)
+MmqPlan mmq_plan(int64_t M, int64_t N, int64_t K)
+{
+    MmqPlan p;
+    if (M <= TILE) {
+        p.dp = mmq_dec_plan(M, N, K);
+        if (p.dp.ok) {
+            p.dec = true;
+            p.workspace_bytes = p.dp.workspace_bytes;
+            return p;
+        }
+    }
+    const int64_t Mp = round_up(M, MPAD);
+    const int tm = M <= 32 ? 1 : (M <= 64 ? 2 : 4);
+    const int64_t nb = K / QK;
+    const int64_t tiles = ((N + TILE - 1) / TILE) * ((Mp + TILE * tm - 1) / (TILE * tm));
+    // enough workgroups to cover the 256 CUs twice, then enough wavefronts
+    // per workgroup for latency hiding; every wave keeps >= 2 super-blocks
+    int ks = 1;
+    while (ks < 8 && tiles * ks < 512 && nb / (ks * 2) >= 4)
+        ks *= 2;
+    // (8 wavefronts per workgroup only for single-subtile tiles: a 512-thread
+    // workgroup caps a lane at 256 registers, too few for TM >= 2)
+    const int kw_max = tm == 1 ? 8 : 4;
+    int kw = 1;
+    while (kw < kw_max && tiles * ks * kw < 4096 && nb / (ks * kw * 2) >= 2)
+        kw *= 2;
+    p.tm = tm;
+    p.kw = kw;
+    p.ks = ks;
+    p.workspace_bytes = ks > 1 ? (size_t)(ks * M * N) * sizeof(float) : 0;
+    return p;
+}
+
+hipError_t launch_mmq(const void *Wv, const XPlanes &x, float *Y, int64_t N, void *workspace,
+                      hipStream_t s)
 {
     const uint8_t *W = (const uint8_t *)Wv;
-    const int64_t ntile = (N + TILE - 1) / TILE;
-    int tm = x.M <= 32 ? 1 : (x.M <= 64 ? 2 : 4);
-    const int64_t wg = ntile * ((x.Mp + TILE * tm - 1) / (TILE * tm));
-    // enough wavefronts to cover the chip several times; nsub is a multiple of 8
-    int kw = 1;
-    while (kw < 8 && wg * kw < 2048)
-        kw *= 2;
+    const MmqPlan p = mmq_plan(x.M, N, x.K);
+    if (p.dec)
+        return launch_mmq_dec(Wv, x, Y, N, workspace, p.dp, s);
+    if (p.ks > 1 && workspace == nullptr)
+        return hipErrorInvalidValue;
+    float *out = p.ks > 1 ? (float *)workspace : Y;
     if (x.M <= 8)
-        return launch_tm<1, 4>(W, x, Y, N, kw, s);
-    if (x.M <= 16)
-        return launch_tm<1, 8>(W, x, Y, N, kw, s);
-    if (x.M <= 32)
-        return launch_tm<1, 16>(W, x, Y, N, kw, s);
-    if (x.M <= 64)
-        return launch_tm<2, 16>(W, x, Y, N, kw, s);
-    return launch_tm<4, 16>(W, x, Y, N, kw, s);
+        launch_tm<1, 4, 8>(W, x, out, N, p.kw, p.ks, s);
+    else if (x.M <= 16)
+        launch_tm<1, 8, 8>(W, x, out, N, p.kw, p.ks, s);
+    else if (x.M <= 32)
+        launch_tm<1, 16, 4>(W, x, out, N, p.kw, p.ks, s);
+    else if (x.M <= 64)
+        launch_tm<2, 16, 2>(W, x, out, N, p.kw, p.ks, s);
+    else
+        launch_tm<4, 16, 1>(W, x, out, N, p.kw, p.ks, s);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.ks == 1)
+        return e;
+    const int64_t MN = x.M * N;
+    hipLaunchKernelGGL(k_sum_splits, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, s,
+                       (const float *)workspace, Y, MN, p.ks);
+    return hipGetLastError();
 }
 
 }  // namespace iq4xs

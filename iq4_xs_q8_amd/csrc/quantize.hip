@@ -47,14 +47,18 @@ __device__ __forceinline__ int quant1(float x, float d)
     return q > 127 ? 127 : (q < -127 ? -127 : q);
 }
 
-// Grid: one thread per 4 activations over Mrows x K, Mrows = Mp when planes
-// are written (rows >= M are written as zero) and M otherwise.
+// Grid: one thread per 4 activations over Mrows x K (Mrows = M).  The plane
+// rows M..Mp-1 are never written: the matmul kernels either skip them or read
+// them through buffer descriptors that stop at row M.
 __global__ void __launch_bounds__(256)
 k_quantize(const float *__restrict__ X, uint8_t *__restrict__ Xq, int8_t *__restrict__ qp,
-           float *__restrict__ dp, uint16_t *__restrict__ Xbf, int64_t M, int64_t Mrows,
-           int64_t Mp, int64_t K)
+           float *__restrict__ dp, uint32_t *__restrict__ cnt, uint16_t *__restrict__ Xbf, int64_t M,
+           int64_t Mrows, int64_t Mp, int64_t K)
 {
     const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (cnt != nullptr)
+        for (int64_t i = tid; i < CNT_MAX; i += (int64_t)gridDim.x * blockDim.x)
+            cnt[i] = 0;
     const int64_t nblk_row = K / SB;
     const int64_t blk = tid >> 3;                 // global Q8_1 block index
     const int t = (int)(tid & 7);                 // lane within the block
@@ -103,12 +107,16 @@ k_quantize(const float *__restrict__ X, uint8_t *__restrict__ Xq, int8_t *__rest
 }
 
 // ABI Q8_1 blocks -> internal planes and/or bf16 X~.  Same grid shape as
-// k_quantize (Mrows = Mp when planes are written, else M).
+// k_quantize.
 __global__ void __launch_bounds__(256)
 k_q8_1_convert(const uint8_t *__restrict__ Xq, int8_t *__restrict__ qp, float *__restrict__ dp,
-               uint16_t *__restrict__ Xbf, int64_t M, int64_t Mrows, int64_t Mp, int64_t K)
+               uint32_t *__restrict__ cnt, uint16_t *__restrict__ Xbf, int64_t M, int64_t Mrows,
+               int64_t Mp, int64_t K)
 {
     const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (cnt != nullptr)
+        for (int64_t i = tid; i < CNT_MAX; i += (int64_t)gridDim.x * blockDim.x)
+            cnt[i] = 0;
     const int64_t nblk_row = K / SB;
     const int64_t blk = tid >> 3;
     const int t = (int)(tid & 7);
@@ -141,11 +149,12 @@ k_q8_1_convert(const uint8_t *__restrict__ Xq, int8_t *__restrict__ qp, float *_
 hipError_t launch_quantize(const float *X, void *Xq, const XPlanes *planes, uint16_t *Xbf,
                            int64_t M, int64_t K, hipStream_t s)
 {
-    const int64_t Mrows = planes ? planes->Mp : M;
+    const int64_t Mrows = M;
     const int64_t threads = Mrows * (K / 4);
     const int64_t grid = (threads + 255) / 256;
     hipLaunchKernelGGL(k_quantize, dim3((unsigned)grid), dim3(256), 0, s, X, (uint8_t *)Xq,
-                       planes ? planes->qp : nullptr, planes ? planes->dp : nullptr, Xbf, M, Mrows,
+                       planes ? planes->qp : nullptr, planes ? planes->dp : nullptr,
+                       planes ? planes->cnt : nullptr, Xbf, M, Mrows,
                        planes ? planes->Mp : M, K);
     return hipGetLastError();
 }
@@ -153,11 +162,12 @@ hipError_t launch_quantize(const float *X, void *Xq, const XPlanes *planes, uint
 hipError_t launch_q8_1_convert(const void *Xq, const XPlanes *planes, uint16_t *Xbf, int64_t M,
                               int64_t K, hipStream_t s)
 {
-    const int64_t Mrows = planes ? planes->Mp : M;
+    const int64_t Mrows = M;
     const int64_t threads = Mrows * (K / 4);
     const int64_t grid = (threads + 255) / 256;
     hipLaunchKernelGGL(k_q8_1_convert, dim3((unsigned)grid), dim3(256), 0, s, (const uint8_t *)Xq,
-                       planes ? planes->qp : nullptr, planes ? planes->dp : nullptr, Xbf, M, Mrows,
+                       planes ? planes->qp : nullptr, planes ? planes->dp : nullptr,
+                       planes ? planes->cnt : nullptr, Xbf, M, Mrows,
                        planes ? planes->Mp : M, K);
     return hipGetLastError();
 }

@@ -93,9 +93,38 @@ def test_unknown_path_and_gemv_limit():
     assert L.iq4xs_gemm_path(A, A * 2, A * 4, 5, 8, 256, iq.PATH_GEMV, None) == iq.EPATH
 
 
+def test_workspace_query_and_checks():
+    size = ctypes.c_size_t()
+    ref = {}
+    for path in (iq.PATH_GEMV, iq.PATH_MMQ, iq.PATH_DEQ_BF16):
+        assert L.iq4xs_gemm_workspace_bytes(4, 1024, 2048, path, ctypes.byref(size)) == iq.OK
+        ref[path] = size.value
+        assert size.value > 0
+    # the bf16 path holds the dequantized weights; the integer paths the Q8_1 planes
+    assert ref[iq.PATH_DEQ_BF16] >= 1024 * 2048 * 2
+    assert ref[iq.PATH_GEMV] >= 4 * 2048 * 1.125
+    assert L.iq4xs_gemm_workspace_bytes(4, 1024, 2048, iq.PATH_AUTO, ctypes.byref(size)) == iq.OK
+    assert size.value == ref[iq.dispatch(4, 1024, 2048)]
+    assert L.iq4xs_gemm_workspace_bytes(5, 1024, 2048, iq.PATH_GEMV, ctypes.byref(size)) == iq.EPATH
+    assert L.iq4xs_gemm_workspace_bytes(4, 1024, 300, iq.PATH_MMQ, ctypes.byref(size)) == iq.EINVAL
+    assert L.iq4xs_gemm_workspace_bytes(4, 1024, 2048, iq.PATH_MMQ, None) == iq.EINVAL
+    assert iq.workspace_bytes(4, 1024, 2048, iq.PATH_MMQ) == ref[iq.PATH_MMQ]
+
+    need = iq.workspace_bytes(4, 8, 256, iq.PATH_MMQ)
+    WS = 1 << 30
+    assert L.iq4xs_gemm_ws(A, A * 2, A * 4, 4, 8, 256, iq.PATH_MMQ, None, need, None) == iq.EINVAL
+    assert L.iq4xs_gemm_ws(A, A * 2, A * 4, 4, 8, 256, iq.PATH_MMQ, WS, need - 1, None) == iq.EINVAL
+    assert L.iq4xs_gemm_ws(A, A * 2, A * 4, 4, 8, 256, iq.PATH_MMQ, WS + 16, need, None) == iq.EALIGN
+    assert L.iq4xs_gemm_ws(A, A * 2, A * 4, 4, 8, 256, iq.PATH_MMQ, A * 4 - 256, need, None) == iq.EINVAL
+    assert L.iq4xs_gemm_ws(A, A * 2, A * 4, 5, 8, 256, iq.PATH_GEMV, WS, need, None) == iq.EPATH
+    assert L.iq4xs_gemm_ws(A, A * 2, A * 4 + 4, 4, 8, 256, iq.PATH_MMQ, WS, need, None) == iq.EALIGN
+
+
 @pytest.mark.skipif(_has_gpu(), reason="checks the no-device error")
 def test_no_device_reports_edevice():
     assert L.iq4xs_gemm(A, A * 2, A * 4, 4, 8, 256, None) == iq.EDEVICE
+    ws = iq.workspace_bytes(4, 8, 256, iq.PATH_MMQ)
+    assert L.iq4xs_gemm_ws(A, A * 2, A * 4, 4, 8, 256, iq.PATH_MMQ, 1 << 30, ws, None) == iq.EDEVICE
     assert "device" in L.iq4xs_last_error().decode()
     assert L.iq4xs_quantize_q8_1(A, A * 2, 4, 256, None) == iq.EDEVICE
     assert L.iq4xs_dequantize_bf16(A, A * 2, 8, 256, None) == iq.EDEVICE

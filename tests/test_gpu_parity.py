@@ -107,6 +107,10 @@ def test_gemm_paths_match_oracle(M, N, K):
             act = iq.prepare_act(Xd)
             y3 = iq.gemm_act(Wd, act, M, K, path=p, out=poisoned((M, N))).cpu().numpy()
             assert np.array_equal(y, y3), f"{iq.path_name(p)}: gemm and gemm_act differ"
+        # and with caller-provided scratch (no allocation inside the call)
+        ws = torch.empty(iq.workspace_bytes(M, N, K, p), dtype=torch.uint8, device="cuda")
+        y4 = iq.gemm(Wd, Xd, path=p, out=poisoned((M, N)), workspace=ws).cpu().numpy()
+        assert np.array_equal(y, y4), f"{iq.path_name(p)}: gemm and gemm_ws differ"
 
 
 @pytest.mark.parametrize("path", [iq.PATH_GEMV, iq.PATH_MMQ])
@@ -153,12 +157,19 @@ def test_deterministic_and_invariant(path):
     y1 = iq.gemm(Wd, Xd, path=path).cpu()
     y2 = iq.gemm(Wd, Xd, path=path).cpu()
     assert torch.equal(y1, y2), "two runs differ"
+    if path == iq.PATH_DEQ_BF16:
+        # the bf16 MFMA's fp32 accumulation is not sign-symmetric bit for bit:
+        # only the tolerance-level invariances hold
+        ref = y1.double().numpy()
+        assert_rows_close(-iq.gemm(Wd, -Xd, path=path).cpu().numpy(), ref, tol=1e-6)
+        assert_rows_close(0.5 * iq.gemm(Wd, 2 * Xd, path=path).cpu().numpy(), ref, tol=1e-6)
+        return
+    # integer paths: exact symmetry and scaling (q flips sign, d doubles exactly)
     assert torch.equal(iq.gemm(Wd, -Xd, path=path).cpu(), -y1)
     assert torch.equal(iq.gemm(Wd, 2 * Xd, path=path).cpu(), 2 * y1)
     # row m does not depend on the other rows (same path, same tile shape)
     y_row = iq.gemm(Wd, Xd[1:2].contiguous(), path=path).cpu()
-    if path != iq.PATH_DEQ_BF16:
-        assert torch.equal(y_row[0], y1[1])
+    assert torch.equal(y_row[0], y1[1])
 
 
 def test_negative_control_corrupted_weight_fails():
@@ -235,3 +246,35 @@ def _wdev_cached(wl, N, K, W):
     if key not in _cache:
         _cache[key] = dev(W)
     return _cache[key]
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1024, 2048), (3, 520, 1280), (8, 2048, 2048), (40, 640, 4096)])
+def test_graph_replays_match_eager(M, N, K):
+    """The caller-workspace entry point recorded in a HIP graph: every replay,
+    with eager work and new inputs in between, equals the eager call."""
+    W, X = _inputs(M, N, K, seed=3)
+    Wd = dev(W)
+    Xd = dev(X)
+    Y = poisoned((M, N))
+    ws = torch.empty(iq.workspace_bytes(M, N, K), dtype=torch.uint8, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        iq.gemm(Wd, Xd, out=Y, workspace=ws)          # warm up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        iq.gemm(Wd, Xd, out=Y, workspace=ws)
+    for rep in range(4):
+        Xn = synth.activations((902, M, K, rep), M, K, sigma=1.0 + rep, outlier_frac=0.01 * rep)
+        Xd.copy_(dev(Xn))
+        Y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = Y.cpu().numpy()
+        want = iq.gemm(Wd, Xd).cpu().numpy()          # eager, allocating entry point
+        assert np.array_equal(got, want), f"replay {rep} differs from the eager call"
+        ref = O.gemm_q8_1(W, O.quantize_q8_1(Xn), K)
+        assert_rows_close(got, ref, what=f"graph replay {rep} M={M}")
