@@ -27,13 +27,19 @@ const TuneOverride &iq4xs::tune_override()
 {
     static const TuneOverride t = [] {
         TuneOverride o;
-        const char *v = getenv("IQ4XS_DEC_PLAN");
-        if (v)
-            sscanf(v, "%d,%d", &o.dec_nw, &o.dec_ks);
+        const char *m = getenv("IQ4XS_MMV");
+        if (m && m[0] == '0')
+            o.mmv = 0;
         return o;
     }();
     return t;
 }
+
+namespace {
+int cus_of_current_device();
+}
+
+int iq4xs::device_cus() { return cus_of_current_device(); }
 
 namespace {
 
@@ -50,6 +56,7 @@ Config g_cfg;
 std::mutex g_mu;                       // guards g_table and g_dev_ok
 Table g_table;
 std::vector<int> g_dev_ok;             // per device: 0 unknown, 1 gfx950, -1 other
+std::vector<int> g_dev_cus;            // per device: compute units (0 unknown)
 
 int fail(int code, const char *fmt, ...)
 {
@@ -126,6 +133,9 @@ int check_device()
             return fail(IQ4XS_EDEVICE, "cannot query device %d", dev);
         }
         g_dev_ok[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+        if ((int)g_dev_cus.size() < count)
+            g_dev_cus.resize(count, 0);
+        g_dev_cus[dev] = prop.multiProcessorCount;
         if (g_dev_ok[dev] == 1) {
             // keep freed scratch in the pool so steady-state calls do not
             // return memory to the driver
@@ -142,6 +152,17 @@ int check_device()
     if (g_table.arch != "gfx950")
         return fail(IQ4XS_ETABLE, "dispatch table is for %s, device is gfx950", g_table.arch.c_str());
     return IQ4XS_OK;
+}
+
+int cus_of_current_device()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    std::lock_guard<std::mutex> lk(g_mu);
+    return dev >= 0 && dev < (int)g_dev_cus.size() && g_dev_cus[dev] > 0 ? g_dev_cus[dev] : 256;
 }
 
 bool mul_ok(int64_t a, int64_t b, int64_t *out)
@@ -265,11 +286,16 @@ int run_gemm(const void *W, const float *X, const void *Xq, float *Y, int64_t M,
     if (path == IQ4XS_PATH_GEMV || path == IQ4XS_PATH_MMQ) {
         const size_t pbytes = (size_t)round_up((int64_t)xplanes_bytes(M, K), 256);
         const XPlanes xp = xplanes_at(base, M, K);
-        hipError_t e = X ? launch_quantize(X, nullptr, &xp, nullptr, M, K, s)
-                         : launch_q8_1_convert(Xq, &xp, nullptr, M, K, s);
+        // a matmul that adds partial tiles into Y gets it zeroed by the quantizer
+        const bool zero = path == IQ4XS_PATH_MMQ && mmq_plan(M, N, K).vp.zero_y;
+        float *yz = zero ? Y : nullptr;
+        const int64_t nz = zero ? M * N : 0;
+        hipError_t e = X ? launch_quantize(X, nullptr, &xp, nullptr, M, K, s, yz, nz)
+                         : launch_q8_1_convert(Xq, &xp, nullptr, M, K, s, yz, nz);
         if ((st = launch_err(e, "quantize")) != IQ4XS_OK)
             return st;
-        e = path == IQ4XS_PATH_GEMV ? launch_gemv(W, xp, Y, N, s) : launch_mmq(W, xp, Y, N, base + pbytes, s);
+        e = path == IQ4XS_PATH_GEMV ? launch_gemv(W, xp, Y, N, s)
+                                    : launch_mmq(W, xp, Y, N, base + pbytes, zero, s);
         return launch_err(e, path_name(path));
     }
     // DEQ_BF16: X~ bf16 [M][K], then W~ bf16 [N][K] (256-byte aligned)
@@ -472,7 +498,7 @@ int iq4xs_gemm_act(const void *W, const void *act, float *Y, int64_t M, int64_t 
         scr.p = nullptr;
         return fail(IQ4XS_ENOMEM, "workspace of %zu bytes", wbytes);
     }
-    return launch_err(launch_mmq(W, xp, Y, N, scr.p, s), path_name(path));
+    return launch_err(launch_mmq(W, xp, Y, N, scr.p, false, s), path_name(path));
 }
 
 int iq4xs_dispatch(int64_t M, int64_t N, int64_t K, int *path_out)

@@ -25,9 +25,9 @@ static_assert(2 + 2 + 4 + QK / 2 == WBLK, "IQ4_XS super-block size");
 static_assert(QS_OFF == 2 + 2 + 4, "qs follows d, scales_h, scales_l");
 static_assert(2 + 2 + SB == XBLK, "Q8_1 block size");
 
-// Rows of the internal activation planes are allocated in multiples of this,
-// so tile kernels can read whole 32-row groups of block scales in bounds.
-constexpr int MPAD = 32;
+// Rows of the internal activation planes are padded to a multiple of this,
+// so the block scales of four consecutive rows are one aligned float4.
+constexpr int MPAD = 4;
 
 // ---- kvalues_iq4nl packed for byte-permute lookups -----------------------
 constexpr int8_t KVALUES[16] = {-127, -104, -83, -65, -49, -35, -22, -10,
@@ -41,16 +41,18 @@ constexpr uint32_t kv_word(int i)
 constexpr uint32_t KV0 = kv_word(0), KV1 = kv_word(1), KV2 = kv_word(2), KV3 = kv_word(3);
 static_assert(KV0 == 0xBFAD9881u && KV3 == 0x71594535u, "codebook packing");
 
-// Four 4-bit indices (one per byte, values 0..15) -> four int8 kvalues.
-// v_perm_b32 picks byte s (0..7) of {hi:lo}; indices 0-7 come from {KV1:KV0},
-// 8-15 from {KV3:KV2}, and a third permute chooses per byte by bit 3.
-__device__ __forceinline__ uint32_t lut4(uint32_t nib)
+// Four 4-bit indices -> four int8 kvalues with byte permutes.  v_perm_b32
+// picks byte s (0..7) of {hi:lo}, gives 0x00 for selector 5 of {0:0} and
+// 0xFF for any selector >= 13: indices 0-7 come from {KV1:KV0}, 8-15 from
+// {KV3:KV2}, and a mask built from bit 3 (selector 5 or 13) chooses per byte.
+// The indices are bits 0-3 of each byte of t; bits 4-7 are ignored.
+__device__ __forceinline__ uint32_t lut4(uint32_t t)
 {
-    const uint32_t s = nib & 0x07070707u;
+    const uint32_t s = t & 0x07070707u;
     const uint32_t a = __builtin_amdgcn_perm(KV1, KV0, s);
     const uint32_t b = __builtin_amdgcn_perm(KV3, KV2, s);
-    const uint32_t sel = ((nib >> 1) & 0x04040404u) | 0x03020100u;
-    return __builtin_amdgcn_perm(b, a, sel);
+    const uint32_t m = __builtin_amdgcn_perm(0u, 0u, (t & 0x08080808u) | 0x05050505u);
+    return (m & b) | (~m & a);
 }
 
 // 8 index bytes (2 dwords of qs) -> 16 int8 weights in "chunk" order:
@@ -58,10 +60,10 @@ __device__ __forceinline__ uint32_t lut4(uint32_t nib)
 // (elements 16+j..16+j+7) of the same bytes.
 __device__ __forceinline__ void expand8(uint32_t w0, uint32_t w1, uint32_t out[4])
 {
-    out[0] = lut4(w0 & 0x0F0F0F0Fu);
-    out[1] = lut4(w1 & 0x0F0F0F0Fu);
-    out[2] = lut4((w0 >> 4) & 0x0F0F0F0Fu);
-    out[3] = lut4((w1 >> 4) & 0x0F0F0F0Fu);
+    out[0] = lut4(w0);
+    out[1] = lut4(w1);
+    out[2] = lut4(w0 >> 4);
+    out[3] = lut4(w1 >> 4);
 }
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t h16)
@@ -81,25 +83,22 @@ __device__ __forceinline__ float sub_scale(uint32_t h0, uint32_t h1, int b)
 }
 
 // ---- internal activation planes ------------------------------------------
-// The matmul kernels read Q8_1 activations from two planes instead of the
-// 36-byte ABI blocks:
-//   qp  int8  [Mp][K]    sub-block b of row m at qp[m*K + 32b], stored in
-//                         "chunk" order: bytes 0-7 = elements 0-7, 8-15 =
-//                         elements 16-23, 16-23 = elements 8-15, 24-31 =
-//                         elements 24-31, so chunk h (16 bytes at 16h) holds the
-//                         elements paired with the low and high nibbles of
-//                         qs[16b+8h .. 16b+8h+7];
-//   dp  float [K/32][Mp] the block scales d (fp16 widened), m fastest.
-// Mp = M rounded up to MPAD; rows M..Mp-1 are allocated but never written
-// (the kernels do not use their values).
-//   cnt   uint32 [CNT_MAX] arrival counters of the split-K decode kernel,
-//                         zeroed when the planes are written and left at zero
-//                         by every matmul launch that uses them.
-constexpr int CNT_MAX = 8192;
+// The matmul kernels read Q8_1 activations from two sub-block-major planes
+// instead of the 36-byte ABI blocks (Mp = M rounded up to MPAD):
+//   qp  int8  [K/32][Mp][32]  the 32 values of block b of row m at
+//                              qp[(b*Mp + m)*32], in "chunk" order: bytes 0-7 =
+//                              elements 0-7, 8-15 = elements 16-23, 16-23 =
+//                              elements 8-15, 24-31 = elements 24-31, so chunk h
+//                              (16 bytes at 16h) holds the elements paired with
+//                              the low and high nibbles of qs[16b'+8h .. +7];
+//   dp  float [K/32][Mp]      the block scales d (fp16 widened).
+// The 32 rows of one block are 1 KB of contiguous bytes, the MFMA operand of a
+// 32-row tile.  Rows M..Mp-1 are allocated but never written: the kernels
+// either read a zero row in their place or discard what they compute from
+// them.
 struct XPlanes {
     int8_t *qp;
     float *dp;
-    uint32_t *cnt;
     int64_t M, Mp, K;
 };
 
@@ -107,7 +106,7 @@ inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 inline size_t xplanes_bytes(int64_t M, int64_t K)
 {
     const int64_t Mp = round_up(M, MPAD);
-    return (size_t)(Mp * K) + (size_t)(Mp * (K / SB)) * sizeof(float) + CNT_MAX * sizeof(uint32_t);
+    return (size_t)(Mp * K) + (size_t)(Mp * (K / SB)) * sizeof(float);
 }
 inline XPlanes xplanes_at(void *base, int64_t M, int64_t K)
 {
@@ -117,50 +116,57 @@ inline XPlanes xplanes_at(void *base, int64_t M, int64_t K)
     p.K = K;
     p.qp = (int8_t *)base;
     p.dp = (float *)((char *)base + p.Mp * K);
-    p.cnt = (uint32_t *)((char *)p.dp + p.Mp * (K / SB) * sizeof(float));
     return p;
 }
 
 // ---- launchers (each defined in the .hip file that holds its kernel) -----
-// All return a hipError_t from hipGetLastError() after the launch.
+// All return a hipError_t from hipGetLastError() after the launch.  The
+// quantizers also zero yz[0..nz) when yz is given (the output of a matmul
+// that adds partial tiles into it).
 hipError_t launch_quantize(const float *X, void *Xq, const XPlanes *planes, uint16_t *Xbf,
-                           int64_t M, int64_t K, hipStream_t s);
+                           int64_t M, int64_t K, hipStream_t s, float *yz = nullptr, int64_t nz = 0);
 hipError_t launch_q8_1_convert(const void *Xq, const XPlanes *planes, uint16_t *Xbf, int64_t M,
-                              int64_t K, hipStream_t s);
+                              int64_t K, hipStream_t s, float *yz = nullptr, int64_t nz = 0);
+hipError_t launch_zero(float *y, int64_t n, hipStream_t s);
 hipError_t launch_gemv(const void *W, const XPlanes &x, float *Y, int64_t N, hipStream_t s);
 // MMQ work split for a shape: TM 32-row subtiles per wavefront, KW
 // wavefronts per workgroup and KS workgroups along K.  With KS > 1 the launch
 // needs a workspace of workspace_bytes (KS partial [M][N] tiles).
-// Decode kernel (M <= 32): NW wavefronts x 32 columns per workgroup, KS
-// workgroups along K.
-struct DecPlan {
-    int nw = 4, ks = 1;
-    bool ok = false;
-    size_t workspace_bytes = 0;
+// Streaming matrix-core kernel for M <= 32 (mmv.hip): `grid` workgroups
+// (at most one per 32-column tile and per compute unit), result registers
+// `live`; zero_y = some tile is shared by two workgroups, which add into a
+// zeroed Y.
+struct MmvPlan {
+    bool ok = false, zero_y = false;
+    int grid = 0, live = 0;
 };
-DecPlan mmq_dec_plan(int64_t M, int64_t N, int64_t K);
-hipError_t launch_mmq_dec(const void *W, const XPlanes &x, float *Y, int64_t N, void *workspace,
-                          const DecPlan &p, hipStream_t s);
+MmvPlan mmv_plan(int64_t M, int64_t N, int64_t K, int cus);
+hipError_t launch_mmv(const void *W, const XPlanes &x, float *Y, int64_t N, const MmvPlan &p,
+                      hipStream_t s);
 struct MmqPlan {
     int tm = 1, kw = 1, ks = 1;
-    bool dec = false;          // the decode kernel runs (M <= 32)
-    DecPlan dp;
+    bool mmv = false;          // the streaming kernel runs (M <= 32)
+    MmvPlan vp;
     size_t workspace_bytes = 0;
 };
 MmqPlan mmq_plan(int64_t M, int64_t N, int64_t K);
+// y_zeroed: the caller has already zeroed Y (else the launcher does it when
+// the plan needs it).
 hipError_t launch_mmq(const void *W, const XPlanes &x, float *Y, int64_t N, void *workspace,
-                      hipStream_t s);
+                      bool y_zeroed, hipStream_t s);
 hipError_t launch_dequant_bf16(const void *W, uint16_t *Wb, int64_t N, int64_t K, hipStream_t s);
 hipError_t launch_gemm_bf16(const uint16_t *Xb, const uint16_t *Wb, float *Y, int64_t M,
                             int64_t N, int64_t K, hipStream_t s);
 
 constexpr int GEMV_MAX_M = 4;
 
-// Tuning override of kernel work splits, read once from IQ4XS_DEC_PLAN="nw,ks"
-// (decode kernel wavefronts per workgroup, K splits); 0 = automatic.
+// Tuning override, read once: IQ4XS_MMV=0 (do not use the streaming kernel).
 struct TuneOverride {
-    int dec_nw = 0, dec_ks = 0;
+    int mmv = 1;
 };
 const TuneOverride &tune_override();
+
+// Compute units of the current device (256 when it cannot be queried).
+int device_cus();
 
 }  // namespace iq4xs

@@ -77,7 +77,7 @@ k_gemv(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, const float
             dx[i] = *reinterpret_cast<const float4 *>(dp + (uint32_t)b * (uint32_t)Mp);
 #pragma unroll
             for (int m = 0; m < M; m++)
-                xv[i][m] = *reinterpret_cast<const int4 *>(qp + (uint32_t)(m * K + 32 * b + 16 * h));
+                xv[i][m] = *reinterpret_cast<const int4 *>(qp + ((uint32_t)(b * Mp + m) * SB + 16 * h));
         }
 #pragma unroll
         for (int i = 0; i < U; i++) {

@@ -67,19 +67,22 @@ k_mmq(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, const float 
     const int64_t jw0 = nb * blockIdx.z / ks, jw1 = nb * (blockIdx.z + 1) / ks;
     const int64_t j_begin = jw0 + (jw1 - jw0) * wave / KW;
     const int64_t j_end = jw0 + (jw1 - jw0) * (wave + 1) / KW;
-    int tm_live = (int)((Mp - m0) / TILE);        // 32-row subtiles inside the padded rows
+    int tm_live = (int)((M - m0 + TILE - 1) / TILE);   // 32-row subtiles holding real rows
     if (tm_live > TM)
         tm_live = TM;
 
-    // Buffer descriptors: rows past N (weights) and past M (activations) lie
-    // beyond num_records, so their loads return zeros without a memory access.
+    // Buffer descriptors: rows past N (weights) and everything past the
+    // activation planes lie beyond num_records, so their loads return zeros
+    // without a memory access.  Activation rows M..m0+32*TM-1 of a block read
+    // pad rows or the next block's rows: they only feed result rows >= M,
+    // which are not stored.
     const int64_t n_rows = (N - n0) < TILE ? (N - n0) : TILE;
     const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(W + n0 * (int64_t)row_bytes), (short)0, (int)(n_rows * row_bytes), BUFFER_FLAGS);
-    const int64_t m_rows = M - m0;                // > 0: the grid covers rows < Mp only
-    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(qp + m0 * K), (short)0,
-        (int)((m_rows < TILE * TM ? m_rows : TILE * TM) * K), BUFFER_FLAGS);
+    const __amdgpu_buffer_rsrc_t xr =
+        __builtin_amdgcn_make_buffer_rsrc((void *)qp, (short)0, (int)(Mp * K), BUFFER_FLAGS);
+    const __amdgpu_buffer_rsrc_t dr =
+        __builtin_amdgcn_make_buffer_rsrc((void *)dp, (short)0, (int)(Mp * (K / SB) * 4), BUFFER_FLAGS);
     const uint32_t w_lane = (uint32_t)col * row_bytes;
 
     float acc[TM][LIVE];
@@ -119,10 +122,11 @@ k_mmq(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, const float 
                     for (int s = 0; s < G; s++) {
                         const int64_t sb = SUBS * j + g + s;
                         ax[t][s] = __builtin_amdgcn_raw_buffer_load_b128(
-                            xr, (uint32_t)((TILE * t + col) * K + 32 * sb + 16 * h), 0, 0);
+                            xr, (uint32_t)((sb * Mp + mt + col) * SB + 16 * h), 0, 0);
 #pragma unroll
                         for (int q = 0; q < LIVE / 4; q++)
-                            dx[t][s][q] = *reinterpret_cast<const float4 *>(dp + sb * Mp + mt + 4 * h + 8 * q);
+                            dx[t][s][q] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                                dr, (uint32_t)((sb * Mp + mt + 4 * h + 8 * q) * 4), 0, 0));
                     }
                 }
             }
@@ -229,11 +233,10 @@ void launch_tm(const uint8_t *W, const XPlanes &x, float *out, int64_t N, int kw
 MmqPlan mmq_plan(int64_t M, int64_t N, int64_t K)
 {
     MmqPlan p;
-    if (M <= TILE) {
-        p.dp = mmq_dec_plan(M, N, K);
-        if (p.dp.ok) {
-            p.dec = true;
-            p.workspace_bytes = p.dp.workspace_bytes;
+    if (M <= TILE && tune_override().mmv != 0) {
+        p.vp = mmv_plan(M, N, K, device_cus());
+        if (p.vp.ok) {
+            p.mmv = true;
             return p;
         }
     }
@@ -260,12 +263,18 @@ MmqPlan mmq_plan(int64_t M, int64_t N, int64_t K)
 }
 
 hipError_t launch_mmq(const void *Wv, const XPlanes &x, float *Y, int64_t N, void *workspace,
-                      hipStream_t s)
+                      bool y_zeroed, hipStream_t s)
 {
     const uint8_t *W = (const uint8_t *)Wv;
     const MmqPlan p = mmq_plan(x.M, N, x.K);
-    if (p.dec)
-        return launch_mmq_dec(Wv, x, Y, N, workspace, p.dp, s);
+    if (p.mmv) {
+        if (p.vp.zero_y && !y_zeroed) {
+            const hipError_t e = launch_zero(Y, x.M * N, s);
+            if (e != hipSuccess)
+                return e;
+        }
+        return launch_mmv(Wv, x, Y, N, p.vp, s);
+    }
     if (p.ks > 1 && workspace == nullptr)
         return hipErrorInvalidValue;
     float *out = p.ks > 1 ? (float *)workspace : Y;

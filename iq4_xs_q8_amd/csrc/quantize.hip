@@ -13,6 +13,8 @@
 // the block reductions are three butterfly steps inside an 8-lane group.
 #include "common.hpp"
 
+#include <algorithm>
+
 namespace iq4xs {
 namespace {
 
@@ -39,6 +41,23 @@ __device__ __forceinline__ int plane_pos(int t)
     return 4 * t + delta;
 }
 
+// yz[0..nz) = 0 over a grid of `stride` threads (yz 16-byte aligned).
+__device__ __forceinline__ void zero_range(float *yz, int64_t nz, int64_t tid, int64_t stride)
+{
+    if (yz == nullptr)
+        return;
+    const int64_t n4 = nz >> 2;
+    for (int64_t i = tid; i < n4; i += stride)
+        reinterpret_cast<float4 *>(yz)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (tid < (nz & 3))
+        yz[4 * n4 + tid] = 0.0f;
+}
+
+__global__ void __launch_bounds__(256) k_zero(float *__restrict__ y, int64_t n)
+{
+    zero_range(y, n, (int64_t)blockIdx.x * blockDim.x + threadIdx.x, (int64_t)gridDim.x * blockDim.x);
+}
+
 __device__ __forceinline__ int quant1(float x, float d)
 {
     if (d == 0.0f)
@@ -52,13 +71,11 @@ __device__ __forceinline__ int quant1(float x, float d)
 // them through buffer descriptors that stop at row M.
 __global__ void __launch_bounds__(256)
 k_quantize(const float *__restrict__ X, uint8_t *__restrict__ Xq, int8_t *__restrict__ qp,
-           float *__restrict__ dp, uint32_t *__restrict__ cnt, uint16_t *__restrict__ Xbf, int64_t M,
-           int64_t Mrows, int64_t Mp, int64_t K)
+           float *__restrict__ dp, float *__restrict__ yz, int64_t nz, uint16_t *__restrict__ Xbf,
+           int64_t M, int64_t Mrows, int64_t Mp, int64_t K)
 {
     const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (cnt != nullptr)
-        for (int64_t i = tid; i < CNT_MAX; i += (int64_t)gridDim.x * blockDim.x)
-            cnt[i] = 0;
+    zero_range(yz, nz, tid, (int64_t)gridDim.x * blockDim.x);
     const int64_t nblk_row = K / SB;
     const int64_t blk = tid >> 3;                 // global Q8_1 block index
     const int t = (int)(tid & 7);                 // lane within the block
@@ -95,7 +112,7 @@ k_quantize(const float *__restrict__ X, uint8_t *__restrict__ Xq, int8_t *__rest
                                                ((uint32_t)__builtin_bit_cast(uint16_t, s16) << 16);
     }
     if (qp != nullptr) {
-        *reinterpret_cast<uint32_t *>(qp + m * K + b * SB + plane_pos(t)) = qword;
+        *reinterpret_cast<uint32_t *>(qp + (b * Mp + m) * SB + plane_pos(t)) = qword;
         if (t == 0)
             dp[b * Mp + m] = dst;
     }
@@ -110,13 +127,11 @@ k_quantize(const float *__restrict__ X, uint8_t *__restrict__ Xq, int8_t *__rest
 // k_quantize.
 __global__ void __launch_bounds__(256)
 k_q8_1_convert(const uint8_t *__restrict__ Xq, int8_t *__restrict__ qp, float *__restrict__ dp,
-               uint32_t *__restrict__ cnt, uint16_t *__restrict__ Xbf, int64_t M, int64_t Mrows,
+               float *__restrict__ yz, int64_t nz, uint16_t *__restrict__ Xbf, int64_t M, int64_t Mrows,
                int64_t Mp, int64_t K)
 {
     const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (cnt != nullptr)
-        for (int64_t i = tid; i < CNT_MAX; i += (int64_t)gridDim.x * blockDim.x)
-            cnt[i] = 0;
+    zero_range(yz, nz, tid, (int64_t)gridDim.x * blockDim.x);
     const int64_t nblk_row = K / SB;
     const int64_t blk = tid >> 3;
     const int t = (int)(tid & 7);
@@ -131,7 +146,7 @@ k_q8_1_convert(const uint8_t *__restrict__ Xq, int8_t *__restrict__ qp, float *_
     }
     const float dst = half_bits_to_float(head & 0xFFFFu);
     if (qp != nullptr) {
-        *reinterpret_cast<uint32_t *>(qp + m * K + b * SB + plane_pos(t)) = qword;
+        *reinterpret_cast<uint32_t *>(qp + (b * Mp + m) * SB + plane_pos(t)) = qword;
         if (t == 0)
             dp[b * Mp + m] = dst;
     }
@@ -146,28 +161,38 @@ k_q8_1_convert(const uint8_t *__restrict__ Xq, int8_t *__restrict__ qp, float *_
 
 }  // namespace
 
+hipError_t launch_zero(float *y, int64_t n, hipStream_t s)
+{
+    if (n <= 0)
+        return hipSuccess;
+    const int64_t n4 = (n + 3) / 4;
+    const int64_t grid = std::min<int64_t>((n4 + 255) / 256, 2048);
+    hipLaunchKernelGGL(k_zero, dim3((unsigned)grid), dim3(256), 0, s, y, n);
+    return hipGetLastError();
+}
+
 hipError_t launch_quantize(const float *X, void *Xq, const XPlanes *planes, uint16_t *Xbf,
-                           int64_t M, int64_t K, hipStream_t s)
+                           int64_t M, int64_t K, hipStream_t s, float *yz, int64_t nz)
 {
     const int64_t Mrows = M;
     const int64_t threads = Mrows * (K / 4);
     const int64_t grid = (threads + 255) / 256;
     hipLaunchKernelGGL(k_quantize, dim3((unsigned)grid), dim3(256), 0, s, X, (uint8_t *)Xq,
                        planes ? planes->qp : nullptr, planes ? planes->dp : nullptr,
-                       planes ? planes->cnt : nullptr, Xbf, M, Mrows,
+                       yz, nz, Xbf, M, Mrows,
                        planes ? planes->Mp : M, K);
     return hipGetLastError();
 }
 
 hipError_t launch_q8_1_convert(const void *Xq, const XPlanes *planes, uint16_t *Xbf, int64_t M,
-                              int64_t K, hipStream_t s)
+                              int64_t K, hipStream_t s, float *yz, int64_t nz)
 {
     const int64_t Mrows = M;
     const int64_t threads = Mrows * (K / 4);
     const int64_t grid = (threads + 255) / 256;
     hipLaunchKernelGGL(k_q8_1_convert, dim3((unsigned)grid), dim3(256), 0, s, (const uint8_t *)Xq,
                        planes ? planes->qp : nullptr, planes ? planes->dp : nullptr,
-                       planes ? planes->cnt : nullptr, Xbf, M, Mrows,
+                       yz, nz, Xbf, M, Mrows,
                        planes ? planes->Mp : M, K);
     return hipGetLastError();
 }
