@@ -66,6 +66,52 @@ __device__ __forceinline__ void expand8(uint32_t w0, uint32_t w1, uint32_t out[4
     out[3] = lut4(w1 >> 4);
 }
 
+// Split codebook: kvalues[x] = KL[x & 7] + kh(x ^ 13), where kh(s) is what
+// v_perm_b32 returns for selector s over the table KH: KH[s] for s < 8, the
+// sign byte of KH[1|3|5|7] (0x00: all are positive) for s = 8..11, 0x00 for
+// 12 and 0xFF (-1) for 13..15.  x ^ 13 maps x = 8..15 onto 0..7 and gives
+// x = 0, 2, 3 the value -1, which KL absorbs (KL[0] = -126 where kvalues[0]
+// = -127).  Both parts fit int8, so a dot product with the codebook values is
+// the sum of two dot products with two byte-permute lookups, one selector
+// op each: no per-byte select between two half-tables.
+constexpr int8_t KL[8] = {-126, -104, -82, -64, -49, -35, -22, -10};
+constexpr int8_t KH[8] = {104, 102, 123, 111, 117, 127, 102, 107};
+constexpr int perm_byte(const int8_t *t8, int sel)
+{
+    return sel >= 13 ? -1 : sel == 12 ? 0 : sel >= 8 ? (t8[2 * (sel - 8) + 1] < 0 ? -1 : 0) : t8[sel];
+}
+constexpr bool split_codebook_ok()
+{
+    for (int x = 0; x < 16; x++)
+        if (KL[x & 7] + perm_byte(KH, x ^ 13) != KVALUES[x])
+            return false;
+    return true;
+}
+static_assert(split_codebook_ok(), "split codebook");
+constexpr uint32_t word4(const int8_t *b)
+{
+    return (uint32_t)(uint8_t)b[0] | ((uint32_t)(uint8_t)b[1] << 8) | ((uint32_t)(uint8_t)b[2] << 16) |
+           ((uint32_t)(uint8_t)b[3] << 24);
+}
+constexpr uint32_t KL0 = word4(KL), KL1 = word4(KL + 4), KH0 = word4(KH), KH1 = word4(KH + 4);
+
+// Four indices (bits 0-3 of each byte of t; bits 4-7 ignored) -> the two
+// int8 parts of their codebook values.
+__device__ __forceinline__ void lut4_split(uint32_t t, uint32_t &lo, uint32_t &hi)
+{
+    lo = __builtin_amdgcn_perm(KL1, KL0, t & 0x07070707u);
+    hi = __builtin_amdgcn_perm(KH1, KH0, (t & 0x0F0F0F0Fu) ^ 0x0D0D0D0Du);
+}
+
+// expand8 as two parts: a[i] + b[i] (bytewise, as integers) = out[i] of expand8.
+__device__ __forceinline__ void expand8_split(uint32_t w0, uint32_t w1, uint32_t a[4], uint32_t b[4])
+{
+    lut4_split(w0, a[0], b[0]);
+    lut4_split(w1, a[1], b[1]);
+    lut4_split(w0 >> 4, a[2], b[2]);
+    lut4_split(w1 >> 4, a[3], b[3]);
+}
+
 __device__ __forceinline__ float half_bits_to_float(uint32_t h16)
 {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)h16);
