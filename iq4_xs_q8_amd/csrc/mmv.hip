@@ -16,15 +16,18 @@
 //    workgroups: every compute unit gets the same work whatever the shape.
 //  * A run is walked in chunks of up to CH super-blocks of one tile, chunk
 //    windows starting at even super-blocks (with K/256 even, every window is
-//    16-byte aligned and ends inside its row).  The list of chunks is worked
-//    out once per workgroup, by one wavefront, into LDS.
+//    16-byte aligned and ends inside its row).  Every wavefront walks the
+//    chunk sequence itself with a scalar cursor.
 //  * A chunk's weights (32 rows x up to CH*136 contiguous bytes per row) and
 //    the activations of its sub-blocks (one contiguous range of the
-//    sub-block-major planes) are copied to LDS with 16-byte loads that follow
-//    the memory layout: every HBM access is a long contiguous run and every
-//    load instruction moves 1 KB.  The first wavefronts copy weights, the
-//    others activations and scales.  Two register sets carry the copies of
-//    the next two chunks while the current one is computed.
+//    sub-block-major planes) go straight from memory into one of NBUF LDS
+//    buffers with 16-byte buffer loads that write LDS (no register staging):
+//    each load instruction fills 1 KB of the buffer, its lanes reading the
+//    global pieces that belong there, so every HBM access is a long run of
+//    whole rows.  The loads of a chunk are issued NBUF-1 chunks ahead of its
+//    use; a step waits for its own loads of the chunk to land, meets the other
+//    wavefronts at one barrier, issues the loads of the chunk NBUF-1 ahead into
+//    the buffer freed by the barrier, then computes.
 //  * Sixteen wavefronts compute: wavefront w takes sub-block w%8 of the
 //    chunk's super-blocks w/8, w/8+2, ... from LDS (the 8 index bytes and
 //    header of its lane's row, the 16 activation bytes of its lane's row;
@@ -37,6 +40,7 @@
 #include "common.hpp"
 
 #include <type_traits>
+#include <utility>
 
 namespace iq4xs {
 namespace {
@@ -50,7 +54,8 @@ constexpr int NT = 64 * NW;                // threads per workgroup
 constexpr int PAR = NW / SUBS;             // wavefronts per sub-block
 constexpr int BUFFER_FLAGS = 0x00020000;   // raw buffer resource, gfx9 family
 constexpr uint32_t OOB = 0x80000000u;      // buffer offset past every range: loads return 0
-constexpr int MAX_CHUNKS = 128;            // chunks of one workgroup's run (checked by the plan)
+
+constexpr int round_up_c(int x, int a) { return (x + a - 1) / a * a; }
 
 // LDS row stride of a weight chunk: CH*136 bytes rounded up to an odd number
 // of 16-byte units, so that the 32 rows of an MFMA operand read spread over
@@ -61,42 +66,88 @@ constexpr int wrow_bytes(int ch)
     return 16 * (u % 2 ? u : u + 1);
 }
 
-constexpr int chunk_sb(int live) { return live <= 4 ? 8 : live == 8 ? 4 : 2; }
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8): LDS operations done and at most n vector memory
+// operations of this wavefront outstanding; or LDS operations done only.
+constexpr int wait_vm_lds(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
+constexpr int WAIT_LDS = 15 | (3 << 14) | (7 << 4);
 
-// LIVE result registers, activation rows padded to MPC (>= Mp) in LDS.
-template <int LIVE, int MPC>
-struct Layout {
-    static constexpr int CH = chunk_sb(LIVE);
-    static_assert(CH % PAR == 0, "every wavefront gets the same number of super-blocks");
+// LDS area I of SZ bytes of the calling kernel.
+template <int I, int SZ>
+__device__ __forceinline__ char *lds_area()
+{
+    __shared__ __attribute__((aligned(16))) char a[SZ];
+    return a;
+}
+
+template <int... I, class F>
+__device__ __forceinline__ void static_for(std::integer_sequence<int, I...>, F &&f)
+{
+    (f(std::integral_constant<int, I>()), ...);
+}
+
+// One 16-byte-per-lane buffer load that writes LDS: lane i's 16 bytes from
+// rsrc at voffset land at lds_dst + 16*i (zeros when voffset is out of
+// range).  Written as assembly so that the compiler neither waits for these
+// loads by itself (it would make every LDS read wait for all of them, also
+// for the loads into other buffers) nor moves memory operations across them;
+// the kernel waits for them explicitly.  M0 holds the LDS address; the kernel
+// uses M0 for nothing else.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, const char *lds_dst, uint32_t voffset)
+{
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_dst);
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(m0), "v"(voffset), "s"(rsrc)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// A barrier that neither waits for the loads in flight nor lets the compiler
+// move memory operations across it (the caller waits for what it needs).
+__device__ __forceinline__ void raw_barrier()
+{
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// LIVE result registers, activation rows padded to MPC (>= Mp) in LDS, CH
+// super-blocks per chunk, NBUF chunk buffers.
+template <int LIVE_, int MPC_, int CH_, int NBUF_>
+struct Cfg {
+    static constexpr int LIVE = LIVE_, MPC = MPC_, CH = CH_, NBUF = NBUF_;
     static constexpr int WROW = wrow_bytes(CH);
-    // one chunk buffer: weights [32][WROW], activations [CH*8][Mp][32], a
-    // 32-byte zero row (the operand of rows >= M), scales [CH*8][Mp] (+ slack
-    // for the rows a lane reads past Mp)
-    static constexpr int W_BYTES = TILE * WROW;
-    static constexpr int A_BYTES = CH * SUBS * MPC * SB;
-    static constexpr int Z_OFF = W_BYTES + A_BYTES;
-    static constexpr int D_OFF = Z_OFF + 32;
-    static constexpr int D_BYTES = CH * SUBS * MPC * 4 + 32 * 4;
-    static constexpr int BUF = D_OFF + D_BYTES;
-    static constexpr int RED = NW * LIVE * 64 * 4;                            // partial tiles
-    static constexpr int SCHED = 2 * BUF + RED;                               // chunk list, count
-    static constexpr int SINK = SCHED + MAX_CHUNKS * 16 + 16;                 // 64 x 16 bytes
-    static constexpr int TOTAL = SINK + 64 * 16;
-    // The copy of a chunk is cut into jobs of one wavefront load (64 lanes x
-    // 16 bytes): JW jobs of weight pieces (32 rows x CH*136 bytes), JQ of
-    // activation pieces, JD of scale pieces.  Every wavefront issues SLOTS
-    // loads per chunk: wavefronts 0..WA-1 take the weight jobs, the others the
-    // activation jobs and then the scale jobs.
     static constexpr int W_PR = CH * WBLK / 16;                               // pieces per row
-    static constexpr int W_PIECES = TILE * W_PR;
-    static constexpr int JW = (W_PIECES + 63) / 64;
-    static constexpr int JQ = (CH * SUBS * MPC * SB / 16 + 63) / 64;
-    static constexpr int JD = (CH * SUBS * MPC * 4 / 16 + 63) / 64;
+    // one chunk buffer: weights [32][WROW] (padded to whole KB), activations
+    // [CH*8][Mp][32], scales [CH*8][Mp] (padded to whole KB), 1 KB that load
+    // slots without a job fill, a 32-byte zero row (the operand of rows >= M)
+    // and slack for the scales a lane reads past the last sub-block's rows
+    static constexpr int W_BYTES = round_up_c(TILE * WROW, 1024);
+    static constexpr int A_OFF = W_BYTES, A_BYTES = CH * SUBS * MPC * SB;
+    static constexpr int D_OFF = A_OFF + A_BYTES, D_BYTES = round_up_c(CH * SUBS * MPC * 4, 1024);
+    static constexpr int DUMP = D_OFF + D_BYTES;
+    static constexpr int Z_OFF = DUMP + 1024;
+    static constexpr int BUF = Z_OFF + 32 + 128;
+    static constexpr int RED = NW * LIVE * 64 * 4;                            // partial tiles
+    static constexpr int TOTAL = NBUF * BUF + RED;
+    template <int B>
+    static __device__ __forceinline__ char *buf() { return lds_area<B, BUF>(); }
+    static __device__ __forceinline__ float *red() { return reinterpret_cast<float *>(lds_area<-1, RED>()); }
+    // A chunk is copied by load jobs of 1 KB of a buffer each: JW of weights,
+    // JQ of activations, JD of scales.  Every wavefront issues SLOTS loads
+    // per chunk: wavefronts 0..WA-1 take the weight jobs, the others the
+    // activation jobs and then the scale jobs; slots left over load nothing
+    // into the dump area.
+    static constexpr int JW = W_BYTES / 1024, JQ = A_BYTES / 1024, JD = D_BYTES / 1024;
     static constexpr int SLOTS = (JW + JQ + JD + NW - 1) / NW;
     static constexpr int WA = (JW + SLOTS - 1) / SLOTS;
-    static_assert(WA + (JQ + JD + SLOTS - 1) / SLOTS <= NW, "copy jobs fit the wavefronts");
-    static_assert(CH * WBLK % 16 == 0, "whole 16-byte pieces per row");
-    static_assert(TOTAL <= 160 * 1024 && TOTAL % 16 == 0 && BUF % 16 == 0, "LDS budget");
+    static_assert(A_BYTES % 1024 == 0 && BUF % 16 == 0, "whole 1 KB load jobs, aligned buffers");
+    static_assert(WA + (JQ + JD + SLOTS - 1) / SLOTS <= NW, "load jobs fit the wavefronts");
+    static_assert(CH % PAR == 0 && CH % 2 == 0, "every wavefront gets the same super-blocks");
+    static_assert(NBUF >= 2 && TOTAL <= 160 * 1024, "LDS budget");
 };
 
 // Result register r of lane (col, h) holds row 8*(r/4) + 4*h + r%4.
@@ -111,62 +162,54 @@ __device__ __forceinline__ void epilogue(const v16i &D, float sw, const float4 *
     }
 }
 
-// The chunks of the run [ua, ub) in order: {t, j0, cl, flags}, flags bit 0 =
-// the tile's units end with this chunk, bit 1 = the tile belongs to this
-// workgroup alone.  Returns the number of chunks.
-__device__ int chunk_list(v4i *out, int ua, int ub, int nb, int ch)
-{
-    int u = ua, t = ua / nb, j = ua - t * nb, n = 0;
-    while (u < ub && n < MAX_CHUNKS) {
-        int l = ub - u;
-        l = l < nb - j ? l : nb - j;
-        const int wl = (j & ~1) + ch - j;
-        l = l < wl ? l : wl;
-        const bool ends = j + l == nb || u + l == ub;
-        const bool owned = t * nb >= ua && (t + 1) * nb <= ub;
-        out[n++] = v4i{t, j, l, (ends ? 1 : 0) | (owned ? 2 : 0)};
-        u += l;
-        j += l;
-        if (j == nb) {
-            j = 0;
-            t++;
+// A chunk: tile t, super-blocks j0..j0+cl-1 (cl = 0: past the run), flags
+// bit 0 = the tile's units end with it, bit 1 = the tile belongs to this
+// workgroup alone.
+struct Chunk {
+    int t, j0, cl, flags;
+};
+
+// Walks the run [ua, ub) of units in chunks (all values wavefront-uniform).
+struct Cursor {
+    int u, t, j, ua, ub, nb;
+    __device__ Chunk next(int ch)
+    {
+        Chunk c{t, j, 0, 0};
+        if (u < ub) {
+            int l = ub - u;
+            l = l < nb - j ? l : nb - j;
+            const int wl = (j & ~1) + ch - j;
+            l = l < wl ? l : wl;
+            const bool ends = j + l == nb || u + l == ub;
+            const bool owned = t * nb >= ua && (t + 1) * nb <= ub;
+            c.cl = l;
+            c.flags = (ends ? 1 : 0) | (owned ? 2 : 0);
+            u += l;
+            j += l;
+            if (j == nb) {
+                j = 0;
+                t++;
+            }
         }
+        return c;
     }
-    return n;
-}
+};
 
 // LIVE: result registers that can hold a real row: 1, 2, 3, 4 (rows 0..LIVE-1
 // in lanes 0-31; LIVE = 4 also serves M <= 8 through lanes 32-63), 8 (M <= 16),
 // 16 (M <= 32).  MPC: a bound on the padded activation rows Mp.
-template <int LIVE, int MPC>
+template <class C>
 __global__ void __launch_bounds__(NT, 1)
 k_mmv(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__restrict__ Y, int M, int N,
       int K, int Mp, int nb, int U, int G)
 {
-    using L = Layout<LIVE, MPC>;
-    constexpr int CH = L::CH;
-    extern __shared__ __attribute__((aligned(16))) char lds[];
+    constexpr int LIVE = C::LIVE, CH = C::CH, NBUF = C::NBUF, SLOTS = C::SLOTS;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int s = wave % SUBS, par = wave / SUBS;             // sub-block, first super-block
     const int col = lane & 31, h = lane >> 5;
     const int ua = (int)((int64_t)U * blockIdx.x / G), ub = (int)((int64_t)U * (blockIdx.x + 1) / G);
     const uint32_t row_bytes = (uint32_t)nb * WBLK;
-    v4i *sched = reinterpret_cast<v4i *>(lds + L::SCHED);
-
-    // the chunk list (one wavefront) and the two zero activation rows
-    int n_chunks = 0;
-    if (wave == 0) {
-        if (lane == 0)
-            n_chunks = chunk_list(sched, ua, ub, nb, CH);
-        n_chunks = __shfl(n_chunks, 0);
-        if (lane < 16)
-            reinterpret_cast<uint32_t *>(lds + (lane >> 3) * L::BUF + L::Z_OFF)[lane & 7] = 0u;
-        if (lane == 0)
-            reinterpret_cast<int *>(lds + L::SCHED + MAX_CHUNKS * 16)[0] = n_chunks;
-    }
-    __syncthreads();
-    n_chunks = __builtin_amdgcn_readfirstlane(reinterpret_cast<const int *>(lds + L::SCHED + MAX_CHUNKS * 16)[0]);
 
     // ---- chunk copy: fixed per-lane geometry ------------------------------
     // descriptors over the whole weight matrix and over both activation planes
@@ -177,99 +220,78 @@ k_mmv(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__res
         __builtin_amdgcn_make_buffer_rsrc((void *)W, (short)0, (int)((uint32_t)N * row_bytes), BUFFER_FLAGS);
     const __amdgpu_buffer_rsrc_t xr =
         __builtin_amdgcn_make_buffer_rsrc((void *)qp, (short)0, dp_at + Mp * (K / SB) * 4, BUFFER_FLAGS);
-    const bool w_group = wave < L::WA;                        // (uniform)
-    const __amdgpu_buffer_rsrc_t rsrc = w_group ? wr : xr;
-    const int sink = L::SINK + 16 * lane;
-    // per slot: this lane's piece offset inside the chunk (global bytes), its
-    // piece number inside its row (weights) or plane range (activations,
-    // scales), whether it is a scale piece, and its LDS target per buffer
-    uint32_t p_go[L::SLOTS];
-    int p_id[L::SLOTS], p_st[2][L::SLOTS];
-    bool p_scale[L::SLOTS];
-    const int qa_full = CH * SUBS * Mp * SB / 16, da_full = CH * SUBS * Mp * 4 / 16;
+    const bool w_group = wave < C::WA;                        // (uniform)
+    // per slot: the LDS offset its load fills inside a buffer (uniform), whether it holds scales (uniform), this lane's global
+    // offset relative to the chunk's base, and the key that decides whether
+    // the lane's piece belongs to the chunk
+    int p_dst[SLOTS];
+    bool p_scale[SLOTS];
+    uint32_t p_go[SLOTS];
+    int p_key[SLOTS];
 #pragma unroll
-    for (int k = 0; k < L::SLOTS; k++) {
+    for (int k = 0; k < SLOTS; k++) {
         if (w_group) {
-            const int p = 64 * (wave * L::SLOTS + k) + lane;
-            const int r = p / L::W_PR, c = p - r * L::W_PR;
-            const bool ok = p < L::W_PIECES;
-            p_go[k] = ok ? (uint32_t)r * row_bytes + 16 * c : OOB;
-            p_id[k] = ok ? c : 1 << 20;
+            const int job = wave * SLOTS + k;
+            const int at = 1024 * job + 16 * lane;             // byte of the weight area
+            const int r = at / C::WROW, c = (at - r * C::WROW) / 16;
+            const bool ok = job < C::JW && r < TILE && c < C::W_PR;
+            p_dst[k] = job < C::JW ? 1024 * job : C::DUMP;
             p_scale[k] = false;
-            p_st[0][k] = ok ? r * L::WROW + 16 * c : sink;
-            p_st[1][k] = ok ? L::BUF + r * L::WROW + 16 * c : sink;
+            p_go[k] = ok ? (uint32_t)r * row_bytes + 16 * c : OOB;
+            p_key[k] = ok ? 16 * c + 15 : -(1 << 30);          // piece bytes [16c, 16c+16)
         } else {
-            const int job = (wave - L::WA) * L::SLOTS + k;    // activation jobs first, then scales
-            const bool isq = job < L::JQ;
-            const int p = 64 * (isq ? job : job - L::JQ) + lane;
-            const bool ok = isq ? p < qa_full : p < da_full;
-            p_go[k] = ok ? (isq ? 16u * p : (uint32_t)dp_at + 16u * p) : OOB;
-            p_id[k] = ok ? p : 1 << 20;
-            p_scale[k] = !isq;
-            const int at = isq ? L::W_BYTES + 16 * p : L::D_OFF + 16 * p;
-            p_st[0][k] = ok ? at : sink;
-            p_st[1][k] = ok ? L::BUF + at : sink;
+            const int job = (wave - C::WA) * SLOTS + k;       // activation jobs, then scales
+            const bool isq = job < C::JQ, isd = !isq && job < C::JQ + C::JD;
+            const int at = 1024 * (isq ? job : job - C::JQ) + 16 * lane;
+            p_dst[k] = isq ? C::A_OFF + 1024 * job : isd ? C::D_OFF + 1024 * (job - C::JQ) : C::DUMP;
+            p_scale[k] = isd;
+            p_go[k] = isq || isd ? (uint32_t)at : OOB;
+            p_key[k] = isq || isd ? at : 1 << 30;
         }
     }
-
-    // two register sets: the copies of two chunks are in flight at once
-    v4i creg[2][L::SLOTS];
-    // Issue the loads of chunk c into register set S.  The weight window
-    // starts at super-block j0 & ~1; pieces holding none of super-blocks
-    // j0..j0+cl-1, and activation or scale pieces past the chunk, are not
-    // read.  Every wavefront issues SLOTS loads per chunk, also past the last
-    // chunk (all out of range then), so the wait counts are the same on every
-    // path.
-    auto load_chunk = [&](auto set, int c) {
-        constexpr int S = decltype(set)::value;
-        v4i info = v4i{0, 0, 0, 0};
-        if (c < n_chunks)
-            info = sched[c];
-        const int t = __builtin_amdgcn_readfirstlane(info[0]);
-        const int j0 = __builtin_amdgcn_readfirstlane(info[1]);
-        const int cl = __builtin_amdgcn_readfirstlane(info[2]);
-        const int je = j0 & ~1;
-        // weights: piece c of a row holds bytes [16c, 16c+16) of the window;
-        // it is read when they meet the chunk's bytes [lo, hi).  Activations
-        // and scales: pieces below the chunk's count are read.  (One load
-        // instruction per slot for both groups: no branch around the loads.)
-        const int lo = (j0 - je) * WBLK, hi = lo + cl * WBLK;
-        const uint32_t wbase = (uint32_t)t * TILE * row_bytes + je * WBLK;
-        const int qa = cl * SUBS * Mp * SB / 16, da = cl * SUBS * Mp * 4 / 16;
-        const uint32_t qbase = j0 * SUBS * Mp * SB, dbase = j0 * SUBS * Mp * 4;
+    // Issue the loads of chunk c into buffer B: weight pieces holding none of
+    // the chunk's super-blocks (the window starts at j0 & ~1), and activation
+    // or scale pieces past the chunk, read nothing and fill zeros.  Every
+    // wavefront issues SLOTS loads per chunk, also for chunks past the run,
+    // so the wait counts are the same on every path.
+    auto issue = [&](const Chunk &c, auto bc) {
+        char *buf = C::template buf<decltype(bc)::value>();
+        if (w_group) {
+            const int lo = (c.j0 & 1) * WBLK, hi = lo + c.cl * WBLK;
+            const uint32_t base = (uint32_t)c.t * TILE * row_bytes + (c.j0 & ~1) * WBLK;
 #pragma unroll
-        for (int k = 0; k < L::SLOTS; k++) {
-            const bool need = w_group ? (uint32_t)(16 * p_id[k] + 15 - lo) < (uint32_t)(hi - lo + 15)
-                                      : p_id[k] < (p_scale[k] ? da : qa);
-            const uint32_t base = w_group ? wbase : p_scale[k] ? dbase : qbase;
-            creg[S][k] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
-                                                     rsrc, need ? p_go[k] + base : OOB, 0, 0));
+            for (int k = 0; k < SLOTS; k++) {
+                const bool need = (uint32_t)(p_key[k] - lo) < (uint32_t)(hi - lo + 15);
+                load_lds16(wr, buf + p_dst[k], need ? p_go[k] + base : OOB);
+            }
+        } else {
+            const int qn = c.cl * SUBS * Mp * SB, dn = c.cl * SUBS * Mp * 4;
+            const uint32_t qb = (uint32_t)c.j0 * SUBS * Mp * SB, db = (uint32_t)dp_at + c.j0 * SUBS * Mp * 4;
+#pragma unroll
+            for (int k = 0; k < SLOTS; k++) {
+                const bool need = p_key[k] < (p_scale[k] ? dn : qn);
+                load_lds16(xr, buf + p_dst[k], need ? p_go[k] + (p_scale[k] ? db : qb) : OOB);
+            }
         }
-        // keep the sets' loads in issue order: a set is always waited for
-        // while the one issued after it stays in flight
-        __builtin_amdgcn_sched_barrier(0);
-    };
-    // (lanes without a piece store to their sink slot)
-    auto store_chunk = [&](auto set, auto bufc) {
-        constexpr int S = decltype(set)::value, buf = decltype(bufc)::value;
-#pragma unroll
-        for (int k = 0; k < L::SLOTS; k++)
-            *reinterpret_cast<v4i *>(lds + p_st[buf][k]) = creg[S][k];
     };
 
     float acc[LIVE];
 #pragma unroll
     for (int r = 0; r < LIVE; r++)
         acc[r] = 0.0f;
-    float *red = reinterpret_cast<float *>(lds + 2 * L::BUF);
+    float *red = C::red();
+    // Sum the wavefronts' partial tiles (the barrier orders the partials'
+    // writes before the reads; the reads are done before this wavefront
+    // reaches the next step's barrier, which every later flush's writes
+    // follow).
     auto flush = [&](int t, bool owned) {
-        __syncthreads();                                      // red is free (previous flush read)
 #pragma unroll
         for (int r = 0; r < LIVE; r++) {
             red[(wave * LIVE + r) * 64 + lane] = acc[r];
             acc[r] = 0.0f;
         }
-        __syncthreads();
+        __builtin_amdgcn_s_waitcnt(WAIT_LDS);
+        raw_barrier();
         for (int slot = tid; slot < LIVE * 64; slot += NT) {
             const int r = slot >> 6, l2 = slot & 63;
             float v = red[r * 64 + l2];
@@ -288,108 +310,116 @@ k_mmv(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__res
     };
 
     // per-lane LDS read offsets inside a chunk buffer (rows >= M: the zero row)
-    const int w_lane = col * L::WROW;
+    const int w_lane = col * C::WROW;
     const int a_step = col < M ? Mp * SB : 0;
     int a_off[CH / PAR], d_off[CH / PAR];
 #pragma unroll
     for (int i = 0; i < CH / PAR; i++) {
         const int sb = (par + PAR * i) * SUBS + s;            // sub-block within the chunk
-        a_off[i] = (col < M ? L::W_BYTES + col * SB : L::Z_OFF) + 16 * h + sb * a_step;
-        d_off[i] = L::D_OFF + 16 * h + 4 * sb * Mp;
+        a_off[i] = (col < M ? C::A_OFF + col * SB : C::Z_OFF) + 16 * h + sb * a_step;
+        d_off[i] = C::D_OFF + 16 * h + 4 * sb * Mp;
     }
-
-    const std::integral_constant<int, 0> S0;
-    const std::integral_constant<int, 1> S1;
-    const std::integral_constant<int, 0> B0;
-    const std::integral_constant<int, 1> B1;
-    load_chunk(S0, 0);                                        // chunk 0 -> set 0
-    load_chunk(S1, 1);                                        // chunk 1 -> set 1
-    store_chunk(S0, B0);
-    load_chunk(S0, 2);                                        // chunk 2 -> set 0
-    __syncthreads();
-
-    // Compute chunk c from LDS buffer c%2, then move chunk c+1 from register
-    // set (c+1)%2 into the other buffer (its loads were issued two chunks
-    // ago) and reuse the set for chunk c+3.
-    auto step = [&](auto set, auto bufc, int c) {
-        constexpr int buf = decltype(bufc)::value;
-        if (c < n_chunks) {                                   // (uniform; no memory loads inside)
-            const v4i info = sched[c];
-            const int t = __builtin_amdgcn_readfirstlane(info[0]);
-            const int j0 = __builtin_amdgcn_readfirstlane(info[1]);
-            const int n_sb = __builtin_amdgcn_readfirstlane(info[2]);
-            const int flags = __builtin_amdgcn_readfirstlane(info[3]);
-            const char *b = lds + buf * L::BUF;
-            const char *wchunk = b + w_lane + (j0 & 1) * WBLK;  // the window starts at j0 & ~1
+    auto compute = [&](const Chunk &c, auto bc) {
+        const char *B = C::template buf<decltype(bc)::value>();
+        const char *wchunk = B + w_lane + (c.j0 & 1) * WBLK;  // the window starts at j0 & ~1
+        // The I = CH/PAR super-blocks are computed without branches, the ones
+        // past the chunk's end with a zero scale (their LDS reads stay inside
+        // the buffer), in groups of GI whose LDS reads are issued together, so
+        // that reads, lookups and MFMAs of different super-blocks overlap.
+        constexpr int I = CH / PAR, DQ = LIVE >= 4 ? LIVE / 4 : 1;
+        constexpr int GI = LIVE <= 4 ? I : (I < 2 ? I : 2);
 #pragma unroll
-            for (int i = 0; i < CH / PAR; i++) {
-                if (par + PAR * i >= n_sb)                    // (uniform) past the chunk's end
-                    break;
-                const char *wrow = wchunk + (par + PAR * i) * WBLK;
-                const uint2 hdr = *reinterpret_cast<const uint2 *>(wrow);
-                const uint2 q = *reinterpret_cast<const uint2 *>(wrow + QS_OFF + 16 * s + 8 * h);
-                const v4i ax = *reinterpret_cast<const v4i *>(b + a_off[i]);
-                float4 dx[LIVE >= 4 ? LIVE / 4 : 1];
+        for (int g = 0; g < I; g += GI) {
+            uint2 hdr[GI], q[GI];
+            v4i ax[GI];
+            float4 dx[GI][DQ];
 #pragma unroll
-                for (int qd = 0; qd < (LIVE >= 4 ? LIVE / 4 : 1); qd++)
-                    dx[qd] = *reinterpret_cast<const float4 *>(b + d_off[i] + 32 * qd);
+            for (int k = 0; k < GI; k++) {
+                const char *wrow = wchunk + (par + PAR * (g + k)) * WBLK;
+                hdr[k] = *reinterpret_cast<const uint2 *>(wrow);
+                q[k] = *reinterpret_cast<const uint2 *>(wrow + QS_OFF + 16 * s + 8 * h);
+                ax[k] = *reinterpret_cast<const v4i *>(B + a_off[g + k]);
+#pragma unroll
+                for (int qd = 0; qd < DQ; qd++)
+                    dx[k][qd] = *reinterpret_cast<const float4 *>(B + d_off[g + k] + 32 * qd);
+            }
+#pragma unroll
+            for (int k = 0; k < GI; k++) {
                 uint32_t wa[4], wb[4];
-                expand8_split(q.x, q.y, wa, wb);
+                expand8_split(q[k].x, q[k].y, wa, wb);
                 const v4i ba = {(int)wa[0], (int)wa[1], (int)wa[2], (int)wa[3]};
                 const v4i bb = {(int)wb[0], (int)wb[1], (int)wb[2], (int)wb[3]};
                 const v16i zero = {0};
                 const v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(
-                    ax, bb, __builtin_amdgcn_mfma_i32_32x32x32_i8(ax, ba, zero, 0, 0, 0), 0, 0, 0);
-                epilogue<LIVE>(D, sub_scale(hdr.x, hdr.y, s), dx, acc);
+                    ax[k], bb, __builtin_amdgcn_mfma_i32_32x32x32_i8(ax[k], ba, zero, 0, 0, 0), 0, 0, 0);
+                const float sw = par + PAR * (g + k) < c.cl ? sub_scale(hdr[k].x, hdr[k].y, s) : 0.0f;
+                epilogue<LIVE>(D, sw, dx[k], acc);
             }
-            if (flags & 1)                                    // the tile's units end here
-                flush(t, (flags & 2) != 0);
         }
-        store_chunk(set, std::integral_constant<int, buf ^ 1>());   // chunk c+1
-        load_chunk(set, c + 3);                                     // chunk c+3
-        __syncthreads();
+        if (c.flags & 1)                                      // the tile's units end here
+            flush(c.t, (c.flags & 2) != 0);
     };
-    // Two chunks per iteration, the second one possibly past the run (then
-    // only its copy part runs): every iteration issues the same loads.
-    for (int c = 0; c < n_chunks; c += 2) {
-        step(S1, B0, c);                                      // chunk c+1 is in set 1
-        step(S0, B1, c + 1);                                  // chunk c+2 is in set 0
+
+    // the zero rows of the buffers (published by the first step's barrier)
+    if (tid < 8)
+        static_for(std::make_integer_sequence<int, NBUF>(), [&](auto bc) {
+            reinterpret_cast<uint32_t *>(C::template buf<decltype(bc)::value>() + C::Z_OFF)[tid] = 0u;
+        });
+
+    Cursor cur;
+    cur.ua = ua;
+    cur.ub = ub;
+    cur.nb = nb;
+    cur.u = ua;
+    cur.t = ua / nb;
+    cur.j = ua - cur.t * nb;
+    Chunk info[NBUF];
+    static_for(std::make_integer_sequence<int, NBUF - 1>(), [&](auto bc) {
+        info[decltype(bc)::value] = cur.next(CH);
+        issue(info[decltype(bc)::value], bc);
+    });
+    // Step on buffer b: wait for this wavefront's loads of its chunk (the
+    // loads of the NBUF-2 chunks issued after it stay in flight), meet the
+    // other wavefronts (all loads of the chunk have landed, and the buffer
+    // computed last is free), refill that buffer NBUF-1 chunks ahead, compute.
+    auto step = [&](auto bc) {
+        constexpr int b = decltype(bc)::value, nxt = (b + NBUF - 1) % NBUF;
+        if (info[b].cl == 0)
+            return false;                                     // (uniform) the run is done
+        __builtin_amdgcn_s_waitcnt(wait_vm_lds(SLOTS * (NBUF - 2)));
+        raw_barrier();
+        info[nxt] = cur.next(CH);
+        issue(info[nxt], std::integral_constant<int, nxt>());
+        compute(info[b], bc);
+        return true;
+    };
+    for (;;) {
+        if (!step(std::integral_constant<int, 0>()))
+            break;
+        if (!step(std::integral_constant<int, 1>()))
+            break;
+        if constexpr (NBUF > 2)
+            if (!step(std::integral_constant<int, 2 % NBUF>()))
+                break;
+        if constexpr (NBUF > 3)
+            if (!step(std::integral_constant<int, 3 % NBUF>()))
+                break;
     }
+    // no load may still write this workgroup's LDS when it ends
+    __builtin_amdgcn_s_waitcnt(wait_vm_lds(0));
 }
 
-template <int LIVE, int MPC>
-hipError_t launch_l(const uint8_t *W, const XPlanes &x, float *Y, int64_t N, const MmvPlan &p, hipStream_t s)
+template <class C>
+hipError_t launch_c(const uint8_t *W, const XPlanes &x, float *Y, int64_t N, const MmvPlan &p, hipStream_t s)
 {
     const int nb = (int)(x.K / QK);
     const int64_t T = (N + TILE - 1) / TILE;
-    const size_t lds = (size_t)Layout<LIVE, MPC>::TOTAL;
     // (the kernel reads both planes through one descriptor)
-    if ((const char *)x.dp != (const char *)x.qp + x.Mp * x.K || x.Mp > MPC)
+    if ((const char *)x.dp != (const char *)x.qp + x.Mp * x.K || x.Mp > C::MPC)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_mmv<LIVE, MPC>), dim3((unsigned)p.grid), dim3(NT), lds, s, W, x.qp, Y, (int)x.M,
-                       (int)N, (int)x.K, (int)x.Mp, nb, (int)(T * nb), p.grid);
+    hipLaunchKernelGGL((k_mmv<C>), dim3((unsigned)p.grid), dim3(NT), 0, s, W, x.qp, Y, (int)x.M, (int)N,
+                       (int)x.K, (int)x.Mp, nb, (int)(T * nb), p.grid);
     return hipGetLastError();
-}
-
-// Chunks of the longest run (the same rule as chunk_list).
-int64_t max_chunks(int64_t U, int64_t nb, int grid, int ch)
-{
-    int64_t most = 0;
-    for (int g = 0; g < grid; g++) {
-        const int64_t ua = U * g / grid, ub = U * (g + 1) / grid;
-        int64_t u = ua, j = ua % nb, n = 0;
-        while (u < ub) {
-            int64_t l = ub - u;
-            l = l < nb - j ? l : nb - j;
-            const int64_t wl = (j & ~1LL) + ch - j;
-            l = l < wl ? l : wl;
-            u += l;
-            j = (j + l) % nb;
-            n++;
-        }
-        most = n > most ? n : most;
-    }
-    return most;
 }
 
 }  // namespace
@@ -409,8 +439,6 @@ MmvPlan mmv_plan(int64_t M, int64_t N, int64_t K, int cus)
     const int64_t U = T * nb;
     p.grid = (int)(T < cus ? T : cus);
     p.live = M <= 4 ? (int)M : M <= 8 ? 4 : M <= 16 ? 8 : 16;
-    if (max_chunks(U, nb, p.grid, chunk_sb(p.live)) > MAX_CHUNKS)
-        return p;
     p.zero_y = false;
     for (int64_t g = 1; g < p.grid; g++)
         if (U * g / p.grid % nb != 0) {
@@ -428,12 +456,13 @@ hipError_t launch_mmv(const void *Wv, const XPlanes &x, float *Y, int64_t N, con
     if (!p.ok)
         return hipErrorInvalidValue;
     switch (p.live) {
-    case 1: return launch_l<1, 4>(W, x, Y, N, p, s);
-    case 2: return launch_l<2, 4>(W, x, Y, N, p, s);
-    case 3: return launch_l<3, 4>(W, x, Y, N, p, s);
-    case 4: return x.Mp <= 4 ? launch_l<4, 4>(W, x, Y, N, p, s) : launch_l<4, 8>(W, x, Y, N, p, s);
-    case 8: return launch_l<8, 16>(W, x, Y, N, p, s);
-    case 16: return launch_l<16, 32>(W, x, Y, N, p, s);
+    case 1: return launch_c<Cfg<1, 4, 8, 3>>(W, x, Y, N, p, s);
+    case 2: return launch_c<Cfg<2, 4, 8, 3>>(W, x, Y, N, p, s);
+    case 3: return launch_c<Cfg<3, 4, 8, 3>>(W, x, Y, N, p, s);
+    case 4:
+        return x.Mp <= 4 ? launch_c<Cfg<4, 4, 8, 3>>(W, x, Y, N, p, s) : launch_c<Cfg<4, 8, 4, 4>>(W, x, Y, N, p, s);
+    case 8: return launch_c<Cfg<8, 16, 4, 3>>(W, x, Y, N, p, s);
+    case 16: return launch_c<Cfg<16, 32, 2, 3>>(W, x, Y, N, p, s);
     default: return hipErrorInvalidValue;
     }
 }
