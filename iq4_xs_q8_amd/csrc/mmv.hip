@@ -103,7 +103,26 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, const ch
                  : "s"(m0), "v"(voffset), "s"(rsrc)
                  : "memory", "m0");
 }
+// The same with 4 bytes per lane (lds_dst + 4*i): here only to pull lines
+// into the cache ahead of their 16-byte copies.
+__device__ __forceinline__ void touch_lds4(__amdgpu_buffer_rsrc_t rsrc, const char *lds_dst, uint32_t voffset)
+{
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_dst);
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 :
+                 : "s"(m0), "v"(voffset), "s"(rsrc)
+                 : "memory", "m0");
+}
 #pragma clang diagnostic pop
+
+// v from the lane D lanes below in the same row of 16 lanes (0 for the first
+// D lanes of the row).
+template <int D>
+__device__ __forceinline__ float shr_row(float v, std::integral_constant<int, D>)
+{
+    static_assert(D >= 1 && D <= 15, "row shift");
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x110 | D, 0xF, 0xF, true));
+}
 
 // A barrier that neither waits for the loads in flight nor lets the compiler
 // move memory operations across it (the caller waits for what it needs).
@@ -116,36 +135,46 @@ __device__ __forceinline__ void raw_barrier()
 
 // LIVE result registers, activation rows padded to MPC (>= Mp) in LDS, CH
 // super-blocks per chunk, NBUF chunk buffers.
-template <int LIVE_, int MPC_, int CH_, int NBUF_>
+template <int LIVE_, int MPC_, int CH_, int NBUF_, int PF_ = 0>
 struct Cfg {
     static constexpr int LIVE = LIVE_, MPC = MPC_, CH = CH_, NBUF = NBUF_;
+    // PF > 0: the last wavefront copies nothing into the buffers but touches
+    // the weights of the chunks PF ahead of the copies, so that HBM streams
+    // ahead into the cache while the buffers are busy
+    static constexpr int PF = PF_, NL = PF > 0 ? NW - 1 : NW;                // copying wavefronts
+    static constexpr int PF_SEG = (CH * WBLK + 63) / 64 + 1;                 // 64-byte pieces per row
+    static constexpr int CH0 = CH < 2 ? CH : 2;                              // first chunk
     static constexpr int WROW = wrow_bytes(CH);
     static constexpr int W_PR = CH * WBLK / 16;                               // pieces per row
     // one chunk buffer: weights [32][WROW] (padded to whole KB), activations
-    // [CH*8][Mp][32], scales [CH*8][Mp] (padded to whole KB), 1 KB that load
+    // [CH*8][MA][32], scales [CH*8][Mp] (padded to whole KB), 1 KB that load
     // slots without a job fill, a 32-byte zero row (the operand of rows >= M)
     // and slack for the scales a lane reads past the last sub-block's rows
+    // (activations: MA rows per sub-block in LDS, MA >= M)
+    static constexpr int MA = LIVE < 4 ? LIVE : MPC;
     static constexpr int W_BYTES = round_up_c(TILE * WROW, 1024);
-    static constexpr int A_OFF = W_BYTES, A_BYTES = CH * SUBS * MPC * SB;
+    static constexpr int A_OFF = W_BYTES, A_BYTES = CH * SUBS * MA * SB;
     static constexpr int D_OFF = A_OFF + A_BYTES, D_BYTES = round_up_c(CH * SUBS * MPC * 4, 1024);
     static constexpr int DUMP = D_OFF + D_BYTES;
     static constexpr int Z_OFF = DUMP + 1024;
     static constexpr int BUF = Z_OFF + 32 + 128;
-    static constexpr int RED = NW * LIVE * 64 * 4;                            // partial tiles
+    static constexpr int RED = LIVE * 64 * (NW + 1) * 4;                      // partial tiles
     static constexpr int TOTAL = NBUF * BUF + RED;
     template <int B>
     static __device__ __forceinline__ char *buf() { return lds_area<B, BUF>(); }
     static __device__ __forceinline__ float *red() { return reinterpret_cast<float *>(lds_area<-1, RED>()); }
+    static __device__ __forceinline__ char *pf_dump() { return lds_area<-2, 256>(); }
     // A chunk is copied by load jobs of 1 KB of a buffer each: JW of weights,
     // JQ of activations, JD of scales.  Every wavefront issues SLOTS loads
     // per chunk: wavefronts 0..WA-1 take the weight jobs, the others the
     // activation jobs and then the scale jobs; slots left over load nothing
     // into the dump area.
     static constexpr int JW = W_BYTES / 1024, JQ = A_BYTES / 1024, JD = D_BYTES / 1024;
-    static constexpr int SLOTS = (JW + JQ + JD + NW - 1) / NW;
+    static constexpr int SLOTS = (JW + JQ + JD + NL - 1) / NL;
     static constexpr int WA = (JW + SLOTS - 1) / SLOTS;
+    static_assert(NW == 16, "the flush sums 16 partials per output in a row of 16 lanes");
     static_assert(A_BYTES % 1024 == 0 && BUF % 16 == 0, "whole 1 KB load jobs, aligned buffers");
-    static_assert(WA + (JQ + JD + SLOTS - 1) / SLOTS <= NW, "load jobs fit the wavefronts");
+    static_assert(WA + (JQ + JD + SLOTS - 1) / SLOTS <= NL, "load jobs fit the wavefronts");
     static_assert(CH % PAR == 0 && CH % 2 == 0, "every wavefront gets the same super-blocks");
     static_assert(NBUF >= 2 && TOTAL <= 160 * 1024, "LDS budget");
 };
@@ -160,6 +189,33 @@ __device__ __forceinline__ void epilogue(const v16i &D, float sw, const float4 *
                       : (r % 4 == 2) ? dx[r / 4].z : dx[r / 4].w;
         acc[r] += (sw * d) * (float)D[r];
     }
+}
+
+// x / d for 0 <= x < 2^31 and 1 <= d < 2^16: a float reciprocal estimate,
+// refined once, then corrected to the exact quotient (cheap for the uniform
+// values here, unlike a full integer division).
+__device__ __forceinline__ int udiv31(int x, int d)
+{
+    const float rd = __builtin_amdgcn_rcpf((float)d);
+    int q = (int)((float)x * rd);
+    int r = (int)((uint32_t)x - (uint32_t)q * (uint32_t)d);
+    q += (int)((float)r * rd);
+    r = (int)((uint32_t)x - (uint32_t)q * (uint32_t)d);
+    if (r < 0) {
+        q--;
+        r += d;
+    }
+    if (r < 0) {
+        q--;
+        r += d;
+    }
+    if (r >= d) {
+        q++;
+        r -= d;
+    }
+    if (r >= d)
+        q++;
+    return q;
 }
 
 // A chunk: tile t, super-blocks j0..j0+cl-1 (cl = 0: past the run), flags
@@ -201,14 +257,16 @@ struct Cursor {
 template <class C>
 __global__ void __launch_bounds__(NT, 1)
 k_mmv(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__restrict__ Y, int M, int N,
-      int K, int Mp, int nb, int U, int G)
+      int K, int Mp, int nb, int qb, int rb, int G)
 {
     constexpr int LIVE = C::LIVE, CH = C::CH, NBUF = C::NBUF, SLOTS = C::SLOTS;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int s = wave % SUBS, par = wave / SUBS;             // sub-block, first super-block
     const int col = lane & 31, h = lane >> 5;
-    const int ua = (int)((int64_t)U * blockIdx.x / G), ub = (int)((int64_t)U * (blockIdx.x + 1) / G);
+    // this workgroup's run [U*g/G, U*(g+1)/G) of the U = qb*G + rb units
+    const int g = blockIdx.x;
+    const int ua = g * qb + udiv31(g * rb, G), ub = (g + 1) * qb + udiv31((g + 1) * rb, G);
     const uint32_t row_bytes = (uint32_t)nb * WBLK;
 
     // ---- chunk copy: fixed per-lane geometry ------------------------------
@@ -221,9 +279,11 @@ k_mmv(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__res
     const __amdgpu_buffer_rsrc_t xr =
         __builtin_amdgcn_make_buffer_rsrc((void *)qp, (short)0, dp_at + Mp * (K / SB) * 4, BUFFER_FLAGS);
     const bool w_group = wave < C::WA;                        // (uniform)
-    // per slot: the LDS offset its load fills inside a buffer (uniform), whether it holds scales (uniform), this lane's global
-    // offset relative to the chunk's base, and the key that decides whether
-    // the lane's piece belongs to the chunk
+    const bool pf_wave = C::PF > 0 && wave == NW - 1;         // (uniform)
+    // per slot: the LDS offset its load fills inside a buffer and whether it
+    // holds scales (both uniform), this lane's global offset relative to the
+    // chunk's base, and the key that decides whether the lane's piece belongs
+    // to the chunk
     int p_dst[SLOTS];
     bool p_scale[SLOTS];
     uint32_t p_go[SLOTS];
@@ -243,10 +303,14 @@ k_mmv(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__res
             const int job = (wave - C::WA) * SLOTS + k;       // activation jobs, then scales
             const bool isq = job < C::JQ, isd = !isq && job < C::JQ + C::JD;
             const int at = 1024 * (isq ? job : job - C::JQ) + 16 * lane;
+            // activation piece: half `hf` of row m of sub-block sb, whose plane
+            // holds Mp rows per sub-block
+            const int sb = at / (32 * C::MA), m = (at - sb * 32 * C::MA) / 32, hf = (at / 16) & 1;
+            const int qo = (sb * Mp + m) * SB + 16 * hf;
             p_dst[k] = isq ? C::A_OFF + 1024 * job : isd ? C::D_OFF + 1024 * (job - C::JQ) : C::DUMP;
             p_scale[k] = isd;
-            p_go[k] = isq || isd ? (uint32_t)at : OOB;
-            p_key[k] = isq || isd ? at : 1 << 30;
+            p_go[k] = isq ? (uint32_t)qo : isd ? (uint32_t)at : OOB;
+            p_key[k] = isq ? qo : isd ? at : 1 << 30;
         }
     }
     // Issue the loads of chunk c into buffer B: weight pieces holding none of
@@ -256,6 +320,8 @@ k_mmv(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__res
     // so the wait counts are the same on every path.
     auto issue = [&](const Chunk &c, auto bc) {
         char *buf = C::template buf<decltype(bc)::value>();
+        if (pf_wave)
+            return;
         if (w_group) {
             const int lo = (c.j0 & 1) * WBLK, hi = lo + c.cl * WBLK;
             const uint32_t base = (uint32_t)c.t * TILE * row_bytes + (c.j0 & ~1) * WBLK;
@@ -266,12 +332,28 @@ k_mmv(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__res
             }
         } else {
             const int qn = c.cl * SUBS * Mp * SB, dn = c.cl * SUBS * Mp * 4;
-            const uint32_t qb = (uint32_t)c.j0 * SUBS * Mp * SB, db = (uint32_t)dp_at + c.j0 * SUBS * Mp * 4;
+            const uint32_t qbase = (uint32_t)c.j0 * SUBS * Mp * SB, dbase = (uint32_t)dp_at + c.j0 * SUBS * Mp * 4;
 #pragma unroll
             for (int k = 0; k < SLOTS; k++) {
                 const bool need = p_key[k] < (p_scale[k] ? dn : qn);
-                load_lds16(xr, buf + p_dst[k], need ? p_go[k] + (p_scale[k] ? db : qb) : OOB);
+                load_lds16(xr, buf + p_dst[k], need ? p_go[k] + (p_scale[k] ? dbase : qbase) : OOB);
             }
+        }
+    };
+
+    // Touch every 64-byte piece of a chunk's weight rows (prefetching wavefront
+    // only; nothing waits for these loads but the kernel's end).
+    auto touch = [&](const Chunk &c) {
+        if (c.cl == 0)
+            return;
+        const uint32_t base = (uint32_t)c.t * TILE * row_bytes + c.j0 * WBLK;
+        const int len = c.cl * WBLK;
+#pragma unroll
+        for (int i = 0; i < (TILE * C::PF_SEG + 63) / 64; i++) {
+            const int seg = 64 * i + lane;
+            const int r = seg / C::PF_SEG, q = seg - r * C::PF_SEG;
+            const bool need = r < TILE && 64 * q < len + 64;
+            touch_lds4(wr, C::pf_dump(), need ? base + (uint32_t)r * row_bytes + 64 * q : OOB);
         }
     };
 
@@ -280,27 +362,50 @@ k_mmv(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__res
     for (int r = 0; r < LIVE; r++)
         acc[r] = 0.0f;
     float *red = C::red();
-    // Sum the wavefronts' partial tiles (the barrier orders the partials'
-    // writes before the reads; the reads are done before this wavefront
-    // reaches the next step's barrier, which every later flush's writes
-    // follow).
+    // Sum the wavefronts' partial tiles: output o (LIVE*64 of them) gathers
+    // its 16 partials at red[o*17 + wave] and adds them in one fixed balanced
+    // tree over the wavefront index, whatever LIVE is (so a row's result does
+    // not depend on how many rows are computed with it).  After the barrier GS
+    // consecutive lanes take one output: each adds 16/GS partials (the lower
+    // levels of the tree), row shifts add the lanes' sums (the upper levels;
+    // the total lands in the group's last lane).  The reads are done before
+    // this wavefront reaches the next step's barrier, which every later
+    // flush's writes follow.
     auto flush = [&](int t, bool owned) {
 #pragma unroll
         for (int r = 0; r < LIVE; r++) {
-            red[(wave * LIVE + r) * 64 + lane] = acc[r];
+            red[(r * 64 + lane) * (NW + 1) + wave] = acc[r];
             acc[r] = 0.0f;
         }
         __builtin_amdgcn_s_waitcnt(WAIT_LDS);
         raw_barrier();
-        for (int slot = tid; slot < LIVE * 64; slot += NT) {
-            const int r = slot >> 6, l2 = slot & 63;
-            float v = red[r * 64 + l2];
+        constexpr int GS = LIVE == 1 ? 16 : LIVE == 2 ? 8 : LIVE <= 4 ? 4 : LIVE == 8 ? 2 : 1;
+        constexpr int PER = NW / GS;
+        const int o = tid / GS, part = tid % GS;
+        if (o < LIVE * 64) {
+            // (the in-lane part continues the same balanced tree)
+            float a[PER];
 #pragma unroll
-            for (int w = 1; w < NW; w++)
-                v += red[(w * LIVE + r) * 64 + l2];
+            for (int q = 0; q < PER; q++)
+                a[q] = red[o * (NW + 1) + part * PER + q];
+#pragma unroll
+            for (int d = 1; d < PER; d *= 2)
+#pragma unroll
+                for (int q = 0; q < PER; q += 2 * d)
+                    a[q] += a[q + d];
+            float v = a[0];
+            if constexpr (GS >= 2)
+                v += shr_row(v, std::integral_constant<int, 1>());
+            if constexpr (GS >= 4)
+                v += shr_row(v, std::integral_constant<int, 2>());
+            if constexpr (GS >= 8)
+                v += shr_row(v, std::integral_constant<int, 4>());
+            if constexpr (GS >= 16)
+                v += shr_row(v, std::integral_constant<int, 8>());
+            const int r = o >> 6, l2 = o & 63;
             const int m = 8 * (r / 4) + 4 * (l2 >> 5) + (r % 4);
             const int n = t * TILE + (l2 & 31);
-            if (m < M && n < N) {
+            if (part == GS - 1 && m < M && n < N) {
                 if (owned)
                     Y[(int64_t)m * N + n] = v;
                 else
@@ -311,7 +416,7 @@ k_mmv(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__res
 
     // per-lane LDS read offsets inside a chunk buffer (rows >= M: the zero row)
     const int w_lane = col * C::WROW;
-    const int a_step = col < M ? Mp * SB : 0;
+    const int a_step = col < M ? C::MA * SB : 0;
     int a_off[CH / PAR], d_off[CH / PAR];
 #pragma unroll
     for (int i = 0; i < CH / PAR; i++) {
@@ -322,14 +427,17 @@ k_mmv(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__res
     auto compute = [&](const Chunk &c, auto bc) {
         const char *B = C::template buf<decltype(bc)::value>();
         const char *wchunk = B + w_lane + (c.j0 & 1) * WBLK;  // the window starts at j0 & ~1
-        // The I = CH/PAR super-blocks are computed without branches, the ones
-        // past the chunk's end with a zero scale (their LDS reads stay inside
-        // the buffer), in groups of GI whose LDS reads are issued together, so
-        // that reads, lookups and MFMAs of different super-blocks overlap.
+        // The I = CH/PAR super-blocks go in groups of GI whose LDS reads are
+        // issued together, so that reads, lookups and MFMAs of different
+        // super-blocks overlap; groups past the chunk's end are skipped, and
+        // a super-block past it inside a group is computed with a zero scale
+        // (its LDS reads stay inside the buffer).
         constexpr int I = CH / PAR, DQ = LIVE >= 4 ? LIVE / 4 : 1;
-        constexpr int GI = LIVE <= 4 ? I : (I < 2 ? I : 2);
+        constexpr int GI = I < 2 ? I : 2;
 #pragma unroll
         for (int g = 0; g < I; g += GI) {
+            if (par + PAR * g >= c.cl)                        // (uniform)
+                break;
             uint2 hdr[GI], q[GI];
             v4i ax[GI];
             float4 dx[GI][DQ];
@@ -371,13 +479,20 @@ k_mmv(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__res
     cur.ub = ub;
     cur.nb = nb;
     cur.u = ua;
-    cur.t = ua / nb;
+    cur.t = udiv31(ua, nb);
     cur.j = ua - cur.t * nb;
+    // (the first chunk is short, so that computing starts early)
     Chunk info[NBUF];
     static_for(std::make_integer_sequence<int, NBUF - 1>(), [&](auto bc) {
-        info[decltype(bc)::value] = cur.next(CH);
-        issue(info[decltype(bc)::value], bc);
+        constexpr int b = decltype(bc)::value;
+        info[b] = cur.next(b == 0 ? C::CH0 : CH);
+        issue(info[b], bc);
     });
+    // the prefetching wavefront runs its own cursor PF chunks ahead of the copies
+    Cursor pcur = cur;
+    if (pf_wave)
+        for (int i = 0; i < C::PF; i++)
+            touch(pcur.next(CH));
     // Step on buffer b: wait for this wavefront's loads of its chunk (the
     // loads of the NBUF-2 chunks issued after it stay in flight), meet the
     // other wavefronts (all loads of the chunk have landed, and the buffer
@@ -386,10 +501,13 @@ k_mmv(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__res
         constexpr int b = decltype(bc)::value, nxt = (b + NBUF - 1) % NBUF;
         if (info[b].cl == 0)
             return false;                                     // (uniform) the run is done
-        __builtin_amdgcn_s_waitcnt(wait_vm_lds(SLOTS * (NBUF - 2)));
+        if (!pf_wave)
+            __builtin_amdgcn_s_waitcnt(wait_vm_lds(SLOTS * (NBUF - 2)));
         raw_barrier();
         info[nxt] = cur.next(CH);
         issue(info[nxt], std::integral_constant<int, nxt>());
+        if (pf_wave)
+            touch(pcur.next(CH));
         compute(info[b], bc);
         return true;
     };
@@ -415,10 +533,11 @@ hipError_t launch_c(const uint8_t *W, const XPlanes &x, float *Y, int64_t N, con
     const int nb = (int)(x.K / QK);
     const int64_t T = (N + TILE - 1) / TILE;
     // (the kernel reads both planes through one descriptor)
-    if ((const char *)x.dp != (const char *)x.qp + x.Mp * x.K || x.Mp > C::MPC)
+    if ((const char *)x.dp != (const char *)x.qp + x.Mp * x.K || x.Mp > C::MPC || x.M > C::MA)
         return hipErrorInvalidValue;
+    const int64_t U = T * nb;
     hipLaunchKernelGGL((k_mmv<C>), dim3((unsigned)p.grid), dim3(NT), 0, s, W, x.qp, Y, (int)x.M, (int)N,
-                       (int)x.K, (int)x.Mp, nb, (int)(T * nb), p.grid);
+                       (int)x.K, (int)x.Mp, nb, (int)(U / p.grid), (int)(U % p.grid), p.grid);
     return hipGetLastError();
 }
 
@@ -430,14 +549,16 @@ MmvPlan mmv_plan(int64_t M, int64_t N, int64_t K, int cus)
     const int64_t nb = K / QK, row_bytes = nb * WBLK;
     const int64_t Mp = round_up(M, MPAD);
     const int64_t T = (N + TILE - 1) / TILE;
-    // K/256 even (16-byte aligned chunk windows); 32-bit buffer offsets and
-    // unit counts: the weight matrix, the activation planes and T*K/256 stay
-    // below 2^31
-    if (M < 1 || M > TILE || nb % 2 != 0 || N * row_bytes >= (1LL << 31) ||
+    // K/256 even (16-byte aligned chunk windows) and below 2^16; 32-bit
+    // buffer offsets and unit counts: the weight matrix, the activation planes
+    // and T*K/256 stay below 2^31
+    if (M < 1 || M > TILE || nb % 2 != 0 || nb >= (1 << 16) || N * row_bytes >= (1LL << 31) ||
         Mp * K + Mp * K / 8 >= (1LL << 31) || T * nb >= (1LL << 31))
         return p;
     const int64_t U = T * nb;
     p.grid = (int)(T < cus ? T : cus);
+    if (p.grid >= (1 << 15))
+        return p;                                           // (the kernel's run split)
     p.live = M <= 4 ? (int)M : M <= 8 ? 4 : M <= 16 ? 8 : 16;
     p.zero_y = false;
     for (int64_t g = 1; g < p.grid; g++)
