@@ -22,11 +22,21 @@ Printed: one JSON line with
 `--sweep FILE` additionally times every (shape, M, path) point of the five
 workloads and writes one JSON object per point to FILE (used for the measured
 dispatch table and the results tables).
+
+Profiling helpers (the commands are recorded in the summaries under profiles/):
+`--profile-run` launches the decode sweep's matmul kernels and a calibration
+copy a fixed number of times (run under rocprofv3); `--summarize-pmc FETCH_DIR
+WRITE_DIR --out FILE` turns the two counter runs into the traffic summary
+that the `roofline.traffic` field is read from (only while the kernel source
+it was measured on is unchanged).
 """
 
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import math
 import os
@@ -47,7 +57,29 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
 INT8_PEAK_TOPS = 5000.0         # MI355X dense int8 MFMA, published
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
 MALL_BYTES = 256 << 20
-KERNEL_NAMES = {iq.PATH_GEMV: "k_gemv", iq.PATH_MMQ: "k_mmq", iq.PATH_DEQ_BF16: "k_gemm_bf16"}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_mmv_decode_n10240_k5120_traffic.txt")
+COPY_BYTES = 256 << 20          # calibration copy of the profiling run
+KERNEL_SOURCES = {"k_mmv": ["mmv.hip", "common.hpp"], "k_gemv": ["gemv.hip", "common.hpp"],
+                  "k_mmq": ["mmq.hip", "common.hpp"], "k_gemm_bf16": ["deq.hip", "common.hpp"]}
+
+
+def kernel_name(M, N, K, path):
+    """The matmul kernel a call launches (the streaming kernel serves MMQ up
+    to M=32 when K/256 is even)."""
+    if path == iq.PATH_GEMV:
+        return "k_gemv"
+    if path == iq.PATH_DEQ_BF16:
+        return "k_gemm_bf16"
+    nb = K // 256
+    return "k_mmv" if M <= 32 and nb % 2 == 0 and N * nb * 136 < (1 << 31) else "k_mmq"
+
+
+def source_hash(kernel):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "iq4_xs_q8_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def algo_bytes_call(M, N, K):
@@ -92,7 +124,9 @@ def time_events(fn, reps, stream):
 
 
 def measure_point(rot, X, N, K, path, reps=30):
-    """ms per iq4xs_gemm call and ms per matmul-kernel launch (prepared act)."""
+    """ms per iq4xs_gemm call, and ms per launch of the matmul kernel alone
+    (prepared activations, Y marked as zeroed so that nothing else runs; its
+    values are not used), both from HIP events on the launching stream."""
     M = X.shape[0]
     Y = torch.empty((M, N), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
@@ -103,7 +137,8 @@ def measure_point(rot, X, N, K, path, reps=30):
     t_kern = None
     if path != iq.PATH_DEQ_BF16:
         act = iq.prepare_act(X)
-        kern = lambda: iq.gemm_act(rot.next(), act, M, K, path=path, out=Y)  # noqa: E731
+        Y.zero_()
+        kern = lambda: iq.gemm_act(rot.next(), act, M, K, path=path, out=Y, y_zeroed=True)  # noqa: E731
         for _ in range(3):
             kern()
         t_kern = time_events(kern, reps, stream)
@@ -157,6 +192,104 @@ def cpu_baseline(wl, N, K, ms, target_s=12.0):
                       f"{reps} pass(es), {t:.1f} s"}
 
 
+def profile_run():
+    """Fixed launches for rocprofv3: per M of the decode sweep, 20 launches
+    of the matmul kernel alone (rotated weights, as in the timed step), then
+    a calibration copy of COPY_BYTES, 5 times."""
+    wl = synth.DECODE_ATTN
+    (N, K), ms = wl.shapes[0], wl.ms
+    rot = Rotation(wl.w(N, K))
+    for M in ms:
+        X = torch.from_numpy(wl.x(M, K, N=N)).cuda()
+        act = iq.prepare_act(X)
+        Y = torch.zeros((M, N), dtype=torch.float32, device="cuda")
+        path = iq.dispatch(M, N, K)
+        for _ in range(20):
+            iq.gemm_act(rot.next(), act, M, K, path=path, out=Y, y_zeroed=True)
+        torch.cuda.synchronize()
+        print(f"[profile-run] M={M} {kernel_name(M, N, K, path)} x20", flush=True)
+    a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(f"[profile-run] copy {COPY_BYTES} bytes x5", flush=True)
+
+
+def _counter_rows(d):
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    return rows
+
+
+def summarize_pmc(fetch_dir, write_dir, out, cmd_fetch, cmd_write):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the matmul kernels and of
+    the calibration copy -> calibrated HBM bytes per launch."""
+    def per_kernel(rows, counter):
+        acc = {}
+        for r in rows:
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"]
+            key = ("copy" if "copy" in name.lower() or "elementwise" in name.lower() else
+                   "k_mmv" if "k_mmv" in name else "k_gemv" if "k_gemv" in name else
+                   "k_mmq" if "k_mmq" in name else None)
+            if key is None:
+                continue
+            label = name.split("Cfg<")[1].split(">")[0].replace(" ", "") if "Cfg<" in name else ""
+            acc.setdefault((key, label), {}).setdefault(r["Dispatch_Id"], 0.0)
+            acc[(key, label)][r["Dispatch_Id"]] += float(r["Counter_Value"])
+        return {k: sum(v.values()) / len(v) for k, v in acc.items()}
+    fetch = per_kernel(_counter_rows(fetch_dir), "FETCH_SIZE")
+    write = per_kernel(_counter_rows(write_dir), "WRITE_SIZE")
+    cf = [v for (k, _), v in fetch.items() if k == "copy"]
+    cw = [v for (k, _), v in write.items() if k == "copy"]
+    if not cf or not cw:
+        raise SystemExit("calibration copy not found in the counter runs")
+    f_scale = COPY_BYTES / (max(cf) * 1024.0)       # true bytes per counted byte
+    w_scale = COPY_BYTES / (max(cw) * 1024.0)
+    wl = synth.DECODE_ATTN
+    (N, K), ms = wl.shapes[0], wl.ms
+    lines = [f"# HBM traffic per launch from rocprofv3 counters, decode sweep N={N} K={K}",
+             f"# fetch run: {cmd_fetch}", f"# write run: {cmd_write}",
+             f"copy_bytes {COPY_BYTES}",
+             f"copy_fetch_kib {max(cf):.1f}  fetch_scale {f_scale:.4f}",
+             f"copy_write_kib {max(cw):.1f}  write_scale {w_scale:.4f}",
+             f"source_hash k_mmv {source_hash('k_mmv')}",
+             "# kernel config  fetch_kib  write_kib  calibrated_bytes  algorithmic_bytes(M)"]
+    for (k, label), fk in sorted(fetch.items()):
+        if k == "copy":
+            continue
+        wk = write.get((k, label), 0.0)
+        total = fk * 1024.0 * f_scale + wk * 1024.0 * w_scale
+        lines.append(f"traffic {k} <{label}> {fk:.1f} {wk:.1f} {total:.0f}")
+    for M in ms:
+        lines.append(f"algorithmic M={M} {algo_bytes_kernel(M, N, K):.0f}")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def traffic_for(kernel, label):
+    """Calibrated bytes per launch from the committed summary, or None when
+    the summary is missing or the kernel source changed since."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as fh:
+        lines = fh.read().splitlines()
+    if f"source_hash {kernel} {source_hash(kernel)}" not in lines:
+        return None
+    for ln in lines:
+        parts = ln.split()
+        if len(parts) == 6 and parts[0] == "traffic" and parts[1] == kernel and parts[2] == f"<{label}>":
+            return float(parts[5])
+    return None
+
+
 def run_sweep(path_out):
     """Every (shape, M, path) point of the five workloads -> JSONL."""
     with open(path_out, "w") as f:
@@ -191,7 +324,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--sweep", default=None, help="also time every workload point -> JSONL")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-run", action="store_true", help="fixed launches for rocprofv3")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--out", default=TRAFFIC_FILE)
+    ap.add_argument("--cmd-fetch", default="")
+    ap.add_argument("--cmd-write", default="")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc, args.out, args.cmd_fetch, args.cmd_write)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the matmul is built and measured on a single MI355X "
               "(multi-GPU sharding is a design note only); run with --gpus 1", file=sys.stderr)
@@ -200,6 +341,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
+    if args.profile_run:
+        profile_run()
+        return
 
     wl = synth.DECODE_ATTN
     (N, K), ms = wl.shapes[0], wl.ms
@@ -255,10 +399,16 @@ def main():
         t_call, t_kern = measure_point(rot, Xs[M], N, K, path)
         per_m.append(point_record(N, K, M, path, t_call, t_kern))
     dom = max(per_m, key=lambda r: r["kernel_ms"])
+    dom_kernel = kernel_name(dom["M"], N, K, iq.PATHS[dom["path"]])
     achieved = algo_bytes_kernel(dom["M"], N, K) / (dom["kernel_ms"] * 1e-3) / 1e9
+    label = {1: "1,4,8,3,0", 2: "2,4,8,3,0", 4: "4,4,8,3,0", 8: "4,8,4,4,0",
+             16: "8,16,4,3,0"}.get(dom["M"], "") if dom_kernel == "k_mmv" else ""
+    traffic = traffic_for(dom_kernel, label)
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                "kernel": KERNEL_NAMES[iq.PATHS[dom["path"]]], "M": dom["M"],
+                "frac": achieved / HBM_PEAK_GBS,
+                "traffic": None if traffic is None else traffic / (dom["kernel_ms"] * 1e-3) / 1e9,
+                "traffic_bytes_per_launch": traffic,
+                "kernel": dom_kernel, "M": dom["M"],
                 "bytes_per_launch": algo_bytes_kernel(dom["M"], N, K),
                 "avg_launch_ms": dom["kernel_ms"]}
 

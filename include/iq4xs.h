@@ -127,7 +127,13 @@ int iq4xs_prepare_act(const float *X, void *act, int64_t M, int64_t K, void *str
 /* Y = X * W^T from prepared activations; path AUTO, GEMV or MMQ (DEQ_BF16 is
  * EPATH here).  Launches the matmul kernel only -- plus, for shapes whose K is
  * split over several workgroups (small N, long K), a fixed-order reduction
- * kernel over a stream-ordered partial-sum workspace. */
+ * kernel over a stream-ordered partial-sum workspace, and, where the
+ * streaming MMQ kernel shares output tiles between two workgroups (which add
+ * into Y), a kernel that zeroes Y first.  OR IQ4XS_Y_ZEROED into `path` when
+ * Y already holds zeros (e.g. cleared together with other buffers): the
+ * zeroing kernel is then skipped and the result is the same; with any other
+ * Y contents the result of such shared tiles is undefined. */
+#define IQ4XS_Y_ZEROED 0x100
 int iq4xs_gemm_act(const void *W, const void *act, float *Y, int64_t M, int64_t N, int64_t K,
                    int path, void *stream);
 

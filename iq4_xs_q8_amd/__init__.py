@@ -27,6 +27,7 @@ LIB_PATH = os.path.join(_HERE, "libiq4xs.so")
 OK, EINVAL, EALIGN, EDEVICE, ETABLE, ELAUNCH, ENOMEM, EPATH = 0, -1, -2, -3, -4, -5, -6, -7
 PATH_AUTO, PATH_GEMV, PATH_MMQ, PATH_DEQ_BF16 = 0, 1, 2, 3
 PATHS = {"AUTO": PATH_AUTO, "GEMV": PATH_GEMV, "MMQ": PATH_MMQ, "DEQ_BF16": PATH_DEQ_BF16}
+Y_ZEROED = 0x100     # gemm_act hint: Y already holds zeros
 
 EXPORTS = ("iq4xs_weight_bytes", "iq4xs_q8_1_bytes", "iq4xs_init", "iq4xs_quantize_q8_1",
            "iq4xs_gemm", "iq4xs_gemm_path", "iq4xs_gemm_workspace_bytes", "iq4xs_gemm_ws",
@@ -200,14 +201,16 @@ def prepare_act(X: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tenso
 
 
 def gemm_act(W: torch.Tensor, act: torch.Tensor, M: int, K: int, path: int = PATH_AUTO,
-             out: torch.Tensor | None = None) -> torch.Tensor:
-    """Y[M, N] from prepared activations (one kernel launch)."""
+             out: torch.Tensor | None = None, y_zeroed: bool = False) -> torch.Tensor:
+    """Y[M, N] from prepared activations (the matmul kernel; y_zeroed: `out`
+    already holds zeros, so no zeroing kernel runs before it)."""
     N = W.shape[0]
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=act.device)
     with _on(act):
         check(_L().iq4xs_gemm_act(_dev(W, torch.uint8, "W"), _dev(act, torch.uint8, "act"),
-                                 _dev(out, torch.float32, "Y"), M, N, K, path, _stream(act)))
+                                 _dev(out, torch.float32, "Y"), M, N, K,
+                                 path | (Y_ZEROED if y_zeroed else 0), _stream(act)))
     return out
 
 

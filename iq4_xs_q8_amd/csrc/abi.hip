@@ -470,6 +470,8 @@ int iq4xs_prepare_act(const float *X, void *act, int64_t M, int64_t K, void *str
 int iq4xs_gemm_act(const void *W, const void *act, float *Y, int64_t M, int64_t N, int64_t K,
                    int path, void *stream)
 {
+    const bool y_zeroed = (path & IQ4XS_Y_ZEROED) != 0;
+    path &= ~IQ4XS_Y_ZEROED;
     if (!W || !act || !Y)
         return fail(IQ4XS_EINVAL, "null pointer");
     int st = check_dims(M, N, K);
@@ -498,7 +500,7 @@ int iq4xs_gemm_act(const void *W, const void *act, float *Y, int64_t M, int64_t 
         scr.p = nullptr;
         return fail(IQ4XS_ENOMEM, "workspace of %zu bytes", wbytes);
     }
-    return launch_err(launch_mmq(W, xp, Y, N, scr.p, false, s), path_name(path));
+    return launch_err(launch_mmq(W, xp, Y, N, scr.p, y_zeroed, s), path_name(path));
 }
 
 int iq4xs_dispatch(int64_t M, int64_t N, int64_t K, int *path_out)

@@ -107,6 +107,10 @@ def test_gemm_paths_match_oracle(M, N, K):
             act = iq.prepare_act(Xd)
             y3 = iq.gemm_act(Wd, act, M, K, path=p, out=poisoned((M, N))).cpu().numpy()
             assert np.array_equal(y, y3), f"{iq.path_name(p)}: gemm and gemm_act differ"
+            # Y_ZEROED: same result on a zeroed Y, without the zeroing kernel
+            y5 = iq.gemm_act(Wd, act, M, K, path=p, out=torch.zeros((M, N), device="cuda"),
+                             y_zeroed=True).cpu().numpy()
+            assert np.array_equal(y, y5), f"{iq.path_name(p)}: gemm_act with Y_ZEROED differs"
         # and with caller-provided scratch (no allocation inside the call)
         ws = torch.empty(iq.workspace_bytes(M, N, K, p), dtype=torch.uint8, device="cuda")
         y4 = iq.gemm(Wd, Xd, path=p, out=poisoned((M, N)), workspace=ws).cpu().numpy()
@@ -223,6 +227,13 @@ def test_full_size_sampled(cid, N, K, M):
     y = iq.gemm(Wd, dev(X), out=poisoned((M, N))).cpu().numpy()
     assert np.all(np.isfinite(y)), "outputs not written"
     assert_rows_close(y[:, cols], ref, what=f"AUTO C{cid} M={M} N={N} K={K}")
+    if M <= 32:
+        # the matmul launch alone (tiles shared by two workgroups at these
+        # sizes): bit-identical, with Y zeroed by the library or by the caller
+        act = iq.prepare_act(dev(X))
+        y2 = iq.gemm_act(Wd, act, M, K, out=poisoned((M, N))).cpu().numpy()
+        y3 = iq.gemm_act(Wd, act, M, K, out=torch.zeros((M, N), device="cuda"), y_zeroed=True).cpu().numpy()
+        assert np.array_equal(y, y2) and np.array_equal(y, y3), "gemm_act differs from gemm"
     if cid == 5 and M in (64, 512):
         yb = iq.gemm(Wd, dev(X), path=iq.PATH_DEQ_BF16, out=poisoned((M, N))).cpu().numpy()
         assert np.all(np.isfinite(yb))
