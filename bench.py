@@ -195,7 +195,7 @@ def cpu_baseline(wl, N, K, ms, target_s=12.0):
 def profile_run():
     """Fixed launches for rocprofv3: per M of the decode sweep, 20 launches
     of the matmul kernel alone (rotated weights, as in the timed step), then
-    a calibration copy of COPY_BYTES, 5 times."""
+    a calibration copy of COPY_BYTES, 4 times."""
     wl = synth.DECODE_ATTN
     (N, K), ms = wl.shapes[0], wl.ms
     rot = Rotation(wl.w(N, K))
@@ -208,12 +208,17 @@ def profile_run():
             iq.gemm_act(rot.next(), act, M, K, path=path, out=Y, y_zeroed=True)
         torch.cuda.synchronize()
         print(f"[profile-run] M={M} {kernel_name(M, N, K, path)} x20", flush=True)
-    a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
-    b = torch.empty_like(a)
-    for _ in range(5):
-        b.copy_(a)
+    # the copy's source must come from HBM, not from the 256 MB Infinity
+    # Cache: fill four buffers, then copy the first (three later fills have
+    # evicted it), once per buffer
+    bufs = [torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(float(i)) for i in range(4)]
+    dst = torch.empty_like(bufs[0])
+    for i in range(4):
+        for j in range(1, 4):
+            bufs[(i + j) % 4].fill_(float(j))
+        dst.copy_(bufs[i])
     torch.cuda.synchronize()
-    print(f"[profile-run] copy {COPY_BYTES} bytes x5", flush=True)
+    print(f"[profile-run] copy {COPY_BYTES} bytes x4", flush=True)
 
 
 def _counter_rows(d):
@@ -235,7 +240,7 @@ def summarize_pmc(fetch_dir, write_dir, out, cmd_fetch, cmd_write):
             if r["Counter_Name"] != counter:
                 continue
             name = r["Kernel_Name"]
-            key = ("copy" if "copy" in name.lower() or "elementwise" in name.lower() else
+            key = ("copy" if "copyBuffer" in name else
                    "k_mmv" if "k_mmv" in name else "k_gemv" if "k_gemv" in name else
                    "k_mmq" if "k_mmq" in name else None)
             if key is None:
@@ -243,22 +248,26 @@ def summarize_pmc(fetch_dir, write_dir, out, cmd_fetch, cmd_write):
             label = name.split("Cfg<")[1].split(">")[0].replace(" ", "") if "Cfg<" in name else ""
             acc.setdefault((key, label), {}).setdefault(r["Dispatch_Id"], 0.0)
             acc[(key, label)][r["Dispatch_Id"]] += float(r["Counter_Value"])
-        return {k: sum(v.values()) / len(v) for k, v in acc.items()}
-    fetch = per_kernel(_counter_rows(fetch_dir), "FETCH_SIZE")
-    write = per_kernel(_counter_rows(write_dir), "WRITE_SIZE")
-    cf = [v for (k, _), v in fetch.items() if k == "copy"]
-    cw = [v for (k, _), v in write.items() if k == "copy"]
+        return {k: list(v.values()) for k, v in acc.items()}
+    fetch_all = per_kernel(_counter_rows(fetch_dir), "FETCH_SIZE")
+    write_all = per_kernel(_counter_rows(write_dir), "WRITE_SIZE")
+    # the calibration copies are the copyBuffer dispatches far above the
+    # weight-copy sizes; everything else is averaged per kernel
+    cf = [v for (k, _), vs in fetch_all.items() if k == "copy" for v in vs if v * 1024.0 > COPY_BYTES / 16]
+    cw = [v for (k, _), vs in write_all.items() if k == "copy" for v in vs if v * 1024.0 > COPY_BYTES / 16]
+    fetch = {k: sum(v) / len(v) for k, v in fetch_all.items()}
+    write = {k: sum(v) / len(v) for k, v in write_all.items()}
     if not cf or not cw:
         raise SystemExit("calibration copy not found in the counter runs")
-    f_scale = COPY_BYTES / (max(cf) * 1024.0)       # true bytes per counted byte
-    w_scale = COPY_BYTES / (max(cw) * 1024.0)
+    f_scale = COPY_BYTES / (sum(cf) / len(cf) * 1024.0)       # true bytes per counted byte
+    w_scale = COPY_BYTES / (sum(cw) / len(cw) * 1024.0)
     wl = synth.DECODE_ATTN
     (N, K), ms = wl.shapes[0], wl.ms
     lines = [f"# HBM traffic per launch from rocprofv3 counters, decode sweep N={N} K={K}",
              f"# fetch run: {cmd_fetch}", f"# write run: {cmd_write}",
              f"copy_bytes {COPY_BYTES}",
-             f"copy_fetch_kib {max(cf):.1f}  fetch_scale {f_scale:.4f}",
-             f"copy_write_kib {max(cw):.1f}  write_scale {w_scale:.4f}",
+             f"copy_fetch_kib {sum(cf) / len(cf):.1f}  fetch_scale {f_scale:.4f}",
+             f"copy_write_kib {sum(cw) / len(cw):.1f}  write_scale {w_scale:.4f}",
              f"source_hash k_mmv {source_hash('k_mmv')}",
              "# kernel config  fetch_kib  write_kib  calibrated_bytes  algorithmic_bytes(M)"]
     for (k, label), fk in sorted(fetch.items()):

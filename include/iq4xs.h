@@ -151,7 +151,8 @@ int iq4xs_dispatch(int64_t M, int64_t N, int64_t K, int *path_out);
 /* Replace the dispatch table with the one in `path` (NULL: the built-in
  * default).  On ETABLE the previous table stays in force.  Format: text lines
  *   arch <gfx name>
- *   band <GEMV|MMQ|DEQ_BF16> <M_lo> <M_hi> <N or *> <K or *>
+ *   band <GEMV|MMQ|DEQ_BF16> <M_lo> <M_hi> <N> <K>
+ * where N and K are "*" (any), a value, or an inclusive range "lo-hi";
  * '#' starts a comment; the first band that matches (M, N, K) wins; DEQ_BF16
  * bands are skipped unless IQ4XS_ALLOW_BF16=1 was set at initialisation. */
 int iq4xs_load_dispatch_table(const char *path);

@@ -52,6 +52,20 @@ static bool parse_int(const std::string &s, int64_t *v, bool allow_star)
     return true;
 }
 
+// "*" (any), "v" or "lo-hi" (inclusive)
+static bool parse_range(const std::string &s, int64_t *lo, int64_t *hi)
+{
+    if (s == "*") {
+        *lo = *hi = -1;
+        return true;
+    }
+    const size_t dash = s.find('-');
+    if (dash == std::string::npos)
+        return parse_int(s, lo, false) && parse_int(s, hi, false) && *lo >= 1;
+    return parse_int(s.substr(0, dash), lo, false) && parse_int(s.substr(dash + 1), hi, false) && *lo >= 1 &&
+           *hi >= *lo;
+}
+
 bool parse_table(const std::string &text, Table *out, std::string *err)
 {
     Table t;
@@ -75,7 +89,7 @@ bool parse_table(const std::string &text, Table *out, std::string *err)
             Band b;
             b.path = path_from_name(tok[1]);
             if (!b.path || !parse_int(tok[2], &b.mlo, false) || !parse_int(tok[3], &b.mhi, false) ||
-                !parse_int(tok[4], &b.n, true) || !parse_int(tok[5], &b.k, true) || b.mlo < 1 ||
+                !parse_range(tok[4], &b.nlo, &b.nhi) || !parse_range(tok[5], &b.klo, &b.khi) || b.mlo < 1 ||
                 b.mhi < b.mlo) {
                 *err = "dispatch table line " + std::to_string(lineno) + ": bad band";
                 return false;
@@ -109,9 +123,9 @@ int table_lookup(const Table &t, int64_t M, int64_t N, int64_t K, bool allow_bf1
             continue;
         if (M < b.mlo || M > b.mhi)
             continue;
-        if (b.n >= 0 && b.n != N)
+        if (b.nlo >= 0 && (N < b.nlo || N > b.nhi))
             continue;
-        if (b.k >= 0 && b.k != K)
+        if (b.klo >= 0 && (K < b.klo || K > b.khi))
             continue;
         return b.path;
     }

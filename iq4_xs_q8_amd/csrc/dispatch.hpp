@@ -13,7 +13,7 @@ constexpr int64_t GEMV_MAX_M_TABLE = 4;
 struct Band {
     int path = 0;
     int64_t mlo = 0, mhi = 0;
-    int64_t n = -1, k = -1;   // -1 = any
+    int64_t nlo = -1, nhi = -1, klo = -1, khi = -1;   // inclusive ranges; -1 = any
 };
 
 struct Table {

@@ -152,12 +152,25 @@ def test_table_loading(tmp_path):
     garbled.write_text("arch gfx950\nband MMQ one 7 * *\n")
     noarch = tmp_path / "n.txt"
     noarch.write_text("band MMQ 1 7 * *\n")
+    ranged = tmp_path / "r.txt"
+    ranged.write_text("arch gfx950\nband GEMV 1 4 1-4096 256-512\nband MMQ 1 100000 * *\n")
+    bad_ranges = []
+    for i, rng in enumerate(("5-3", "0-9", "1-", "-4", "1-2-3", "a-b")):
+        f = tmp_path / f"br{i}.txt"
+        f.write_text(f"arch gfx950\nband MMQ 1 7 {rng} *\n")
+        bad_ranges.append(f)
     try:
+        iq.load_dispatch_table(str(ranged))
+        assert iq.dispatch(4, 4096, 256) == iq.PATH_GEMV
+        assert iq.dispatch(1, 1, 512) == iq.PATH_GEMV
+        assert iq.dispatch(4, 4097, 256) == iq.PATH_MMQ
+        assert iq.dispatch(4, 4096, 768) == iq.PATH_MMQ
+        assert iq.dispatch(5, 4096, 256) == iq.PATH_MMQ
         iq.load_dispatch_table(str(good))
         assert iq.dispatch(3, 4096, 256) == iq.PATH_MMQ
         assert iq.dispatch(4, 1024, 256) == iq.PATH_GEMV
         assert iq.dispatch(4, 2048, 256) == iq.PATH_MMQ
-        for f in (bad_gemv, garbled, noarch, tmp_path / "missing.txt"):
+        for f in (bad_gemv, garbled, noarch, tmp_path / "missing.txt", *bad_ranges):
             assert L.iq4xs_load_dispatch_table(str(f).encode()) == iq.ETABLE
             # previous table still in force
             assert iq.dispatch(3, 4096, 256) == iq.PATH_MMQ
