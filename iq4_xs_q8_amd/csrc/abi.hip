@@ -30,6 +30,9 @@ const TuneOverride &iq4xs::tune_override()
         const char *m = getenv("IQ4XS_MMV");
         if (m && m[0] == '0')
             o.mmv = 0;
+        const char *t = getenv("IQ4XS_TILE");
+        if (t && t[0] == '0')
+            o.tile = 0;
         return o;
     }();
     return t;
@@ -287,7 +290,7 @@ int run_gemm(const void *W, const float *X, const void *Xq, float *Y, int64_t M,
         const size_t pbytes = (size_t)round_up((int64_t)xplanes_bytes(M, K), 256);
         const XPlanes xp = xplanes_at(base, M, K);
         // a matmul that adds partial tiles into Y gets it zeroed by the quantizer
-        const bool zero = path == IQ4XS_PATH_MMQ && mmq_plan(M, N, K).vp.zero_y;
+        const bool zero = path == IQ4XS_PATH_MMQ && mmq_plan(M, N, K).zero_y;
         float *yz = zero ? Y : nullptr;
         const int64_t nz = zero ? M * N : 0;
         hipError_t e = X ? launch_quantize(X, nullptr, &xp, nullptr, M, K, s, yz, nz)

@@ -189,10 +189,21 @@ struct MmvPlan {
 MmvPlan mmv_plan(int64_t M, int64_t N, int64_t K, int cus);
 hipError_t launch_mmv(const void *W, const XPlanes &x, float *Y, int64_t N, const MmvPlan &p,
                       hipStream_t s);
+// Tile kernel for M > 32 (mmqt.hip): 128 x 128 tiles, runs of (tile,
+// super-block) units over `grid` workgroups.
+struct MmqtPlan {
+    bool ok = false, zero_y = false;
+    int grid = 0, mblocks = 0;
+};
+MmqtPlan mmqt_plan(int64_t M, int64_t N, int64_t K, int cus);
+hipError_t launch_mmqt(const void *W, const XPlanes &x, float *Y, int64_t N, const MmqtPlan &p, hipStream_t s);
 struct MmqPlan {
     int tm = 1, kw = 1, ks = 1;
     bool mmv = false;          // the streaming kernel runs (M <= 32)
     MmvPlan vp;
+    bool tile = false;         // the 128 x 128 tile kernel runs
+    MmqtPlan tp;
+    bool zero_y = false;       // Y must hold zeros before the launch
     size_t workspace_bytes = 0;
 };
 MmqPlan mmq_plan(int64_t M, int64_t N, int64_t K);
@@ -208,7 +219,8 @@ constexpr int GEMV_MAX_M = 4;
 
 // Tuning override, read once: IQ4XS_MMV=0 (do not use the streaming kernel).
 struct TuneOverride {
-    int mmv = 1;
+    int mmv = 1;    // IQ4XS_MMV=0: no streaming kernel for M <= 32
+    int tile = 1;   // IQ4XS_TILE=0: no 128 x 128 tile kernel for M > 32
 };
 const TuneOverride &tune_override();
 

@@ -237,6 +237,15 @@ MmqPlan mmq_plan(int64_t M, int64_t N, int64_t K)
         p.vp = mmv_plan(M, N, K, device_cus());
         if (p.vp.ok) {
             p.mmv = true;
+            p.zero_y = p.vp.zero_y;
+            return p;
+        }
+    }
+    if (M > TILE && tune_override().tile != 0) {
+        p.tp = mmqt_plan(M, N, K, device_cus());
+        if (p.tp.ok) {
+            p.tile = true;
+            p.zero_y = p.tp.zero_y;
             return p;
         }
     }
@@ -274,6 +283,14 @@ hipError_t launch_mmq(const void *Wv, const XPlanes &x, float *Y, int64_t N, voi
                 return e;
         }
         return launch_mmv(Wv, x, Y, N, p.vp, s);
+    }
+    if (p.tile) {
+        if (p.tp.zero_y && !y_zeroed) {
+            const hipError_t e = launch_zero(Y, x.M * N, s);
+            if (e != hipSuccess)
+                return e;
+        }
+        return launch_mmqt(Wv, x, Y, N, p.tp, s);
     }
     if (p.ks > 1 && workspace == nullptr)
         return hipErrorInvalidValue;

@@ -1,0 +1,353 @@
+// mmqt.hip -- IQ4_XS x Q8_1 for many activation rows (M > 32) on the int8
+// matrix cores: 128 x 128 output tiles, each output owned by one wavefront.
+//
+// Arithmetic (batched IQ4_XS kernel section of the "V100TPS engine log",
+// agent-report.daedalus.work/V100TPS/engine.html): per 32-element sub-block
+// the exact integer dot of the int8 codebook values with the int8
+// activations (two chained v_mfma_i32_32x32x32_i8, one per part of the split
+// codebook), then y += d_w*(ls-32) * d_x * dot in fp32.
+//
+// Work split:
+//  * Output tiles are 128 activation rows (4 MFMA subtiles) x 128 weight rows
+//    (4 subtiles), ordered with the activation block fastest.  Units are
+//    (tile, super-block), tile-major; each workgroup gets one contiguous run
+//    of equal length (at least one tile's units, so a tile has at most two
+//    owners; shared tiles add into a zeroed Y: 0 + a + b == 0 + b + a).
+//  * Half a super-block of a tile at a time (4 sub-blocks) goes straight
+//    from memory into one of five LDS buffers with 16-byte LDS-writing buffer
+//    loads: for each of the 128 weight rows its header and the half's 64
+//    index bytes (an 80-byte LDS row), the 128 activation rows of the 4
+//    sub-blocks (sub-block-major planes, 4 KB per sub-block) and their 512
+//    scales.  The loads of a half run four halves ahead of its use, so the
+//    memory system always has about 90 KB per compute unit in flight; one
+//    barrier per half.
+//  * A half super-block reads only 80 of a weight row's 2720+ bytes, a
+//    pattern HBM serves poorly; so the last wavefront copies nothing but walks
+//    the run ahead, tile portion by tile portion, touching each weight row's
+//    whole byte range of the portion (4-byte loads 64 bytes apart: long
+//    contiguous runs), which brings the weights into the caches before the
+//    copies ask for them.
+//  * Eight wavefronts: wavefront w owns weight subtile w%4 and activation
+//    subtiles 2*(w/4), 2*(w/4)+1, i.e. 2 x 16 accumulators per lane.  Per
+//    sub-block it expands its weight subtile's index bytes once (byte
+//    permutes) and uses them for both activation subtiles, so the fp32
+//    rescale of the integer dots (three VALU operations per output and
+//    sub-block) is the bulk of the work.
+#include "common.hpp"
+#include "stream.hpp"
+
+#include <algorithm>
+
+namespace iq4xs {
+namespace {
+
+using namespace stream;
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+constexpr int TILE = 32;
+constexpr int BM = 128, BN = 128;          // output tile: activation rows x weight rows
+constexpr int NWQ = 8, NTQ = 64 * NWQ;     // wavefronts, threads per workgroup
+constexpr int HALF = SUBS / 2;             // sub-blocks per step
+constexpr int WROWQ = 80;                  // LDS weight row: header, 8 unused, 64 index bytes
+constexpr int W_BYTES = BN * WROWQ;        // 10 KB
+constexpr int A_OFF = W_BYTES, A_BYTES = HALF * BM * SB;              // 16 KB
+constexpr int D_OFF = A_OFF + A_BYTES, D_BYTES = HALF * BM * 4;       // 2 KB
+constexpr int DUMP = D_OFF + D_BYTES;                                  // slots without a job
+constexpr int BUFQ = DUMP + 1024;
+constexpr int NBUFQ = 5;
+constexpr int JW = W_BYTES / 1024, JA = A_BYTES / 1024, JD = (D_BYTES + 1023) / 1024;
+constexpr int NLQ = NWQ - 1;               // copying wavefronts (the last one prefetches)
+constexpr int SLOTS = (JW + JA + JD + NLQ - 1) / NLQ;
+constexpr int PF_PER_STEP = 4;             // touch loads per step of the prefetching wavefront
+constexpr int PF_START = 24;               // and at the start
+static_assert(W_BYTES % 1024 == 0 && D_BYTES == 2048 && NBUFQ * BUFQ + 256 <= 160 * 1024, "LDS budget");
+
+// Unit cursor: one half super-block of one tile per step (j counts halves,
+// nh = 2 * K/256 of them per tile).
+struct UnitCursor {
+    int u, t, j, ua, ub, nh;
+    __device__ Chunk next()
+    {
+        Chunk c{t, j, 0, 0};
+        if (u < ub) {
+            const bool ends = j + 1 == nh || u + 1 == ub;
+            const bool owned = t * nh >= ua && (t + 1) * nh <= ub;
+            c.cl = 1;
+            c.flags = (ends ? 1 : 0) | (owned ? 2 : 0);
+            u++;
+            if (++j == nh) {
+                j = 0;
+                t++;
+            }
+        }
+        return c;
+    }
+};
+
+__global__ void __launch_bounds__(NTQ, 1)
+k_mmqt(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__restrict__ Y, int M, int N,
+       int K, int Mp, int nb, int mblocks, int qb, int rb, int G)
+{
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nt = wave & 3, mp = wave >> 2;                  // weight subtile, activation pair
+    const int col = lane & 31, h = lane >> 5;
+    // Workgroups are dealt round-robin to the 8 XCDs (each with its own L2):
+    // give the workgroups of one XCD consecutive runs, so that the activation
+    // blocks that share a weight block meet in one L2.
+    const int g = G % 8 == 0 ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+    const int ua = g * qb + udiv31(g * rb, G), ub = (g + 1) * qb + udiv31((g + 1) * rb, G);
+    const uint32_t row_bytes = (uint32_t)nb * WBLK;
+    const int dp_at = Mp * K;
+    const __amdgpu_buffer_rsrc_t wr =
+        __builtin_amdgcn_make_buffer_rsrc((void *)W, (short)0, (int)((uint32_t)N * row_bytes), BUFFER_FLAGS);
+    const __amdgpu_buffer_rsrc_t xr =
+        __builtin_amdgcn_make_buffer_rsrc((void *)qp, (short)0, dp_at + Mp * (K / SB) * 4, BUFFER_FLAGS);
+
+    // Per slot: the LDS offset its load fills (uniform), which plane it reads
+    // (uniform: 0 weights, 1 activations, 2 scales, 3 none) and this lane's
+    // offset relative to the unit's base, for the first and the second half
+    // of a super-block (weights: 16-byte piece p of an 80-byte LDS row holds
+    // super-block bytes [0,16) for p = 0, else the half's index bytes).
+    int p_dst[SLOTS], p_kind[SLOTS];
+    uint32_t p_go0[SLOTS], p_go1[SLOTS];
+#pragma unroll
+    for (int k = 0; k < SLOTS; k++) {
+        const int job = wave < NLQ ? wave * SLOTS + k : 1 << 20;
+        if (job < JW) {
+            const int at = 1024 * job + 16 * lane;
+            const int r = at / WROWQ, pc = (at - r * WROWQ) / 16;   // row, piece (5 per row)
+            p_dst[k] = 1024 * job;
+            p_kind[k] = 0;
+            p_go0[k] = (uint32_t)r * row_bytes + (pc == 0 ? 0 : 16 * pc - 8);
+            p_go1[k] = (uint32_t)r * row_bytes + (pc == 0 ? 0 : 16 * pc + 56);
+        } else if (job < JW + JA) {
+            const int a = job - JW;                               // 1 KB = 32 rows of one sub-block
+            const int sb = a >> 2, r = 32 * (a & 3) + (lane >> 1);
+            p_dst[k] = A_OFF + 1024 * a;
+            p_kind[k] = 1;
+            p_go0[k] = p_go1[k] = (uint32_t)((sb * Mp + r) * SB + 16 * (lane & 1));
+        } else if (job < JW + JA + JD) {
+            const int d = job - JW - JA;                          // 1 KB = 2 sub-blocks x 128 scales
+            const int sb = 2 * d + (lane >> 5), r = 4 * (lane & 31);
+            p_dst[k] = D_OFF + 1024 * d;
+            p_kind[k] = 2;
+            p_go0[k] = p_go1[k] = (uint32_t)((sb * Mp + r) * 4);
+        } else {
+            p_dst[k] = DUMP;
+            p_kind[k] = 3;
+            p_go0[k] = p_go1[k] = OOB;
+        }
+    }
+    // tile t -> (activation block, weight block), the activation block fastest;
+    // unit half j: super-block j/2, sub-blocks 4*(j%2) .. 4*(j%2)+3
+    const bool pf_wave = wave == NWQ - 1;                    // (uniform)
+    auto issue = [&](const Chunk &c, auto bc) __attribute__((always_inline)) {
+        char *buf = lds_area<decltype(bc)::value, BUFQ>();
+        if (pf_wave)
+            return;
+        const int mb = c.t % mblocks, wb = c.t / mblocks, js = c.j0 >> 1, hf = c.j0 & 1;
+        const bool live = c.cl > 0;
+        const uint32_t wbase = (uint32_t)wb * BN * row_bytes + (uint32_t)js * WBLK;
+        const int sb0 = js * SUBS + HALF * hf;
+        const uint32_t abase = (uint32_t)((sb0 * Mp + mb * BM) * SB);
+        const uint32_t dbase = (uint32_t)(dp_at + (sb0 * Mp + mb * BM) * 4);
+#pragma unroll
+        for (int k = 0; k < SLOTS; k++) {
+            const uint32_t base = p_kind[k] == 0 ? wbase : p_kind[k] == 1 ? abase : dbase;
+            const bool ok = live && p_kind[k] != 3;
+            load_lds16(p_kind[k] == 0 ? wr : xr, buf + p_dst[k], ok ? (hf ? p_go1[k] : p_go0[k]) + base : OOB);
+        }
+    };
+
+    // Prefetch walker (last wavefront): the run's tile portions in order; a
+    // portion is (tile, super-blocks [ja, jb)) of its 128 weight rows, touched
+    // as rows x q points, q = 0 .. Q-1 at 64-byte steps over [ja, jb)*136.
+    int pf_u = ua;                  // first half-unit of the current portion
+    int pf_t = 0, pf_ja = 0, pf_q = 0, pf_n = 0, pf_i = 0;   // portion, points per row, loads, next load
+    auto pf_portion = [&]() __attribute__((always_inline)) {
+        pf_t = udiv31(pf_u, 2 * nb);
+        const int j2a = pf_u - pf_t * 2 * nb;
+        const int j2b = min(2 * nb, ub - pf_t * 2 * nb);
+        pf_ja = j2a >> 1;
+        const int jb = (j2b + 1) >> 1;
+        pf_q = ((jb - pf_ja) * WBLK + 63) / 64 + 1;
+        pf_n = (BN * pf_q + 63) / 64;
+        pf_i = 0;
+        pf_u = pf_t * 2 * nb + j2b;
+    };
+    auto prefetch = [&](int count) __attribute__((always_inline)) {
+        for (int k = 0; k < count; k++) {
+            if (pf_i == pf_n) {
+                if (pf_u >= ub)
+                    return;
+                pf_portion();
+            }
+            const int wb = pf_t / mblocks;
+            const int idx = 64 * pf_i + lane;
+            const int r = udiv31(idx, pf_q), q = idx - r * pf_q;
+            const uint32_t off = (uint32_t)(wb * BN + r) * row_bytes + (uint32_t)pf_ja * WBLK + 64u * q;
+            touch_lds4(wr, lds_area<-1, 256>(), r < BN ? off : OOB);
+            pf_i++;
+        }
+    };
+    if (pf_wave) {
+        pf_n = pf_i = 0;
+        prefetch(PF_START);
+    }
+
+    float acc[2][16];
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int r = 0; r < 16; r++)
+            acc[i][r] = 0.0f;
+    // result register r of lane (col, h) holds activation row 8*(r/4) + 4*h + r%4
+    auto flush = [&](int t, bool owned) __attribute__((always_inline)) {
+        const int mb = t % mblocks, wb = t / mblocks;
+        const int n = wb * BN + nt * TILE + col;
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int m = mb * BM + (2 * mp + i) * TILE + 8 * (r / 4) + 4 * h + (r % 4);
+                if (m < M && n < N) {
+                    if (owned)
+                        Y[(int64_t)m * N + n] = acc[i][r];
+                    else
+                        atomicAdd(Y + (int64_t)m * N + n, acc[i][r]);
+                }
+                acc[i][r] = 0.0f;
+            }
+    };
+    auto compute = [&](const Chunk &c, auto bc) __attribute__((always_inline)) {
+        const char *B = lds_area<decltype(bc)::value, BUFQ>();
+        const char *wrow = B + (nt * TILE + col) * WROWQ;
+        const uint2 hdr = *reinterpret_cast<const uint2 *>(wrow);
+        const int hf = c.j0 & 1;
+#pragma unroll 2
+        for (int s = 0; s < HALF; s++) {
+            const uint2 q = *reinterpret_cast<const uint2 *>(wrow + 16 + 16 * s + 8 * h);
+            v4i ax[2];
+            float4 dx[2][4];
+#pragma unroll
+            for (int i = 0; i < 2; i++) {
+                const int mt = 2 * mp + i;
+                ax[i] = *reinterpret_cast<const v4i *>(B + A_OFF + (s * BM + mt * TILE + col) * SB + 16 * h);
+#pragma unroll
+                for (int qd = 0; qd < 4; qd++)
+                    dx[i][qd] = *reinterpret_cast<const float4 *>(B + D_OFF + (s * BM + mt * TILE + 4 * h + 8 * qd) * 4);
+            }
+            uint32_t wa[4], wb4[4];
+            expand8_split(q.x, q.y, wa, wb4);
+            const v4i ba = {(int)wa[0], (int)wa[1], (int)wa[2], (int)wa[3]};
+            const v4i bb = {(int)wb4[0], (int)wb4[1], (int)wb4[2], (int)wb4[3]};
+            const float sw = sub_scale(hdr.x, hdr.y, HALF * hf + s);
+#pragma unroll
+            for (int i = 0; i < 2; i++) {
+                const v16i zero = {0};
+                const v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                    ax[i], bb, __builtin_amdgcn_mfma_i32_32x32x32_i8(ax[i], ba, zero, 0, 0, 0), 0, 0, 0);
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const float d = (r % 4 == 0) ? dx[i][r / 4].x : (r % 4 == 1) ? dx[i][r / 4].y
+                                  : (r % 4 == 2) ? dx[i][r / 4].z : dx[i][r / 4].w;
+                    acc[i][r] += (sw * d) * (float)D[r];
+                }
+            }
+        }
+        if (c.flags & 1)
+            flush(c.t, (c.flags & 2) != 0);
+    };
+
+    UnitCursor cur;
+    cur.ua = ua;
+    cur.ub = ub;
+    cur.nh = 2 * nb;
+    cur.u = ua;
+    cur.t = udiv31(ua, 2 * nb);
+    cur.j = ua - cur.t * 2 * nb;
+    Chunk info[NBUFQ];
+    static_for(std::make_integer_sequence<int, NBUFQ - 1>(), [&](auto bc) {
+        info[decltype(bc)::value] = cur.next();
+        issue(info[decltype(bc)::value], bc);
+    });
+    // Step on buffer b: wait for this wavefront's loads of the unit (those of
+    // the NBUFQ-2 units issued after it stay in flight), meet the others (all
+    // loads landed; the buffer computed last is free), load the unit NBUFQ-1
+    // ahead into that buffer, compute.
+    auto step = [&](auto bc) __attribute__((always_inline)) {
+        constexpr int b = decltype(bc)::value, nxt = (b + NBUFQ - 1) % NBUFQ;
+        if (info[b].cl == 0)
+            return false;
+        if (!pf_wave)
+            __builtin_amdgcn_s_waitcnt(wait_vm_lds(SLOTS * (NBUFQ - 2)));
+        raw_barrier();
+        info[nxt] = cur.next();
+        issue(info[nxt], std::integral_constant<int, nxt>());
+        if (pf_wave)
+            prefetch(PF_PER_STEP);
+        compute(info[b], bc);
+        return true;
+    };
+    for (;;) {
+        if (!step(std::integral_constant<int, 0>()))
+            break;
+        if (!step(std::integral_constant<int, 1>()))
+            break;
+        if (!step(std::integral_constant<int, 2>()))
+            break;
+        if (!step(std::integral_constant<int, 3>()))
+            break;
+        if (!step(std::integral_constant<int, 4>()))
+            break;
+    }
+    __builtin_amdgcn_s_waitcnt(wait_vm_lds(0));
+}
+
+}  // namespace
+
+MmqtPlan mmqt_plan(int64_t M, int64_t N, int64_t K, int cus)
+{
+    MmqtPlan p;
+    const int64_t nb = K / QK, row_bytes = nb * WBLK;
+    const int64_t Mp = round_up(M, MPAD);
+    const int64_t mblocks = (M + BM - 1) / BM, wblocks = (N + BN - 1) / BN;
+    const int64_t T = mblocks * wblocks, U = T * 2 * nb;
+    // 32-bit offsets; no more workgroups than tiles (a run covers at least one
+    // tile's units, so a tile has at most two owners).  Measured on MI355X:
+    // with M <= 64 (half a tile of real rows) or fewer than 64 tiles the
+    // K-split kernel of mmq.hip is faster (M=64, 10240 x 5120: 50 vs 108 us;
+    // M=96, 5120 x 17408: 197 vs 335 us), from M=96 and 64 tiles on this one
+    // (M=96, 17408 x 5120: 113 vs 182 us; M=512, 10240 x 5120: 168 vs 442 us).
+    if (M <= 2 * TILE || T < 64 || nb >= (1 << 15) || N * row_bytes >= (1LL << 31) ||
+        Mp * K + Mp * K / 8 + BM * 288 >= (1LL << 31) || U >= (1LL << 31))
+        return p;
+    p.grid = (int)std::min<int64_t>(T, cus);
+    p.mblocks = (int)mblocks;
+    p.zero_y = false;
+    for (int64_t g = 1; g < p.grid; g++)
+        if (U * g / p.grid % (2 * nb) != 0) {
+            p.zero_y = true;
+            break;
+        }
+    p.ok = true;
+    return p;
+}
+
+hipError_t launch_mmqt(const void *W, const XPlanes &x, float *Y, int64_t N, const MmqtPlan &p, hipStream_t s)
+{
+    if (!p.ok)
+        return hipErrorInvalidValue;
+    if ((const char *)x.dp != (const char *)x.qp + x.Mp * x.K)
+        return hipErrorInvalidValue;
+    const int nb = (int)(x.K / QK);
+    const int64_t U = (int64_t)p.mblocks * ((N + BN - 1) / BN) * 2 * nb;
+    hipLaunchKernelGGL(k_mmqt, dim3((unsigned)p.grid), dim3(NTQ), 0, s, (const uint8_t *)W, x.qp, Y, (int)x.M,
+                       (int)N, (int)x.K, (int)x.Mp, nb, p.mblocks, (int)(U / p.grid), (int)(U % p.grid), p.grid);
+    return hipGetLastError();
+}
+
+}  // namespace iq4xs

@@ -38,12 +38,15 @@
 //    been zeroed beforehand: 0 + a + b == 0 + b + a in floating point, so the
 //    result does not depend on which workgroup comes first.
 #include "common.hpp"
+#include "stream.hpp"
 
 #include <type_traits>
 #include <utility>
 
 namespace iq4xs {
 namespace {
+
+using namespace stream;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
@@ -52,11 +55,6 @@ constexpr int TILE = 32;
 constexpr int NW = 16;                     // wavefronts per workgroup
 constexpr int NT = 64 * NW;                // threads per workgroup
 constexpr int PAR = NW / SUBS;             // wavefronts per sub-block
-constexpr int BUFFER_FLAGS = 0x00020000;   // raw buffer resource, gfx9 family
-constexpr uint32_t OOB = 0x80000000u;      // buffer offset past every range: loads return 0
-
-constexpr int round_up_c(int x, int a) { return (x + a - 1) / a * a; }
-
 // LDS row stride of a weight chunk: CH*136 bytes rounded up to an odd number
 // of 16-byte units, so that the 32 rows of an MFMA operand read spread over
 // the banks.
@@ -66,83 +64,11 @@ constexpr int wrow_bytes(int ch)
     return 16 * (u % 2 ? u : u + 1);
 }
 
-// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
-// 6:4, lgkmcnt 11:8): LDS operations done and at most n vector memory
-// operations of this wavefront outstanding; or LDS operations done only.
-constexpr int wait_vm_lds(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
-constexpr int WAIT_LDS = 15 | (3 << 14) | (7 << 4);
-
-// LDS area I of SZ bytes of the calling kernel.
-template <int I, int SZ>
-__device__ __forceinline__ char *lds_area()
-{
-    __shared__ __attribute__((aligned(16))) char a[SZ];
-    return a;
-}
-
-template <int... I, class F>
-__device__ __forceinline__ void static_for(std::integer_sequence<int, I...>, F &&f)
-{
-    (f(std::integral_constant<int, I>()), ...);
-}
-
-// One 16-byte-per-lane buffer load that writes LDS: lane i's 16 bytes from
-// rsrc at voffset land at lds_dst + 16*i (zeros when voffset is out of
-// range).  Written as assembly so that the compiler neither waits for these
-// loads by itself (it would make every LDS read wait for all of them, also
-// for the loads into other buffers) nor moves memory operations across them;
-// the kernel waits for them explicitly.  M0 holds the LDS address; the kernel
-// uses M0 for nothing else.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, const char *lds_dst, uint32_t voffset)
-{
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_dst);
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :
-                 : "s"(m0), "v"(voffset), "s"(rsrc)
-                 : "memory", "m0");
-}
-// The same with 4 bytes per lane (lds_dst + 4*i): here only to pull lines
-// into the cache ahead of their 16-byte copies.
-__device__ __forceinline__ void touch_lds4(__amdgpu_buffer_rsrc_t rsrc, const char *lds_dst, uint32_t voffset)
-{
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_dst);
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-                 :
-                 : "s"(m0), "v"(voffset), "s"(rsrc)
-                 : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-// v from the lane D lanes below in the same row of 16 lanes (0 for the first
-// D lanes of the row).
-template <int D>
-__device__ __forceinline__ float shr_row(float v, std::integral_constant<int, D>)
-{
-    static_assert(D >= 1 && D <= 15, "row shift");
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x110 | D, 0xF, 0xF, true));
-}
-
-// A barrier that neither waits for the loads in flight nor lets the compiler
-// move memory operations across it (the caller waits for what it needs).
-__device__ __forceinline__ void raw_barrier()
-{
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-}
-
 // LIVE result registers, activation rows padded to MPC (>= Mp) in LDS, CH
 // super-blocks per chunk, NBUF chunk buffers.
-template <int LIVE_, int MPC_, int CH_, int NBUF_, int PF_ = 0>
+template <int LIVE_, int MPC_, int CH_, int NBUF_>
 struct Cfg {
     static constexpr int LIVE = LIVE_, MPC = MPC_, CH = CH_, NBUF = NBUF_;
-    // PF > 0: the last wavefront copies nothing into the buffers but touches
-    // the weights of the chunks PF ahead of the copies, so that HBM streams
-    // ahead into the cache while the buffers are busy
-    static constexpr int PF = PF_, NL = PF > 0 ? NW - 1 : NW;                // copying wavefronts
-    static constexpr int PF_SEG = (CH * WBLK + 63) / 64 + 1;                 // 64-byte pieces per row
     static constexpr int CH0 = CH < 2 ? CH : 2;                              // first chunk
     static constexpr int WROW = wrow_bytes(CH);
     static constexpr int W_PR = CH * WBLK / 16;                               // pieces per row
@@ -163,18 +89,17 @@ struct Cfg {
     template <int B>
     static __device__ __forceinline__ char *buf() { return lds_area<B, BUF>(); }
     static __device__ __forceinline__ float *red() { return reinterpret_cast<float *>(lds_area<-1, RED>()); }
-    static __device__ __forceinline__ char *pf_dump() { return lds_area<-2, 256>(); }
     // A chunk is copied by load jobs of 1 KB of a buffer each: JW of weights,
     // JQ of activations, JD of scales.  Every wavefront issues SLOTS loads
     // per chunk: wavefronts 0..WA-1 take the weight jobs, the others the
     // activation jobs and then the scale jobs; slots left over load nothing
     // into the dump area.
     static constexpr int JW = W_BYTES / 1024, JQ = A_BYTES / 1024, JD = D_BYTES / 1024;
-    static constexpr int SLOTS = (JW + JQ + JD + NL - 1) / NL;
+    static constexpr int SLOTS = (JW + JQ + JD + NW - 1) / NW;
     static constexpr int WA = (JW + SLOTS - 1) / SLOTS;
     static_assert(NW == 16, "the flush sums 16 partials per output in a row of 16 lanes");
     static_assert(A_BYTES % 1024 == 0 && BUF % 16 == 0, "whole 1 KB load jobs, aligned buffers");
-    static_assert(WA + (JQ + JD + SLOTS - 1) / SLOTS <= NL, "load jobs fit the wavefronts");
+    static_assert(WA + (JQ + JD + SLOTS - 1) / SLOTS <= NW, "load jobs fit the wavefronts");
     static_assert(CH % PAR == 0 && CH % 2 == 0, "every wavefront gets the same super-blocks");
     static_assert(NBUF >= 2 && TOTAL <= 160 * 1024, "LDS budget");
 };
@@ -190,66 +115,6 @@ __device__ __forceinline__ void epilogue(const v16i &D, float sw, const float4 *
         acc[r] += (sw * d) * (float)D[r];
     }
 }
-
-// x / d for 0 <= x < 2^31 and 1 <= d < 2^16: a float reciprocal estimate,
-// refined once, then corrected to the exact quotient (cheap for the uniform
-// values here, unlike a full integer division).
-__device__ __forceinline__ int udiv31(int x, int d)
-{
-    const float rd = __builtin_amdgcn_rcpf((float)d);
-    int q = (int)((float)x * rd);
-    int r = (int)((uint32_t)x - (uint32_t)q * (uint32_t)d);
-    q += (int)((float)r * rd);
-    r = (int)((uint32_t)x - (uint32_t)q * (uint32_t)d);
-    if (r < 0) {
-        q--;
-        r += d;
-    }
-    if (r < 0) {
-        q--;
-        r += d;
-    }
-    if (r >= d) {
-        q++;
-        r -= d;
-    }
-    if (r >= d)
-        q++;
-    return q;
-}
-
-// A chunk: tile t, super-blocks j0..j0+cl-1 (cl = 0: past the run), flags
-// bit 0 = the tile's units end with it, bit 1 = the tile belongs to this
-// workgroup alone.
-struct Chunk {
-    int t, j0, cl, flags;
-};
-
-// Walks the run [ua, ub) of units in chunks (all values wavefront-uniform).
-struct Cursor {
-    int u, t, j, ua, ub, nb;
-    __device__ Chunk next(int ch)
-    {
-        Chunk c{t, j, 0, 0};
-        if (u < ub) {
-            int l = ub - u;
-            l = l < nb - j ? l : nb - j;
-            const int wl = (j & ~1) + ch - j;
-            l = l < wl ? l : wl;
-            const bool ends = j + l == nb || u + l == ub;
-            const bool owned = t * nb >= ua && (t + 1) * nb <= ub;
-            c.cl = l;
-            c.flags = (ends ? 1 : 0) | (owned ? 2 : 0);
-            u += l;
-            j += l;
-            if (j == nb) {
-                j = 0;
-                t++;
-            }
-        }
-        return c;
-    }
-};
 
 // LIVE: result registers that can hold a real row: 1, 2, 3, 4 (rows 0..LIVE-1
 // in lanes 0-31; LIVE = 4 also serves M <= 8 through lanes 32-63), 8 (M <= 16),
@@ -279,7 +144,6 @@ k_mmv(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__res
     const __amdgpu_buffer_rsrc_t xr =
         __builtin_amdgcn_make_buffer_rsrc((void *)qp, (short)0, dp_at + Mp * (K / SB) * 4, BUFFER_FLAGS);
     const bool w_group = wave < C::WA;                        // (uniform)
-    const bool pf_wave = C::PF > 0 && wave == NW - 1;         // (uniform)
     // per slot: the LDS offset its load fills inside a buffer and whether it
     // holds scales (both uniform), this lane's global offset relative to the
     // chunk's base, and the key that decides whether the lane's piece belongs
@@ -318,10 +182,8 @@ k_mmv(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__res
     // or scale pieces past the chunk, read nothing and fill zeros.  Every
     // wavefront issues SLOTS loads per chunk, also for chunks past the run,
     // so the wait counts are the same on every path.
-    auto issue = [&](const Chunk &c, auto bc) {
+    auto issue = [&](const Chunk &c, auto bc) __attribute__((always_inline)) {
         char *buf = C::template buf<decltype(bc)::value>();
-        if (pf_wave)
-            return;
         if (w_group) {
             const int lo = (c.j0 & 1) * WBLK, hi = lo + c.cl * WBLK;
             const uint32_t base = (uint32_t)c.t * TILE * row_bytes + (c.j0 & ~1) * WBLK;
@@ -341,22 +203,6 @@ k_mmv(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__res
         }
     };
 
-    // Touch every 64-byte piece of a chunk's weight rows (prefetching wavefront
-    // only; nothing waits for these loads but the kernel's end).
-    auto touch = [&](const Chunk &c) {
-        if (c.cl == 0)
-            return;
-        const uint32_t base = (uint32_t)c.t * TILE * row_bytes + c.j0 * WBLK;
-        const int len = c.cl * WBLK;
-#pragma unroll
-        for (int i = 0; i < (TILE * C::PF_SEG + 63) / 64; i++) {
-            const int seg = 64 * i + lane;
-            const int r = seg / C::PF_SEG, q = seg - r * C::PF_SEG;
-            const bool need = r < TILE && 64 * q < len + 64;
-            touch_lds4(wr, C::pf_dump(), need ? base + (uint32_t)r * row_bytes + 64 * q : OOB);
-        }
-    };
-
     float acc[LIVE];
 #pragma unroll
     for (int r = 0; r < LIVE; r++)
@@ -371,7 +217,7 @@ k_mmv(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__res
     // the total lands in the group's last lane).  The reads are done before
     // this wavefront reaches the next step's barrier, which every later
     // flush's writes follow.
-    auto flush = [&](int t, bool owned) {
+    auto flush = [&](int t, bool owned) __attribute__((always_inline)) {
 #pragma unroll
         for (int r = 0; r < LIVE; r++) {
             red[(r * 64 + lane) * (NW + 1) + wave] = acc[r];
@@ -424,7 +270,7 @@ k_mmv(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__res
         a_off[i] = (col < M ? C::A_OFF + col * SB : C::Z_OFF) + 16 * h + sb * a_step;
         d_off[i] = C::D_OFF + 16 * h + 4 * sb * Mp;
     }
-    auto compute = [&](const Chunk &c, auto bc) {
+    auto compute = [&](const Chunk &c, auto bc) __attribute__((always_inline)) {
         const char *B = C::template buf<decltype(bc)::value>();
         const char *wchunk = B + w_lane + (c.j0 & 1) * WBLK;  // the window starts at j0 & ~1
         // The I = CH/PAR super-blocks go in groups of GI whose LDS reads are
@@ -488,26 +334,18 @@ k_mmv(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__res
         info[b] = cur.next(b == 0 ? C::CH0 : CH);
         issue(info[b], bc);
     });
-    // the prefetching wavefront runs its own cursor PF chunks ahead of the copies
-    Cursor pcur = cur;
-    if (pf_wave)
-        for (int i = 0; i < C::PF; i++)
-            touch(pcur.next(CH));
     // Step on buffer b: wait for this wavefront's loads of its chunk (the
     // loads of the NBUF-2 chunks issued after it stay in flight), meet the
     // other wavefronts (all loads of the chunk have landed, and the buffer
     // computed last is free), refill that buffer NBUF-1 chunks ahead, compute.
-    auto step = [&](auto bc) {
+    auto step = [&](auto bc) __attribute__((always_inline)) {
         constexpr int b = decltype(bc)::value, nxt = (b + NBUF - 1) % NBUF;
         if (info[b].cl == 0)
             return false;                                     // (uniform) the run is done
-        if (!pf_wave)
-            __builtin_amdgcn_s_waitcnt(wait_vm_lds(SLOTS * (NBUF - 2)));
+        __builtin_amdgcn_s_waitcnt(wait_vm_lds(SLOTS * (NBUF - 2)));
         raw_barrier();
         info[nxt] = cur.next(CH);
         issue(info[nxt], std::integral_constant<int, nxt>());
-        if (pf_wave)
-            touch(pcur.next(CH));
         compute(info[b], bc);
         return true;
     };
