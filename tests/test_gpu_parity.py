@@ -176,6 +176,26 @@ def test_deterministic_and_invariant(path):
     assert torch.equal(y_row[0], y1[1])
 
 
+@pytest.mark.parametrize("M,N,K", [(300, 2800, 512), (97, 8200, 256), (130, 8320, 1024)])
+def test_tile_kernel_shapes(M, N, K):
+    """Shapes the 128 x 128 tile kernel takes (M > 64, at least 64 tiles):
+    ragged M and N, K of one super-block (runs cross tiles, so tiles are
+    shared by two workgroups and added into a zeroed Y), several super-blocks;
+    through gemm, gemm_act and both Y-zeroing routes, bit-identical."""
+    W, X = _inputs(M, N, K, seed=M + N)
+    ref = O.gemm_q8_1(W, O.quantize_q8_1(X), K)
+    Wd, Xd = dev(W), dev(X)
+    y = iq.gemm(Wd, Xd, path=iq.PATH_MMQ, out=poisoned((M, N))).cpu().numpy()
+    assert np.all(np.isfinite(y)), "outputs not written"
+    assert_rows_close(y, ref, what=f"tile M={M} N={N} K={K}")
+    act = iq.prepare_act(Xd)
+    y2 = iq.gemm_act(Wd, act, M, K, path=iq.PATH_MMQ, out=poisoned((M, N))).cpu().numpy()
+    y3 = iq.gemm_act(Wd, act, M, K, path=iq.PATH_MMQ, out=torch.zeros((M, N), device="cuda"),
+                     y_zeroed=True).cpu().numpy()
+    assert np.array_equal(y, y2) and np.array_equal(y, y3)
+    assert torch.equal(iq.gemm(Wd, Xd, path=iq.PATH_MMQ).cpu(), torch.from_numpy(y)), "two runs differ"
+
+
 def test_negative_control_corrupted_weight_fails():
     # a one-byte change in W must push the affected row outside the bound
     M, N, K = 4, 64, 1024
