@@ -124,16 +124,33 @@ def time_events(fn, reps, stream):
 
 
 def measure_point(rot, X, N, K, path, reps=30):
-    """ms per iq4xs_gemm call, and ms per launch of the matmul kernel alone
-    (prepared activations, Y marked as zeroed so that nothing else runs; its
-    values are not used), both from HIP events on the launching stream."""
+    """Per iq4xs_gemm call: ms on the device (`reps` calls over rotating
+    weight copies recorded in one HIP graph and replayed, so host launch
+    cost is not counted) and ms launched eagerly from the host; and ms per
+    launch of the matmul kernel alone (prepared activations, Y marked as
+    zeroed so that nothing else runs; its values are not used).  All from HIP
+    events on the launching stream."""
     M = X.shape[0]
     Y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    ws = torch.empty(iq.workspace_bytes(M, N, K, path), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
-    call = lambda: iq.gemm(rot.next(), X, path=path, out=Y)  # noqa: E731
+    call = lambda: iq.gemm(rot.next(), X, path=path, out=Y, workspace=ws)  # noqa: E731
     for _ in range(3):
         call()
-    t_call = time_events(call, reps, stream)
+    t_eager = time_events(call, reps, stream)
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        call()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            call()
+    g.replay()
+    t_call = time_events(g.replay, 3, stream) / reps
+    del g
     t_kern = None
     if path != iq.PATH_DEQ_BF16:
         act = iq.prepare_act(X)
@@ -142,13 +159,13 @@ def measure_point(rot, X, N, K, path, reps=30):
         for _ in range(3):
             kern()
         t_kern = time_events(kern, reps, stream)
-    return t_call, t_kern
+    return t_call, t_kern, t_eager
 
 
-def point_record(N, K, M, path, t_call, t_kern):
+def point_record(N, K, M, path, t_call, t_kern, t_eager=None):
     wb = 0.53125 * N * K
     ops = 2.0 * M * N * K
-    rec = {"N": N, "K": K, "M": M, "path": iq.path_name(path), "ms": t_call,
+    rec = {"N": N, "K": K, "M": M, "path": iq.path_name(path), "ms": t_call, "eager_ms": t_eager,
            "weight_GBs": wb / (t_call * 1e-3) / 1e9,
            "int8_TOPS": ops / (t_call * 1e-3) / 1e12,
            "hbm_frac": algo_bytes_call(M, N, K) / (t_call * 1e-3) / 1e9 / HBM_PEAK_GBS}
@@ -313,8 +330,7 @@ def run_sweep(path_out):
                     if M >= 32:
                         paths.append(iq.PATH_DEQ_BF16)
                     for p in paths:
-                        t_call, t_kern = measure_point(rot, X, N, K, p, reps=20)
-                        rec = point_record(N, K, M, p, t_call, t_kern)
+                        rec = point_record(N, K, M, p, *measure_point(rot, X, N, K, p, reps=20))
                         rec["workload"] = wl.name
                         if p == iq.PATH_AUTO:
                             rec["auto"] = iq.path_name(iq.dispatch(M, N, K))
@@ -405,8 +421,7 @@ def main():
     per_m = []
     for M in ms:
         path = iq.dispatch(M, N, K)
-        t_call, t_kern = measure_point(rot, Xs[M], N, K, path)
-        per_m.append(point_record(N, K, M, path, t_call, t_kern))
+        per_m.append(point_record(N, K, M, path, *measure_point(rot, Xs[M], N, K, path)))
     dom = max(per_m, key=lambda r: r["kernel_ms"])
     dom_kernel = kernel_name(dom["M"], N, K, iq.PATHS[dom["path"]])
     achieved = algo_bytes_kernel(dom["M"], N, K) / (dom["kernel_ms"] * 1e-3) / 1e9

@@ -6,6 +6,7 @@ back as EINVAL / EALIGN even where no GPU exists, and well-formed calls on a
 machine without a gfx950 device come back as EDEVICE.
 """
 import ctypes
+import json
 import os
 import re
 import subprocess
@@ -208,3 +209,33 @@ def test_env_table_read_once_and_fail_closed(tmp_path):
     out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
                          check=True).stdout.split()
     assert [int(v) for v in out] == [iq.ETABLE, iq.ETABLE]
+
+
+def test_calibrate_writes_a_loadable_table(tmp_path):
+    """The sweep -> table step: bands follow the measured winners."""
+    from iq4_xs_q8_amd import calibrate
+    recs = []
+    def rec(N, K, M, path, ms):
+        recs.append({"N": N, "K": K, "M": M, "path": path, "ms": ms})
+    for M, g, q in ((1, 0.010, 0.012), (2, 0.011, 0.012), (4, 0.013, 0.012)):
+        rec(4096, 1024, M, "GEMV", g)
+        rec(4096, 1024, M, "MMQ", q)
+    rec(8192, 1024, 1, "GEMV", 0.02)
+    rec(8192, 1024, 1, "MMQ", 0.01)
+    for M, q, b in ((128, 0.1, 0.2), (256, 0.3, 0.2), (512, 0.6, 0.4)):
+        rec(4096, 4096, M, "MMQ", q)
+        rec(4096, 4096, M, "DEQ_BF16", b)
+    sweep = tmp_path / "sweep.jsonl"
+    sweep.write_text("\n".join(json.dumps(r) for r in recs) + "\n")
+    out = tmp_path / "table.txt"
+    calibrate.main([str(sweep), str(out)])
+    text = out.read_text()
+    assert "band GEMV 1 3 4096 1024" in text and "band DEQ_BF16 256 1000000000 4096 4096" in text
+    try:
+        iq.load_dispatch_table(str(out))
+        assert iq.dispatch(2, 4096, 1024) == iq.PATH_GEMV
+        assert iq.dispatch(4, 4096, 1024) == iq.PATH_MMQ
+        assert iq.dispatch(1, 8192, 1024) == iq.PATH_MMQ
+        assert iq.dispatch(300, 4096, 4096) == iq.PATH_MMQ      # bf16 bands need the opt-in
+    finally:
+        iq.load_dispatch_table(None)
