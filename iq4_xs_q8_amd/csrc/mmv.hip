@@ -11,7 +11,7 @@
 // Work split:
 //  * The weights are cut into units (32-column tile t, super-block j), ordered
 //    tile-major, and every workgroup gets one contiguous run of units of equal
-//    length.  The grid never has more workgroups than tiles, so a run covers at
+//    length (the run bounds are computed on the host and passed in).  The grid never has more workgroups than tiles, so a run covers at
 //    least one tile's worth of units and a tile is shared by at most two
 //    workgroups: every compute unit gets the same work whatever the shape.
 //  * A run is walked in chunks of up to CH super-blocks of one tile, chunk
@@ -31,7 +31,9 @@
 //  * Sixteen wavefronts compute: wavefront w takes sub-block w%8 of the
 //    chunk's super-blocks w/8, w/8+2, ... from LDS (the 8 index bytes and
 //    header of its lane's row, the 16 activation bytes of its lane's row;
-//    rows past M read a zero row).
+//    rows past M read a zero row).  The two halves of a wavefront hold the
+//    same 32 rows, so each decodes the scales of one of two super-blocks and
+//    they swap them with one cross-half lane permute.
 //  * When a tile's units end, the wavefronts' partial tiles are summed in LDS
 //    in wavefront order.  A tile owned by one workgroup is stored; a tile
 //    shared by two is added into Y with one atomic add per element, Y having
@@ -104,6 +106,14 @@ struct Cfg {
     static_assert(NBUF >= 2 && TOTAL <= 160 * 1024, "LDS budget");
 };
 
+// The workgroups' runs, computed on the host: workgroup g takes units
+// [u[g], u[g+1]) and starts in tile t[g].
+constexpr int MAXG = 256;
+struct Runs {
+    int u[MAXG + 1];
+    int t[MAXG];
+};
+
 // Result register r of lane (col, h) holds row 8*(r/4) + 4*h + r%4.
 template <int LIVE>
 __device__ __forceinline__ void epilogue(const v16i &D, float sw, const float4 *dx, float acc[LIVE])
@@ -122,16 +132,16 @@ __device__ __forceinline__ void epilogue(const v16i &D, float sw, const float4 *
 template <class C>
 __global__ void __launch_bounds__(NT, 1)
 k_mmv(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__restrict__ Y, int M, int N,
-      int K, int Mp, int nb, int qb, int rb, int G)
+      int K, int Mp, int nb, Runs runs)
 {
     constexpr int LIVE = C::LIVE, CH = C::CH, NBUF = C::NBUF, SLOTS = C::SLOTS;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int s = wave % SUBS, par = wave / SUBS;             // sub-block, first super-block
     const int col = lane & 31, h = lane >> 5;
-    // this workgroup's run [U*g/G, U*(g+1)/G) of the U = qb*G + rb units
+    // this workgroup's run of units
     const int g = blockIdx.x;
-    const int ua = g * qb + udiv31(g * rb, G), ub = (g + 1) * qb + udiv31((g + 1) * rb, G);
+    const int ua = runs.u[g], ub = runs.u[g + 1];
     const uint32_t row_bytes = (uint32_t)nb * WBLK;
 
     // ---- chunk copy: fixed per-lane geometry ------------------------------
@@ -152,25 +162,30 @@ k_mmv(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__res
     bool p_scale[SLOTS];
     uint32_t p_go[SLOTS];
     int p_key[SLOTS];
+    // (geometry in 16-byte pieces: piece i of a 1 KB job is lane i's)
+    constexpr uint32_t LIM = 64 * NW * SLOTS;                 // bound on the piece indices
 #pragma unroll
     for (int k = 0; k < SLOTS; k++) {
         if (w_group) {
             const int job = wave * SLOTS + k;
-            const int at = 1024 * job + 16 * lane;             // byte of the weight area
-            const int r = at / C::WROW, c = (at - r * C::WROW) / 16;
+            const uint32_t pi = 64 * job + lane;               // piece of the weight area
+            const uint32_t r = div_small<C::WROW / 16, LIM>(pi);
+            const uint32_t c = pi - (uint32_t)__umul24(r, C::WROW / 16);
             const bool ok = job < C::JW && r < TILE && c < C::W_PR;
             p_dst[k] = job < C::JW ? 1024 * job : C::DUMP;
             p_scale[k] = false;
-            p_go[k] = ok ? (uint32_t)r * row_bytes + 16 * c : OOB;
-            p_key[k] = ok ? 16 * c + 15 : -(1 << 30);          // piece bytes [16c, 16c+16)
+            p_go[k] = ok ? r * row_bytes + 16 * c : OOB;
+            p_key[k] = ok ? (int)(16 * c + 15) : -(1 << 30);   // piece bytes [16c, 16c+16)
         } else {
             const int job = (wave - C::WA) * SLOTS + k;       // activation jobs, then scales
             const bool isq = job < C::JQ, isd = !isq && job < C::JQ + C::JD;
-            const int at = 1024 * (isq ? job : job - C::JQ) + 16 * lane;
+            const uint32_t pi = 64 * (isq ? job : job - C::JQ) + lane;
             // activation piece: half `hf` of row m of sub-block sb, whose plane
             // holds Mp rows per sub-block
-            const int sb = at / (32 * C::MA), m = (at - sb * 32 * C::MA) / 32, hf = (at / 16) & 1;
-            const int qo = (sb * Mp + m) * SB + 16 * hf;
+            const uint32_t sb2 = div_small<2 * C::MA, LIM>(pi);
+            const uint32_t m = (pi - 2 * C::MA * sb2) >> 1, hf = pi & 1;
+            const int qo = (int)(((uint32_t)__umul24(sb2, (uint32_t)Mp) + m) * SB + 16 * hf);
+            const int at = (int)(16 * pi);
             p_dst[k] = isq ? C::A_OFF + 1024 * job : isd ? C::D_OFF + 1024 * (job - C::JQ) : C::DUMP;
             p_scale[k] = isd;
             p_go[k] = isq ? (uint32_t)qo : isd ? (uint32_t)at : OOB;
@@ -287,16 +302,41 @@ k_mmv(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__res
             uint2 hdr[GI], q[GI];
             v4i ax[GI];
             float4 dx[GI][DQ];
+            // With two super-blocks in the group, the two halves of the
+            // wavefront (same rows) each decode one of the two scales and
+            // swap them.
+            if constexpr (GI == 2)
+                hdr[0] = *reinterpret_cast<const uint2 *>(wchunk + (par + PAR * (g + h)) * WBLK);
 #pragma unroll
             for (int k = 0; k < GI; k++) {
                 const char *wrow = wchunk + (par + PAR * (g + k)) * WBLK;
-                hdr[k] = *reinterpret_cast<const uint2 *>(wrow);
+                if constexpr (GI != 2)
+                    hdr[k] = *reinterpret_cast<const uint2 *>(wrow);
                 q[k] = *reinterpret_cast<const uint2 *>(wrow + QS_OFF + 16 * s + 8 * h);
                 ax[k] = *reinterpret_cast<const v4i *>(B + a_off[g + k]);
 #pragma unroll
                 for (int qd = 0; qd < DQ; qd++)
                     dx[k][qd] = *reinterpret_cast<const float4 *>(B + d_off[g + k] + 32 * qd);
             }
+            // (all of the group's reads are issued before any of them is used)
+            __builtin_amdgcn_sched_barrier(0);
+            float sw[GI];
+            if constexpr (GI == 2) {
+                // (a super-block past the chunk gets d = 0: a zero scale)
+                const uint32_t d_bits = par + PAR * (g + h) < c.cl ? hdr[0].x : 0u;
+                const float own = sub_scale(d_bits, hdr[0].y, s);
+                const uint32_t ob = __builtin_bit_cast(uint32_t, own);
+                // (lanes 0-31 of the first result: their own scale; lanes
+                // 32-63: that of lanes 0-31; the second result the converse)
+                const auto both = __builtin_amdgcn_permlane32_swap(ob, ob, false, false);
+                sw[0] = __builtin_bit_cast(float, (uint32_t)both[0]);
+                sw[1] = __builtin_bit_cast(float, (uint32_t)both[1]);
+            } else {
+#pragma unroll
+                for (int k = 0; k < GI; k++)
+                    sw[k] = par + PAR * (g + k) < c.cl ? sub_scale(hdr[k].x, hdr[k].y, s) : 0.0f;
+            }
+            v16i D[GI];
 #pragma unroll
             for (int k = 0; k < GI; k++) {
                 uint32_t wa[4], wb[4];
@@ -304,11 +344,18 @@ k_mmv(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__res
                 const v4i ba = {(int)wa[0], (int)wa[1], (int)wa[2], (int)wa[3]};
                 const v4i bb = {(int)wb[0], (int)wb[1], (int)wb[2], (int)wb[3]};
                 const v16i zero = {0};
-                const v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                D[k] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
                     ax[k], bb, __builtin_amdgcn_mfma_i32_32x32x32_i8(ax[k], ba, zero, 0, 0, 0), 0, 0, 0);
-                const float sw = par + PAR * (g + k) < c.cl ? sub_scale(hdr[k].x, hdr[k].y, s) : 0.0f;
-                epilogue<LIVE>(D, sw, dx[k], acc);
             }
+            // (the group's products are all issued before the first is read,
+            // each into registers of its own)
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int k = 0; k < GI; k++)
+                epilogue<LIVE>(D[k], sw[k], dx[k], acc);
+#pragma unroll
+            for (int k = 0; k < GI; k++)
+                keep_live(D[k]);
         }
         if (c.flags & 1)                                      // the tile's units end here
             flush(c.t, (c.flags & 2) != 0);
@@ -325,7 +372,7 @@ k_mmv(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__res
     cur.ub = ub;
     cur.nb = nb;
     cur.u = ua;
-    cur.t = udiv31(ua, nb);
+    cur.t = runs.t[g];
     cur.j = ua - cur.t * nb;
     // (the first chunk is short, so that computing starts early)
     Chunk info[NBUF];
@@ -349,18 +396,11 @@ k_mmv(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__res
         compute(info[b], bc);
         return true;
     };
-    for (;;) {
-        if (!step(std::integral_constant<int, 0>()))
-            break;
-        if (!step(std::integral_constant<int, 1>()))
-            break;
-        if constexpr (NBUF > 2)
-            if (!step(std::integral_constant<int, 2 % NBUF>()))
-                break;
-        if constexpr (NBUF > 3)
-            if (!step(std::integral_constant<int, 3 % NBUF>()))
-                break;
-    }
+    for (bool go = true; go;)
+        static_for(std::make_integer_sequence<int, NBUF>(), [&](auto bc) __attribute__((always_inline)) {
+            if (go)
+                go = step(bc);
+        });
     // no load may still write this workgroup's LDS when it ends
     __builtin_amdgcn_s_waitcnt(wait_vm_lds(0));
 }
@@ -374,8 +414,16 @@ hipError_t launch_c(const uint8_t *W, const XPlanes &x, float *Y, int64_t N, con
     if ((const char *)x.dp != (const char *)x.qp + x.Mp * x.K || x.Mp > C::MPC || x.M > C::MA)
         return hipErrorInvalidValue;
     const int64_t U = T * nb;
+    if (p.grid < 1 || p.grid > MAXG)
+        return hipErrorInvalidValue;
+    Runs runs;
+    for (int g = 0; g <= p.grid; g++) {
+        runs.u[g] = (int)(U * g / p.grid);
+        if (g < p.grid)
+            runs.t[g] = runs.u[g] / nb;
+    }
     hipLaunchKernelGGL((k_mmv<C>), dim3((unsigned)p.grid), dim3(NT), 0, s, W, x.qp, Y, (int)x.M, (int)N,
-                       (int)x.K, (int)x.Mp, nb, (int)(U / p.grid), (int)(U % p.grid), p.grid);
+                       (int)x.K, (int)x.Mp, nb, runs);
     return hipGetLastError();
 }
 
@@ -395,8 +443,8 @@ MmvPlan mmv_plan(int64_t M, int64_t N, int64_t K, int cus)
         return p;
     const int64_t U = T * nb;
     p.grid = (int)(T < cus ? T : cus);
-    if (p.grid >= (1 << 15))
-        return p;                                           // (the kernel's run split)
+    if (p.grid > MAXG)
+        p.grid = MAXG;
     p.live = M <= 4 ? (int)M : M <= 8 ? 4 : M <= 16 ? 8 : 16;
     p.zero_y = false;
     for (int64_t g = 1; g < p.grid; g++)

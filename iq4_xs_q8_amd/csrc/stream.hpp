@@ -64,6 +64,43 @@ __device__ __forceinline__ void touch_lds4(__amdgpu_buffer_rsrc_t rsrc, const ch
                  : "s"(m0), "v"(voffset), "s"(rsrc)
                  : "memory", "m0");
 }
+// x / D for 0 <= x < LIM with one 24-bit multiply and a shift: the smallest
+// shift S whose multiplier ceil(2^S / D) gives the exact quotient for every
+// x < LIM, checked exhaustively at compile time.
+struct DivMagic {
+    uint32_t mul, shift;
+};
+template <uint32_t D, uint32_t LIM>
+constexpr DivMagic div_magic()
+{
+    for (uint32_t s = 0; s < 32; s++) {
+        const uint64_t mg = ((1ull << s) + D - 1) / D;
+        if (mg >= (1u << 24) || mg * (LIM - 1) >= (1ull << 32))
+            continue;
+        bool ok = true;
+        for (uint32_t x = 0; x < LIM && ok; x++)
+            ok = (uint32_t)((x * mg) >> s) == x / D;
+        if (ok)
+            return DivMagic{(uint32_t)mg, s};
+    }
+    return DivMagic{0, 0};
+}
+template <uint32_t D, uint32_t LIM>
+__device__ __forceinline__ uint32_t div_small(uint32_t x)
+{
+    constexpr DivMagic m = div_magic<D, LIM>();
+    static_assert(m.mul != 0, "no 24-bit multiplier for this divisor and range");
+    return (uint32_t)__umul24(x, m.mul) >> m.shift;
+}
+
+// Keeps the registers of v allocated, unchanged, up to this point (so that
+// nothing else is written into a register the matrix core may still be
+// writing, which would stall the wavefront).
+typedef int v16i_keep __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ void keep_live(const v16i_keep &v)
+{
+    asm volatile("" ::"v"(v));
+}
 #pragma clang diagnostic pop
 
 // v from the lane D lanes below in the same row of 16 lanes (0 for the first
