@@ -59,8 +59,9 @@ BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
 MALL_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_mmv_decode_n10240_k5120_traffic.txt")
 COPY_BYTES = 256 << 20          # calibration copy of the profiling run
-KERNEL_SOURCES = {"k_mmv": ["mmv.hip", "common.hpp"], "k_gemv": ["gemv.hip", "common.hpp"],
-                  "k_mmq": ["mmq.hip", "common.hpp"], "k_gemm_bf16": ["deq.hip", "common.hpp"]}
+KERNEL_SOURCES = {"k_mmv": ["mmv.hip", "common.hpp", "stream.hpp"], "k_gemv": ["gemv.hip", "common.hpp"],
+                  "k_mmq": ["mmq.hip", "common.hpp"], "k_mmqt": ["mmqt.hip", "common.hpp", "stream.hpp"],
+                  "k_gemm_bf16": ["deq.hip", "common.hpp"]}
 
 
 def kernel_name(M, N, K, path):
@@ -71,7 +72,9 @@ def kernel_name(M, N, K, path):
     if path == iq.PATH_DEQ_BF16:
         return "k_gemm_bf16"
     nb = K // 256
-    return "k_mmv" if M <= 32 and nb % 2 == 0 and N * nb * 136 < (1 << 31) else "k_mmq"
+    if M <= 32 and nb % 2 == 0 and N * nb * 136 < (1 << 31):
+        return "k_mmv"
+    return "k_mmqt" if M > 64 else "k_mmq"
 
 
 def source_hash(kernel):

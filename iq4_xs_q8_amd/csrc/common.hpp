@@ -189,14 +189,17 @@ struct MmvPlan {
 MmvPlan mmv_plan(int64_t M, int64_t N, int64_t K, int cus);
 hipError_t launch_mmv(const void *W, const XPlanes &x, float *Y, int64_t N, const MmvPlan &p,
                       hipStream_t s);
-// Tile kernel for M > 32 (mmqt.hip): 128 x 128 tiles, runs of (tile,
-// super-block) units over `grid` workgroups.
+// Tile kernel for M > 32 (mmqt.hip): 128 x 128 tiles, runs of (tile, half
+// super-block) units over `grid` workgroups; tiles shared by several
+// workgroups are summed from a workspace of partial tiles by a second kernel.
 struct MmqtPlan {
-    bool ok = false, zero_y = false;
+    bool ok = false;
     int grid = 0, mblocks = 0;
+    size_t workspace_bytes = 0;
 };
 MmqtPlan mmqt_plan(int64_t M, int64_t N, int64_t K, int cus);
-hipError_t launch_mmqt(const void *W, const XPlanes &x, float *Y, int64_t N, const MmqtPlan &p, hipStream_t s);
+hipError_t launch_mmqt(const void *W, const XPlanes &x, float *Y, int64_t N, const MmqtPlan &p, void *workspace,
+                       hipStream_t s);
 struct MmqPlan {
     int tm = 1, kw = 1, ks = 1;
     bool mmv = false;          // the streaming kernel runs (M <= 32)

@@ -10,9 +10,13 @@
 // Work split:
 //  * Output tiles are 128 activation rows (4 MFMA subtiles) x 128 weight rows
 //    (4 subtiles), ordered with the activation block fastest.  Units are
-//    (tile, super-block), tile-major; each workgroup gets one contiguous run
-//    of equal length (at least one tile's units, so a tile has at most two
-//    owners; shared tiles add into a zeroed Y: 0 + a + b == 0 + b + a).
+//    (tile, half super-block), tile-major; each workgroup gets one contiguous
+//    run of equal length (stream-K style: every compute unit gets the same
+//    work, also when there are fewer tiles than compute units).  A tile
+//    covered by one run is stored by its workgroup; the other workgroups
+//    store their partial tiles (at most two per run: its first and its last)
+//    in a workspace, and a second kernel adds the partials of every shared
+//    tile in run order, so the result does not depend on timing.
 //  * Half a super-block of a tile at a time (4 sub-blocks) goes straight
 //    from memory into one of five LDS buffers with 16-byte LDS-writing buffer
 //    loads: for each of the 128 weight rows its header and the half's 64
@@ -86,9 +90,18 @@ struct UnitCursor {
     }
 };
 
+// Partial tile slot (run g, 0 = its first tile, 1 = its last): 8 float4 per
+// thread, float4 e of thread tid at [e][tid] (coalesced stores and loads);
+// e = 4*i + r/4 for accumulator i, result register r.
+constexpr int SLOT_F4 = 8 * NTQ;
+__device__ __forceinline__ float4 *slot_at(float *ws, int g, int which)
+{
+    return reinterpret_cast<float4 *>(ws) + (size_t)(2 * g + which) * SLOT_F4;
+}
+
 __global__ void __launch_bounds__(NTQ, 1)
-k_mmqt(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__restrict__ Y, int M, int N,
-       int K, int Mp, int nb, int mblocks, int qb, int rb, int G)
+k_mmqt(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__restrict__ Y,
+       float *__restrict__ ws, int M, int N, int K, int Mp, int nb, int mblocks, int G, Runs runs)
 {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -98,7 +111,7 @@ k_mmqt(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__re
     // give the workgroups of one XCD consecutive runs, so that the activation
     // blocks that share a weight block meet in one L2.
     const int g = G % 8 == 0 ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
-    const int ua = g * qb + udiv31(g * rb, G), ub = (g + 1) * qb + udiv31((g + 1) * rb, G);
+    const int ua = runs.u[g], ub = runs.u[g + 1], t_first = runs.t[g];
     const uint32_t row_bytes = (uint32_t)nb * WBLK;
     const int dp_at = Mp * K;
     const __amdgpu_buffer_rsrc_t wr =
@@ -206,21 +219,31 @@ k_mmqt(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__re
             acc[i][r] = 0.0f;
     // result register r of lane (col, h) holds activation row 8*(r/4) + 4*h + r%4
     auto flush = [&](int t, bool owned) __attribute__((always_inline)) {
-        const int mb = t % mblocks, wb = t / mblocks;
-        const int n = wb * BN + nt * TILE + col;
+        if (owned) {
+            const int mb = t % mblocks, wb = t / mblocks;
+            const int n = wb * BN + nt * TILE + col;
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const int m = mb * BM + (2 * mp + i) * TILE + 8 * (r / 4) + 4 * h + (r % 4);
+                    if (m < M && n < N)
+                        Y[(int64_t)m * N + n] = acc[i][r];
+                }
+        } else {
+            float4 *slot = slot_at(ws, g, t == t_first ? 0 : 1);
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+#pragma unroll
+                for (int q = 0; q < 4; q++)
+                    slot[(4 * i + q) * NTQ + tid] =
+                        make_float4(acc[i][4 * q], acc[i][4 * q + 1], acc[i][4 * q + 2], acc[i][4 * q + 3]);
+        }
 #pragma unroll
         for (int i = 0; i < 2; i++)
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int m = mb * BM + (2 * mp + i) * TILE + 8 * (r / 4) + 4 * h + (r % 4);
-                if (m < M && n < N) {
-                    if (owned)
-                        Y[(int64_t)m * N + n] = acc[i][r];
-                    else
-                        atomicAdd(Y + (int64_t)m * N + n, acc[i][r]);
-                }
+            for (int r = 0; r < 16; r++)
                 acc[i][r] = 0.0f;
-            }
     };
     auto compute = [&](const Chunk &c, auto bc) __attribute__((always_inline)) {
         const char *B = lds_area<decltype(bc)::value, BUFQ>();
@@ -267,7 +290,7 @@ k_mmqt(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__re
     cur.ub = ub;
     cur.nh = 2 * nb;
     cur.u = ua;
-    cur.t = udiv31(ua, 2 * nb);
+    cur.t = t_first;
     cur.j = ua - cur.t * 2 * nb;
     Chunk info[NBUFQ];
     static_for(std::make_integer_sequence<int, NBUFQ - 1>(), [&](auto bc) {
@@ -307,6 +330,56 @@ k_mmqt(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__re
     __builtin_amdgcn_s_waitcnt(wait_vm_lds(0));
 }
 
+// The shared tiles: workgroup k takes the tile its run starts in when the run
+// starts inside that tile and reaches the tile's end (each shared tile is the
+// first tile of exactly one such run, the last of its owners), and adds the
+// partials of the owners k', k'+1, .., k in that order.
+__global__ void __launch_bounds__(NTQ, 1)
+k_mmqt_fix(const float *__restrict__ ws, float *__restrict__ Y, int M, int N, int nh, int mblocks, Runs runs)
+{
+    const int k = blockIdx.x, tid = threadIdx.x;
+    const int t = runs.t[k];
+    const int t0 = t * nh;
+    if (runs.u[k] == runs.u[k + 1] || runs.u[k] == t0 || runs.u[k + 1] < t0 + nh)
+        return;                                               // (uniform) not such a run
+    int g0 = k - 1;
+    while (runs.u[g0] > t0)                                    // runs.u[0] == 0 <= t0
+        g0--;
+    float4 sum[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++)
+        sum[e] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int gg = g0; gg <= k; gg++) {
+        if (runs.u[gg] == runs.u[gg + 1])
+            continue;
+        const float4 *slot = reinterpret_cast<const float4 *>(ws) +
+                             (size_t)(2 * gg + (runs.t[gg] == t ? 0 : 1)) * SLOT_F4;
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            const float4 v = slot[e * NTQ + tid];
+            sum[e].x += v.x;
+            sum[e].y += v.y;
+            sum[e].z += v.z;
+            sum[e].w += v.w;
+        }
+    }
+    const int lane = tid & 63, wave = tid >> 6;
+    const int nt = wave & 3, mp = wave >> 2, col = lane & 31, h = lane >> 5;
+    const int mb = t % mblocks, wb = t / mblocks;
+    const int n = wb * BN + nt * TILE + col;
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+        const float v4[4] = {sum[e].x, sum[e].y, sum[e].z, sum[e].w};
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+            const int i = e / 4, r = 4 * (e % 4) + c;
+            const int m = mb * BM + (2 * mp + i) * TILE + 8 * (r / 4) + 4 * h + (r % 4);
+            if (m < M && n < N)
+                Y[(int64_t)m * N + n] = v4[c];
+        }
+    }
+}
+
 }  // namespace
 
 MmqtPlan mmqt_plan(int64_t M, int64_t N, int64_t K, int cus)
@@ -316,37 +389,47 @@ MmqtPlan mmqt_plan(int64_t M, int64_t N, int64_t K, int cus)
     const int64_t Mp = round_up(M, MPAD);
     const int64_t mblocks = (M + BM - 1) / BM, wblocks = (N + BN - 1) / BN;
     const int64_t T = mblocks * wblocks, U = T * 2 * nb;
-    // 32-bit offsets; no more workgroups than tiles (a run covers at least one
-    // tile's units, so a tile has at most two owners).  Measured on MI355X:
-    // with M <= 64 (half a tile of real rows) or fewer than 64 tiles the
-    // K-split kernel of mmq.hip is faster (M=64, 10240 x 5120: 50 vs 108 us;
-    // M=96, 5120 x 17408: 197 vs 335 us), from M=96 and 64 tiles on this one
-    // (M=96, 17408 x 5120: 113 vs 182 us; M=512, 10240 x 5120: 168 vs 442 us).
-    if (M <= 2 * TILE || T < 64 || nb >= (1 << 15) || N * row_bytes >= (1LL << 31) ||
+    // 32-bit offsets.  Measured on MI355X: with M <= 64 (half a tile of real
+    // rows) the K-split kernel of mmq.hip is faster (M=64, 10240 x 5120: 50
+    // vs 108 us).
+    if (M <= 2 * TILE || nb >= (1 << 15) || N * row_bytes >= (1LL << 31) ||
         Mp * K + Mp * K / 8 + BM * 288 >= (1LL << 31) || U >= (1LL << 31))
         return p;
-    p.grid = (int)std::min<int64_t>(T, cus);
+    // every run at least MIN_RUN units, so that writing and re-reading a
+    // partial tile (64 KB) stays small against the run's work
+    constexpr int64_t MIN_RUN = 8;
+    int64_t G = U / MIN_RUN;
+    G = std::min<int64_t>(G, std::min<int64_t>(cus, MAXG));
+    p.grid = (int)std::max<int64_t>(G, 1);
     p.mblocks = (int)mblocks;
-    p.zero_y = false;
-    for (int64_t g = 1; g < p.grid; g++)
-        if (U * g / p.grid % (2 * nb) != 0) {
-            p.zero_y = true;
-            break;
-        }
+    p.workspace_bytes = (size_t)p.grid * 2 * SLOT_F4 * sizeof(float4);
     p.ok = true;
     return p;
 }
 
-hipError_t launch_mmqt(const void *W, const XPlanes &x, float *Y, int64_t N, const MmqtPlan &p, hipStream_t s)
+hipError_t launch_mmqt(const void *W, const XPlanes &x, float *Y, int64_t N, const MmqtPlan &p, void *workspace,
+                       hipStream_t s)
 {
-    if (!p.ok)
+    if (!p.ok || p.grid < 1 || p.grid > MAXG || workspace == nullptr)
         return hipErrorInvalidValue;
     if ((const char *)x.dp != (const char *)x.qp + x.Mp * x.K)
         return hipErrorInvalidValue;
-    const int nb = (int)(x.K / QK);
-    const int64_t U = (int64_t)p.mblocks * ((N + BN - 1) / BN) * 2 * nb;
-    hipLaunchKernelGGL(k_mmqt, dim3((unsigned)p.grid), dim3(NTQ), 0, s, (const uint8_t *)W, x.qp, Y, (int)x.M,
-                       (int)N, (int)x.K, (int)x.Mp, nb, p.mblocks, (int)(U / p.grid), (int)(U % p.grid), p.grid);
+    const int nb = (int)(x.K / QK), nh = 2 * nb;
+    const int64_t U = (int64_t)p.mblocks * ((N + BN - 1) / BN) * nh;
+    Runs runs;
+    for (int g = 0; g <= p.grid; g++) {
+        runs.u[g] = (int)(U * g / p.grid);
+        if (g < p.grid)
+            runs.t[g] = runs.u[g] / nh;
+    }
+    float *ws = (float *)workspace;
+    hipLaunchKernelGGL(k_mmqt, dim3((unsigned)p.grid), dim3(NTQ), 0, s, (const uint8_t *)W, x.qp, Y, ws, (int)x.M,
+                       (int)N, (int)x.K, (int)x.Mp, nb, p.mblocks, p.grid, runs);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(k_mmqt_fix, dim3((unsigned)p.grid), dim3(NTQ), 0, s, (const float *)ws, Y, (int)x.M,
+                       (int)N, nh, p.mblocks, runs);
     return hipGetLastError();
 }
 

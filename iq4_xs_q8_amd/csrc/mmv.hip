@@ -106,14 +106,6 @@ struct Cfg {
     static_assert(NBUF >= 2 && TOTAL <= 160 * 1024, "LDS budget");
 };
 
-// The workgroups' runs, computed on the host: workgroup g takes units
-// [u[g], u[g+1]) and starts in tile t[g].
-constexpr int MAXG = 256;
-struct Runs {
-    int u[MAXG + 1];
-    int t[MAXG];
-};
-
 // Result register r of lane (col, h) holds row 8*(r/4) + 4*h + r%4.
 template <int LIVE>
 __device__ __forceinline__ void epilogue(const v16i &D, float sw, const float4 *dx, float acc[LIVE])

@@ -156,6 +156,14 @@ struct Chunk {
 };
 
 // Walks the run [ua, ub) of units in chunks (all values wavefront-uniform).
+// Runs of units over at most MAXG workgroups, computed on the host: run g is
+// units [u[g], u[g+1]) and starts in tile t[g].
+constexpr int MAXG = 256;
+struct Runs {
+    int u[MAXG + 1];
+    int t[MAXG];
+};
+
 struct Cursor {
     int u, t, j, ua, ub, nb;
     __device__ Chunk next(int ch)

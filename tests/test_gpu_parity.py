@@ -176,12 +176,15 @@ def test_deterministic_and_invariant(path):
     assert torch.equal(y_row[0], y1[1])
 
 
-@pytest.mark.parametrize("M,N,K", [(300, 2800, 512), (97, 8200, 256), (130, 8320, 1024)])
+@pytest.mark.parametrize("M,N,K", [(300, 2800, 512), (97, 8200, 256), (130, 8320, 1024),
+                                   (100, 200, 4096), (130, 1000, 2048), (257, 384, 8192), (200, 300, 2816)])
 def test_tile_kernel_shapes(M, N, K):
-    """Shapes the 128 x 128 tile kernel takes (M > 64, at least 64 tiles):
-    ragged M and N, K of one super-block (runs cross tiles, so tiles are
-    shared by two workgroups and added into a zeroed Y), several super-blocks;
-    through gemm, gemm_act and both Y-zeroing routes, bit-identical."""
+    """Shapes the 128 x 128 tile kernel takes (M > 64): ragged M and N, K of
+    one super-block (runs cross tiles), few tiles and long K (runs shorter
+    than a tile: two to eight workgroups share a tile, their partial tiles
+    summed in run order by the second kernel; run bounds on and off tile and
+    super-block boundaries); through gemm and gemm_act (with and without the
+    Y-zeroed hint, which this path does not need), bit-identical."""
     W, X = _inputs(M, N, K, seed=M + N)
     ref = O.gemm_q8_1(W, O.quantize_q8_1(X), K)
     Wd, Xd = dev(W), dev(X)
