@@ -117,6 +117,9 @@ int ensure_init()
 // The current device must be a gfx950 and the table must be for it.
 int check_device()
 {
+    // (the built-in table, at least, is loaded by the first call of any entry
+    // point, whichever path it names)
+    ensure_init();
     int dev = -1, count = 0;
     if (hipGetDeviceCount(&count) != hipSuccess || count < 1) {
         (void)hipGetLastError();
@@ -221,6 +224,7 @@ int resolve_path(int path, int64_t M, int64_t N, int64_t K, int *out)
 {
     if (path < 0 || path >= IQ4XS_NUM_PATHS)
         return fail(IQ4XS_EINVAL, "unknown path %d", path);
+    ensure_init();
     if (path == IQ4XS_PATH_AUTO) {
         int st = ensure_init();
         if (st != IQ4XS_OK)

@@ -194,7 +194,7 @@ hipError_t launch_mmv(const void *W, const XPlanes &x, float *Y, int64_t N, cons
 // workgroups are summed from a workspace of partial tiles by a second kernel.
 struct MmqtPlan {
     bool ok = false;
-    int grid = 0, mblocks = 0;
+    int grid = 0, mblocks = 0, bm = 0;
     size_t workspace_bytes = 0;
 };
 MmqtPlan mmqt_plan(int64_t M, int64_t N, int64_t K, int cus);

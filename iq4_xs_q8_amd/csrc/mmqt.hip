@@ -51,22 +51,31 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
 constexpr int TILE = 32;
-constexpr int BM = 128, BN = 128;          // output tile: activation rows x weight rows
 constexpr int NWQ = 8, NTQ = 64 * NWQ;     // wavefronts, threads per workgroup
 constexpr int HALF = SUBS / 2;             // sub-blocks per step
 constexpr int WROWQ = 80;                  // LDS weight row: header, 8 unused, 64 index bytes
-constexpr int W_BYTES = BN * WROWQ;        // 10 KB
-constexpr int A_OFF = W_BYTES, A_BYTES = HALF * BM * SB;              // 16 KB
-constexpr int D_OFF = A_OFF + A_BYTES, D_BYTES = HALF * BM * 4;       // 2 KB
-constexpr int DUMP = D_OFF + D_BYTES;                                  // slots without a job
-constexpr int BUFQ = DUMP + 1024;
 constexpr int NBUFQ = 5;
-constexpr int JW = W_BYTES / 1024, JA = A_BYTES / 1024, JD = (D_BYTES + 1023) / 1024;
 constexpr int NLQ = NWQ - 1;               // copying wavefronts (the last one prefetches)
-constexpr int SLOTS = (JW + JA + JD + NLQ - 1) / NLQ;
 constexpr int PF_PER_STEP = 4;             // touch loads per step of the prefetching wavefront
 constexpr int PF_START = 24;               // and at the start
-static_assert(W_BYTES % 1024 == 0 && D_BYTES == 2048 && NBUFQ * BUFQ + 256 <= 160 * 1024, "LDS budget");
+
+// Output tile BM activation rows x BN weight rows: 128 x 128, or 64 x 256 for
+// M <= 64.  Wavefront w owns weight subtile w % (BN/32) and the activation
+// subtile pair w / (BN/32).  One LDS buffer: weights [BN][80], activations
+// [HALF][BM][32], scales [HALF][BM], 1 KB for slots without a job.
+template <int BM_, int BN_>
+struct QCfg {
+    static constexpr int BM = BM_, BN = BN_, NTW = BN / TILE;
+    static constexpr int W_BYTES = BN * WROWQ;
+    static constexpr int A_OFF = W_BYTES, A_BYTES = HALF * BM * SB;
+    static constexpr int D_OFF = A_OFF + A_BYTES, D_BYTES = HALF * BM * 4;
+    static constexpr int DUMP = D_OFF + D_BYTES;
+    static constexpr int BUFQ = DUMP + 1024;
+    static constexpr int JW = W_BYTES / 1024, JA = A_BYTES / 1024, JD = D_BYTES / 1024;
+    static constexpr int SLOTS = (JW + JA + JD + NLQ - 1) / NLQ;
+    static_assert(NTW * (BM / (2 * TILE)) == NWQ, "eight wavefronts: weight subtile x activation pair");
+    static_assert(W_BYTES % 1024 == 0 && D_BYTES % 1024 == 0 && NBUFQ * BUFQ + 256 <= 160 * 1024, "LDS budget");
+};
 
 // Unit cursor: one half super-block of one tile per step (j counts halves,
 // nh = 2 * K/256 of them per tile).
@@ -99,13 +108,16 @@ __device__ __forceinline__ float4 *slot_at(float *ws, int g, int which)
     return reinterpret_cast<float4 *>(ws) + (size_t)(2 * g + which) * SLOT_F4;
 }
 
+template <class C>
 __global__ void __launch_bounds__(NTQ, 1)
 k_mmqt(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__restrict__ Y,
        float *__restrict__ ws, int M, int N, int K, int Mp, int nb, int mblocks, int G, Runs runs)
 {
+    constexpr int BM = C::BM, BN = C::BN, SLOTS = C::SLOTS, JW = C::JW, JA = C::JA, JD = C::JD;
+    constexpr int A_OFF = C::A_OFF, D_OFF = C::D_OFF, BUFQ = C::BUFQ;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int nt = wave & 3, mp = wave >> 2;                  // weight subtile, activation pair
+    const int nt = wave % C::NTW, mp = wave / C::NTW;        // weight subtile, activation pair
     const int col = lane & 31, h = lane >> 5;
     // Workgroups are dealt round-robin to the 8 XCDs (each with its own L2):
     // give the workgroups of one XCD consecutive runs, so that the activation
@@ -138,18 +150,18 @@ k_mmqt(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__re
             p_go1[k] = (uint32_t)r * row_bytes + (pc == 0 ? 0 : 16 * pc + 56);
         } else if (job < JW + JA) {
             const int a = job - JW;                               // 1 KB = 32 rows of one sub-block
-            const int sb = a >> 2, r = 32 * (a & 3) + (lane >> 1);
+            const int sb = a / (BM / TILE), r = TILE * (a % (BM / TILE)) + (lane >> 1);
             p_dst[k] = A_OFF + 1024 * a;
             p_kind[k] = 1;
             p_go0[k] = p_go1[k] = (uint32_t)((sb * Mp + r) * SB + 16 * (lane & 1));
         } else if (job < JW + JA + JD) {
-            const int d = job - JW - JA;                          // 1 KB = 2 sub-blocks x 128 scales
-            const int sb = 2 * d + (lane >> 5), r = 4 * (lane & 31);
+            const int d = job - JW - JA;                          // 1 KB = 1024/(4 BM) sub-blocks' scales
+            const int sb = (256 / BM) * d + lane / (BM / 4), r = 4 * (lane % (BM / 4));
             p_dst[k] = D_OFF + 1024 * d;
             p_kind[k] = 2;
             p_go0[k] = p_go1[k] = (uint32_t)((sb * Mp + r) * 4);
         } else {
-            p_dst[k] = DUMP;
+            p_dst[k] = C::DUMP;
             p_kind[k] = 3;
             p_go0[k] = p_go1[k] = OOB;
         }
@@ -334,9 +346,11 @@ k_mmqt(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__re
 // starts inside that tile and reaches the tile's end (each shared tile is the
 // first tile of exactly one such run, the last of its owners), and adds the
 // partials of the owners k', k'+1, .., k in that order.
+template <class C>
 __global__ void __launch_bounds__(NTQ, 1)
 k_mmqt_fix(const float *__restrict__ ws, float *__restrict__ Y, int M, int N, int nh, int mblocks, Runs runs)
 {
+    constexpr int BM = C::BM, BN = C::BN;
     const int k = blockIdx.x, tid = threadIdx.x;
     const int t = runs.t[k];
     const int t0 = t * nh;
@@ -364,7 +378,7 @@ k_mmqt_fix(const float *__restrict__ ws, float *__restrict__ Y, int M, int N, in
         }
     }
     const int lane = tid & 63, wave = tid >> 6;
-    const int nt = wave & 3, mp = wave >> 2, col = lane & 31, h = lane >> 5;
+    const int nt = wave % C::NTW, mp = wave / C::NTW, col = lane & 31, h = lane >> 5;
     const int mb = t % mblocks, wb = t / mblocks;
     const int n = wb * BN + nt * TILE + col;
 #pragma unroll
@@ -380,6 +394,21 @@ k_mmqt_fix(const float *__restrict__ ws, float *__restrict__ Y, int M, int N, in
     }
 }
 
+template <class C>
+hipError_t launch_cfg(const void *W, const XPlanes &x, float *Y, float *ws, int64_t N, const MmqtPlan &p,
+                      const Runs &runs, hipStream_t s)
+{
+    const int nb = (int)(x.K / QK);
+    hipLaunchKernelGGL((k_mmqt<C>), dim3((unsigned)p.grid), dim3(NTQ), 0, s, (const uint8_t *)W, x.qp, Y, ws,
+                       (int)x.M, (int)N, (int)x.K, (int)x.Mp, nb, p.mblocks, p.grid, runs);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL((k_mmqt_fix<C>), dim3((unsigned)p.grid), dim3(NTQ), 0, s, (const float *)ws, Y,
+                       (int)x.M, (int)N, 2 * nb, p.mblocks, runs);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 MmqtPlan mmqt_plan(int64_t M, int64_t N, int64_t K, int cus)
@@ -387,12 +416,12 @@ MmqtPlan mmqt_plan(int64_t M, int64_t N, int64_t K, int cus)
     MmqtPlan p;
     const int64_t nb = K / QK, row_bytes = nb * WBLK;
     const int64_t Mp = round_up(M, MPAD);
+    // 64 x 256 tiles up to M = 64, else 128 x 128
+    const int64_t BM = M <= 2 * TILE ? 64 : 128, BN = 16384 / BM;
     const int64_t mblocks = (M + BM - 1) / BM, wblocks = (N + BN - 1) / BN;
     const int64_t T = mblocks * wblocks, U = T * 2 * nb;
-    // 32-bit offsets.  Measured on MI355X: with M <= 64 (half a tile of real
-    // rows) the K-split kernel of mmq.hip is faster (M=64, 10240 x 5120: 50
-    // vs 108 us).
-    if (M <= 2 * TILE || nb >= (1 << 15) || N * row_bytes >= (1LL << 31) ||
+    // 32-bit offsets
+    if (M <= TILE || nb >= (1 << 15) || N * row_bytes >= (1LL << 31) ||
         Mp * K + Mp * K / 8 + BM * 288 >= (1LL << 31) || U >= (1LL << 31))
         return p;
     // every run at least MIN_RUN units, so that writing and re-reading a
@@ -402,6 +431,7 @@ MmqtPlan mmqt_plan(int64_t M, int64_t N, int64_t K, int cus)
     G = std::min<int64_t>(G, std::min<int64_t>(cus, MAXG));
     p.grid = (int)std::max<int64_t>(G, 1);
     p.mblocks = (int)mblocks;
+    p.bm = (int)BM;
     p.workspace_bytes = (size_t)p.grid * 2 * SLOT_F4 * sizeof(float4);
     p.ok = true;
     return p;
@@ -415,6 +445,7 @@ hipError_t launch_mmqt(const void *W, const XPlanes &x, float *Y, int64_t N, con
     if ((const char *)x.dp != (const char *)x.qp + x.Mp * x.K)
         return hipErrorInvalidValue;
     const int nb = (int)(x.K / QK), nh = 2 * nb;
+    const int64_t BN = 16384 / p.bm;
     const int64_t U = (int64_t)p.mblocks * ((N + BN - 1) / BN) * nh;
     Runs runs;
     for (int g = 0; g <= p.grid; g++) {
@@ -423,14 +454,11 @@ hipError_t launch_mmqt(const void *W, const XPlanes &x, float *Y, int64_t N, con
             runs.t[g] = runs.u[g] / nh;
     }
     float *ws = (float *)workspace;
-    hipLaunchKernelGGL(k_mmqt, dim3((unsigned)p.grid), dim3(NTQ), 0, s, (const uint8_t *)W, x.qp, Y, ws, (int)x.M,
-                       (int)N, (int)x.K, (int)x.Mp, nb, p.mblocks, p.grid, runs);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess)
-        return e;
-    hipLaunchKernelGGL(k_mmqt_fix, dim3((unsigned)p.grid), dim3(NTQ), 0, s, (const float *)ws, Y, (int)x.M,
-                       (int)N, nh, p.mblocks, runs);
-    return hipGetLastError();
+    if (p.bm == 64)
+        return launch_cfg<QCfg<64, 256>>(W, x, Y, ws, N, p, runs, s);
+    if (p.bm == 128)
+        return launch_cfg<QCfg<128, 128>>(W, x, Y, ws, N, p, runs, s);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace iq4xs

@@ -6,6 +6,10 @@ oracle of its own formulation (integer dot for GEMV and MMQ, bf16 products
 for DEQ_BF16); a reference row that is exactly zero must come back exactly
 zero.  Every output buffer is poisoned first and checked to be fully written.
 """
+import os
+import subprocess
+import sys
+
 import numpy as np
 import pytest
 import torch
@@ -15,6 +19,8 @@ import oracle
 import oracle_pins
 import synth
 from gpu_util import ROW_TOL, assert_rows_close, dev, poisoned
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 pytestmark = pytest.mark.gpu
 
@@ -177,9 +183,11 @@ def test_deterministic_and_invariant(path):
 
 
 @pytest.mark.parametrize("M,N,K", [(300, 2800, 512), (97, 8200, 256), (130, 8320, 1024),
-                                   (100, 200, 4096), (130, 1000, 2048), (257, 384, 8192), (200, 300, 2816)])
+                                   (100, 200, 4096), (130, 1000, 2048), (257, 384, 8192), (200, 300, 2816),
+                                   (40, 1000, 2048), (64, 600, 4096), (50, 5000, 512), (33, 300, 2816)])
 def test_tile_kernel_shapes(M, N, K):
-    """Shapes the 128 x 128 tile kernel takes (M > 64): ragged M and N, K of
+    """Shapes the tile kernel takes (128 x 128 tiles for M > 64, 64 x 256 for
+    32 < M <= 64): ragged M and N, K of
     one super-block (runs cross tiles), few tiles and long K (runs shorter
     than a tile: two to eight workgroups share a tile, their partial tiles
     summed in run order by the second kernel; run bounds on and off tile and
@@ -197,6 +205,37 @@ def test_tile_kernel_shapes(M, N, K):
                      y_zeroed=True).cpu().numpy()
     assert np.array_equal(y, y2) and np.array_equal(y, y3)
     assert torch.equal(iq.gemm(Wd, Xd, path=iq.PATH_MMQ).cpu(), torch.from_numpy(y)), "two runs differ"
+
+
+def test_ksplit_kernel_when_the_others_are_switched_off(tmp_path):
+    """The K-split kernel of the MMQ path (the fallback for shapes the
+    streaming and tile kernels do not take, and for odd K/256 at M <= 32),
+    forced for every M by switching the other two off; it runs in a child
+    process because the switches are read once per process."""
+    shapes = [(8, 300, 1024), (48, 300, 1280), (64, 97, 768), (100, 200, 2048)]
+    inputs = {}
+    for i, (M, N, K) in enumerate(shapes):
+        W, X = _inputs(M, N, K, seed=40 + i)
+        np.save(tmp_path / f"w{i}.npy", W)
+        np.save(tmp_path / f"x{i}.npy", X)
+        inputs[i] = (W, X)
+    code = (
+        "import sys, numpy as np, torch\n"
+        "import iq4_xs_q8_amd as iq\n"
+        f"d = {str(tmp_path)!r}\n"
+        f"for i in range({len(shapes)}):\n"
+        "    W = torch.from_numpy(np.load(f'{d}/w{i}.npy')).cuda()\n"
+        "    X = torch.from_numpy(np.load(f'{d}/x{i}.npy')).cuda()\n"
+        "    Y = torch.full((X.shape[0], W.shape[0]), float('nan'), device='cuda')\n"
+        "    iq.gemm(W, X, path=iq.PATH_MMQ, out=Y)\n"
+        "    np.save(f'{d}/y{i}.npy', Y.cpu().numpy())\n")
+    env = dict(os.environ, IQ4XS_MMV="0", IQ4XS_TILE="0",
+               PYTHONPATH=os.pathsep.join([ROOT, os.environ.get("PYTHONPATH", "")]))
+    subprocess.run([sys.executable, "-c", code], env=env, check=True, timeout=120)
+    for i, (M, N, K) in enumerate(shapes):
+        W, X = inputs[i]
+        y = np.load(tmp_path / f"y{i}.npy")
+        assert_rows_close(y, O.gemm_q8_1(W, O.quantize_q8_1(X), K), what=f"k_mmq M={M} N={N} K={K}")
 
 
 def test_negative_control_corrupted_weight_fails():
