@@ -19,20 +19,16 @@
 //    tile in run order, so the result does not depend on timing.
 //  * Half a super-block of a tile at a time (4 sub-blocks) goes straight
 //    from memory into one of five LDS buffers with 16-byte LDS-writing buffer
-//    loads: for each of the 128 weight rows its header and the half's 64
-//    index bytes (an 80-byte LDS row), the 128 activation rows of the 4
-//    sub-blocks (sub-block-major planes, 4 KB per sub-block) and their 512
-//    scales.  The loads of a half run four halves ahead of its use, so the
-//    memory system always has about 90 KB per compute unit in flight; one
-//    barrier per half.
-//  * A half super-block reads only 80 of a weight row's 2720+ bytes, a
-//    pattern HBM serves poorly; so the last wavefront copies nothing but walks
-//    the run ahead, tile portion by tile portion, touching each weight row's
-//    whole byte range of the portion (4-byte loads 64 bytes apart: long
-//    contiguous runs), which brings the weights into the caches before the
-//    copies ask for them.
-//  * Eight wavefronts: wavefront w owns weight subtile w%4 and activation
-//    subtiles 2*(w/4), 2*(w/4)+1, i.e. 2 x 16 accumulators per lane.  Per
+//    loads: for each of the BN weight rows its header and the half's 64 index
+//    bytes (an 80-byte LDS row), the BM activation rows of the 4 sub-blocks
+//    (sub-block-major planes) and their scales.  The loads of a half run four
+//    halves ahead of its use, so the memory system always has about 90 KB per
+//    compute unit in flight; one barrier per half.  (A wavefront that walked
+//    the run ahead touching whole weight rows, to turn the 72-byte pieces
+//    into long contiguous reads, made every measured shape 4-9% slower: it
+//    arrived last at every barrier.)
+//  * Eight wavefronts: wavefront w owns weight subtile w%(BN/32) and the
+//    activation subtile pair w/(BN/32), i.e. 2 x 16 accumulators per lane.  Per
 //    sub-block it expands its weight subtile's index bytes once (byte
 //    permutes) and uses them for both activation subtiles, so the fp32
 //    rescale of the integer dots (three VALU operations per output and
@@ -55,9 +51,7 @@ constexpr int NWQ = 8, NTQ = 64 * NWQ;     // wavefronts, threads per workgroup
 constexpr int HALF = SUBS / 2;             // sub-blocks per step
 constexpr int WROWQ = 80;                  // LDS weight row: header, 8 unused, 64 index bytes
 constexpr int NBUFQ = 5;
-constexpr int NLQ = NWQ - 1;               // copying wavefronts (the last one prefetches)
-constexpr int PF_PER_STEP = 4;             // touch loads per step of the prefetching wavefront
-constexpr int PF_START = 24;               // and at the start
+constexpr int NLQ = NWQ;                   // copying wavefronts
 
 // Output tile BM activation rows x BN weight rows: 128 x 128, or 64 x 256 for
 // M <= 64.  Wavefront w owns weight subtile w % (BN/32) and the activation
@@ -140,7 +134,7 @@ k_mmqt(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__re
     uint32_t p_go0[SLOTS], p_go1[SLOTS];
 #pragma unroll
     for (int k = 0; k < SLOTS; k++) {
-        const int job = wave < NLQ ? wave * SLOTS + k : 1 << 20;
+        const int job = wave * SLOTS + k;
         if (job < JW) {
             const int at = 1024 * job + 16 * lane;
             const int r = at / WROWQ, pc = (at - r * WROWQ) / 16;   // row, piece (5 per row)
@@ -168,11 +162,8 @@ k_mmqt(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__re
     }
     // tile t -> (activation block, weight block), the activation block fastest;
     // unit half j: super-block j/2, sub-blocks 4*(j%2) .. 4*(j%2)+3
-    const bool pf_wave = wave == NWQ - 1;                    // (uniform)
     auto issue = [&](const Chunk &c, auto bc) __attribute__((always_inline)) {
         char *buf = lds_area<decltype(bc)::value, BUFQ>();
-        if (pf_wave)
-            return;
         const int mb = c.t % mblocks, wb = c.t / mblocks, js = c.j0 >> 1, hf = c.j0 & 1;
         const bool live = c.cl > 0;
         const uint32_t wbase = (uint32_t)wb * BN * row_bytes + (uint32_t)js * WBLK;
@@ -186,42 +177,6 @@ k_mmqt(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__re
             load_lds16(p_kind[k] == 0 ? wr : xr, buf + p_dst[k], ok ? (hf ? p_go1[k] : p_go0[k]) + base : OOB);
         }
     };
-
-    // Prefetch walker (last wavefront): the run's tile portions in order; a
-    // portion is (tile, super-blocks [ja, jb)) of its 128 weight rows, touched
-    // as rows x q points, q = 0 .. Q-1 at 64-byte steps over [ja, jb)*136.
-    int pf_u = ua;                  // first half-unit of the current portion
-    int pf_t = 0, pf_ja = 0, pf_q = 0, pf_n = 0, pf_i = 0;   // portion, points per row, loads, next load
-    auto pf_portion = [&]() __attribute__((always_inline)) {
-        pf_t = udiv31(pf_u, 2 * nb);
-        const int j2a = pf_u - pf_t * 2 * nb;
-        const int j2b = min(2 * nb, ub - pf_t * 2 * nb);
-        pf_ja = j2a >> 1;
-        const int jb = (j2b + 1) >> 1;
-        pf_q = ((jb - pf_ja) * WBLK + 63) / 64 + 1;
-        pf_n = (BN * pf_q + 63) / 64;
-        pf_i = 0;
-        pf_u = pf_t * 2 * nb + j2b;
-    };
-    auto prefetch = [&](int count) __attribute__((always_inline)) {
-        for (int k = 0; k < count; k++) {
-            if (pf_i == pf_n) {
-                if (pf_u >= ub)
-                    return;
-                pf_portion();
-            }
-            const int wb = pf_t / mblocks;
-            const int idx = 64 * pf_i + lane;
-            const int r = udiv31(idx, pf_q), q = idx - r * pf_q;
-            const uint32_t off = (uint32_t)(wb * BN + r) * row_bytes + (uint32_t)pf_ja * WBLK + 64u * q;
-            touch_lds4(wr, lds_area<-1, 256>(), r < BN ? off : OOB);
-            pf_i++;
-        }
-    };
-    if (pf_wave) {
-        pf_n = pf_i = 0;
-        prefetch(PF_START);
-    }
 
     float acc[2][16];
 #pragma unroll
@@ -317,28 +272,20 @@ k_mmqt(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__re
         constexpr int b = decltype(bc)::value, nxt = (b + NBUFQ - 1) % NBUFQ;
         if (info[b].cl == 0)
             return false;
-        if (!pf_wave)
-            __builtin_amdgcn_s_waitcnt(wait_vm_lds(SLOTS * (NBUFQ - 2)));
+        __builtin_amdgcn_s_waitcnt(wait_vm_lds(SLOTS * (NBUFQ - 2)));
         raw_barrier();
         info[nxt] = cur.next();
         issue(info[nxt], std::integral_constant<int, nxt>());
-        if (pf_wave)
-            prefetch(PF_PER_STEP);
         compute(info[b], bc);
         return true;
     };
-    for (;;) {
-        if (!step(std::integral_constant<int, 0>()))
-            break;
-        if (!step(std::integral_constant<int, 1>()))
-            break;
-        if (!step(std::integral_constant<int, 2>()))
-            break;
-        if (!step(std::integral_constant<int, 3>()))
-            break;
-        if (!step(std::integral_constant<int, 4>()))
-            break;
-    }
+    bool go = true;
+    do
+        static_for(std::make_integer_sequence<int, NBUFQ>(), [&](auto bc) __attribute__((always_inline)) {
+            if (go)
+                go = step(bc);
+        });
+    while (go);
     __builtin_amdgcn_s_waitcnt(wait_vm_lds(0));
 }
 

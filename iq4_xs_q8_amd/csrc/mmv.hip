@@ -388,11 +388,13 @@ k_mmv(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__res
         compute(info[b], bc);
         return true;
     };
-    for (bool go = true; go;)
+    bool go = true;
+    do
         static_for(std::make_integer_sequence<int, NBUF>(), [&](auto bc) __attribute__((always_inline)) {
             if (go)
                 go = step(bc);
         });
+    while (go);
     // no load may still write this workgroup's LDS when it ends
     __builtin_amdgcn_s_waitcnt(wait_vm_lds(0));
 }

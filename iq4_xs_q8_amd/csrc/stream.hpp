@@ -54,16 +54,6 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, const ch
                  : "s"(m0), "v"(voffset), "s"(rsrc)
                  : "memory", "m0");
 }
-// The same with 4 bytes per lane (lds_dst + 4*i): used only to pull lines
-// into the caches ahead of their 16-byte copies.
-__device__ __forceinline__ void touch_lds4(__amdgpu_buffer_rsrc_t rsrc, const char *lds_dst, uint32_t voffset)
-{
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_dst);
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-                 :
-                 : "s"(m0), "v"(voffset), "s"(rsrc)
-                 : "memory", "m0");
-}
 // x / D for 0 <= x < LIM with one 24-bit multiply and a shift: the smallest
 // shift S whose multiplier ceil(2^S / D) gives the exact quotient for every
 // x < LIM, checked exhaustively at compile time.
@@ -119,33 +109,6 @@ __device__ __forceinline__ void raw_barrier()
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-}
-
-// x / d for 0 <= x < 2^31 and 1 <= d < 2^16: a float reciprocal estimate,
-// refined once, then corrected to the exact quotient (cheap for the uniform
-// values here, unlike a full integer division).
-__device__ __forceinline__ int udiv31(int x, int d)
-{
-    const float rd = __builtin_amdgcn_rcpf((float)d);
-    int q = (int)((float)x * rd);
-    int r = (int)((uint32_t)x - (uint32_t)q * (uint32_t)d);
-    q += (int)((float)r * rd);
-    r = (int)((uint32_t)x - (uint32_t)q * (uint32_t)d);
-    if (r < 0) {
-        q--;
-        r += d;
-    }
-    if (r < 0) {
-        q--;
-        r += d;
-    }
-    if (r >= d) {
-        q++;
-        r -= d;
-    }
-    if (r >= d)
-        q++;
-    return q;
 }
 
 // A chunk: tile t, super-blocks j0..j0+cl-1 (cl = 0: past the run), flags
