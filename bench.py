@@ -5,11 +5,12 @@ Default run: `python bench.py [--steps K] [--warmup W]`.
 One *step* is the whole hot path over the decode sweep of the attention/GDN
 input-projection shape, N=10240, K=5120: for each M in {1, 2, 4, 8, 16} one
 iq4xs_gemm_ws call (Q8_1 quantization of X on the device, the dispatcher's
-choice of path, the matmul), with all inputs resident in HBM.  The calls of a
-step are recorded into a HIP graph and replayed (one graph per group of
-weight copies); weight copies are rotated (>= 640 MB in total) so the 256 MB
-Infinity Cache cannot serve them.  The same step launched eagerly from the
-host is reported as eager_ms_per_step.
+choice of path, the matmul), with all inputs resident in HBM, launched on one
+stream (the host runs ahead of the device, so the time is the device's);
+weight copies are rotated (>= 640 MB in total) so the 256 MB Infinity Cache
+cannot serve them.  The same calls recorded into HIP graphs and replayed are
+reported as graph_ms_per_step (slower here: the replay leaves larger gaps
+between the ten short kernels).
 
 Printed: one JSON line with
   value      whole-step weight bandwidth = weight bytes read / step time (GB/s)
@@ -303,6 +304,28 @@ def summarize_pmc(fetch_dir, write_dir, out, cmd_fetch, cmd_write):
     print("\n".join(lines))
 
 
+def summarize_trace(trace_dir, out, cmd, title):
+    """The kernel-trace statistics of a rocprofv3 --stats run as a short text
+    table (kernel, calls, average / min / max microseconds, share of GPU
+    time)."""
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {trace_dir}")
+    with open(files[0]) as fh:
+        rows = list(csv.DictReader(fh))
+    def short(name):
+        name = name.replace("iq4xs::(anonymous namespace)::", "").replace("iq4xs::", "")
+        return name.split("(")[0] if not name.startswith("void k_") else name.split("(")[0]
+    lines = [f"# rocprofv3 kernel-trace statistics: {title}", f"# command: {cmd}",
+             f"{'kernel':60s} {'calls':>6s} {'avg_us':>8s} {'min_us':>8s} {'max_us':>8s} {'pct':>6s}"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append(f"{short(r['Name'])[:60]:60s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:8.2f} "
+                     f"{float(r['MinNs']) / 1e3:8.2f} {float(r['MaxNs']) / 1e3:8.2f} {float(r['Percentage']):6.2f}")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def traffic_for(kernel, label):
     """Calibrated bytes per launch from the committed summary, or None when
     the summary is missing or the kernel source changed since."""
@@ -354,12 +377,20 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-run", action="store_true", help="fixed launches for rocprofv3")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR")
+    ap.add_argument("--cmd", default="")
+    ap.add_argument("--title", default="")
     ap.add_argument("--out", default=TRAFFIC_FILE)
     ap.add_argument("--cmd-fetch", default="")
     ap.add_argument("--cmd-write", default="")
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, args.out, args.cmd_fetch, args.cmd_write)
+        return
+    if args.summarize_trace:
+        if args.out == TRAFFIC_FILE:
+            raise SystemExit("--summarize-trace needs its own --out")
+        summarize_trace(args.summarize_trace, args.out, args.cmd, args.title)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the matmul is built and measured on a single MI355X "
@@ -380,10 +411,9 @@ def main():
     Ys = {M: torch.empty((M, N), dtype=torch.float32, device="cuda") for M in ms}
     wss = {M: torch.empty(iq.workspace_bytes(M, N, K), dtype=torch.uint8, device="cuda") for M in ms}
 
-    # One step = one iq4xs_gemm_ws call per M (quantization + matmul), the
-    # calls recorded once into a HIP graph per group of weight copies, as a
-    # decode loop would replay them.  The eager (host-launched) rate is
-    # reported beside it.
+    # One step = one iq4xs_gemm_ws call per M (quantization + matmul) on one
+    # stream.  The same calls recorded into a HIP graph per group of weight
+    # copies, as a decode loop might replay them, are timed beside it.
     def step_on(ws_list):
         for M, w in zip(ms, ws_list):
             iq.gemm(w, Xs[M], out=Ys[M], workspace=wss[M])
@@ -416,8 +446,8 @@ def main():
         torch.cuda.synchronize()
         return ev0.elapsed_time(ev1) / steps, time.perf_counter() - t0
 
-    step_ms, wall = timed(lambda i: graphs[i % len(graphs)].replay(), args.steps, args.warmup)
-    eager_ms, _ = timed(lambda i: step_on(groups[i % len(groups)]), args.steps, args.warmup)
+    step_ms, wall = timed(lambda i: step_on(groups[i % len(groups)]), args.steps, args.warmup)
+    graph_ms, _ = timed(lambda i: graphs[i % len(graphs)].replay(), args.steps, args.warmup)
     wbytes = 0.53125 * N * K * len(ms)
     value = wbytes / (step_ms * 1e-3) / 1e9
 
@@ -428,8 +458,8 @@ def main():
     dom = max(per_m, key=lambda r: r["kernel_ms"])
     dom_kernel = kernel_name(dom["M"], N, K, iq.PATHS[dom["path"]])
     achieved = algo_bytes_kernel(dom["M"], N, K) / (dom["kernel_ms"] * 1e-3) / 1e9
-    label = {1: "1,4,8,3,0", 2: "2,4,8,3,0", 4: "4,4,8,3,0", 8: "4,8,4,4,0",
-             16: "8,16,4,3,0"}.get(dom["M"], "") if dom_kernel == "k_mmv" else ""
+    label = {1: "1,4,8,3", 2: "2,4,8,3", 4: "4,4,8,3", 8: "4,8,4,4",
+             16: "8,16,4,3"}.get(dom["M"], "") if dom_kernel == "k_mmv" else ""
     traffic = traffic_for(dom_kernel, label)
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS,
@@ -446,8 +476,8 @@ def main():
            "config": {"workload": "IQ4_XS x Q8_1 GEMM decode sweep, attention/GDN input projection "
                                   "N=10240 K=5120, M in {1,2,4,8,16}, quantize included",
                       "N": N, "K": K, "M": list(ms), "weight_copies": len(rot.ws)},
-           "wall_s": wall, "eager_ms_per_step": eager_ms,
-           "eager_weight_GBs": wbytes / (eager_ms * 1e-3) / 1e9, "per_m": per_m, "roofline": roofline}
+           "wall_s": wall, "graph_ms_per_step": graph_ms,
+           "graph_weight_GBs": wbytes / (graph_ms * 1e-3) / 1e9, "per_m": per_m, "roofline": roofline}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, N, K, ms)
     if args.sweep:

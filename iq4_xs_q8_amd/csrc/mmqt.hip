@@ -289,16 +289,17 @@ k_mmqt(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__re
     __builtin_amdgcn_s_waitcnt(wait_vm_lds(0));
 }
 
-// The shared tiles: workgroup k takes the tile its run starts in when the run
-// starts inside that tile and reaches the tile's end (each shared tile is the
-// first tile of exactly one such run, the last of its owners), and adds the
-// partials of the owners k', k'+1, .., k in that order.
+// The shared tiles: workgroups (k, e) take the tile run k starts in when the
+// run starts inside that tile and reaches the tile's end (each shared tile is
+// the first tile of exactly one such run, the last of its owners); workgroup
+// (k, e) adds float4 e of every thread's slot over the owners k', k'+1, .., k
+// in that order.
 template <class C>
 __global__ void __launch_bounds__(NTQ, 1)
 k_mmqt_fix(const float *__restrict__ ws, float *__restrict__ Y, int M, int N, int nh, int mblocks, Runs runs)
 {
     constexpr int BM = C::BM, BN = C::BN;
-    const int k = blockIdx.x, tid = threadIdx.x;
+    const int k = blockIdx.x, e = blockIdx.y, tid = threadIdx.x;
     const int t = runs.t[k];
     const int t0 = t * nh;
     if (runs.u[k] == runs.u[k + 1] || runs.u[k] == t0 || runs.u[k + 1] < t0 + nh)
@@ -306,38 +307,29 @@ k_mmqt_fix(const float *__restrict__ ws, float *__restrict__ Y, int M, int N, in
     int g0 = k - 1;
     while (runs.u[g0] > t0)                                    // runs.u[0] == 0 <= t0
         g0--;
-    float4 sum[8];
-#pragma unroll
-    for (int e = 0; e < 8; e++)
-        sum[e] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    float4 sum = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     for (int gg = g0; gg <= k; gg++) {
         if (runs.u[gg] == runs.u[gg + 1])
             continue;
         const float4 *slot = reinterpret_cast<const float4 *>(ws) +
                              (size_t)(2 * gg + (runs.t[gg] == t ? 0 : 1)) * SLOT_F4;
-#pragma unroll
-        for (int e = 0; e < 8; e++) {
-            const float4 v = slot[e * NTQ + tid];
-            sum[e].x += v.x;
-            sum[e].y += v.y;
-            sum[e].z += v.z;
-            sum[e].w += v.w;
-        }
+        const float4 v = slot[e * NTQ + tid];
+        sum.x += v.x;
+        sum.y += v.y;
+        sum.z += v.z;
+        sum.w += v.w;
     }
     const int lane = tid & 63, wave = tid >> 6;
     const int nt = wave % C::NTW, mp = wave / C::NTW, col = lane & 31, h = lane >> 5;
     const int mb = t % mblocks, wb = t / mblocks;
     const int n = wb * BN + nt * TILE + col;
+    const float v4[4] = {sum.x, sum.y, sum.z, sum.w};
 #pragma unroll
-    for (int e = 0; e < 8; e++) {
-        const float v4[4] = {sum[e].x, sum[e].y, sum[e].z, sum[e].w};
-#pragma unroll
-        for (int c = 0; c < 4; c++) {
-            const int i = e / 4, r = 4 * (e % 4) + c;
-            const int m = mb * BM + (2 * mp + i) * TILE + 8 * (r / 4) + 4 * h + (r % 4);
-            if (m < M && n < N)
-                Y[(int64_t)m * N + n] = v4[c];
-        }
+    for (int c = 0; c < 4; c++) {
+        const int i = e / 4, r = 4 * (e % 4) + c;
+        const int m = mb * BM + (2 * mp + i) * TILE + 8 * (r / 4) + 4 * h + (r % 4);
+        if (m < M && n < N)
+            Y[(int64_t)m * N + n] = v4[c];
     }
 }
 
@@ -351,7 +343,7 @@ hipError_t launch_cfg(const void *W, const XPlanes &x, float *Y, float *ws, int6
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL((k_mmqt_fix<C>), dim3((unsigned)p.grid), dim3(NTQ), 0, s, (const float *)ws, Y,
+    hipLaunchKernelGGL((k_mmqt_fix<C>), dim3((unsigned)p.grid, 8), dim3(NTQ), 0, s, (const float *)ws, Y,
                        (int)x.M, (int)N, 2 * nb, p.mblocks, runs);
     return hipGetLastError();
 }
@@ -371,11 +363,16 @@ MmqtPlan mmqt_plan(int64_t M, int64_t N, int64_t K, int cus)
     if (M <= TILE || nb >= (1 << 15) || N * row_bytes >= (1LL << 31) ||
         Mp * K + Mp * K / 8 + BM * 288 >= (1LL << 31) || U >= (1LL << 31))
         return p;
-    // every run at least MIN_RUN units, so that writing and re-reading a
-    // partial tile (64 KB) stays small against the run's work
-    constexpr int64_t MIN_RUN = 8;
-    int64_t G = U / MIN_RUN;
-    G = std::min<int64_t>(G, std::min<int64_t>(cus, MAXG));
+    // Runs of at least 8 units (writing and re-reading a partial tile, 64 KB,
+    // stays small against a run's work) while that keeps at least half of
+    // the compute units busy, else of 4, else of 2 (measured on MI355X: 8 is
+    // best at M=64, 10240 x 5120 (44 vs 50 us with 4); 4 at M=64, 5120 x
+    // 5120 (37 vs 40 us); 2 at M=64, 5120 x 1024 (26 vs 28 us)).
+    const int64_t cap = std::min<int64_t>(cus, MAXG);
+    int64_t G = U / 8;
+    if (G < cap / 2)
+        G = U / 4 >= cap / 4 ? U / 4 : U / 2;
+    G = std::min<int64_t>(G, cap);
     p.grid = (int)std::max<int64_t>(G, 1);
     p.mblocks = (int)mblocks;
     p.bm = (int)BM;
