@@ -75,22 +75,23 @@ struct Cfg {
     static constexpr int WROW = wrow_bytes(CH);
     static constexpr int W_PR = CH * WBLK / 16;                               // pieces per row
     // one chunk buffer: weights [32][WROW] (padded to whole KB), activations
-    // [CH*8][MA][32], scales [CH*8][Mp] (padded to whole KB), 1 KB that load
-    // slots without a job fill, a 32-byte zero row (the operand of rows >= M)
-    // and slack for the scales a lane reads past the last sub-block's rows
-    // (activations: MA rows per sub-block in LDS, MA >= M)
+    // [CH*8][MA][32], scales [CH*8][Mp] (padded to whole KB), a 32-byte zero
+    // row (the operand of rows >= M) and slack for the scales a lane reads
+    // past the last sub-block's rows (activations: MA rows per sub-block in
+    // LDS, MA >= M); besides the buffers, one 1 KB area that load slots
+    // without a job fill (shared: nothing reads it)
     static constexpr int MA = LIVE < 4 ? LIVE : MPC;
     static constexpr int W_BYTES = round_up_c(TILE * WROW, 1024);
     static constexpr int A_OFF = W_BYTES, A_BYTES = CH * SUBS * MA * SB;
     static constexpr int D_OFF = A_OFF + A_BYTES, D_BYTES = round_up_c(CH * SUBS * MPC * 4, 1024);
-    static constexpr int DUMP = D_OFF + D_BYTES;
-    static constexpr int Z_OFF = DUMP + 1024;
+    static constexpr int Z_OFF = D_OFF + D_BYTES;
     static constexpr int BUF = Z_OFF + 32 + 128;
     static constexpr int RED = LIVE * 64 * (NW + 1) * 4;                      // partial tiles
-    static constexpr int TOTAL = NBUF * BUF + RED;
+    static constexpr int TOTAL = NBUF * BUF + RED + 1024;
     template <int B>
     static __device__ __forceinline__ char *buf() { return lds_area<B, BUF>(); }
     static __device__ __forceinline__ float *red() { return reinterpret_cast<float *>(lds_area<-1, RED>()); }
+    static __device__ __forceinline__ char *dump() { return lds_area<-2, 1024>(); }
     // A chunk is copied by load jobs of 1 KB of a buffer each: JW of weights,
     // JQ of activations, JD of scales.  Every wavefront issues SLOTS loads
     // per chunk: wavefronts 0..WA-1 take the weight jobs, the others the
@@ -164,7 +165,7 @@ k_mmv(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__res
             const uint32_t r = div_small<C::WROW / 16, LIM>(pi);
             const uint32_t c = pi - (uint32_t)__umul24(r, C::WROW / 16);
             const bool ok = job < C::JW && r < TILE && c < C::W_PR;
-            p_dst[k] = job < C::JW ? 1024 * job : C::DUMP;
+            p_dst[k] = job < C::JW ? 1024 * job : -1;          // (-1: the dump area)
             p_scale[k] = false;
             p_go[k] = ok ? r * row_bytes + 16 * c : OOB;
             p_key[k] = ok ? (int)(16 * c + 15) : -(1 << 30);   // piece bytes [16c, 16c+16)
@@ -178,7 +179,7 @@ k_mmv(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__res
             const uint32_t m = (pi - 2 * C::MA * sb2) >> 1, hf = pi & 1;
             const int qo = (int)(((uint32_t)__umul24(sb2, (uint32_t)Mp) + m) * SB + 16 * hf);
             const int at = (int)(16 * pi);
-            p_dst[k] = isq ? C::A_OFF + 1024 * job : isd ? C::D_OFF + 1024 * (job - C::JQ) : C::DUMP;
+            p_dst[k] = isq ? C::A_OFF + 1024 * job : isd ? C::D_OFF + 1024 * (job - C::JQ) : -1;
             p_scale[k] = isd;
             p_go[k] = isq ? (uint32_t)qo : isd ? (uint32_t)at : OOB;
             p_key[k] = isq ? qo : isd ? at : 1 << 30;
@@ -197,7 +198,7 @@ k_mmv(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__res
 #pragma unroll
             for (int k = 0; k < SLOTS; k++) {
                 const bool need = (uint32_t)(p_key[k] - lo) < (uint32_t)(hi - lo + 15);
-                load_lds16(wr, buf + p_dst[k], need ? p_go[k] + base : OOB);
+                load_lds16(wr, p_dst[k] < 0 ? C::dump() : buf + p_dst[k], need ? p_go[k] + base : OOB);
             }
         } else {
             const int qn = c.cl * SUBS * Mp * SB, dn = c.cl * SUBS * Mp * 4;
@@ -205,7 +206,8 @@ k_mmv(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__res
 #pragma unroll
             for (int k = 0; k < SLOTS; k++) {
                 const bool need = p_key[k] < (p_scale[k] ? dn : qn);
-                load_lds16(xr, buf + p_dst[k], need ? p_go[k] + (p_scale[k] ? dbase : qbase) : OOB);
+                load_lds16(xr, p_dst[k] < 0 ? C::dump() : buf + p_dst[k],
+                           need ? p_go[k] + (p_scale[k] ? dbase : qbase) : OOB);
             }
         }
     };
