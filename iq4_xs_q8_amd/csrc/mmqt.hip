@@ -217,36 +217,63 @@ k_mmqt(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__re
         const char *wrow = B + (nt * TILE + col) * WROWQ;
         const uint2 hdr = *reinterpret_cast<const uint2 *>(wrow);
         const int hf = c.j0 & 1;
-#pragma unroll 2
-        for (int s = 0; s < HALF; s++) {
-            const uint2 q = *reinterpret_cast<const uint2 *>(wrow + 16 + 16 * s + 8 * h);
-            v4i ax[2];
-            float4 dx[2][4];
+        // Two sub-blocks at a time: all their LDS reads first, then all four
+        // products (each into registers of its own), then the epilogues, so
+        // that reads, lookups, matrix-core work and rescaling of the two
+        // overlap.
 #pragma unroll
-            for (int i = 0; i < 2; i++) {
-                const int mt = 2 * mp + i;
-                ax[i] = *reinterpret_cast<const v4i *>(B + A_OFF + (s * BM + mt * TILE + col) * SB + 16 * h);
+        for (int s0 = 0; s0 < HALF; s0 += 2) {
+            uint2 q[2];
+            v4i ax[2][2];
+            float4 dx[2][2][4];
 #pragma unroll
-                for (int qd = 0; qd < 4; qd++)
-                    dx[i][qd] = *reinterpret_cast<const float4 *>(B + D_OFF + (s * BM + mt * TILE + 4 * h + 8 * qd) * 4);
-            }
-            uint32_t wa[4], wb4[4];
-            expand8_split(q.x, q.y, wa, wb4);
-            const v4i ba = {(int)wa[0], (int)wa[1], (int)wa[2], (int)wa[3]};
-            const v4i bb = {(int)wb4[0], (int)wb4[1], (int)wb4[2], (int)wb4[3]};
-            const float sw = sub_scale(hdr.x, hdr.y, HALF * hf + s);
+            for (int u = 0; u < 2; u++) {
+                const int s = s0 + u;
+                q[u] = *reinterpret_cast<const uint2 *>(wrow + 16 + 16 * s + 8 * h);
 #pragma unroll
-            for (int i = 0; i < 2; i++) {
-                const v16i zero = {0};
-                const v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(
-                    ax[i], bb, __builtin_amdgcn_mfma_i32_32x32x32_i8(ax[i], ba, zero, 0, 0, 0), 0, 0, 0);
+                for (int i = 0; i < 2; i++) {
+                    const int mt = 2 * mp + i;
+                    ax[u][i] = *reinterpret_cast<const v4i *>(B + A_OFF + (s * BM + mt * TILE + col) * SB + 16 * h);
 #pragma unroll
-                for (int r = 0; r < 16; r++) {
-                    const float d = (r % 4 == 0) ? dx[i][r / 4].x : (r % 4 == 1) ? dx[i][r / 4].y
-                                  : (r % 4 == 2) ? dx[i][r / 4].z : dx[i][r / 4].w;
-                    acc[i][r] += (sw * d) * (float)D[r];
+                    for (int qd = 0; qd < 4; qd++)
+                        dx[u][i][qd] =
+                            *reinterpret_cast<const float4 *>(B + D_OFF + (s * BM + mt * TILE + 4 * h + 8 * qd) * 4);
                 }
             }
+            __builtin_amdgcn_sched_barrier(0);
+            v16i D[2][2];
+            float sw[2];
+#pragma unroll
+            for (int u = 0; u < 2; u++) {
+                uint32_t wa[4], wb4[4];
+                expand8_split(q[u].x, q[u].y, wa, wb4);
+                const v4i ba = {(int)wa[0], (int)wa[1], (int)wa[2], (int)wa[3]};
+                const v4i bb = {(int)wb4[0], (int)wb4[1], (int)wb4[2], (int)wb4[3]};
+                sw[u] = sub_scale(hdr.x, hdr.y, HALF * hf + s0 + u);
+#pragma unroll
+                for (int i = 0; i < 2; i++) {
+                    const v16i zero = {0};
+                    D[u][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                        ax[u][i], bb, __builtin_amdgcn_mfma_i32_32x32x32_i8(ax[u][i], ba, zero, 0, 0, 0), 0, 0, 0);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < 2; u++)
+#pragma unroll
+                for (int i = 0; i < 2; i++) {
+#pragma unroll
+                    for (int r = 0; r < 16; r++) {
+                        const float d = (r % 4 == 0) ? dx[u][i][r / 4].x : (r % 4 == 1) ? dx[u][i][r / 4].y
+                                      : (r % 4 == 2) ? dx[u][i][r / 4].z : dx[u][i][r / 4].w;
+                        acc[i][r] += (sw[u] * d) * (float)D[u][i][r];
+                    }
+                }
+#pragma unroll
+            for (int u = 0; u < 2; u++)
+#pragma unroll
+                for (int i = 0; i < 2; i++)
+                    keep_live(D[u][i]);
         }
         if (c.flags & 1)
             flush(c.t, (c.flags & 2) != 0);
