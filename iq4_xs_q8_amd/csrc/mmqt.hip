@@ -242,14 +242,21 @@ k_mmqt(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__re
             }
             __builtin_amdgcn_sched_barrier(0);
             v16i D[2][2];
+            // (the two halves of the wavefront, same rows, each decode one of
+            // the two sub-blocks' scales and swap them)
             float sw[2];
+            {
+                const uint32_t own = __builtin_bit_cast(uint32_t, sub_scale(hdr.x, hdr.y, HALF * hf + s0 + h));
+                const auto both = __builtin_amdgcn_permlane32_swap(own, own, false, false);
+                sw[0] = __builtin_bit_cast(float, (uint32_t)both[0]);
+                sw[1] = __builtin_bit_cast(float, (uint32_t)both[1]);
+            }
 #pragma unroll
             for (int u = 0; u < 2; u++) {
                 uint32_t wa[4], wb4[4];
                 expand8_split(q[u].x, q[u].y, wa, wb4);
                 const v4i ba = {(int)wa[0], (int)wa[1], (int)wa[2], (int)wa[3]};
                 const v4i bb = {(int)wb4[0], (int)wb4[1], (int)wb4[2], (int)wb4[3]};
-                sw[u] = sub_scale(hdr.x, hdr.y, HALF * hf + s0 + u);
 #pragma unroll
                 for (int i = 0; i < 2; i++) {
                     const v16i zero = {0};
