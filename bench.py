@@ -242,6 +242,27 @@ def profile_run():
     print(f"[profile-run] copy {COPY_BYTES} bytes x4", flush=True)
 
 
+def profile_shapes(specs):
+    """Fixed launches for rocprofv3 at given shapes ("MxNxK", comma
+    separated): per shape, 20 launches of the matmul kernel(s) alone
+    (gemm_act, rotated weights), inputs of the workload the shape belongs to
+    (else the prefill recipe)."""
+    for spec in specs.split(","):
+        M, N, K = (int(v) for v in spec.split("x"))
+        wl = next((w for w in synth.WORKLOADS if (N, K) in w.shapes), synth.WORKLOADS[-1])
+        rot = Rotation(wl.w(N, K))
+        X = torch.from_numpy(wl.x(M, K, N=N)).cuda()
+        act = iq.prepare_act(X)
+        Y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        path = iq.dispatch(M, N, K)
+        for _ in range(20):
+            iq.gemm_act(rot.next(), act, M, K, path=path, out=Y)
+        torch.cuda.synchronize()
+        print(f"[profile-shapes] M={M} N={N} K={K} {kernel_name(M, N, K, path)} x20", flush=True)
+        del rot
+        torch.cuda.empty_cache()
+
+
 def _counter_rows(d):
     rows = []
     for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
@@ -263,6 +284,7 @@ def summarize_pmc(fetch_dir, write_dir, out, cmd_fetch, cmd_write):
             name = r["Kernel_Name"]
             key = ("copy" if "copyBuffer" in name else
                    "k_mmv" if "k_mmv" in name else "k_gemv" if "k_gemv" in name else
+                   "k_mmqt_fix" if "k_mmqt_fix" in name else "k_mmqt" if "k_mmqt" in name else
                    "k_mmq" if "k_mmq" in name else None)
             if key is None:
                 continue
@@ -326,6 +348,45 @@ def summarize_trace(trace_dir, out, cmd, title):
     print("\n".join(lines))
 
 
+def summarize_pmc_shapes(fetch_dir, write_dir, out, cmd_fetch, cmd_write, specs):
+    """Per shape of a --profile-shapes run (20 launches each, in order): mean
+    FETCH_SIZE / WRITE_SIZE per launch of the tile kernel and of its
+    shared-tile kernel, calibrated with the copy runs of a --profile-run
+    summary (TRAFFIC_FILE), against the algorithmic bytes."""
+    with open(TRAFFIC_FILE) as fh:
+        sc = {ln.split()[2]: float(ln.split()[3]) for ln in fh if ln.startswith("copy_") and "scale" in ln}
+    f_scale, w_scale = sc["fetch_scale"], sc["write_scale"]
+    def per_dispatch(d, counter):
+        acc = {}
+        for r in _counter_rows(d):
+            if r["Counter_Name"] == counter and "k_mmqt" in r["Kernel_Name"]:
+                k = (int(r["Dispatch_Id"]), "fix" if "k_mmqt_fix" in r["Kernel_Name"] else "main")
+                acc[k] = acc.get(k, 0.0) + float(r["Counter_Value"])
+        return acc
+    fd, wd = per_dispatch(fetch_dir, "FETCH_SIZE"), per_dispatch(write_dir, "WRITE_SIZE")
+    shapes = [tuple(int(v) for v in sp.split("x")) for sp in specs.split(",")]
+    lines = ["# HBM traffic per launch of the tile kernel from rocprofv3 counters (20 launches per shape)",
+             f"# fetch run: {cmd_fetch}", f"# write run: {cmd_write}",
+             f"# scales from the copy calibration of {os.path.basename(TRAFFIC_FILE)}: fetch x{f_scale:.4f}, write x{w_scale:.4f}",
+             f"source_hash k_mmqt {source_hash('k_mmqt')}",
+             "# M N K  kernel  fetch_MB  write_MB  calibrated_MB  algorithmic_MB (W + planes + Y)"]
+    for part in ("main", "fix"):
+        fk = [v for (i, p), v in sorted(fd.items()) if p == part]
+        wk = [v for (i, p), v in sorted(wd.items()) if p == part]
+        for n, (M, N, K) in enumerate(shapes):
+            f = fk[20 * n:20 * (n + 1)]
+            w = wk[20 * n:20 * (n + 1)]
+            if not f or not w:
+                continue
+            fb = sum(f) / len(f) * 1024.0 * f_scale
+            wb = sum(w) / len(w) * 1024.0 * w_scale
+            lines.append(f"{M} {N} {K}  {'k_mmqt' if part == 'main' else 'k_mmqt_fix'}  {fb / 1e6:.1f}  {wb / 1e6:.1f}  "
+                         f"{(fb + wb) / 1e6:.1f}  {algo_bytes_kernel(M, N, K) / 1e6 if part == 'main' else 0:.1f}")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def traffic_for(kernel, label):
     """Calibrated bytes per launch from the committed summary, or None when
     the summary is missing or the kernel source changed since."""
@@ -376,8 +437,10 @@ def main():
     ap.add_argument("--sweep", default=None, help="also time every workload point -> JSONL")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-run", action="store_true", help="fixed launches for rocprofv3")
+    ap.add_argument("--profile-shapes", default=None, help="MxNxK,...: fixed launches for rocprofv3")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR")
+    ap.add_argument("--summarize-pmc-shapes", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "SHAPES"))
     ap.add_argument("--cmd", default="")
     ap.add_argument("--title", default="")
     ap.add_argument("--out", default=TRAFFIC_FILE)
@@ -386,6 +449,12 @@ def main():
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, args.out, args.cmd_fetch, args.cmd_write)
+        return
+    if args.summarize_pmc_shapes:
+        if args.out == TRAFFIC_FILE:
+            raise SystemExit("--summarize-pmc-shapes needs its own --out")
+        summarize_pmc_shapes(*args.summarize_pmc_shapes[:2], args.out, args.cmd_fetch, args.cmd_write,
+                             args.summarize_pmc_shapes[2])
         return
     if args.summarize_trace:
         if args.out == TRAFFIC_FILE:
@@ -402,6 +471,9 @@ def main():
     torch.cuda.set_device(0)
     if args.profile_run:
         profile_run()
+        return
+    if args.profile_shapes:
+        profile_shapes(args.profile_shapes)
         return
 
     wl = synth.DECODE_ATTN

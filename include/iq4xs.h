@@ -125,16 +125,16 @@ int iq4xs_gemm_q8_1(const void *W, const void *Xq, float *Y, int64_t M, int64_t 
 int iq4xs_act_bytes(int64_t M, int64_t K, size_t *out);
 int iq4xs_prepare_act(const float *X, void *act, int64_t M, int64_t K, void *stream);
 /* Y = X * W^T from prepared activations; path AUTO, GEMV or MMQ (DEQ_BF16 is
- * EPATH here).  Launches the matmul kernel only -- plus, for the MMQ tile
- * kernel (M > 32) and the K-split fallback, a second kernel that adds the
- * partial results of output tiles shared by several workgroups, in a fixed
- * order, from a stream-ordered workspace; and, where the streaming MMQ kernel
- * (M <= 32) shares output tiles between two workgroups (which add into Y), a
- * kernel that zeroes Y first.  OR IQ4XS_Y_ZEROED into `path` when Y already
- * holds zeros (e.g. cleared together with other buffers): that zeroing kernel
- * is then skipped and the result is the same; with any other Y contents the
- * result of such shared tiles is undefined.  The other kernels overwrite Y
- * and ignore the flag. */
+ * EPATH here).  Launches the matmul kernel only -- plus, where output tiles
+ * are shared by more than two workgroups (MMQ tile kernel with few tiles,
+ * K-split fallback), a second kernel that adds their partial results in a
+ * fixed order from a stream-ordered workspace; and, where the MMQ kernels
+ * share output tiles between two workgroups (which add into Y), a kernel
+ * that zeroes Y first.  OR IQ4XS_Y_ZEROED into `path` when Y already holds
+ * zeros (e.g. cleared together with other buffers): that zeroing kernel is
+ * then skipped and the result is the same; with any other Y contents the
+ * result of such shared tiles is undefined.  Shapes without such tiles
+ * overwrite Y and ignore the flag. */
 #define IQ4XS_Y_ZEROED 0x100
 int iq4xs_gemm_act(const void *W, const void *act, float *Y, int64_t M, int64_t N, int64_t K,
                    int path, void *stream);

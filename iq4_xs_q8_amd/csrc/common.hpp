@@ -193,9 +193,9 @@ hipError_t launch_mmv(const void *W, const XPlanes &x, float *Y, int64_t N, cons
 // super-block) units over `grid` workgroups; tiles shared by several
 // workgroups are summed from a workspace of partial tiles by a second kernel.
 struct MmqtPlan {
-    bool ok = false;
+    bool ok = false, zero_y = false;    // zero_y: shared tiles add into a zeroed Y
     int grid = 0, mblocks = 0, bm = 0;
-    size_t workspace_bytes = 0;
+    size_t workspace_bytes = 0;         // else partial tiles in a workspace
 };
 MmqtPlan mmqt_plan(int64_t M, int64_t N, int64_t K, int cus);
 hipError_t launch_mmqt(const void *W, const XPlanes &x, float *Y, int64_t N, const MmqtPlan &p, void *workspace,

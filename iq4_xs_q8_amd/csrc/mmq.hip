@@ -245,6 +245,7 @@ MmqPlan mmq_plan(int64_t M, int64_t N, int64_t K)
         p.tp = mmqt_plan(M, N, K, device_cus());
         if (p.tp.ok) {
             p.tile = true;
+            p.zero_y = p.tp.zero_y;
             p.workspace_bytes = p.tp.workspace_bytes;
             return p;
         }
@@ -287,6 +288,11 @@ hipError_t launch_mmq(const void *Wv, const XPlanes &x, float *Y, int64_t N, voi
     if (p.tile) {
         if (p.tp.workspace_bytes && workspace == nullptr)
             return hipErrorInvalidValue;
+        if (p.tp.zero_y && !y_zeroed) {
+            const hipError_t e = launch_zero(Y, x.M * N, s);
+            if (e != hipSuccess)
+                return e;
+        }
         return launch_mmqt(Wv, x, Y, N, p.tp, workspace, s);
     }
     if (p.ks > 1 && workspace == nullptr)

@@ -13,10 +13,13 @@
 //    (tile, half super-block), tile-major; each workgroup gets one contiguous
 //    run of equal length (stream-K style: every compute unit gets the same
 //    work, also when there are fewer tiles than compute units).  A tile
-//    covered by one run is stored by its workgroup; the other workgroups
-//    store their partial tiles (at most two per run: its first and its last)
-//    in a workspace, and a second kernel adds the partials of every shared
-//    tile in run order, so the result does not depend on timing.
+//    covered by one run is stored by its workgroup.  When every run covers
+//    at least a tile's units, a tile has two owners at most and they add
+//    into a Y zeroed beforehand (0 + a + b == 0 + b + a); otherwise the
+//    owners store their partial tiles (at most two per run: its first and
+//    its last) in a workspace, and a second kernel adds the partials of every
+//    shared tile in run order.  Either way the result does not depend on
+//    timing.
 //  * Half a super-block of a tile at a time (4 sub-blocks) goes straight
 //    from memory into one of five LDS buffers with 16-byte LDS-writing buffer
 //    loads: for each of the BN weight rows its header and the half's 64 index
@@ -105,7 +108,7 @@ __device__ __forceinline__ float4 *slot_at(float *ws, int g, int which)
 template <class C>
 __global__ void __launch_bounds__(NTQ, 1)
 k_mmqt(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__restrict__ Y,
-       float *__restrict__ ws, int M, int N, int K, int Mp, int nb, int mblocks, int G, Runs runs)
+       float *__restrict__ ws, int M, int N, int K, int Mp, int nb, int mblocks, int G, int add_into_y, Runs runs)
 {
     constexpr int BM = C::BM, BN = C::BN, SLOTS = C::SLOTS, JW = C::JW, JA = C::JA, JD = C::JD;
     constexpr int A_OFF = C::A_OFF, D_OFF = C::D_OFF, BUFQ = C::BUFQ;
@@ -196,6 +199,17 @@ k_mmqt(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__re
                     const int m = mb * BM + (2 * mp + i) * TILE + 8 * (r / 4) + 4 * h + (r % 4);
                     if (m < M && n < N)
                         Y[(int64_t)m * N + n] = acc[i][r];
+                }
+        } else if (add_into_y) {                              // (uniform) two owners at most
+            const int mb = t % mblocks, wb = t / mblocks;
+            const int n = wb * BN + nt * TILE + col;
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const int m = mb * BM + (2 * mp + i) * TILE + 8 * (r / 4) + 4 * h + (r % 4);
+                    if (m < M && n < N)
+                        atomicAdd(Y + (int64_t)m * N + n, acc[i][r]);
                 }
         } else {
             float4 *slot = slot_at(ws, g, t == t_first ? 0 : 1);
@@ -373,9 +387,9 @@ hipError_t launch_cfg(const void *W, const XPlanes &x, float *Y, float *ws, int6
 {
     const int nb = (int)(x.K / QK);
     hipLaunchKernelGGL((k_mmqt<C>), dim3((unsigned)p.grid), dim3(NTQ), 0, s, (const uint8_t *)W, x.qp, Y, ws,
-                       (int)x.M, (int)N, (int)x.K, (int)x.Mp, nb, p.mblocks, p.grid, runs);
+                       (int)x.M, (int)N, (int)x.K, (int)x.Mp, nb, p.mblocks, p.grid, p.zero_y ? 1 : 0, runs);
     const hipError_t e = hipGetLastError();
-    if (e != hipSuccess)
+    if (e != hipSuccess || p.workspace_bytes == 0)
         return e;
     hipLaunchKernelGGL((k_mmqt_fix<C>), dim3((unsigned)p.grid, 8), dim3(NTQ), 0, s, (const float *)ws, Y,
                        (int)x.M, (int)N, 2 * nb, p.mblocks, runs);
@@ -410,7 +424,22 @@ MmqtPlan mmqt_plan(int64_t M, int64_t N, int64_t K, int cus)
     p.grid = (int)std::max<int64_t>(G, 1);
     p.mblocks = (int)mblocks;
     p.bm = (int)BM;
-    p.workspace_bytes = (size_t)p.grid * 2 * SLOT_F4 * sizeof(float4);
+    // With at least one tile's units per run a tile has two owners at most:
+    // they add into a zeroed Y (0 + a + b == 0 + b + a), which costs less
+    // than writing and summing partial tiles (M=512, 10240 x 5120: the
+    // summing kernel took 10 of 150 us).  With shorter runs the partial
+    // tiles go to the workspace.
+    p.zero_y = false;
+    if (G <= T) {
+        for (int64_t g = 1; g < p.grid; g++)
+            if (U * g / p.grid % (2 * nb) != 0) {
+                p.zero_y = true;
+                break;
+            }
+        p.workspace_bytes = 0;
+    } else {
+        p.workspace_bytes = (size_t)p.grid * 2 * SLOT_F4 * sizeof(float4);
+    }
     p.ok = true;
     return p;
 }
@@ -418,7 +447,7 @@ MmqtPlan mmqt_plan(int64_t M, int64_t N, int64_t K, int cus)
 hipError_t launch_mmqt(const void *W, const XPlanes &x, float *Y, int64_t N, const MmqtPlan &p, void *workspace,
                        hipStream_t s)
 {
-    if (!p.ok || p.grid < 1 || p.grid > MAXG || workspace == nullptr)
+    if (!p.ok || p.grid < 1 || p.grid > MAXG || (p.workspace_bytes && workspace == nullptr))
         return hipErrorInvalidValue;
     if ((const char *)x.dp != (const char *)x.qp + x.Mp * x.K)
         return hipErrorInvalidValue;
