@@ -370,18 +370,26 @@ def summarize_pmc_shapes(fetch_dir, write_dir, out, cmd_fetch, cmd_write, specs)
              f"# scales from the copy calibration of {os.path.basename(TRAFFIC_FILE)}: fetch x{f_scale:.4f}, write x{w_scale:.4f}",
              f"source_hash k_mmqt {source_hash('k_mmqt')}",
              "# M N K  kernel  fetch_MB  write_MB  calibrated_MB  algorithmic_MB (W + planes + Y)"]
-    for part in ("main", "fix"):
-        fk = [v for (i, p), v in sorted(fd.items()) if p == part]
-        wk = [v for (i, p), v in sorted(wd.items()) if p == part]
-        for n, (M, N, K) in enumerate(shapes):
-            f = fk[20 * n:20 * (n + 1)]
-            w = wk[20 * n:20 * (n + 1)]
-            if not f or not w:
-                continue
-            fb = sum(f) / len(f) * 1024.0 * f_scale
-            wb = sum(w) / len(w) * 1024.0 * w_scale
-            lines.append(f"{M} {N} {K}  {'k_mmqt' if part == 'main' else 'k_mmqt_fix'}  {fb / 1e6:.1f}  {wb / 1e6:.1f}  "
-                         f"{(fb + wb) / 1e6:.1f}  {algo_bytes_kernel(M, N, K) / 1e6 if part == 'main' else 0:.1f}")
+    # dispatches in launch order: 20 tile-kernel launches per shape, each
+    # followed by its summing kernel where the shape has one
+    sums = {}
+    n_main = -1
+    for (i, part) in sorted(set(fd) | set(wd)):
+        if part == "main":
+            n_main += 1
+        shape = n_main // 20
+        acc = sums.setdefault((shape, part), [0.0, 0.0, 0])
+        acc[0] += fd.get((i, part), 0.0)
+        acc[1] += wd.get((i, part), 0.0)
+        acc[2] += 1
+    for (shape, part), (f, w, cnt) in sorted(sums.items(), key=lambda kv: (kv[0][1] != "main", kv[0][0])):
+        if shape >= len(shapes):
+            continue
+        M, N, K = shapes[shape]
+        fb = f / cnt * 1024.0 * f_scale
+        wb = w / cnt * 1024.0 * w_scale
+        lines.append(f"{M} {N} {K}  {'k_mmqt' if part == 'main' else 'k_mmqt_fix'}  {fb / 1e6:.1f}  {wb / 1e6:.1f}  "
+                     f"{(fb + wb) / 1e6:.1f}  {algo_bytes_kernel(M, N, K) / 1e6 if part == 'main' else 0:.1f}")
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
