@@ -187,12 +187,12 @@ def test_deterministic_and_invariant(path):
                                    (40, 1000, 2048), (64, 600, 4096), (50, 5000, 512), (33, 300, 2816)])
 def test_tile_kernel_shapes(M, N, K):
     """Shapes the tile kernel takes (128 x 128 tiles for M > 64, 64 x 256 for
-    32 < M <= 64): ragged M and N, K of
-    one super-block (runs cross tiles), few tiles and long K (runs shorter
-    than a tile: two to eight workgroups share a tile, their partial tiles
-    summed in run order by the second kernel; run bounds on and off tile and
-    super-block boundaries); through gemm and gemm_act (with and without the
-    Y-zeroed hint, which this path does not need), bit-identical."""
+    32 < M <= 64): ragged M and N; K of one super-block (runs of more than a
+    tile: two owners per shared tile, adding into a zeroed Y); few tiles and
+    long K (runs shorter than a tile: two to eight workgroups share a tile,
+    their partial tiles summed in run order by the second kernel); run bounds
+    on and off tile and super-block boundaries; through gemm and gemm_act
+    (with and without the Y-zeroed hint), bit-identical."""
     W, X = _inputs(M, N, K, seed=M + N)
     ref = O.gemm_q8_1(W, O.quantize_q8_1(X), K)
     Wd, Xd = dev(W), dev(X)
