@@ -96,6 +96,12 @@ struct UnitCursor {
     }
 };
 
+// The runs whose first tile is shared and ends inside them (the last owner
+// of each tile with more than one), found on the host.
+struct FixRuns {
+    int k[MAXG];
+};
+
 // Partial tile slot (run g, 0 = its first tile, 1 = its last): 8 float4 per
 // thread, float4 e of thread tid at [e][tid] (coalesced stores and loads);
 // e = 4*i + r/4 for accumulator i, result register r.
@@ -337,35 +343,43 @@ k_mmqt(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__re
     __builtin_amdgcn_s_waitcnt(wait_vm_lds(0));
 }
 
-// The shared tiles: workgroups (k, e) take the tile run k starts in when the
-// run starts inside that tile and reaches the tile's end (each shared tile is
-// the first tile of exactly one such run, the last of its owners); workgroup
-// (k, e) adds float4 e of every thread's slot over the owners k', k'+1, .., k
-// in that order.
+// The shared tiles: workgroup (i, e) takes run k = fix.k[i], which starts
+// inside its first tile and reaches that tile's end (each shared tile is the
+// first tile of exactly one such run, the last of its owners), and adds
+// float4 e of every thread's slot over the owners k', k'+1, .., k in that
+// order.
 template <class C>
 __global__ void __launch_bounds__(NTQ, 1)
-k_mmqt_fix(const float *__restrict__ ws, float *__restrict__ Y, int M, int N, int nh, int mblocks, Runs runs)
+k_mmqt_fix(const float *__restrict__ ws, float *__restrict__ Y, int M, int N, int nh, int mblocks, Runs runs,
+           FixRuns fix)
 {
     constexpr int BM = C::BM, BN = C::BN;
-    const int k = blockIdx.x, e = blockIdx.y, tid = threadIdx.x;
+    const int k = fix.k[blockIdx.x], e = blockIdx.y, tid = threadIdx.x;
     const int t = runs.t[k];
     const int t0 = t * nh;
-    if (runs.u[k] == runs.u[k + 1] || runs.u[k] == t0 || runs.u[k + 1] < t0 + nh)
-        return;                                               // (uniform) not such a run
     int g0 = k - 1;
     while (runs.u[g0] > t0)                                    // runs.u[0] == 0 <= t0
         g0--;
+    // owners in groups of eight: all loads of a group in flight together,
+    // then the adds in owner order (an owner with an empty run adds zero)
     float4 sum = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    for (int gg = g0; gg <= k; gg++) {
-        if (runs.u[gg] == runs.u[gg + 1])
-            continue;
-        const float4 *slot = reinterpret_cast<const float4 *>(ws) +
-                             (size_t)(2 * gg + (runs.t[gg] == t ? 0 : 1)) * SLOT_F4;
-        const float4 v = slot[e * NTQ + tid];
-        sum.x += v.x;
-        sum.y += v.y;
-        sum.z += v.z;
-        sum.w += v.w;
+    for (int gg0 = g0; gg0 <= k; gg0 += 8) {
+        float4 v[8];
+#pragma unroll
+        for (int q = 0; q < 8; q++) {
+            const int gg = gg0 + q;
+            v[q] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if (gg <= k && runs.u[gg] != runs.u[gg + 1])          // (uniform)
+                v[q] = (reinterpret_cast<const float4 *>(ws) +
+                        (size_t)(2 * gg + (runs.t[gg] == t ? 0 : 1)) * SLOT_F4)[e * NTQ + tid];
+        }
+#pragma unroll
+        for (int q = 0; q < 8; q++) {
+            sum.x += v[q].x;
+            sum.y += v[q].y;
+            sum.z += v[q].z;
+            sum.w += v[q].w;
+        }
     }
     const int lane = tid & 63, wave = tid >> 6;
     const int nt = wave % C::NTW, mp = wave / C::NTW, col = lane & 31, h = lane >> 5;
@@ -391,8 +405,20 @@ hipError_t launch_cfg(const void *W, const XPlanes &x, float *Y, float *ws, int6
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.workspace_bytes == 0)
         return e;
-    hipLaunchKernelGGL((k_mmqt_fix<C>), dim3((unsigned)p.grid, 8), dim3(NTQ), 0, s, (const float *)ws, Y,
-                       (int)x.M, (int)N, 2 * nb, p.mblocks, runs);
+    // one group of 8 workgroups per shared tile: the runs that start inside
+    // their first tile and reach its end
+    FixRuns fix;
+    int nfix = 0;
+    const int nh = 2 * nb;
+    for (int k = 0; k < p.grid; k++) {
+        const int t0 = runs.t[k] * nh;
+        if (runs.u[k] != runs.u[k + 1] && runs.u[k] != t0 && runs.u[k + 1] >= t0 + nh)
+            fix.k[nfix++] = k;
+    }
+    if (nfix == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL((k_mmqt_fix<C>), dim3((unsigned)nfix, 8), dim3(NTQ), 0, s, (const float *)ws, Y,
+                       (int)x.M, (int)N, nh, p.mblocks, runs, fix);
     return hipGetLastError();
 }
 
