@@ -184,7 +184,8 @@ def test_deterministic_and_invariant(path):
 
 @pytest.mark.parametrize("M,N,K", [(300, 2800, 512), (97, 8200, 256), (130, 8320, 1024),
                                    (100, 200, 4096), (130, 1000, 2048), (257, 384, 8192), (200, 300, 2816),
-                                   (40, 1000, 2048), (64, 600, 4096), (50, 5000, 512), (33, 300, 2816)])
+                                   (40, 1000, 2048), (64, 600, 4096), (50, 5000, 512), (33, 300, 2816),
+                                   (65, 16768, 256), (130, 11392, 768)])
 def test_tile_kernel_shapes(M, N, K):
     """Shapes the tile kernel takes (128 x 128 tiles for M > 64, 64 x 256 for
     32 < M <= 64): ragged M and N; K of one super-block (runs of more than a
