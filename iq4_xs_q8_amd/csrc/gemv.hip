@@ -144,10 +144,12 @@ hipError_t launch_gemv(const void *W, const XPlanes &x, float *Y, int64_t N, hip
 {
     const uint8_t *w = (const uint8_t *)W;
     switch (x.M) {
-    case 1: launch_m<1, 4, 6>(w, x, Y, N, s); break;
-    case 2: launch_m<2, 4, 6>(w, x, Y, N, s); break;
-    case 3: launch_m<3, 4, 4>(w, x, Y, N, s); break;
-    case 4: launch_m<4, 4, 4>(w, x, Y, N, s); break;
+    // two rows per wavefront (measured on MI355X, M=1, 10240 x 5120: 11.6 us
+    // against 12.8 with four rows and 13.1 with one)
+    case 1: launch_m<1, 2, 6>(w, x, Y, N, s); break;
+    case 2: launch_m<2, 2, 6>(w, x, Y, N, s); break;
+    case 3: launch_m<3, 2, 4>(w, x, Y, N, s); break;
+    case 4: launch_m<4, 2, 4>(w, x, Y, N, s); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
