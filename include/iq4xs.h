@@ -56,7 +56,9 @@ extern "C" {
 
 /* ---- status codes ---- */
 #define IQ4XS_OK 0
-#define IQ4XS_EINVAL (-1)  /* null pointer, M/N < 1, K not a multiple of 256, size overflow,
+#define IQ4XS_EINVAL (-1)  /* null pointer, M/N < 1, K not a multiple of 256, size overflow
+                              (for the matmul entry points also M*K >= 1.9e9: the
+                              activations' internal copy must stay below 2 GiB),
                               Y overlapping an input, unknown path                         */
 #define IQ4XS_EALIGN (-2)  /* W, X or Y not 16-byte aligned, Xq not 4-byte aligned          */
 #define IQ4XS_EDEVICE (-3) /* no HIP device, or the current device is not gfx950            */

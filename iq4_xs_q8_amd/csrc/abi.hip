@@ -191,6 +191,11 @@ int check_dims(int64_t M, int64_t N, int64_t K)
     if (M > (1LL << 31) || N > (1LL << 31) || K > (1LL << 31) || !mul_ok(M, K, &t) ||
         !mul_ok(N, K, &t) || !mul_ok(M, N, &t) || !mul_ok(t, 4, &t))
         return fail(IQ4XS_EINVAL, "sizes overflow");
+    // the matmul kernels address the activation planes (1.125 bytes per
+    // element, rows padded to 4) with 32-bit offsets
+    if (round_up(M, MPAD) * K / 8 * 9 >= (1LL << 31))
+        return fail(IQ4XS_EINVAL, "M*K too large: the activation planes must stay below 2 GiB (M=%lld K=%lld)",
+                    (long long)M, (long long)K);
     return IQ4XS_OK;
 }
 

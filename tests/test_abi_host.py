@@ -61,7 +61,7 @@ def test_sizes():
 
 
 @pytest.mark.parametrize("M,N,K", [(0, 8, 256), (4, 0, 256), (4, 8, 0), (4, 8, 128), (4, 8, 300),
-                                   (1 << 40, 8, 256), (4, 1 << 40, 256)])
+                                   (1 << 40, 8, 256), (4, 1 << 40, 256), (70000, 8, 32768)])
 def test_gemm_bad_sizes(M, N, K):
     assert L.iq4xs_gemm(A, A * 2, A * 4, M, N, K, None) == iq.EINVAL
     assert L.iq4xs_gemm_q8_1(A, A * 2, A * 4, M, N, K, 0, None) == iq.EINVAL

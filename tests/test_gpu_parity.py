@@ -261,6 +261,30 @@ def test_large_m_grid():
     assert_rows_close(y.T, O.gemm(W, X).T)
 
 
+def test_weights_above_2gib():
+    """A weight matrix larger than 2 GiB (N = 2^20 rows, K = 4096): the
+    streaming and tile kernels address W with 32-bit offsets and decline it,
+    so MMQ runs the K-split kernel (a buffer descriptor per 32-row tile); the
+    GEMV addresses rows with 64-bit pointers.  Sampled columns against the
+    oracle, the last rows included."""
+    M, N, K = 2, 1 << 20, 4096
+    W = synth.weights((55, N, K), N, K)
+    assert W.nbytes > (2 << 30)
+    X = synth.activations((56, M, K), M, K)
+    Wd, Xd = dev(W), dev(X)
+    cols = np.unique(np.concatenate([_sample_cols(N, n=96, seed=5), np.arange(N - 40, N)]))
+    ref = O.gemm_q8_1(W[cols], O.quantize_q8_1(X), K)
+    for p in (iq.PATH_MMQ, iq.PATH_GEMV):
+        y = iq.gemm(Wd, Xd, path=p, out=poisoned((M, N)))
+        torch.cuda.synchronize()
+        ys = y[:, torch.from_numpy(cols).cuda()].cpu().numpy()
+        assert np.all(np.isfinite(y.cpu().numpy())), f"{iq.path_name(p)}: outputs not written"
+        assert_rows_close(ys, ref, what=f"{iq.path_name(p)} N={N} K={K}")
+        del y
+    del Wd
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------------ full sizes
 def _sample_cols(N, n=192, seed=0):
     rng = np.random.default_rng(seed)
