@@ -71,7 +71,6 @@ constexpr int wrow_bytes(int ch)
 template <int LIVE_, int MPC_, int CH_, int NBUF_>
 struct Cfg {
     static constexpr int LIVE = LIVE_, MPC = MPC_, CH = CH_, NBUF = NBUF_;
-    static constexpr int CH0 = CH < 2 ? CH : 2;                              // first chunk
     static constexpr int WROW = wrow_bytes(CH);
     static constexpr int W_PR = CH * WBLK / 16;                               // pieces per row
     // one chunk buffer: weights [32][WROW] (padded to whole KB), activations
@@ -368,11 +367,12 @@ k_mmv(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__res
     cur.u = ua;
     cur.t = runs.t[g];
     cur.j = ua - cur.t * nb;
-    // (the first chunk is short, so that computing starts early)
+    // (every chunk is CH super-blocks long where the run allows: a short first
+    // chunk, to start computing earlier, measured slower on every shape)
     Chunk info[NBUF];
     static_for(std::make_integer_sequence<int, NBUF - 1>(), [&](auto bc) {
         constexpr int b = decltype(bc)::value;
-        info[b] = cur.next(b == 0 ? C::CH0 : CH);
+        info[b] = cur.next(CH);
         issue(info[b], bc);
     });
     // Step on buffer b: wait for this wavefront's loads of its chunk (the
@@ -463,7 +463,7 @@ hipError_t launch_mmv(const void *Wv, const XPlanes &x, float *Y, int64_t N, con
     case 2: return launch_c<Cfg<2, 4, 8, 3>>(W, x, Y, N, p, s);
     case 3: return launch_c<Cfg<3, 4, 8, 3>>(W, x, Y, N, p, s);
     case 4:
-        return x.Mp <= 4 ? launch_c<Cfg<4, 4, 8, 3>>(W, x, Y, N, p, s) : launch_c<Cfg<4, 8, 4, 4>>(W, x, Y, N, p, s);
+        return x.Mp <= 4 ? launch_c<Cfg<4, 4, 8, 3>>(W, x, Y, N, p, s) : launch_c<Cfg<4, 8, 4, 3>>(W, x, Y, N, p, s);
     case 8: return launch_c<Cfg<8, 16, 4, 3>>(W, x, Y, N, p, s);
     case 16: return launch_c<Cfg<16, 32, 2, 3>>(W, x, Y, N, p, s);
     default: return hipErrorInvalidValue;
