@@ -346,7 +346,45 @@ def _wdev_cached(wl, N, K, W):
     return _cache[key]
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 1024, 2048), (3, 520, 1280), (8, 2048, 2048), (40, 640, 4096)])
+# More 32-column tiles than compute units: the streaming kernel's balanced runs
+# end inside tiles, and each such tile is summed from its two owners' partial
+# tiles through the workspace (flag swap, fixed order).  With M <= 4 and an
+# fp32 X the kernel also quantizes X itself; the pre-quantized and prepared-
+# activation entry points run the same matmul on planes from the quantize
+# kernel, so all of them must agree bit for bit.
+SHARED_SHAPES = [(1, 8224, 512), (2, 10240, 1024), (3, 8224, 1024), (4, 10240, 2048),
+                 (7, 8224, 512), (16, 10240, 1024), (32, 8224, 512)]
+
+
+@pytest.mark.parametrize("M,N,K", SHARED_SHAPES)
+def test_shared_tiles_match_oracle(M, N, K):
+    W, X = _inputs(M, N, K, seed=5)
+    Xq = O.quantize_q8_1(X)
+    ref = O.gemm_q8_1(W, Xq, K)
+    Wd, Xd = dev(W), dev(X)
+    p = iq.PATH_MMQ
+    y = iq.gemm(Wd, Xd, path=p, out=poisoned((M, N))).cpu().numpy()
+    assert_rows_close(y, ref, what=f"MMQ shared tiles M={M} N={N} K={K}")
+    y2 = iq.gemm_q8_1(Wd, dev(Xq), K, path=p, out=poisoned((M, N))).cpu().numpy()
+    assert np.array_equal(y, y2), "gemm and gemm_q8_1 differ"
+    act = iq.prepare_act(Xd)
+    y3 = iq.gemm_act(Wd, act, M, K, path=p, out=poisoned((M, N))).cpu().numpy()
+    assert np.array_equal(y, y3), "gemm and gemm_act differ"
+    # the workspace may hold anything on entry, also what a call left behind
+    ws = torch.empty(iq.workspace_bytes(M, N, K, p), dtype=torch.uint8, device="cuda")
+    for fill in (0, 255, None, None):
+        if fill is None:
+            ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8).cuda())
+        else:
+            ws.fill_(fill)
+        y4 = iq.gemm(Wd, Xd, path=p, out=poisoned((M, N)), workspace=ws).cpu().numpy()
+        assert np.array_equal(y, y4), f"gemm_ws differs (workspace fill {fill})"
+        y5 = iq.gemm(Wd, Xd, path=p, out=poisoned((M, N)), workspace=ws).cpu().numpy()
+        assert np.array_equal(y, y5), "second call on the same workspace differs"
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1024, 2048), (3, 520, 1280), (8, 2048, 2048), (40, 640, 4096),
+                                   (4, 8224, 1024), (16, 10240, 512)])
 def test_graph_replays_match_eager(M, N, K):
     """The caller-workspace entry point recorded in a HIP graph: every replay,
     with eager work and new inputs in between, equals the eager call."""
