@@ -75,7 +75,7 @@ def kernel_name(M, N, K, path):
     nb = K // 256
     if M <= 32 and nb % 2 == 0 and N * nb * 136 < (1 << 31):
         return "k_mmv"
-    return "k_mmqt" if M > 64 else "k_mmq"
+    return "k_mmqt" if M > 32 else "k_mmq"
 
 
 def source_hash(kernel):
