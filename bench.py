@@ -18,6 +18,8 @@ Printed: one JSON line with
   roofline   for the dominant kernel (the matmul launch with the largest
              duration): algorithmic bytes per launch / its average duration,
              timed with HIP events on the stream the kernel runs on
+  group      one X against the MLP gate/up pair: the grouped call (one
+             quantization, one matmul launch) against two separate calls
   cpu_baseline  the CPU oracle (never tuned) on a bounded sample of the same
              sweep, in the same unit.
 `--sweep FILE` additionally times every (shape, M, path) point of the five
@@ -164,6 +166,52 @@ def measure_point(rot, X, N, K, path, reps=30):
             kern()
         t_kern = time_events(kern, reps, stream)
     return t_call, t_kern, t_eager
+
+
+def measure_group(ms=(1, 8, 16), reps=20):
+    """One X against the MLP gate/up pair (two N=17408, K=5120 matrices): one
+    grouped call (one quantization, one matmul launch over both) against two
+    iq4xs_gemm calls; ms per pair from HIP events over back-to-back calls on
+    one stream, weight pairs rotated past the Infinity Cache."""
+    wl = synth.MLP_UP
+    N, K = wl.shapes[0]
+    base = torch.from_numpy(wl.w(N, K)).cuda()
+    npairs = max(2, math.ceil((640 << 20) / (2 * base.numel())))
+    pairs = [(base.clone(), base.clone()) for _ in range(npairs)]
+    del base
+    stream = torch.cuda.current_stream()
+    wb = 2 * 0.53125 * N * K
+    points = []
+    for M in ms:
+        X = torch.from_numpy(wl.x(M, K, N=N)).cuda()
+        Y = [torch.empty((M, N), dtype=torch.float32, device="cuda") for _ in range(2)]
+        it = [0]
+
+        def nxt():
+            it[0] += 1
+            return pairs[it[0] % npairs]
+
+        def grouped():
+            a, b = nxt()
+            iq.gemm_group([a, b], X, Y)
+
+        def separate():
+            a, b = nxt()
+            iq.gemm(a, X, out=Y[0])
+            iq.gemm(b, X, out=Y[1])
+
+        for f in (grouped, separate):
+            for _ in range(3):
+                f()
+        tg = time_events(grouped, reps, stream)
+        ts = time_events(separate, reps, stream)
+        points.append({"M": M, "grouped_ms": tg, "separate_ms": ts, "speedup": ts / tg,
+                       "grouped_weight_GBs": wb / (tg * 1e-3) / 1e9,
+                       "grouped_hbm_frac": (wb + (4 + 2.25) * M * K + 8 * M * N) / (tg * 1e-3) / 1e9 / HBM_PEAK_GBS})
+    del pairs
+    torch.cuda.empty_cache()
+    return {"workload": "MLP gate/up pair, two matrices N=17408 K=5120 sharing X, quantize included",
+            "points": points}
 
 
 def point_record(N, K, M, path, t_call, t_kern, t_eager=None):
@@ -538,7 +586,7 @@ def main():
     dom = max(per_m, key=lambda r: r["kernel_ms"])
     dom_kernel = kernel_name(dom["M"], N, K, iq.PATHS[dom["path"]])
     achieved = algo_bytes_kernel(dom["M"], N, K) / (dom["kernel_ms"] * 1e-3) / 1e9
-    label = {1: "1,4,8,3", 2: "2,4,8,3", 4: "4,4,8,3", 8: "4,8,4,4",
+    label = {1: "1,4,8,3", 2: "2,4,8,3", 4: "4,4,8,3", 8: "4,8,4,3",
              16: "8,16,4,3"}.get(dom["M"], "") if dom_kernel == "k_mmv" else ""
     traffic = traffic_for(dom_kernel, label)
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -558,6 +606,8 @@ def main():
                       "N": N, "K": K, "M": list(ms), "weight_copies": len(rot.ws)},
            "wall_s": wall, "graph_ms_per_step": graph_ms,
            "graph_weight_GBs": wbytes / (graph_ms * 1e-3) / 1e9, "per_m": per_m, "roofline": roofline}
+    del graphs
+    out["group"] = measure_group()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, N, K, ms)
     if args.sweep:

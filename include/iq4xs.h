@@ -141,6 +141,24 @@ int iq4xs_prepare_act(const float *X, void *act, int64_t M, int64_t K, void *str
 int iq4xs_gemm_act(const void *W, const void *act, float *Y, int64_t M, int64_t N, int64_t K,
                    int path, void *stream);
 
+/* Several weight matrices that share one X ("SGLang MoE port thread",
+ * decode measurements of the grouped expert call: one call per layer,
+ * because a single small call is dominated by launch cost and a grouped one
+ * adds little per extra unit): Y[g] = X * W[g]^T for g < G, with X quantized
+ * once and, when the shapes allow (M <= 32, K/256 even), one launch of the
+ * streaming matmul kernel over the tiles of all G matrices, numbered one
+ * matrix after the other.  W, Y and N are host arrays of G entries:
+ * W[g] [N[g]][K/256] IQ4_XS super-blocks, Y[g] fp32 [M][N[g]] (overwritten);
+ * 1 <= G <= IQ4XS_MAX_GROUP; pointers 16-byte aligned; no Y[g] may overlap X,
+ * any W[h] or another Y[h].  Other shapes run one iq4xs_gemm per matrix.
+ * Every output is within the same bound of the oracle as iq4xs_gemm; where a
+ * tile's K range is split between workgroups at other points than in a
+ * single-matrix call, the last bits can differ from that call's.  Scratch
+ * comes from the device's default pool, stream-ordered. */
+#define IQ4XS_MAX_GROUP 4
+int iq4xs_gemm_group(const void *const *W, float *const *Y, const int64_t *N, int G, const float *X,
+                     int64_t M, int64_t K, void *stream);
+
 /* Dequantize W [N][K] to bf16 Wb [N][K] (row-major): each weight
  * d*(ls-32)*kvalues[index], computed exactly in fp32, rounded to the nearest
  * bf16 (ties to even).  ("V100TPS engine log", M=64 kernel-launch table:

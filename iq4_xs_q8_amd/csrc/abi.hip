@@ -515,6 +515,70 @@ int iq4xs_gemm_act(const void *W, const void *act, float *Y, int64_t M, int64_t 
     return launch_err(launch_mmq(W, xp, Y, N, scr.p, y_zeroed, s), path_name(path));
 }
 
+static_assert(IQ4XS_MAX_GROUP == MAXGRP, "group bound of the header and the kernels");
+
+int iq4xs_gemm_group(const void *const *W, float *const *Y, const int64_t *N, int G, const float *X,
+                     int64_t M, int64_t K, void *stream)
+{
+    if (!W || !Y || !N || !X)
+        return fail(IQ4XS_EINVAL, "null pointer");
+    if (G < 1 || G > IQ4XS_MAX_GROUP)
+        return fail(IQ4XS_EINVAL, "group of %d matrices (1..%d)", G, IQ4XS_MAX_GROUP);
+    if (!aligned(X, 16))
+        return fail(IQ4XS_EALIGN, "X must be 16-byte aligned");
+    for (int g = 0; g < G; g++) {
+        if (!W[g] || !Y[g])
+            return fail(IQ4XS_EINVAL, "null pointer (matrix %d)", g);
+        int st = check_dims(M, N[g], K);
+        if (st != IQ4XS_OK)
+            return st;
+        if (!aligned(W[g], 16) || !aligned(Y[g], 16))
+            return fail(IQ4XS_EALIGN, "W and Y must be 16-byte aligned (matrix %d)", g);
+    }
+    for (int g = 0; g < G; g++) {
+        const size_t yb = (size_t)(M * N[g] * 4);
+        if (overlaps(Y[g], yb, X, (size_t)(M * K * 4)))
+            return fail(IQ4XS_EINVAL, "Y overlaps an input (matrix %d)", g);
+        for (int h = 0; h < G; h++)
+            if (overlaps(Y[g], yb, W[h], (size_t)(N[h] * (K / QK) * WBLK)) ||
+                (h != g && overlaps(Y[g], yb, Y[h], (size_t)(M * N[h] * 4))))
+                return fail(IQ4XS_EINVAL, "Y of matrix %d overlaps a weight matrix or another output", g);
+    }
+    ensure_init();
+    int st = check_device();
+    if (st != IQ4XS_OK)
+        return st;
+    const hipStream_t s = (hipStream_t)stream;
+    const MmvPlan p = tune_override().mmv != 0 ? mmv_plan_group(M, N, G, K, device_cus()) : MmvPlan();
+    if (!p.ok) {
+        // shapes the streaming kernel does not take: one call per matrix
+        for (int g = 0; g < G; g++)
+            if ((st = run_gemm(W[g], X, nullptr, Y[g], M, N[g], K, IQ4XS_PATH_AUTO, nullptr, 0, s)) != IQ4XS_OK)
+                return st;
+        return IQ4XS_OK;
+    }
+    Scratch scr;
+    scr.s = s;
+    const size_t need = xplanes_bytes(M, K);
+    if (hipMallocAsync(&scr.p, need, s) != hipSuccess) {
+        (void)hipGetLastError();
+        scr.p = nullptr;
+        return fail(IQ4XS_ENOMEM, "scratch of %zu bytes", need);
+    }
+    const XPlanes xp = xplanes_at(scr.p, M, K);
+    ZeroList zl;
+    if (p.zero_y) {
+        zl.count = G;
+        for (int g = 0; g < G; g++) {
+            zl.p[g] = Y[g];
+            zl.n[g] = M * N[g];
+        }
+    }
+    if ((st = launch_err(launch_quantize(X, nullptr, &xp, nullptr, M, K, s, zl), "quantize")) != IQ4XS_OK)
+        return st;
+    return launch_err(launch_mmv_group(mmv_group(W, Y, N, G), xp, p, s), "MMQ group");
+}
+
 int iq4xs_dispatch(int64_t M, int64_t N, int64_t K, int *path_out)
 {
     if (!path_out)

@@ -165,12 +165,43 @@ inline XPlanes xplanes_at(void *base, int64_t M, int64_t K)
     return p;
 }
 
+// Up to MAXGRP weight matrices with the same K that share one X (the
+// streaming kernel's grouped launch): matrix g has N[g] rows at w[g] and its
+// own output y[g] ([M][N[g]]); its 32-column tiles are t0[g] .. t0[g+1]-1 of
+// the tiles numbered across the group.
+constexpr int MAXGRP = 4;
+struct MmvGroup {
+    const uint8_t *w[MAXGRP];
+    float *y[MAXGRP];
+    int n[MAXGRP];
+    int t0[MAXGRP + 1];
+    int count;
+    __device__ __forceinline__ int matrix_of(int t) const
+    {
+        int gi = 0;
+#pragma unroll
+        for (int q = 1; q < MAXGRP; q++)
+            gi += (q < count && t >= t0[q]) ? 1 : 0;
+        return gi;
+    }
+};
+
+// Outputs the quantize kernels zero on the way (for matmuls that add partial
+// tiles into Y): up to MAXGRP ranges p[i][0..n[i]), 16-byte aligned.
+struct ZeroList {
+    float *p[MAXGRP] = {};
+    int64_t n[MAXGRP] = {};
+    int count = 0;
+};
+
 // ---- launchers (each defined in the .hip file that holds its kernel) -----
 // All return a hipError_t from hipGetLastError() after the launch.  The
 // quantizers also zero yz[0..nz) when yz is given (the output of a matmul
 // that adds partial tiles into it).
 hipError_t launch_quantize(const float *X, void *Xq, const XPlanes *planes, uint16_t *Xbf,
                            int64_t M, int64_t K, hipStream_t s, float *yz = nullptr, int64_t nz = 0);
+hipError_t launch_quantize(const float *X, void *Xq, const XPlanes *planes, uint16_t *Xbf,
+                           int64_t M, int64_t K, hipStream_t s, const ZeroList &zl);
 hipError_t launch_q8_1_convert(const void *Xq, const XPlanes *planes, uint16_t *Xbf, int64_t M,
                               int64_t K, hipStream_t s, float *yz = nullptr, int64_t nz = 0);
 hipError_t launch_zero(float *y, int64_t n, hipStream_t s);
@@ -189,6 +220,10 @@ struct MmvPlan {
 MmvPlan mmv_plan(int64_t M, int64_t N, int64_t K, int cus);
 hipError_t launch_mmv(const void *W, const XPlanes &x, float *Y, int64_t N, const MmvPlan &p,
                       hipStream_t s);
+// The same over a group of matrices (one launch; zero_y: every y[g] zeroed).
+MmvPlan mmv_plan_group(int64_t M, const int64_t *N, int count, int64_t K, int cus);
+MmvGroup mmv_group(const void *const *W, float *const *Y, const int64_t *N, int count);
+hipError_t launch_mmv_group(const MmvGroup &grp, const XPlanes &x, const MmvPlan &p, hipStream_t s);
 // Tile kernel for M > 32 (mmqt.hip): 128 x 128 tiles, runs of (tile, half
 // super-block) units over `grid` workgroups; tiles shared by several
 // workgroups are summed from a workspace of partial tiles by a second kernel.

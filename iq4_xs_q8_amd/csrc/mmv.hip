@@ -120,11 +120,11 @@ __device__ __forceinline__ void epilogue(const v16i &D, float sw, const float4 *
 
 // LIVE: result registers that can hold a real row: 1, 2, 3, 4 (rows 0..LIVE-1
 // in lanes 0-31; LIVE = 4 also serves M <= 8 through lanes 32-63), 8 (M <= 16),
-// 16 (M <= 32).  MPC: a bound on the padded activation rows Mp.
-template <class C>
+// 16 (M <= 32).  MPC: a bound on the padded activation rows Mp.  GRP: grp
+// holds several matrices (else only matrix 0 is read, at fixed offsets).
+template <class C, bool GRP>
 __global__ void __launch_bounds__(NT, 1)
-k_mmv(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__restrict__ Y, int M, int N,
-      int K, int Mp, int nb, Runs runs)
+k_mmv(MmvGroup grp, const int8_t *__restrict__ qp, int M, int K, int Mp, int nb, Runs runs)
 {
     constexpr int LIVE = C::LIVE, CH = C::CH, NBUF = C::NBUF, SLOTS = C::SLOTS;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -141,8 +141,6 @@ k_mmv(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__res
     // (contiguous: scales at qp + Mp*K); offsets are per lane, so rows past N
     // and pieces past a plane read as zero
     const int dp_at = Mp * K;
-    const __amdgpu_buffer_rsrc_t wr =
-        __builtin_amdgcn_make_buffer_rsrc((void *)W, (short)0, (int)((uint32_t)N * row_bytes), BUFFER_FLAGS);
     const __amdgpu_buffer_rsrc_t xr =
         __builtin_amdgcn_make_buffer_rsrc((void *)qp, (short)0, dp_at + Mp * (K / SB) * 4, BUFFER_FLAGS);
     const bool w_group = wave < C::WA;                        // (uniform)
@@ -192,8 +190,12 @@ k_mmv(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__res
     auto issue = [&](const Chunk &c, auto bc) __attribute__((always_inline)) {
         char *buf = C::template buf<decltype(bc)::value>();
         if (w_group) {
+            // the chunk's matrix (tiles are numbered across the matrices)
+            const int gi = GRP ? grp.matrix_of(c.t) : 0;
+            const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)grp.w[gi], (short)0, (int)((uint32_t)grp.n[gi] * row_bytes), BUFFER_FLAGS);
             const int lo = (c.j0 & 1) * WBLK, hi = lo + c.cl * WBLK;
-            const uint32_t base = (uint32_t)c.t * TILE * row_bytes + (c.j0 & ~1) * WBLK;
+            const uint32_t base = (uint32_t)(c.t - grp.t0[gi]) * TILE * row_bytes + (c.j0 & ~1) * WBLK;
 #pragma unroll
             for (int k = 0; k < SLOTS; k++) {
                 const bool need = (uint32_t)(p_key[k] - lo) < (uint32_t)(hi - lo + 15);
@@ -256,9 +258,12 @@ k_mmv(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__res
                 v += shr_row(v, std::integral_constant<int, 4>());
             if constexpr (GS >= 16)
                 v += shr_row(v, std::integral_constant<int, 8>());
+            const int gi = GRP ? grp.matrix_of(t) : 0;
+            const int N = grp.n[gi];
+            float *const Y = grp.y[gi];
             const int r = o >> 6, l2 = o & 63;
             const int m = 8 * (r / 4) + 4 * (l2 >> 5) + (r % 4);
-            const int n = t * TILE + (l2 & 31);
+            const int n = (t - grp.t0[gi]) * TILE + (l2 & 31);
             if (part == GS - 1 && m < M && n < N) {
                 if (owned)
                     Y[(int64_t)m * N + n] = v;
@@ -402,10 +407,10 @@ k_mmv(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__res
 }
 
 template <class C>
-hipError_t launch_c(const uint8_t *W, const XPlanes &x, float *Y, int64_t N, const MmvPlan &p, hipStream_t s)
+hipError_t launch_c(const MmvGroup &grp, const XPlanes &x, const MmvPlan &p, hipStream_t s)
 {
     const int nb = (int)(x.K / QK);
-    const int64_t T = (N + TILE - 1) / TILE;
+    const int64_t T = grp.t0[grp.count];
     // (the kernel reads both planes through one descriptor)
     if ((const char *)x.dp != (const char *)x.qp + x.Mp * x.K || x.Mp > C::MPC || x.M > C::MA)
         return hipErrorInvalidValue;
@@ -418,24 +423,35 @@ hipError_t launch_c(const uint8_t *W, const XPlanes &x, float *Y, int64_t N, con
         if (g < p.grid)
             runs.t[g] = runs.u[g] / nb;
     }
-    hipLaunchKernelGGL((k_mmv<C>), dim3((unsigned)p.grid), dim3(NT), 0, s, W, x.qp, Y, (int)x.M, (int)N,
-                       (int)x.K, (int)x.Mp, nb, runs);
+    if (grp.count > 1)
+        hipLaunchKernelGGL((k_mmv<C, true>), dim3((unsigned)p.grid), dim3(NT), 0, s, grp, x.qp, (int)x.M,
+                           (int)x.K, (int)x.Mp, nb, runs);
+    else
+        hipLaunchKernelGGL((k_mmv<C, false>), dim3((unsigned)p.grid), dim3(NT), 0, s, grp, x.qp, (int)x.M,
+                           (int)x.K, (int)x.Mp, nb, runs);
     return hipGetLastError();
 }
 
 }  // namespace
 
-MmvPlan mmv_plan(int64_t M, int64_t N, int64_t K, int cus)
+MmvPlan mmv_plan_group(int64_t M, const int64_t *N, int count, int64_t K, int cus)
 {
     MmvPlan p;
     const int64_t nb = K / QK, row_bytes = nb * WBLK;
     const int64_t Mp = round_up(M, MPAD);
-    const int64_t T = (N + TILE - 1) / TILE;
+    if (count < 1 || count > MAXGRP)
+        return p;
     // K/256 even (16-byte aligned chunk windows) and below 2^16; 32-bit
-    // buffer offsets and unit counts: the weight matrix, the activation planes
-    // and T*K/256 stay below 2^31
-    if (M < 1 || M > TILE || nb % 2 != 0 || nb >= (1 << 16) || N * row_bytes >= (1LL << 31) ||
-        Mp * K + Mp * K / 8 >= (1LL << 31) || T * nb >= (1LL << 31))
+    // buffer offsets and unit counts: each weight matrix, the activation
+    // planes and (all tiles)*K/256 stay below 2^31
+    int64_t T = 0;
+    for (int g = 0; g < count; g++) {
+        if (N[g] < 1 || N[g] * row_bytes >= (1LL << 31))
+            return p;
+        T += (N[g] + TILE - 1) / TILE;
+    }
+    if (M < 1 || M > TILE || nb % 2 != 0 || nb >= (1 << 16) || Mp * K + Mp * K / 8 >= (1LL << 31) ||
+        T * nb >= (1LL << 31))
         return p;
     const int64_t U = T * nb;
     p.grid = (int)(T < cus ? T : cus);
@@ -452,22 +468,43 @@ MmvPlan mmv_plan(int64_t M, int64_t N, int64_t K, int cus)
     return p;
 }
 
-hipError_t launch_mmv(const void *Wv, const XPlanes &x, float *Y, int64_t N, const MmvPlan &p,
-                      hipStream_t s)
+MmvPlan mmv_plan(int64_t M, int64_t N, int64_t K, int cus) { return mmv_plan_group(M, &N, 1, K, cus); }
+
+MmvGroup mmv_group(const void *const *W, float *const *Y, const int64_t *N, int count)
 {
-    const uint8_t *W = (const uint8_t *)Wv;
-    if (!p.ok)
+    MmvGroup g{};
+    g.count = count;
+    g.t0[0] = 0;
+    for (int i = 0; i < count; i++) {
+        g.w[i] = (const uint8_t *)W[i];
+        g.y[i] = Y[i];
+        g.n[i] = (int)N[i];
+        g.t0[i + 1] = g.t0[i] + (int)((N[i] + TILE - 1) / TILE);
+    }
+    for (int i = count; i < MAXGRP; i++)
+        g.t0[i + 1] = g.t0[count];
+    return g;
+}
+
+hipError_t launch_mmv_group(const MmvGroup &grp, const XPlanes &x, const MmvPlan &p, hipStream_t s)
+{
+    if (!p.ok || grp.count < 1 || grp.count > MAXGRP)
         return hipErrorInvalidValue;
     switch (p.live) {
-    case 1: return launch_c<Cfg<1, 4, 8, 3>>(W, x, Y, N, p, s);
-    case 2: return launch_c<Cfg<2, 4, 8, 3>>(W, x, Y, N, p, s);
-    case 3: return launch_c<Cfg<3, 4, 8, 3>>(W, x, Y, N, p, s);
+    case 1: return launch_c<Cfg<1, 4, 8, 3>>(grp, x, p, s);
+    case 2: return launch_c<Cfg<2, 4, 8, 3>>(grp, x, p, s);
+    case 3: return launch_c<Cfg<3, 4, 8, 3>>(grp, x, p, s);
     case 4:
-        return x.Mp <= 4 ? launch_c<Cfg<4, 4, 8, 3>>(W, x, Y, N, p, s) : launch_c<Cfg<4, 8, 4, 3>>(W, x, Y, N, p, s);
-    case 8: return launch_c<Cfg<8, 16, 4, 3>>(W, x, Y, N, p, s);
-    case 16: return launch_c<Cfg<16, 32, 2, 3>>(W, x, Y, N, p, s);
+        return x.Mp <= 4 ? launch_c<Cfg<4, 4, 8, 3>>(grp, x, p, s) : launch_c<Cfg<4, 8, 4, 3>>(grp, x, p, s);
+    case 8: return launch_c<Cfg<8, 16, 4, 3>>(grp, x, p, s);
+    case 16: return launch_c<Cfg<16, 32, 2, 3>>(grp, x, p, s);
     default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_mmv(const void *W, const XPlanes &x, float *Y, int64_t N, const MmvPlan &p, hipStream_t s)
+{
+    return launch_mmv_group(mmv_group(&W, &Y, &N, 1), x, p, s);
 }
 
 }  // namespace iq4xs

@@ -53,6 +53,14 @@ __device__ __forceinline__ void zero_range(float *yz, int64_t nz, int64_t tid, i
         yz[4 * n4 + tid] = 0.0f;
 }
 
+__device__ __forceinline__ void zero_list(const ZeroList &zl, int64_t tid, int64_t stride)
+{
+#pragma unroll
+    for (int i = 0; i < MAXGRP; i++)
+        if (i < zl.count)
+            zero_range(zl.p[i], zl.n[i], tid, stride);
+}
+
 __global__ void __launch_bounds__(256) k_zero(float *__restrict__ y, int64_t n)
 {
     zero_range(y, n, (int64_t)blockIdx.x * blockDim.x + threadIdx.x, (int64_t)gridDim.x * blockDim.x);
@@ -71,11 +79,11 @@ __device__ __forceinline__ int quant1(float x, float d)
 // them through buffer descriptors that stop at row M.
 __global__ void __launch_bounds__(256)
 k_quantize(const float *__restrict__ X, uint8_t *__restrict__ Xq, int8_t *__restrict__ qp,
-           float *__restrict__ dp, float *__restrict__ yz, int64_t nz, uint16_t *__restrict__ Xbf,
+           float *__restrict__ dp, ZeroList zl, uint16_t *__restrict__ Xbf,
            int64_t M, int64_t Mrows, int64_t Mp, int64_t K)
 {
     const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    zero_range(yz, nz, tid, (int64_t)gridDim.x * blockDim.x);
+    zero_list(zl, tid, (int64_t)gridDim.x * blockDim.x);
     const int64_t nblk_row = K / SB;
     const int64_t blk = tid >> 3;                 // global Q8_1 block index
     const int t = (int)(tid & 7);                 // lane within the block
@@ -127,11 +135,11 @@ k_quantize(const float *__restrict__ X, uint8_t *__restrict__ Xq, int8_t *__rest
 // k_quantize.
 __global__ void __launch_bounds__(256)
 k_q8_1_convert(const uint8_t *__restrict__ Xq, int8_t *__restrict__ qp, float *__restrict__ dp,
-               float *__restrict__ yz, int64_t nz, uint16_t *__restrict__ Xbf, int64_t M, int64_t Mrows,
+               ZeroList zl, uint16_t *__restrict__ Xbf, int64_t M, int64_t Mrows,
                int64_t Mp, int64_t K)
 {
     const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    zero_range(yz, nz, tid, (int64_t)gridDim.x * blockDim.x);
+    zero_list(zl, tid, (int64_t)gridDim.x * blockDim.x);
     const int64_t nblk_row = K / SB;
     const int64_t blk = tid >> 3;
     const int t = (int)(tid & 7);
@@ -172,16 +180,28 @@ hipError_t launch_zero(float *y, int64_t n, hipStream_t s)
 }
 
 hipError_t launch_quantize(const float *X, void *Xq, const XPlanes *planes, uint16_t *Xbf,
-                           int64_t M, int64_t K, hipStream_t s, float *yz, int64_t nz)
+                           int64_t M, int64_t K, hipStream_t s, const ZeroList &zl)
 {
     const int64_t Mrows = M;
     const int64_t threads = Mrows * (K / 4);
     const int64_t grid = (threads + 255) / 256;
     hipLaunchKernelGGL(k_quantize, dim3((unsigned)grid), dim3(256), 0, s, X, (uint8_t *)Xq,
                        planes ? planes->qp : nullptr, planes ? planes->dp : nullptr,
-                       yz, nz, Xbf, M, Mrows,
+                       zl, Xbf, M, Mrows,
                        planes ? planes->Mp : M, K);
     return hipGetLastError();
+}
+
+hipError_t launch_quantize(const float *X, void *Xq, const XPlanes *planes, uint16_t *Xbf,
+                           int64_t M, int64_t K, hipStream_t s, float *yz, int64_t nz)
+{
+    ZeroList zl;
+    if (yz != nullptr && nz > 0) {
+        zl.p[0] = yz;
+        zl.n[0] = nz;
+        zl.count = 1;
+    }
+    return launch_quantize(X, Xq, planes, Xbf, M, K, s, zl);
 }
 
 hipError_t launch_q8_1_convert(const void *Xq, const XPlanes *planes, uint16_t *Xbf, int64_t M,
@@ -190,9 +210,15 @@ hipError_t launch_q8_1_convert(const void *Xq, const XPlanes *planes, uint16_t *
     const int64_t Mrows = M;
     const int64_t threads = Mrows * (K / 4);
     const int64_t grid = (threads + 255) / 256;
+    ZeroList zl;
+    if (yz != nullptr && nz > 0) {
+        zl.p[0] = yz;
+        zl.n[0] = nz;
+        zl.count = 1;
+    }
     hipLaunchKernelGGL(k_q8_1_convert, dim3((unsigned)grid), dim3(256), 0, s, (const uint8_t *)Xq,
                        planes ? planes->qp : nullptr, planes ? planes->dp : nullptr,
-                       yz, nz, Xbf, M, Mrows,
+                       zl, Xbf, M, Mrows,
                        planes ? planes->Mp : M, K);
     return hipGetLastError();
 }

@@ -131,6 +131,42 @@ def test_no_device_reports_edevice():
     assert L.iq4xs_dequantize_bf16(A, A * 2, 8, 256, None) == iq.EDEVICE
 
 
+def _group_args(ws, ys, ns):
+    G = max(len(ws), 1)
+    return ((ctypes.c_void_p * G)(*ws), (ctypes.c_void_p * G)(*ys), (ctypes.c_int64 * G)(*ns))
+
+
+def test_gemm_group_validation():
+    g = L.iq4xs_gemm_group
+    w, y, n = _group_args([A, A * 2], [A * 4, A * 8], [8, 16])
+    assert g(None, y, n, 2, A * 16, 4, 256, None) == iq.EINVAL
+    assert g(w, y, n, 2, None, 4, 256, None) == iq.EINVAL
+    assert g(w, y, n, 0, A * 16, 4, 256, None) == iq.EINVAL
+    w5, y5, n5 = _group_args([A] * 5, [A * 4] * 5, [8] * 5)
+    assert g(w5, y5, n5, 5, A * 16, 4, 256, None) == iq.EINVAL
+    assert g(w, y, n, 2, A * 16 + 4, 4, 256, None) == iq.EALIGN
+    wa, ya, na = _group_args([A, A * 2 + 8], [A * 4, A * 8], [8, 16])
+    assert g(wa, ya, na, 2, A * 16, 4, 256, None) == iq.EALIGN
+    wz, yz, nz = _group_args([A, None], [A * 4, A * 8], [8, 16])
+    assert g(wz, yz, nz, 2, A * 16, 4, 256, None) == iq.EINVAL
+    wb, yb, nb = _group_args([A, A * 2], [A * 4, A * 8], [8, 0])
+    assert g(wb, yb, nb, 2, A * 16, 4, 256, None) == iq.EINVAL
+    assert g(w, y, n, 2, A * 16, 4, 300, None) == iq.EINVAL
+    # an output overlapping another output, a weight matrix or X
+    wo, yo, no = _group_args([A, A * 2], [A * 4, A * 4 + 64], [8, 16])
+    assert g(wo, yo, no, 2, A * 16, 4, 256, None) == iq.EINVAL
+    wo, yo, no = _group_args([A, A * 2], [A * 4, A * 2], [8, 16])
+    assert g(wo, yo, no, 2, A * 16, 4, 256, None) == iq.EINVAL
+    assert g(w, y, n, 2, A * 8, 4, 256, None) == iq.EINVAL
+    assert "overlap" in L.iq4xs_last_error().decode()
+
+
+@pytest.mark.skipif(_has_gpu(), reason="checks the no-device error")
+def test_gemm_group_no_device():
+    w, y, n = _group_args([A, A * 2], [A * 4, A * 8], [8, 16])
+    assert L.iq4xs_gemm_group(w, y, n, 2, A * 16, 4, 256, None) == iq.EDEVICE
+
+
 def test_default_dispatch_table():
     iq.load_dispatch_table(None)
     seen = set()

@@ -383,6 +383,31 @@ def test_shared_tiles_match_oracle(M, N, K):
         assert np.array_equal(y, y5), "second call on the same workspace differs"
 
 
+# One X against several weight matrices (one quantization, one streaming
+# launch over the tiles of all of them): ragged sizes, a group with more tiles
+# than compute units (runs that cross from one matrix into the next, shared
+# tiles), and shapes that fall back to one call per matrix (M > 32, odd K/256).
+GROUP_CASES = [(1, (300, 520), 1024), (3, (256, 64, 96), 512), (8, (4100, 2050, 3000, 1000), 512),
+               (16, (2048, 2048), 2048), (32, (6200, 2100), 512), (40, (300, 200), 512),
+               (4, (257, 100), 1280)]
+
+
+@pytest.mark.parametrize("M,Ns,K", GROUP_CASES)
+def test_gemm_group_matches_oracle(M, Ns, K):
+    Ws = [synth.weights((903, N, K, g), N, K) for g, N in enumerate(Ns)]
+    X = synth.activations((904, M, K, 0), M, K)
+    Xq = O.quantize_q8_1(X)
+    Wd = [dev(W) for W in Ws]
+    Xd = dev(X)
+    outs = iq.gemm_group(Wd, Xd, [poisoned((M, N)) for N in Ns])
+    again = iq.gemm_group(Wd, Xd, [poisoned((M, N)) for N in Ns])
+    for g, (W, N) in enumerate(zip(Ws, Ns)):
+        y = outs[g].cpu().numpy()
+        assert np.all(np.isfinite(y)), f"matrix {g}: outputs not written"
+        assert_rows_close(y, O.gemm_q8_1(W, Xq, K), what=f"group matrix {g} M={M} N={N} K={K}")
+        assert np.array_equal(y, again[g].cpu().numpy()), f"matrix {g}: repeated call differs"
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 1024, 2048), (3, 520, 1280), (8, 2048, 2048), (40, 640, 4096),
                                    (4, 8224, 1024), (16, 10240, 512)])
 def test_graph_replays_match_eager(M, N, K):
