@@ -408,6 +408,55 @@ def test_gemm_group_matches_oracle(M, Ns, K):
         assert np.array_equal(y, again[g].cpu().numpy()), f"matrix {g}: repeated call differs"
 
 
+def test_gemm_group_graph_replays_match_eager():
+    """The grouped call recorded in a HIP graph (its scratch is stream-ordered):
+    every replay, with new inputs in between, equals the eager call."""
+    M, Ns, K = 8, (4100, 2050, 3000, 1000), 512
+    Ws = [dev(synth.weights((905, N, K, g), N, K)) for g, N in enumerate(Ns)]
+    Xd = dev(synth.activations((906, M, K, 0), M, K))
+    outs = [poisoned((M, N)) for N in Ns]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        iq.gemm_group(Ws, Xd, outs)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        iq.gemm_group(Ws, Xd, outs)
+    for rep in range(4):
+        Xd.copy_(dev(synth.activations((907, M, K, rep), M, K, sigma=1.0 + rep)))
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        want = iq.gemm_group(Ws, Xd)
+        for i in range(len(Ns)):
+            assert np.array_equal(outs[i].cpu().numpy(), want[i].cpu().numpy()), f"replay {rep} matrix {i}"
+
+
+def test_two_streams_at_once():
+    """Calls in flight on two streams at the same time share no state (scratch
+    is per call and stream-ordered): each equals its result run alone."""
+    cases = [(16, 10240, 512), (4, 8224, 1024), (64, 2048, 1024), (2, 1000, 2048)]
+    data = []
+    for i, (M, N, K) in enumerate(cases):
+        W, X = _inputs(M, N, K, seed=40 + i)
+        data.append((dev(W), dev(X), M, N, K))
+    alone = [iq.gemm(W, X).cpu().numpy() for W, X, *_ in data]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [poisoned((M, N)) for _, _, M, N, _ in data]
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for i, (W, X, M, N, K) in enumerate(data):
+            with torch.cuda.stream(streams[i % 2]):
+                iq.gemm(W, X, out=outs[i])
+        torch.cuda.synchronize()
+        for i in range(len(data)):
+            assert np.array_equal(outs[i].cpu().numpy(), alone[i]), f"case {cases[i]} on stream {i % 2}"
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 1024, 2048), (3, 520, 1280), (8, 2048, 2048), (40, 640, 4096),
                                    (4, 8224, 1024), (16, 10240, 512)])
 def test_graph_replays_match_eager(M, N, K):
