@@ -67,10 +67,15 @@ constexpr int wrow_bytes(int ch)
 }
 
 // LIVE result registers, activation rows padded to MPC (>= Mp) in LDS, CH
-// super-blocks per chunk, NBUF chunk buffers.
-template <int LIVE_, int MPC_, int CH_, int NBUF_>
+// super-blocks per chunk, NBUF chunk buffers.  SPLIT (M <= 4): the
+// activation rows go to MFMA rows 0..LIVE-1 and 4..4+LIVE-1, so that both
+// halves of a wavefront hold real rows in their LIVE result registers (row
+// h*LIVE + r in register r of half h): half the rescale work of putting all
+// rows in the first half.
+template <int LIVE_, int MPC_, int CH_, int NBUF_, bool SPLIT_ = false>
 struct Cfg {
     static constexpr int LIVE = LIVE_, MPC = MPC_, CH = CH_, NBUF = NBUF_;
+    static constexpr bool SPLIT = SPLIT_;
     static constexpr int WROW = wrow_bytes(CH);
     static constexpr int W_PR = CH * WBLK / 16;                               // pieces per row
     // one chunk buffer: weights [32][WROW] (padded to whole KB), activations
@@ -79,7 +84,7 @@ struct Cfg {
     // past the last sub-block's rows (activations: MA rows per sub-block in
     // LDS, MA >= M); besides the buffers, one 1 KB area that load slots
     // without a job fill (shared: nothing reads it)
-    static constexpr int MA = LIVE < 4 ? LIVE : MPC;
+    static constexpr int MA = SPLIT ? 2 * LIVE : LIVE < 4 ? LIVE : MPC;
     static constexpr int W_BYTES = round_up_c(TILE * WROW, 1024);
     static constexpr int A_OFF = W_BYTES, A_BYTES = CH * SUBS * MA * SB;
     static constexpr int D_OFF = A_OFF + A_BYTES, D_BYTES = round_up_c(CH * SUBS * MPC * 4, 1024);
@@ -104,6 +109,7 @@ struct Cfg {
     static_assert(WA + (JQ + JD + SLOTS - 1) / SLOTS <= NW, "load jobs fit the wavefronts");
     static_assert(CH % PAR == 0 && CH % 2 == 0, "every wavefront gets the same super-blocks");
     static_assert(NBUF >= 2 && TOTAL <= 160 * 1024, "LDS budget");
+    static_assert(!SPLIT || (LIVE <= 2 && MPC == 4), "split rows: M <= 4");
 };
 
 // Result register r of lane (col, h) holds row 8*(r/4) + 4*h + r%4.
@@ -262,7 +268,7 @@ k_mmv(MmvGroup grp, const int8_t *__restrict__ qp, int M, int K, int Mp, int nb,
             const int N = grp.n[gi];
             float *const Y = grp.y[gi];
             const int r = o >> 6, l2 = o & 63;
-            const int m = 8 * (r / 4) + 4 * (l2 >> 5) + (r % 4);
+            const int m = C::SPLIT ? (l2 >> 5) * LIVE + r : 8 * (r / 4) + 4 * (l2 >> 5) + (r % 4);
             const int n = (t - grp.t0[gi]) * TILE + (l2 & 31);
             if (part == GS - 1 && m < M && n < N) {
                 if (owned)
@@ -275,13 +281,15 @@ k_mmv(MmvGroup grp, const int8_t *__restrict__ qp, int M, int K, int Mp, int nb,
 
     // per-lane LDS read offsets inside a chunk buffer (rows >= M: the zero row)
     const int w_lane = col * C::WROW;
-    const int a_step = col < M ? C::MA * SB : 0;
+    // the activation row feeding this lane's MFMA row (M or more: the zero row)
+    const int arow = C::SPLIT ? ((col < 8 && (col & 3) < LIVE) ? ((col >> 2) & 1) * LIVE + (col & 3) : M) : col;
+    const int a_step = arow < M ? C::MA * SB : 0;
     int a_off[CH / PAR], d_off[CH / PAR];
 #pragma unroll
     for (int i = 0; i < CH / PAR; i++) {
         const int sb = (par + PAR * i) * SUBS + s;            // sub-block within the chunk
-        a_off[i] = (col < M ? C::A_OFF + col * SB : C::Z_OFF) + 16 * h + sb * a_step;
-        d_off[i] = C::D_OFF + 16 * h + 4 * sb * Mp;
+        a_off[i] = (arow < M ? C::A_OFF + arow * SB : C::Z_OFF) + 16 * h + sb * a_step;
+        d_off[i] = C::D_OFF + (C::SPLIT ? 4 * LIVE * h : 16 * h) + 4 * sb * Mp;
     }
     auto compute = [&](const Chunk &c, auto bc) __attribute__((always_inline)) {
         const char *B = C::template buf<decltype(bc)::value>();
@@ -314,7 +322,14 @@ k_mmv(MmvGroup grp, const int8_t *__restrict__ qp, int M, int K, int Mp, int nb,
                 ax[k] = *reinterpret_cast<const v4i *>(B + a_off[g + k]);
 #pragma unroll
                 for (int qd = 0; qd < DQ; qd++)
-                    dx[k][qd] = *reinterpret_cast<const float4 *>(B + d_off[g + k] + 32 * qd);
+                    if constexpr (!C::SPLIT)
+                        dx[k][qd] = *reinterpret_cast<const float4 *>(B + d_off[g + k] + 32 * qd);
+                    else if constexpr (LIVE == 1)
+                        dx[k][qd] = make_float4(*reinterpret_cast<const float *>(B + d_off[g + k]), 0.f, 0.f, 0.f);
+                    else {
+                        const float2 d2 = *reinterpret_cast<const float2 *>(B + d_off[g + k]);
+                        dx[k][qd] = make_float4(d2.x, d2.y, 0.f, 0.f);
+                    }
             }
             // (all of the group's reads are issued before any of them is used)
             __builtin_amdgcn_sched_barrier(0);
@@ -491,11 +506,13 @@ hipError_t launch_mmv_group(const MmvGroup &grp, const XPlanes &x, const MmvPlan
     if (!p.ok || grp.count < 1 || grp.count > MAXGRP)
         return hipErrorInvalidValue;
     switch (p.live) {
+    // (M = 2..4: rows split over both halves of the MFMA tile; measured 2-4%
+    // faster than all rows in the first half)
     case 1: return launch_c<Cfg<1, 4, 8, 3>>(grp, x, p, s);
-    case 2: return launch_c<Cfg<2, 4, 8, 3>>(grp, x, p, s);
-    case 3: return launch_c<Cfg<3, 4, 8, 3>>(grp, x, p, s);
+    case 2: return launch_c<Cfg<1, 4, 8, 3, true>>(grp, x, p, s);
+    case 3: return launch_c<Cfg<2, 4, 8, 3, true>>(grp, x, p, s);
     case 4:
-        return x.Mp <= 4 ? launch_c<Cfg<4, 4, 8, 3>>(grp, x, p, s) : launch_c<Cfg<4, 8, 4, 3>>(grp, x, p, s);
+        return x.Mp <= 4 ? launch_c<Cfg<2, 4, 8, 3, true>>(grp, x, p, s) : launch_c<Cfg<4, 8, 4, 3>>(grp, x, p, s);
     case 8: return launch_c<Cfg<8, 16, 4, 3>>(grp, x, p, s);
     case 16: return launch_c<Cfg<16, 32, 2, 3>>(grp, x, p, s);
     default: return hipErrorInvalidValue;
