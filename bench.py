@@ -586,8 +586,8 @@ def main():
     dom = max(per_m, key=lambda r: r["kernel_ms"])
     dom_kernel = kernel_name(dom["M"], N, K, iq.PATHS[dom["path"]])
     achieved = algo_bytes_kernel(dom["M"], N, K) / (dom["kernel_ms"] * 1e-3) / 1e9
-    label = {1: "1,4,8,3", 2: "1,4,8,3,true", 4: "2,4,8,3,true", 8: "4,8,4,3",
-             16: "8,16,4,3"}.get(dom["M"], "") if dom_kernel == "k_mmv" else ""
+    label = {1: "1,4,8,3,false", 2: "1,4,8,3,true", 4: "2,4,8,3,true", 8: "4,8,4,3,false",
+             16: "8,16,4,3,false"}.get(dom["M"], "") if dom_kernel == "k_mmv" else ""
     traffic = traffic_for(dom_kernel, label)
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS,
