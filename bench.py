@@ -18,8 +18,8 @@ Printed: one JSON line with
   roofline   for the dominant kernel (the matmul launch with the largest
              duration): algorithmic bytes per launch / its average duration,
              timed with HIP events on the stream the kernel runs on
-  group      one X against the MLP gate/up pair: the grouped call (one
-             quantization, one matmul launch) against two separate calls
+  group      one X against a pair of decode-shape matrices: the grouped call
+             (one quantization, one matmul launch) against two separate calls
   cpu_baseline  the CPU oracle (never tuned) on a bounded sample of the same
              sweep, in the same unit.
 `--sweep FILE` additionally times every (shape, M, path) point of the five
@@ -169,11 +169,14 @@ def measure_point(rot, X, N, K, path, reps=30):
 
 
 def measure_group(ms=(1, 8, 16), reps=20):
-    """One X against the MLP gate/up pair (two N=17408, K=5120 matrices): one
-    grouped call (one quantization, one matmul launch over both) against two
-    iq4xs_gemm calls; ms per pair from HIP events over back-to-back calls on
-    one stream, weight pairs rotated past the Infinity Cache."""
-    wl = synth.MLP_UP
+    """One X against two weight matrices of the decode shape (N=10240,
+    K=5120; e.g. two input projections of one layer): one grouped call (one
+    quantization, one matmul launch over both) against two iq4xs_gemm calls,
+    both with caller workspaces.  ms per pair on the device: `reps` pairs (each on another rotated weight
+    pair, past the Infinity Cache) recorded in one HIP graph and replayed, as
+    for the per-call times.  (The same shape as the decode sweep, so that a
+    kernel trace of the bench run averages one shape per kernel.)"""
+    wl = synth.DECODE_ATTN
     N, K = wl.shapes[0]
     base = torch.from_numpy(wl.w(N, K)).cuda()
     npairs = max(2, math.ceil((640 << 20) / (2 * base.numel())))
@@ -185,33 +188,44 @@ def measure_group(ms=(1, 8, 16), reps=20):
     for M in ms:
         X = torch.from_numpy(wl.x(M, K, N=N)).cuda()
         Y = [torch.empty((M, N), dtype=torch.float32, device="cuda") for _ in range(2)]
-        it = [0]
+        # caller workspaces on both sides: nothing is allocated inside the calls
+        gws = torch.empty(iq.group_workspace_bytes([N, N], M, K), dtype=torch.uint8, device="cuda")
+        sws = torch.empty(iq.workspace_bytes(M, N, K), dtype=torch.uint8, device="cuda")
 
-        def nxt():
-            it[0] += 1
-            return pairs[it[0] % npairs]
+        def grouped(i):
+            a, b = pairs[i % npairs]
+            iq.gemm_group([a, b], X, Y, workspace=gws)
 
-        def grouped():
-            a, b = nxt()
-            iq.gemm_group([a, b], X, Y)
+        def separate(i):
+            a, b = pairs[i % npairs]
+            iq.gemm(a, X, out=Y[0], workspace=sws)
+            iq.gemm(b, X, out=Y[1], workspace=sws)
 
-        def separate():
-            a, b = nxt()
-            iq.gemm(a, X, out=Y[0])
-            iq.gemm(b, X, out=Y[1])
-
-        for f in (grouped, separate):
-            for _ in range(3):
-                f()
-        tg = time_events(grouped, reps, stream)
-        ts = time_events(separate, reps, stream)
-        points.append({"M": M, "grouped_ms": tg, "separate_ms": ts, "speedup": ts / tg,
-                       "grouped_weight_GBs": wb / (tg * 1e-3) / 1e9,
-                       "grouped_hbm_frac": (wb + (4 + 2.25) * M * K + 8 * M * N) / (tg * 1e-3) / 1e9 / HBM_PEAK_GBS})
+        t = {}
+        for name, f in (("grouped", grouped), ("separate", separate)):
+            side = torch.cuda.Stream()
+            side.wait_stream(stream)
+            with torch.cuda.stream(side):
+                for i in range(3):
+                    f(i)
+            stream.wait_stream(side)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(reps):
+                    f(i)
+            g.replay()
+            t[name] = time_events(g.replay, 3, stream) / reps
+            del g
+        points.append({"M": M, "grouped_ms": t["grouped"], "separate_ms": t["separate"],
+                       "speedup": t["separate"] / t["grouped"],
+                       "grouped_weight_GBs": wb / (t["grouped"] * 1e-3) / 1e9,
+                       "grouped_hbm_frac": (wb + (4 + 2.25) * M * K + 8 * M * N) / (t["grouped"] * 1e-3) / 1e9
+                       / HBM_PEAK_GBS})
     del pairs
     torch.cuda.empty_cache()
-    return {"workload": "MLP gate/up pair, two matrices N=17408 K=5120 sharing X, quantize included",
-            "points": points}
+    return {"workload": "pair of N=10240 K=5120 matrices sharing X (grouped call vs two calls), "
+                        "quantize included, graph replay", "points": points}
 
 
 def point_record(N, K, M, path, t_call, t_kern, t_eager=None):

@@ -153,11 +153,15 @@ int iq4xs_gemm_act(const void *W, const void *act, float *Y, int64_t M, int64_t 
  * any W[h] or another Y[h].  Other shapes run one iq4xs_gemm per matrix.
  * Every output is within the same bound of the oracle as iq4xs_gemm; where a
  * tile's K range is split between workgroups at other points than in a
- * single-matrix call, the last bits can differ from that call's.  Scratch
- * comes from the device's default pool, stream-ordered. */
+ * single-matrix call, the last bits can differ from that call's.  Scratch:
+ * `workspace` (256-byte aligned, at least iq4xs_gemm_group_workspace_bytes
+ * bytes, overlapping no input or output; then nothing is allocated and the
+ * call can be captured in a graph), or NULL for stream-ordered scratch from
+ * the device's default pool. */
 #define IQ4XS_MAX_GROUP 4
+int iq4xs_gemm_group_workspace_bytes(const int64_t *N, int G, int64_t M, int64_t K, size_t *out);
 int iq4xs_gemm_group(const void *const *W, float *const *Y, const int64_t *N, int G, const float *X,
-                     int64_t M, int64_t K, void *stream);
+                     int64_t M, int64_t K, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Dequantize W [N][K] to bf16 Wb [N][K] (row-major): each weight
  * d*(ls-32)*kvalues[index], computed exactly in fp32, rounded to the nearest

@@ -32,7 +32,8 @@ Y_ZEROED = 0x100     # gemm_act hint: Y already holds zeros
 EXPORTS = ("iq4xs_weight_bytes", "iq4xs_q8_1_bytes", "iq4xs_init", "iq4xs_quantize_q8_1",
            "iq4xs_gemm", "iq4xs_gemm_path", "iq4xs_gemm_workspace_bytes", "iq4xs_gemm_ws",
            "iq4xs_gemm_q8_1", "iq4xs_act_bytes",
-           "iq4xs_prepare_act", "iq4xs_gemm_act", "iq4xs_gemm_group", "iq4xs_dequantize_bf16",
+           "iq4xs_prepare_act", "iq4xs_gemm_act", "iq4xs_gemm_group_workspace_bytes", "iq4xs_gemm_group",
+           "iq4xs_dequantize_bf16",
            "iq4xs_dispatch", "iq4xs_load_dispatch_table", "iq4xs_path_name", "iq4xs_last_error")
 
 
@@ -61,7 +62,9 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "iq4xs_act_bytes": [i64, i64, sz],
         "iq4xs_prepare_act": [p, p, i64, i64, p],
         "iq4xs_gemm_act": [p, p, p, i64, i64, i64, i32, p],
-        "iq4xs_gemm_group": [ctypes.POINTER(p), ctypes.POINTER(p), ctypes.POINTER(i64), i32, p, i64, i64, p],
+        "iq4xs_gemm_group_workspace_bytes": [ctypes.POINTER(i64), i32, i64, i64, sz],
+        "iq4xs_gemm_group": [ctypes.POINTER(p), ctypes.POINTER(p), ctypes.POINTER(i64), i32, p, i64, i64, p,
+                             ctypes.c_size_t, p],
         "iq4xs_dequantize_bf16": [p, p, i64, i64, p],
         "iq4xs_dispatch": [i64, i64, i64, ctypes.POINTER(ctypes.c_int)],
         "iq4xs_load_dispatch_table": [ctypes.c_char_p],
@@ -218,10 +221,19 @@ def gemm_act(W: torch.Tensor, act: torch.Tensor, M: int, K: int, path: int = PAT
 MAX_GROUP = 4     # IQ4XS_MAX_GROUP
 
 
-def gemm_group(Ws: list, X: torch.Tensor, outs: list | None = None) -> list:
+def group_workspace_bytes(Ns: list, M: int, K: int) -> int:
+    n = (ctypes.c_int64 * max(len(Ns), 1))(*Ns)
+    out = ctypes.c_size_t()
+    check(_L().iq4xs_gemm_group_workspace_bytes(n, len(Ns), M, K, ctypes.byref(out)))
+    return out.value
+
+
+def gemm_group(Ws: list, X: torch.Tensor, outs: list | None = None,
+               workspace: torch.Tensor | None = None) -> list:
     """Y[g] = X * Ws[g]^T for every weight matrix of the group (same K): X is
     quantized once and, where the shapes allow, one matmul launch covers all
-    of them."""
+    of them.  With `workspace` (uint8, group_workspace_bytes(...) bytes)
+    nothing is allocated inside the call."""
     M, K = X.shape
     G = len(Ws)
     if outs is None:
@@ -232,7 +244,9 @@ def gemm_group(Ws: list, X: torch.Tensor, outs: list | None = None) -> list:
     y = (ctypes.c_void_p * max(G, 1))(*[_dev(o, torch.float32, "Y") for o in outs])
     n = (ctypes.c_int64 * max(G, 1))(*[W.shape[0] for W in Ws])
     with _on(X):
-        check(_L().iq4xs_gemm_group(w, y, n, G, _dev(X, torch.float32, "X"), M, K, _stream(X)))
+        ws = _dev(workspace, torch.uint8, "workspace") if workspace is not None else None
+        wsb = workspace.numel() if workspace is not None else 0
+        check(_L().iq4xs_gemm_group(w, y, n, G, _dev(X, torch.float32, "X"), M, K, ws, wsb, _stream(X)))
     return outs
 
 

@@ -517,8 +517,55 @@ int iq4xs_gemm_act(const void *W, const void *act, float *Y, int64_t M, int64_t 
 
 static_assert(IQ4XS_MAX_GROUP == MAXGRP, "group bound of the header and the kernels");
 
+// Scratch of a grouped call: the activation planes of the one-launch path,
+// or the largest per-matrix need of the one-call-per-matrix path.
+static int group_need(const int64_t *N, int G, int64_t M, int64_t K, bool *one_launch, size_t *need)
+{
+    const MmvPlan p = tune_override().mmv != 0 ? mmv_plan_group(M, N, G, K, device_cus()) : MmvPlan();
+    *one_launch = p.ok;
+    if (p.ok) {
+        *need = xplanes_bytes(M, K);
+        return IQ4XS_OK;
+    }
+    size_t most = 0;
+    for (int g = 0; g < G; g++) {
+        int path = IQ4XS_PATH_AUTO;
+        const int st = resolve_path(path, M, N[g], K, &path);
+        if (st != IQ4XS_OK)
+            return st;
+        most = std::max(most, workspace_need(path, M, N[g], K));
+    }
+    *need = most;
+    return IQ4XS_OK;
+}
+
+static int check_group_sizes(const int64_t *N, int G, int64_t M, int64_t K)
+{
+    if (!N)
+        return fail(IQ4XS_EINVAL, "null pointer");
+    if (G < 1 || G > IQ4XS_MAX_GROUP)
+        return fail(IQ4XS_EINVAL, "group of %d matrices (1..%d)", G, IQ4XS_MAX_GROUP);
+    for (int g = 0; g < G; g++) {
+        const int st = check_dims(M, N[g], K);
+        if (st != IQ4XS_OK)
+            return st;
+    }
+    return IQ4XS_OK;
+}
+
+int iq4xs_gemm_group_workspace_bytes(const int64_t *N, int G, int64_t M, int64_t K, size_t *out)
+{
+    if (!out)
+        return fail(IQ4XS_EINVAL, "null output pointer");
+    int st = check_group_sizes(N, G, M, K);
+    if (st != IQ4XS_OK)
+        return st;
+    bool one = false;
+    return group_need(N, G, M, K, &one, out);
+}
+
 int iq4xs_gemm_group(const void *const *W, float *const *Y, const int64_t *N, int G, const float *X,
-                     int64_t M, int64_t K, void *stream)
+                     int64_t M, int64_t K, void *workspace, size_t workspace_bytes, void *stream)
 {
     if (!W || !Y || !N || !X)
         return fail(IQ4XS_EINVAL, "null pointer");
@@ -544,28 +591,48 @@ int iq4xs_gemm_group(const void *const *W, float *const *Y, const int64_t *N, in
                 (h != g && overlaps(Y[g], yb, Y[h], (size_t)(M * N[h] * 4))))
                 return fail(IQ4XS_EINVAL, "Y of matrix %d overlaps a weight matrix or another output", g);
     }
+    if (workspace != nullptr) {
+        if (!aligned(workspace, 256))
+            return fail(IQ4XS_EALIGN, "workspace must be 256-byte aligned");
+        if (overlaps(workspace, workspace_bytes, X, (size_t)(M * K * 4)))
+            return fail(IQ4XS_EINVAL, "workspace overlaps X");
+        for (int g = 0; g < G; g++)
+            if (overlaps(workspace, workspace_bytes, Y[g], (size_t)(M * N[g] * 4)) ||
+                overlaps(workspace, workspace_bytes, W[g], (size_t)(N[g] * (K / QK) * WBLK)))
+                return fail(IQ4XS_EINVAL, "workspace overlaps W or Y (matrix %d)", g);
+    }
     ensure_init();
     int st = check_device();
     if (st != IQ4XS_OK)
         return st;
     const hipStream_t s = (hipStream_t)stream;
-    const MmvPlan p = tune_override().mmv != 0 ? mmv_plan_group(M, N, G, K, device_cus()) : MmvPlan();
-    if (!p.ok) {
+    bool one_launch = false;
+    size_t need = 0;
+    if ((st = group_need(N, G, M, K, &one_launch, &need)) != IQ4XS_OK)
+        return st;
+    if (workspace != nullptr && workspace_bytes < need)
+        return fail(IQ4XS_EINVAL, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    if (!one_launch) {
         // shapes the streaming kernel does not take: one call per matrix
         for (int g = 0; g < G; g++)
-            if ((st = run_gemm(W[g], X, nullptr, Y[g], M, N[g], K, IQ4XS_PATH_AUTO, nullptr, 0, s)) != IQ4XS_OK)
+            if ((st = run_gemm(W[g], X, nullptr, Y[g], M, N[g], K, IQ4XS_PATH_AUTO, workspace,
+                               workspace_bytes, s)) != IQ4XS_OK)
                 return st;
         return IQ4XS_OK;
     }
+    const MmvPlan p = mmv_plan_group(M, N, G, K, device_cus());
     Scratch scr;
     scr.s = s;
-    const size_t need = xplanes_bytes(M, K);
-    if (hipMallocAsync(&scr.p, need, s) != hipSuccess) {
-        (void)hipGetLastError();
-        scr.p = nullptr;
-        return fail(IQ4XS_ENOMEM, "scratch of %zu bytes", need);
+    void *base = workspace;
+    if (base == nullptr) {
+        if (hipMallocAsync(&scr.p, need, s) != hipSuccess) {
+            (void)hipGetLastError();
+            scr.p = nullptr;
+            return fail(IQ4XS_ENOMEM, "scratch of %zu bytes", need);
+        }
+        base = scr.p;
     }
-    const XPlanes xp = xplanes_at(scr.p, M, K);
+    const XPlanes xp = xplanes_at(base, M, K);
     ZeroList zl;
     if (p.zero_y) {
         zl.count = G;

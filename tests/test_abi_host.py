@@ -139,32 +139,39 @@ def _group_args(ws, ys, ns):
 def test_gemm_group_validation():
     g = L.iq4xs_gemm_group
     w, y, n = _group_args([A, A * 2], [A * 4, A * 8], [8, 16])
-    assert g(None, y, n, 2, A * 16, 4, 256, None) == iq.EINVAL
-    assert g(w, y, n, 2, None, 4, 256, None) == iq.EINVAL
-    assert g(w, y, n, 0, A * 16, 4, 256, None) == iq.EINVAL
+    assert g(None, y, n, 2, A * 16, 4, 256, None, 0, None) == iq.EINVAL
+    assert g(w, y, n, 2, None, 4, 256, None, 0, None) == iq.EINVAL
+    assert g(w, y, n, 0, A * 16, 4, 256, None, 0, None) == iq.EINVAL
     w5, y5, n5 = _group_args([A] * 5, [A * 4] * 5, [8] * 5)
-    assert g(w5, y5, n5, 5, A * 16, 4, 256, None) == iq.EINVAL
-    assert g(w, y, n, 2, A * 16 + 4, 4, 256, None) == iq.EALIGN
+    assert g(w5, y5, n5, 5, A * 16, 4, 256, None, 0, None) == iq.EINVAL
+    assert g(w, y, n, 2, A * 16 + 4, 4, 256, None, 0, None) == iq.EALIGN
     wa, ya, na = _group_args([A, A * 2 + 8], [A * 4, A * 8], [8, 16])
-    assert g(wa, ya, na, 2, A * 16, 4, 256, None) == iq.EALIGN
+    assert g(wa, ya, na, 2, A * 16, 4, 256, None, 0, None) == iq.EALIGN
     wz, yz, nz = _group_args([A, None], [A * 4, A * 8], [8, 16])
-    assert g(wz, yz, nz, 2, A * 16, 4, 256, None) == iq.EINVAL
+    assert g(wz, yz, nz, 2, A * 16, 4, 256, None, 0, None) == iq.EINVAL
     wb, yb, nb = _group_args([A, A * 2], [A * 4, A * 8], [8, 0])
-    assert g(wb, yb, nb, 2, A * 16, 4, 256, None) == iq.EINVAL
-    assert g(w, y, n, 2, A * 16, 4, 300, None) == iq.EINVAL
+    assert g(wb, yb, nb, 2, A * 16, 4, 256, None, 0, None) == iq.EINVAL
+    assert g(w, y, n, 2, A * 16, 4, 300, None, 0, None) == iq.EINVAL
     # an output overlapping another output, a weight matrix or X
     wo, yo, no = _group_args([A, A * 2], [A * 4, A * 4 + 64], [8, 16])
-    assert g(wo, yo, no, 2, A * 16, 4, 256, None) == iq.EINVAL
+    assert g(wo, yo, no, 2, A * 16, 4, 256, None, 0, None) == iq.EINVAL
     wo, yo, no = _group_args([A, A * 2], [A * 4, A * 2], [8, 16])
-    assert g(wo, yo, no, 2, A * 16, 4, 256, None) == iq.EINVAL
-    assert g(w, y, n, 2, A * 8, 4, 256, None) == iq.EINVAL
+    assert g(wo, yo, no, 2, A * 16, 4, 256, None, 0, None) == iq.EINVAL
+    assert g(w, y, n, 2, A * 8, 4, 256, None, 0, None) == iq.EINVAL
     assert "overlap" in L.iq4xs_last_error().decode()
+    # caller workspace: aligned, and overlapping nothing
+    assert g(w, y, n, 2, A * 16, 4, 256, A * 64 + 16, 1 << 20, None) == iq.EALIGN
+    assert g(w, y, n, 2, A * 16, 4, 256, A * 4, 1 << 20, None) == iq.EINVAL
+    size = ctypes.c_size_t()
+    assert L.iq4xs_gemm_group_workspace_bytes(n, 0, 4, 256, ctypes.byref(size)) == iq.EINVAL
+    assert L.iq4xs_gemm_group_workspace_bytes(n, 2, 4, 300, ctypes.byref(size)) == iq.EINVAL
+    assert L.iq4xs_gemm_group_workspace_bytes(n, 2, 4, 256, None) == iq.EINVAL
 
 
 @pytest.mark.skipif(_has_gpu(), reason="checks the no-device error")
 def test_gemm_group_no_device():
     w, y, n = _group_args([A, A * 2], [A * 4, A * 8], [8, 16])
-    assert L.iq4xs_gemm_group(w, y, n, 2, A * 16, 4, 256, None) == iq.EDEVICE
+    assert L.iq4xs_gemm_group(w, y, n, 2, A * 16, 4, 256, None, 0, None) == iq.EDEVICE
 
 
 def test_default_dispatch_table():

@@ -401,11 +401,15 @@ def test_gemm_group_matches_oracle(M, Ns, K):
     Xd = dev(X)
     outs = iq.gemm_group(Wd, Xd, [poisoned((M, N)) for N in Ns])
     again = iq.gemm_group(Wd, Xd, [poisoned((M, N)) for N in Ns])
+    # caller workspace with arbitrary contents: nothing allocated, same result
+    ws = torch.randint(0, 256, (iq.group_workspace_bytes(list(Ns), M, K),), dtype=torch.uint8).cuda()
+    with_ws = iq.gemm_group(Wd, Xd, [poisoned((M, N)) for N in Ns], workspace=ws)
     for g, (W, N) in enumerate(zip(Ws, Ns)):
         y = outs[g].cpu().numpy()
         assert np.all(np.isfinite(y)), f"matrix {g}: outputs not written"
         assert_rows_close(y, O.gemm_q8_1(W, Xq, K), what=f"group matrix {g} M={M} N={N} K={K}")
         assert np.array_equal(y, again[g].cpu().numpy()), f"matrix {g}: repeated call differs"
+        assert np.array_equal(y, with_ws[g].cpu().numpy()), f"matrix {g}: call with a workspace differs"
 
 
 def test_gemm_group_graph_replays_match_eager():
@@ -415,15 +419,16 @@ def test_gemm_group_graph_replays_match_eager():
     Ws = [dev(synth.weights((905, N, K, g), N, K)) for g, N in enumerate(Ns)]
     Xd = dev(synth.activations((906, M, K, 0), M, K))
     outs = [poisoned((M, N)) for N in Ns]
+    ws = torch.empty(iq.group_workspace_bytes(list(Ns), M, K), dtype=torch.uint8, device="cuda")
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        iq.gemm_group(Ws, Xd, outs)
+        iq.gemm_group(Ws, Xd, outs, workspace=ws)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        iq.gemm_group(Ws, Xd, outs)
+        iq.gemm_group(Ws, Xd, outs, workspace=ws)
     for rep in range(4):
         Xd.copy_(dev(synth.activations((907, M, K, rep), M, K, sigma=1.0 + rep)))
         for o in outs:
