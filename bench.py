@@ -388,6 +388,77 @@ def summarize_pmc(fetch_dir, write_dir, out, cmd_fetch, cmd_write):
     print("\n".join(lines))
 
 
+SQ_PASSES = (("SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU",
+              "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES"),
+             ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_LDS_BANK_CONFLICT",
+              "SQ_WAIT_INST_LDS", "SQ_WAIT_ANY", "SQ_ACTIVE_INST_ANY"))
+
+
+def _sq_key(name, order, shapes):
+    """Kernel label; the tile kernel's launches of a --profile-shapes run
+    (20 per shape, in order) also carry their shape."""
+    key = name.replace("void ", "").replace("iq4xs::(anonymous namespace)::", "").split("(")[0]
+    if shapes and "k_mmqt<" in key and order is not None:
+        i = order // 20
+        if i < len(shapes):
+            key += " [M=%d N=%d K=%d]" % shapes[i]
+    return key
+
+
+def _tile_order(rows, id_field):
+    """Launch index of every tile-kernel dispatch (not the summing kernel)."""
+    ids = sorted({int(r[id_field]) for r in rows if "k_mmqt<" in r["Kernel_Name"]})
+    return {i: n for n, i in enumerate(ids)}
+
+
+def summarize_sq(dirs, trace_dirs, out, cmds, specs=""):
+    """Per matmul kernel (by template arguments, and shape for the tile
+    kernel): the average per dispatch of the SQ counters of the given runs;
+    VALU instructions per MFMA instruction, LDS bank-conflict cycles per LDS
+    instruction; and, with kernel traces of the same launches, the share of
+    the kernel's duration that VALU issue (instructions x 4 cycles, spread
+    over 1024 SIMDs at 2.4 GHz) and the matrix cores (busy cycles over 1024
+    SIMDs) take."""
+    shapes = [tuple(int(v) for v in sp.split("x")) for sp in specs.split(",")] if specs else []
+    per = {}
+    for d in dirs:
+        rows = _counter_rows(d)
+        order = _tile_order(rows, "Dispatch_Id")
+        for r in rows:
+            name = r["Kernel_Name"]
+            if not any(k in name for k in ("k_mmv", "k_gemv", "k_mmqt", "k_mmq", "k_quantize")):
+                continue
+            key = _sq_key(name, order.get(int(r["Dispatch_Id"])), shapes)
+            per.setdefault(key, {}).setdefault(r["Counter_Name"], {}).setdefault(r["Dispatch_Id"], 0.0)
+            per[key][r["Counter_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    dur = {}
+    for td in trace_dirs:
+        files = glob.glob(os.path.join(td, "**", "*kernel_trace.csv"), recursive=True)
+        rows = list(csv.DictReader(open(files[0])))
+        order = _tile_order(rows, "Dispatch_Id")
+        for r in rows:
+            key = _sq_key(r["Kernel_Name"], order.get(int(r["Dispatch_Id"])), shapes)
+            dur.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+    lines = ["# SQ counters per dispatch (averages), matmul and quantize kernels of the decode sweep and the tile shapes",
+             *[f"# run: {c}" for c in cmds],
+             "# VALU/MFMA: instructions; LDS-conflict: bank-conflict cycles per LDS instruction; VALU-issue and "
+             "MFMA-busy: per SIMD, as a share of the kernel's average duration in the trace",
+             "# kernel | " + " ".join(c for p_ in SQ_PASSES for c in p_) +
+             " | VALU/MFMA  LDS-conflict  trace-us  VALU-issue  MFMA-busy"]
+    for key in sorted(per):
+        v = {c: sum(d.values()) / len(d) for c, d in per[key].items()}
+        vals = " ".join(f"{v.get(c, float('nan')):.4g}" for p_ in SQ_PASSES for c in p_)
+        valu, mfma = v.get("SQ_INSTS_VALU", 0.0), v.get("SQ_INSTS_MFMA", 0.0)
+        lds, conf = v.get("SQ_INSTS_LDS", 0.0), v.get("SQ_LDS_BANK_CONFLICT", 0.0)
+        d_us = sum(dur[key]) / len(dur[key]) if key in dur else float("nan")
+        issue = valu * 4 / 1024 / 2.4e3 / d_us
+        busy = v.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / 1024 / 2.4e3 / d_us
+        lines.append(f"{key} | {vals} | {valu / mfma if mfma else float('nan'):.2f}  "
+                     f"{conf / lds if lds else float('nan'):.3f}  {d_us:.2f}  {issue:.2f}  {busy:.2f}")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def summarize_trace(trace_dir, out, cmd, title):
     """The kernel-trace statistics of a rocprofv3 --stats run as a short text
     table (kernel, calls, average / min / max microseconds, share of GPU
@@ -511,6 +582,9 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR")
     ap.add_argument("--summarize-pmc-shapes", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "SHAPES"))
+    ap.add_argument("--summarize-sq", nargs="+", metavar="DIR", help="SQ counter runs -> instruction mix")
+    ap.add_argument("--trace-dir", default=None, help="kernel-trace runs of the same launches, comma-separated")
+    ap.add_argument("--shapes", default="", help="MxNxK,... of the --profile-shapes runs")
     ap.add_argument("--cmd", default="")
     ap.add_argument("--title", default="")
     ap.add_argument("--out", default=TRAFFIC_FILE)
@@ -525,6 +599,12 @@ def main():
             raise SystemExit("--summarize-pmc-shapes needs its own --out")
         summarize_pmc_shapes(*args.summarize_pmc_shapes[:2], args.out, args.cmd_fetch, args.cmd_write,
                              args.summarize_pmc_shapes[2])
+        return
+    if args.summarize_sq:
+        if args.out == TRAFFIC_FILE:
+            raise SystemExit("--summarize-sq needs its own --out")
+        summarize_sq(args.summarize_sq, [d for d in (args.trace_dir or "").split(",") if d], args.out,
+                     [c for c in args.cmd.split(";;") if c], args.shapes)
         return
     if args.summarize_trace:
         if args.out == TRAFFIC_FILE:
