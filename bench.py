@@ -18,6 +18,8 @@ Printed: one JSON line with
   roofline   for the dominant kernel (the matmul launch with the largest
              duration): algorithmic bytes per launch / its average duration,
              timed with HIP events on the stream the kernel runs on
+  t_m2_over_m1  per-call time at M=2 over M=1 (flat in M is the aim)
+  read_probe what a plain 1 GiB read achieves here (torch.sum), beside 8 TB/s
   group      one X against a pair of decode-shape matrices: the grouped call
              (one quantization, one matmul launch) against two separate calls
   cpu_baseline  the CPU oracle (never tuned) on a bounded sample of the same
@@ -226,6 +228,21 @@ def measure_group(ms=(1, 8, 16), reps=20):
     torch.cuda.empty_cache()
     return {"workload": "pair of N=10240 K=5120 matrices sharing X (grouped call vs two calls), "
                         "quantize included, graph replay", "points": points}
+
+
+def read_probe(nbytes=1 << 30, reps=10):
+    """What a plain read of nbytes achieves on this device (torch.sum over a
+    fresh fp32 buffer, so the Infinity Cache holds at most a quarter of it):
+    a reference beside the published 8 TB/s, not a kernel of this library."""
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    y = torch.ones_like(x)
+    stream = torch.cuda.current_stream()
+    for _ in range(2):
+        x.sum()
+    t = time_events(lambda: (x.sum(), y.sum()), reps, stream) / 2
+    del x, y
+    torch.cuda.empty_cache()
+    return {"bytes": nbytes, "ms": t, "GBs": nbytes / (t * 1e-3) / 1e9, "kernel": "torch.sum (fp32, 1 GiB)"}
 
 
 def point_record(N, K, M, path, t_call, t_kern, t_eager=None):
@@ -701,7 +718,11 @@ def main():
            "wall_s": wall, "graph_ms_per_step": graph_ms,
            "graph_weight_GBs": wbytes / (graph_ms * 1e-3) / 1e9, "per_m": per_m, "roofline": roofline}
     del graphs
+    by_m = {r["M"]: r for r in per_m}
+    if 1 in by_m and 2 in by_m:
+        out["t_m2_over_m1"] = by_m[2]["ms"] / by_m[1]["ms"]
     out["group"] = measure_group()
+    out["read_probe"] = read_probe()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, N, K, ms)
     if args.sweep:
