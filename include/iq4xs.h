@@ -106,7 +106,7 @@ int iq4xs_gemm_path(const void *W, const float *X, float *Y, int64_t M, int64_t 
 /* Caller-provided scratch: iq4xs_gemm_ws is iq4xs_gemm_path with the
  * scratch supplied by the caller (`workspace`, at least
  * iq4xs_gemm_workspace_bytes(M, N, K, path) bytes, 256-byte aligned, not
- * overlapping W or Y).  It allocates nothing, so it can be recorded into a
+ * overlapping W, X or Y: IQ4XS_EINVAL).  It allocates nothing, so it can be recorded into a
  * HIP graph; calls that share one workspace must be ordered on one stream.
  * The size query resolves AUTO with the dispatch table in force. */
 int iq4xs_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int path, size_t *out);

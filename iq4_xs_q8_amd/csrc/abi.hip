@@ -278,8 +278,10 @@ int run_gemm(const void *W, const float *X, const void *Xq, float *Y, int64_t M,
         if (ws_bytes < need)
             return fail(IQ4XS_EINVAL, "workspace of %zu bytes, %zu needed", ws_bytes, need);
         if (overlaps(ws, ws_bytes, Y, (size_t)(M * N * 4)) ||
-            overlaps(ws, ws_bytes, W, (size_t)(N * (K / QK) * WBLK)))
-            return fail(IQ4XS_EINVAL, "workspace overlaps W or Y");
+            overlaps(ws, ws_bytes, W, (size_t)(N * (K / QK) * WBLK)) ||
+            (X && overlaps(ws, ws_bytes, X, (size_t)(M * K * 4))) ||
+            (Xq && overlaps(ws, ws_bytes, Xq, (size_t)(M * (K / SB) * XBLK))))
+            return fail(IQ4XS_EINVAL, "workspace overlaps W, X or Y");
     }
     if ((st = check_device()) != IQ4XS_OK)
         return st;

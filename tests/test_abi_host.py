@@ -117,6 +117,10 @@ def test_workspace_query_and_checks():
     assert L.iq4xs_gemm_ws(A, A * 2, A * 4, 4, 8, 256, iq.PATH_MMQ, WS, need - 1, None) == iq.EINVAL
     assert L.iq4xs_gemm_ws(A, A * 2, A * 4, 4, 8, 256, iq.PATH_MMQ, WS + 16, need, None) == iq.EALIGN
     assert L.iq4xs_gemm_ws(A, A * 2, A * 4, 4, 8, 256, iq.PATH_MMQ, A * 4 - 256, need, None) == iq.EINVAL
+    # the workspace must not overlap X either (the quantizer reads X while it
+    # writes the activation planes into the workspace)
+    assert L.iq4xs_gemm_ws(A, A * 2, A * 4, 4, 8, 256, iq.PATH_MMQ, A * 2 + 256, need, None) == iq.EINVAL
+    assert "workspace overlaps" in L.iq4xs_last_error().decode()
     assert L.iq4xs_gemm_ws(A, A * 2, A * 4, 5, 8, 256, iq.PATH_GEMV, WS, need, None) == iq.EPATH
     assert L.iq4xs_gemm_ws(A, A * 2, A * 4 + 4, 4, 8, 256, iq.PATH_MMQ, WS, need, None) == iq.EALIGN
 
