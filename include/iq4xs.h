@@ -75,8 +75,13 @@ extern "C" {
                                  rounds W~ and X~ to 8 significant bits)                 */
 #define IQ4XS_NUM_PATHS 4
 
-/* Sizes in bytes of an IQ4_XS matrix [N][K] and of a Q8_1 matrix [M][K].
- * EINVAL for non-positive sizes, K % 256 != 0 (K % 32 for Q8_1), overflow. */
+/* Sizes in bytes of an IQ4_XS matrix [N][K] and of a Q8_1 matrix [M][K]:
+ * N*(K/256)*136 and M*(K/32)*36.  The "V100TPS engine log", section on the
+ * batched IQ4_XS kernel, names both formats and the 32-weight sub-block with
+ * its own scale d*(ls-32); the byte counts per block are the GGUF formats'
+ * (the pages print none).  *out is written only on success.  EINVAL for a
+ * null `out`, non-positive sizes, K % 256 != 0 (K % 32 for Q8_1), overflow.
+ * Host-only: no HIP call. */
 int iq4xs_weight_bytes(int64_t N, int64_t K, size_t *out);
 int iq4xs_q8_1_bytes(int64_t M, int64_t K, size_t *out);
 
@@ -113,7 +118,13 @@ int iq4xs_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int path, size_t
 int iq4xs_gemm_ws(const void *W, const float *X, float *Y, int64_t M, int64_t N, int64_t K, int path,
                   void *workspace, size_t workspace_bytes, void *stream);
 
-/* Y = dequant(Xq) * W^T from an already-quantized Q8_1 Xq (layout above). */
+/* Y = X * W^T from activations already quantized to Q8_1 (Xq [M][K/32]
+ * blocks of 36 bytes, layout above; caller-owned, 4-byte aligned, read only).
+ * The "V100TPS engine log", M=64 kernel-launch table, shows quantize_q8_1 as
+ * a launch of its own ahead of the matmul: this entry point is that matmul
+ * on its own, on the same path choice as iq4xs_gemm_path.  Y is overwritten;
+ * the result equals iq4xs_gemm_path's on the X that Xq quantizes.  Errors as
+ * iq4xs_gemm_path (EALIGN for Xq not 4-byte aligned). */
 int iq4xs_gemm_q8_1(const void *W, const void *Xq, float *Y, int64_t M, int64_t N, int64_t K,
                     int path, void *stream);
 
@@ -175,18 +186,30 @@ int iq4xs_dequantize_bf16(const void *W, void *Wb, int64_t N, int64_t K, void *s
 int iq4xs_dispatch(int64_t M, int64_t N, int64_t K, int *path_out);
 
 /* Replace the dispatch table with the one in `path` (NULL: the built-in
- * default).  On ETABLE the previous table stays in force.  Format: text lines
+ * default).  "V100TPS engine log", mmvq vs dequant+GEMM table: the measured
+ * crossover sat near M = 15 while the dispatcher's hard-coded threshold was 8;
+ * here the bands are data measured on the device they name, and a table that
+ * cannot be read or parsed is refused as a whole (ETABLE; the previous table
+ * stays in force).  `path` is a host file path, read once during the call.
+ * Format: text lines
  *   arch <gfx name>
+ *   cus <compute units>        (optional: the device the bands were measured on)
  *   band <GEMV|MMQ|DEQ_BF16> <M_lo> <M_hi> <N> <K>
  * where N and K are "*" (any), a value, or an inclusive range "lo-hi";
  * '#' starts a comment; the first band that matches (M, N, K) wins; DEQ_BF16
- * bands are skipped unless IQ4XS_ALLOW_BF16=1 was set at initialisation. */
+ * bands are skipped unless IQ4XS_ALLOW_BF16=1 was set at initialisation.
+ * With a `cus` line, a call that asks for IQ4XS_PATH_AUTO on a device with
+ * another number of compute units (e.g. a partitioned one) fails with ETABLE;
+ * explicit paths and the host-only iq4xs_dispatch query are unaffected. */
 int iq4xs_load_dispatch_table(const char *path);
 
 /* Name of a path ("AUTO", "GEMV", "MMQ", "DEQ_BF16") or "?" */
 const char *iq4xs_path_name(int path);
 
-/* Message for the last error on this thread ("" if none). */
+/* Message for the last error on this thread ("" if none); the pointer stays
+ * valid until the thread's next failing call.  Convention of this C ABI (no
+ * passage): status codes are returned, never thrown across the boundary, and
+ * the text is kept per thread. */
 const char *iq4xs_last_error(void);
 
 #ifdef __cplusplus

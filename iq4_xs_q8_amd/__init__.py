@@ -108,8 +108,8 @@ def _stream(t: torch.Tensor) -> int:
 
 def _on(t: torch.Tensor):
     """Make t's device current for the call (a no-op when it already is)."""
-    if t.is_cuda and t.device.index == torch.cuda.current_device():
-        return contextlib.nullcontext()
+    if not t.is_cuda or t.device.index == torch.cuda.current_device():
+        return contextlib.nullcontext()      # (a non-GPU tensor is rejected inside)
     return torch.cuda.device(t.device)
 
 
@@ -121,6 +121,47 @@ def _dev(t: torch.Tensor, dtype: torch.dtype, name: str) -> int:
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return t.data_ptr()
+
+
+def _shape(t, name: str, shape) -> None:
+    """t must be a tensor of exactly `shape` (checked before anything reaches
+    the library, which only sees raw pointers)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _at_least(t, name: str, nbytes: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, {nbytes} needed")
+
+
+def _one_device(*ts) -> None:
+    devs = {t.device for t in ts if isinstance(t, torch.Tensor)}
+    if len(devs) > 1:
+        raise ValueError(f"tensors on different devices: {sorted(str(d) for d in devs)}")
+
+
+def _mk(t, name: str) -> tuple:
+    """(M, K) of a 2-D activation tensor."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D [M, K], got shape {tuple(t.shape)}")
+    return int(t.shape[0]), int(t.shape[1])
+
+
+def _wrows(W, K: int) -> int:
+    """N of an IQ4_XS weight tensor [N, K/256*136] (K a multiple of 256)."""
+    if K % 256:
+        raise ValueError(f"K must be a multiple of 256, got {K}")
+    if not isinstance(W, torch.Tensor) or W.dim() != 2:
+        raise ValueError("W must be a 2-D tensor [N, K/256*136]")
+    _shape(W, "W", (W.shape[0], K // 256 * 136))
+    return int(W.shape[0])
 
 
 def weight_bytes(N: int, K: int) -> int:
@@ -137,9 +178,11 @@ def q8_1_bytes(M: int, K: int) -> int:
 
 def quantize_q8_1(X: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     """fp32 [M, K] -> Q8_1 uint8 [M, K/32*36]."""
-    M, K = X.shape
+    M, K = _mk(X, "X")
     if out is None:
         out = torch.empty((M, (K // 32) * 36), dtype=torch.uint8, device=X.device)
+    _shape(out, "Xq", (M, (K // 32) * 36))
+    _one_device(X, out)
     with _on(X):
         check(_L().iq4xs_quantize_q8_1(_dev(X, torch.float32, "X"), _dev(out, torch.uint8, "Xq"),
                                       M, K, _stream(X)))
@@ -158,10 +201,12 @@ def gemm(W: torch.Tensor, X: torch.Tensor, path: int = PATH_AUTO,
 
     With `workspace` (uint8, workspace_bytes(M, N, K, path) bytes) nothing is
     allocated inside the call, so it can be captured in a graph."""
-    M, K = X.shape
-    N = W.shape[0]
+    M, K = _mk(X, "X")
+    N = _wrows(W, K)
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=X.device)
+    _shape(out, "Y", (M, N))
+    _one_device(W, X, out, workspace)
     with _on(X):
         if workspace is None:
             check(_L().iq4xs_gemm_path(_dev(W, torch.uint8, "W"), _dev(X, torch.float32, "X"),
@@ -177,10 +222,15 @@ def gemm(W: torch.Tensor, X: torch.Tensor, path: int = PATH_AUTO,
 def gemm_q8_1(W: torch.Tensor, Xq: torch.Tensor, K: int, path: int = PATH_AUTO,
               out: torch.Tensor | None = None) -> torch.Tensor:
     """Y[M, N] from already-quantized Q8_1 activations Xq [M, K/32*36]."""
-    M = Xq.shape[0]
-    N = W.shape[0]
+    N = _wrows(W, K)
+    if not isinstance(Xq, torch.Tensor) or Xq.dim() != 2:
+        raise ValueError("Xq must be a 2-D tensor [M, K/32*36]")
+    M = int(Xq.shape[0])
+    _shape(Xq, "Xq", (M, K // 32 * 36))
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=Xq.device)
+    _shape(out, "Y", (M, N))
+    _one_device(W, Xq, out)
     with _on(Xq):
         check(_L().iq4xs_gemm_q8_1(_dev(W, torch.uint8, "W"), _dev(Xq, torch.uint8, "Xq"),
                                   _dev(out, torch.float32, "Y"), M, N, K, path, _stream(Xq)))
@@ -195,9 +245,12 @@ def act_bytes(M: int, K: int) -> int:
 
 def prepare_act(X: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     """Quantize fp32 X [M, K] into the kernels' activation layout (opaque uint8)."""
-    M, K = X.shape
+    M, K = _mk(X, "X")
+    need = act_bytes(M, K)
     if out is None:
-        out = torch.empty(act_bytes(M, K), dtype=torch.uint8, device=X.device)
+        out = torch.empty(need, dtype=torch.uint8, device=X.device)
+    _at_least(out, "act", need)
+    _one_device(X, out)
     with _on(X):
         check(_L().iq4xs_prepare_act(_dev(X, torch.float32, "X"), _dev(out, torch.uint8, "act"),
                                     M, K, _stream(X)))
@@ -208,9 +261,12 @@ def gemm_act(W: torch.Tensor, act: torch.Tensor, M: int, K: int, path: int = PAT
              out: torch.Tensor | None = None, y_zeroed: bool = False) -> torch.Tensor:
     """Y[M, N] from prepared activations (the matmul kernel; y_zeroed: `out`
     already holds zeros, so no zeroing kernel runs before it)."""
-    N = W.shape[0]
+    N = _wrows(W, K)
+    _at_least(act, "act", act_bytes(M, K))
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=act.device)
+    _shape(out, "Y", (M, N))
+    _one_device(W, act, out)
     with _on(act):
         check(_L().iq4xs_gemm_act(_dev(W, torch.uint8, "W"), _dev(act, torch.uint8, "act"),
                                  _dev(out, torch.float32, "Y"), M, N, K,
@@ -234,12 +290,16 @@ def gemm_group(Ws: list, X: torch.Tensor, outs: list | None = None,
     quantized once and, where the shapes allow, one matmul launch covers all
     of them.  With `workspace` (uint8, group_workspace_bytes(...) bytes)
     nothing is allocated inside the call."""
-    M, K = X.shape
+    M, K = _mk(X, "X")
     G = len(Ws)
+    Ns = [_wrows(W, K) for W in Ws]
     if outs is None:
-        outs = [torch.empty((M, W.shape[0]), dtype=torch.float32, device=X.device) for W in Ws]
+        outs = [torch.empty((M, N), dtype=torch.float32, device=X.device) for N in Ns]
     if len(outs) != G:
         raise ValueError("one output per weight matrix")
+    for g, (o, N) in enumerate(zip(outs, Ns)):
+        _shape(o, f"Y[{g}]", (M, N))
+    _one_device(X, workspace, *Ws, *outs)
     w = (ctypes.c_void_p * max(G, 1))(*[_dev(W, torch.uint8, "W") for W in Ws])
     y = (ctypes.c_void_p * max(G, 1))(*[_dev(o, torch.float32, "Y") for o in outs])
     n = (ctypes.c_int64 * max(G, 1))(*[W.shape[0] for W in Ws])
@@ -252,9 +312,11 @@ def gemm_group(Ws: list, X: torch.Tensor, outs: list | None = None,
 
 def dequantize_bf16(W: torch.Tensor, K: int, out: torch.Tensor | None = None) -> torch.Tensor:
     """IQ4_XS [N, K/256*136] -> bf16 [N, K]."""
-    N = W.shape[0]
+    N = _wrows(W, K)
     if out is None:
         out = torch.empty((N, K), dtype=torch.bfloat16, device=W.device)
+    _shape(out, "Wb", (N, K))
+    _one_device(W, out)
     with _on(W):
         check(_L().iq4xs_dequantize_bf16(_dev(W, torch.uint8, "W"), _dev(out, torch.bfloat16, "Wb"),
                                         N, K, _stream(W)))

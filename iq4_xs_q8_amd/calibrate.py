@@ -32,19 +32,28 @@ BIG = 1000000000
 
 
 def load(path):
-    best = collections.defaultdict(dict)      # (N, K) -> M -> {path: ms}
+    """(N, K) -> M -> {path: ms}, and the compute-unit count the sweep ran on
+    (None when its records do not say)."""
+    best = collections.defaultdict(dict)
+    cus = set()
     for line in open(path):
         r = json.loads(line)
+        if "cus" in r:
+            cus.add(int(r["cus"]))
         if r["path"] == "AUTO":
             continue
         best[(r["N"], r["K"])].setdefault(r["M"], {})[r["path"]] = r["ms"]
-    return best
+    if len(cus) > 1:
+        raise SystemExit(f"sweep mixes devices with {sorted(cus)} compute units")
+    return best, (cus.pop() if cus else None)
 
 
-def table(best, arch="gfx950"):
+def table(best, arch="gfx950", cus=None):
     lines = [f"# Dispatch table for IQ4XS_PATH_AUTO on {arch}, written by iq4_xs_q8_amd/calibrate.py",
              "# from a bench.py --sweep run (per-call device ms from graph replays, quantization included).",
              "# band <path> <M_lo> <M_hi> <N> <K>; first match wins.", f"arch {arch}"]
+    if cus is not None:
+        lines.append(f"cus {cus}")
     gemv_ok_n = []                           # shapes where the GEMV won every measured M <= 4
     gemv_lost_n = []
     for (N, K), pts in sorted(best.items()):
@@ -96,7 +105,8 @@ def main(argv=None):
     if not argv:
         print(__doc__)
         sys.exit(2)
-    text = table(load(argv[0]))
+    best, cus = load(argv[0])
+    text = table(best, cus=cus)
     if len(argv) > 1:
         with open(argv[1], "w") as f:
             f.write(text)

@@ -171,6 +171,21 @@ int cus_of_current_device()
     return dev >= 0 && dev < (int)g_dev_cus.size() && g_dev_cus[dev] > 0 ? g_dev_cus[dev] : 256;
 }
 
+// A call that asked for AUTO runs on a device (checked): the table's bands
+// hold for it only if they were measured on as many compute units (a table
+// that names no count applies to any).
+int check_auto_cus(int requested_path)
+{
+    if (requested_path != IQ4XS_PATH_AUTO)
+        return IQ4XS_OK;
+    const int cus = cus_of_current_device();
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (g_table.cus > 0 && g_table.cus != cus)
+        return fail(IQ4XS_ETABLE, "dispatch table measured on %d compute units, the device has %d", g_table.cus,
+                    cus);
+    return IQ4XS_OK;
+}
+
 bool mul_ok(int64_t a, int64_t b, int64_t *out)
 {
     if (a < 0 || b < 0)
@@ -268,6 +283,7 @@ size_t workspace_need(int path, int64_t M, int64_t N, int64_t K)
 int run_gemm(const void *W, const float *X, const void *Xq, float *Y, int64_t M, int64_t N, int64_t K,
              int path, void *ws, size_t ws_bytes, hipStream_t s)
 {
+    const int requested = path;
     int st = resolve_path(path, M, N, K, &path);
     if (st != IQ4XS_OK)
         return st;
@@ -283,7 +299,7 @@ int run_gemm(const void *W, const float *X, const void *Xq, float *Y, int64_t M,
             (Xq && overlaps(ws, ws_bytes, Xq, (size_t)(M * (K / SB) * XBLK))))
             return fail(IQ4XS_EINVAL, "workspace overlaps W, X or Y");
     }
-    if ((st = check_device()) != IQ4XS_OK)
+    if ((st = check_device()) != IQ4XS_OK || (st = check_auto_cus(requested)) != IQ4XS_OK)
         return st;
 
     Scratch scr;
@@ -496,11 +512,12 @@ int iq4xs_gemm_act(const void *W, const void *act, float *Y, int64_t M, int64_t 
     const size_t yb = (size_t)(M * N * 4);
     if (overlaps(Y, yb, W, (size_t)(N * (K / QK) * WBLK)) || overlaps(Y, yb, act, xplanes_bytes(M, K)))
         return fail(IQ4XS_EINVAL, "Y overlaps an input");
+    const int requested = path;
     if ((st = resolve_path(path, M, N, K, &path)) != IQ4XS_OK)
         return st;
     if (path == IQ4XS_PATH_DEQ_BF16)
         return fail(IQ4XS_EPATH, "prepared activations feed the GEMV and MMQ paths only");
-    if ((st = check_device()) != IQ4XS_OK)
+    if ((st = check_device()) != IQ4XS_OK || (st = check_auto_cus(requested)) != IQ4XS_OK)
         return st;
     const XPlanes xp = xplanes_at((void *)act, M, K);
     const hipStream_t s = (hipStream_t)stream;

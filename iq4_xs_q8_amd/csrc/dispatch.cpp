@@ -85,6 +85,16 @@ bool parse_table(const std::string &text, Table *out, std::string *err)
             continue;
         if (tok[0] == "arch" && tok.size() == 2) {
             t.arch = tok[1];
+        } else if (tok[0] == "cus" && tok.size() == 2) {
+            // the bands were measured on a device with this many compute
+            // units; a device with another count (e.g. a partitioned one)
+            // does not use them
+            int64_t c = 0;
+            if (!parse_int(tok[1], &c, false) || c < 1 || c > 65536) {
+                *err = "dispatch table line " + std::to_string(lineno) + ": bad compute-unit count";
+                return false;
+            }
+            t.cus = (int)c;
         } else if (tok[0] == "band" && tok.size() == 6) {
             Band b;
             b.path = path_from_name(tok[1]);

@@ -18,6 +18,7 @@ struct Band {
 
 struct Table {
     std::string arch;
+    int cus = 0;                  // compute units the bands were measured on (0: any)
     std::vector<Band> bands;
 };
 

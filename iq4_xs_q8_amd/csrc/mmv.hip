@@ -284,16 +284,24 @@ k_mmv(MmvGroup grp, const int8_t *__restrict__ qp, int M, int K, int Mp, int nb,
     // the activation row feeding this lane's MFMA row (M or more: the zero row)
     const int arow = C::SPLIT ? ((col < 8 && (col & 3) < LIVE) ? ((col >> 2) & 1) * LIVE + (col & 3) : M) : col;
     const int a_step = arow < M ? C::MA * SB : 0;
+    // (offsets for the wavefronts that take the chunk's even super-blocks; the
+    // others add one super-block's worth, see compute)
     int a_off[CH / PAR], d_off[CH / PAR];
 #pragma unroll
     for (int i = 0; i < CH / PAR; i++) {
-        const int sb = (par + PAR * i) * SUBS + s;            // sub-block within the chunk
+        const int sb = (PAR * i) * SUBS + s;                  // sub-block within the chunk
         a_off[i] = (arow < M ? C::A_OFF + arow * SB : C::Z_OFF) + 16 * h + sb * a_step;
         d_off[i] = C::D_OFF + (C::SPLIT ? 4 * LIVE * h : 16 * h) + 4 * sb * Mp;
     }
     auto compute = [&](const Chunk &c, auto bc) __attribute__((always_inline)) {
         const char *B = C::template buf<decltype(bc)::value>();
         const char *wchunk = B + w_lane + (c.j0 & 1) * WBLK;  // the window starts at j0 & ~1
+        // Wavefront pair `par` takes the super-blocks whose absolute index j
+        // has j % 2 == par, in increasing order, whatever the chunk length
+        // (which depends on M) and wherever the chunk starts: every output
+        // then sums the same products in the same order for every M.
+        const int pc = par ^ (c.j0 & 1);                      // first one within the chunk (uniform)
+        const int a_pc = pc * SUBS * a_step, d_pc = pc * SUBS * 4 * Mp;
         // The I = CH/PAR super-blocks go in groups of GI whose LDS reads are
         // issued together, so that reads, lookups and MFMAs of different
         // super-blocks overlap; groups past the chunk's end are skipped, and
@@ -303,7 +311,7 @@ k_mmv(MmvGroup grp, const int8_t *__restrict__ qp, int M, int K, int Mp, int nb,
         constexpr int GI = I < 2 ? I : 2;
 #pragma unroll
         for (int g = 0; g < I; g += GI) {
-            if (par + PAR * g >= c.cl)                        // (uniform)
+            if (pc + PAR * g >= c.cl)                        // (uniform)
                 break;
             uint2 hdr[GI], q[GI];
             v4i ax[GI];
@@ -312,22 +320,22 @@ k_mmv(MmvGroup grp, const int8_t *__restrict__ qp, int M, int K, int Mp, int nb,
             // wavefront (same rows) each decode one of the two scales and
             // swap them.
             if constexpr (GI == 2)
-                hdr[0] = *reinterpret_cast<const uint2 *>(wchunk + (par + PAR * (g + h)) * WBLK);
+                hdr[0] = *reinterpret_cast<const uint2 *>(wchunk + (pc + PAR * (g + h)) * WBLK);
 #pragma unroll
             for (int k = 0; k < GI; k++) {
-                const char *wrow = wchunk + (par + PAR * (g + k)) * WBLK;
+                const char *wrow = wchunk + (pc + PAR * (g + k)) * WBLK;
                 if constexpr (GI != 2)
                     hdr[k] = *reinterpret_cast<const uint2 *>(wrow);
                 q[k] = *reinterpret_cast<const uint2 *>(wrow + QS_OFF + 16 * s + 8 * h);
-                ax[k] = *reinterpret_cast<const v4i *>(B + a_off[g + k]);
+                ax[k] = *reinterpret_cast<const v4i *>(B + a_off[g + k] + a_pc);
 #pragma unroll
                 for (int qd = 0; qd < DQ; qd++)
                     if constexpr (!C::SPLIT)
-                        dx[k][qd] = *reinterpret_cast<const float4 *>(B + d_off[g + k] + 32 * qd);
+                        dx[k][qd] = *reinterpret_cast<const float4 *>(B + d_off[g + k] + d_pc + 32 * qd);
                     else if constexpr (LIVE == 1)
-                        dx[k][qd] = make_float4(*reinterpret_cast<const float *>(B + d_off[g + k]), 0.f, 0.f, 0.f);
+                        dx[k][qd] = make_float4(*reinterpret_cast<const float *>(B + d_off[g + k] + d_pc), 0.f, 0.f, 0.f);
                     else {
-                        const float2 d2 = *reinterpret_cast<const float2 *>(B + d_off[g + k]);
+                        const float2 d2 = *reinterpret_cast<const float2 *>(B + d_off[g + k] + d_pc);
                         dx[k][qd] = make_float4(d2.x, d2.y, 0.f, 0.f);
                     }
             }
@@ -336,7 +344,7 @@ k_mmv(MmvGroup grp, const int8_t *__restrict__ qp, int M, int K, int Mp, int nb,
             float sw[GI];
             if constexpr (GI == 2) {
                 // (a super-block past the chunk gets d = 0: a zero scale)
-                const uint32_t d_bits = par + PAR * (g + h) < c.cl ? hdr[0].x : 0u;
+                const uint32_t d_bits = pc + PAR * (g + h) < c.cl ? hdr[0].x : 0u;
                 const float own = sub_scale(d_bits, hdr[0].y, s);
                 const uint32_t ob = __builtin_bit_cast(uint32_t, own);
                 // (lanes 0-31 of the first result: their own scale; lanes
@@ -347,7 +355,7 @@ k_mmv(MmvGroup grp, const int8_t *__restrict__ qp, int M, int K, int Mp, int nb,
             } else {
 #pragma unroll
                 for (int k = 0; k < GI; k++)
-                    sw[k] = par + PAR * (g + k) < c.cl ? sub_scale(hdr[k].x, hdr[k].y, s) : 0.0f;
+                    sw[k] = pc + PAR * (g + k) < c.cl ? sub_scale(hdr[k].x, hdr[k].y, s) : 0.0f;
             }
             v16i D[GI];
 #pragma unroll

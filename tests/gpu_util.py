@@ -40,6 +40,13 @@ def row_errors(y: np.ndarray, y_ref: np.ndarray) -> np.ndarray:
 def assert_rows_close(y: np.ndarray, y_ref: np.ndarray, tol: float = ROW_TOL, what: str = "") -> float:
     assert y.shape == y_ref.shape, (y.shape, y_ref.shape)
     assert np.all(np.isfinite(y)), f"{what}: {np.sum(~np.isfinite(y))} outputs not written (NaN poison left)"
+    # Outputs that a kernel adds into a Y zeroed beforehand are not covered
+    # by the NaN poison: an element nobody wrote would stay 0.  A computed
+    # fp32 result is exactly 0 only if the reference is (about) 0 too, so a
+    # zero where the reference is far from 0 means "not written".
+    big = np.abs(y_ref) > 1e-6 * np.max(np.abs(y_ref), axis=1, keepdims=True)
+    unwritten = (np.asarray(y) == 0) & big
+    assert not unwritten.any(), f"{what}: {int(unwritten.sum())} outputs are 0 where the reference is not"
     e = row_errors(y, y_ref)
     worst = int(np.argmax(e))
     assert e[worst] <= tol, f"{what}: row {worst} error {e[worst]:.3e} > {tol:g}"

@@ -286,3 +286,40 @@ def test_calibrate_writes_a_loadable_table(tmp_path):
         assert iq.dispatch(300, 4096, 4096) == iq.PATH_MMQ      # bf16 bands need the opt-in
     finally:
         iq.load_dispatch_table(None)
+
+
+def test_table_compute_unit_key(tmp_path):
+    """The table may name the compute-unit count its bands were measured on;
+    a malformed count is refused as a whole, a valid one loads (the count is
+    compared with the device's only when an AUTO call runs on a device, which
+    the GPU tests check), and the built-in table names 256."""
+    ok = tmp_path / "ok.txt"
+    ok.write_text("arch gfx950\ncus 128\nband MMQ 1 1000000000 * *\n")
+    try:
+        iq.load_dispatch_table(str(ok))
+        assert iq.dispatch(8, 4096, 4096) == iq.PATH_MMQ      # host-only query: no device check
+        for i, bad in enumerate(("cus 0", "cus x", "cus -4", "cus 1 2", "cus 99999999")):
+            f = tmp_path / f"bad{i}.txt"
+            f.write_text(f"arch gfx950\n{bad}\nband GEMV 1 4 * *\n")
+            assert L.iq4xs_load_dispatch_table(str(f).encode()) == iq.ETABLE, bad
+            assert iq.dispatch(2, 4096, 4096) == iq.PATH_MMQ  # the previous table stays
+    finally:
+        iq.load_dispatch_table(None)
+    builtin = open(os.path.join(ROOT, "iq4_xs_q8_amd", "csrc", "dispatch_gfx950.txt")).read()
+    assert re.search(r"^cus 256$", builtin, flags=re.M)
+
+
+def test_calibrate_carries_the_compute_unit_count(tmp_path):
+    from iq4_xs_q8_amd import calibrate
+    recs = [{"N": 4096, "K": 1024, "M": 1, "path": p, "ms": t, "cus": 256}
+            for p, t in (("GEMV", 0.01), ("MMQ", 0.02))]
+    sweep = tmp_path / "sweep.jsonl"
+    sweep.write_text("\n".join(json.dumps(r) for r in recs) + "\n")
+    out = tmp_path / "table.txt"
+    calibrate.main([str(sweep), str(out)])
+    assert "\ncus 256\n" in out.read_text()
+    recs.append(dict(recs[0], cus=128))
+    sweep.write_text("\n".join(json.dumps(r) for r in recs) + "\n")
+    with pytest.raises(SystemExit):
+        calibrate.main([str(sweep), str(out)])
+

@@ -18,7 +18,7 @@ import iq4_xs_q8_amd as iq
 import oracle
 import oracle_pins
 import synth
-from gpu_util import ROW_TOL, assert_rows_close, dev, poisoned
+from gpu_util import ROW_TOL, assert_rows_close, dev, poisoned, row_errors
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -159,27 +159,94 @@ def test_single_nonzero_activation(path):
         assert_rows_close(y[None, :], (V[:, kstar] * d16 * 127)[None, :], tol=1e-6)
 
 
-@pytest.mark.parametrize("path", [iq.PATH_GEMV, iq.PATH_MMQ, iq.PATH_DEQ_BF16])
-def test_deterministic_and_invariant(path):
-    M = 3 if path == iq.PATH_GEMV else 20
-    W, X = _inputs(M, 300, 1536, seed=5)
+def _double_dw(W: np.ndarray, K: int) -> np.ndarray:
+    """The same weights with every super-block's fp16 d doubled (exponent + 1;
+    the synthetic d never reaches the top exponent)."""
+    nb = K // 256
+    W2 = W.copy().reshape(W.shape[0], nb, 136)
+    d = W2[..., 0:2].copy().view(np.uint16)
+    assert np.all((d & 0x7C00) < 0x7800)
+    W2[..., 0:2] = (d + np.uint16(0x400)).view(np.uint8)
+    return W2.reshape(W.shape)
+
+
+def _check_invariants(Wd, W2d, Xd, path, what):
+    """Bitwise: deterministic, X -> -X gives -y, X -> 2X gives 2y, d_w -> 2 d_w
+    gives 2y, and a row does not depend on the other rows' values (same M,
+    so the same plan)."""
+    y1 = iq.gemm(Wd, Xd, path=path, out=poisoned(Xd.shape[:1] + Wd.shape[:1])).cpu()
+    assert torch.isfinite(y1).all(), f"{what}: outputs not written"
+    assert torch.equal(iq.gemm(Wd, Xd, path=path).cpu(), y1), f"{what}: two runs differ"
+    assert torch.equal(iq.gemm(Wd, -Xd, path=path).cpu(), -y1), f"{what}: y(-X) != -y(X)"
+    assert torch.equal(iq.gemm(Wd, 2 * Xd, path=path).cpu(), 2 * y1), f"{what}: y(2X) != 2y(X)"
+    assert torch.equal(iq.gemm(W2d, Xd, path=path).cpu(), 2 * y1), f"{what}: y(2 d_w) != 2y"
+    m = Xd.shape[0] // 2
+    Xo = torch.randn_like(Xd) * 3
+    Xo[m] = Xd[m]
+    assert torch.equal(iq.gemm(Wd, Xo, path=path).cpu()[m], y1[m]), f"{what}: row {m} depends on other rows"
+    return y1
+
+
+# Every kernel and work split of the integer paths.  The tile-kernel cases
+# were chosen with the host plan's rules (grid size, run length, tile shape):
+# 64 x 256 tiles up to M = 64, 128 x 128 above; "two owners": runs longer
+# than a tile, shared tiles added into a zeroed Y; "workspace": runs shorter
+# than a tile, 2..16 owners per tile summed in run order by the second kernel.
+INVARIANT_CASES = [
+    ("GEMV", iq.PATH_GEMV, 3, 300, 1536),
+    ("streaming M=20", iq.PATH_MMQ, 20, 300, 1536),
+    ("streaming M=16, shared tiles", iq.PATH_MMQ, 16, 10240, 5120),
+    ("tile 64x256, two owners", iq.PATH_MMQ, 40, 40000, 256),
+    ("tile 64x256, workspace (16 owners)", iq.PATH_MMQ, 64, 600, 4096),
+    ("tile 64x256, workspace (5 owners)", iq.PATH_MMQ, 64, 17408, 5120),
+    ("tile 128x128, one owner", iq.PATH_MMQ, 130, 8320, 1024),
+    ("tile 128x128, two owners", iq.PATH_MMQ, 65, 16768, 256),
+    ("tile 128x128, workspace (16 owners)", iq.PATH_MMQ, 100, 200, 4096),
+    ("tile 128x128, workspace (5 owners)", iq.PATH_MMQ, 96, 5120, 5120),
+    ("tile 128x128, two owners, M=512", iq.PATH_MMQ, 512, 10240, 5120),
+]
+
+
+@pytest.mark.parametrize("what,path,M,N,K", INVARIANT_CASES, ids=[c[0] for c in INVARIANT_CASES])
+def test_invariants_bitwise(what, path, M, N, K):
+    W, X = _inputs(M, N, K, seed=5)
+    Wd, W2d, Xd = dev(W), dev(_double_dw(W, K)), dev(X)
+    y = _check_invariants(Wd, W2d, Xd, path, what).numpy()
+    cols = _sample_cols(N, n=128, seed=M)
+    assert_rows_close(y[:, cols], O.gemm_q8_1(W[cols], O.quantize_q8_1(X), K), what=what)
+
+
+def test_bf16_path_invariants_within_tolerance():
+    # the bf16 MFMA's fp32 accumulation is not sign-symmetric bit for bit:
+    # only the tolerance-level invariances hold
+    W, X = _inputs(20, 300, 1536, seed=5)
     Wd, Xd = dev(W), dev(X)
-    y1 = iq.gemm(Wd, Xd, path=path).cpu()
-    y2 = iq.gemm(Wd, Xd, path=path).cpu()
-    assert torch.equal(y1, y2), "two runs differ"
-    if path == iq.PATH_DEQ_BF16:
-        # the bf16 MFMA's fp32 accumulation is not sign-symmetric bit for bit:
-        # only the tolerance-level invariances hold
-        ref = y1.double().numpy()
-        assert_rows_close(-iq.gemm(Wd, -Xd, path=path).cpu().numpy(), ref, tol=1e-6)
-        assert_rows_close(0.5 * iq.gemm(Wd, 2 * Xd, path=path).cpu().numpy(), ref, tol=1e-6)
-        return
-    # integer paths: exact symmetry and scaling (q flips sign, d doubles exactly)
-    assert torch.equal(iq.gemm(Wd, -Xd, path=path).cpu(), -y1)
-    assert torch.equal(iq.gemm(Wd, 2 * Xd, path=path).cpu(), 2 * y1)
-    # row m does not depend on the other rows (same path, same tile shape)
-    y_row = iq.gemm(Wd, Xd[1:2].contiguous(), path=path).cpu()
-    assert torch.equal(y_row[0], y1[1])
+    p = iq.PATH_DEQ_BF16
+    y1 = iq.gemm(Wd, Xd, path=p).cpu()
+    assert torch.equal(iq.gemm(Wd, Xd, path=p).cpu(), y1), "two runs differ"
+    ref = y1.double().numpy()
+    assert_rows_close(-iq.gemm(Wd, -Xd, path=p).cpu().numpy(), ref, tol=1e-6)
+    assert_rows_close(0.5 * iq.gemm(Wd, 2 * Xd, path=p).cpu().numpy(), ref, tol=1e-6)
+
+
+def test_rows_independent_of_m_streaming_and_gemv():
+    """The streaming kernel gives row m the same bits for every M it serves
+    (each M band has its own chunk length and register layout, but every
+    output sums the same products in the same order), here on the decode
+    shape whose runs start at odd super-blocks; so does the GEMV for M <= 4.
+    The tile kernel (M > 32) keeps this only within one M: its tile shape and
+    stream-K split follow M."""
+    N, K = 10240, 5120
+    W = synth.weights((905, N, K), N, K)
+    X = synth.activations((906, 32, K), 32, K, outlier_frac=0.01)
+    Wd, Xd = dev(W), dev(X)
+    full = iq.gemm(Wd, Xd, path=iq.PATH_MMQ).cpu()
+    for M in (1, 2, 3, 4, 5, 8, 9, 16, 17, 31):
+        y = iq.gemm(Wd, Xd[:M].contiguous(), path=iq.PATH_MMQ).cpu()
+        assert torch.equal(y, full[:M]), f"streaming kernel: rows of M={M} differ from M=32"
+    g4 = iq.gemm(Wd, Xd[:4].contiguous(), path=iq.PATH_GEMV).cpu()
+    for M in (1, 2, 3):
+        assert torch.equal(iq.gemm(Wd, Xd[:M].contiguous(), path=iq.PATH_GEMV).cpu(), g4[:M]), f"GEMV M={M}"
 
 
 @pytest.mark.parametrize("M,N,K", [(300, 2800, 512), (97, 8200, 256), (130, 8320, 1024),
@@ -213,30 +280,44 @@ def test_ksplit_kernel_when_the_others_are_switched_off(tmp_path):
     streaming and tile kernels do not take, and for odd K/256 at M <= 32),
     forced for every M by switching the other two off; it runs in a child
     process because the switches are read once per process."""
-    shapes = [(8, 300, 1024), (48, 300, 1280), (64, 97, 768), (100, 200, 2048)]
+    shapes = [(8, 300, 1024), (48, 300, 1280), (64, 97, 768), (100, 200, 2048), (20, 64, 8192)]
     inputs = {}
     for i, (M, N, K) in enumerate(shapes):
         W, X = _inputs(M, N, K, seed=40 + i)
+        Xo = X.copy()
+        Xo[np.arange(M) != M // 2] = synth.activations((41, M, K, i), M, K)[np.arange(M) != M // 2]
         np.save(tmp_path / f"w{i}.npy", W)
+        np.save(tmp_path / f"w2{i}.npy", _double_dw(W, K))
         np.save(tmp_path / f"x{i}.npy", X)
+        np.save(tmp_path / f"xo{i}.npy", Xo)
         inputs[i] = (W, X)
+    # in the child: y(X), y(-X), y(2X), y with every d_w doubled, and y(X')
+    # where X' differs from X in every row but M/2
     code = (
         "import sys, numpy as np, torch\n"
         "import iq4_xs_q8_amd as iq\n"
         f"d = {str(tmp_path)!r}\n"
         f"for i in range({len(shapes)}):\n"
         "    W = torch.from_numpy(np.load(f'{d}/w{i}.npy')).cuda()\n"
+        "    W2 = torch.from_numpy(np.load(f'{d}/w2{i}.npy')).cuda()\n"
         "    X = torch.from_numpy(np.load(f'{d}/x{i}.npy')).cuda()\n"
-        "    Y = torch.full((X.shape[0], W.shape[0]), float('nan'), device='cuda')\n"
-        "    iq.gemm(W, X, path=iq.PATH_MMQ, out=Y)\n"
-        "    np.save(f'{d}/y{i}.npy', Y.cpu().numpy())\n")
+        "    Xo = torch.from_numpy(np.load(f'{d}/xo{i}.npy')).cuda()\n"
+        "    for tag, w, x in (('y', W, X), ('neg', W, -X), ('dbl', W, 2 * X), ('dw', W2, X), ('oth', W, Xo)):\n"
+        "        Y = torch.full((X.shape[0], W.shape[0]), float('nan'), device='cuda')\n"
+        "        iq.gemm(w, x, path=iq.PATH_MMQ, out=Y)\n"
+        "        np.save(f'{d}/{tag}{i}.npy', Y.cpu().numpy())\n")
     env = dict(os.environ, IQ4XS_MMV="0", IQ4XS_TILE="0",
                PYTHONPATH=os.pathsep.join([ROOT, os.environ.get("PYTHONPATH", "")]))
     subprocess.run([sys.executable, "-c", code], env=env, check=True, timeout=120)
     for i, (M, N, K) in enumerate(shapes):
         W, X = inputs[i]
         y = np.load(tmp_path / f"y{i}.npy")
-        assert_rows_close(y, O.gemm_q8_1(W, O.quantize_q8_1(X), K), what=f"k_mmq M={M} N={N} K={K}")
+        what = f"k_mmq M={M} N={N} K={K}"
+        assert_rows_close(y, O.gemm_q8_1(W, O.quantize_q8_1(X), K), what=what)
+        assert np.array_equal(np.load(tmp_path / f"neg{i}.npy"), -y), f"{what}: y(-X) != -y"
+        assert np.array_equal(np.load(tmp_path / f"dbl{i}.npy"), 2 * y), f"{what}: y(2X) != 2y"
+        assert np.array_equal(np.load(tmp_path / f"dw{i}.npy"), 2 * y), f"{what}: y(2 d_w) != 2y"
+        assert np.array_equal(np.load(tmp_path / f"oth{i}.npy")[M // 2], y[M // 2]), f"{what}: row independence"
 
 
 def test_negative_control_corrupted_weight_fails():
@@ -325,6 +406,13 @@ def test_full_size_sampled(cid, N, K, M):
         yb = iq.gemm(Wd, dev(X), path=iq.PATH_DEQ_BF16, out=poisoned((M, N))).cpu().numpy()
         assert np.all(np.isfinite(yb))
         assert_rows_close(yb[:, cols], O.gemm_bf16(W[cols], Xq, K), what="DEQ_BF16")
+        # the same output against the integer formulation: bf16 keeps 8
+        # significant bits of W~ and X~, so the per-row ratio sits near
+        # 2-3e-3, far above the 1e-4 of the exact paths
+        ratio = row_errors(yb[:, cols], ref)
+        print(f"[bf16-vs-integer-oracle] N={N} K={K} M={M} per-row ratio max {ratio.max():.3e} "
+              f"median {np.median(ratio):.3e}", flush=True)
+        assert 1e-4 < ratio.max() < 2e-2
 
 
 _cache = {}
@@ -347,11 +435,11 @@ def _wdev_cached(wl, N, K, W):
 
 
 # More 32-column tiles than compute units: the streaming kernel's balanced runs
-# end inside tiles, and each such tile is summed from its two owners' partial
-# tiles through the workspace (flag swap, fixed order).  With M <= 4 and an
-# fp32 X the kernel also quantizes X itself; the pre-quantized and prepared-
-# activation entry points run the same matmul on planes from the quantize
-# kernel, so all of them must agree bit for bit.
+# end inside tiles, and each such tile's two owners add their partial tiles
+# into a Y that the quantize kernel of the same call zeroed (0 + a + b ==
+# 0 + b + a).  The pre-quantized and prepared-activation entry points and the
+# caller-workspace entry point run the same matmul kernel, so all of them must
+# agree bit for bit, whatever the workspace held before.
 SHARED_SHAPES = [(1, 8224, 512), (2, 10240, 1024), (3, 8224, 1024), (4, 10240, 2048),
                  (7, 8224, 512), (16, 10240, 1024), (32, 8224, 512)]
 
@@ -493,3 +581,24 @@ def test_graph_replays_match_eager(M, N, K):
         assert np.array_equal(got, want), f"replay {rep} differs from the eager call"
         ref = O.gemm_q8_1(W, O.quantize_q8_1(Xn), K)
         assert_rows_close(got, ref, what=f"graph replay {rep} M={M}")
+
+
+def test_table_for_another_compute_unit_count_is_refused(tmp_path):
+    """A dispatch table measured on another number of compute units does not
+    drive AUTO on this device (fail-closed: ETABLE); explicit paths still run."""
+    t = tmp_path / "t.txt"
+    t.write_text("arch gfx950\ncus 7\nband MMQ 1 1000000000 * *\n")
+    W, X = _inputs(4, 300, 1024, seed=2)
+    Wd, Xd = dev(W), dev(X)
+    try:
+        iq.load_dispatch_table(str(t))
+        with pytest.raises(iq.Iq4xsError) as e:
+            iq.gemm(Wd, Xd)
+        assert e.value.code == iq.ETABLE and "compute units" in str(e.value)
+        y = iq.gemm(Wd, Xd, path=iq.PATH_MMQ, out=poisoned((4, 300))).cpu().numpy()
+        assert_rows_close(y, O.gemm(W, X))
+    finally:
+        iq.load_dispatch_table(None)
+    props = torch.cuda.get_device_properties(0)
+    assert props.multi_processor_count == 256, "the built-in table was measured on 256 compute units"
+    assert_rows_close(iq.gemm(Wd, Xd, out=poisoned((4, 300))).cpu().numpy(), O.gemm(W, X))
