@@ -118,6 +118,22 @@ int iq4xs_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int path, size_t
 int iq4xs_gemm_ws(const void *W, const float *X, float *Y, int64_t M, int64_t N, int64_t K, int path,
                   void *workspace, size_t workspace_bytes, void *stream);
 
+/* For callers that cannot allocate -- code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc: iq4xs_gemm_path with its
+ * scratch taken from a static device array of the library, of
+ * IQ4XS_STATIC_SCRATCH_BYTES per device, instead of the stream-ordered
+ * allocation.  Nothing is allocated: no hipMalloc/hipFree, no pool call.
+ * Arguments, result and errors are iq4xs_gemm_path's; in addition EINVAL
+ * when the shape and path need more scratch than the array holds (the need
+ * is iq4xs_gemm_workspace_bytes(M, N, K, path)).  Each device has its own
+ * array, held from the first call on that device until the process ends.
+ * Every call on one device uses that device's array and leaves its contents
+ * behind: calls that overlap in time on one device (two streams, two threads)
+ * race and give undefined results, so order them on one stream. */
+#define IQ4XS_STATIC_SCRATCH_BYTES (64u << 20)
+int iq4xs_gemm_noalloc(const void *W, const float *X, float *Y, int64_t M, int64_t N, int64_t K,
+                       int path, void *stream);
+
 /* Y = X * W^T from activations already quantized to Q8_1 (Xq [M][K/32]
  * blocks of 36 bytes, layout above; caller-owned, 4-byte aligned, read only).
  * The "V100TPS engine log", M=64 kernel-launch table, shows quantize_q8_1 as

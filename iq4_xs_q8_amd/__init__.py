@@ -31,7 +31,7 @@ Y_ZEROED = 0x100     # gemm_act hint: Y already holds zeros
 
 EXPORTS = ("iq4xs_weight_bytes", "iq4xs_q8_1_bytes", "iq4xs_init", "iq4xs_quantize_q8_1",
            "iq4xs_gemm", "iq4xs_gemm_path", "iq4xs_gemm_workspace_bytes", "iq4xs_gemm_ws",
-           "iq4xs_gemm_q8_1", "iq4xs_act_bytes",
+           "iq4xs_gemm_noalloc", "iq4xs_gemm_q8_1", "iq4xs_act_bytes",
            "iq4xs_prepare_act", "iq4xs_gemm_act", "iq4xs_gemm_group_workspace_bytes", "iq4xs_gemm_group",
            "iq4xs_dequantize_bf16",
            "iq4xs_dispatch", "iq4xs_load_dispatch_table", "iq4xs_path_name", "iq4xs_last_error")
@@ -58,6 +58,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "iq4xs_gemm_path": [p, p, p, i64, i64, i64, i32, p],
         "iq4xs_gemm_workspace_bytes": [i64, i64, i64, i32, sz],
         "iq4xs_gemm_ws": [p, p, p, i64, i64, i64, i32, p, ctypes.c_size_t, p],
+        "iq4xs_gemm_noalloc": [p, p, p, i64, i64, i64, i32, p],
         "iq4xs_gemm_q8_1": [p, p, p, i64, i64, i64, i32, p],
         "iq4xs_act_bytes": [i64, i64, sz],
         "iq4xs_prepare_act": [p, p, i64, i64, p],
@@ -216,6 +217,23 @@ def gemm(W: torch.Tensor, X: torch.Tensor, path: int = PATH_AUTO,
                                     _dev(out, torch.float32, "Y"), M, N, K, path,
                                     _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
                                     _stream(X)))
+    return out
+
+
+STATIC_SCRATCH_BYTES = 64 << 20     # IQ4XS_STATIC_SCRATCH_BYTES
+
+
+def gemm_noalloc(W: torch.Tensor, X: torch.Tensor, out: torch.Tensor, path: int = PATH_AUTO) -> torch.Tensor:
+    """gemm() with the library's static per-device scratch: nothing is
+    allocated (the output must be given).  Calls that overlap on one device
+    race on that scratch."""
+    M, K = _mk(X, "X")
+    N = _wrows(W, K)
+    _shape(out, "Y", (M, N))
+    _one_device(W, X, out)
+    with _on(X):
+        check(_L().iq4xs_gemm_noalloc(_dev(W, torch.uint8, "W"), _dev(X, torch.float32, "X"),
+                                     _dev(out, torch.float32, "Y"), M, N, K, path, _stream(X)))
     return out
 
 

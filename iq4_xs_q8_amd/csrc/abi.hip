@@ -186,6 +186,39 @@ int check_auto_cus(int requested_path)
     return IQ4XS_OK;
 }
 
+// The scratch of iq4xs_gemm_noalloc.  In host code `scratch` names a host-side
+// stand-in, not the device copy: the device address of the current device's
+// copy is looked up once per device (with that device current) and only that
+// address is ever passed to kernels.
+static_assert(IQ4XS_STATIC_SCRATCH_BYTES % 256 == 0, "whole 256-byte units");
+static __device__ __align__(256) char scratch[IQ4XS_STATIC_SCRATCH_BYTES];
+std::vector<void *> g_scratch;         // per device: address of its copy of `scratch`
+
+int static_scratch(void **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return fail(IQ4XS_EDEVICE, "no current HIP device");
+    }
+    std::lock_guard<std::mutex> lk(g_mu);
+    if ((int)g_scratch.size() <= dev)
+        g_scratch.resize(dev + 1, nullptr);
+    if (g_scratch[dev] == nullptr) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr) {
+            (void)hipGetLastError();
+            return fail(IQ4XS_ELAUNCH, "static scratch of device %d: %s", dev, hipGetErrorString(e));
+        }
+        if ((uintptr_t)p % 256 != 0)
+            return fail(IQ4XS_ELAUNCH, "static scratch of device %d is not 256-byte aligned", dev);
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return IQ4XS_OK;
+}
+
 bool mul_ok(int64_t a, int64_t b, int64_t *out)
 {
     if (a < 0 || b < 0)
@@ -427,6 +460,35 @@ int iq4xs_gemm_ws(const void *W, const float *X, float *Y, int64_t M, int64_t N,
     if (overlaps(Y, yb, W, (size_t)(N * (K / QK) * WBLK)) || overlaps(Y, yb, X, (size_t)(M * K * 4)))
         return fail(IQ4XS_EINVAL, "Y overlaps an input");
     return run_gemm(W, X, nullptr, Y, M, N, K, path, workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+int iq4xs_gemm_noalloc(const void *W, const float *X, float *Y, int64_t M, int64_t N, int64_t K, int path,
+                       void *stream)
+{
+    if (!W || !X || !Y)
+        return fail(IQ4XS_EINVAL, "null pointer");
+    int st = check_dims(M, N, K);
+    if (st != IQ4XS_OK)
+        return st;
+    if (!aligned(W, 16) || !aligned(X, 16) || !aligned(Y, 16))
+        return fail(IQ4XS_EALIGN, "W, X and Y must be 16-byte aligned");
+    const size_t yb = (size_t)(M * N * 4);
+    if (overlaps(Y, yb, W, (size_t)(N * (K / QK) * WBLK)) || overlaps(Y, yb, X, (size_t)(M * K * 4)))
+        return fail(IQ4XS_EINVAL, "Y overlaps an input");
+    int resolved = 0;
+    if ((st = resolve_path(path, M, N, K, &resolved)) != IQ4XS_OK)
+        return st;
+    const size_t need = workspace_need(resolved, M, N, K);
+    if (need > IQ4XS_STATIC_SCRATCH_BYTES)
+        return fail(IQ4XS_EINVAL, "M=%lld N=%lld K=%lld on %s needs %zu bytes of scratch; the static scratch holds %u",
+                    (long long)M, (long long)N, (long long)K, path_name(resolved), need,
+                    (unsigned)IQ4XS_STATIC_SCRATCH_BYTES);
+    if ((st = check_device()) != IQ4XS_OK)
+        return st;
+    void *ws = nullptr;
+    if ((st = static_scratch(&ws)) != IQ4XS_OK)
+        return st;
+    return run_gemm(W, X, nullptr, Y, M, N, K, path, ws, IQ4XS_STATIC_SCRATCH_BYTES, (hipStream_t)stream);
 }
 
 int iq4xs_gemm(const void *W, const float *X, float *Y, int64_t M, int64_t N, int64_t K, void *stream)

@@ -323,3 +323,23 @@ def test_calibrate_carries_the_compute_unit_count(tmp_path):
     with pytest.raises(SystemExit):
         calibrate.main([str(sweep), str(out)])
 
+
+def test_noalloc_rejects_shapes_beyond_the_static_scratch():
+    """The allocation-free entry point refuses, on the host and before any
+    HIP call, a shape whose scratch would not fit the static array."""
+    assert iq.STATIC_SCRATCH_BYTES == 64 << 20
+    text = open(HEADER).read()
+    assert re.search(r"#define IQ4XS_STATIC_SCRATCH_BYTES \(64u << 20\)", text)
+    # activation planes of 4096 x 17408 alone are 80 MB
+    far = 1 << 44                     # fake addresses far apart: no overlap
+    assert L.iq4xs_gemm_noalloc(A, far, 2 * far, 4096, 8, 17408, iq.PATH_MMQ, None) == iq.EINVAL
+    assert b"static scratch" in L.iq4xs_last_error()
+    # the bf16 path's operands at 100000 x 5120
+    assert L.iq4xs_gemm_noalloc(A, far, 2 * far, 64, 100000, 5120, iq.PATH_DEQ_BF16, None) == iq.EINVAL
+    assert b"static scratch" in L.iq4xs_last_error()
+    # argument checks as iq4xs_gemm_path
+    assert L.iq4xs_gemm_noalloc(None, A * 2, A * 4, 4, 8, 256, 0, None) == iq.EINVAL
+    assert L.iq4xs_gemm_noalloc(A + 8, A * 2, A * 4, 4, 8, 256, 0, None) == iq.EALIGN
+    assert L.iq4xs_gemm_noalloc(A, A * 2, A * 4, 4, 8, 300, 0, None) == iq.EINVAL
+    if not _has_gpu():
+        assert L.iq4xs_gemm_noalloc(A, A * 2, A * 4, 4, 8, 256, 0, None) == iq.EDEVICE
