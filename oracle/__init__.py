@@ -34,6 +34,9 @@ def build(out: str = LIB, src: str = SRC, extra=()) -> str:
     return out
 
 
+# weight formats (the oracle's own numbering)
+FMT_IQ4_XS, FMT_IQ4_NL, FMT_Q4_0 = 0, 1, 2
+
 _p = ctypes.c_void_p
 _i64 = ctypes.c_int64
 
@@ -66,6 +69,12 @@ class Oracle:
                      "oracle_double_to_bf16_array"):
             getattr(lib, name).argtypes = [_p, _i64, _p]
             getattr(lib, name).restype = None
+        lib.oracle_row_bytes.argtypes = [ctypes.c_int, _i64]
+        lib.oracle_row_bytes.restype = _i64
+        lib.oracle_dequantize_fmt.argtypes = [ctypes.c_int, _p, _i64, _i64, _p]
+        lib.oracle_dequantize_fmt.restype = None
+        lib.oracle_gemm_fmt_q8_1.argtypes = [ctypes.c_int, _p, _p, _i64, _i64, _i64, _p]
+        lib.oracle_gemm_fmt_q8_1.restype = None
         lib.oracle_set_threads.argtypes = [ctypes.c_int]
         lib.oracle_set_threads.restype = None
         lib.oracle_get_threads.argtypes = []
@@ -165,6 +174,36 @@ class Oracle:
         """Quantize fp32 X to Q8_1, then the integer-dot GEMM."""
         K = X.shape[1]
         return self.gemm_q8_1(W, self.quantize_q8_1(X), K)
+
+    # -- other weight formats (FMT_IQ4_XS, FMT_IQ4_NL, FMT_Q4_0) --------
+    def row_bytes(self, fmt: int, K: int) -> int:
+        return self.lib.oracle_row_bytes(int(fmt), int(K))
+
+    def _wcheck_fmt(self, fmt: int, W: np.ndarray, K: int) -> tuple:
+        rb = self.row_bytes(fmt, K)
+        if rb <= 0 or K % (256 if fmt == FMT_IQ4_XS else 32):
+            raise ValueError("unknown format or K not a whole number of blocks")
+        W = np.ascontiguousarray(W, dtype=np.uint8)
+        if W.ndim != 2 or W.shape[1] != rb:
+            raise ValueError(f"W must be uint8 [N, {rb}]")
+        return W, W.shape[0]
+
+    def dequantize_fmt(self, fmt: int, W: np.ndarray, K: int) -> np.ndarray:
+        W, N = self._wcheck_fmt(fmt, W, K)
+        out = np.empty((N, K), dtype=np.float64)
+        self.lib.oracle_dequantize_fmt(int(fmt), W.ctypes.data, N, K, out.ctypes.data)
+        return out
+
+    def gemm_fmt_q8_1(self, fmt: int, W: np.ndarray, Xq: np.ndarray, K: int) -> np.ndarray:
+        W, N = self._wcheck_fmt(fmt, W, K)
+        Xq, M = self._xqcheck(Xq, K)
+        Y = np.empty((M, N), dtype=np.float64)
+        self.lib.oracle_gemm_fmt_q8_1(int(fmt), W.ctypes.data, Xq.ctypes.data, M, N, K, Y.ctypes.data)
+        return Y
+
+    def gemm_fmt(self, fmt: int, W: np.ndarray, X: np.ndarray) -> np.ndarray:
+        K = X.shape[1]
+        return self.gemm_fmt_q8_1(fmt, W, self.quantize_q8_1(X), K)
 
 
 _default = None

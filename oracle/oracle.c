@@ -21,6 +21,18 @@
  *        block {fp16 d, fp16 s, int8 qs[32]}.  The pages name these formats
  *        but print neither the byte layout nor the constants.
  *
+ *   [S]  "SGLang MoE port thread" (lcz.me/post/31556), the passage that takes
+ *        back an earlier conclusion about TP block alignment: an IQ4_NL block
+ *        holds 32 values in 18 bytes (it had been mistaken for a 256-value
+ *        block); and the passage on the per-layer embedding table, whose
+ *        IQ4_NL rows were checked bit for bit against an independent decoder.
+ *   The engine log's batched-kernel section also fixes the two 32-weight
+ *   formats beside IQ4_XS: a Q4_0 block is exactly the geometry of an IQ4_XS
+ *   sub-block (four 32-bit words of nibbles, low nibbles elements 0-15, high
+ *   nibbles 16-31) with one scale d per block and the value q-8; IQ4_NL
+ *   (the format the kvalues_iq4nl codebook is named for) has the same block
+ *   with the value kvalues_iq4nl[q].
+ *
  * Readings where the pages are silent (each one stated where it is used):
  *   R1  field order and 6-bit scale assembly follow [G];
  *   R2  Q8_1 of a 32-element block: amax = max|x| (fp32), d = amax/127 as an
@@ -31,7 +43,10 @@
  *       single rounding to fp16);
  *   R3  the GEMM uses the stored fp16 d of each Q8_1 block and ignores s;
  *   R4  the dequantize-to-bf16 variant rounds W~ = d*(ls-32)*kv and
- *       X~ = d_x*q to bf16 (nearest even) and sums their exact products.
+ *       X~ = d_x*q to bf16 (nearest even) and sums their exact products;
+ *   R5  an IQ4_NL or Q4_0 block of 18 bytes is {fp16 d, u8 qs[16]} (the GGUF
+ *       order: the scale first, then the 16 nibble bytes laid out as in an
+ *       IQ4_XS sub-block); a row of K weights is K/32 consecutive blocks.
  *
  * Arithmetic.  Every decoded weight d*(ls-32)*kv needs at most 11+6+7 = 24
  * significant bits and every product term d_w*(ls-32)*d_x*D at most 48, so
@@ -278,6 +293,87 @@ void oracle_gemm_bf16(const uint8_t *W, const uint8_t *Xq, int64_t M, int64_t N,
                 acc += w * x;
             }
             Y[m * N + n] = acc;
+        }
+}
+
+/* ------------------------------------------ IQ4_NL and Q4_0 (R5, [E], [S]) */
+
+#define ORACLE_B18 18      /* bytes per IQ4_NL / Q4_0 block of 32 weights */
+
+/* Weight formats of oracle_dequantize_fmt / oracle_gemm_fmt_q8_1. */
+#define ORACLE_FMT_IQ4_XS 0
+#define ORACLE_FMT_IQ4_NL 1
+#define ORACLE_FMT_Q4_0 2
+
+/* Value of element t (0..31) of an 18-byte block, without its scale: the
+   nibble placement of an IQ4_XS sub-block ([E]: low nibbles are elements
+   0-15, high nibbles 16-31), the 16 nibble bytes after the fp16 d (R5). */
+static int value18(int fmt, const uint8_t *blk, int t)
+{
+    uint8_t byte = blk[2 + (t % 16)];
+    int c = t < 16 ? (byte & 15) : (byte >> 4);
+    return fmt == ORACLE_FMT_IQ4_NL ? ORACLE_KV[c] : c - 8;   /* Q4_0: q - 8 */
+}
+
+static double scale18(const uint8_t *blk)
+{
+    return oracle_half_to_double((uint16_t)(blk[0] | (blk[1] << 8)));
+}
+
+/* Bytes of one row of K weights in a format (K % 256 == 0 for IQ4_XS, K % 32
+   for the 32-weight formats); 0 for an unknown format. */
+int64_t oracle_row_bytes(int fmt, int64_t K)
+{
+    if (fmt == ORACLE_FMT_IQ4_XS)
+        return K / ORACLE_QK * ORACLE_WBLK;
+    if (fmt == ORACLE_FMT_IQ4_NL || fmt == ORACLE_FMT_Q4_0)
+        return K / ORACLE_SB * ORACLE_B18;
+    return 0;
+}
+
+/* W~[n,k], exact in fp64, for any of the three formats.  out is [N][K]. */
+void oracle_dequantize_fmt(int fmt, const uint8_t *W, int64_t N, int64_t K, double *out)
+{
+    if (fmt == ORACLE_FMT_IQ4_XS) {
+        oracle_dequantize(W, N, K, out);
+        return;
+    }
+    int64_t rb = oracle_row_bytes(fmt, K);
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t k = 0; k < K; k++) {
+            const uint8_t *blk = W + n * rb + (k / ORACLE_SB) * ORACLE_B18;
+            out[n * K + k] = scale18(blk) * (double)value18(fmt, blk, (int)(k % ORACLE_SB));
+        }
+}
+
+/* Integer-dot formulation for any format ([E], R3, R5):
+     Y[m,n] = sum_b s_w[n,b] * d_x[m,b] * D[m,n,b],
+   s_w = d of block b (IQ4_NL, Q4_0) or d*(ls-32) (IQ4_XS), D the exact
+   integer dot of the 32 block values with the Q8_1 values.  Every term is
+   exact in fp64 (11 + 11 + 20 significant bits); the sum runs over b in
+   ascending order. */
+void oracle_gemm_fmt_q8_1(int fmt, const uint8_t *W, const uint8_t *Xq, int64_t M, int64_t N, int64_t K,
+                          double *Y)
+{
+    if (fmt == ORACLE_FMT_IQ4_XS) {
+        oracle_gemm_q8_1(W, Xq, M, N, K, Y);
+        return;
+    }
+    int64_t rb = oracle_row_bytes(fmt, K), nblk = K / ORACLE_SB;
+#pragma omp parallel for schedule(static) num_threads(oracle_get_threads())
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t m = 0; m < M; m++) {
+            double sum = 0.0;
+            for (int64_t j = 0; j < nblk; j++) {
+                const uint8_t *blk = W + n * rb + j * ORACLE_B18;
+                const uint8_t *xq = Xq + (m * nblk + j) * ORACLE_XBLK;
+                double d_x = oracle_half_to_double((uint16_t)(xq[0] | (xq[1] << 8)));
+                int64_t dot = 0;
+                for (int t = 0; t < ORACLE_SB; t++)
+                    dot += (int64_t)value18(fmt, blk, t) * (int64_t)(int8_t)xq[4 + t];
+                sum += scale18(blk) * d_x * (double)dot;
+            }
+            Y[m * N + n] = sum;
         }
 }
 

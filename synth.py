@@ -63,6 +63,28 @@ def weights(key: Sequence[int], N: int, K: int,
     return out.reshape(N, nb * BLOCK_BYTES)
 
 
+BLOCK18_BYTES = 18  # bytes per IQ4_NL / Q4_0 block of 32 weights
+
+
+def weights18(key: Sequence[int], N: int, K: int,
+              d_lo: float = 1e-3, d_hi: float = 4e-3) -> np.ndarray:
+    """Random IQ4_NL or Q4_0 weights (both store a block of 32 weights as an
+    fp16 d and 16 bytes of 4-bit indices) as uint8 [N, (K/32)*18].  The 16
+    index bytes use every bit, so uniform random bytes are exactly uniform
+    indices; d is drawn as for IQ4_XS."""
+    if K % 32 or N < 0:
+        raise ValueError("need N >= 0 and K a multiple of 32")
+    nb = K // 32
+    out = np.empty((N, nb, BLOCK18_BYTES), dtype=np.uint8)
+    rng = _rng(key)
+    for r0 in range(0, N, _ROW_CHUNK):
+        r1 = min(N, r0 + _ROW_CHUNK)
+        out[r0:r1] = rng.integers(0, 256, size=(r1 - r0, nb, BLOCK18_BYTES), dtype=np.uint8)
+        d = rng.uniform(d_lo, d_hi, size=(r1 - r0, nb)).astype(np.float16)
+        out[r0:r1, :, 0:2] = d.view(np.uint8).reshape(r1 - r0, nb, 2)
+    return out.reshape(N, nb * BLOCK18_BYTES)
+
+
 def activations(key: Sequence[int], M: int, K: int, sigma: float = 1.0,
                 outlier_frac: float = 0.0, outlier_scale: float = 20.0) -> np.ndarray:
     """fp32 activations [M, K] ~ N(0, sigma^2), optionally with outlier channels."""

@@ -18,6 +18,10 @@ What pins what:
     invariances Y(-X) = -Y(X), Y(2X) = 2Y(X), Y(2 d_w) = 2Y.
   * bf16 GEMM variant: torch's bf16 cast and an fp64 matmul of the rounded
     operands.
+  * IQ4_NL and Q4_0 (18-byte blocks of 32 weights): hand-worked blocks
+    (tests/golden/b18_handworked.txt), an encoder, exact rationals, closed
+    forms, invariants, and the identity "an IQ4_XS sub-block is an IQ4_NL
+    block with d = d*(ls-32)" against the IQ4_XS oracle.
 """
 
 from __future__ import annotations
@@ -385,7 +389,178 @@ def pin_gemm_bf16(o):
                           .view(torch.int16).numpy().view(np.uint16))
 
 
+# ------------------------------------------------- IQ4_NL and Q4_0 blocks
+FMT_IQ4_XS, FMT_IQ4_NL, FMT_Q4_0 = 0, 1, 2
+
+
+def encode_block18(d_bits: int, codes) -> np.ndarray:
+    """The 18 bytes of one IQ4_NL / Q4_0 block from its fields: d's fp16 bit
+    pattern and 32 indices, codes[t] being element t."""
+    codes = [int(v) for v in codes]
+    assert len(codes) == 32
+    out = np.zeros(18, dtype=np.uint8)
+    out[0], out[1] = d_bits & 0xFF, (d_bits >> 8) & 0xFF
+    for t in range(16):
+        out[2 + t] = codes[t] | (codes[16 + t] << 4)
+    return out
+
+
+def block18_values(fmt: int, d: float, codes) -> np.ndarray:
+    """W~ of one block from its fields (no byte decoding)."""
+    return np.array([d * (KV[c] if fmt == FMT_IQ4_NL else c - 8) for c in codes], dtype=np.float64)
+
+
+def build_matrix18(fmt, d_bits, codes, N, K):
+    """Encode N rows of K/32 blocks; returns (bytes [N, K/32*18], W~ [N, K])."""
+    nb = K // 32
+    W = np.zeros((N, nb * 18), dtype=np.uint8)
+    V = np.zeros((N, K))
+    for n in range(N):
+        for j in range(nb):
+            i = n * nb + j
+            W[n, 18 * j:18 * j + 18] = encode_block18(int(d_bits[i]), codes[i])
+            d = float(np.array(d_bits[i], dtype=np.uint16).view(np.float16))
+            V[n, 32 * j:32 * j + 32] = block18_values(fmt, d, codes[i])
+    return W, V
+
+
+def random_fields18(rng, nblocks):
+    d_bits = rng.uniform(1e-3, 4e-3, nblocks).astype(np.float16).view(np.uint16)
+    codes = rng.integers(0, 16, (nblocks, 32))
+    return d_bits, codes
+
+
+def read_handworked_b18():
+    blocks, vals = {}, []
+    with open(os.path.join(GOLDEN, "b18_handworked.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if not line:
+                continue
+            if line.startswith("block"):
+                name = line.split()[1]
+                blocks[name] = np.array([int(t, 16) for t in line.split("=")[1].split()], dtype=np.uint8)
+            else:
+                tag, name, e, v = line.split()
+                vals.append((FMT_IQ4_NL if tag == "nl" else FMT_Q4_0, name, int(e), float(v)))
+    return blocks, vals
+
+
+def pin_b18_handworked(o):
+    blocks, vals = read_handworked_b18()
+    assert len(vals) >= 28
+    assert np.array_equal(blocks["A"], encode_block18(0x3800, list(range(16)) + [15 - t for t in range(16)]))
+    for fmt, name, e, v in vals:
+        got = o.dequantize_fmt(fmt, blocks[name][None, :], 32)[0]
+        assert got[e] == v, (fmt, name, e, got[e], v)
+
+
+def pin_b18_random_blocks(o):
+    rng = np.random.default_rng(29)
+    for fmt in (FMT_IQ4_NL, FMT_Q4_0):
+        d_bits, codes = random_fields18(rng, 5 * 24)
+        W, V = build_matrix18(fmt, d_bits, codes, 5, 768)
+        assert np.array_equal(o.dequantize_fmt(fmt, W, 768), V)
+        # every index in isolation, at every position
+        for c in range(16):
+            for t in (0, 7, 15, 16, 24, 31):
+                cs = [c if i == t else 8 for i in range(32)]
+                v = o.dequantize_fmt(fmt, encode_block18(0x3C00, cs)[None, :], 32)[0]
+                want = KV[c] if fmt == FMT_IQ4_NL else c - 8
+                assert v[t] == want, (fmt, c, t)
+    assert o.row_bytes(FMT_IQ4_NL, 5120) == o.row_bytes(FMT_Q4_0, 5120) == 160 * 18
+
+
+def pin_b18_gemm_exact(o):
+    rng = np.random.default_rng(31)
+    for fmt in (FMT_IQ4_NL, FMT_Q4_0):
+        for (M, N, K) in ((3, 4, 64), (2, 3, 256)):
+            d_bits, codes = random_fields18(rng, N * K // 32)
+            W, V = build_matrix18(fmt, d_bits, codes, N, K)
+            X = rng.standard_normal((M, K)).astype(np.float32)
+            Xq = o.quantize_q8_1(X)
+            Y = o.gemm_fmt_q8_1(fmt, W, Xq, K)
+            exact, absum = _exact_gemm(V, Xq, M, K)
+            for m in range(M):
+                for n in range(N):
+                    err = abs(Fraction(float(Y[m, n])) - exact[m][n])
+                    assert err <= absum[m][n] * Fraction(1, 2**50), (fmt, m, n, float(err))
+
+
+def pin_b18_closed_forms(o):
+    rng = np.random.default_rng(37)
+    N, K = 6, 256
+    for fmt in (FMT_IQ4_NL, FMT_Q4_0):
+        d_bits, codes = random_fields18(rng, N * K // 32)
+        W, V = build_matrix18(fmt, d_bits, codes, N, K)
+        # one non-zero activation at column k*: Y[n] = W~[n,k*] * d16 * (+-127)
+        for kstar in (0, 15, 16, 31, 32, 100, 255):
+            for v in (2.5, -0.61):
+                X1 = np.zeros((1, K), dtype=np.float32)
+                X1[0, kstar] = v
+                d16 = float(np.float16(np.float32(abs(v)) / np.float32(127)))
+                want = V[:, kstar] * d16 * (127 if v > 0 else -127)
+                assert np.array_equal(o.gemm_fmt(fmt, W, X1)[0], want), (fmt, kstar, v)
+        # d = 0 everywhere: Y == 0
+        W0, _ = build_matrix18(fmt, np.zeros_like(d_bits), codes, N, K)
+        assert np.all(o.gemm_fmt(fmt, W0, rng.standard_normal((2, K)).astype(np.float32)) == 0)
+    # Q4_0 index 8 is the value 0
+    Wz, _ = build_matrix18(FMT_Q4_0, d_bits, np.full_like(codes, 8), N, K)
+    assert np.all(o.gemm_fmt(FMT_Q4_0, Wz, rng.standard_normal((3, K)).astype(np.float32)) == 0)
+
+
+def pin_b18_invariants(o):
+    rng = np.random.default_rng(41)
+    N, K, M = 5, 512, 3
+    for fmt in (FMT_IQ4_NL, FMT_Q4_0):
+        d_bits, codes = random_fields18(rng, N * K // 32)
+        W, _ = build_matrix18(fmt, d_bits, codes, N, K)
+        X = rng.standard_normal((M, K)).astype(np.float32)
+        Y = o.gemm_fmt(fmt, W, X)
+        assert Y.shape == (M, N)
+        assert np.array_equal(o.gemm_fmt(fmt, W, -X), -Y)
+        assert np.array_equal(o.gemm_fmt(fmt, W, 2 * X), 2 * Y)
+        W2, _ = build_matrix18(fmt, (d_bits.astype(np.uint32) + 0x400).astype(np.uint16), codes, N, K)
+        assert np.array_equal(o.gemm_fmt(fmt, W2, X), 2 * Y)
+        for m in range(M):
+            assert np.array_equal(o.gemm_fmt(fmt, W, X[m:m + 1])[0], Y[m])
+
+
+def pin_iq4_nl_is_an_iq4_xs_sub_block(o):
+    """An IQ4_XS sub-block whose scale d*(ls-32) is exact in fp16 (|ls-32| a
+    power of two) is an IQ4_NL block with that d and the same 16 nibble bytes
+    (the engine log's batched-kernel section: same block geometry and the
+    same kvalues lookup, only the scale is stored differently).  The IQ4_NL
+    matrix repacked from IQ4_XS must give the IQ4_XS oracle's output bit for
+    bit, tying the new format to the already pinned IQ4_XS decode."""
+    rng = np.random.default_rng(43)
+    N, K, M = 6, 768, 4
+    d_bits, _, codes = random_fields(rng, N * K // 256)
+    ls = rng.choice([32 - 32, 32 - 16, 32 - 8, 32 - 4, 32 - 2, 32 - 1, 33, 34, 36, 40, 48], size=(len(d_bits), 8))
+    Wxs, Vxs = build_matrix(d_bits, ls, codes, N, K)
+    Wnl = np.zeros((N, K // 32 * 18), dtype=np.uint8)
+    nb = K // 256
+    for n in range(N):
+        for j in range(nb):
+            i = n * nb + j
+            d = np.array(d_bits[i], dtype=np.uint16).view(np.float16).astype(np.float64)
+            for b in range(8):
+                db = np.float16(d * (ls[i, b] - 32))
+                assert float(db) == d * (ls[i, b] - 32)          # exact in fp16
+                off = (8 * j + b) * 18
+                Wnl[n, off:off + 18] = encode_block18(int(np.array(db).view(np.uint16)),
+                                                      codes[i][32 * b:32 * b + 32])
+    assert np.array_equal(o.dequantize_fmt(FMT_IQ4_NL, Wnl, K), Vxs)
+    X = rng.standard_normal((M, K)).astype(np.float32)
+    Xq = o.quantize_q8_1(X)
+    assert np.array_equal(o.gemm_fmt_q8_1(FMT_IQ4_NL, Wnl, Xq, K), o.gemm_q8_1(Wxs, Xq, K))
+    assert np.array_equal(o.gemm_fmt_q8_1(FMT_IQ4_XS, Wxs, Xq, K), o.gemm_q8_1(Wxs, Xq, K))
+
+
+B18_PINS = (pin_b18_handworked, pin_b18_random_blocks, pin_b18_gemm_exact, pin_b18_closed_forms,
+            pin_b18_invariants, pin_iq4_nl_is_an_iq4_xs_sub_block)
+
 ALL_PINS = (pin_half_decode, pin_half_encode, pin_bf16, pin_codebook, pin_handworked_block,
             pin_random_blocks, pin_q8_1_handworked, pin_q8_1_ieee,
             pin_q8_1_division_not_reciprocal, pin_gemm_exact, pin_gemm_closed_forms,
-            pin_gemm_invariants, pin_gemm_bf16)
+            pin_gemm_invariants, pin_gemm_bf16) + B18_PINS

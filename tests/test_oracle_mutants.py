@@ -52,6 +52,25 @@ MUTANTS = {
     "bf16 gemm drops activation rounding": (
         "double x = oracle_bf16_to_double(\n                    oracle_double_to_bf16(dx * (double)(int8_t)xb[4 + k % ORACLE_SB]));",
         "double x = dx * (double)(int8_t)xb[4 + k % ORACLE_SB];"),
+    # IQ4_NL and Q4_0 (18-byte blocks)
+    "b18 nibble order swapped": ("int c = t < 16 ? (byte & 15) : (byte >> 4);",
+                                 "int c = t < 16 ? (byte >> 4) : (byte & 15);"),
+    "q4_0 offset 7": ("return fmt == ORACLE_FMT_IQ4_NL ? ORACLE_KV[c] : c - 8;",
+                      "return fmt == ORACLE_FMT_IQ4_NL ? ORACLE_KV[c] : c - 7;"),
+    "iq4_nl and q4_0 values swapped": ("return fmt == ORACLE_FMT_IQ4_NL ? ORACLE_KV[c] : c - 8;",
+                                       "return fmt == ORACLE_FMT_Q4_0 ? ORACLE_KV[c] : c - 8;"),
+    "b18 index bytes start at 0": ("uint8_t byte = blk[2 + (t % 16)];", "uint8_t byte = blk[(t % 16)];"),
+    "b18 scale from the last two bytes": ("return oracle_half_to_double((uint16_t)(blk[0] | (blk[1] << 8)));\n}\n\n/* Bytes",
+                                          "return oracle_half_to_double((uint16_t)(blk[16] | (blk[17] << 8)));\n}\n\n/* Bytes"),
+    "b18 gemm block stride 16": ("const uint8_t *blk = W + n * rb + j * ORACLE_B18;",
+                                 "const uint8_t *blk = W + n * rb + j * 16;"),
+    "b18 gemm activation block of the next weight block": (
+        "const uint8_t *xq = Xq + (m * nblk + j) * ORACLE_XBLK;",
+        "const uint8_t *xq = Xq + (m * nblk + (j + 1) % nblk) * ORACLE_XBLK;"),
+    "b18 dequant block stride 16": ("const uint8_t *blk = W + n * rb + (k / ORACLE_SB) * ORACLE_B18;",
+                                    "const uint8_t *blk = W + n * rb + (k / ORACLE_SB) * 16;"),
+    "b18 gemm drops the weight scale": ("sum += scale18(blk) * d_x * (double)dot;", "sum += d_x * (double)dot;"),
+    "b18 row bytes of 16 per block": ("return K / ORACLE_SB * ORACLE_B18;", "return K / ORACLE_SB * 16;"),
 }
 
 # one mutant above needs a second edit to take effect
@@ -67,7 +86,7 @@ def _run_pins(o):
     for pin in oracle_pins.ALL_PINS:
         try:
             pin(o)
-        except AssertionError:
+        except Exception:          # a mismatch, or a mutant whose output cannot even be read
             failed.append(pin.__name__)
     return failed
 
