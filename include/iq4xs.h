@@ -75,6 +75,21 @@ extern "C" {
                                  rounds W~ and X~ to 8 significant bits)                 */
 #define IQ4XS_NUM_PATHS 4
 
+/* ---- weight formats (the iq4xs_*_fmt entry points) ----
+ * "V100TPS engine log", batched IQ4_XS kernel section: an IQ4_XS sub-block of
+ * 32 weights has the geometry of a whole Q4_0 block (16 bytes of nibbles, low
+ * nibbles elements 0-15, high nibbles 16-31); Q4_0 keeps one scale d per block
+ * and the value q-8, IQ4_XS stores d*(ls-32) per sub-block and looks the value
+ * up in kvalues_iq4nl.  "SGLang MoE port thread", the passage that retracts a
+ * TP block-alignment conclusion: an IQ4_NL block is 32 values in 18 bytes.
+ * Byte order (GGUF; convention): IQ4_NL and Q4_0 blocks are {fp16 d, u8 qs[16]}
+ * with the IQ4_XS sub-block's nibble placement; a row of K weights is K/32
+ * consecutive blocks.  The kernels work in units of 256 weights, so K must be
+ * a multiple of 256 for every format. */
+#define IQ4XS_FMT_IQ4_XS 0 /* 136-byte super-blocks of 256 weights (above)            */
+#define IQ4XS_FMT_IQ4_NL 1 /* 18-byte blocks of 32 weights, weight d*kvalues_iq4nl[q] */
+#define IQ4XS_FMT_Q4_0 2   /* 18-byte blocks of 32 weights, weight d*(q-8)             */
+
 /* Sizes in bytes of an IQ4_XS matrix [N][K] and of a Q8_1 matrix [M][K]:
  * N*(K/256)*136 and M*(K/32)*36.  The "V100TPS engine log", section on the
  * batched IQ4_XS kernel, names both formats and the 32-weight sub-block with
@@ -133,6 +148,25 @@ int iq4xs_gemm_ws(const void *W, const float *X, float *Y, int64_t M, int64_t N,
 #define IQ4XS_STATIC_SCRATCH_BYTES (64u << 20)
 int iq4xs_gemm_noalloc(const void *W, const float *X, float *Y, int64_t M, int64_t N, int64_t K,
                        int path, void *stream);
+
+/* The matmul for weights in any of the three formats: W is [N] rows of
+ * iq4xs_weight_bytes_fmt(fmt, 1, K) bytes (caller-owned, 16-byte aligned),
+ * X fp32 [M][K], Y fp32 [M][N] (overwritten).  Arithmetic as iq4xs_gemm:
+ * X quantized to Q8_1, per 32-weight block the exact integer dot of the
+ * block's values with the Q8_1 values, scaled in fp32 by d (or d*(ls-32))
+ * and d_x; the result is within the same per-row bound of the oracle.
+ * `path`: AUTO (the measured table's GEMV / MMQ bands; its DEQ_BF16 bands
+ * apply to IQ4_XS only), GEMV (M <= 4) or MMQ; DEQ_BF16 is EPATH for IQ4_NL
+ * and Q4_0, and so is MMQ for a matrix of 2 GiB or more in those formats
+ * (the fallback kernel for such sizes reads IQ4_XS only).  `workspace` as in
+ * iq4xs_gemm_ws (at least iq4xs_gemm_fmt_workspace_bytes bytes, 256-byte
+ * aligned; then nothing is allocated), or NULL for stream-ordered scratch.
+ * EINVAL for an unknown `fmt` and as iq4xs_gemm_path otherwise.
+ * iq4xs_weight_bytes_fmt: N*(K/256)*136 (IQ4_XS) or N*(K/32)*18. */
+int iq4xs_weight_bytes_fmt(int fmt, int64_t N, int64_t K, size_t *out);
+int iq4xs_gemm_fmt_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, int path, size_t *out);
+int iq4xs_gemm_fmt(int fmt, const void *W, const float *X, float *Y, int64_t M, int64_t N, int64_t K,
+                   int path, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Y = X * W^T from activations already quantized to Q8_1 (Xq [M][K/32]
  * blocks of 36 bytes, layout above; caller-owned, 4-byte aligned, read only).

@@ -27,11 +27,15 @@ LIB_PATH = os.path.join(_HERE, "libiq4xs.so")
 OK, EINVAL, EALIGN, EDEVICE, ETABLE, ELAUNCH, ENOMEM, EPATH = 0, -1, -2, -3, -4, -5, -6, -7
 PATH_AUTO, PATH_GEMV, PATH_MMQ, PATH_DEQ_BF16 = 0, 1, 2, 3
 PATHS = {"AUTO": PATH_AUTO, "GEMV": PATH_GEMV, "MMQ": PATH_MMQ, "DEQ_BF16": PATH_DEQ_BF16}
+FMT_IQ4_XS, FMT_IQ4_NL, FMT_Q4_0 = 0, 1, 2
+FMTS = {"IQ4_XS": FMT_IQ4_XS, "IQ4_NL": FMT_IQ4_NL, "Q4_0": FMT_Q4_0}
+_UNIT_BYTES = {FMT_IQ4_XS: 136, FMT_IQ4_NL: 144, FMT_Q4_0: 144}    # bytes per 256 weights
 Y_ZEROED = 0x100     # gemm_act hint: Y already holds zeros
 
 EXPORTS = ("iq4xs_weight_bytes", "iq4xs_q8_1_bytes", "iq4xs_init", "iq4xs_quantize_q8_1",
            "iq4xs_gemm", "iq4xs_gemm_path", "iq4xs_gemm_workspace_bytes", "iq4xs_gemm_ws",
-           "iq4xs_gemm_noalloc", "iq4xs_gemm_q8_1", "iq4xs_act_bytes",
+           "iq4xs_gemm_noalloc", "iq4xs_weight_bytes_fmt", "iq4xs_gemm_fmt_workspace_bytes",
+           "iq4xs_gemm_fmt", "iq4xs_gemm_q8_1", "iq4xs_act_bytes",
            "iq4xs_prepare_act", "iq4xs_gemm_act", "iq4xs_gemm_group_workspace_bytes", "iq4xs_gemm_group",
            "iq4xs_dequantize_bf16",
            "iq4xs_dispatch", "iq4xs_load_dispatch_table", "iq4xs_path_name", "iq4xs_last_error")
@@ -59,6 +63,9 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "iq4xs_gemm_workspace_bytes": [i64, i64, i64, i32, sz],
         "iq4xs_gemm_ws": [p, p, p, i64, i64, i64, i32, p, ctypes.c_size_t, p],
         "iq4xs_gemm_noalloc": [p, p, p, i64, i64, i64, i32, p],
+        "iq4xs_weight_bytes_fmt": [i32, i64, i64, sz],
+        "iq4xs_gemm_fmt_workspace_bytes": [i32, i64, i64, i64, i32, sz],
+        "iq4xs_gemm_fmt": [i32, p, p, p, i64, i64, i64, i32, p, ctypes.c_size_t, p],
         "iq4xs_gemm_q8_1": [p, p, p, i64, i64, i64, i32, p],
         "iq4xs_act_bytes": [i64, i64, sz],
         "iq4xs_prepare_act": [p, p, i64, i64, p],
@@ -155,13 +162,16 @@ def _mk(t, name: str) -> tuple:
     return int(t.shape[0]), int(t.shape[1])
 
 
-def _wrows(W, K: int) -> int:
-    """N of an IQ4_XS weight tensor [N, K/256*136] (K a multiple of 256)."""
+def _wrows(W, K: int, fmt: int = FMT_IQ4_XS) -> int:
+    """N of a weight tensor [N, K/256 * unit bytes] (K a multiple of 256; a
+    unit of 256 weights is 136 bytes in IQ4_XS, 144 in IQ4_NL and Q4_0)."""
     if K % 256:
         raise ValueError(f"K must be a multiple of 256, got {K}")
+    if fmt not in _UNIT_BYTES:
+        raise ValueError(f"unknown weight format {fmt}")
     if not isinstance(W, torch.Tensor) or W.dim() != 2:
-        raise ValueError("W must be a 2-D tensor [N, K/256*136]")
-    _shape(W, "W", (W.shape[0], K // 256 * 136))
+        raise ValueError(f"W must be a 2-D tensor [N, {K // 256 * _UNIT_BYTES[fmt]}]")
+    _shape(W, "W", (W.shape[0], K // 256 * _UNIT_BYTES[fmt]))
     return int(W.shape[0])
 
 
@@ -234,6 +244,36 @@ def gemm_noalloc(W: torch.Tensor, X: torch.Tensor, out: torch.Tensor, path: int 
     with _on(X):
         check(_L().iq4xs_gemm_noalloc(_dev(W, torch.uint8, "W"), _dev(X, torch.float32, "X"),
                                      _dev(out, torch.float32, "Y"), M, N, K, path, _stream(X)))
+    return out
+
+
+def weight_bytes_fmt(fmt: int, N: int, K: int) -> int:
+    out = ctypes.c_size_t()
+    check(_L().iq4xs_weight_bytes_fmt(fmt, N, K, ctypes.byref(out)))
+    return out.value
+
+
+def fmt_workspace_bytes(fmt: int, M: int, N: int, K: int, path: int = PATH_AUTO) -> int:
+    out = ctypes.c_size_t()
+    check(_L().iq4xs_gemm_fmt_workspace_bytes(fmt, M, N, K, path, ctypes.byref(out)))
+    return out.value
+
+
+def gemm_fmt(W: torch.Tensor, X: torch.Tensor, fmt: int, path: int = PATH_AUTO,
+             out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Y[M, N] = X[M, K] * W[N, K]^T for W in IQ4_XS, IQ4_NL or Q4_0 (uint8
+    [N, K/256 * 136] or [N, K/32 * 18]); X quantized to Q8_1 on the device."""
+    M, K = _mk(X, "X")
+    N = _wrows(W, K, fmt)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=X.device)
+    _shape(out, "Y", (M, N))
+    _one_device(W, X, out, workspace)
+    with _on(X):
+        ws = _dev(workspace, torch.uint8, "workspace") if workspace is not None else None
+        wsb = workspace.numel() if workspace is not None else 0
+        check(_L().iq4xs_gemm_fmt(fmt, _dev(W, torch.uint8, "W"), _dev(X, torch.float32, "X"),
+                                 _dev(out, torch.float32, "Y"), M, N, K, path, ws, wsb, _stream(X)))
     return out
 
 

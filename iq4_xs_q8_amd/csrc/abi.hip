@@ -273,10 +273,12 @@ int launch_err(hipError_t e, const char *what)
     return fail(IQ4XS_ELAUNCH, "%s: %s", what, hipGetErrorString(e));
 }
 
-int resolve_path(int path, int64_t M, int64_t N, int64_t K, int *out)
+int resolve_path(int path, int64_t M, int64_t N, int64_t K, int *out, int fmt = FMT_IQ4_XS)
 {
     if (path < 0 || path >= IQ4XS_NUM_PATHS)
         return fail(IQ4XS_EINVAL, "unknown path %d", path);
+    if (fmt != FMT_IQ4_XS && path == IQ4XS_PATH_DEQ_BF16)
+        return fail(IQ4XS_EPATH, "the bf16 path reads IQ4_XS weights only");
     ensure_init();
     if (path == IQ4XS_PATH_AUTO) {
         int st = ensure_init();
@@ -284,7 +286,9 @@ int resolve_path(int path, int64_t M, int64_t N, int64_t K, int *out)
             return fail(st, "dispatch table not loaded: %s", g_err.c_str());
         {
             std::lock_guard<std::mutex> lk(g_mu);
-            path = table_lookup(g_table, M, N, K, g_cfg.allow_bf16);
+            // (the bands were measured on IQ4_XS; for the 32-weight formats the
+            // same GEMV / MMQ kernels run, and bf16 bands do not apply)
+            path = table_lookup(g_table, M, N, K, g_cfg.allow_bf16 && fmt == FMT_IQ4_XS);
         }
         if (!path)
             return fail(IQ4XS_EPATH, "no dispatch band covers M=%lld N=%lld K=%lld", (long long)M,
@@ -301,11 +305,11 @@ int resolve_path(int path, int64_t M, int64_t N, int64_t K, int *out)
 
 // Scratch a path needs: activation planes (+ the split-K partial sums of
 // MMQ), or for DEQ_BF16 the bf16 activations and weights.
-size_t workspace_need(int path, int64_t M, int64_t N, int64_t K)
+size_t workspace_need(int path, int64_t M, int64_t N, int64_t K, int fmt = FMT_IQ4_XS)
 {
     if (path == IQ4XS_PATH_GEMV || path == IQ4XS_PATH_MMQ)
         return (size_t)round_up((int64_t)xplanes_bytes(M, K), 256) +
-               (path == IQ4XS_PATH_MMQ ? mmq_plan(M, N, K).workspace_bytes : 0);
+               (path == IQ4XS_PATH_MMQ ? mmq_plan(M, N, K, fmt).workspace_bytes : 0);
     return (size_t)round_up(M * K * 2, 256) + (size_t)(N * K * 2);
 }
 
@@ -314,20 +318,23 @@ size_t workspace_need(int path, int64_t M, int64_t N, int64_t K)
 // device's default pool, stream-ordered; otherwise ws (ws_bytes, 256-byte
 // aligned) is used and nothing is allocated.
 int run_gemm(const void *W, const float *X, const void *Xq, float *Y, int64_t M, int64_t N, int64_t K,
-             int path, void *ws, size_t ws_bytes, hipStream_t s)
+             int path, void *ws, size_t ws_bytes, hipStream_t s, int fmt = FMT_IQ4_XS)
 {
     const int requested = path;
-    int st = resolve_path(path, M, N, K, &path);
+    int st = resolve_path(path, M, N, K, &path, fmt);
     if (st != IQ4XS_OK)
         return st;
-    const size_t need = workspace_need(path, M, N, K);
+    if (path == IQ4XS_PATH_MMQ && !mmq_plan(M, N, K, fmt).ok)
+        return fail(IQ4XS_EPATH, "no MMQ kernel takes a %s matrix of %lld x %lld (2 GiB or more)",
+                    fmt == FMT_IQ4_NL ? "IQ4_NL" : "Q4_0", (long long)N, (long long)K);
+    const size_t need = workspace_need(path, M, N, K, fmt);
     if (ws != nullptr) {
         if (!aligned(ws, 256))
             return fail(IQ4XS_EALIGN, "workspace must be 256-byte aligned");
         if (ws_bytes < need)
             return fail(IQ4XS_EINVAL, "workspace of %zu bytes, %zu needed", ws_bytes, need);
         if (overlaps(ws, ws_bytes, Y, (size_t)(M * N * 4)) ||
-            overlaps(ws, ws_bytes, W, (size_t)(N * (K / QK) * WBLK)) ||
+            overlaps(ws, ws_bytes, W, (size_t)(N * (K / QK) * sblk_bytes(fmt))) ||
             (X && overlaps(ws, ws_bytes, X, (size_t)(M * K * 4))) ||
             (Xq && overlaps(ws, ws_bytes, Xq, (size_t)(M * (K / SB) * XBLK))))
             return fail(IQ4XS_EINVAL, "workspace overlaps W, X or Y");
@@ -350,15 +357,15 @@ int run_gemm(const void *W, const float *X, const void *Xq, float *Y, int64_t M,
         const size_t pbytes = (size_t)round_up((int64_t)xplanes_bytes(M, K), 256);
         const XPlanes xp = xplanes_at(base, M, K);
         // a matmul that adds partial tiles into Y gets it zeroed by the quantizer
-        const bool zero = path == IQ4XS_PATH_MMQ && mmq_plan(M, N, K).zero_y;
+        const bool zero = path == IQ4XS_PATH_MMQ && mmq_plan(M, N, K, fmt).zero_y;
         float *yz = zero ? Y : nullptr;
         const int64_t nz = zero ? M * N : 0;
         hipError_t e = X ? launch_quantize(X, nullptr, &xp, nullptr, M, K, s, yz, nz)
                          : launch_q8_1_convert(Xq, &xp, nullptr, M, K, s, yz, nz);
         if ((st = launch_err(e, "quantize")) != IQ4XS_OK)
             return st;
-        e = path == IQ4XS_PATH_GEMV ? launch_gemv(W, xp, Y, N, s)
-                                    : launch_mmq(W, xp, Y, N, base + pbytes, zero, s);
+        e = path == IQ4XS_PATH_GEMV ? launch_gemv(W, xp, Y, N, s, fmt)
+                                    : launch_mmq(W, xp, Y, N, base + pbytes, zero, s, fmt);
         return launch_err(e, path_name(path));
     }
     // DEQ_BF16: X~ bf16 [M][K], then W~ bf16 [N][K] (256-byte aligned)
@@ -489,6 +496,53 @@ int iq4xs_gemm_noalloc(const void *W, const float *X, float *Y, int64_t M, int64
     if ((st = static_scratch(&ws)) != IQ4XS_OK)
         return st;
     return run_gemm(W, X, nullptr, Y, M, N, K, path, ws, IQ4XS_STATIC_SCRATCH_BYTES, (hipStream_t)stream);
+}
+
+static bool fmt_ok(int fmt) { return fmt == FMT_IQ4_XS || fmt == FMT_IQ4_NL || fmt == FMT_Q4_0; }
+
+int iq4xs_weight_bytes_fmt(int fmt, int64_t N, int64_t K, size_t *out)
+{
+    if (!out)
+        return fail(IQ4XS_EINVAL, "null output pointer");
+    if (!fmt_ok(fmt))
+        return fail(IQ4XS_EINVAL, "unknown weight format %d", fmt);
+    if (N < 1 || K < QK || K % QK || N > (1LL << 40) || K > (1LL << 40))
+        return fail(IQ4XS_EINVAL, "need N >= 1 and K a positive multiple of 256");
+    *out = (size_t)N * (size_t)(K / QK) * sblk_bytes(fmt);
+    return IQ4XS_OK;
+}
+
+int iq4xs_gemm_fmt_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, int path, size_t *out)
+{
+    if (!out)
+        return fail(IQ4XS_EINVAL, "null output pointer");
+    if (!fmt_ok(fmt))
+        return fail(IQ4XS_EINVAL, "unknown weight format %d", fmt);
+    int st = check_dims(M, N, K);
+    if (st != IQ4XS_OK)
+        return st;
+    if ((st = resolve_path(path, M, N, K, &path, fmt)) != IQ4XS_OK)
+        return st;
+    *out = workspace_need(path, M, N, K, fmt);
+    return IQ4XS_OK;
+}
+
+int iq4xs_gemm_fmt(int fmt, const void *W, const float *X, float *Y, int64_t M, int64_t N, int64_t K, int path,
+                   void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!fmt_ok(fmt))
+        return fail(IQ4XS_EINVAL, "unknown weight format %d", fmt);
+    if (!W || !X || !Y)
+        return fail(IQ4XS_EINVAL, "null pointer");
+    int st = check_dims(M, N, K);
+    if (st != IQ4XS_OK)
+        return st;
+    if (!aligned(W, 16) || !aligned(X, 16) || !aligned(Y, 16))
+        return fail(IQ4XS_EALIGN, "W, X and Y must be 16-byte aligned");
+    const size_t yb = (size_t)(M * N * 4);
+    if (overlaps(Y, yb, W, (size_t)(N * (K / QK) * sblk_bytes(fmt))) || overlaps(Y, yb, X, (size_t)(M * K * 4)))
+        return fail(IQ4XS_EINVAL, "Y overlaps an input");
+    return run_gemm(W, X, nullptr, Y, M, N, K, path, workspace, workspace_bytes, (hipStream_t)stream, fmt);
 }
 
 int iq4xs_gemm(const void *W, const float *X, float *Y, int64_t M, int64_t N, int64_t K, void *stream)

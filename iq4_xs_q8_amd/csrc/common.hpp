@@ -29,6 +29,20 @@ static_assert(2 + 2 + SB == XBLK, "Q8_1 block size");
 // so the block scales of four consecutive rows are one aligned float4.
 constexpr int MPAD = 4;
 
+// ---- weight formats ---------------------------------------------------------
+// IQ4_XS: 136-byte super-blocks of 256 weights (above).  IQ4_NL and Q4_0: a
+// block of 32 weights is 18 bytes {fp16 d, u8 qs[16]} with the nibble layout
+// of an IQ4_XS sub-block ("V100TPS engine log", batched IQ4_XS kernel
+// section: a Q4_0 block has exactly that geometry, one scale d per block and
+// the value q-8; "SGLang MoE port thread": an IQ4_NL block is 32 values in 18
+// bytes, its values the kvalues_iq4nl codebook).  The kernels walk every
+// format in units of 256 weights: eight 18-byte blocks make a 144-byte unit,
+// which (unlike 136 bytes) is always 16-byte aligned.
+enum : int { FMT_IQ4_XS = 0, FMT_IQ4_NL = 1, FMT_Q4_0 = 2, NUM_FMTS = 3 };
+constexpr int B18 = 18;   // bytes per IQ4_NL / Q4_0 block
+constexpr int sblk_bytes(int f) { return f == FMT_IQ4_XS ? 136 : 8 * B18; }
+static_assert(sblk_bytes(FMT_IQ4_NL) % 16 == 0, "144-byte units stay 16-byte aligned");
+
 // ---- kvalues_iq4nl packed for byte-permute lookups -----------------------
 constexpr int8_t KVALUES[16] = {-127, -104, -83, -65, -49, -35, -22, -10,
                                 1,    13,   25,  38,  53,  69,  89,  113};
@@ -41,16 +55,35 @@ constexpr uint32_t kv_word(int i)
 constexpr uint32_t KV0 = kv_word(0), KV1 = kv_word(1), KV2 = kv_word(2), KV3 = kv_word(3);
 static_assert(KV0 == 0xBFAD9881u && KV3 == 0x71594535u, "codebook packing");
 
-// Four 4-bit indices -> four int8 kvalues with byte permutes.  v_perm_b32
+// Q4_0's values q-8 as a 16-entry table of the same kind.
+constexpr int8_t Q40VALUES[16] = {-8, -7, -6, -5, -4, -3, -2, -1, 0, 1, 2, 3, 4, 5, 6, 7};
+
+// The 16-entry value table of a format, packed four bytes per word.
+template <int F>
+struct Values {
+    static constexpr const int8_t *t = F == FMT_Q4_0 ? Q40VALUES : KVALUES;
+    static constexpr uint32_t w(int i)
+    {
+        return (uint32_t)(uint8_t)t[4 * i] | ((uint32_t)(uint8_t)t[4 * i + 1] << 8) |
+               ((uint32_t)(uint8_t)t[4 * i + 2] << 16) | ((uint32_t)(uint8_t)t[4 * i + 3] << 24);
+    }
+    static constexpr uint32_t W0 = w(0), W1 = w(1), W2 = w(2), W3 = w(3);
+};
+static_assert(Values<FMT_IQ4_XS>::W0 == KV0 && Values<FMT_IQ4_NL>::W3 == KV3, "codebook packing");
+static_assert(Values<FMT_Q4_0>::W0 == 0xFBFAF9F8u && Values<FMT_Q4_0>::W3 == 0x07060504u, "q-8 packing");
+
+// Four 4-bit indices -> four int8 values with byte permutes.  v_perm_b32
 // picks byte s (0..7) of {hi:lo}, gives 0x00 for selector 5 of {0:0} and
-// 0xFF for any selector >= 13: indices 0-7 come from {KV1:KV0}, 8-15 from
-// {KV3:KV2}, and a mask built from bit 3 (selector 5 or 13) chooses per byte.
+// 0xFF for any selector >= 13: indices 0-7 come from {W1:W0}, 8-15 from
+// {W3:W2}, and a mask built from bit 3 (selector 5 or 13) chooses per byte.
 // The indices are bits 0-3 of each byte of t; bits 4-7 are ignored.
+template <int F = FMT_IQ4_XS>
 __device__ __forceinline__ uint32_t lut4(uint32_t t)
 {
+    using V = Values<F>;
     const uint32_t s = t & 0x07070707u;
-    const uint32_t a = __builtin_amdgcn_perm(KV1, KV0, s);
-    const uint32_t b = __builtin_amdgcn_perm(KV3, KV2, s);
+    const uint32_t a = __builtin_amdgcn_perm(V::W1, V::W0, s);
+    const uint32_t b = __builtin_amdgcn_perm(V::W3, V::W2, s);
     const uint32_t m = __builtin_amdgcn_perm(0u, 0u, (t & 0x08080808u) | 0x05050505u);
     return (m & b) | (~m & a);
 }
@@ -58,12 +91,13 @@ __device__ __forceinline__ uint32_t lut4(uint32_t t)
 // 8 index bytes (2 dwords of qs) -> 16 int8 weights in "chunk" order:
 // out[0..1] = low nibbles (elements j..j+7), out[2..3] = high nibbles
 // (elements 16+j..16+j+7) of the same bytes.
+template <int F = FMT_IQ4_XS>
 __device__ __forceinline__ void expand8(uint32_t w0, uint32_t w1, uint32_t out[4])
 {
-    out[0] = lut4(w0);
-    out[1] = lut4(w1);
-    out[2] = lut4(w0 >> 4);
-    out[3] = lut4(w1 >> 4);
+    out[0] = lut4<F>(w0);
+    out[1] = lut4<F>(w1);
+    out[2] = lut4<F>(w0 >> 4);
+    out[3] = lut4<F>(w1 >> 4);
 }
 
 // Split codebook: kvalues[x] = KL[x & 7] + kh(x ^ 13), where kh(s) is what
@@ -76,40 +110,55 @@ __device__ __forceinline__ void expand8(uint32_t w0, uint32_t w1, uint32_t out[4
 // op each: no per-byte select between two half-tables.
 constexpr int8_t KL[8] = {-126, -104, -82, -64, -49, -35, -22, -10};
 constexpr int8_t KH[8] = {104, 102, 123, 111, 117, 127, 102, 107};
+// The same split of Q4_0's q-8 (all KH parts positive, so selectors 8-11
+// give 0 and x = 0, 2, 3 get the -1 that KL absorbs).
+constexpr int8_t QL[8] = {-7, -7, -5, -4, -4, -3, -2, -1};
+constexpr int8_t QH[8] = {8, 8, 8, 8, 8, 7, 7, 7};
 constexpr int perm_byte(const int8_t *t8, int sel)
 {
     return sel >= 13 ? -1 : sel == 12 ? 0 : sel >= 8 ? (t8[2 * (sel - 8) + 1] < 0 ? -1 : 0) : t8[sel];
 }
-constexpr bool split_codebook_ok()
+constexpr bool split_ok(const int8_t *lo, const int8_t *hi, const int8_t *want)
 {
     for (int x = 0; x < 16; x++)
-        if (KL[x & 7] + perm_byte(KH, x ^ 13) != KVALUES[x])
+        if (lo[x & 7] + perm_byte(hi, x ^ 13) != want[x])
             return false;
     return true;
 }
-static_assert(split_codebook_ok(), "split codebook");
+static_assert(split_ok(KL, KH, KVALUES), "split codebook");
+static_assert(split_ok(QL, QH, Q40VALUES), "split q-8");
 constexpr uint32_t word4(const int8_t *b)
 {
     return (uint32_t)(uint8_t)b[0] | ((uint32_t)(uint8_t)b[1] << 8) | ((uint32_t)(uint8_t)b[2] << 16) |
            ((uint32_t)(uint8_t)b[3] << 24);
 }
 constexpr uint32_t KL0 = word4(KL), KL1 = word4(KL + 4), KH0 = word4(KH), KH1 = word4(KH + 4);
+template <int F>
+struct Split {
+    static constexpr const int8_t *lo = F == FMT_Q4_0 ? QL : KL;
+    static constexpr const int8_t *hi = F == FMT_Q4_0 ? QH : KH;
+    static constexpr uint32_t L0 = word4(lo), L1 = word4(lo + 4), H0 = word4(hi), H1 = word4(hi + 4);
+};
+static_assert(Split<FMT_IQ4_NL>::L0 == KL0 && Split<FMT_IQ4_XS>::H1 == KH1, "split packing");
 
 // Four indices (bits 0-3 of each byte of t; bits 4-7 ignored) -> the two
-// int8 parts of their codebook values.
+// int8 parts of their values.
+template <int F = FMT_IQ4_XS>
 __device__ __forceinline__ void lut4_split(uint32_t t, uint32_t &lo, uint32_t &hi)
 {
-    lo = __builtin_amdgcn_perm(KL1, KL0, t & 0x07070707u);
-    hi = __builtin_amdgcn_perm(KH1, KH0, (t & 0x0F0F0F0Fu) ^ 0x0D0D0D0Du);
+    using S = Split<F>;
+    lo = __builtin_amdgcn_perm(S::L1, S::L0, t & 0x07070707u);
+    hi = __builtin_amdgcn_perm(S::H1, S::H0, (t & 0x0F0F0F0Fu) ^ 0x0D0D0D0Du);
 }
 
 // expand8 as two parts: a[i] + b[i] (bytewise, as integers) = out[i] of expand8.
+template <int F = FMT_IQ4_XS>
 __device__ __forceinline__ void expand8_split(uint32_t w0, uint32_t w1, uint32_t a[4], uint32_t b[4])
 {
-    lut4_split(w0, a[0], b[0]);
-    lut4_split(w1, a[1], b[1]);
-    lut4_split(w0 >> 4, a[2], b[2]);
-    lut4_split(w1 >> 4, a[3], b[3]);
+    lut4_split<F>(w0, a[0], b[0]);
+    lut4_split<F>(w1, a[1], b[1]);
+    lut4_split<F>(w0 >> 4, a[2], b[2]);
+    lut4_split<F>(w1 >> 4, a[3], b[3]);
 }
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t h16)
@@ -126,6 +175,61 @@ __device__ __forceinline__ float sub_scale(uint32_t h0, uint32_t h1, int b)
     const uint32_t hi2 = (h0 >> (16 + 2 * b)) & 3u;       // bits 2b..2b+1 of scales_h
     const int ls = (int)(lo4 | (hi2 << 4));
     return half_bits_to_float(h0 & 0xFFFFu) * (float)(ls - 32);
+}
+
+// ---- one 256-weight unit of any format -------------------------------------
+// `u` points at the unit (4-byte aligned): an IQ4_XS super-block, or eight
+// IQ4_NL / Q4_0 blocks.  The 18-byte blocks put d and the index bytes at
+// offsets that are only 2-byte aligned, so they are read as aligned dwords
+// and shifted into place (v_alignbit), and nothing past the unit is read.
+
+// Scale of sub-block b (0..7): d*(ls_b - 32), or the d of block b, in two
+// steps so that the read can be issued with other loads and decoded later:
+// the raw bytes (IQ4_XS: the 8 header bytes; else the dword holding d_b), then
+// the value.  live == false gives 0 (a sub-block that only pads a group).
+template <int F>
+__device__ __forceinline__ uint2 unit_scale_raw(const char *u, int b)
+{
+    if constexpr (F == FMT_IQ4_XS)
+        return *reinterpret_cast<const uint2 *>(u);
+    else
+        return make_uint2(*reinterpret_cast<const uint32_t *>(u + ((B18 * b) & ~3)), 0u);
+}
+template <int F>
+__device__ __forceinline__ float unit_scale_dec(uint2 raw, int b, bool live)
+{
+    if constexpr (F == FMT_IQ4_XS) {
+        return sub_scale(live ? raw.x : 0u, raw.y, b);
+    } else {
+        // d_b sits at byte 18b: the low half of its dword for even b, the
+        // high half of the dword before for odd b
+        const uint32_t bits = (b & 1) ? (raw.x >> 16) : (raw.x & 0xFFFFu);
+        return live ? half_bits_to_float(bits) : 0.0f;
+    }
+}
+template <int F>
+__device__ __forceinline__ float unit_scale(const char *u, int b, bool live)
+{
+    return unit_scale_dec<F>(unit_scale_raw<F>(u, b), b, live);
+}
+
+// The 8 index bytes qs[8h..8h+7] of sub-block b (16 weights: elements
+// 8h..8h+7 in the low nibbles, 16+8h..16+8h+7 in the high ones).
+template <int F>
+__device__ __forceinline__ uint2 unit_qs(const char *u, int b, int h)
+{
+    if constexpr (F == FMT_IQ4_XS) {
+        return *reinterpret_cast<const uint2 *>(u + QS_OFF + 16 * b + 8 * h);
+    } else {
+        const int o = B18 * b + 2 + 8 * h;                     // 0 or 2 mod 4
+        const uint32_t *w = reinterpret_cast<const uint32_t *>(u + (o & ~3));
+        const uint32_t w0 = w[0], w1 = w[1];
+        if (o & 2) {                                           // bytes o..o+7 span three dwords
+            const uint32_t w2 = w[2];
+            return make_uint2(__builtin_amdgcn_alignbit(w1, w0, 16), __builtin_amdgcn_alignbit(w2, w1, 16));
+        }
+        return make_uint2(w0, w1);
+    }
 }
 
 // ---- internal activation planes ------------------------------------------
@@ -205,7 +309,8 @@ hipError_t launch_quantize(const float *X, void *Xq, const XPlanes *planes, uint
 hipError_t launch_q8_1_convert(const void *Xq, const XPlanes *planes, uint16_t *Xbf, int64_t M,
                               int64_t K, hipStream_t s, float *yz = nullptr, int64_t nz = 0);
 hipError_t launch_zero(float *y, int64_t n, hipStream_t s);
-hipError_t launch_gemv(const void *W, const XPlanes &x, float *Y, int64_t N, hipStream_t s);
+hipError_t launch_gemv(const void *W, const XPlanes &x, float *Y, int64_t N, hipStream_t s,
+                       int fmt = FMT_IQ4_XS);
 // MMQ work split for a shape: TM 32-row subtiles per wavefront, KW
 // wavefronts per workgroup and KS workgroups along K.  With KS > 1 the launch
 // needs a workspace of workspace_bytes (KS partial [M][N] tiles).
@@ -216,12 +321,13 @@ hipError_t launch_gemv(const void *W, const XPlanes &x, float *Y, int64_t N, hip
 struct MmvPlan {
     bool ok = false, zero_y = false;
     int grid = 0, live = 0;
+    int fmt = FMT_IQ4_XS;
 };
-MmvPlan mmv_plan(int64_t M, int64_t N, int64_t K, int cus);
+MmvPlan mmv_plan(int64_t M, int64_t N, int64_t K, int cus, int fmt = FMT_IQ4_XS);
 hipError_t launch_mmv(const void *W, const XPlanes &x, float *Y, int64_t N, const MmvPlan &p,
                       hipStream_t s);
 // The same over a group of matrices (one launch; zero_y: every y[g] zeroed).
-MmvPlan mmv_plan_group(int64_t M, const int64_t *N, int count, int64_t K, int cus);
+MmvPlan mmv_plan_group(int64_t M, const int64_t *N, int count, int64_t K, int cus, int fmt = FMT_IQ4_XS);
 MmvGroup mmv_group(const void *const *W, float *const *Y, const int64_t *N, int count);
 hipError_t launch_mmv_group(const MmvGroup &grp, const XPlanes &x, const MmvPlan &p, hipStream_t s);
 // Tile kernel for M > 32 (mmqt.hip): 128 x 128 tiles, runs of (tile, half
@@ -230,12 +336,14 @@ hipError_t launch_mmv_group(const MmvGroup &grp, const XPlanes &x, const MmvPlan
 struct MmqtPlan {
     bool ok = false, zero_y = false;    // zero_y: shared tiles add into a zeroed Y
     int grid = 0, mblocks = 0, bm = 0;
+    int fmt = FMT_IQ4_XS;
     size_t workspace_bytes = 0;         // else partial tiles in a workspace
 };
-MmqtPlan mmqt_plan(int64_t M, int64_t N, int64_t K, int cus);
+MmqtPlan mmqt_plan(int64_t M, int64_t N, int64_t K, int cus, int fmt = FMT_IQ4_XS);
 hipError_t launch_mmqt(const void *W, const XPlanes &x, float *Y, int64_t N, const MmqtPlan &p, void *workspace,
                        hipStream_t s);
 struct MmqPlan {
+    bool ok = true;            // false: no MMQ kernel takes this shape in this format
     int tm = 1, kw = 1, ks = 1;
     bool mmv = false;          // the streaming kernel runs (M <= 32)
     MmvPlan vp;
@@ -244,11 +352,14 @@ struct MmqPlan {
     bool zero_y = false;       // Y must hold zeros before the launch
     size_t workspace_bytes = 0;
 };
-MmqPlan mmq_plan(int64_t M, int64_t N, int64_t K);
+// The K-split fallback reads IQ4_XS only: for the other formats a shape
+// that neither the streaming nor the tile kernel takes (a weight matrix of
+// 2 GiB or more) has no MMQ plan (ok == false).
+MmqPlan mmq_plan(int64_t M, int64_t N, int64_t K, int fmt = FMT_IQ4_XS);
 // y_zeroed: the caller has already zeroed Y (else the launcher does it when
 // the plan needs it).
 hipError_t launch_mmq(const void *W, const XPlanes &x, float *Y, int64_t N, void *workspace,
-                      bool y_zeroed, hipStream_t s);
+                      bool y_zeroed, hipStream_t s, int fmt = FMT_IQ4_XS);
 hipError_t launch_dequant_bf16(const void *W, uint16_t *Wb, int64_t N, int64_t K, hipStream_t s);
 hipError_t launch_gemm_bf16(const uint16_t *Xb, const uint16_t *Wb, float *Y, int64_t M,
                             int64_t N, int64_t K, hipStream_t s);

@@ -31,11 +31,14 @@ __device__ __forceinline__ float wave_sum(float v)
     return v;
 }
 
-template <int M, int R, int U>
+// F: the weight format (its 256-weight unit is 136 or 144 bytes; the scale
+// and index bytes of sub-block b are read through unit_scale_raw / unit_qs).
+template <int M, int R, int U, int F>
 __global__ void __launch_bounds__(64 * GEMV_WAVES)
 k_gemv(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, const float *__restrict__ dp,
        float *__restrict__ Y, int64_t N, int64_t K, int64_t Mp)
 {
+    constexpr int UB = sblk_bytes(F);
     static_assert(M >= 1 && M <= GEMV_MAX_M, "GEMV handles 1..4 rows");
     const int lane = threadIdx.x & 63;
     const int64_t n0 = ((int64_t)blockIdx.x * GEMV_WAVES + (threadIdx.x >> 6)) * R;
@@ -46,7 +49,7 @@ k_gemv(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, const float
     const uint8_t *row[R];
 #pragma unroll
     for (int r = 0; r < R; r++)
-        row[r] = W + (n0 + r < N ? n0 + r : N - 1) * nb * WBLK;   // clamp loads, mask stores
+        row[r] = W + (n0 + r < N ? n0 + r : N - 1) * nb * UB;     // clamp loads, mask stores
 
     float acc[R][M];
 #pragma unroll
@@ -67,12 +70,12 @@ k_gemv(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, const float
             const int u0 = base + lane + 64 * i;
             const int u = u0 < units ? u0 : units - 1;
             const int b = u >> 1, h = u & 1;
-            const uint32_t off_blk = (uint32_t)(b >> 3) * WBLK;
-            const uint32_t off_qs = off_blk + QS_OFF + 16 * (b & 7) + 8 * h;
+            const uint32_t off_blk = (uint32_t)(b >> 3) * UB;
 #pragma unroll
             for (int r = 0; r < R; r++) {
-                hdr[i][r] = *reinterpret_cast<const uint2 *>(row[r] + off_blk);
-                qs[i][r] = *reinterpret_cast<const uint2 *>(row[r] + off_qs);
+                const char *unit = reinterpret_cast<const char *>(row[r] + off_blk);
+                hdr[i][r] = unit_scale_raw<F>(unit, b & 7);
+                qs[i][r] = unit_qs<F>(unit, b & 7, h);
             }
             dx[i] = *reinterpret_cast<const float4 *>(dp + (uint32_t)b * (uint32_t)Mp);
 #pragma unroll
@@ -88,8 +91,8 @@ k_gemv(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, const float
 #pragma unroll
                 for (int r = 0; r < R; r++) {
                     uint32_t wv[4];
-                    expand8(qs[i][r].x, qs[i][r].y, wv);
-                    const float sw = sub_scale(hdr[i][r].x, hdr[i][r].y, b & 7);
+                    expand8<F>(qs[i][r].x, qs[i][r].y, wv);
+                    const float sw = unit_scale_dec<F>(hdr[i][r], b & 7, true);
 #pragma unroll
                     for (int m = 0; m < M; m++) {
                         int D = __builtin_amdgcn_sdot4((int)wv[0], xv[i][m].x, 0, false);
@@ -112,47 +115,58 @@ k_gemv(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, const float
         }
 }
 
-template <int M, int R, int U>
+template <int M, int R, int U, int F>
 void launch_mru(const uint8_t *w, const XPlanes &x, float *Y, int64_t N, hipStream_t s)
 {
     const int64_t rows_per_block = (int64_t)GEMV_WAVES * R;
     const dim3 grid((unsigned)((N + rows_per_block - 1) / rows_per_block)), block(64 * GEMV_WAVES);
-    hipLaunchKernelGGL((k_gemv<M, R, U>), grid, block, 0, s, w, x.qp, x.dp, Y, N, x.K, x.Mp);
+    hipLaunchKernelGGL((k_gemv<M, R, U, F>), grid, block, 0, s, w, x.qp, x.dp, Y, N, x.K, x.Mp);
 }
 
 // Chunk size: the units each lane owns (K/16/64), split into equal chunks
 // of at most UMAX so every load of a chunk is in flight at once.
-template <int M, int R, int UMAX>
+template <int M, int R, int UMAX, int F>
 void launch_m(const uint8_t *w, const XPlanes &x, float *Y, int64_t N, hipStream_t s)
 {
     const int64_t per_lane = (x.K / 16 + 63) / 64;
     const int64_t chunks = (per_lane + UMAX - 1) / UMAX;
     const int u = (int)((per_lane + chunks - 1) / chunks);
     switch (u) {
-    case 1: launch_mru<M, R, 1>(w, x, Y, N, s); break;
-    case 2: launch_mru<M, R, 2>(w, x, Y, N, s); break;
-    case 3: launch_mru<M, R, 3>(w, x, Y, N, s); break;
-    case 4: launch_mru<M, R, 4>(w, x, Y, N, s); break;
-    case 5: if constexpr (UMAX >= 5) launch_mru<M, R, 5>(w, x, Y, N, s); break;
-    default: if constexpr (UMAX >= 6) launch_mru<M, R, 6>(w, x, Y, N, s); break;
+    case 1: launch_mru<M, R, 1, F>(w, x, Y, N, s); break;
+    case 2: launch_mru<M, R, 2, F>(w, x, Y, N, s); break;
+    case 3: launch_mru<M, R, 3, F>(w, x, Y, N, s); break;
+    case 4: launch_mru<M, R, 4, F>(w, x, Y, N, s); break;
+    case 5: if constexpr (UMAX >= 5) launch_mru<M, R, 5, F>(w, x, Y, N, s); break;
+    default: if constexpr (UMAX >= 6) launch_mru<M, R, 6, F>(w, x, Y, N, s); break;
     }
+}
+
+template <int F>
+hipError_t launch_gemv_fmt(const uint8_t *w, const XPlanes &x, float *Y, int64_t N, hipStream_t s)
+{
+    switch (x.M) {
+    // two rows per wavefront (measured on MI355X, M=1, 10240 x 5120: 11.6 us
+    // against 12.8 with four rows and 13.1 with one)
+    case 1: launch_m<1, 2, 6, F>(w, x, Y, N, s); break;
+    case 2: launch_m<2, 2, 6, F>(w, x, Y, N, s); break;
+    case 3: launch_m<3, 2, 4, F>(w, x, Y, N, s); break;
+    case 4: launch_m<4, 2, 4, F>(w, x, Y, N, s); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_gemv(const void *W, const XPlanes &x, float *Y, int64_t N, hipStream_t s)
+hipError_t launch_gemv(const void *W, const XPlanes &x, float *Y, int64_t N, hipStream_t s, int fmt)
 {
     const uint8_t *w = (const uint8_t *)W;
-    switch (x.M) {
-    // two rows per wavefront (measured on MI355X, M=1, 10240 x 5120: 11.6 us
-    // against 12.8 with four rows and 13.1 with one)
-    case 1: launch_m<1, 2, 6>(w, x, Y, N, s); break;
-    case 2: launch_m<2, 2, 6>(w, x, Y, N, s); break;
-    case 3: launch_m<3, 2, 4>(w, x, Y, N, s); break;
-    case 4: launch_m<4, 2, 4>(w, x, Y, N, s); break;
+    switch (fmt) {
+    case FMT_IQ4_XS: return launch_gemv_fmt<FMT_IQ4_XS>(w, x, Y, N, s);
+    case FMT_IQ4_NL: return launch_gemv_fmt<FMT_IQ4_NL>(w, x, Y, N, s);
+    case FMT_Q4_0: return launch_gemv_fmt<FMT_Q4_0>(w, x, Y, N, s);
     default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 }  // namespace iq4xs

@@ -230,11 +230,11 @@ void launch_tm(const uint8_t *W, const XPlanes &x, float *out, int64_t N, int kw
 
 }  // namespace
 
-MmqPlan mmq_plan(int64_t M, int64_t N, int64_t K)
+MmqPlan mmq_plan(int64_t M, int64_t N, int64_t K, int fmt)
 {
     MmqPlan p;
     if (M <= TILE && tune_override().mmv != 0) {
-        p.vp = mmv_plan(M, N, K, device_cus());
+        p.vp = mmv_plan(M, N, K, device_cus(), fmt);
         if (p.vp.ok) {
             p.mmv = true;
             p.zero_y = p.vp.zero_y;
@@ -242,13 +242,17 @@ MmqPlan mmq_plan(int64_t M, int64_t N, int64_t K)
         }
     }
     if (M > TILE && tune_override().tile != 0) {
-        p.tp = mmqt_plan(M, N, K, device_cus());
+        p.tp = mmqt_plan(M, N, K, device_cus(), fmt);
         if (p.tp.ok) {
             p.tile = true;
             p.zero_y = p.tp.zero_y;
             p.workspace_bytes = p.tp.workspace_bytes;
             return p;
         }
+    }
+    if (fmt != FMT_IQ4_XS) {
+        p.ok = false;
+        return p;
     }
     const int64_t Mp = round_up(M, MPAD);
     const int tm = M <= 32 ? 1 : (M <= 64 ? 2 : 4);
@@ -273,10 +277,12 @@ MmqPlan mmq_plan(int64_t M, int64_t N, int64_t K)
 }
 
 hipError_t launch_mmq(const void *Wv, const XPlanes &x, float *Y, int64_t N, void *workspace,
-                      bool y_zeroed, hipStream_t s)
+                      bool y_zeroed, hipStream_t s, int fmt)
 {
     const uint8_t *W = (const uint8_t *)Wv;
-    const MmqPlan p = mmq_plan(x.M, N, x.K);
+    const MmqPlan p = mmq_plan(x.M, N, x.K, fmt);
+    if (!p.ok)
+        return hipErrorInvalidValue;
     if (p.mmv) {
         if (p.vp.zero_y && !y_zeroed) {
             const hipError_t e = launch_zero(Y, x.M * N, s);

@@ -59,10 +59,15 @@ constexpr int NLQ = NWQ;                   // copying wavefronts
 // Output tile BM activation rows x BN weight rows: 128 x 128, or 64 x 256 for
 // M <= 64.  Wavefront w owns weight subtile w % (BN/32) and the activation
 // subtile pair w / (BN/32).  One LDS buffer: weights [BN][80], activations
-// [HALF][BM][32], scales [HALF][BM], 1 KB for slots without a job.
-template <int BM_, int BN_>
+// [HALF][BM][32], scales [HALF][BM], 1 KB for slots without a job.  F: the
+// weight format.  An 80-byte weight row holds, for IQ4_XS, the super-block's
+// 8 header bytes, 8 unused bytes and the half's 64 index bytes; for IQ4_NL
+// and Q4_0, bytes [0, 80) of the 144-byte unit for the first half and
+// [64, 144) for the second (its four 18-byte blocks at 8 + 18s), so that no
+// copy reaches past the unit.
+template <int BM_, int BN_, int F_ = FMT_IQ4_XS>
 struct QCfg {
-    static constexpr int BM = BM_, BN = BN_, NTW = BN / TILE;
+    static constexpr int BM = BM_, BN = BN_, NTW = BN / TILE, F = F_;
     static constexpr int W_BYTES = BN * WROWQ;
     static constexpr int A_OFF = W_BYTES, A_BYTES = HALF * BM * SB;
     static constexpr int D_OFF = A_OFF + A_BYTES, D_BYTES = HALF * BM * 4;
@@ -127,7 +132,7 @@ k_mmqt(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__re
     // blocks that share a weight block meet in one L2.
     const int g = G % 8 == 0 ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
     const int ua = runs.u[g], ub = runs.u[g + 1], t_first = runs.t[g];
-    const uint32_t row_bytes = (uint32_t)nb * WBLK;
+    const uint32_t row_bytes = (uint32_t)nb * sblk_bytes(C::F);
     const int dp_at = Mp * K;
     const __amdgpu_buffer_rsrc_t wr =
         __builtin_amdgcn_make_buffer_rsrc((void *)W, (short)0, (int)((uint32_t)N * row_bytes), BUFFER_FLAGS);
@@ -149,8 +154,13 @@ k_mmqt(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__re
             const int r = at / WROWQ, pc = (at - r * WROWQ) / 16;   // row, piece (5 per row)
             p_dst[k] = 1024 * job;
             p_kind[k] = 0;
-            p_go0[k] = (uint32_t)r * row_bytes + (pc == 0 ? 0 : 16 * pc - 8);
-            p_go1[k] = (uint32_t)r * row_bytes + (pc == 0 ? 0 : 16 * pc + 56);
+            if constexpr (C::F == FMT_IQ4_XS) {
+                p_go0[k] = (uint32_t)r * row_bytes + (pc == 0 ? 0 : 16 * pc - 8);
+                p_go1[k] = (uint32_t)r * row_bytes + (pc == 0 ? 0 : 16 * pc + 56);
+            } else {
+                p_go0[k] = (uint32_t)r * row_bytes + 16 * pc;
+                p_go1[k] = (uint32_t)r * row_bytes + 64 + 16 * pc;
+            }
         } else if (job < JW + JA) {
             const int a = job - JW;                               // 1 KB = 32 rows of one sub-block
             const int sb = a / (BM / TILE), r = TILE * (a % (BM / TILE)) + (lane >> 1);
@@ -175,7 +185,7 @@ k_mmqt(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__re
         char *buf = lds_area<decltype(bc)::value, BUFQ>();
         const int mb = c.t % mblocks, wb = c.t / mblocks, js = c.j0 >> 1, hf = c.j0 & 1;
         const bool live = c.cl > 0;
-        const uint32_t wbase = (uint32_t)wb * BN * row_bytes + (uint32_t)js * WBLK;
+        const uint32_t wbase = (uint32_t)wb * BN * row_bytes + (uint32_t)js * sblk_bytes(C::F);
         const int sb0 = js * SUBS + HALF * hf;
         const uint32_t abase = (uint32_t)((sb0 * Mp + mb * BM) * SB);
         const uint32_t dbase = (uint32_t)(dp_at + (sb0 * Mp + mb * BM) * 4);
@@ -235,8 +245,12 @@ k_mmqt(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__re
     auto compute = [&](const Chunk &c, auto bc) __attribute__((always_inline)) {
         const char *B = lds_area<decltype(bc)::value, BUFQ>();
         const char *wrow = B + (nt * TILE + col) * WROWQ;
-        const uint2 hdr = *reinterpret_cast<const uint2 *>(wrow);
         const int hf = c.j0 & 1;
+        // (IQ4_XS: the header; the other formats read each block's d)
+        uint2 hdr = make_uint2(0u, 0u);
+        if constexpr (C::F == FMT_IQ4_XS)
+            hdr = *reinterpret_cast<const uint2 *>(wrow);
+        const char *unit = wrow - 64 * hf;                    // where the 144-byte unit would start
         // Two sub-blocks at a time: all their LDS reads first, then all four
         // products (each into registers of its own), then the epilogues, so
         // that reads, lookups, matrix-core work and rescaling of the two
@@ -249,7 +263,10 @@ k_mmqt(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__re
 #pragma unroll
             for (int u = 0; u < 2; u++) {
                 const int s = s0 + u;
-                q[u] = *reinterpret_cast<const uint2 *>(wrow + 16 + 16 * s + 8 * h);
+                if constexpr (C::F == FMT_IQ4_XS)
+                    q[u] = *reinterpret_cast<const uint2 *>(wrow + 16 + 16 * s + 8 * h);
+                else
+                    q[u] = unit_qs<C::F>(unit, HALF * hf + s, h);
 #pragma unroll
                 for (int i = 0; i < 2; i++) {
                     const int mt = 2 * mp + i;
@@ -266,7 +283,9 @@ k_mmqt(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__re
             // the two sub-blocks' scales and swap them)
             float sw[2];
             {
-                const uint32_t own = __builtin_bit_cast(uint32_t, sub_scale(hdr.x, hdr.y, HALF * hf + s0 + h));
+                const float sc = C::F == FMT_IQ4_XS ? sub_scale(hdr.x, hdr.y, HALF * hf + s0 + h)
+                                                    : unit_scale<C::F>(unit, HALF * hf + s0 + h, true);
+                const uint32_t own = __builtin_bit_cast(uint32_t, sc);
                 const auto both = __builtin_amdgcn_permlane32_swap(own, own, false, false);
                 sw[0] = __builtin_bit_cast(float, (uint32_t)both[0]);
                 sw[1] = __builtin_bit_cast(float, (uint32_t)both[1]);
@@ -274,7 +293,7 @@ k_mmqt(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__re
 #pragma unroll
             for (int u = 0; u < 2; u++) {
                 uint32_t wa[4], wb4[4];
-                expand8_split(q[u].x, q[u].y, wa, wb4);
+                expand8_split<C::F>(q[u].x, q[u].y, wa, wb4);
                 const v4i ba = {(int)wa[0], (int)wa[1], (int)wa[2], (int)wa[3]};
                 const v4i bb = {(int)wb4[0], (int)wb4[1], (int)wb4[2], (int)wb4[3]};
 #pragma unroll
@@ -424,10 +443,10 @@ hipError_t launch_cfg(const void *W, const XPlanes &x, float *Y, float *ws, int6
 
 }  // namespace
 
-MmqtPlan mmqt_plan(int64_t M, int64_t N, int64_t K, int cus)
+MmqtPlan mmqt_plan(int64_t M, int64_t N, int64_t K, int cus, int fmt)
 {
     MmqtPlan p;
-    const int64_t nb = K / QK, row_bytes = nb * WBLK;
+    const int64_t nb = K / QK, row_bytes = nb * sblk_bytes(fmt);
     const int64_t Mp = round_up(M, MPAD);
     // 64 x 256 tiles up to M = 64, else 128 x 128
     const int64_t BM = M <= 2 * TILE ? 64 : 128, BN = 16384 / BM;
@@ -466,6 +485,7 @@ MmqtPlan mmqt_plan(int64_t M, int64_t N, int64_t K, int cus)
     } else {
         p.workspace_bytes = (size_t)p.grid * 2 * SLOT_F4 * sizeof(float4);
     }
+    p.fmt = fmt;
     p.ok = true;
     return p;
 }
@@ -487,11 +507,15 @@ hipError_t launch_mmqt(const void *W, const XPlanes &x, float *Y, int64_t N, con
             runs.t[g] = runs.u[g] / nh;
     }
     float *ws = (float *)workspace;
-    if (p.bm == 64)
-        return launch_cfg<QCfg<64, 256>>(W, x, Y, ws, N, p, runs, s);
-    if (p.bm == 128)
-        return launch_cfg<QCfg<128, 128>>(W, x, Y, ws, N, p, runs, s);
-    return hipErrorInvalidValue;
+    switch (p.fmt * 2 + (p.bm == 128 ? 1 : 0)) {
+    case 2 * FMT_IQ4_XS: return launch_cfg<QCfg<64, 256, FMT_IQ4_XS>>(W, x, Y, ws, N, p, runs, s);
+    case 2 * FMT_IQ4_XS + 1: return launch_cfg<QCfg<128, 128, FMT_IQ4_XS>>(W, x, Y, ws, N, p, runs, s);
+    case 2 * FMT_IQ4_NL: return launch_cfg<QCfg<64, 256, FMT_IQ4_NL>>(W, x, Y, ws, N, p, runs, s);
+    case 2 * FMT_IQ4_NL + 1: return launch_cfg<QCfg<128, 128, FMT_IQ4_NL>>(W, x, Y, ws, N, p, runs, s);
+    case 2 * FMT_Q4_0: return launch_cfg<QCfg<64, 256, FMT_Q4_0>>(W, x, Y, ws, N, p, runs, s);
+    case 2 * FMT_Q4_0 + 1: return launch_cfg<QCfg<128, 128, FMT_Q4_0>>(W, x, Y, ws, N, p, runs, s);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace iq4xs

@@ -57,12 +57,12 @@ constexpr int TILE = 32;
 constexpr int NW = 16;                     // wavefronts per workgroup
 constexpr int NT = 64 * NW;                // threads per workgroup
 constexpr int PAR = NW / SUBS;             // wavefronts per sub-block
-// LDS row stride of a weight chunk: CH*136 bytes rounded up to an odd number
-// of 16-byte units, so that the 32 rows of an MFMA operand read spread over
-// the banks.
-constexpr int wrow_bytes(int ch)
+// LDS row stride of a weight chunk: CH units of UB bytes (136 or 144) rounded
+// up to an odd number of 16-byte units, so that the 32 rows of an MFMA operand
+// read spread over the banks.
+constexpr int wrow_bytes(int ch, int ub)
 {
-    const int u = (ch * WBLK + 15) / 16;
+    const int u = (ch * ub + 15) / 16;
     return 16 * (u % 2 ? u : u + 1);
 }
 
@@ -71,13 +71,15 @@ constexpr int wrow_bytes(int ch)
 // activation rows go to MFMA rows 0..LIVE-1 and 4..4+LIVE-1, so that both
 // halves of a wavefront hold real rows in their LIVE result registers (row
 // h*LIVE + r in register r of half h): half the rescale work of putting all
-// rows in the first half.
-template <int LIVE_, int MPC_, int CH_, int NBUF_, bool SPLIT_ = false>
+// rows in the first half.  F: the weight format; a "super-block" below is
+// its 256-weight unit of UB bytes.
+template <int LIVE_, int MPC_, int CH_, int NBUF_, bool SPLIT_ = false, int F_ = FMT_IQ4_XS>
 struct Cfg {
     static constexpr int LIVE = LIVE_, MPC = MPC_, CH = CH_, NBUF = NBUF_;
     static constexpr bool SPLIT = SPLIT_;
-    static constexpr int WROW = wrow_bytes(CH);
-    static constexpr int W_PR = CH * WBLK / 16;                               // pieces per row
+    static constexpr int F = F_, UB = sblk_bytes(F_);
+    static constexpr int WROW = wrow_bytes(CH, UB);
+    static constexpr int W_PR = CH * UB / 16;                                 // pieces per row
     // one chunk buffer: weights [32][WROW] (padded to whole KB), activations
     // [CH*8][MA][32], scales [CH*8][Mp] (padded to whole KB), a 32-byte zero
     // row (the operand of rows >= M) and slack for the scales a lane reads
@@ -140,7 +142,8 @@ k_mmv(MmvGroup grp, const int8_t *__restrict__ qp, int M, int K, int Mp, int nb,
     // this workgroup's run of units
     const int g = blockIdx.x;
     const int ua = runs.u[g], ub = runs.u[g + 1];
-    const uint32_t row_bytes = (uint32_t)nb * WBLK;
+    constexpr int UB = C::UB;
+    const uint32_t row_bytes = (uint32_t)nb * UB;
 
     // ---- chunk copy: fixed per-lane geometry ------------------------------
     // descriptors over the whole weight matrix and over both activation planes
@@ -200,8 +203,8 @@ k_mmv(MmvGroup grp, const int8_t *__restrict__ qp, int M, int K, int Mp, int nb,
             const int gi = GRP ? grp.matrix_of(c.t) : 0;
             const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
                 (void *)grp.w[gi], (short)0, (int)((uint32_t)grp.n[gi] * row_bytes), BUFFER_FLAGS);
-            const int lo = (c.j0 & 1) * WBLK, hi = lo + c.cl * WBLK;
-            const uint32_t base = (uint32_t)(c.t - grp.t0[gi]) * TILE * row_bytes + (c.j0 & ~1) * WBLK;
+            const int lo = (c.j0 & 1) * UB, hi = lo + c.cl * UB;
+            const uint32_t base = (uint32_t)(c.t - grp.t0[gi]) * TILE * row_bytes + (c.j0 & ~1) * UB;
 #pragma unroll
             for (int k = 0; k < SLOTS; k++) {
                 const bool need = (uint32_t)(p_key[k] - lo) < (uint32_t)(hi - lo + 15);
@@ -295,7 +298,7 @@ k_mmv(MmvGroup grp, const int8_t *__restrict__ qp, int M, int K, int Mp, int nb,
     }
     auto compute = [&](const Chunk &c, auto bc) __attribute__((always_inline)) {
         const char *B = C::template buf<decltype(bc)::value>();
-        const char *wchunk = B + w_lane + (c.j0 & 1) * WBLK;  // the window starts at j0 & ~1
+        const char *wchunk = B + w_lane + (c.j0 & 1) * UB;    // the window starts at j0 & ~1
         // Wavefront pair `par` takes the super-blocks whose absolute index j
         // has j % 2 == par, in increasing order, whatever the chunk length
         // (which depends on M) and wherever the chunk starts: every output
@@ -320,13 +323,13 @@ k_mmv(MmvGroup grp, const int8_t *__restrict__ qp, int M, int K, int Mp, int nb,
             // wavefront (same rows) each decode one of the two scales and
             // swap them.
             if constexpr (GI == 2)
-                hdr[0] = *reinterpret_cast<const uint2 *>(wchunk + (pc + PAR * (g + h)) * WBLK);
+                hdr[0] = unit_scale_raw<C::F>(wchunk + (pc + PAR * (g + h)) * UB, s);
 #pragma unroll
             for (int k = 0; k < GI; k++) {
-                const char *wrow = wchunk + (pc + PAR * (g + k)) * WBLK;
+                const char *wrow = wchunk + (pc + PAR * (g + k)) * UB;
                 if constexpr (GI != 2)
-                    hdr[k] = *reinterpret_cast<const uint2 *>(wrow);
-                q[k] = *reinterpret_cast<const uint2 *>(wrow + QS_OFF + 16 * s + 8 * h);
+                    hdr[k] = unit_scale_raw<C::F>(wrow, s);
+                q[k] = unit_qs<C::F>(wrow, s, h);
                 ax[k] = *reinterpret_cast<const v4i *>(B + a_off[g + k] + a_pc);
 #pragma unroll
                 for (int qd = 0; qd < DQ; qd++)
@@ -343,9 +346,8 @@ k_mmv(MmvGroup grp, const int8_t *__restrict__ qp, int M, int K, int Mp, int nb,
             __builtin_amdgcn_sched_barrier(0);
             float sw[GI];
             if constexpr (GI == 2) {
-                // (a super-block past the chunk gets d = 0: a zero scale)
-                const uint32_t d_bits = pc + PAR * (g + h) < c.cl ? hdr[0].x : 0u;
-                const float own = sub_scale(d_bits, hdr[0].y, s);
+                // (a super-block past the chunk gets a zero scale)
+                const float own = unit_scale_dec<C::F>(hdr[0], s, pc + PAR * (g + h) < c.cl);
                 const uint32_t ob = __builtin_bit_cast(uint32_t, own);
                 // (lanes 0-31 of the first result: their own scale; lanes
                 // 32-63: that of lanes 0-31; the second result the converse)
@@ -355,13 +357,13 @@ k_mmv(MmvGroup grp, const int8_t *__restrict__ qp, int M, int K, int Mp, int nb,
             } else {
 #pragma unroll
                 for (int k = 0; k < GI; k++)
-                    sw[k] = pc + PAR * (g + k) < c.cl ? sub_scale(hdr[k].x, hdr[k].y, s) : 0.0f;
+                    sw[k] = unit_scale_dec<C::F>(hdr[k], s, pc + PAR * (g + k) < c.cl);
             }
             v16i D[GI];
 #pragma unroll
             for (int k = 0; k < GI; k++) {
                 uint32_t wa[4], wb[4];
-                expand8_split(q[k].x, q[k].y, wa, wb);
+                expand8_split<C::F>(q[k].x, q[k].y, wa, wb);
                 const v4i ba = {(int)wa[0], (int)wa[1], (int)wa[2], (int)wa[3]};
                 const v4i bb = {(int)wb[0], (int)wb[1], (int)wb[2], (int)wb[3]};
                 const v16i zero = {0};
@@ -457,10 +459,10 @@ hipError_t launch_c(const MmvGroup &grp, const XPlanes &x, const MmvPlan &p, hip
 
 }  // namespace
 
-MmvPlan mmv_plan_group(int64_t M, const int64_t *N, int count, int64_t K, int cus)
+MmvPlan mmv_plan_group(int64_t M, const int64_t *N, int count, int64_t K, int cus, int fmt)
 {
     MmvPlan p;
-    const int64_t nb = K / QK, row_bytes = nb * WBLK;
+    const int64_t nb = K / QK, row_bytes = nb * sblk_bytes(fmt);
     const int64_t Mp = round_up(M, MPAD);
     if (count < 1 || count > MAXGRP)
         return p;
@@ -473,8 +475,9 @@ MmvPlan mmv_plan_group(int64_t M, const int64_t *N, int count, int64_t K, int cu
             return p;
         T += (N[g] + TILE - 1) / TILE;
     }
-    if (M < 1 || M > TILE || nb % 2 != 0 || nb >= (1 << 16) || Mp * K + Mp * K / 8 >= (1LL << 31) ||
-        T * nb >= (1LL << 31))
+    // (144-byte units are 16-byte aligned wherever a window starts)
+    if (M < 1 || M > TILE || (fmt == FMT_IQ4_XS && nb % 2 != 0) || nb >= (1 << 16) ||
+        Mp * K + Mp * K / 8 >= (1LL << 31) || T * nb >= (1LL << 31))
         return p;
     const int64_t U = T * nb;
     p.grid = (int)(T < cus ? T : cus);
@@ -487,11 +490,12 @@ MmvPlan mmv_plan_group(int64_t M, const int64_t *N, int count, int64_t K, int cu
             p.zero_y = true;                                // some tile has two owners
             break;
         }
+    p.fmt = fmt;
     p.ok = true;
     return p;
 }
 
-MmvPlan mmv_plan(int64_t M, int64_t N, int64_t K, int cus) { return mmv_plan_group(M, &N, 1, K, cus); }
+MmvPlan mmv_plan(int64_t M, int64_t N, int64_t K, int cus, int fmt) { return mmv_plan_group(M, &N, 1, K, cus, fmt); }
 
 MmvGroup mmv_group(const void *const *W, float *const *Y, const int64_t *N, int count)
 {
@@ -509,20 +513,32 @@ MmvGroup mmv_group(const void *const *W, float *const *Y, const int64_t *N, int 
     return g;
 }
 
+template <int F>
+hipError_t launch_fmt(const MmvGroup &grp, const XPlanes &x, const MmvPlan &p, hipStream_t s)
+{
+    switch (p.live) {
+    // (M = 2..4: rows split over both halves of the MFMA tile; measured 2-4%
+    // faster than all rows in the first half)
+    case 1: return launch_c<Cfg<1, 4, 8, 3, false, F>>(grp, x, p, s);
+    case 2: return launch_c<Cfg<1, 4, 8, 3, true, F>>(grp, x, p, s);
+    case 3: return launch_c<Cfg<2, 4, 8, 3, true, F>>(grp, x, p, s);
+    case 4:
+        return x.Mp <= 4 ? launch_c<Cfg<2, 4, 8, 3, true, F>>(grp, x, p, s)
+                         : launch_c<Cfg<4, 8, 4, 3, false, F>>(grp, x, p, s);
+    case 8: return launch_c<Cfg<8, 16, 4, 3, false, F>>(grp, x, p, s);
+    case 16: return launch_c<Cfg<16, 32, 2, 3, false, F>>(grp, x, p, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 hipError_t launch_mmv_group(const MmvGroup &grp, const XPlanes &x, const MmvPlan &p, hipStream_t s)
 {
     if (!p.ok || grp.count < 1 || grp.count > MAXGRP)
         return hipErrorInvalidValue;
-    switch (p.live) {
-    // (M = 2..4: rows split over both halves of the MFMA tile; measured 2-4%
-    // faster than all rows in the first half)
-    case 1: return launch_c<Cfg<1, 4, 8, 3>>(grp, x, p, s);
-    case 2: return launch_c<Cfg<1, 4, 8, 3, true>>(grp, x, p, s);
-    case 3: return launch_c<Cfg<2, 4, 8, 3, true>>(grp, x, p, s);
-    case 4:
-        return x.Mp <= 4 ? launch_c<Cfg<2, 4, 8, 3, true>>(grp, x, p, s) : launch_c<Cfg<4, 8, 4, 3>>(grp, x, p, s);
-    case 8: return launch_c<Cfg<8, 16, 4, 3>>(grp, x, p, s);
-    case 16: return launch_c<Cfg<16, 32, 2, 3>>(grp, x, p, s);
+    switch (p.fmt) {
+    case FMT_IQ4_XS: return launch_fmt<FMT_IQ4_XS>(grp, x, p, s);
+    case FMT_IQ4_NL: return launch_fmt<FMT_IQ4_NL>(grp, x, p, s);
+    case FMT_Q4_0: return launch_fmt<FMT_Q4_0>(grp, x, p, s);
     default: return hipErrorInvalidValue;
     }
 }

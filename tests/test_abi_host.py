@@ -343,3 +343,40 @@ def test_noalloc_rejects_shapes_beyond_the_static_scratch():
     assert L.iq4xs_gemm_noalloc(A, A * 2, A * 4, 4, 8, 300, 0, None) == iq.EINVAL
     if not _has_gpu():
         assert L.iq4xs_gemm_noalloc(A, A * 2, A * 4, 4, 8, 256, 0, None) == iq.EDEVICE
+
+
+def test_format_entry_points_validate_on_the_host():
+    out = ctypes.c_size_t()
+    assert L.iq4xs_weight_bytes_fmt(iq.FMT_IQ4_XS, 10, 512, ctypes.byref(out)) == iq.OK and out.value == 10 * 2 * 136
+    assert L.iq4xs_weight_bytes_fmt(iq.FMT_IQ4_NL, 10, 512, ctypes.byref(out)) == iq.OK and out.value == 10 * 16 * 18
+    assert L.iq4xs_weight_bytes_fmt(iq.FMT_Q4_0, 10, 512, ctypes.byref(out)) == iq.OK and out.value == 10 * 16 * 18
+    assert iq.weight_bytes_fmt(iq.FMT_Q4_0, 5120, 17408) == 5120 * 544 * 18
+    assert L.iq4xs_weight_bytes_fmt(3, 10, 512, ctypes.byref(out)) == iq.EINVAL
+    assert L.iq4xs_weight_bytes_fmt(-1, 10, 512, ctypes.byref(out)) == iq.EINVAL
+    assert L.iq4xs_weight_bytes_fmt(iq.FMT_IQ4_NL, 10, 480, ctypes.byref(out)) == iq.EINVAL   # K % 256
+    far = 1 << 44
+    for bad_fmt in (3, 7, -2):
+        assert L.iq4xs_gemm_fmt(bad_fmt, A, far, 2 * far, 4, 8, 256, 0, None, 0, None) == iq.EINVAL
+    for fmt in (iq.FMT_IQ4_NL, iq.FMT_Q4_0):
+        # the bf16 path reads IQ4_XS only
+        assert L.iq4xs_gemm_fmt(fmt, A, far, 2 * far, 64, 8, 256, iq.PATH_DEQ_BF16, None, 0, None) == iq.EPATH
+        assert L.iq4xs_gemm_fmt_workspace_bytes(fmt, 64, 8, 256, iq.PATH_DEQ_BF16, ctypes.byref(out)) == iq.EPATH
+        assert L.iq4xs_gemm_fmt(fmt, A, far, 2 * far, 4, 8, 300, 0, None, 0, None) == iq.EINVAL
+        assert L.iq4xs_gemm_fmt(fmt, A + 8, far, 2 * far, 4, 8, 256, 0, None, 0, None) == iq.EALIGN
+        assert L.iq4xs_gemm_fmt(fmt, A, far, 2 * far, 5, 8, 256, iq.PATH_GEMV, None, 0, None) == iq.EPATH
+        # Y overlapping W (18-byte blocks: 8 x 256 weights = 1152 bytes)
+        assert L.iq4xs_gemm_fmt(fmt, A, far, A + 1024, 4, 8, 256, 0, None, 0, None) == iq.EINVAL
+        if not _has_gpu():
+            assert L.iq4xs_gemm_fmt(fmt, A, far, 2 * far, 4, 8, 256, 0, None, 0, None) == iq.EDEVICE
+        assert iq.fmt_workspace_bytes(fmt, 16, 1024, 512, iq.PATH_MMQ) > 0
+
+
+def test_format_binding_shapes():
+    import torch
+    X = torch.zeros((4, 512))
+    with pytest.raises(ValueError, match="W must have shape"):
+        iq.gemm_fmt(torch.zeros((8, 512 // 256 * 136), dtype=torch.uint8), X, iq.FMT_IQ4_NL)
+    with pytest.raises(ValueError, match="unknown weight format"):
+        iq.gemm_fmt(torch.zeros((8, 288), dtype=torch.uint8), X, 5)
+    with pytest.raises(TypeError, match="CUDA"):
+        iq.gemm_fmt(torch.zeros((8, 288), dtype=torch.uint8), X, iq.FMT_Q4_0)
