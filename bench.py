@@ -2,38 +2,49 @@
 """Benchmark of the IQ4_XS x Q8_1 matmul on one MI355X.
 
 Default run: `python bench.py [--steps K] [--warmup W]`.
-One *step* is the whole hot path over the decode sweep of the attention/GDN
-input-projection shape, N=10240, K=5120: for each M in {1, 2, 4, 8, 16} one
-iq4xs_gemm_ws call (Q8_1 quantization of X on the device, the dispatcher's
-choice of path, the matmul), with all inputs resident in HBM, launched on one
-stream (the host runs ahead of the device, so the time is the device's);
-weight copies are rotated (>= 640 MB in total) so the 256 MB Infinity Cache
-cannot serve them.  The same calls recorded into HIP graphs and replayed are
-reported as graph_ms_per_step (slower here: the replay leaves larger gaps
-between the ten short kernels).
+One *step* is one pass of the whole hot path over the five synthetic
+workloads, M = 1..512: one iq4xs_gemm call (Q8_1 quantization of X on the
+device, the measured dispatcher's choice of path, the matmul) for every
+point of
+  - a single 2048 x 2048 GEMM at M=4;
+  - the attention/GDN input projection N=10240 K=5120, decode M in {1,2,4,8,16};
+  - the MLP gate/up shape N=17408 K=5120, M in {8,16,32,64,96};
+  - the MLP down shape N=5120 K=17408, M in {1,12,32,64,96};
+  - the prefill sweep: nine (N, K) shapes x M in {64,128,256,512}
+(52 calls), all inputs resident in HBM, launched back to back on one stream
+(the host runs ahead, so the time is the device's); every shape's weights
+are rotated over copies of >= 640 MB, so the 256 MB Infinity Cache cannot
+serve them.
 
 Printed: one JSON line with
-  value      whole-step weight bandwidth = weight bytes read / step time (GB/s)
-  per_m      ms per call, weight-GB/s, int8 TOPS and % of the HBM roofline
-  roofline   for the dominant kernel (the matmul launch with the largest
-             duration): algorithmic bytes per launch / its average duration,
-             timed with HIP events on the stream the kernel runs on
-  t_m2_over_m1  per-call time at M=2 over M=1 (flat in M is the aim)
-  read_probe what a plain 1 GiB read achieves here (torch.sum), beside 8 TB/s
-  group      one X against a pair of decode-shape matrices: the grouped call
-             (one quantization, one matmul launch) against two separate calls
-  cpu_baseline  the CPU oracle (never tuned) on a bounded sample of the same
-             sweep, in the same unit.
-`--sweep FILE` additionally times every (shape, M, path) point of the five
-workloads and writes one JSON object per point to FILE (used for the measured
-dispatch table and the results tables).
+  value        whole-step weight bandwidth = weight bytes of all 52 calls / step time
+  int8_TOPS    2*sum(M*N*K) / step time
+  points       per (shape, M): ms per call (graph replay, quantization included),
+               ms of the matmul kernel(s) alone, weight-GB/s, int8 TOPS, the
+               fractions of the HBM and int8-MFMA rooflines, the bound that
+               binds (the larger of bytes/8 TB/s and ops/5 POP/s), the kernel
+  roofline     the dominant kernel (largest share of the step's kernel time):
+               algorithmic work per launch / its average duration, timed with
+               HIP events on the stream it runs on
+  rooflines    the same for the dominant point of each matmul kernel
+  probes       this device's own ceilings: a stream read (28 MB, 95 MB, 1 GiB,
+               rotated past the Infinity Cache), a stream write, back-to-back
+               int8 and bf16 matrix-core instructions
+  group        one X against a pair of decode-shape matrices: grouped call vs two calls
+  formats      a few points with IQ4_NL and Q4_0 weights
+  cpu_baseline the CPU oracle (never tuned) on a bounded column sample of the
+               same 52 points, in the same unit.
+`--sweep FILE` times every (shape, M, path) point and writes one JSON object
+per point to FILE (the input of the dispatch-table calibration).
 
-Profiling helpers (the commands are recorded in the summaries under profiles/):
-`--profile-run` launches the decode sweep's matmul kernels and a calibration
-copy a fixed number of times (run under rocprofv3); `--summarize-pmc FETCH_DIR
-WRITE_DIR --out FILE` turns the two counter runs into the traffic summary
-that the `roofline.traffic` field is read from (only while the kernel source
-it was measured on is unchanged).
+Profiling helpers (the commands are recorded in the summaries under
+profiles/): `--profile-points` launches every point's call with a marker
+kernel between points (run under rocprofv3 --kernel-trace; `--check-trace`
+then checks that every call launched the quantizer and the matmul kernel its
+path names); `--profile-run` / `--profile-shapes` launch matmul kernels and
+the read / write probes of known bytes a fixed number of times (run under
+rocprofv3 --pmc; `--summarize-pmc*` turns FETCH_SIZE / WRITE_SIZE into
+calibrated bytes per launch).
 """
 
 from __future__ import annotations
@@ -62,16 +73,23 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
 INT8_PEAK_TOPS = 5000.0         # MI355X dense int8 MFMA, published
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
 MALL_BYTES = 256 << 20
+PROBE_BYTES = 1 << 30           # calibration read / write of the profiling runs
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_mmv_decode_n10240_k5120_traffic.txt")
-COPY_BYTES = 256 << 20          # calibration copy of the profiling run
+TILE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_mmqt_tile_shapes_traffic.txt")
 KERNEL_SOURCES = {"k_mmv": ["mmv.hip", "common.hpp", "stream.hpp"], "k_gemv": ["gemv.hip", "common.hpp"],
                   "k_mmq": ["mmq.hip", "common.hpp"], "k_mmqt": ["mmqt.hip", "common.hpp", "stream.hpp"],
                   "k_gemm_bf16": ["deq.hip", "common.hpp"]}
+# Exact formulation on the matrix cores: per (output, 32-wide sub-block) the
+# int8 MFMA does 32 MACs (0.031 cycles per SIMD at 2048 ops/cycle) and the
+# fp32 rescale three VALU instructions (0.1875 cycles at 16 lanes/cycle,
+# packed fp32 off): the tile kernel cannot pass 1/6 of the int8 peak.
+VALU_CEILING_FRAC = (64 / 2048) / (3 * 4 / 64)
 
 
 def kernel_name(M, N, K, path):
     """The matmul kernel a call launches (the streaming kernel serves MMQ up
-    to M=32 when K/256 is even)."""
+    to M=32 when K/256 is even; --check-trace verifies this against the
+    rocprofv3 trace)."""
     if path == iq.PATH_GEMV:
         return "k_gemv"
     if path == iq.PATH_DEQ_BF16:
@@ -79,7 +97,7 @@ def kernel_name(M, N, K, path):
     nb = K // 256
     if M <= 32 and nb % 2 == 0 and N * nb * 136 < (1 << 31):
         return "k_mmv"
-    return "k_mmqt" if M > 32 else "k_mmq"
+    return "k_mmqt" if M > 32 and N * nb * 136 < (1 << 31) else "k_mmq"
 
 
 def source_hash(kernel):
@@ -101,6 +119,11 @@ def algo_bytes_kernel(M, N, K):
     """Algorithmic bytes of one matmul launch: weights, prepared activations
     (1 B per value + 4 B scale per 32), Y."""
     return 0.53125 * N * K + 1.125 * M * K + 4 * M * N
+
+
+def sweep_points():
+    """(workload, N, K, M) of the 52 calls of one step."""
+    return [(wl, N, K, M) for wl in synth.WORKLOADS for (N, K) in wl.shapes for M in wl.ms]
 
 
 class Rotation:
@@ -131,18 +154,22 @@ def time_events(fn, reps, stream):
     return start.elapsed_time(stop) / reps      # ms
 
 
-def measure_point(rot, X, N, K, path, reps=30):
-    """Per iq4xs_gemm call: ms on the device (`reps` calls over rotating
-    weight copies recorded in one HIP graph and replayed, so host launch
-    cost is not counted) and ms launched eagerly from the host; and ms per
-    launch of the matmul kernel alone (prepared activations, Y marked as
-    zeroed so that nothing else runs; its values are not used).  All from HIP
-    events on the launching stream."""
+def measure_point(rot, X, N, K, path, reps=20, fmt=iq.FMT_IQ4_XS):
+    """Per call: ms on the device (`reps` calls over rotating weight copies
+    recorded in one HIP graph and replayed, so host launch cost is not
+    counted) and ms launched eagerly; and ms per launch of the matmul
+    kernel(s) alone (prepared activations, Y marked as zeroed so that nothing
+    else runs; its values are not used).  All from HIP events on the
+    launching stream."""
     M = X.shape[0]
     Y = torch.empty((M, N), dtype=torch.float32, device="cuda")
-    ws = torch.empty(iq.workspace_bytes(M, N, K, path), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
-    call = lambda: iq.gemm(rot.next(), X, path=path, out=Y, workspace=ws)  # noqa: E731
+    if fmt == iq.FMT_IQ4_XS:
+        ws = torch.empty(iq.workspace_bytes(M, N, K, path), dtype=torch.uint8, device="cuda")
+        call = lambda: iq.gemm(rot.next(), X, path=path, out=Y, workspace=ws)  # noqa: E731
+    else:
+        ws = torch.empty(iq.fmt_workspace_bytes(fmt, M, N, K, path), dtype=torch.uint8, device="cuda")
+        call = lambda: iq.gemm_fmt(rot.next(), X, fmt, path=path, out=Y, workspace=ws)  # noqa: E731
     for _ in range(3):
         call()
     t_eager = time_events(call, reps, stream)
@@ -160,24 +187,71 @@ def measure_point(rot, X, N, K, path, reps=30):
     t_call = time_events(g.replay, 3, stream) / reps
     del g
     t_kern = None
-    if path != iq.PATH_DEQ_BF16:
+    if path != iq.PATH_DEQ_BF16 and fmt == iq.FMT_IQ4_XS:
         act = iq.prepare_act(X)
         Y.zero_()
         kern = lambda: iq.gemm_act(rot.next(), act, M, K, path=path, out=Y, y_zeroed=True)  # noqa: E731
         for _ in range(3):
             kern()
-        t_kern = time_events(kern, reps, stream)
+        # without a partial-tile workspace the launch allocates nothing and is
+        # replayed from a graph like the calls (no host gaps between short
+        # kernels); with one, it is launched eagerly
+        planes = -(-iq.act_bytes(M, K) // 256) * 256
+        if path == iq.PATH_GEMV or iq.workspace_bytes(M, N, K, path) == planes:
+            side = torch.cuda.Stream()
+            side.wait_stream(stream)
+            with torch.cuda.stream(side):
+                kern()
+            stream.wait_stream(side)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(reps):
+                    kern()
+            g.replay()
+            t_kern = time_events(g.replay, 3, stream) / reps
+            del g
+        else:
+            t_kern = time_events(kern, reps, stream)
     return t_call, t_kern, t_eager
+
+
+def point_record(N, K, M, path, t_call, t_kern, t_eager=None):
+    """Per point: ms, weight-GB/s, int8 TOPS, the fraction of each roofline
+    and the one that binds.  Algorithmic bytes and ops (2*M*N*K) per call;
+    with the kernel alone, its own algorithmic bytes."""
+    wb = 0.53125 * N * K
+    ops = 2.0 * M * N * K
+    t_hbm = algo_bytes_call(M, N, K) / (HBM_PEAK_GBS * 1e9) * 1e3      # ms at the HBM peak
+    t_mfma = ops / (INT8_PEAK_TOPS * 1e12) * 1e3                         # ms at the int8 peak
+    rec = {"N": N, "K": K, "M": M, "path": iq.path_name(path), "ms": t_call, "eager_ms": t_eager,
+           "weight_GBs": wb / (t_call * 1e-3) / 1e9,
+           "int8_TOPS": ops / (t_call * 1e-3) / 1e12,
+           "hbm_frac": t_hbm / t_call, "mfma_frac": t_mfma / t_call,
+           "bound": "hbm" if t_hbm >= t_mfma else "mfma",
+           "roofline_frac": max(t_hbm, t_mfma) / t_call}
+    if t_kern is not None:
+        tk_hbm = algo_bytes_kernel(M, N, K) / (HBM_PEAK_GBS * 1e9) * 1e3
+        rec["kernel_ms"] = t_kern
+        rec["kernel_GBs"] = algo_bytes_kernel(M, N, K) / (t_kern * 1e-3) / 1e9
+        rec["kernel_hbm_frac"] = tk_hbm / t_kern
+        rec["kernel_mfma_frac"] = t_mfma / t_kern
+        rec["kernel_roofline_frac"] = max(tk_hbm, t_mfma) / t_kern
+    rec["kernel"] = kernel_name(M, N, K, path)
+    # impossible-throughput flag: faster than the card can move the bytes or
+    # do the operations ("V100TPS engine log", opening section)
+    rec["impossible"] = bool(rec["hbm_frac"] > 1.0 or rec["mfma_frac"] > 1.0 or
+                             rec.get("kernel_hbm_frac", 0) > 1.0 or rec.get("kernel_mfma_frac", 0) > 1.0)
+    return rec
 
 
 def measure_group(ms=(1, 8, 16), reps=20):
     """One X against two weight matrices of the decode shape (N=10240,
     K=5120; e.g. two input projections of one layer): one grouped call (one
     quantization, one matmul launch over both) against two iq4xs_gemm calls,
-    both with caller workspaces.  ms per pair on the device: `reps` pairs (each on another rotated weight
-    pair, past the Infinity Cache) recorded in one HIP graph and replayed, as
-    for the per-call times.  (The same shape as the decode sweep, so that a
-    kernel trace of the bench run averages one shape per kernel.)"""
+    both with caller workspaces.  ms per pair on the device: `reps` pairs
+    (each on another rotated weight pair, past the Infinity Cache) recorded
+    in one HIP graph and replayed, as for the per-call times."""
     wl = synth.DECODE_ATTN
     N, K = wl.shapes[0]
     base = torch.from_numpy(wl.w(N, K)).cuda()
@@ -190,7 +264,6 @@ def measure_group(ms=(1, 8, 16), reps=20):
     for M in ms:
         X = torch.from_numpy(wl.x(M, K, N=N)).cuda()
         Y = [torch.empty((M, N), dtype=torch.float32, device="cuda") for _ in range(2)]
-        # caller workspaces on both sides: nothing is allocated inside the calls
         gws = torch.empty(iq.group_workspace_bytes([N, N], M, K), dtype=torch.uint8, device="cuda")
         sws = torch.empty(iq.workspace_bytes(M, N, K), dtype=torch.uint8, device="cuda")
 
@@ -230,72 +303,249 @@ def measure_group(ms=(1, 8, 16), reps=20):
                         "quantize included, graph replay", "points": points}
 
 
-def read_probe(nbytes=1 << 30, reps=10):
-    """What a plain read of nbytes achieves on this device (torch.sum over a
-    fresh fp32 buffer, so the Infinity Cache holds at most a quarter of it):
-    a reference beside the published 8 TB/s, not a kernel of this library."""
-    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
-    y = torch.ones_like(x)
+def probes(reps=10):
+    """This device's own ceilings, from the library's measurement kernels:
+    stream reads of 28 MB (one decode-shape weight matrix), 95 MB and 1 GiB,
+    each buffer rotated with others so that >= 768 MB lie between two reads
+    of it (the Infinity Cache holds 256 MB); a 1 GiB stream write; and
+    back-to-back int8 and bf16 MFMA instructions on every SIMD."""
     stream = torch.cuda.current_stream()
-    for _ in range(2):
-        x.sum()
-    t = time_events(lambda: (x.sum(), y.sum()), reps, stream) / 2
-    del x, y
+    sink = torch.empty(65536, dtype=torch.int32, device="cuda")
+    out = {"read": [], "write": None, "mfma": {}}
+    for nbytes in (27_852_800, 95_027_200, 1 << 30):
+        n = max(2, math.ceil((1 << 30) * 0.75 / nbytes) + 1)
+        bufs = [torch.full((nbytes,), i, dtype=torch.uint8, device="cuda") for i in range(n)]
+        k = [0]
+
+        def rd():
+            iq.probe_read(bufs[k[0] % n], sink, grid=4096)
+            k[0] += 1
+        for _ in range(n):
+            rd()
+        t = time_events(rd, reps * n if nbytes < (1 << 30) else reps, stream)
+        out["read"].append({"bytes": nbytes, "ms": t, "GBs": nbytes / (t * 1e-3) / 1e9,
+                            "frac_of_8TBs": nbytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, "buffers": n})
+        del bufs
+    buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    iq.probe_write(buf)
+    t = time_events(lambda: iq.probe_write(buf), reps, stream)
+    out["write"] = {"bytes": 1 << 30, "ms": t, "GBs": (1 << 30) / (t * 1e-3) / 1e9}
+    del buf
     torch.cuda.empty_cache()
-    return {"bytes": nbytes, "ms": t, "GBs": nbytes / (t * 1e-3) / 1e9, "kernel": "torch.sum (fp32, 1 GiB)"}
+    grid, iters = 2048, 2000
+    res = torch.empty(grid * 256, dtype=torch.int32, device="cuda")
+    resf = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+    for kind, name, flops, peak, o in ((iq.PROBE_MFMA_I8, "int8", 65536, INT8_PEAK_TOPS, res),
+                                       (iq.PROBE_MFMA_BF16, "bf16", 32768, BF16_PEAK_TFLOPS, resf)):
+        iq.probe_mfma(kind, 10, o, grid)
+        t = time_events(lambda: iq.probe_mfma(kind, iters, o, grid), 3, stream)
+        rate = grid * 4 * 4 * iters * flops / (t * 1e-3) / 1e12
+        out["mfma"][name] = {"T_per_s": rate, "published_peak": peak, "frac": rate / peak,
+                             "instructions_per_wave": 4 * iters, "waves": grid * 4}
+    return out
 
 
-def point_record(N, K, M, path, t_call, t_kern, t_eager=None):
-    wb = 0.53125 * N * K
-    ops = 2.0 * M * N * K
-    rec = {"N": N, "K": K, "M": M, "path": iq.path_name(path), "ms": t_call, "eager_ms": t_eager,
-           "weight_GBs": wb / (t_call * 1e-3) / 1e9,
-           "int8_TOPS": ops / (t_call * 1e-3) / 1e12,
-           "hbm_frac": algo_bytes_call(M, N, K) / (t_call * 1e-3) / 1e9 / HBM_PEAK_GBS}
-    if t_kern is not None:
-        rec["kernel_ms"] = t_kern
-        rec["kernel_GBs"] = algo_bytes_kernel(M, N, K) / (t_kern * 1e-3) / 1e9
-        rec["kernel_hbm_frac"] = rec["kernel_GBs"] / HBM_PEAK_GBS
-        rec["kernel_mfma_frac"] = ops / (t_kern * 1e-3) / 1e12 / INT8_PEAK_TOPS
-    rec["mfma_frac"] = rec["int8_TOPS"] / INT8_PEAK_TOPS
-    # impossible-throughput flag: faster than the card can move the bytes
-    rec["impossible"] = bool(rec["hbm_frac"] > 1.0 or rec.get("kernel_hbm_frac", 0) > 1.0
-                             or rec["mfma_frac"] > 1.0)
-    return rec
-
-
-def cpu_baseline(wl, N, K, ms, target_s=12.0):
-    """The oracle (as it stands) on a sample of output columns of the same
-    sweep; returns weight-GB/s of that sample."""
+def cpu_baseline(points, target_s=12.0):
+    """The oracle (as it stands, all host threads) on a column sample of the
+    same 52 calls (quantization included), in weight-GB/s of the sample.  The
+    sample is the same fraction of every point's output columns, sized so the
+    pass takes about target_s."""
     import oracle
     o = oracle.get()
-    W = wl.w(N, K)
-    Xs = {M: wl.x(M, K, N=N) for M in ms}
+    cache = {}
 
-    def run(ncols):
-        Ws = np.ascontiguousarray(W[:ncols])
-        t0 = time.perf_counter()
-        for M in ms:
-            o.gemm_q8_1(Ws, o.quantize_q8_1(Xs[M]), K)
-        return time.perf_counter() - t0
+    def run(frac):
+        t = 0.0
+        wbytes = 0.0
+        for wl, N, K, M in points:
+            ncols = max(1, int(round(frac * N)))
+            key = (wl.cid, N, K)
+            if key not in cache:
+                cache.clear()
+                cache[key] = wl.w(N, K)
+            W = np.ascontiguousarray(cache[key][:ncols])
+            X = wl.x(M, K, N=N)
+            t0 = time.perf_counter()
+            o.gemm_q8_1(W, o.quantize_q8_1(X), K)
+            t += time.perf_counter() - t0
+            wbytes += 0.53125 * ncols * K
+        return t, wbytes
 
-    probe = 64
-    t = run(probe)
-    ncols = int(min(N, max(probe, probe * target_s / max(t, 1e-3))))
-    reps, t = 0, 0.0
-    while reps == 0 or t < target_s:      # the whole sweep can take well under target_s
-        t += run(ncols)
-        reps += 1
-    wbytes = 0.53125 * ncols * K * len(ms) * reps
+    # grow the sample until one pass takes at least a quarter of target_s,
+    # then size it to target_s (each pass has a fixed cost per call)
+    frac = 2e-4
+    t, _ = run(frac)
+    while t < target_s / 4 and frac < 1.0:
+        frac = min(1.0, frac * 4)
+        t, _ = run(frac)
+    frac = min(1.0, frac * target_s / max(t, 1e-3))
+    t, wbytes = run(frac)
     return {"value": wbytes / t / 1e9, "unit": "weight-GB/s", "cores": o.threads(), "kind": "oracle",
-            "sample": f"{ncols} of {N} output columns, every M in {list(ms)}, quantize included, "
-                      f"{reps} pass(es), {t:.1f} s"}
+            "sample": f"{frac * 100:.3f}% of the output columns of each of the {len(points)} calls "
+                      f"(at least one), quantize included, {t:.1f} s"}
+
+
+def dominant_rooflines(recs):
+    """Per matmul kernel, the point where it takes the most time: its
+    algorithmic work per launch over the kernel's average duration against
+    the roofline that binds at that point (HBM below M ~ 166, int8 MFMA
+    above); the headline entry is the kernel with the largest share of the
+    step's kernel time."""
+    by_kernel = {}
+    for r in recs:
+        if r.get("kernel_ms") is None:
+            continue
+        by_kernel.setdefault(r["kernel"], []).append(r)
+    out = []
+    for k, rs in by_kernel.items():
+        r = max(rs, key=lambda r: r["kernel_ms"])
+        M, N, K = r["M"], r["N"], r["K"]
+        if r["kernel_hbm_frac"] >= r["kernel_mfma_frac"]:
+            ent = {"bound": "hbm", "achieved": algo_bytes_kernel(M, N, K) / (r["kernel_ms"] * 1e-3) / 1e9,
+                   "peak": HBM_PEAK_GBS, "unit": "GB/s", "work_per_launch": algo_bytes_kernel(M, N, K),
+                   "work_unit": "bytes (0.53125 per weight + 1.125 per activation + 4 per output)"}
+        else:
+            ent = {"bound": "mfma", "achieved": 2.0 * M * N * K / (r["kernel_ms"] * 1e-3) / 1e12,
+                   "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s", "op": "int8 multiply-add = 2 ops",
+                   "work_per_launch": 2.0 * M * N * K, "work_unit": "int8 ops (2*M*N*K)",
+                   "valu_ceiling_frac": VALU_CEILING_FRAC}
+        ent["frac"] = ent["achieved"] / ent["peak"]
+        ent.update({"kernel": k, "M": M, "N": N, "K": K, "avg_launch_ms": r["kernel_ms"],
+                    "share_of_kernel_time": sum(x["kernel_ms"] for x in rs) /
+                    sum(x["kernel_ms"] for x in recs if x.get("kernel_ms") is not None)})
+        ent["traffic_bytes_per_launch"] = traffic_for(k, M, N, K)
+        ent["traffic"] = (None if ent["traffic_bytes_per_launch"] is None else
+                          ent["traffic_bytes_per_launch"] / (r["kernel_ms"] * 1e-3) / 1e9)
+        out.append(ent)
+    out.sort(key=lambda e: -e["share_of_kernel_time"])
+    return out
+
+
+def format_points(reps=20):
+    """A few points with IQ4_NL and Q4_0 weights (iq4xs_gemm_fmt, AUTO)."""
+    out = []
+    for fmt, name in ((iq.FMT_IQ4_NL, "IQ4_NL"), (iq.FMT_Q4_0, "Q4_0")):
+        for wl, M in ((synth.DECODE_ATTN, 1), (synth.DECODE_ATTN, 16), (synth.MLP_UP, 64), (synth.MLP_DOWN, 96)):
+            N, K = wl.shapes[0]
+            rot = Rotation(synth.weights18((wl.cid, N, K, 0), N, K))
+            X = torch.from_numpy(wl.x(M, K, N=N)).cuda()
+            t_call, _, _ = measure_point(rot, X, N, K, iq.PATH_AUTO, reps=reps, fmt=fmt)
+            wb = 0.5625 * N * K
+            out.append({"format": name, "N": N, "K": K, "M": M, "ms": t_call,
+                        "weight_GBs": wb / (t_call * 1e-3) / 1e9,
+                        "hbm_frac": (wb + 6.25 * M * K + 4 * M * N) / (t_call * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                        "int8_TOPS": 2.0 * M * N * K / (t_call * 1e-3) / 1e12})
+            del rot
+            torch.cuda.empty_cache()
+    return out
+
+
+# ------------------------------------------------------------- profiling
+def _marker(i, buf):
+    """A tiny write-probe launch whose position in a kernel trace separates
+    the dispatches of consecutive points."""
+    iq.probe_write(buf, value=i, grid=1)
+
+
+def profile_points():
+    """For --check-trace under rocprofv3 --kernel-trace: every point's full
+    iq4xs_gemm call (AUTO) twice, a marker launch before each point."""
+    marker = torch.empty(256, dtype=torch.uint8, device="cuda")
+    plan = []
+    cur = None
+    for i, (wl, N, K, M) in enumerate(sweep_points()):
+        if cur != (wl.cid, N, K):
+            W = torch.from_numpy(wl.w(N, K)).cuda()
+            cur = (wl.cid, N, K)
+        X = torch.from_numpy(wl.x(M, K, N=N)).cuda()
+        Y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        _marker(i, marker)
+        for _ in range(2):
+            iq.gemm(W, X, out=Y)
+        torch.cuda.synchronize()
+        path = iq.dispatch(M, N, K)
+        plan.append({"point": i, "M": M, "N": N, "K": K, "path": iq.path_name(path),
+                     "kernel": kernel_name(M, N, K, path), "calls": 2})
+        print(f"[profile-points] {i} M={M} N={N} K={K} {iq.path_name(path)}", flush=True)
+    _marker(len(plan), marker)
+    torch.cuda.synchronize()
+    return plan
+
+
+def check_trace(trace_dir, out, cmd):
+    """Between consecutive marker launches of a --profile-points trace: the
+    kernels each call launched.  Every call must launch the quantizer and a
+    matmul kernel of its path, and the matmul kernel must be the one
+    kernel_name() (which the roofline entries use) names."""
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_trace.csv under {trace_dir}")
+    rows = sorted(csv.DictReader(open(files[0])), key=lambda r: int(r["Start_Timestamp"]))
+
+    def short(n):
+        # "ns::(anonymous namespace)::k_name<...>(args)" -> "k_name"
+        n = n.replace("void ", "").replace("(anonymous namespace)", "anon")
+        return n.split("(")[0].split("<")[0].split("::")[-1].strip()
+    groups, cur = [], None
+    for r in rows:
+        k = short(r["Kernel_Name"])
+        if k == "k_probe_write":
+            if cur is not None:
+                groups.append(cur)
+            cur = []
+        elif cur is not None:
+            cur.append((k, (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3))
+    pts = sweep_points()
+    families = {"GEMV": {"k_gemv"}, "MMQ": {"k_mmv", "k_mmqt", "k_mmq"}, "DEQ_BF16": {"k_gemm_bf16"}}
+    lines = ["# kernels launched per call, from a rocprofv3 kernel trace of bench.py --profile-points",
+             f"# command: {cmd}",
+             "# every call of every point launches the quantizer and a matmul kernel of the path the",
+             "# dispatcher names, and that kernel is the one the benchmark's roofline entries attribute",
+             "# point  M  N  K  path  expected  launched (per call)  matmul-us (mean)  ok"]
+    bad = 0
+    if len(groups) != len(pts):
+        raise SystemExit(f"{len(groups)} marker groups, {len(pts)} points")
+    for i, ((wl, N, K, M), g) in enumerate(zip(pts, groups)):
+        names = [k for k, _ in g]
+        path = iq.path_name(iq.dispatch(M, N, K))
+        expect = kernel_name(M, N, K, iq.PATHS[path])
+        per_call = names[:len(names) // 2]
+        mat = [k for k in per_call if k.startswith(("k_gemv", "k_mmv", "k_mmqt", "k_mmq", "k_gemm_bf16"))]
+        ok = (len(names) % 2 == 0 and names[:len(names) // 2] == names[len(names) // 2:] and
+              per_call[0] == "k_quantize" and mat and mat[0] == expect and mat[0] in families[path])
+        bad += not ok
+        mus = [d for k, d in g if k == expect]
+        lines.append(f"{i:3d} {M:4d} {N:6d} {K:6d}  {path:8s} {expect:7s} {'+'.join(per_call):40s} "
+                     f"{sum(mus) / max(len(mus), 1):9.2f}  {'ok' if ok else 'MISMATCH'}")
+    lines.append(f"# {len(pts) - bad} of {len(pts)} points ok")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    if bad:
+        raise SystemExit(f"{bad} points launched other kernels than expected")
+
+
+def _probe_pair():
+    """The calibration read and write of known bytes (PROBE_BYTES each),
+    four times, the read buffer evicted from the Infinity Cache in between by
+    writes to three others."""
+    bufs = [torch.empty(PROBE_BYTES, dtype=torch.uint8, device="cuda") for _ in range(4)]
+    sink = torch.empty(65536, dtype=torch.int32, device="cuda")
+    for i in range(4):
+        for j in range(1, 4):
+            iq.probe_write(bufs[(i + j) % 4], value=j)
+        torch.cuda.synchronize()
+        iq.probe_read(bufs[i], sink)
+        torch.cuda.synchronize()
+    print(f"[profile] read and write probes of {PROBE_BYTES} bytes", flush=True)
+    del bufs
+    torch.cuda.empty_cache()
 
 
 def profile_run():
-    """Fixed launches for rocprofv3: per M of the decode sweep, 20 launches
-    of the matmul kernel alone (rotated weights, as in the timed step), then
-    a calibration copy of COPY_BYTES, 4 times."""
+    """Fixed launches for rocprofv3 --pmc: per M of the decode sweep, 20
+    launches of the matmul kernel alone (rotated weights, as in the timed
+    step), then the calibration probes."""
     wl = synth.DECODE_ATTN
     (N, K), ms = wl.shapes[0], wl.ms
     rot = Rotation(wl.w(N, K))
@@ -308,24 +558,16 @@ def profile_run():
             iq.gemm_act(rot.next(), act, M, K, path=path, out=Y, y_zeroed=True)
         torch.cuda.synchronize()
         print(f"[profile-run] M={M} {kernel_name(M, N, K, path)} x20", flush=True)
-    # the copy's source must come from HBM, not from the 256 MB Infinity
-    # Cache: fill four buffers, then copy the first (three later fills have
-    # evicted it), once per buffer
-    bufs = [torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(float(i)) for i in range(4)]
-    dst = torch.empty_like(bufs[0])
-    for i in range(4):
-        for j in range(1, 4):
-            bufs[(i + j) % 4].fill_(float(j))
-        dst.copy_(bufs[i])
-    torch.cuda.synchronize()
-    print(f"[profile-run] copy {COPY_BYTES} bytes x4", flush=True)
+    del rot
+    torch.cuda.empty_cache()
+    _probe_pair()
 
 
 def profile_shapes(specs):
     """Fixed launches for rocprofv3 at given shapes ("MxNxK", comma
     separated): per shape, 20 launches of the matmul kernel(s) alone
     (gemm_act, rotated weights), inputs of the workload the shape belongs to
-    (else the prefill recipe)."""
+    (else the prefill recipe); then the calibration probes."""
     for spec in specs.split(","):
         M, N, K = (int(v) for v in spec.split("x"))
         wl = next((w for w in synth.WORKLOADS if (N, K) in w.shapes), synth.WORKLOADS[-1])
@@ -340,6 +582,7 @@ def profile_shapes(specs):
         print(f"[profile-shapes] M={M} N={N} K={K} {kernel_name(M, N, K, path)} x20", flush=True)
         del rot
         torch.cuda.empty_cache()
+    _probe_pair()
 
 
 def _counter_rows(d):
@@ -352,57 +595,141 @@ def _counter_rows(d):
     return rows
 
 
+def _probe_scales(fetch_rows, write_rows):
+    """true bytes per counted byte: FETCH_SIZE of the read probe and
+    WRITE_SIZE of the write probe over their known sizes (the probes of
+    PROBE_BYTES; the small marker writes are ignored)."""
+    def per(rows, counter, kname):
+        acc = {}
+        for r in rows:
+            if r["Counter_Name"] == counter and kname in r["Kernel_Name"]:
+                acc[r["Dispatch_Id"]] = acc.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+        return [v for v in acc.values() if v * 1024.0 > PROBE_BYTES / 16]
+    f = per(fetch_rows, "FETCH_SIZE", "k_probe_read")
+    w = per(write_rows, "WRITE_SIZE", "k_probe_write")
+    if not f or not w:
+        raise SystemExit("calibration probes not found in the counter runs")
+    fk, wk = sum(f) / len(f), sum(w) / len(w)
+    return fk, wk, PROBE_BYTES / (fk * 1024.0), PROBE_BYTES / (wk * 1024.0)
+
+
 def summarize_pmc(fetch_dir, write_dir, out, cmd_fetch, cmd_write):
-    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the matmul kernels and of
-    the calibration copy -> calibrated HBM bytes per launch."""
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the decode sweep's matmul
+    kernels, calibrated by the read and write probes -> HBM bytes per launch."""
+    fr, wr = _counter_rows(fetch_dir), _counter_rows(write_dir)
+
     def per_kernel(rows, counter):
         acc = {}
         for r in rows:
             if r["Counter_Name"] != counter:
                 continue
             name = r["Kernel_Name"]
-            key = ("copy" if "copyBuffer" in name else
-                   "k_mmv" if "k_mmv" in name else "k_gemv" if "k_gemv" in name else
-                   "k_mmqt_fix" if "k_mmqt_fix" in name else "k_mmqt" if "k_mmqt" in name else
-                   "k_mmq" if "k_mmq" in name else None)
+            key = ("k_mmv" if "k_mmv" in name else "k_gemv" if "k_gemv" in name else None)
             if key is None:
                 continue
             label = name.split("Cfg<")[1].split(">")[0].replace(" ", "") if "Cfg<" in name else ""
             acc.setdefault((key, label), {}).setdefault(r["Dispatch_Id"], 0.0)
             acc[(key, label)][r["Dispatch_Id"]] += float(r["Counter_Value"])
-        return {k: list(v.values()) for k, v in acc.items()}
-    fetch_all = per_kernel(_counter_rows(fetch_dir), "FETCH_SIZE")
-    write_all = per_kernel(_counter_rows(write_dir), "WRITE_SIZE")
-    # the calibration copies are the copyBuffer dispatches far above the
-    # weight-copy sizes; everything else is averaged per kernel
-    cf = [v for (k, _), vs in fetch_all.items() if k == "copy" for v in vs if v * 1024.0 > COPY_BYTES / 16]
-    cw = [v for (k, _), vs in write_all.items() if k == "copy" for v in vs if v * 1024.0 > COPY_BYTES / 16]
-    fetch = {k: sum(v) / len(v) for k, v in fetch_all.items()}
-    write = {k: sum(v) / len(v) for k, v in write_all.items()}
-    if not cf or not cw:
-        raise SystemExit("calibration copy not found in the counter runs")
-    f_scale = COPY_BYTES / (sum(cf) / len(cf) * 1024.0)       # true bytes per counted byte
-    w_scale = COPY_BYTES / (sum(cw) / len(cw) * 1024.0)
+        return {k: sum(v.values()) / len(v) for k, v in acc.items()}
+    fk, wk, f_scale, w_scale = _probe_scales(fr, wr)
+    fetch, write = per_kernel(fr, "FETCH_SIZE"), per_kernel(wr, "WRITE_SIZE")
     wl = synth.DECODE_ATTN
     (N, K), ms = wl.shapes[0], wl.ms
     lines = [f"# HBM traffic per launch from rocprofv3 counters, decode sweep N={N} K={K}",
              f"# fetch run: {cmd_fetch}", f"# write run: {cmd_write}",
-             f"copy_bytes {COPY_BYTES}",
-             f"copy_fetch_kib {sum(cf) / len(cf):.1f}  fetch_scale {f_scale:.4f}",
-             f"copy_write_kib {sum(cw) / len(cw):.1f}  write_scale {w_scale:.4f}",
+             f"# calibration: a read of {PROBE_BYTES} bytes (probe_read, plain 16-byte loads) and a write of",
+             f"# {PROBE_BYTES} bytes (probe_write, plain 16-byte stores), each buffer evicted from the Infinity Cache",
+             f"probe_bytes {PROBE_BYTES}",
+             f"probe_fetch_kib {fk:.1f}  fetch_scale {f_scale:.4f}",
+             f"probe_write_kib {wk:.1f}  write_scale {w_scale:.4f}",
              f"source_hash k_mmv {source_hash('k_mmv')}",
-             "# kernel config  fetch_kib  write_kib  calibrated_bytes  algorithmic_bytes(M)"]
-    for (k, label), fk in sorted(fetch.items()):
-        if k == "copy":
-            continue
-        wk = write.get((k, label), 0.0)
-        total = fk * 1024.0 * f_scale + wk * 1024.0 * w_scale
-        lines.append(f"traffic {k} <{label}> {fk:.1f} {wk:.1f} {total:.0f}")
+             f"source_hash k_gemv {source_hash('k_gemv')}",
+             "# kernel config  fetch_kib  write_kib  calibrated_bytes"]
+    for (k, label), f in sorted(fetch.items()):
+        w = write.get((k, label), 0.0)
+        lines.append(f"traffic {k} <{label}> {f:.1f} {w:.1f} {f * 1024.0 * f_scale + w * 1024.0 * w_scale:.0f}")
     for M in ms:
         lines.append(f"algorithmic M={M} {algo_bytes_kernel(M, N, K):.0f}")
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+
+
+def summarize_pmc_shapes(fetch_dir, write_dir, out, cmd_fetch, cmd_write, specs):
+    """Per shape of a --profile-shapes run (20 launches each, in order): mean
+    FETCH_SIZE / WRITE_SIZE per launch of the tile kernel and of its
+    shared-tile kernel, calibrated by the probes of the same runs, against
+    the algorithmic bytes."""
+    fr, wr = _counter_rows(fetch_dir), _counter_rows(write_dir)
+    fk, wk, f_scale, w_scale = _probe_scales(fr, wr)
+
+    def per_dispatch(rows, counter):
+        acc = {}
+        for r in rows:
+            if r["Counter_Name"] == counter and "k_mmqt" in r["Kernel_Name"]:
+                k = (int(r["Dispatch_Id"]), "fix" if "k_mmqt_fix" in r["Kernel_Name"] else "main")
+                acc[k] = acc.get(k, 0.0) + float(r["Counter_Value"])
+        return acc
+    fd, wd = per_dispatch(fr, "FETCH_SIZE"), per_dispatch(wr, "WRITE_SIZE")
+    shapes = [tuple(int(v) for v in sp.split("x")) for sp in specs.split(",")]
+    lines = ["# HBM traffic per launch of the tile kernel from rocprofv3 counters (20 launches per shape)",
+             f"# fetch run: {cmd_fetch}", f"# write run: {cmd_write}",
+             f"# calibration by the runs' own probes ({PROBE_BYTES} bytes read / written): "
+             f"fetch x{f_scale:.4f} ({fk:.1f} KiB counted), write x{w_scale:.4f} ({wk:.1f} KiB counted)",
+             f"source_hash k_mmqt {source_hash('k_mmqt')}",
+             "# M N K  kernel  fetch_MB  write_MB  calibrated_MB  algorithmic_MB (W + planes + Y)"]
+    sums = {}
+    n_main = -1
+    for (i, part) in sorted(set(fd) | set(wd)):
+        if part == "main":
+            n_main += 1
+        shape = n_main // 20
+        acc = sums.setdefault((shape, part), [0.0, 0.0, 0])
+        acc[0] += fd.get((i, part), 0.0)
+        acc[1] += wd.get((i, part), 0.0)
+        acc[2] += 1
+    for (shape, part), (f, w, cnt) in sorted(sums.items(), key=lambda kv: (kv[0][1] != "main", kv[0][0])):
+        if shape >= len(shapes):
+            continue
+        M, N, K = shapes[shape]
+        fb = f / cnt * 1024.0 * f_scale
+        wb = w / cnt * 1024.0 * w_scale
+        lines.append(f"{M} {N} {K}  {'k_mmqt' if part == 'main' else 'k_mmqt_fix'}  {fb / 1e6:.1f}  {wb / 1e6:.1f}  "
+                     f"{(fb + wb) / 1e6:.1f}  {algo_bytes_kernel(M, N, K) / 1e6 if part == 'main' else 0:.1f}")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def traffic_for(kernel, M, N, K):
+    """Calibrated HBM bytes per launch of `kernel` at (M, N, K) from the
+    committed counter summaries, or None when there is none for that point or
+    the kernel's source changed since it was measured."""
+    if kernel in ("k_mmv", "k_gemv") and os.path.exists(TRAFFIC_FILE) and (N, K) == (10240, 5120):
+        lines = open(TRAFFIC_FILE).read().splitlines()
+        if f"source_hash {kernel} {source_hash(kernel)}" not in lines:
+            return None
+        labels = {1: "1,4,8,3,false,0", 2: "1,4,8,3,true,0", 4: "2,4,8,3,true,0", 8: "4,8,4,3,false,0",
+                  16: "8,16,4,3,false,0"}
+        want = f"<{labels.get(M, '')}>" if kernel == "k_mmv" else "<>"
+        for ln in lines:
+            p = ln.split()
+            if len(p) == 6 and p[0] == "traffic" and p[1] == kernel and p[2] == want:
+                return float(p[5])
+        return None
+    if kernel == "k_mmqt" and os.path.exists(TILE_TRAFFIC_FILE):
+        lines = open(TILE_TRAFFIC_FILE).read().splitlines()
+        if f"source_hash k_mmqt {source_hash('k_mmqt')}" not in lines:
+            return None
+        total = 0.0
+        found = False
+        for ln in lines:
+            p = ln.split()
+            if len(p) == 8 and p[:3] == [str(M), str(N), str(K)]:
+                total += float(p[6]) * 1e6
+                found = True
+        return total if found else None
+    return None
 
 
 SQ_PASSES = (("SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU",
@@ -476,6 +803,8 @@ def summarize_sq(dirs, trace_dirs, out, cmds, specs=""):
         f.write("\n".join(lines) + "\n")
 
 
+
+
 def summarize_trace(trace_dir, out, cmd, title):
     """The kernel-trace statistics of a rocprofv3 --stats run as a short text
     table (kernel, calls, average / min / max microseconds, share of GPU
@@ -485,9 +814,10 @@ def summarize_trace(trace_dir, out, cmd, title):
         raise SystemExit(f"no kernel_stats.csv under {trace_dir}")
     with open(files[0]) as fh:
         rows = list(csv.DictReader(fh))
+
     def short(name):
         name = name.replace("iq4xs::(anonymous namespace)::", "").replace("iq4xs::", "")
-        return name.split("(")[0] if not name.startswith("void k_") else name.split("(")[0]
+        return name.replace("(anonymous namespace)::", "").split("(")[0]
     lines = [f"# rocprofv3 kernel-trace statistics: {title}", f"# command: {cmd}",
              f"{'kernel':60s} {'calls':>6s} {'avg_us':>8s} {'min_us':>8s} {'max_us':>8s} {'pct':>6s}"]
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
@@ -498,71 +828,39 @@ def summarize_trace(trace_dir, out, cmd, title):
     print("\n".join(lines))
 
 
-def summarize_pmc_shapes(fetch_dir, write_dir, out, cmd_fetch, cmd_write, specs):
-    """Per shape of a --profile-shapes run (20 launches each, in order): mean
-    FETCH_SIZE / WRITE_SIZE per launch of the tile kernel and of its
-    shared-tile kernel, calibrated with the copy runs of a --profile-run
-    summary (TRAFFIC_FILE), against the algorithmic bytes."""
-    with open(TRAFFIC_FILE) as fh:
-        sc = {ln.split()[2]: float(ln.split()[3]) for ln in fh if ln.startswith("copy_") and "scale" in ln}
-    f_scale, w_scale = sc["fetch_scale"], sc["write_scale"]
-    def per_dispatch(d, counter):
-        acc = {}
-        for r in _counter_rows(d):
-            if r["Counter_Name"] == counter and "k_mmqt" in r["Kernel_Name"]:
-                k = (int(r["Dispatch_Id"]), "fix" if "k_mmqt_fix" in r["Kernel_Name"] else "main")
-                acc[k] = acc.get(k, 0.0) + float(r["Counter_Value"])
-        return acc
-    fd, wd = per_dispatch(fetch_dir, "FETCH_SIZE"), per_dispatch(write_dir, "WRITE_SIZE")
+def summarize_trace_shapes(trace_dir, out, cmd, specs):
+    """Per shape of a --profile-shapes kernel trace (20 launches per shape,
+    in order): the tile kernel's and its summing kernel's durations."""
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_trace.csv under {trace_dir}")
+    rows = sorted(csv.DictReader(open(files[0])), key=lambda r: int(r["Start_Timestamp"]))
     shapes = [tuple(int(v) for v in sp.split("x")) for sp in specs.split(",")]
-    lines = ["# HBM traffic per launch of the tile kernel from rocprofv3 counters (20 launches per shape)",
-             f"# fetch run: {cmd_fetch}", f"# write run: {cmd_write}",
-             f"# scales from the copy calibration of {os.path.basename(TRAFFIC_FILE)}: fetch x{f_scale:.4f}, write x{w_scale:.4f}",
-             f"source_hash k_mmqt {source_hash('k_mmqt')}",
-             "# M N K  kernel  fetch_MB  write_MB  calibrated_MB  algorithmic_MB (W + planes + Y)"]
-    # dispatches in launch order: 20 tile-kernel launches per shape, each
-    # followed by its summing kernel where the shape has one
-    sums = {}
-    n_main = -1
-    for (i, part) in sorted(set(fd) | set(wd)):
-        if part == "main":
-            n_main += 1
-        shape = n_main // 20
-        acc = sums.setdefault((shape, part), [0.0, 0.0, 0])
-        acc[0] += fd.get((i, part), 0.0)
-        acc[1] += wd.get((i, part), 0.0)
-        acc[2] += 1
-    for (shape, part), (f, w, cnt) in sorted(sums.items(), key=lambda kv: (kv[0][1] != "main", kv[0][0])):
-        if shape >= len(shapes):
+    per, n_main = {}, -1
+    for r in rows:
+        name = r["Kernel_Name"]
+        if "k_mmqt" not in name:
             continue
-        M, N, K = shapes[shape]
-        fb = f / cnt * 1024.0 * f_scale
-        wb = w / cnt * 1024.0 * w_scale
-        lines.append(f"{M} {N} {K}  {'k_mmqt' if part == 'main' else 'k_mmqt_fix'}  {fb / 1e6:.1f}  {wb / 1e6:.1f}  "
-                     f"{(fb + wb) / 1e6:.1f}  {algo_bytes_kernel(M, N, K) / 1e6 if part == 'main' else 0:.1f}")
+        part = "k_mmqt_fix" if "k_mmqt_fix" in name else "k_mmqt"
+        if part == "k_mmqt":
+            n_main += 1
+        per.setdefault((n_main // 20, part), []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+    lines = ["# tile-kernel durations per shape from a rocprofv3 kernel trace (20 launches per shape, gemm_act, "
+             "rotated weights)", f"# command: {cmd}", f"source_hash k_mmqt {source_hash('k_mmqt')}",
+             "# M N K  kernel  calls  avg_us  min_us  max_us"]
+    for (i, part), d in sorted(per.items()):
+        if i < len(shapes):
+            M, N, K = shapes[i]
+            lines.append(f"{M} {N} {K}  {part}  {len(d)}  {sum(d) / len(d):.2f}  {min(d):.2f}  {max(d):.2f}")
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
-def traffic_for(kernel, label):
-    """Calibrated bytes per launch from the committed summary, or None when
-    the summary is missing or the kernel source changed since."""
-    if not os.path.exists(TRAFFIC_FILE):
-        return None
-    with open(TRAFFIC_FILE) as fh:
-        lines = fh.read().splitlines()
-    if f"source_hash {kernel} {source_hash(kernel)}" not in lines:
-        return None
-    for ln in lines:
-        parts = ln.split()
-        if len(parts) == 6 and parts[0] == "traffic" and parts[1] == kernel and parts[2] == f"<{label}>":
-            return float(parts[5])
-    return None
-
-
 def run_sweep(path_out):
-    """Every (shape, M, path) point of the five workloads -> JSONL."""
+    """Every (shape, M, path) point of the five workloads -> JSONL (with the
+    device's compute-unit count, which the dispatch table records)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
     with open(path_out, "w") as f:
         for wl in synth.WORKLOADS:
             for (N, K) in wl.shapes:
@@ -577,6 +875,7 @@ def run_sweep(path_out):
                     for p in paths:
                         rec = point_record(N, K, M, p, *measure_point(rot, X, N, K, p, reps=20))
                         rec["workload"] = wl.name
+                        rec["cus"] = cus
                         if p == iq.PATH_AUTO:
                             rec["auto"] = iq.path_name(iq.dispatch(M, N, K))
                         f.write(json.dumps(rec) + "\n")
@@ -587,46 +886,78 @@ def run_sweep(path_out):
                 torch.cuda.empty_cache()
 
 
+def summarize_sweep(jsonl, out, cmd):
+    """A --sweep JSONL as a compact text table (one line per shape, M and
+    path: us per call and us of the matmul kernel alone), the record behind
+    the dispatch table; iq4_xs_q8_amd.calibrate reads this table as well."""
+    recs = [json.loads(line) for line in open(jsonl)]
+    cus = sorted({r.get("cus") for r in recs if r.get("cus")})
+    lines = ["# per-call device time of every (shape, M, path) point of the five workloads",
+             f"# command: {cmd}", f"# compute units: {','.join(map(str, cus))}",
+             "# N K M path us_per_call us_kernel"]
+    for r in recs:
+        if r["path"] == "AUTO":
+            continue
+        k = r.get("kernel_ms")
+        lines.append(f"{r['N']} {r['K']} {r['M']} {r['path']} {r['ms'] * 1e3:.2f} "
+                     f"{'-' if k is None else f'{k * 1e3:.2f}'}")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(f"{len(lines) - 4} points -> {out}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--sweep", default=None, help="also time every workload point -> JSONL")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--sweep", default=None, help="also time every workload point and path -> JSONL")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--profile-run", action="store_true", help="fixed launches for rocprofv3")
+    ap.add_argument("--profile-run", action="store_true", help="fixed launches for rocprofv3 --pmc")
     ap.add_argument("--profile-shapes", default=None, help="MxNxK,...: fixed launches for rocprofv3")
+    ap.add_argument("--profile-points", action="store_true", help="every point's call, markers between")
+    ap.add_argument("--check-trace", metavar="TRACE_DIR")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR")
     ap.add_argument("--summarize-pmc-shapes", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "SHAPES"))
     ap.add_argument("--summarize-sq", nargs="+", metavar="DIR", help="SQ counter runs -> instruction mix")
+    ap.add_argument("--summarize-sweep", metavar="JSONL")
+    ap.add_argument("--summarize-trace-shapes", nargs=2, metavar=("TRACE_DIR", "SHAPES"))
     ap.add_argument("--trace-dir", default=None, help="kernel-trace runs of the same launches, comma-separated")
     ap.add_argument("--shapes", default="", help="MxNxK,... of the --profile-shapes runs")
     ap.add_argument("--cmd", default="")
     ap.add_argument("--title", default="")
-    ap.add_argument("--out", default=TRAFFIC_FILE)
+    ap.add_argument("--out", default=None)
     ap.add_argument("--cmd-fetch", default="")
     ap.add_argument("--cmd-write", default="")
     args = ap.parse_args()
     if args.summarize_pmc:
-        summarize_pmc(*args.summarize_pmc, args.out, args.cmd_fetch, args.cmd_write)
+        summarize_pmc(*args.summarize_pmc, args.out or TRAFFIC_FILE, args.cmd_fetch, args.cmd_write)
         return
+    for flag in ("summarize_pmc_shapes", "summarize_sq", "summarize_trace", "check_trace", "summarize_sweep"):
+        if getattr(args, flag) and not args.out:
+            raise SystemExit(f"--{flag.replace('_', '-')} needs --out")
     if args.summarize_pmc_shapes:
-        if args.out == TRAFFIC_FILE:
-            raise SystemExit("--summarize-pmc-shapes needs its own --out")
         summarize_pmc_shapes(*args.summarize_pmc_shapes[:2], args.out, args.cmd_fetch, args.cmd_write,
                              args.summarize_pmc_shapes[2])
         return
     if args.summarize_sq:
-        if args.out == TRAFFIC_FILE:
-            raise SystemExit("--summarize-sq needs its own --out")
         summarize_sq(args.summarize_sq, [d for d in (args.trace_dir or "").split(",") if d], args.out,
                      [c for c in args.cmd.split(";;") if c], args.shapes)
         return
     if args.summarize_trace:
-        if args.out == TRAFFIC_FILE:
-            raise SystemExit("--summarize-trace needs its own --out")
         summarize_trace(args.summarize_trace, args.out, args.cmd, args.title)
+        return
+    if args.summarize_sweep:
+        summarize_sweep(args.summarize_sweep, args.out, args.cmd)
+        return
+    if args.summarize_trace_shapes:
+        if not args.out:
+            raise SystemExit("--summarize-trace-shapes needs --out")
+        summarize_trace_shapes(args.summarize_trace_shapes[0], args.out, args.cmd, args.summarize_trace_shapes[1])
+        return
+    if args.check_trace:
+        check_trace(args.check_trace, args.out, args.cmd)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the matmul is built and measured on a single MI355X "
@@ -642,91 +973,82 @@ def main():
     if args.profile_shapes:
         profile_shapes(args.profile_shapes)
         return
+    if args.profile_points:
+        profile_points()
+        return
 
-    wl = synth.DECODE_ATTN
-    (N, K), ms = wl.shapes[0], wl.ms
-    rot = Rotation(wl.w(N, K), group=len(ms))
-    Xs = {M: torch.from_numpy(wl.x(M, K, N=N)).cuda() for M in ms}
-    Ys = {M: torch.empty((M, N), dtype=torch.float32, device="cuda") for M in ms}
-    wss = {M: torch.empty(iq.workspace_bytes(M, N, K), dtype=torch.uint8, device="cuda") for M in ms}
-
-    # One step = one iq4xs_gemm_ws call per M (quantization + matmul) on one
-    # stream.  The same calls recorded into a HIP graph per group of weight
-    # copies, as a decode loop might replay them, are timed beside it.
-    def step_on(ws_list):
-        for M, w in zip(ms, ws_list):
-            iq.gemm(w, Xs[M], out=Ys[M], workspace=wss[M])
-
-    groups = [rot.ws[i:i + len(ms)] for i in range(0, len(rot.ws), len(ms))]
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        step_on(groups[0])
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    graphs = []
-    for grp in groups:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            step_on(grp)
-        graphs.append(g)
+    t_setup = time.perf_counter()
+    pts = sweep_points()
+    rots, calls = {}, []
+    for wl, N, K, M in pts:
+        if (wl.cid, N, K) not in rots:
+            rots[(wl.cid, N, K)] = Rotation(wl.w(N, K))
+        X = torch.from_numpy(wl.x(M, K, N=N)).cuda()
+        Y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        ws = torch.empty(iq.workspace_bytes(M, N, K), dtype=torch.uint8, device="cuda")
+        calls.append((rots[(wl.cid, N, K)], X, Y, ws))
+    print(f"[bench] {len(pts)} points, {sum(len(r.ws) for r in rots.values())} weight copies, "
+          f"setup {time.perf_counter() - t_setup:.1f} s", file=sys.stderr, flush=True)
     stream = torch.cuda.current_stream()
 
-    def timed(fn, steps, warmup):
-        for i in range(warmup):
-            fn(i)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ev0.record(stream)
-        for i in range(steps):
-            fn(i)
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        return ev0.elapsed_time(ev1) / steps, time.perf_counter() - t0
+    # One step = one iq4xs_gemm_ws call per point (quantization + dispatch +
+    # matmul), in workload order, on one stream.
+    def step():
+        for rot, X, Y, ws in calls:
+            iq.gemm(rot.next(), X, out=Y, workspace=ws)
 
-    step_ms, wall = timed(lambda i: step_on(groups[i % len(groups)]), args.steps, args.warmup)
-    graph_ms, _ = timed(lambda i: graphs[i % len(graphs)].replay(), args.steps, args.warmup)
-    wbytes = 0.53125 * N * K * len(ms)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = ev0.elapsed_time(ev1) / args.steps
+    wbytes = sum(0.53125 * N * K for _, N, K, _ in pts)
+    ops = sum(2.0 * M * N * K for _, N, K, M in pts)
     value = wbytes / (step_ms * 1e-3) / 1e9
+    print(f"[bench] step {step_ms:.3f} ms ({value:.0f} weight-GB/s)", file=sys.stderr, flush=True)
 
-    per_m = []
-    for M in ms:
+    recs = []
+    for (wl, N, K, M), (rot, X, _, _) in zip(pts, calls):
         path = iq.dispatch(M, N, K)
-        per_m.append(point_record(N, K, M, path, *measure_point(rot, Xs[M], N, K, path)))
-    dom = max(per_m, key=lambda r: r["kernel_ms"])
-    dom_kernel = kernel_name(dom["M"], N, K, iq.PATHS[dom["path"]])
-    achieved = algo_bytes_kernel(dom["M"], N, K) / (dom["kernel_ms"] * 1e-3) / 1e9
-    label = {1: "1,4,8,3,false", 2: "1,4,8,3,true", 4: "2,4,8,3,true", 8: "4,8,4,3,false",
-             16: "8,16,4,3,false"}.get(dom["M"], "") if dom_kernel == "k_mmv" else ""
-    traffic = traffic_for(dom_kernel, label)
-    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS,
-                "traffic": None if traffic is None else traffic / (dom["kernel_ms"] * 1e-3) / 1e9,
-                "traffic_bytes_per_launch": traffic,
-                "kernel": dom_kernel, "M": dom["M"],
-                "bytes_per_launch": algo_bytes_kernel(dom["M"], N, K),
-                "avg_launch_ms": dom["kernel_ms"]}
-
+        r = point_record(N, K, M, path, *measure_point(rot, X, N, K, path))
+        r["workload"] = wl.name
+        recs.append(r)
+    del calls
+    print("[bench] per-point times done", file=sys.stderr, flush=True)
+    rl = dominant_rooflines(recs)
+    by = {(r["N"], r["K"], r["M"]): r for r in recs}
     out = {"metric": METRIC, "value": value, "unit": "weight-GB/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": step_ms,
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
-           "data": "synthetic (seeded IQ4_XS weights, N(0,1) activations with 1% outlier channels)",
-           "config": {"workload": "IQ4_XS x Q8_1 GEMM decode sweep, attention/GDN input projection "
-                                  "N=10240 K=5120, M in {1,2,4,8,16}, quantize included",
-                      "N": N, "K": K, "M": list(ms), "weight_copies": len(rot.ws)},
-           "wall_s": wall, "graph_ms_per_step": graph_ms,
-           "graph_weight_GBs": wbytes / (graph_ms * 1e-3) / 1e9, "per_m": per_m, "roofline": roofline}
-    del graphs
-    by_m = {r["M"]: r for r in per_m}
-    if 1 in by_m and 2 in by_m:
-        out["t_m2_over_m1"] = by_m[2]["ms"] / by_m[1]["ms"]
+           "data": "synthetic (seeded IQ4_XS weights; N(0,1) activations, 1% outlier channels x20 on the "
+                   "decode shape, sigma 0.5 on the MLP-down shape)",
+           "config": {"workload": "IQ4_XS x Q8_1 GEMM sweep M=1..512: 2048x2048 at M=4; N=10240 K=5120 at "
+                                  "M=1,2,4,8,16; N=17408 K=5120 at M=8..96; N=5120 K=17408 at M=1..96; nine "
+                                  "prefill shapes up to N=248320 at M=64,128,256,512 (52 calls per step, "
+                                  "quantize included)",
+                      "points": len(pts), "weight_bytes_per_step": wbytes,
+                      "weight_copies": sum(len(r.ws) for r in rots.values())},
+           "int8_TOPS": ops / (step_ms * 1e-3) / 1e12, "wall_s": wall,
+           "roofline": dict(rl[0]), "rooflines": rl, "points": recs}
+    del rots
+    torch.cuda.empty_cache()
+    if (10240, 5120, 1) in by and (10240, 5120, 2) in by:
+        out["t_m2_over_m1"] = by[(10240, 5120, 2)]["ms"] / by[(10240, 5120, 1)]["ms"]
+    out["probes"] = probes()
+    print("[bench] probes done", file=sys.stderr, flush=True)
     out["group"] = measure_group()
-    out["read_probe"] = read_probe()
+    out["formats"] = format_points()
+    print("[bench] group and formats done", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, N, K, ms)
+        out["cpu_baseline"] = cpu_baseline(pts)
     if args.sweep:
-        del rot
         torch.cuda.empty_cache()
         run_sweep(args.sweep)
     print(json.dumps(out), flush=True)

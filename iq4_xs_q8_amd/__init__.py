@@ -41,6 +41,11 @@ EXPORTS = ("iq4xs_weight_bytes", "iq4xs_q8_1_bytes", "iq4xs_init", "iq4xs_quanti
            "iq4xs_dispatch", "iq4xs_load_dispatch_table", "iq4xs_path_name", "iq4xs_last_error")
 
 
+# measurement kernels (include/iq4xs_probe.h)
+PROBE_EXPORTS = ("iq4xs_probe_read", "iq4xs_probe_write", "iq4xs_probe_mfma")
+PROBE_MFMA_I8, PROBE_MFMA_BF16 = 0, 1
+
+
 class Iq4xsError(RuntimeError):
     def __init__(self, code: int, message: str):
         super().__init__(f"iq4xs error {code}: {message}")
@@ -77,6 +82,11 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "iq4xs_dispatch": [i64, i64, i64, ctypes.POINTER(ctypes.c_int)],
         "iq4xs_load_dispatch_table": [ctypes.c_char_p],
     }
+    sig.update({
+        "iq4xs_probe_read": [p, ctypes.c_size_t, p, i32, p],
+        "iq4xs_probe_write": [p, ctypes.c_size_t, ctypes.c_uint32, i32, p],
+        "iq4xs_probe_mfma": [i32, i32, p, i32, p],
+    })
     for name, args in sig.items():
         fn = getattr(lib, name)
         fn.argtypes = args
@@ -393,3 +403,31 @@ def load_dispatch_table(path: str | None = None) -> None:
 
 def path_name(p: int) -> str:
     return _L().iq4xs_path_name(p).decode()
+
+
+# ---------------------------------------------------------------- probes
+def _probe_check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise Iq4xsError(rc, f"{what} failed")
+
+
+def probe_read(buf: torch.Tensor, sink: torch.Tensor, grid: int = 4096) -> None:
+    """Stream-read all of buf (uint8, 16-byte multiple) with the library's read probe."""
+    _at_least(sink, "sink", 4 * grid)
+    with _on(buf):
+        _probe_check(_L().iq4xs_probe_read(_dev(buf, torch.uint8, "buf"), buf.numel(),
+                                          _dev(sink, torch.int32, "sink"), grid, _stream(buf)), "probe_read")
+
+
+def probe_write(buf: torch.Tensor, value: int = 0x3F800000, grid: int = 4096) -> None:
+    with _on(buf):
+        _probe_check(_L().iq4xs_probe_write(_dev(buf, torch.uint8, "buf"), buf.numel(), value, grid,
+                                           _stream(buf)), "probe_write")
+
+
+def probe_mfma(kind: int, iters: int, out: torch.Tensor, grid: int) -> None:
+    """out: int32 (int8 probe) or float32 (bf16 probe), grid * 256 elements."""
+    _at_least(out, "out", 4 * 256 * grid)
+    dt = torch.int32 if kind == PROBE_MFMA_I8 else torch.float32
+    with _on(out):
+        _probe_check(_L().iq4xs_probe_mfma(kind, iters, _dev(out, dt, "out"), grid, _stream(out)), "probe_mfma")

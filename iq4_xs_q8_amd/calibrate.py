@@ -1,8 +1,9 @@
 """Turn a measured sweep into the dispatch table behind IQ4XS_PATH_AUTO.
 
-Usage:  python -m iq4_xs_q8_amd.calibrate SWEEP.jsonl [OUT.txt]
+Usage:  python -m iq4_xs_q8_amd.calibrate SWEEP [OUT.txt]
 
-SWEEP.jsonl is what `bench.py --sweep` writes on the device: one record per
+SWEEP is what `bench.py --sweep` writes on the device (JSONL), or its text
+summary (`bench.py --summarize-sweep`, kept under profiles/): one record per
 (workload shape, M, path) with the per-call device time `ms` (quantization
 included, calls replayed from a HIP graph so that host launch cost is not
 counted, weights rotated past the Infinity Cache).  The table ("V100TPS engine log",
@@ -33,16 +34,29 @@ BIG = 1000000000
 
 def load(path):
     """(N, K) -> M -> {path: ms}, and the compute-unit count the sweep ran on
-    (None when its records do not say)."""
+    (None when its records do not say).  Reads the JSONL of a sweep run or
+    its text summary (bench.py --summarize-sweep: "N K M path us_per_call
+    us_kernel" lines and a "# compute units: C" line)."""
     best = collections.defaultdict(dict)
     cus = set()
     for line in open(path):
-        r = json.loads(line)
-        if "cus" in r:
-            cus.add(int(r["cus"]))
-        if r["path"] == "AUTO":
+        line = line.strip()
+        if not line:
             continue
-        best[(r["N"], r["K"])].setdefault(r["M"], {})[r["path"]] = r["ms"]
+        if line.startswith("#"):
+            if line.startswith("# compute units:") and line.split(":")[1].strip():
+                cus.update(int(c) for c in line.split(":")[1].split(","))
+            continue
+        if line.startswith("{"):
+            r = json.loads(line)
+            if "cus" in r:
+                cus.add(int(r["cus"]))
+            if r["path"] == "AUTO":
+                continue
+            best[(r["N"], r["K"])].setdefault(r["M"], {})[r["path"]] = r["ms"]
+        else:
+            N, K, M, p, us = line.split()[:5]
+            best[(int(N), int(K))].setdefault(int(M), {})[p] = float(us) * 1e-3
     if len(cus) > 1:
         raise SystemExit(f"sweep mixes devices with {sorted(cus)} compute units")
     return best, (cus.pop() if cus else None)

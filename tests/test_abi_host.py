@@ -28,13 +28,27 @@ def _has_gpu():
 
 
 def test_header_declarations_are_exported():
-    text = open(HEADER).read()
-    declared = set(re.findall(r"^\w[\w\s\*]*?\b(iq4xs_\w+)\s*\(", text, flags=re.M))
-    assert declared == set(iq.EXPORTS)
+    """Every function of every header under include/ is exported by the
+    library and bound by the Python package."""
     out = subprocess.run(["nm", "-D", "--defined-only", iq.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (iq4xs_\w+)$", out, flags=re.M))
-    assert declared <= exported, declared - exported
+    for header, names in ((HEADER, iq.EXPORTS), (os.path.join(ROOT, "include", "iq4xs_probe.h"), iq.PROBE_EXPORTS)):
+        text = open(header).read()
+        declared = set(re.findall(r"^\w[\w\s\*]*?\b(iq4xs_\w+)\s*\(", text, flags=re.M))
+        assert declared == set(names), (header, declared ^ set(names))
+        assert declared <= exported, declared - exported
+    headers = sorted(f for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h"))
+    assert headers == ["iq4xs.h", "iq4xs_probe.h"], headers
+
+
+def test_probe_arguments_checked_on_the_host():
+    assert L.iq4xs_probe_read(None, 16, A, 1, None) == -1
+    assert L.iq4xs_probe_read(A, 15, A, 1, None) == -1
+    assert L.iq4xs_probe_read(A + 4, 16, A, 1, None) == -1
+    assert L.iq4xs_probe_write(A, 0, 1, 1, None) == -1
+    assert L.iq4xs_probe_mfma(7, 1, A, 1, None) == -1
+    assert L.iq4xs_probe_mfma(0, 0, A, 1, None) == -1
 
 
 def test_header_constants_match_binding():
@@ -380,3 +394,29 @@ def test_format_binding_shapes():
         iq.gemm_fmt(torch.zeros((8, 288), dtype=torch.uint8), X, 5)
     with pytest.raises(TypeError, match="CUDA"):
         iq.gemm_fmt(torch.zeros((8, 288), dtype=torch.uint8), X, iq.FMT_Q4_0)
+
+
+def test_calibrate_reads_the_text_summary(tmp_path):
+    """The committed sweep summary reproduces the table calibrate.py writes
+    from the JSONL it was made from."""
+    from iq4_xs_q8_amd import calibrate
+    recs = []
+    for M, g, q in ((1, 0.010, 0.012), (2, 0.011, 0.012), (4, 0.013, 0.012)):
+        recs += [{"N": 4096, "K": 1024, "M": M, "path": "GEMV", "ms": g, "cus": 256},
+                 {"N": 4096, "K": 1024, "M": M, "path": "MMQ", "ms": q, "cus": 256, "kernel_ms": q * 0.8}]
+    sweep = tmp_path / "sweep.jsonl"
+    sweep.write_text("\n".join(json.dumps(r) for r in recs) + "\n")
+    text = tmp_path / "sweep.txt"
+    subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--summarize-sweep", str(sweep), "--out",
+                    str(text), "--cmd", "test"], check=True, capture_output=True, env=dict(os.environ, PYTHONPATH=ROOT))
+    a, b = tmp_path / "a.txt", tmp_path / "b.txt"
+    calibrate.main([str(sweep), str(a)])
+    calibrate.main([str(text), str(b)])
+    assert a.read_text() == b.read_text() and "cus 256" in a.read_text()
+    # the committed summary reproduces the built-in table
+    committed = os.path.join(ROOT, "profiles", "dispatch_sweep_gfx950.txt")
+    if os.path.exists(committed):
+        c = tmp_path / "c.txt"
+        calibrate.main([committed, str(c)])
+        builtin = open(os.path.join(ROOT, "iq4_xs_q8_amd", "csrc", "dispatch_gfx950.txt")).read()
+        assert c.read_text() == builtin
