@@ -62,7 +62,7 @@ class Oracle:
             getattr(lib, name).restype = None
         lib.oracle_quantize_q8_1.argtypes = [_p, _i64, _i64, _p]
         lib.oracle_quantize_q8_1.restype = None
-        for name in ("oracle_gemm_q8_1", "oracle_gemm_bf16"):
+        for name in ("oracle_gemm_q8_1", "oracle_gemm_bf16", "oracle_gemm_bf16x3"):
             getattr(lib, name).argtypes = [_p, _p, _i64, _i64, _i64, _p]
             getattr(lib, name).restype = None
         for name in ("oracle_float_to_half_array", "oracle_half_to_double_array",
@@ -168,6 +168,15 @@ class Oracle:
         Xq, M = self._xqcheck(Xq, K)
         Y = np.empty((M, N), dtype=np.float64)
         self.lib.oracle_gemm_bf16(W.ctypes.data, Xq.ctypes.data, M, N, K, Y.ctypes.data)
+        return Y
+
+    def gemm_bf16x3(self, W: np.ndarray, Xq: np.ndarray, K: int) -> np.ndarray:
+        """Compensated bf16 formulation: W~ and X~ each split into bf16 hi
+        and lo parts, Wh*Xh + Wh*Xl + Wl*Xh summed exactly."""
+        W, N = self._wcheck(W, K)
+        Xq, M = self._xqcheck(Xq, K)
+        Y = np.empty((M, N), dtype=np.float64)
+        self.lib.oracle_gemm_bf16x3(W.ctypes.data, Xq.ctypes.data, M, N, K, Y.ctypes.data)
         return Y
 
     def gemm(self, W: np.ndarray, X: np.ndarray) -> np.ndarray:

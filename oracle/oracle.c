@@ -46,7 +46,12 @@
  *       X~ = d_x*q to bf16 (nearest even) and sums their exact products;
  *   R5  an IQ4_NL or Q4_0 block of 18 bytes is {fp16 d, u8 qs[16]} (the GGUF
  *       order: the scale first, then the 16 nibble bytes laid out as in an
- *       IQ4_XS sub-block); a row of K weights is K/32 consecutive blocks.
+ *       IQ4_XS sub-block); a row of K weights is K/32 consecutive blocks;
+ *   R6  the compensated bf16 variant (this library's route to putting the
+ *       dequantize-then-GEMM path under the same per-row bound as the
+ *       integer path) splits each of W~ and X~ into hi = bf16(v) and
+ *       lo = bf16(v - hi), both nearest even, and sums
+ *       Wh*Xh + Wh*Xl + Wl*Xh per element (the lo*lo product is dropped).
  *
  * Arithmetic.  Every decoded weight d*(ls-32)*kv needs at most 11+6+7 = 24
  * significant bits and every product term d_w*(ls-32)*d_x*D at most 48, so
@@ -293,6 +298,39 @@ void oracle_gemm_bf16(const uint8_t *W, const uint8_t *Xq, int64_t M, int64_t N,
                 acc += w * x;
             }
             Y[m * N + n] = acc;
+        }
+}
+
+/* hi and lo bf16 parts of v (R6): hi = bf16(v), lo = bf16(v - hi). */
+static void split_bf16(double v, double *hi, double *lo)
+{
+    *hi = oracle_bf16_to_double(oracle_double_to_bf16(v));
+    *lo = oracle_bf16_to_double(oracle_double_to_bf16(v - *hi));
+}
+
+/* Compensated bf16 formulation (R6):
+     Y[m,n] = sum_k Wh*Xh + Wh*Xl + Wl*Xh,
+   (Wh, Wl) the split of W~[n,k] = d*(ls-32)*kv, (Xh, Xl) that of
+   X~[m,k] = d_x*q; products exact in fp64, summed in ascending k. */
+void oracle_gemm_bf16x3(const uint8_t *W, const uint8_t *Xq, int64_t M, int64_t N, int64_t K,
+                        double *Y)
+{
+    int64_t nb = K / ORACLE_QK, nsub = K / ORACLE_SB;
+#pragma omp parallel for schedule(static) num_threads(oracle_get_threads())
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t m = 0; m < M; m++) {
+            double total = 0.0;
+            for (int64_t k = 0; k < K; k++) {
+                const uint8_t *wblk = W + (n * nb + k / ORACLE_QK) * ORACLE_WBLK;
+                int e = (int)(k % ORACLE_QK);
+                double wh, wl, xh, xl;
+                split_bf16(sb_scale(wblk, e / ORACLE_SB) * ORACLE_KV[code_at(wblk, e)], &wh, &wl);
+                const uint8_t *xblk = Xq + (m * nsub + k / ORACLE_SB) * ORACLE_XBLK;
+                double d_act = oracle_half_to_double((uint16_t)(xblk[0] | (xblk[1] << 8)));
+                split_bf16(d_act * (double)(int8_t)xblk[4 + k % ORACLE_SB], &xh, &xl);
+                total += wh * xh + wh * xl + wl * xh;
+            }
+            Y[m * N + n] = total;
         }
 }
 

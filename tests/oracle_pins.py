@@ -389,6 +389,71 @@ def pin_gemm_bf16(o):
                           .view(torch.int16).numpy().view(np.uint16))
 
 
+def _x_values(Xq, M, K):
+    """X~ = d_x * q of Q8_1 bytes, exact in fp64 ([M, K])."""
+    xb = Xq.reshape(M, K // 32, 36)
+    d = xb[..., 0:2].copy().view(np.float16).astype(np.float64).reshape(M, K // 32)
+    q = xb[..., 4:].view(np.int8).astype(np.float64).reshape(M, K)
+    return q * np.repeat(d, 32, axis=1)
+
+
+def pin_gemm_bf16x3_bound(o):
+    """Each of W~ and X~ is within 2^-16 (relative) of its hi + lo, and the
+    dropped lo*lo product is below 2^-16 |W~ X~|: every term of the
+    compensated sum is within 3.02 * 2^-16 of the exact product.  One-hot
+    activation rows make each output a single term, so a dropped or doubled
+    product (about 2^-9 of the term) shows; dense rows check the sum."""
+    rng = np.random.default_rng(29)
+    N, K = 9, 512
+    d_bits, ls, codes = random_fields(rng, N * K // 256)
+    W, V = build_matrix(d_bits, ls, codes, N, K)
+    ks = (0, 1, 15, 16, 31, 33, 100, 255, 256, 300, 477, 511)
+    X1 = np.zeros((len(ks), K), dtype=np.float32)
+    for i, k in enumerate(ks):
+        X1[i, k] = rng.standard_normal() * 3
+    Xq1 = o.quantize_q8_1(X1)
+    xt1 = _x_values(Xq1, len(ks), K)
+    got = o.gemm_bf16x3(W, Xq1, K)
+    exact = xt1 @ V.T                                 # one non-zero term per output
+    terms = np.abs(xt1) @ np.abs(V).T
+    assert np.all(np.abs(got - exact) <= 3.02 * 2.0**-16 * terms)
+    # not the plain bf16 formulation: somewhere it is closer than bf16 can be
+    plain = o.gemm_bf16(W, Xq1, K)
+    assert np.max(np.abs(plain - exact) / np.maximum(terms, 1e-300)) > 2.0**-12
+    assert np.max(np.abs(got - exact) / np.maximum(terms, 1e-300)) < 2.0**-14
+    # dense activations: the sum of the per-term bounds
+    M = 3
+    X = rng.standard_normal((M, K)).astype(np.float32)
+    Xq = o.quantize_q8_1(X)
+    exact, absum = _exact_gemm(V, Xq, M, K)
+    got = o.gemm_bf16x3(W, Xq, K)
+    for m in range(M):
+        for n in range(N):
+            err = abs(Fraction(float(got[m, n])) - exact[m][n])
+            assert err <= absum[m][n] * (Fraction(302, 100) * Fraction(1, 2**16) + Fraction(1, 2**50))
+
+
+def pin_gemm_bf16x3_exact_when_representable(o):
+    """Weights with power-of-two d and ls - 32 and activations whose Q8_1
+    scale is a power of two: every W~ and X~ is a bf16 number, every lo part
+    is zero, and the compensated sum equals the exact integer-path result."""
+    rng = np.random.default_rng(31)
+    N, K, M = 4, 512, 3
+    nblk = N * K // 256
+    d_bits = np.full(nblk, 0x1800, dtype=np.uint16)          # fp16 2^-9
+    ls = rng.choice([16, 24, 28, 30, 31, 33, 34, 36, 40, 48, 0], size=(nblk, 8)).astype(np.int64)
+    codes = rng.integers(0, 16, size=(nblk, 256))
+    W, V = build_matrix(d_bits, ls, codes, N, K)
+    q = rng.integers(-127, 128, size=(M, K)).astype(np.float32)
+    q[:, ::32] = 127                                          # amax = 127 * 2^-5 in every block
+    X = q * np.float32(2.0**-5)
+    Xq = o.quantize_q8_1(X)
+    assert np.all(Xq.reshape(M, K // 32, 36)[..., 0:2].copy().view(np.float16) == np.float16(2.0**-5))
+    want = o.gemm_q8_1(W, Xq, K)
+    assert np.array_equal(o.gemm_bf16x3(W, Xq, K), want)
+    assert np.array_equal(o.gemm_bf16(W, Xq, K), want)
+
+
 # ------------------------------------------------- IQ4_NL and Q4_0 blocks
 FMT_IQ4_XS, FMT_IQ4_NL, FMT_Q4_0 = 0, 1, 2
 
@@ -563,4 +628,5 @@ B18_PINS = (pin_b18_handworked, pin_b18_random_blocks, pin_b18_gemm_exact, pin_b
 ALL_PINS = (pin_half_decode, pin_half_encode, pin_bf16, pin_codebook, pin_handworked_block,
             pin_random_blocks, pin_q8_1_handworked, pin_q8_1_ieee,
             pin_q8_1_division_not_reciprocal, pin_gemm_exact, pin_gemm_closed_forms,
-            pin_gemm_invariants, pin_gemm_bf16) + B18_PINS
+            pin_gemm_invariants, pin_gemm_bf16, pin_gemm_bf16x3_bound,
+            pin_gemm_bf16x3_exact_when_representable) + B18_PINS

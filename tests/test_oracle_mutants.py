@@ -52,6 +52,18 @@ MUTANTS = {
     "bf16 gemm drops activation rounding": (
         "double x = oracle_bf16_to_double(\n                    oracle_double_to_bf16(dx * (double)(int8_t)xb[4 + k % ORACLE_SB]));",
         "double x = dx * (double)(int8_t)xb[4 + k % ORACLE_SB];"),
+    "bf16x3 drops the Wl*Xh product": ("total += wh * xh + wh * xl + wl * xh;", "total += wh * xh + wh * xl;"),
+    "bf16x3 lo*lo in place of Wl*Xh": ("total += wh * xh + wh * xl + wl * xh;",
+                                        "total += wh * xh + wh * xl + wl * xl;"),
+    "bf16x3 lo rounds the value, not the residual": (
+        "*lo = oracle_bf16_to_double(oracle_double_to_bf16(v - *hi));",
+        "*lo = oracle_bf16_to_double(oracle_double_to_bf16(v)) - *hi;"),
+    "bf16x3 activation scale of the next block": (
+        "const uint8_t *xblk = Xq + (m * nsub + k / ORACLE_SB) * ORACLE_XBLK;",
+        "const uint8_t *xblk = Xq + (m * nsub + (k / ORACLE_SB + 1) % nsub) * ORACLE_XBLK;"),
+    "bf16x3 weight of the next sub-block": (
+        "split_bf16(sb_scale(wblk, e / ORACLE_SB) * ORACLE_KV[code_at(wblk, e)], &wh, &wl);",
+        "split_bf16(sb_scale(wblk, (e / ORACLE_SB + 1) % 8) * ORACLE_KV[code_at(wblk, e)], &wh, &wl);"),
     # IQ4_NL and Q4_0 (18-byte blocks)
     "b18 nibble order swapped": ("int c = t < 16 ? (byte & 15) : (byte >> 4);",
                                  "int c = t < 16 ? (byte >> 4) : (byte & 15);"),
