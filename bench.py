@@ -78,7 +78,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_mmv_decode_n10240_k5120_traffic
 TILE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_mmqt_tile_shapes_traffic.txt")
 KERNEL_SOURCES = {"k_mmv": ["mmv.hip", "common.hpp", "stream.hpp"], "k_gemv": ["gemv.hip", "common.hpp"],
                   "k_mmq": ["mmq.hip", "common.hpp"], "k_mmqt": ["mmqt.hip", "common.hpp", "stream.hpp"],
-                  "k_gemm_bf16": ["deq.hip", "common.hpp"]}
+                  "k_gemm_bf16": ["deq.hip", "common.hpp"],
+                  "k_gemm_x3": ["fused.hip", "common.hpp", "stream.hpp"]}
 # Exact formulation on the matrix cores: per (output, 32-wide sub-block) the
 # int8 MFMA does 32 MACs (0.031 cycles per SIMD at 2048 ops/cycle) and the
 # fp32 rescale three VALU instructions (0.1875 cycles at 16 lanes/cycle,
@@ -94,6 +95,8 @@ def kernel_name(M, N, K, path):
         return "k_gemv"
     if path == iq.PATH_DEQ_BF16:
         return "k_gemm_bf16"
+    if path == iq.PATH_BF16X3:
+        return "k_gemm_x3"
     nb = K // 256
     if M <= 32 and nb % 2 == 0 and N * nb * 136 < (1 << 31):
         return "k_mmv"
@@ -187,7 +190,7 @@ def measure_point(rot, X, N, K, path, reps=20, fmt=iq.FMT_IQ4_XS):
     t_call = time_events(g.replay, 3, stream) / reps
     del g
     t_kern = None
-    if path != iq.PATH_DEQ_BF16 and fmt == iq.FMT_IQ4_XS:
+    if path not in (iq.PATH_DEQ_BF16, iq.PATH_BF16X3) and fmt == iq.FMT_IQ4_XS:
         act = iq.prepare_act(X)
         Y.zero_()
         kern = lambda: iq.gemm_act(rot.next(), act, M, K, path=path, out=Y, y_zeroed=True)  # noqa: E731
@@ -496,7 +499,8 @@ def check_trace(trace_dir, out, cmd):
         elif cur is not None:
             cur.append((k, (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3))
     pts = sweep_points()
-    families = {"GEMV": {"k_gemv"}, "MMQ": {"k_mmv", "k_mmqt", "k_mmq"}, "DEQ_BF16": {"k_gemm_bf16"}}
+    families = {"GEMV": {"k_gemv"}, "MMQ": {"k_mmv", "k_mmqt", "k_mmq"}, "DEQ_BF16": {"k_gemm_bf16"},
+                "BF16X3": {"k_gemm_x3"}}
     lines = ["# kernels launched per call, from a rocprofv3 kernel trace of bench.py --profile-points",
              f"# command: {cmd}",
              "# every call of every point launches the quantizer and a matmul kernel of the path the",
@@ -510,7 +514,7 @@ def check_trace(trace_dir, out, cmd):
         path = iq.path_name(iq.dispatch(M, N, K))
         expect = kernel_name(M, N, K, iq.PATHS[path])
         per_call = names[:len(names) // 2]
-        mat = [k for k in per_call if k.startswith(("k_gemv", "k_mmv", "k_mmqt", "k_mmq", "k_gemm_bf16"))]
+        mat = [k for k in per_call if k.startswith(("k_gemv", "k_mmv", "k_mmqt", "k_mmq", "k_gemm_bf16", "k_gemm_x3"))]
         ok = (len(names) % 2 == 0 and names[:len(names) // 2] == names[len(names) // 2:] and
               per_call[0] == "k_quantize" and mat and mat[0] == expect and mat[0] in families[path])
         bad += not ok

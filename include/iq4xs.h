@@ -73,7 +73,9 @@ extern "C" {
 #define IQ4XS_PATH_MMQ 2      /* int8-MFMA tile kernel, any M                             */
 #define IQ4XS_PATH_DEQ_BF16 3 /* dequantize W and X~ to bf16, bf16-MFMA GEMM (inexact:
                                  rounds W~ and X~ to 8 significant bits)                 */
-#define IQ4XS_NUM_PATHS 4
+#define IQ4XS_PATH_BF16X3 4   /* W dequantized inside the GEMM into LDS, W~ and X~ each as
+                                 bf16 hi + lo, three bf16-MFMA products per term          */
+#define IQ4XS_NUM_PATHS 5
 
 /* ---- weight formats (the iq4xs_*_fmt entry points) ----
  * "V100TPS engine log", batched IQ4_XS kernel section: an IQ4_XS sub-block of

@@ -25,8 +25,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libiq4xs.so")
 
 OK, EINVAL, EALIGN, EDEVICE, ETABLE, ELAUNCH, ENOMEM, EPATH = 0, -1, -2, -3, -4, -5, -6, -7
-PATH_AUTO, PATH_GEMV, PATH_MMQ, PATH_DEQ_BF16 = 0, 1, 2, 3
-PATHS = {"AUTO": PATH_AUTO, "GEMV": PATH_GEMV, "MMQ": PATH_MMQ, "DEQ_BF16": PATH_DEQ_BF16}
+PATH_AUTO, PATH_GEMV, PATH_MMQ, PATH_DEQ_BF16, PATH_BF16X3 = 0, 1, 2, 3, 4
+PATHS = {"AUTO": PATH_AUTO, "GEMV": PATH_GEMV, "MMQ": PATH_MMQ, "DEQ_BF16": PATH_DEQ_BF16,
+         "BF16X3": PATH_BF16X3}
 FMT_IQ4_XS, FMT_IQ4_NL, FMT_Q4_0 = 0, 1, 2
 FMTS = {"IQ4_XS": FMT_IQ4_XS, "IQ4_NL": FMT_IQ4_NL, "Q4_0": FMT_Q4_0}
 _UNIT_BYTES = {FMT_IQ4_XS: 136, FMT_IQ4_NL: 144, FMT_Q4_0: 144}    # bytes per 256 weights

@@ -22,7 +22,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libiq4xs.so")
 
-HIP_SOURCES = ("quantize.hip", "gemv.hip", "mmq.hip", "mmv.hip", "mmqt.hip", "deq.hip", "abi.hip", "probe.hip")
+HIP_SOURCES = ("quantize.hip", "gemv.hip", "mmq.hip", "mmv.hip", "mmqt.hip", "deq.hip", "fused.hip", "abi.hip",
+               "probe.hip")
 CXX_SOURCES = ("dispatch.cpp",)
 ARCH = "gfx950"
 

@@ -277,8 +277,8 @@ int resolve_path(int path, int64_t M, int64_t N, int64_t K, int *out, int fmt = 
 {
     if (path < 0 || path >= IQ4XS_NUM_PATHS)
         return fail(IQ4XS_EINVAL, "unknown path %d", path);
-    if (fmt != FMT_IQ4_XS && path == IQ4XS_PATH_DEQ_BF16)
-        return fail(IQ4XS_EPATH, "the bf16 path reads IQ4_XS weights only");
+    if (fmt != FMT_IQ4_XS && (path == IQ4XS_PATH_DEQ_BF16 || path == IQ4XS_PATH_BF16X3))
+        return fail(IQ4XS_EPATH, "the bf16 paths read IQ4_XS weights only");
     ensure_init();
     if (path == IQ4XS_PATH_AUTO) {
         int st = ensure_init();
@@ -288,7 +288,7 @@ int resolve_path(int path, int64_t M, int64_t N, int64_t K, int *out, int fmt = 
             std::lock_guard<std::mutex> lk(g_mu);
             // (the bands were measured on IQ4_XS; for the 32-weight formats the
             // same GEMV / MMQ kernels run, and bf16 bands do not apply)
-            path = table_lookup(g_table, M, N, K, g_cfg.allow_bf16 && fmt == FMT_IQ4_XS);
+            path = table_lookup(g_table, M, N, K, g_cfg.allow_bf16 && fmt == FMT_IQ4_XS, fmt == FMT_IQ4_XS);
         }
         if (!path)
             return fail(IQ4XS_EPATH, "no dispatch band covers M=%lld N=%lld K=%lld", (long long)M,
@@ -304,12 +304,15 @@ int resolve_path(int path, int64_t M, int64_t N, int64_t K, int *out, int fmt = 
 }
 
 // Scratch a path needs: activation planes (+ the split-K partial sums of
-// MMQ), or for DEQ_BF16 the bf16 activations and weights.
+// MMQ), for BF16X3 the compensated bf16 activation planes, or for DEQ_BF16
+// the bf16 activations and weights.
 size_t workspace_need(int path, int64_t M, int64_t N, int64_t K, int fmt = FMT_IQ4_XS)
 {
     if (path == IQ4XS_PATH_GEMV || path == IQ4XS_PATH_MMQ)
         return (size_t)round_up((int64_t)xplanes_bytes(M, K), 256) +
                (path == IQ4XS_PATH_MMQ ? mmq_plan(M, N, K, fmt).workspace_bytes : 0);
+    if (path == IQ4XS_PATH_BF16X3)
+        return fused_xs_bytes(M, K);
     return (size_t)round_up(M * K * 2, 256) + (size_t)(N * K * 2);
 }
 
@@ -367,6 +370,19 @@ int run_gemm(const void *W, const float *X, const void *Xq, float *Y, int64_t M,
         e = path == IQ4XS_PATH_GEMV ? launch_gemv(W, xp, Y, N, s, fmt)
                                     : launch_mmq(W, xp, Y, N, base + pbytes, zero, s, fmt);
         return launch_err(e, path_name(path));
+    }
+    if (path == IQ4XS_PATH_BF16X3) {
+        if (fused_grid(M, N) > INT32_MAX || fused_xs_bytes(M, K) >= (size_t)INT32_MAX)
+            return fail(IQ4XS_EPATH, "BF16X3 takes fewer than 2^31 workgroups and activation planes "
+                        "below 2 GiB (M=%lld N=%lld K=%lld)", (long long)M, (long long)N, (long long)K);
+        XSplit xsp;
+        xsp.p = (uint16_t *)base;
+        xsp.Ms = fused_ms(M);
+        const hipError_t e = X ? launch_quantize(X, nullptr, nullptr, nullptr, M, K, s, nullptr, 0, &xsp)
+                               : launch_q8_1_convert(Xq, nullptr, nullptr, M, K, s, nullptr, 0, &xsp);
+        if ((st = launch_err(e, "quantize")) != IQ4XS_OK)
+            return st;
+        return launch_err(launch_fused_x3(W, xsp.p, Y, M, N, K, s), "gemm_x3");
     }
     // DEQ_BF16: X~ bf16 [M][K], then W~ bf16 [N][K] (256-byte aligned)
     const size_t xbytes = (size_t)round_up(M * K * 2, 256);
@@ -631,7 +647,11 @@ int iq4xs_gemm_act(const void *W, const void *act, float *Y, int64_t M, int64_t 
     const int requested = path;
     if ((st = resolve_path(path, M, N, K, &path)) != IQ4XS_OK)
         return st;
-    if (path == IQ4XS_PATH_DEQ_BF16)
+    // the table's bf16 bands do not apply to prepared activations: the
+    // integer kernel takes those shapes
+    if (requested == IQ4XS_PATH_AUTO && path == IQ4XS_PATH_BF16X3)
+        path = IQ4XS_PATH_MMQ;
+    if (path == IQ4XS_PATH_DEQ_BF16 || path == IQ4XS_PATH_BF16X3)
         return fail(IQ4XS_EPATH, "prepared activations feed the GEMV and MMQ paths only");
     if ((st = check_device()) != IQ4XS_OK || (st = check_auto_cus(requested)) != IQ4XS_OK)
         return st;

@@ -292,6 +292,33 @@ struct MmvGroup {
 
 // Outputs the quantize kernels zero on the way (for matmuls that add partial
 // tiles into Y): up to MAXGRP ranges p[i][0..n[i]), 16-byte aligned.
+// ---- compensated bf16 activations (fused.hip) ------------------------------
+// The fused dequantize-in-LDS kernel reads X~ = d_x*q (exact in fp32) as two
+// bf16 numbers, hi = bf16(X~) and lo = bf16(X~ - hi), from planes the
+// quantizer writes: u16 [K/32][Ms][64], row m of block b at (b*Ms + m)*64,
+// hi[32] then lo[32] in element order; Ms = M rounded up to FUSED_ROWS, rows
+// M..Ms-1 zero.
+constexpr int FUSED_ROWS = 256;
+struct XSplit {
+    uint16_t *p = nullptr;
+    int64_t Ms = 0;
+};
+inline int64_t fused_ms(int64_t M) { return (M + FUSED_ROWS - 1) / FUSED_ROWS * FUSED_ROWS; }
+inline size_t fused_xs_bytes(int64_t M, int64_t K) { return (size_t)(K / SB) * (size_t)fused_ms(M) * 128; }
+
+// hi = bf16(a), bf16(b) (nearest even; v_cvt_pk_bf16_f32) and lo = the bf16
+// of what hi leaves out (exact in fp32), packed low element first.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void bf16x2_split(float a, float b, uint32_t &hi, uint32_t &lo)
+{
+    const bf16x2_t h = {(__bf16)a, (__bf16)b};
+    hi = __builtin_bit_cast(uint32_t, h);
+    const float ra = a - __builtin_bit_cast(float, hi << 16);
+    const float rb = b - __builtin_bit_cast(float, hi & 0xFFFF0000u);
+    const bf16x2_t l = {(__bf16)ra, (__bf16)rb};
+    lo = __builtin_bit_cast(uint32_t, l);
+}
+
 struct ZeroList {
     float *p[MAXGRP] = {};
     int64_t n[MAXGRP] = {};
@@ -302,12 +329,16 @@ struct ZeroList {
 // All return a hipError_t from hipGetLastError() after the launch.  The
 // quantizers also zero yz[0..nz) when yz is given (the output of a matmul
 // that adds partial tiles into it).
+// xs (optional) receives the compensated bf16 planes.
 hipError_t launch_quantize(const float *X, void *Xq, const XPlanes *planes, uint16_t *Xbf,
-                           int64_t M, int64_t K, hipStream_t s, float *yz = nullptr, int64_t nz = 0);
+                           int64_t M, int64_t K, hipStream_t s, float *yz = nullptr, int64_t nz = 0,
+                           const XSplit *xs = nullptr);
 hipError_t launch_quantize(const float *X, void *Xq, const XPlanes *planes, uint16_t *Xbf,
-                           int64_t M, int64_t K, hipStream_t s, const ZeroList &zl);
+                           int64_t M, int64_t K, hipStream_t s, const ZeroList &zl,
+                           const XSplit *xs = nullptr);
 hipError_t launch_q8_1_convert(const void *Xq, const XPlanes *planes, uint16_t *Xbf, int64_t M,
-                              int64_t K, hipStream_t s, float *yz = nullptr, int64_t nz = 0);
+                              int64_t K, hipStream_t s, float *yz = nullptr, int64_t nz = 0,
+                              const XSplit *xs = nullptr);
 hipError_t launch_zero(float *y, int64_t n, hipStream_t s);
 hipError_t launch_gemv(const void *W, const XPlanes &x, float *Y, int64_t N, hipStream_t s,
                        int fmt = FMT_IQ4_XS);
@@ -363,6 +394,11 @@ hipError_t launch_mmq(const void *W, const XPlanes &x, float *Y, int64_t N, void
 hipError_t launch_dequant_bf16(const void *W, uint16_t *Wb, int64_t N, int64_t K, hipStream_t s);
 hipError_t launch_gemm_bf16(const uint16_t *Xb, const uint16_t *Wb, float *Y, int64_t M,
                             int64_t N, int64_t K, hipStream_t s);
+
+// Fused dequantize-in-LDS GEMM (fused.hip): Xs as XSplit with Ms = fused_ms(M).
+int64_t fused_grid(int64_t M, int64_t N);
+hipError_t launch_fused_x3(const void *W, const uint16_t *Xs, float *Y, int64_t M, int64_t N, int64_t K,
+                           hipStream_t s);
 
 constexpr int GEMV_MAX_M = 4;
 

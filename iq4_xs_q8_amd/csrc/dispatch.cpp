@@ -25,6 +25,7 @@ const char *path_name(int p)
     case IQ4XS_PATH_GEMV: return "GEMV";
     case IQ4XS_PATH_MMQ: return "MMQ";
     case IQ4XS_PATH_DEQ_BF16: return "DEQ_BF16";
+    case IQ4XS_PATH_BF16X3: return "BF16X3";
     default: return "?";
     }
 }
@@ -126,10 +127,10 @@ bool parse_table(const std::string &text, Table *out, std::string *err)
     return true;
 }
 
-int table_lookup(const Table &t, int64_t M, int64_t N, int64_t K, bool allow_bf16)
+int table_lookup(const Table &t, int64_t M, int64_t N, int64_t K, bool allow_bf16, bool allow_x3)
 {
     for (const Band &b : t.bands) {
-        if (b.path == IQ4XS_PATH_DEQ_BF16 && !allow_bf16)
+        if ((b.path == IQ4XS_PATH_DEQ_BF16 && !allow_bf16) || (b.path == IQ4XS_PATH_BF16X3 && !allow_x3))
             continue;
         if (M < b.mlo || M > b.mhi)
             continue;

@@ -24,8 +24,9 @@ struct Table {
 
 const char *path_name(int p);
 bool parse_table(const std::string &text, Table *out, std::string *err);
-// First band matching (M, N, K); DEQ_BF16 bands only when allow_bf16.  0 = none.
-int table_lookup(const Table &t, int64_t M, int64_t N, int64_t K, bool allow_bf16);
+// First band matching (M, N, K); DEQ_BF16 bands only when allow_bf16, BF16X3
+// bands only when allow_x3 (IQ4_XS weights).  0 = none.
+int table_lookup(const Table &t, int64_t M, int64_t N, int64_t K, bool allow_bf16, bool allow_x3 = true);
 // The table compiled into the library (dispatch_gfx950.txt).
 const char *default_table_text();
 

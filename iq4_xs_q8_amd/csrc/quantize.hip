@@ -66,6 +66,21 @@ __global__ void __launch_bounds__(256) k_zero(float *__restrict__ y, int64_t n)
     zero_range(y, n, (int64_t)blockIdx.x * blockDim.x + threadIdx.x, (int64_t)gridDim.x * blockDim.x);
 }
 
+// Elements 4t..4t+3 of block b of row m into the compensated bf16 planes
+// (rows past M carry q = 0, so zeros).  d*q is exact in fp32.
+__device__ __forceinline__ void write_split(const XSplit &xs, int64_t m, int64_t b, int t, float d, int q0,
+                                            int q1, int q2, int q3)
+{
+    if (xs.p == nullptr || m >= xs.Ms)
+        return;
+    uint32_t h01, l01, h23, l23;
+    bf16x2_split(d * (float)q0, d * (float)q1, h01, l01);
+    bf16x2_split(d * (float)q2, d * (float)q3, h23, l23);
+    uint16_t *o = xs.p + (b * xs.Ms + m) * 64 + 4 * t;
+    *reinterpret_cast<uint2 *>(o) = make_uint2(h01, h23);
+    *reinterpret_cast<uint2 *>(o + 32) = make_uint2(l01, l23);
+}
+
 __device__ __forceinline__ int quant1(float x, float d)
 {
     if (d == 0.0f)
@@ -74,12 +89,14 @@ __device__ __forceinline__ int quant1(float x, float d)
     return q > 127 ? 127 : (q < -127 ? -127 : q);
 }
 
-// Grid: one thread per 4 activations over Mrows x K (Mrows = M).  The plane
-// rows M..Mp-1 are never written: the matmul kernels either skip them or read
-// them through buffer descriptors that stop at row M.
+// Grid: one thread per 4 activations over Mrows x K (Mrows = M, or the
+// padded row count of the compensated bf16 planes when those are written:
+// their rows past M get zeros).  The plane rows M..Mp-1 are never written:
+// the matmul kernels either skip them or read them through buffer
+// descriptors that stop at row M.
 __global__ void __launch_bounds__(256)
 k_quantize(const float *__restrict__ X, uint8_t *__restrict__ Xq, int8_t *__restrict__ qp,
-           float *__restrict__ dp, ZeroList zl, uint16_t *__restrict__ Xbf,
+           float *__restrict__ dp, ZeroList zl, uint16_t *__restrict__ Xbf, XSplit xs,
            int64_t M, int64_t Mrows, int64_t Mp, int64_t K)
 {
     const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -119,7 +136,7 @@ k_quantize(const float *__restrict__ X, uint8_t *__restrict__ Xq, int8_t *__rest
             *reinterpret_cast<uint32_t *>(o) = (uint32_t)__builtin_bit_cast(uint16_t, d16) |
                                                ((uint32_t)__builtin_bit_cast(uint16_t, s16) << 16);
     }
-    if (qp != nullptr) {
+    if (qp != nullptr && m < Mp) {
         *reinterpret_cast<uint32_t *>(qp + (b * Mp + m) * SB + plane_pos(t)) = qword;
         if (t == 0)
             dp[b * Mp + m] = dst;
@@ -129,13 +146,14 @@ k_quantize(const float *__restrict__ X, uint8_t *__restrict__ Xq, int8_t *__rest
         const uint32_t hi = f32_to_bf16_rne(dst * (float)q2) | ((uint32_t)f32_to_bf16_rne(dst * (float)q3) << 16);
         *reinterpret_cast<uint2 *>(Xbf + m * K + b * SB + 4 * t) = make_uint2(lo, hi);
     }
+    write_split(xs, m, b, t, dst, q0, q1, q2, q3);
 }
 
 // ABI Q8_1 blocks -> internal planes and/or bf16 X~.  Same grid shape as
 // k_quantize.
 __global__ void __launch_bounds__(256)
 k_q8_1_convert(const uint8_t *__restrict__ Xq, int8_t *__restrict__ qp, float *__restrict__ dp,
-               ZeroList zl, uint16_t *__restrict__ Xbf, int64_t M, int64_t Mrows,
+               ZeroList zl, uint16_t *__restrict__ Xbf, XSplit xs, int64_t M, int64_t Mrows,
                int64_t Mp, int64_t K)
 {
     const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -153,7 +171,7 @@ k_q8_1_convert(const uint8_t *__restrict__ Xq, int8_t *__restrict__ qp, float *_
         head = *reinterpret_cast<const uint32_t *>(src);
     }
     const float dst = half_bits_to_float(head & 0xFFFFu);
-    if (qp != nullptr) {
+    if (qp != nullptr && m < Mp) {
         *reinterpret_cast<uint32_t *>(qp + (b * Mp + m) * SB + plane_pos(t)) = qword;
         if (t == 0)
             dp[b * Mp + m] = dst;
@@ -165,6 +183,8 @@ k_q8_1_convert(const uint8_t *__restrict__ Xq, int8_t *__restrict__ qp, float *_
         const uint32_t hi = f32_to_bf16_rne(dst * (float)q2) | ((uint32_t)f32_to_bf16_rne(dst * (float)q3) << 16);
         *reinterpret_cast<uint2 *>(Xbf + m * K + b * SB + 4 * t) = make_uint2(lo, hi);
     }
+    write_split(xs, m, b, t, dst, (int8_t)(qword & 0xFF), (int8_t)((qword >> 8) & 0xFF),
+                (int8_t)((qword >> 16) & 0xFF), (int8_t)(qword >> 24));
 }
 
 }  // namespace
@@ -180,20 +200,20 @@ hipError_t launch_zero(float *y, int64_t n, hipStream_t s)
 }
 
 hipError_t launch_quantize(const float *X, void *Xq, const XPlanes *planes, uint16_t *Xbf,
-                           int64_t M, int64_t K, hipStream_t s, const ZeroList &zl)
+                           int64_t M, int64_t K, hipStream_t s, const ZeroList &zl, const XSplit *xs)
 {
-    const int64_t Mrows = M;
+    const int64_t Mrows = xs ? xs->Ms : M;
     const int64_t threads = Mrows * (K / 4);
     const int64_t grid = (threads + 255) / 256;
     hipLaunchKernelGGL(k_quantize, dim3((unsigned)grid), dim3(256), 0, s, X, (uint8_t *)Xq,
                        planes ? planes->qp : nullptr, planes ? planes->dp : nullptr,
-                       zl, Xbf, M, Mrows,
+                       zl, Xbf, xs ? *xs : XSplit(), M, Mrows,
                        planes ? planes->Mp : M, K);
     return hipGetLastError();
 }
 
 hipError_t launch_quantize(const float *X, void *Xq, const XPlanes *planes, uint16_t *Xbf,
-                           int64_t M, int64_t K, hipStream_t s, float *yz, int64_t nz)
+                           int64_t M, int64_t K, hipStream_t s, float *yz, int64_t nz, const XSplit *xs)
 {
     ZeroList zl;
     if (yz != nullptr && nz > 0) {
@@ -201,13 +221,13 @@ hipError_t launch_quantize(const float *X, void *Xq, const XPlanes *planes, uint
         zl.n[0] = nz;
         zl.count = 1;
     }
-    return launch_quantize(X, Xq, planes, Xbf, M, K, s, zl);
+    return launch_quantize(X, Xq, planes, Xbf, M, K, s, zl, xs);
 }
 
 hipError_t launch_q8_1_convert(const void *Xq, const XPlanes *planes, uint16_t *Xbf, int64_t M,
-                              int64_t K, hipStream_t s, float *yz, int64_t nz)
+                              int64_t K, hipStream_t s, float *yz, int64_t nz, const XSplit *xs)
 {
-    const int64_t Mrows = M;
+    const int64_t Mrows = xs ? xs->Ms : M;
     const int64_t threads = Mrows * (K / 4);
     const int64_t grid = (threads + 255) / 256;
     ZeroList zl;
@@ -218,7 +238,7 @@ hipError_t launch_q8_1_convert(const void *Xq, const XPlanes *planes, uint16_t *
     }
     hipLaunchKernelGGL(k_q8_1_convert, dim3((unsigned)grid), dim3(256), 0, s, (const uint8_t *)Xq,
                        planes ? planes->qp : nullptr, planes ? planes->dp : nullptr,
-                       zl, Xbf, M, Mrows,
+                       zl, Xbf, xs ? *xs : XSplit(), M, Mrows,
                        planes ? planes->Mp : M, K);
     return hipGetLastError();
 }
