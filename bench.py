@@ -876,6 +876,8 @@ def run_sweep(path_out):
                         paths.append(iq.PATH_GEMV)
                     if M >= 32:
                         paths.append(iq.PATH_DEQ_BF16)
+                    if M >= 64:
+                        paths.append(iq.PATH_BF16X3)
                     for p in paths:
                         rec = point_record(N, K, M, p, *measure_point(rot, X, N, K, p, reps=20))
                         rec["workload"] = wl.name

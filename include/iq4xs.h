@@ -74,7 +74,8 @@ extern "C" {
 #define IQ4XS_PATH_DEQ_BF16 3 /* dequantize W and X~ to bf16, bf16-MFMA GEMM (inexact:
                                  rounds W~ and X~ to 8 significant bits)                 */
 #define IQ4XS_PATH_BF16X3 4   /* W dequantized inside the GEMM into LDS, W~ and X~ each as
-                                 bf16 hi + lo, three bf16-MFMA products per term          */
+                                 bf16 hi + lo, three bf16-MFMA products per term (within
+                                 the per-row bound; see iq4xs_gemm_path)                 */
 #define IQ4XS_NUM_PATHS 5
 
 /* ---- weight formats (the iq4xs_*_fmt entry points) ----
@@ -115,13 +116,23 @@ int iq4xs_quantize_q8_1(const float *X, void *Xq, int64_t M, int64_t K, void *st
 /* Y = X * W^T with X quantized to Q8_1 on the device ("V100TPS engine log",
  * batched IQ4_XS kernel section).  Quantization, the dispatcher's choice of
  * path and the matmul are all enqueued on `stream`.  Y is overwritten.
- * Stream-ordered scratch (about 1.2*M*K bytes, plus 2*(M+N)*K for the bf16
- * path) is allocated from the device's default memory pool and released on
- * `stream`. */
+ * Stream-ordered scratch (about 1.2*M*K bytes; 2*(M+N)*K for DEQ_BF16;
+ * 4*K*M' for BF16X3, M' = M rounded up to 256) is allocated from the
+ * device's default memory pool and released on `stream`. */
 int iq4xs_gemm(const void *W, const float *X, float *Y, int64_t M, int64_t N, int64_t K,
                void *stream);
 
-/* As iq4xs_gemm with the path forced (IQ4XS_PATH_*; AUTO = dispatcher). */
+/* As iq4xs_gemm with the path forced (IQ4XS_PATH_*; AUTO = dispatcher).
+ * BF16X3 ("V100TPS engine log", M=64 kernel-launch table: dequantize, then a
+ * dense tensor-core GEMM; "V100TPS MTP investigation", crossover passage:
+ * the dense path wins at larger M): each weight d*(ls-32)*kv and each
+ * d_x*q is split into hi = bf16(v) and lo = bf16(v - hi) (nearest even),
+ * and Wh*Xh + Wh*Xl + Wl*Xh is summed in fp32 on the matrix cores, the
+ * weights dequantized per 32-weight sub-block into LDS (no bf16 copy of W in
+ * HBM).  Each product is within 3.02*2^-16 of the exact one, so the result
+ * meets the same per-row bound as GEMV and MMQ (measured per-row ratio near
+ * 1e-5) and the table may route to it without an opt-in.  IQ4_XS weights
+ * only; EPATH when the activation planes would reach 2 GiB. */
 int iq4xs_gemm_path(const void *W, const float *X, float *Y, int64_t M, int64_t N, int64_t K,
                     int path, void *stream);
 
@@ -157,8 +168,8 @@ int iq4xs_gemm_noalloc(const void *W, const float *X, float *Y, int64_t M, int64
  * X quantized to Q8_1, per 32-weight block the exact integer dot of the
  * block's values with the Q8_1 values, scaled in fp32 by d (or d*(ls-32))
  * and d_x; the result is within the same per-row bound of the oracle.
- * `path`: AUTO (the measured table's GEMV / MMQ bands; its DEQ_BF16 bands
- * apply to IQ4_XS only), GEMV (M <= 4) or MMQ; DEQ_BF16 is EPATH for IQ4_NL
+ * `path`: AUTO (the measured table's GEMV / MMQ bands; its bf16 bands
+ * apply to IQ4_XS only), GEMV (M <= 4) or MMQ; DEQ_BF16 and BF16X3 are EPATH for IQ4_NL
  * and Q4_0, and so is MMQ for a matrix of 2 GiB or more in those formats
  * (the fallback kernel for such sizes reads IQ4_XS only).  `workspace` as in
  * iq4xs_gemm_ws (at least iq4xs_gemm_fmt_workspace_bytes bytes, 256-byte
@@ -189,8 +200,8 @@ int iq4xs_gemm_q8_1(const void *W, const void *Xq, float *Y, int64_t M, int64_t 
  * block, rows padded to a multiple of 4).  K % 256 == 0. */
 int iq4xs_act_bytes(int64_t M, int64_t K, size_t *out);
 int iq4xs_prepare_act(const float *X, void *act, int64_t M, int64_t K, void *stream);
-/* Y = X * W^T from prepared activations; path AUTO, GEMV or MMQ (DEQ_BF16 is
- * EPATH here).  Launches the matmul kernel only -- plus, where output tiles
+/* Y = X * W^T from prepared activations; path AUTO, GEMV or MMQ (DEQ_BF16 and
+ * BF16X3 are EPATH here; AUTO takes MMQ where the table names BF16X3).  Launches the matmul kernel only -- plus, where output tiles
  * are shared by more than two workgroups (MMQ tile kernel with few tiles,
  * K-split fallback), a second kernel that adds their partial results in a
  * fixed order from a stream-ordered workspace; and, where the MMQ kernels
@@ -246,7 +257,7 @@ int iq4xs_dispatch(int64_t M, int64_t N, int64_t K, int *path_out);
  * Format: text lines
  *   arch <gfx name>
  *   cus <compute units>        (optional: the device the bands were measured on)
- *   band <GEMV|MMQ|DEQ_BF16> <M_lo> <M_hi> <N> <K>
+ *   band <GEMV|MMQ|BF16X3|DEQ_BF16> <M_lo> <M_hi> <N> <K>
  * where N and K are "*" (any), a value, or an inclusive range "lo-hi";
  * '#' starts a comment; the first band that matches (M, N, K) wins; DEQ_BF16
  * bands are skipped unless IQ4XS_ALLOW_BF16=1 was set at initialisation.
@@ -255,7 +266,7 @@ int iq4xs_dispatch(int64_t M, int64_t N, int64_t K, int *path_out);
  * explicit paths and the host-only iq4xs_dispatch query are unaffected. */
 int iq4xs_load_dispatch_table(const char *path);
 
-/* Name of a path ("AUTO", "GEMV", "MMQ", "DEQ_BF16") or "?" */
+/* Name of a path ("AUTO", "GEMV", "MMQ", "DEQ_BF16", "BF16X3") or "?" */
 const char *iq4xs_path_name(int path);
 
 /* Message for the last error on this thread ("" if none); the pointer stays

@@ -13,6 +13,9 @@ hard-coded) is written as
   * per measured shape, bands of consecutive measured M whose fastest exact
     path (GEMV or MMQ) is the GEMV, each band reaching up to the next
     measured M minus one;
+  * per measured shape, a BF16X3 band from the smallest measured M from
+    which the fused compensated-bf16 path is faster than GEMV and MMQ at
+    every larger measured M (it meets the same per-row bound as they do);
   * per measured shape, a DEQ_BF16 band from the smallest measured M from
     which the bf16 path is fastest at every larger measured M (these bands
     only apply with IQ4XS_ALLOW_BF16=1: the bf16 path is not exact);
@@ -90,6 +93,19 @@ def table(best, arch="gfx950", cus=None):
             lines.append(f"# {N}x{K}: {detail}")
             lines.append(f"band GEMV {ms[i]} {hi} {N} {K}")
             i = j + 1
+        # the fused path from the smallest M after which it beats the others
+        # that meet the bound
+        lo = None
+        for m in reversed(ms):
+            cand = {p: t for p, t in pts[m].items() if p in ("GEMV", "MMQ", "BF16X3")}
+            if "BF16X3" in cand and min(cand, key=cand.get) == "BF16X3":
+                lo = m
+            else:
+                break
+        if lo is not None:
+            lines.append(f"# {N}x{K}: BF16X3 fastest exact-bound path from M={lo} "
+                         f"({pts[lo]['BF16X3'] * 1e3:.1f} us vs MMQ {pts[lo]['MMQ'] * 1e3:.1f} us)")
+            lines.append(f"band BF16X3 {lo} {BIG} {N} {K}")
         # bf16 from the smallest M after which it always wins
         lo = None
         for m in reversed(ms):

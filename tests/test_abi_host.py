@@ -286,18 +286,25 @@ def test_calibrate_writes_a_loadable_table(tmp_path):
     for M, q, b in ((128, 0.1, 0.2), (256, 0.3, 0.2), (512, 0.6, 0.4)):
         rec(4096, 4096, M, "MMQ", q)
         rec(4096, 4096, M, "DEQ_BF16", b)
+    for M, q, x in ((64, 0.1, 0.2), (128, 0.2, 0.15), (256, 0.3, 0.35), (512, 0.6, 0.5)):
+        rec(8192, 4096, M, "MMQ", q)
+        rec(8192, 4096, M, "BF16X3", x)
     sweep = tmp_path / "sweep.jsonl"
     sweep.write_text("\n".join(json.dumps(r) for r in recs) + "\n")
     out = tmp_path / "table.txt"
     calibrate.main([str(sweep), str(out)])
     text = out.read_text()
     assert "band GEMV 1 3 4096 1024" in text and "band DEQ_BF16 256 1000000000 4096 4096" in text
+    # the fused path wins at 128 but not at 256, so only from 512 on
+    assert "band BF16X3 512 1000000000 8192 4096" in text
     try:
         iq.load_dispatch_table(str(out))
         assert iq.dispatch(2, 4096, 1024) == iq.PATH_GEMV
         assert iq.dispatch(4, 4096, 1024) == iq.PATH_MMQ
         assert iq.dispatch(1, 8192, 1024) == iq.PATH_MMQ
         assert iq.dispatch(300, 4096, 4096) == iq.PATH_MMQ      # bf16 bands need the opt-in
+        assert iq.dispatch(600, 8192, 4096) == iq.PATH_BF16X3    # within the bound: no opt-in
+        assert iq.dispatch(300, 8192, 4096) == iq.PATH_MMQ
     finally:
         iq.load_dispatch_table(None)
 

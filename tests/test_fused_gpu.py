@@ -25,7 +25,17 @@ from gpu_util import assert_rows_close, dev, poisoned, row_errors
 pytestmark = pytest.mark.gpu
 
 P = iq.PATH_BF16X3
-X3_TOL = 4e-6      # against the compensated formulation (fp32 accumulation only)
+
+
+def x3_tol(K):
+    """Per-row bound against the compensated formulation: only the fp32
+    accumulation of 3K products differs, an error that grows like sqrt(K)
+    (measured 4.2e-6 at K = 17408); a dropped or doubled product would be
+    near 1e-3."""
+    return 4e-6 * max(1.0, (K / 2048) ** 0.5)
+
+
+X3_TOL = x3_tol(2048)
 O = None
 
 
@@ -51,7 +61,7 @@ def test_matches_both_formulations(M, N, K):
     Xq = O.quantize_q8_1(X)
     Wd, Xd = dev(W), dev(X)
     y = iq.gemm(Wd, Xd, path=P, out=poisoned((M, N))).cpu().numpy()
-    assert_rows_close(y, O.gemm_bf16x3(W, Xq, K), tol=X3_TOL, what=f"BF16X3 vs compensated M={M} N={N} K={K}")
+    assert_rows_close(y, O.gemm_bf16x3(W, Xq, K), tol=x3_tol(K), what=f"BF16X3 vs compensated M={M} N={N} K={K}")
     r = assert_rows_close(y, O.gemm_q8_1(W, Xq, K), what=f"BF16X3 vs integer M={M} N={N} K={K}")
     print(f"[bf16x3-vs-integer-oracle] M={M} N={N} K={K} per-row ratio max {r:.3e}", flush=True)
     # the pre-quantized and caller-workspace entry points: the same launches
@@ -173,7 +183,7 @@ def test_prefill_full_size_sampled(N, K, M):
     Xq = O.quantize_q8_1(X)
     y = iq.gemm(Wd, dev(X), path=P, out=poisoned((M, N))).cpu().numpy()
     assert np.all(np.isfinite(y)), "outputs not written"
-    assert_rows_close(y[:, cols], O.gemm_bf16x3(W[cols], Xq, K), tol=X3_TOL, what="vs compensated")
+    assert_rows_close(y[:, cols], O.gemm_bf16x3(W[cols], Xq, K), tol=x3_tol(K), what="vs compensated")
     r = row_errors(y[:, cols], O.gemm_q8_1(W[cols], Xq, K))
     print(f"[bf16x3-vs-integer-oracle] N={N} K={K} M={M} per-row ratio max {r.max():.3e} "
           f"median {np.median(r):.3e}", flush=True)

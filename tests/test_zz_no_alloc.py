@@ -38,6 +38,8 @@ PAIRS = [
     ((512, 2048, 1024, iq.PATH_MMQ), (33, 130, 1280, iq.PATH_MMQ)),
     # GEMV
     ((4, 2048, 2048, iq.PATH_GEMV), (1, 257, 1024, iq.PATH_GEMV)),
+    # fused dequantize-in-LDS path: compensated activation planes in the scratch
+    ((300, 1000, 2048, iq.PATH_BF16X3), (37, 260, 512, iq.PATH_BF16X3)),
 ]
 
 
@@ -64,8 +66,12 @@ def test_noalloc_matches_allocating_entry_point(pair):
             assert np.all(np.isfinite(a)), "outputs not written"
             assert np.array_equal(a, b), f"noalloc differs from iq4xs_gemm_path (M={M} N={N} K={K})"
             cols = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(M).integers(0, N, 96)]))
-            ref = O.gemm_q8_1(W[cols], O.quantize_q8_1(X), K)
+            Xq = O.quantize_q8_1(X)
+            ref = O.gemm_q8_1(W[cols], Xq, K)
             assert_rows_close(a[:, cols], ref, what=f"noalloc M={M} N={N} K={K}")
+            if path == iq.PATH_BF16X3:
+                assert_rows_close(a[:, cols], O.gemm_bf16x3(W[cols], Xq, K), tol=4e-6,
+                                  what=f"noalloc BF16X3 M={M} N={N} K={K}")
 
 
 def test_noalloc_refuses_oversized_scratch_on_the_device():
