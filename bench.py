@@ -32,6 +32,8 @@ Printed: one JSON line with
                int8 and bf16 matrix-core instructions
   group        one X against a pair of decode-shape matrices: grouped call vs two calls
   formats      a few points with IQ4_NL and Q4_0 weights
+  fused_bf16x3 the fused compensated-bf16 path at every prefill point, beside
+               the path the table picks there
   cpu_baseline the CPU oracle (never tuned) on a bounded column sample of the
                same 52 points, in the same unit.
 `--sweep FILE` times every (shape, M, path) point and writes one JSON object
@@ -424,6 +426,32 @@ def dominant_rooflines(recs):
     return out
 
 
+def fused_points(recs, reps=10):
+    """The fused compensated-bf16 path (BF16X3) at every prefill point, per
+    call (quantization included, graph replay) beside the point's own path.
+    Work: three bf16 products per weight x activation, 6*M*N*K flops against
+    the bf16 MFMA peak."""
+    by = {(r["N"], r["K"], r["M"]): r for r in recs}
+    out = []
+    for (N, K) in synth.PREFILL.shapes:
+        rot = Rotation(synth.PREFILL.w(N, K))
+        for M in synth.PREFILL.ms:
+            X = torch.from_numpy(synth.PREFILL.x(M, K, N=N)).cuda()
+            t_call, _, _ = measure_point(rot, X, N, K, iq.PATH_BF16X3, reps=reps)
+            flops = 6.0 * M * N * K
+            ent = {"N": N, "K": K, "M": M, "ms": t_call, "bf16_TFLOPs": flops / (t_call * 1e-3) / 1e12,
+                   "bf16_frac": flops / (t_call * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                   "int8_equiv_TOPS": 2.0 * M * N * K / (t_call * 1e-3) / 1e12}
+            if (N, K, M) in by:
+                ent["auto_ms"] = by[(N, K, M)]["ms"]
+                ent["auto_path"] = by[(N, K, M)]["path"]
+                ent["speedup_vs_auto"] = by[(N, K, M)]["ms"] / t_call
+            out.append(ent)
+        del rot
+        torch.cuda.empty_cache()
+    return out
+
+
 def format_points(reps=20):
     """A few points with IQ4_NL and Q4_0 weights (iq4xs_gemm_fmt, AUTO)."""
     out = []
@@ -571,17 +599,26 @@ def profile_shapes(specs):
     """Fixed launches for rocprofv3 at given shapes ("MxNxK", comma
     separated): per shape, 20 launches of the matmul kernel(s) alone
     (gemm_act, rotated weights), inputs of the workload the shape belongs to
-    (else the prefill recipe); then the calibration probes."""
+    (else the prefill recipe); then the calibration probes.  "MxNxK:PATH"
+    forces a path and launches whole calls (for the paths gemm_act does not
+    take: their quantize kernel shows in the trace beside the matmul)."""
     for spec in specs.split(","):
-        M, N, K = (int(v) for v in spec.split("x"))
+        shape, _, pname = spec.partition(":")
+        M, N, K = (int(v) for v in shape.split("x"))
         wl = next((w for w in synth.WORKLOADS if (N, K) in w.shapes), synth.WORKLOADS[-1])
         rot = Rotation(wl.w(N, K))
         X = torch.from_numpy(wl.x(M, K, N=N)).cuda()
-        act = iq.prepare_act(X)
         Y = torch.empty((M, N), dtype=torch.float32, device="cuda")
-        path = iq.dispatch(M, N, K)
-        for _ in range(20):
-            iq.gemm_act(rot.next(), act, M, K, path=path, out=Y)
+        if pname:
+            path = iq.PATHS[pname]
+            ws = torch.empty(iq.workspace_bytes(M, N, K, path), dtype=torch.uint8, device="cuda")
+            for _ in range(20):
+                iq.gemm(rot.next(), X, path=path, out=Y, workspace=ws)
+        else:
+            act = iq.prepare_act(X)
+            path = iq.dispatch(M, N, K)
+            for _ in range(20):
+                iq.gemm_act(rot.next(), act, M, K, path=path, out=Y)
         torch.cuda.synchronize()
         print(f"[profile-shapes] M={M} N={N} K={K} {kernel_name(M, N, K, path)} x20", flush=True)
         del rot
@@ -654,6 +691,57 @@ def summarize_pmc(fetch_dir, write_dir, out, cmd_fetch, cmd_write):
         lines.append(f"traffic {k} <{label}> {f:.1f} {w:.1f} {f * 1024.0 * f_scale + w * 1024.0 * w_scale:.0f}")
     for M in ms:
         lines.append(f"algorithmic M={M} {algo_bytes_kernel(M, N, K):.0f}")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_fused(trace_dir, fetch_dir, write_dir, out, cmds, spec):
+    """One shape of a --profile-shapes run with the BF16X3 path forced
+    ("MxNxK:BF16X3"): the fused kernel's and the quantizer's durations from
+    the kernel trace, the fused kernel's HBM bytes per launch from the
+    counter runs (calibrated by their probes), its algorithmic bytes and its
+    bf16 rate (three products per term, 6*M*N*K flops) at the trace's
+    average duration."""
+    M, N, K = (int(v) for v in spec.split(":")[0].split("x"))
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_trace.csv under {trace_dir}")
+    durs = {}
+    for r in csv.DictReader(open(files[0])):
+        for k in ("k_gemm_x3", "k_quantize"):
+            if k in r["Kernel_Name"]:
+                durs.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+    fr, wr = _counter_rows(fetch_dir), _counter_rows(write_dir)
+    fk, wk, f_scale, w_scale = _probe_scales(fr, wr)
+
+    def per_launch(rows, counter):
+        acc = {}
+        for r in rows:
+            if r["Counter_Name"] == counter and "k_gemm_x3" in r["Kernel_Name"]:
+                acc[r["Dispatch_Id"]] = acc.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+        return sum(acc.values()) / len(acc) if acc else float("nan")
+    f_kib, w_kib = per_launch(fr, "FETCH_SIZE"), per_launch(wr, "WRITE_SIZE")
+    traffic = f_kib * 1024.0 * f_scale + w_kib * 1024.0 * w_scale
+    ms_rows = -(-M // 256) * 256
+    algo = 0.53125 * N * K + 4.0 * ms_rows * K + 4.0 * M * N
+    x3 = durs.get("k_gemm_x3", [float("nan")])
+    avg = sum(x3) / len(x3)
+    lines = [f"# fused compensated-bf16 kernel (BF16X3 path), M={M} N={N} K={K}: kernel trace and HBM counters "
+             "(20 whole calls, rotated weights)",
+             *[f"# command: {c}" for c in cmds],
+             f"source_hash k_gemm_x3 {source_hash('k_gemm_x3')}",
+             f"# calibration by the runs' own probes ({PROBE_BYTES} bytes read / written): fetch x{f_scale:.4f}, "
+             f"write x{w_scale:.4f}",
+             "# kernel  calls  avg_us  min_us  max_us"]
+    for k, v in sorted(durs.items()):
+        lines.append(f"{k} {len(v)} {sum(v) / len(v):.2f} {min(v):.2f} {max(v):.2f}")
+    lines += [f"k_gemm_x3 fetch_kib {f_kib:.1f} write_kib {w_kib:.1f} traffic_bytes_per_launch {traffic:.0f}",
+              f"k_gemm_x3 algorithmic_bytes_per_launch {algo:.0f} (weights 0.53125/weight, compensated activation "
+              "planes 4 B per element of the padded rows, Y)",
+              f"k_gemm_x3 traffic/algorithmic {traffic / algo:.2f}",
+              f"k_gemm_x3 bf16 TFLOP/s at avg {6.0 * M * N * K / (avg * 1e-6) / 1e12:.0f} "
+              f"({6.0 * M * N * K / (avg * 1e-6) / 1e12 / BF16_PEAK_TFLOPS * 100:.1f}% of 2.5 PFLOP/s)"]
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -928,6 +1016,7 @@ def main():
     ap.add_argument("--summarize-pmc-shapes", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "SHAPES"))
     ap.add_argument("--summarize-sq", nargs="+", metavar="DIR", help="SQ counter runs -> instruction mix")
     ap.add_argument("--summarize-sweep", metavar="JSONL")
+    ap.add_argument("--summarize-fused", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace-shapes", nargs=2, metavar=("TRACE_DIR", "SHAPES"))
     ap.add_argument("--trace-dir", default=None, help="kernel-trace runs of the same launches, comma-separated")
     ap.add_argument("--shapes", default="", help="MxNxK,... of the --profile-shapes runs")
@@ -940,7 +1029,8 @@ def main():
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, args.out or TRAFFIC_FILE, args.cmd_fetch, args.cmd_write)
         return
-    for flag in ("summarize_pmc_shapes", "summarize_sq", "summarize_trace", "check_trace", "summarize_sweep"):
+    for flag in ("summarize_pmc_shapes", "summarize_sq", "summarize_trace", "check_trace", "summarize_sweep",
+                 "summarize_fused"):
         if getattr(args, flag) and not args.out:
             raise SystemExit(f"--{flag.replace('_', '-')} needs --out")
     if args.summarize_pmc_shapes:
@@ -953,6 +1043,9 @@ def main():
         return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.out, args.cmd, args.title)
+        return
+    if args.summarize_fused:
+        summarize_fused(*args.summarize_fused, args.out, [c for c in args.cmd.split(";;") if c], args.shapes)
         return
     if args.summarize_sweep:
         summarize_sweep(args.summarize_sweep, args.out, args.cmd)
@@ -1052,6 +1145,8 @@ def main():
     out["group"] = measure_group()
     out["formats"] = format_points()
     print("[bench] group and formats done", file=sys.stderr, flush=True)
+    out["fused_bf16x3"] = fused_points(recs)
+    print("[bench] fused path points done", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(pts)
     if args.sweep:
