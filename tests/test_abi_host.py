@@ -108,6 +108,22 @@ def test_unknown_path_and_gemv_limit():
     assert L.iq4xs_gemm_path(A, A * 2, A * 4, 5, 8, 256, iq.PATH_GEMV, None) == iq.EPATH
 
 
+def test_fused_path_on_the_host():
+    """The fused compensated path (BF16X3): its name, its scratch (the hi/lo
+    activation planes, 4 bytes per element of M rounded up to 256 rows), its
+    band in a table, and the prepared-activation entry point refusing it."""
+    assert iq.path_name(iq.PATH_BF16X3) == "BF16X3" and iq.PATHS["BF16X3"] == iq.PATH_BF16X3
+    size = ctypes.c_size_t()
+    for M, K in ((1, 256), (256, 5120), (257, 5120), (512, 17408)):
+        assert L.iq4xs_gemm_workspace_bytes(M, 4096, K, iq.PATH_BF16X3, ctypes.byref(size)) == iq.OK
+        assert size.value == (K // 32) * (-(-M // 256) * 256) * 128, (M, K)
+    assert L.iq4xs_gemm_workspace_bytes(4, 1024, 300, iq.PATH_BF16X3, ctypes.byref(size)) == iq.EINVAL
+    # prepared activations feed the integer kernels only
+    ab = ctypes.c_size_t()
+    assert L.iq4xs_act_bytes(256, 512, ctypes.byref(ab)) == iq.OK
+    assert L.iq4xs_gemm_act(A, 1 << 44, 2 << 44, 256, 512, 512, iq.PATH_BF16X3, None) == iq.EPATH
+
+
 def test_workspace_query_and_checks():
     size = ctypes.c_size_t()
     ref = {}
@@ -379,9 +395,10 @@ def test_format_entry_points_validate_on_the_host():
     for bad_fmt in (3, 7, -2):
         assert L.iq4xs_gemm_fmt(bad_fmt, A, far, 2 * far, 4, 8, 256, 0, None, 0, None) == iq.EINVAL
     for fmt in (iq.FMT_IQ4_NL, iq.FMT_Q4_0):
-        # the bf16 path reads IQ4_XS only
-        assert L.iq4xs_gemm_fmt(fmt, A, far, 2 * far, 64, 8, 256, iq.PATH_DEQ_BF16, None, 0, None) == iq.EPATH
-        assert L.iq4xs_gemm_fmt_workspace_bytes(fmt, 64, 8, 256, iq.PATH_DEQ_BF16, ctypes.byref(out)) == iq.EPATH
+        # the bf16 paths read IQ4_XS only
+        for p in (iq.PATH_DEQ_BF16, iq.PATH_BF16X3):
+            assert L.iq4xs_gemm_fmt(fmt, A, far, 2 * far, 64, 8, 256, p, None, 0, None) == iq.EPATH
+            assert L.iq4xs_gemm_fmt_workspace_bytes(fmt, 64, 8, 256, p, ctypes.byref(out)) == iq.EPATH
         assert L.iq4xs_gemm_fmt(fmt, A, far, 2 * far, 4, 8, 300, 0, None, 0, None) == iq.EINVAL
         assert L.iq4xs_gemm_fmt(fmt, A + 8, far, 2 * far, 4, 8, 256, 0, None, 0, None) == iq.EALIGN
         assert L.iq4xs_gemm_fmt(fmt, A, far, 2 * far, 5, 8, 256, iq.PATH_GEMV, None, 0, None) == iq.EPATH
