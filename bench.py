@@ -80,7 +80,6 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_mmv_decode_n10240_k5120_traffic
 TILE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_mmqt_tile_shapes_traffic.txt")
 KERNEL_SOURCES = {"k_mmv": ["mmv.hip", "common.hpp", "stream.hpp"], "k_gemv": ["gemv.hip", "common.hpp"],
                   "k_mmq": ["mmq.hip", "common.hpp"], "k_mmqt": ["mmqt.hip", "common.hpp", "stream.hpp"],
-                  "k_gemm_bf16": ["deq.hip", "common.hpp"],
                   "k_gemm_x3": ["fused.hip", "common.hpp", "stream.hpp"]}
 # Exact formulation on the matrix cores: per (output, 32-wide sub-block) the
 # int8 MFMA does 32 MACs (0.031 cycles per SIMD at 2048 ops/cycle) and the
@@ -95,9 +94,7 @@ def kernel_name(M, N, K, path):
     rocprofv3 trace)."""
     if path == iq.PATH_GEMV:
         return "k_gemv"
-    if path == iq.PATH_DEQ_BF16:
-        return "k_gemm_bf16"
-    if path == iq.PATH_BF16X3:
+    if path in (iq.PATH_DEQ_BF16, iq.PATH_BF16X3):
         return "k_gemm_x3"
     nb = K // 256
     if M <= 32 and nb % 2 == 0 and N * nb * 136 < (1 << 31):
@@ -527,7 +524,7 @@ def check_trace(trace_dir, out, cmd):
         elif cur is not None:
             cur.append((k, (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3))
     pts = sweep_points()
-    families = {"GEMV": {"k_gemv"}, "MMQ": {"k_mmv", "k_mmqt", "k_mmq"}, "DEQ_BF16": {"k_gemm_bf16"},
+    families = {"GEMV": {"k_gemv"}, "MMQ": {"k_mmv", "k_mmqt", "k_mmq"}, "DEQ_BF16": {"k_gemm_x3"},
                 "BF16X3": {"k_gemm_x3"}}
     lines = ["# kernels launched per call, from a rocprofv3 kernel trace of bench.py --profile-points",
              f"# command: {cmd}",
@@ -542,7 +539,7 @@ def check_trace(trace_dir, out, cmd):
         path = iq.path_name(iq.dispatch(M, N, K))
         expect = kernel_name(M, N, K, iq.PATHS[path])
         per_call = names[:len(names) // 2]
-        mat = [k for k in per_call if k.startswith(("k_gemv", "k_mmv", "k_mmqt", "k_mmq", "k_gemm_bf16", "k_gemm_x3"))]
+        mat = [k for k in per_call if k.startswith(("k_gemv", "k_mmv", "k_mmqt", "k_mmq", "k_gemm_x3"))]
         ok = (len(names) % 2 == 0 and names[:len(names) // 2] == names[len(names) // 2:] and
               per_call[0] == "k_quantize" and mat and mat[0] == expect and mat[0] in families[path])
         bad += not ok

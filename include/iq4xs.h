@@ -71,8 +71,8 @@ extern "C" {
 #define IQ4XS_PATH_AUTO 0     /* the dispatcher picks from its measured table            */
 #define IQ4XS_PATH_GEMV 1     /* wavefront-per-row integer-dot kernel, 1 <= M <= 4        */
 #define IQ4XS_PATH_MMQ 2      /* int8-MFMA tile kernel, any M                             */
-#define IQ4XS_PATH_DEQ_BF16 3 /* dequantize W and X~ to bf16, bf16-MFMA GEMM (inexact:
-                                 rounds W~ and X~ to 8 significant bits)                 */
+#define IQ4XS_PATH_DEQ_BF16 3 /* W~ and X~ rounded to bf16, bf16-MFMA GEMM, W dequantized
+                                 inside the GEMM (inexact: 8 significant bits per operand) */
 #define IQ4XS_PATH_BF16X3 4   /* W dequantized inside the GEMM into LDS, W~ and X~ each as
                                  bf16 hi + lo, three bf16-MFMA products per term (within
                                  the per-row bound; see iq4xs_gemm_path)                 */
@@ -116,9 +116,9 @@ int iq4xs_quantize_q8_1(const float *X, void *Xq, int64_t M, int64_t K, void *st
 /* Y = X * W^T with X quantized to Q8_1 on the device ("V100TPS engine log",
  * batched IQ4_XS kernel section).  Quantization, the dispatcher's choice of
  * path and the matmul are all enqueued on `stream`.  Y is overwritten.
- * Stream-ordered scratch (about 1.2*M*K bytes; 2*(M+N)*K for DEQ_BF16;
- * 4*K*M' for BF16X3, M' = M rounded up to 256) is allocated from the
- * device's default memory pool and released on `stream`. */
+ * Stream-ordered scratch (about 1.2*M*K bytes; 4*K*M' for the bf16 paths,
+ * M' = M rounded up to 256) is allocated from the device's default memory
+ * pool and released on `stream`. */
 int iq4xs_gemm(const void *W, const float *X, float *Y, int64_t M, int64_t N, int64_t K,
                void *stream);
 

@@ -304,16 +304,13 @@ int resolve_path(int path, int64_t M, int64_t N, int64_t K, int *out, int fmt = 
 }
 
 // Scratch a path needs: activation planes (+ the split-K partial sums of
-// MMQ), for BF16X3 the compensated bf16 activation planes, or for DEQ_BF16
-// the bf16 activations and weights.
+// MMQ), or for the bf16 paths the hi/lo bf16 activation planes.
 size_t workspace_need(int path, int64_t M, int64_t N, int64_t K, int fmt = FMT_IQ4_XS)
 {
     if (path == IQ4XS_PATH_GEMV || path == IQ4XS_PATH_MMQ)
         return (size_t)round_up((int64_t)xplanes_bytes(M, K), 256) +
                (path == IQ4XS_PATH_MMQ ? mmq_plan(M, N, K, fmt).workspace_bytes : 0);
-    if (path == IQ4XS_PATH_BF16X3)
-        return fused_xs_bytes(M, K);
-    return (size_t)round_up(M * K * 2, 256) + (size_t)(N * K * 2);
+    return fused_xs_bytes(M, K);
 }
 
 // Common tail of the gemm entry points.  Exactly one of X (fp32) and Xq (Q8_1
@@ -363,38 +360,27 @@ int run_gemm(const void *W, const float *X, const void *Xq, float *Y, int64_t M,
         const bool zero = path == IQ4XS_PATH_MMQ && mmq_plan(M, N, K, fmt).zero_y;
         float *yz = zero ? Y : nullptr;
         const int64_t nz = zero ? M * N : 0;
-        hipError_t e = X ? launch_quantize(X, nullptr, &xp, nullptr, M, K, s, yz, nz)
-                         : launch_q8_1_convert(Xq, &xp, nullptr, M, K, s, yz, nz);
+        hipError_t e = X ? launch_quantize(X, nullptr, &xp, M, K, s, yz, nz)
+                         : launch_q8_1_convert(Xq, &xp, M, K, s, yz, nz);
         if ((st = launch_err(e, "quantize")) != IQ4XS_OK)
             return st;
         e = path == IQ4XS_PATH_GEMV ? launch_gemv(W, xp, Y, N, s, fmt)
                                     : launch_mmq(W, xp, Y, N, base + pbytes, zero, s, fmt);
         return launch_err(e, path_name(path));
     }
-    if (path == IQ4XS_PATH_BF16X3) {
-        if (fused_grid(M, N) > INT32_MAX || fused_xs_bytes(M, K) >= (size_t)INT32_MAX)
-            return fail(IQ4XS_EPATH, "BF16X3 takes fewer than 2^31 workgroups and activation planes "
-                        "below 2 GiB (M=%lld N=%lld K=%lld)", (long long)M, (long long)N, (long long)K);
-        XSplit xsp;
-        xsp.p = (uint16_t *)base;
-        xsp.Ms = fused_ms(M);
-        const hipError_t e = X ? launch_quantize(X, nullptr, nullptr, nullptr, M, K, s, nullptr, 0, &xsp)
-                               : launch_q8_1_convert(Xq, nullptr, nullptr, M, K, s, nullptr, 0, &xsp);
-        if ((st = launch_err(e, "quantize")) != IQ4XS_OK)
-            return st;
-        return launch_err(launch_fused_x3(W, xsp.p, Y, M, N, K, s), "gemm_x3");
-    }
-    // DEQ_BF16: X~ bf16 [M][K], then W~ bf16 [N][K] (256-byte aligned)
-    const size_t xbytes = (size_t)round_up(M * K * 2, 256);
-    uint16_t *xb = (uint16_t *)base;
-    uint16_t *wb = (uint16_t *)(base + xbytes);
-    const hipError_t e = X ? launch_quantize(X, nullptr, nullptr, xb, M, K, s)
-                           : launch_q8_1_convert(Xq, nullptr, xb, M, K, s);
+    // BF16X3 and DEQ_BF16: the fused kernel, from the hi/lo activation planes
+    // (DEQ_BF16 uses the hi parts only: the plain bf16 formulation)
+    if (fused_grid(M, N) > INT32_MAX || fused_xs_bytes(M, K) >= (size_t)INT32_MAX)
+        return fail(IQ4XS_EPATH, "the bf16 paths take fewer than 2^31 workgroups and activation planes "
+                    "below 2 GiB (M=%lld N=%lld K=%lld)", (long long)M, (long long)N, (long long)K);
+    XSplit xsp;
+    xsp.p = (uint16_t *)base;
+    xsp.Ms = fused_ms(M);
+    const hipError_t e = X ? launch_quantize(X, nullptr, nullptr, M, K, s, nullptr, 0, &xsp)
+                           : launch_q8_1_convert(Xq, nullptr, M, K, s, nullptr, 0, &xsp);
     if ((st = launch_err(e, "quantize")) != IQ4XS_OK)
         return st;
-    if ((st = launch_err(launch_dequant_bf16(W, wb, N, K, s), "dequant_bf16")) != IQ4XS_OK)
-        return st;
-    return launch_err(launch_gemm_bf16(xb, wb, Y, M, N, K, s), "gemm_bf16");
+    return launch_err(launch_fused_x3(W, xsp.p, Y, M, N, K, s, path == IQ4XS_PATH_BF16X3), "gemm_x3");
 }
 
 }  // namespace
@@ -437,7 +423,7 @@ int iq4xs_quantize_q8_1(const float *X, void *Xq, int64_t M, int64_t K, void *st
     int st = check_device();
     if (st != IQ4XS_OK)
         return st;
-    return launch_err(launch_quantize(X, Xq, nullptr, nullptr, M, K, (hipStream_t)stream), "quantize");
+    return launch_err(launch_quantize(X, Xq, nullptr, M, K, (hipStream_t)stream), "quantize");
 }
 
 int iq4xs_gemm_path(const void *W, const float *X, float *Y, int64_t M, int64_t N, int64_t K,
@@ -626,7 +612,7 @@ int iq4xs_prepare_act(const float *X, void *act, int64_t M, int64_t K, void *str
     if ((st = check_device()) != IQ4XS_OK)
         return st;
     const XPlanes xp = xplanes_at(act, M, K);
-    return launch_err(launch_quantize(X, nullptr, &xp, nullptr, M, K, (hipStream_t)stream), "quantize");
+    return launch_err(launch_quantize(X, nullptr, &xp, M, K, (hipStream_t)stream), "quantize");
 }
 
 int iq4xs_gemm_act(const void *W, const void *act, float *Y, int64_t M, int64_t N, int64_t K,
@@ -796,7 +782,7 @@ int iq4xs_gemm_group(const void *const *W, float *const *Y, const int64_t *N, in
             zl.n[g] = M * N[g];
         }
     }
-    if ((st = launch_err(launch_quantize(X, nullptr, &xp, nullptr, M, K, s, zl), "quantize")) != IQ4XS_OK)
+    if ((st = launch_err(launch_quantize(X, nullptr, &xp, M, K, s, zl), "quantize")) != IQ4XS_OK)
         return st;
     return launch_err(launch_mmv_group(mmv_group(W, Y, N, G), xp, p, s), "MMQ group");
 }

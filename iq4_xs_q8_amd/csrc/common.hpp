@@ -330,15 +330,12 @@ struct ZeroList {
 // quantizers also zero yz[0..nz) when yz is given (the output of a matmul
 // that adds partial tiles into it).
 // xs (optional) receives the compensated bf16 planes.
-hipError_t launch_quantize(const float *X, void *Xq, const XPlanes *planes, uint16_t *Xbf,
-                           int64_t M, int64_t K, hipStream_t s, float *yz = nullptr, int64_t nz = 0,
-                           const XSplit *xs = nullptr);
-hipError_t launch_quantize(const float *X, void *Xq, const XPlanes *planes, uint16_t *Xbf,
-                           int64_t M, int64_t K, hipStream_t s, const ZeroList &zl,
-                           const XSplit *xs = nullptr);
-hipError_t launch_q8_1_convert(const void *Xq, const XPlanes *planes, uint16_t *Xbf, int64_t M,
-                              int64_t K, hipStream_t s, float *yz = nullptr, int64_t nz = 0,
-                              const XSplit *xs = nullptr);
+hipError_t launch_quantize(const float *X, void *Xq, const XPlanes *planes, int64_t M, int64_t K, hipStream_t s,
+                           float *yz = nullptr, int64_t nz = 0, const XSplit *xs = nullptr);
+hipError_t launch_quantize(const float *X, void *Xq, const XPlanes *planes, int64_t M, int64_t K, hipStream_t s,
+                           const ZeroList &zl, const XSplit *xs = nullptr);
+hipError_t launch_q8_1_convert(const void *Xq, const XPlanes *planes, int64_t M, int64_t K, hipStream_t s,
+                              float *yz = nullptr, int64_t nz = 0, const XSplit *xs = nullptr);
 hipError_t launch_zero(float *y, int64_t n, hipStream_t s);
 hipError_t launch_gemv(const void *W, const XPlanes &x, float *Y, int64_t N, hipStream_t s,
                        int fmt = FMT_IQ4_XS);
@@ -392,13 +389,12 @@ MmqPlan mmq_plan(int64_t M, int64_t N, int64_t K, int fmt = FMT_IQ4_XS);
 hipError_t launch_mmq(const void *W, const XPlanes &x, float *Y, int64_t N, void *workspace,
                       bool y_zeroed, hipStream_t s, int fmt = FMT_IQ4_XS);
 hipError_t launch_dequant_bf16(const void *W, uint16_t *Wb, int64_t N, int64_t K, hipStream_t s);
-hipError_t launch_gemm_bf16(const uint16_t *Xb, const uint16_t *Wb, float *Y, int64_t M,
-                            int64_t N, int64_t K, hipStream_t s);
-
 // Fused dequantize-in-LDS GEMM (fused.hip): Xs as XSplit with Ms = fused_ms(M).
 int64_t fused_grid(int64_t M, int64_t N);
+// lo: the compensated formulation (hi and lo parts, three products); else
+// the plain bf16 one (hi parts only, one product).
 hipError_t launch_fused_x3(const void *W, const uint16_t *Xs, float *Y, int64_t M, int64_t N, int64_t K,
-                           hipStream_t s);
+                           hipStream_t s, bool lo = true);
 
 constexpr int GEMV_MAX_M = 4;
 

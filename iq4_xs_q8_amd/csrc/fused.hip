@@ -115,6 +115,27 @@ __device__ __forceinline__ void expand8_x3(uint32_t qa, uint32_t qb, float sw, f
     *reinterpret_cast<u32x4 *>(dst + 32) = u32x4{l0, l1, l2, l3};
 }
 
+// As expand8_x3 with the hi parts only (the plain bf16 formulation).
+__device__ __forceinline__ void expand8_hi(uint32_t qa, uint32_t qb, float sw, float c, uint16_t *dst)
+{
+    const uint32_t ua = lut4_biased(qa), ub = lut4_biased(qb);
+    const bf16x2_t h0 = {(__bf16)fmaf((float)(ua & 0xFFu), sw, c), (__bf16)fmaf((float)((ua >> 8) & 0xFFu), sw, c)};
+    const bf16x2_t h1 = {(__bf16)fmaf((float)((ua >> 16) & 0xFFu), sw, c), (__bf16)fmaf((float)(ua >> 24), sw, c)};
+    const bf16x2_t h2 = {(__bf16)fmaf((float)(ub & 0xFFu), sw, c), (__bf16)fmaf((float)((ub >> 8) & 0xFFu), sw, c)};
+    const bf16x2_t h3 = {(__bf16)fmaf((float)((ub >> 16) & 0xFFu), sw, c), (__bf16)fmaf((float)(ub >> 24), sw, c)};
+    *reinterpret_cast<u32x4 *>(dst) = u32x4{__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1),
+                                            __builtin_bit_cast(uint32_t, h2), __builtin_bit_cast(uint32_t, h3)};
+}
+
+template <bool LO>
+__device__ __forceinline__ void expand8(uint32_t qa, uint32_t qb, float sw, float c, uint16_t *dst)
+{
+    if constexpr (LO)
+        expand8_x3(qa, qb, sw, c, dst);
+    else
+        expand8_hi(qa, qb, sw, c, dst);
+}
+
 // A thread's share of its weight column for one sub-block: 16 index bytes
 // (or 8, with two threads per column) and the super-block header.
 struct WStage {
@@ -136,21 +157,21 @@ __device__ __forceinline__ void load_w(WStage &st, const char *__restrict__ wrow
 
 // Expands the thread's share of its column into the weight area of an LDS
 // stage: index bytes 8h..8h+7 hold elements 8h..8h+7 (low nibbles) and
-// 16+8h..16+8h+7 (high nibbles).
-template <class C>
+// 16+8h..16+8h+7 (high nibbles).  LO: also the lo parts.
+template <class C, bool LO>
 __device__ __forceinline__ void store_w(const WStage &st, uint16_t *__restrict__ lw, int s, int colidx, int part)
 {
     const float sw = sub_scale(st.hdr.x, st.hdr.y, s % SUBS);
     const float c = -128.0f * sw;
     uint16_t *col = lw + colidx * WROW;
     if constexpr (C::TPC == 1) {
-        expand8_x3(st.q0.x, st.q0.y, sw, c, col);
-        expand8_x3(st.q1.x, st.q1.y, sw, c, col + 8);
-        expand8_x3(st.q0.x >> 4, st.q0.y >> 4, sw, c, col + 16);
-        expand8_x3(st.q1.x >> 4, st.q1.y >> 4, sw, c, col + 24);
+        expand8<LO>(st.q0.x, st.q0.y, sw, c, col);
+        expand8<LO>(st.q1.x, st.q1.y, sw, c, col + 8);
+        expand8<LO>(st.q0.x >> 4, st.q0.y >> 4, sw, c, col + 16);
+        expand8<LO>(st.q1.x >> 4, st.q1.y >> 4, sw, c, col + 24);
     } else {
-        expand8_x3(st.q0.x, st.q0.y, sw, c, col + 8 * part);
-        expand8_x3(st.q0.x >> 4, st.q0.y >> 4, sw, c, col + 16 + 8 * part);
+        expand8<LO>(st.q0.x, st.q0.y, sw, c, col + 8 * part);
+        expand8<LO>(st.q0.x >> 4, st.q0.y >> 4, sw, c, col + 16 + 8 * part);
     }
 }
 
@@ -192,7 +213,7 @@ struct Ctx {
 // The MFMAs of one sub-block from an LDS stage: per 16-wide k half, the
 // wavefront's TN weight operands (hi, lo) and TM activation operands (hi, lo),
 // three products per tile.
-template <class C>
+template <class C, bool LO>
 __device__ __forceinline__ void mfmas(v16f (&acc)[C::TM][C::TN], const char *cur, const Ctx &cx)
 {
     const char *lx = cur + cx.lx_off;
@@ -204,23 +225,26 @@ __device__ __forceinline__ void mfmas(v16f (&acc)[C::TM][C::TN], const char *cur
 #pragma unroll
         for (int j = 0; j < C::TN; j++) {
             bh[j] = lds_bf8(lw + 64 * j * WROW + 32 * c);
-            bl[j] = lds_bf8(lw + 64 * j * WROW + 32 * c + 64);
+            if constexpr (LO)
+                bl[j] = lds_bf8(lw + 64 * j * WROW + 32 * c + 64);
         }
 #pragma unroll
         for (int i = 0; i < C::TM; i++) {
             // hi piece 2c+h and lo piece 4+2c+h of row 32i + col (swz of the
             // row is swz(col): the tile offsets are multiples of 32)
             const v8bf ah = lds_bf8(lx + 32 * i * 128 + 16 * ((2 * c + h) ^ sw));
-            const v8bf al = lds_bf8(lx + 32 * i * 128 + 16 * ((4 + 2 * c + h) ^ sw));
 #pragma unroll
             for (int j = 0; j < C::TN; j++)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh[j], acc[i][j], 0, 0, 0);
+            if constexpr (LO) {
+                const v8bf al = lds_bf8(lx + 32 * i * 128 + 16 * ((4 + 2 * c + h) ^ sw));
 #pragma unroll
-            for (int j = 0; j < C::TN; j++)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl[j], acc[i][j], 0, 0, 0);
+                for (int j = 0; j < C::TN; j++)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl[j], acc[i][j], 0, 0, 0);
 #pragma unroll
-            for (int j = 0; j < C::TN; j++)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh[j], acc[i][j], 0, 0, 0);
+                for (int j = 0; j < C::TN; j++)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh[j], acc[i][j], 0, 0, 0);
+            }
         }
     }
 }
@@ -231,7 +255,7 @@ __device__ __forceinline__ void mfmas(v16f (&acc)[C::TM][C::TN], const char *cur
 // weights of sub-block s+1 (`ready`, loaded one step earlier) are expanded
 // into `nxt` (the compiler interleaves the two).  Indices past the last
 // sub-block are clamped: what they load and expand is never read.
-template <class C>
+template <class C, bool LO>
 __device__ __forceinline__ void step(v16f (&acc)[C::TM][C::TN], const char *cur, char *nxt, const WStage &ready,
                                      WStage &loading, int s, const Ctx &cx)
 {
@@ -239,8 +263,8 @@ __device__ __forceinline__ void step(v16f (&acc)[C::TM][C::TN], const char *cur,
     const int s2 = s + 2 < cx.S ? s + 2 : cx.S - 1;
     load_x<C>(cx.xr, nxt, cx.x0 + (uint32_t)s1 * cx.xstep, cx.wave, cx.lane);
     load_w<C>(loading, cx.wrow, s2, cx.part);
-    mfmas<C>(acc, cur, cx);
-    store_w<C>(ready, reinterpret_cast<uint16_t *>(nxt + C::XBYTES), s1, cx.colidx, cx.part);
+    mfmas<C, LO>(acc, cur, cx);
+    store_w<C, LO>(ready, reinterpret_cast<uint16_t *>(nxt + C::XBYTES), s1, cx.colidx, cx.part);
     // this wavefront's activation loads and LDS writes are done (and its
     // weight loads, issued at the same time); the barrier makes them everyone's
     __builtin_amdgcn_s_waitcnt(stream::wait_vm_lds(0));
@@ -250,7 +274,7 @@ __device__ __forceinline__ void step(v16f (&acc)[C::TM][C::TN], const char *cur,
 // Xs: the quantizer's hi/lo planes, [K/32][Ms][64] bf16 (Ms = M rounded up to
 // FUSED_ROWS; rows M..Ms-1 are zero), fewer than 2^31 bytes.  W: [N][K/256]
 // IQ4_XS super-blocks.
-template <class C>
+template <class C, bool LO>
 __global__ void __launch_bounds__(C::NT, 1)
 k_gemm_x3(const char *__restrict__ W, const uint16_t *__restrict__ Xs, float *__restrict__ Y, int64_t M,
           int64_t N, int64_t K, int64_t Ms)
@@ -294,14 +318,14 @@ k_gemm_x3(const char *__restrict__ W, const uint16_t *__restrict__ Xs, float *__
     WStage wa, wb;
     load_x<C>(cx.xr, lds, cx.x0, cx.wave, cx.lane);
     load_w<C>(wa, cx.wrow, 0, cx.part);
-    store_w<C>(wa, reinterpret_cast<uint16_t *>(lds + C::XBYTES), 0, cx.colidx, cx.part);
+    store_w<C, LO>(wa, reinterpret_cast<uint16_t *>(lds + C::XBYTES), 0, cx.colidx, cx.part);
     load_w<C>(wa, cx.wrow, 1, cx.part);
     __builtin_amdgcn_s_waitcnt(stream::wait_vm_lds(0));
     stream::raw_barrier();
     // two steps per trip, so that the two LDS stages are fixed offsets
     for (int s = 0; s < cx.S; s += 2) {
-        step<C>(acc, lds, lds + C::STAGE, wa, wb, s, cx);
-        step<C>(acc, lds + C::STAGE, lds, wb, wa, s + 1, cx);
+        step<C, LO>(acc, lds, lds + C::STAGE, wa, wb, s, cx);
+        step<C, LO>(acc, lds + C::STAGE, lds, wb, wa, s + 1, cx);
     }
 
     // lane (col, h) of tile (i, j) holds Y[m][n] for n = its column and
@@ -348,15 +372,25 @@ int64_t fused_grid(int64_t M, int64_t N)
 }
 
 hipError_t launch_fused_x3(const void *W, const uint16_t *Xs, float *Y, int64_t M, int64_t N, int64_t K,
-                           hipStream_t s)
+                           hipStream_t s, bool lo)
 {
     const int64_t Ms = fused_ms(M);
-    if (x3_config() == 0)
-        hipLaunchKernelGGL(k_gemm_x3<X3Big>, dim3((unsigned)grid_of<X3Big>(M, N)), dim3(X3Big::NT), 0, s,
-                           (const char *)W, Xs, Y, M, N, K, Ms);
-    else
-        hipLaunchKernelGGL(k_gemm_x3<X3Pair>, dim3((unsigned)grid_of<X3Pair>(M, N)), dim3(X3Pair::NT), 0, s,
-                           (const char *)W, Xs, Y, M, N, K, Ms);
+    const char *w = (const char *)W;
+    if (x3_config() == 0) {
+        if (lo)
+            hipLaunchKernelGGL((k_gemm_x3<X3Big, true>), dim3((unsigned)grid_of<X3Big>(M, N)), dim3(X3Big::NT), 0,
+                               s, w, Xs, Y, M, N, K, Ms);
+        else
+            hipLaunchKernelGGL((k_gemm_x3<X3Big, false>), dim3((unsigned)grid_of<X3Big>(M, N)), dim3(X3Big::NT), 0,
+                               s, w, Xs, Y, M, N, K, Ms);
+    } else {
+        if (lo)
+            hipLaunchKernelGGL((k_gemm_x3<X3Pair, true>), dim3((unsigned)grid_of<X3Pair>(M, N)), dim3(X3Pair::NT),
+                               0, s, w, Xs, Y, M, N, K, Ms);
+        else
+            hipLaunchKernelGGL((k_gemm_x3<X3Pair, false>), dim3((unsigned)grid_of<X3Pair>(M, N)), dim3(X3Pair::NT),
+                               0, s, w, Xs, Y, M, N, K, Ms);
+    }
     return hipGetLastError();
 }
 

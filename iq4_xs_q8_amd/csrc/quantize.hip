@@ -18,13 +18,6 @@
 namespace iq4xs {
 namespace {
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
-{
-    // finite inputs only (the activations here are exact fp32 products)
-    const uint32_t u = __builtin_bit_cast(uint32_t, f);
-    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-}
-
 __device__ __forceinline__ uint32_t pack_q(int q0, int q1, int q2, int q3)
 {
     return (uint32_t)(uint8_t)q0 | ((uint32_t)(uint8_t)q1 << 8) | ((uint32_t)(uint8_t)q2 << 16) |
@@ -96,7 +89,7 @@ __device__ __forceinline__ int quant1(float x, float d)
 // descriptors that stop at row M.
 __global__ void __launch_bounds__(256)
 k_quantize(const float *__restrict__ X, uint8_t *__restrict__ Xq, int8_t *__restrict__ qp,
-           float *__restrict__ dp, ZeroList zl, uint16_t *__restrict__ Xbf, XSplit xs,
+           float *__restrict__ dp, ZeroList zl, XSplit xs,
            int64_t M, int64_t Mrows, int64_t Mp, int64_t K)
 {
     const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -141,19 +134,14 @@ k_quantize(const float *__restrict__ X, uint8_t *__restrict__ Xq, int8_t *__rest
         if (t == 0)
             dp[b * Mp + m] = dst;
     }
-    if (Xbf != nullptr && m < M) {
-        const uint32_t lo = f32_to_bf16_rne(dst * (float)q0) | ((uint32_t)f32_to_bf16_rne(dst * (float)q1) << 16);
-        const uint32_t hi = f32_to_bf16_rne(dst * (float)q2) | ((uint32_t)f32_to_bf16_rne(dst * (float)q3) << 16);
-        *reinterpret_cast<uint2 *>(Xbf + m * K + b * SB + 4 * t) = make_uint2(lo, hi);
-    }
     write_split(xs, m, b, t, dst, q0, q1, q2, q3);
 }
 
-// ABI Q8_1 blocks -> internal planes and/or bf16 X~.  Same grid shape as
-// k_quantize.
+// ABI Q8_1 blocks -> internal planes and/or the compensated bf16 planes.
+// Same grid shape as k_quantize.
 __global__ void __launch_bounds__(256)
 k_q8_1_convert(const uint8_t *__restrict__ Xq, int8_t *__restrict__ qp, float *__restrict__ dp,
-               ZeroList zl, uint16_t *__restrict__ Xbf, XSplit xs, int64_t M, int64_t Mrows,
+               ZeroList zl, XSplit xs, int64_t M, int64_t Mrows,
                int64_t Mp, int64_t K)
 {
     const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -176,13 +164,6 @@ k_q8_1_convert(const uint8_t *__restrict__ Xq, int8_t *__restrict__ qp, float *_
         if (t == 0)
             dp[b * Mp + m] = dst;
     }
-    if (Xbf != nullptr && m < M) {
-        const int q0 = (int8_t)(qword & 0xFF), q1 = (int8_t)((qword >> 8) & 0xFF);
-        const int q2 = (int8_t)((qword >> 16) & 0xFF), q3 = (int8_t)(qword >> 24);
-        const uint32_t lo = f32_to_bf16_rne(dst * (float)q0) | ((uint32_t)f32_to_bf16_rne(dst * (float)q1) << 16);
-        const uint32_t hi = f32_to_bf16_rne(dst * (float)q2) | ((uint32_t)f32_to_bf16_rne(dst * (float)q3) << 16);
-        *reinterpret_cast<uint2 *>(Xbf + m * K + b * SB + 4 * t) = make_uint2(lo, hi);
-    }
     write_split(xs, m, b, t, dst, (int8_t)(qword & 0xFF), (int8_t)((qword >> 8) & 0xFF),
                 (int8_t)((qword >> 16) & 0xFF), (int8_t)(qword >> 24));
 }
@@ -199,21 +180,21 @@ hipError_t launch_zero(float *y, int64_t n, hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t launch_quantize(const float *X, void *Xq, const XPlanes *planes, uint16_t *Xbf,
-                           int64_t M, int64_t K, hipStream_t s, const ZeroList &zl, const XSplit *xs)
+hipError_t launch_quantize(const float *X, void *Xq, const XPlanes *planes, int64_t M, int64_t K, hipStream_t s,
+                           const ZeroList &zl, const XSplit *xs)
 {
     const int64_t Mrows = xs ? xs->Ms : M;
     const int64_t threads = Mrows * (K / 4);
     const int64_t grid = (threads + 255) / 256;
     hipLaunchKernelGGL(k_quantize, dim3((unsigned)grid), dim3(256), 0, s, X, (uint8_t *)Xq,
                        planes ? planes->qp : nullptr, planes ? planes->dp : nullptr,
-                       zl, Xbf, xs ? *xs : XSplit(), M, Mrows,
+                       zl, xs ? *xs : XSplit(), M, Mrows,
                        planes ? planes->Mp : M, K);
     return hipGetLastError();
 }
 
-hipError_t launch_quantize(const float *X, void *Xq, const XPlanes *planes, uint16_t *Xbf,
-                           int64_t M, int64_t K, hipStream_t s, float *yz, int64_t nz, const XSplit *xs)
+hipError_t launch_quantize(const float *X, void *Xq, const XPlanes *planes, int64_t M, int64_t K, hipStream_t s,
+                           float *yz, int64_t nz, const XSplit *xs)
 {
     ZeroList zl;
     if (yz != nullptr && nz > 0) {
@@ -221,11 +202,11 @@ hipError_t launch_quantize(const float *X, void *Xq, const XPlanes *planes, uint
         zl.n[0] = nz;
         zl.count = 1;
     }
-    return launch_quantize(X, Xq, planes, Xbf, M, K, s, zl, xs);
+    return launch_quantize(X, Xq, planes, M, K, s, zl, xs);
 }
 
-hipError_t launch_q8_1_convert(const void *Xq, const XPlanes *planes, uint16_t *Xbf, int64_t M,
-                              int64_t K, hipStream_t s, float *yz, int64_t nz, const XSplit *xs)
+hipError_t launch_q8_1_convert(const void *Xq, const XPlanes *planes, int64_t M, int64_t K, hipStream_t s,
+                              float *yz, int64_t nz, const XSplit *xs)
 {
     const int64_t Mrows = xs ? xs->Ms : M;
     const int64_t threads = Mrows * (K / 4);
@@ -238,7 +219,7 @@ hipError_t launch_q8_1_convert(const void *Xq, const XPlanes *planes, uint16_t *
     }
     hipLaunchKernelGGL(k_q8_1_convert, dim3((unsigned)grid), dim3(256), 0, s, (const uint8_t *)Xq,
                        planes ? planes->qp : nullptr, planes ? planes->dp : nullptr,
-                       zl, Xbf, xs ? *xs : XSplit(), M, Mrows,
+                       zl, xs ? *xs : XSplit(), M, Mrows,
                        planes ? planes->Mp : M, K);
     return hipGetLastError();
 }

@@ -131,8 +131,9 @@ def test_workspace_query_and_checks():
         assert L.iq4xs_gemm_workspace_bytes(4, 1024, 2048, path, ctypes.byref(size)) == iq.OK
         ref[path] = size.value
         assert size.value > 0
-    # the bf16 path holds the dequantized weights; the integer paths the Q8_1 planes
-    assert ref[iq.PATH_DEQ_BF16] >= 1024 * 2048 * 2
+    # the bf16 path holds the hi/lo bf16 activation planes of 256 padded rows (no
+    # weight copy: it dequantizes inside the GEMM); the integer paths the Q8_1 planes
+    assert ref[iq.PATH_DEQ_BF16] == (2048 // 32) * 256 * 128
     assert ref[iq.PATH_GEMV] >= 4 * 2048 * 1.125
     assert L.iq4xs_gemm_workspace_bytes(4, 1024, 2048, iq.PATH_AUTO, ctypes.byref(size)) == iq.OK
     assert size.value == ref[iq.dispatch(4, 1024, 2048)]
@@ -371,8 +372,9 @@ def test_noalloc_rejects_shapes_beyond_the_static_scratch():
     far = 1 << 44                     # fake addresses far apart: no overlap
     assert L.iq4xs_gemm_noalloc(A, far, 2 * far, 4096, 8, 17408, iq.PATH_MMQ, None) == iq.EINVAL
     assert b"static scratch" in L.iq4xs_last_error()
-    # the bf16 path's operands at 100000 x 5120
-    assert L.iq4xs_gemm_noalloc(A, far, 2 * far, 64, 100000, 5120, iq.PATH_DEQ_BF16, None) == iq.EINVAL
+    # the bf16 paths' activation planes at 4096 x 17408: 285 MB
+    for p in (iq.PATH_DEQ_BF16, iq.PATH_BF16X3):
+        assert L.iq4xs_gemm_noalloc(A, far, 2 * far, 4096, 8, 17408, p, None) == iq.EINVAL
     assert b"static scratch" in L.iq4xs_last_error()
     # argument checks as iq4xs_gemm_path
     assert L.iq4xs_gemm_noalloc(None, A * 2, A * 4, 4, 8, 256, 0, None) == iq.EINVAL
