@@ -32,8 +32,8 @@ Printed: one JSON line with
                int8 and bf16 matrix-core instructions
   group        one X against a pair of decode-shape matrices: grouped call vs two calls
   formats      a few points with IQ4_NL and Q4_0 weights
-  fused_bf16x3 the fused compensated-bf16 path at every prefill point, beside
-               the path the table picks there
+  fused_bf16x3 the fused bf16 paths (BF16X3, and DEQ_BF16) at every prefill
+               point, beside the path the table picks there
   cpu_baseline the CPU oracle (never tuned) on a bounded column sample of the
                same 52 points, in the same unit.
 `--sweep FILE` times every (shape, M, path) point and writes one JSON object
@@ -424,10 +424,11 @@ def dominant_rooflines(recs):
 
 
 def fused_points(recs, reps=10):
-    """The fused compensated-bf16 path (BF16X3) at every prefill point, per
-    call (quantization included, graph replay) beside the point's own path.
-    Work: three bf16 products per weight x activation, 6*M*N*K flops against
-    the bf16 MFMA peak."""
+    """The fused bf16 paths at every prefill point, per call (quantization
+    included, graph replay) beside the point's own path: BF16X3 (compensated,
+    within the per-row bound; three bf16 products per term, 6*M*N*K flops)
+    and DEQ_BF16 (the plain bf16 formulation, one product, 2*M*N*K flops),
+    against the bf16 MFMA peak."""
     by = {(r["N"], r["K"], r["M"]): r for r in recs}
     out = []
     for (N, K) in synth.PREFILL.shapes:
@@ -435,10 +436,13 @@ def fused_points(recs, reps=10):
         for M in synth.PREFILL.ms:
             X = torch.from_numpy(synth.PREFILL.x(M, K, N=N)).cuda()
             t_call, _, _ = measure_point(rot, X, N, K, iq.PATH_BF16X3, reps=reps)
+            t_plain, _, _ = measure_point(rot, X, N, K, iq.PATH_DEQ_BF16, reps=reps)
             flops = 6.0 * M * N * K
             ent = {"N": N, "K": K, "M": M, "ms": t_call, "bf16_TFLOPs": flops / (t_call * 1e-3) / 1e12,
                    "bf16_frac": flops / (t_call * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-                   "int8_equiv_TOPS": 2.0 * M * N * K / (t_call * 1e-3) / 1e12}
+                   "int8_equiv_TOPS": 2.0 * M * N * K / (t_call * 1e-3) / 1e12,
+                   "deq_bf16_ms": t_plain,
+                   "deq_bf16_TFLOPs": 2.0 * M * N * K / (t_plain * 1e-3) / 1e12}
             if (N, K, M) in by:
                 ent["auto_ms"] = by[(N, K, M)]["ms"]
                 ent["auto_path"] = by[(N, K, M)]["path"]
