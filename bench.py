@@ -855,15 +855,17 @@ def summarize_sq(dirs, trace_dirs, out, cmds, specs=""):
     instruction; and, with kernel traces of the same launches, the share of
     the kernel's duration that VALU issue (instructions x 4 cycles, spread
     over 1024 SIMDs at 2.4 GHz) and the matrix cores (busy cycles over 1024
-    SIMDs) take."""
-    shapes = [tuple(int(v) for v in sp.split("x")) for sp in specs.split(",")] if specs else []
+    SIMDs) take; and the same two shares at the clock the run implies
+    (SQ_BUSY_CYCLES counted once per shader engine, 32 of them), with their
+    sum: near 1 when VALU and matrix-core issue do not overlap."""
+    shapes = [tuple(int(v) for v in sp.split(":")[0].split("x")) for sp in specs.split(",")] if specs else []
     per = {}
     for d in dirs:
         rows = _counter_rows(d)
         order = _tile_order(rows, "Dispatch_Id")
         for r in rows:
             name = r["Kernel_Name"]
-            if not any(k in name for k in ("k_mmv", "k_gemv", "k_mmqt", "k_mmq", "k_quantize")):
+            if not any(k in name for k in ("k_mmv", "k_gemv", "k_mmqt", "k_mmq", "k_quantize", "k_gemm_x3")):
                 continue
             key = _sq_key(name, order.get(int(r["Dispatch_Id"])), shapes)
             per.setdefault(key, {}).setdefault(r["Counter_Name"], {}).setdefault(r["Dispatch_Id"], 0.0)
@@ -881,7 +883,7 @@ def summarize_sq(dirs, trace_dirs, out, cmds, specs=""):
              "# VALU/MFMA: instructions; LDS-conflict: bank-conflict cycles per LDS instruction; VALU-issue and "
              "MFMA-busy: per SIMD, as a share of the kernel's average duration in the trace",
              "# kernel | " + " ".join(c for p_ in SQ_PASSES for c in p_) +
-             " | VALU/MFMA  LDS-conflict  trace-us  VALU-issue  MFMA-busy"]
+             " | VALU/MFMA  LDS-conflict  trace-us  VALU-issue  MFMA-busy | clock-GHz  VALU-issue  MFMA-busy  sum"]
     for key in sorted(per):
         v = {c: sum(d.values()) / len(d) for c, d in per[key].items()}
         vals = " ".join(f"{v.get(c, float('nan')):.4g}" for p_ in SQ_PASSES for c in p_)
@@ -890,8 +892,11 @@ def summarize_sq(dirs, trace_dirs, out, cmds, specs=""):
         d_us = sum(dur[key]) / len(dur[key]) if key in dur else float("nan")
         issue = valu * 4 / 1024 / 2.4e3 / d_us
         busy = v.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / 1024 / 2.4e3 / d_us
+        clk = v.get("SQ_BUSY_CYCLES", float("nan")) / 32 / d_us / 1e3      # GHz
+        issue_c, busy_c = issue * 2.4 / clk, busy * 2.4 / clk
         lines.append(f"{key} | {vals} | {valu / mfma if mfma else float('nan'):.2f}  "
-                     f"{conf / lds if lds else float('nan'):.3f}  {d_us:.2f}  {issue:.2f}  {busy:.2f}")
+                     f"{conf / lds if lds else float('nan'):.3f}  {d_us:.2f}  {issue:.2f}  {busy:.2f} | "
+                     f"{clk:.2f}  {issue_c:.2f}  {busy_c:.2f}  {issue_c + busy_c:.2f}")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
 
