@@ -368,9 +368,9 @@ int run_gemm(const void *W, const float *X, const void *Xq, float *Y, int64_t M,
                                     : launch_mmq(W, xp, Y, N, base + pbytes, zero, s, fmt);
         return launch_err(e, path_name(path));
     }
-    // BF16X3 and DEQ_BF16: the fused kernel, from the hi/lo activation planes
-    // (DEQ_BF16 uses the hi parts only: the plain bf16 formulation)
-    if (fused_grid(M, N) > INT32_MAX || fused_xs_bytes(M, K) >= (size_t)INT32_MAX)
+    // BF16X3 and DEQ_BF16: the fused kernels, from the hi/lo activation planes
+    // (DEQ_BF16 reads the hi parts only: the plain bf16 formulation)
+    if (std::max(fused_grid(M, N), deq_grid(M, N)) > INT32_MAX || fused_xs_bytes(M, K) >= (size_t)INT32_MAX)
         return fail(IQ4XS_EPATH, "the bf16 paths take fewer than 2^31 workgroups and activation planes "
                     "below 2 GiB (M=%lld N=%lld K=%lld)", (long long)M, (long long)N, (long long)K);
     XSplit xsp;
@@ -380,7 +380,9 @@ int run_gemm(const void *W, const float *X, const void *Xq, float *Y, int64_t M,
                            : launch_q8_1_convert(Xq, nullptr, M, K, s, nullptr, 0, &xsp);
     if ((st = launch_err(e, "quantize")) != IQ4XS_OK)
         return st;
-    return launch_err(launch_fused_x3(W, xsp.p, Y, M, N, K, s, path == IQ4XS_PATH_BF16X3), "gemm_x3");
+    if (path == IQ4XS_PATH_BF16X3)
+        return launch_err(launch_fused_x3(W, xsp.p, Y, M, N, K, s), "gemm_x3");
+    return launch_err(launch_fused_deq(W, xsp.p, Y, M, N, K, s), "gemm_deq");
 }
 
 }  // namespace

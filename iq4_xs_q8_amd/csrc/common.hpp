@@ -389,12 +389,15 @@ MmqPlan mmq_plan(int64_t M, int64_t N, int64_t K, int fmt = FMT_IQ4_XS);
 hipError_t launch_mmq(const void *W, const XPlanes &x, float *Y, int64_t N, void *workspace,
                       bool y_zeroed, hipStream_t s, int fmt = FMT_IQ4_XS);
 hipError_t launch_dequant_bf16(const void *W, uint16_t *Wb, int64_t N, int64_t K, hipStream_t s);
-// Fused dequantize-in-LDS GEMM (fused.hip): Xs as XSplit with Ms = fused_ms(M).
+// Fused dequantize-in-LDS GEMMs (fused.hip), from the hi/lo planes Xs (an
+// XSplit with Ms = fused_ms(M)): the compensated formulation (hi and lo parts,
+// three products) and the plain bf16 one (hi parts only, one product).
 int64_t fused_grid(int64_t M, int64_t N);
-// lo: the compensated formulation (hi and lo parts, three products); else
-// the plain bf16 one (hi parts only, one product).
 hipError_t launch_fused_x3(const void *W, const uint16_t *Xs, float *Y, int64_t M, int64_t N, int64_t K,
-                           hipStream_t s, bool lo = true);
+                           hipStream_t s);
+int64_t deq_grid(int64_t M, int64_t N);
+hipError_t launch_fused_deq(const void *W, const uint16_t *Xs, float *Y, int64_t M, int64_t N, int64_t K,
+                            hipStream_t s);
 
 constexpr int GEMV_MAX_M = 4;
 
