@@ -80,7 +80,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_mmv_decode_n10240_k5120_traffic
 TILE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_mmqt_tile_shapes_traffic.txt")
 KERNEL_SOURCES = {"k_mmv": ["mmv.hip", "common.hpp", "stream.hpp"], "k_gemv": ["gemv.hip", "common.hpp"],
                   "k_mmq": ["mmq.hip", "common.hpp"], "k_mmqt": ["mmqt.hip", "common.hpp", "stream.hpp"],
-                  "k_gemm_x3": ["fused.hip", "common.hpp", "stream.hpp"]}
+                  "k_gemm_x3": ["fused.hip", "common.hpp", "stream.hpp"],
+                  "k_gemm_deq": ["fused.hip", "common.hpp", "stream.hpp"]}
 # Exact formulation on the matrix cores: per (output, 32-wide sub-block) the
 # int8 MFMA does 32 MACs (0.031 cycles per SIMD at 2048 ops/cycle) and the
 # fp32 rescale three VALU instructions (0.1875 cycles at 16 lanes/cycle,
@@ -94,8 +95,10 @@ def kernel_name(M, N, K, path):
     rocprofv3 trace)."""
     if path == iq.PATH_GEMV:
         return "k_gemv"
-    if path in (iq.PATH_DEQ_BF16, iq.PATH_BF16X3):
+    if path == iq.PATH_BF16X3:
         return "k_gemm_x3"
+    if path == iq.PATH_DEQ_BF16:
+        return "k_gemm_deq"
     nb = K // 256
     if M <= 32 and nb % 2 == 0 and N * nb * 136 < (1 << 31):
         return "k_mmv"
@@ -528,7 +531,7 @@ def check_trace(trace_dir, out, cmd):
         elif cur is not None:
             cur.append((k, (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3))
     pts = sweep_points()
-    families = {"GEMV": {"k_gemv"}, "MMQ": {"k_mmv", "k_mmqt", "k_mmq"}, "DEQ_BF16": {"k_gemm_x3"},
+    families = {"GEMV": {"k_gemv"}, "MMQ": {"k_mmv", "k_mmqt", "k_mmq"}, "DEQ_BF16": {"k_gemm_deq"},
                 "BF16X3": {"k_gemm_x3"}}
     lines = ["# kernels launched per call, from a rocprofv3 kernel trace of bench.py --profile-points",
              f"# command: {cmd}",
@@ -543,7 +546,7 @@ def check_trace(trace_dir, out, cmd):
         path = iq.path_name(iq.dispatch(M, N, K))
         expect = kernel_name(M, N, K, iq.PATHS[path])
         per_call = names[:len(names) // 2]
-        mat = [k for k in per_call if k.startswith(("k_gemv", "k_mmv", "k_mmqt", "k_mmq", "k_gemm_x3"))]
+        mat = [k for k in per_call if k.startswith(("k_gemv", "k_mmv", "k_mmqt", "k_mmq", "k_gemm_x3", "k_gemm_deq"))]
         ok = (len(names) % 2 == 0 and names[:len(names) // 2] == names[len(names) // 2:] and
               per_call[0] == "k_quantize" and mat and mat[0] == expect and mat[0] in families[path])
         bad += not ok
@@ -698,19 +701,23 @@ def summarize_pmc(fetch_dir, write_dir, out, cmd_fetch, cmd_write):
 
 
 def summarize_fused(trace_dir, fetch_dir, write_dir, out, cmds, spec):
-    """One shape of a --profile-shapes run with the BF16X3 path forced
-    ("MxNxK:BF16X3"): the fused kernel's and the quantizer's durations from
-    the kernel trace, the fused kernel's HBM bytes per launch from the
-    counter runs (calibrated by their probes), its algorithmic bytes and its
-    bf16 rate (three products per term, 6*M*N*K flops) at the trace's
-    average duration."""
-    M, N, K = (int(v) for v in spec.split(":")[0].split("x"))
+    """One shape of a --profile-shapes run with a fused bf16 path forced
+    ("MxNxK:BF16X3" or "MxNxK:DEQ_BF16"): the fused kernel's and the
+    quantizer's durations from the kernel trace, the fused kernel's HBM bytes
+    per launch from the counter runs (calibrated by their probes), its
+    algorithmic bytes and its bf16 rate at the trace's average duration
+    (BF16X3: three products per term, 6*M*N*K flops, both activation planes
+    read; DEQ_BF16: one product, 2*M*N*K, the hi plane)."""
+    shape, _, pname = spec.partition(":")
+    M, N, K = (int(v) for v in shape.split("x"))
+    x3 = pname != "DEQ_BF16"
+    kern = "k_gemm_x3" if x3 else "k_gemm_deq"
     files = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
     if not files:
         raise SystemExit(f"no kernel_trace.csv under {trace_dir}")
     durs = {}
     for r in csv.DictReader(open(files[0])):
-        for k in ("k_gemm_x3", "k_quantize"):
+        for k in (kern, "k_quantize"):
             if k in r["Kernel_Name"]:
                 durs.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
     fr, wr = _counter_rows(fetch_dir), _counter_rows(write_dir)
@@ -719,30 +726,32 @@ def summarize_fused(trace_dir, fetch_dir, write_dir, out, cmds, spec):
     def per_launch(rows, counter):
         acc = {}
         for r in rows:
-            if r["Counter_Name"] == counter and "k_gemm_x3" in r["Kernel_Name"]:
+            if r["Counter_Name"] == counter and kern in r["Kernel_Name"]:
                 acc[r["Dispatch_Id"]] = acc.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
         return sum(acc.values()) / len(acc) if acc else float("nan")
     f_kib, w_kib = per_launch(fr, "FETCH_SIZE"), per_launch(wr, "WRITE_SIZE")
     traffic = f_kib * 1024.0 * f_scale + w_kib * 1024.0 * w_scale
     ms_rows = -(-M // 256) * 256
-    algo = 0.53125 * N * K + 4.0 * ms_rows * K + 4.0 * M * N
-    x3 = durs.get("k_gemm_x3", [float("nan")])
-    avg = sum(x3) / len(x3)
-    lines = [f"# fused compensated-bf16 kernel (BF16X3 path), M={M} N={N} K={K}: kernel trace and HBM counters "
-             "(20 whole calls, rotated weights)",
+    act = 4.0 if x3 else 2.0
+    algo = 0.53125 * N * K + act * ms_rows * K + 4.0 * M * N
+    flops = (6.0 if x3 else 2.0) * M * N * K
+    d = durs.get(kern, [float("nan")])
+    avg = sum(d) / len(d)
+    title = "compensated-bf16 kernel (BF16X3 path)" if x3 else "plain bf16 kernel (DEQ_BF16 path)"
+    lines = [f"# fused {title}, M={M} N={N} K={K}: kernel trace and HBM counters (20 whole calls, rotated weights)",
              *[f"# command: {c}" for c in cmds],
-             f"source_hash k_gemm_x3 {source_hash('k_gemm_x3')}",
+             f"source_hash {kern} {source_hash(kern)}",
              f"# calibration by the runs' own probes ({PROBE_BYTES} bytes read / written): fetch x{f_scale:.4f}, "
              f"write x{w_scale:.4f}",
              "# kernel  calls  avg_us  min_us  max_us"]
     for k, v in sorted(durs.items()):
         lines.append(f"{k} {len(v)} {sum(v) / len(v):.2f} {min(v):.2f} {max(v):.2f}")
-    lines += [f"k_gemm_x3 fetch_kib {f_kib:.1f} write_kib {w_kib:.1f} traffic_bytes_per_launch {traffic:.0f}",
-              f"k_gemm_x3 algorithmic_bytes_per_launch {algo:.0f} (weights 0.53125/weight, compensated activation "
-              "planes 4 B per element of the padded rows, Y)",
-              f"k_gemm_x3 traffic/algorithmic {traffic / algo:.2f}",
-              f"k_gemm_x3 bf16 TFLOP/s at avg {6.0 * M * N * K / (avg * 1e-6) / 1e12:.0f} "
-              f"({6.0 * M * N * K / (avg * 1e-6) / 1e12 / BF16_PEAK_TFLOPS * 100:.1f}% of 2.5 PFLOP/s)"]
+    lines += [f"{kern} fetch_kib {f_kib:.1f} write_kib {w_kib:.1f} traffic_bytes_per_launch {traffic:.0f}",
+              f"{kern} algorithmic_bytes_per_launch {algo:.0f} (weights 0.53125/weight, activation planes "
+              f"{act:.0f} B per element of the padded rows, Y)",
+              f"{kern} traffic/algorithmic {traffic / algo:.2f}",
+              f"{kern} bf16 TFLOP/s at avg {flops / (avg * 1e-6) / 1e12:.0f} "
+              f"({flops / (avg * 1e-6) / 1e12 / BF16_PEAK_TFLOPS * 100:.1f}% of 2.5 PFLOP/s)"]
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -865,7 +874,8 @@ def summarize_sq(dirs, trace_dirs, out, cmds, specs=""):
         order = _tile_order(rows, "Dispatch_Id")
         for r in rows:
             name = r["Kernel_Name"]
-            if not any(k in name for k in ("k_mmv", "k_gemv", "k_mmqt", "k_mmq", "k_quantize", "k_gemm_x3")):
+            if not any(k in name for k in ("k_mmv", "k_gemv", "k_mmqt", "k_mmq", "k_quantize", "k_gemm_x3",
+                                           "k_gemm_deq")):
                 continue
             key = _sq_key(name, order.get(int(r["Dispatch_Id"])), shapes)
             per.setdefault(key, {}).setdefault(r["Counter_Name"], {}).setdefault(r["Dispatch_Id"], 0.0)
