@@ -4,8 +4,11 @@
 // Arithmetic (batched IQ4_XS kernel section of the "V100TPS engine log",
 // agent-report.daedalus.work/V100TPS/engine.html): per 32-element sub-block
 // the exact integer dot of the int8 codebook values with the int8
-// activations (two chained v_mfma_i32_32x32x32_i8, one per part of the split
-// codebook), then y += d_w*(ls-32) * d_x * dot in fp32.
+// activations (one v_mfma_i32_32x32x32_i8 over the full 16-entry lookup),
+// then y += d_w*(ls-32) * d_x * dot in fp32.  (The split codebook of the
+// streaming kernel would save lookup work for a second MFMA; here the VALU
+// and matrix-core work of a SIMD add up rather than overlap, and the single
+// MFMA measured faster.)
 //
 // Work split:
 //  * Output tiles are 128 activation rows (4 MFMA subtiles) x 128 weight rows
@@ -292,15 +295,13 @@ k_mmqt(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__re
             }
 #pragma unroll
             for (int u = 0; u < 2; u++) {
-                uint32_t wa[4], wb4[4];
-                expand8_split<C::F>(q[u].x, q[u].y, wa, wb4);
-                const v4i ba = {(int)wa[0], (int)wa[1], (int)wa[2], (int)wa[3]};
-                const v4i bb = {(int)wb4[0], (int)wb4[1], (int)wb4[2], (int)wb4[3]};
+                uint32_t wf[4];
+                expand8<C::F>(q[u].x, q[u].y, wf);
+                const v4i bf = {(int)wf[0], (int)wf[1], (int)wf[2], (int)wf[3]};
 #pragma unroll
                 for (int i = 0; i < 2; i++) {
                     const v16i zero = {0};
-                    D[u][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
-                        ax[u][i], bb, __builtin_amdgcn_mfma_i32_32x32x32_i8(ax[u][i], ba, zero, 0, 0, 0), 0, 0, 0);
+                    D[u][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ax[u][i], bf, zero, 0, 0, 0);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
