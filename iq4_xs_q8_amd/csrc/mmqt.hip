@@ -56,14 +56,17 @@ constexpr int TILE = 32;
 constexpr int NWQ = 8, NTQ = 64 * NWQ;     // wavefronts, threads per workgroup
 constexpr int HALF = SUBS / 2;             // sub-blocks per step
 constexpr int WROWQ = 80;                  // LDS weight row: header, 8 unused, 64 index bytes
-constexpr int NBUFQ = 5;
 constexpr int NLQ = NWQ;                   // copying wavefronts
 
-// Output tile BM activation rows x BN weight rows: 128 x 128, or 64 x 256 for
-// M <= 64.  Wavefront w owns weight subtile w % (BN/32) and the activation
-// subtile pair w / (BN/32).  One LDS buffer: weights [BN][80], activations
-// [HALF][BM][32], scales [HALF][BM], 1 KB for slots without a job.  F: the
-// weight format.  An 80-byte weight row holds, for IQ4_XS, the super-block's
+// Output tile BM activation rows x BN weight rows: 128 x 128, 64 x 256 for
+// M <= 64, or 256 x 128 for large M.  Wavefront w owns weight subtile
+// w % (BN/32) and the group of G activation subtiles w / (BN/32): G = 2, or
+// 4 for 256 x 128, where each wavefront's codebook lookup serves four
+// activation subtiles (half the lookup work per output; the rescale, three
+// VALU instructions per output, is the rest).  One LDS buffer: weights
+// [BN][80], activations [HALF][BM][32], scales [HALF][BM], 1 KB for slots
+// without a job; NBUF buffers (5, or 3 for the larger tile).  F: the weight
+// format.  An 80-byte weight row holds, for IQ4_XS, the super-block's
 // 8 header bytes, 8 unused bytes and the half's 64 index bytes; for IQ4_NL
 // and Q4_0, bytes [0, 80) of the 144-byte unit for the first half and
 // [64, 144) for the second (its four 18-byte blocks at 8 + 18s), so that no
@@ -71,6 +74,9 @@ constexpr int NLQ = NWQ;                   // copying wavefronts
 template <int BM_, int BN_, int F_ = FMT_IQ4_XS>
 struct QCfg {
     static constexpr int BM = BM_, BN = BN_, NTW = BN / TILE, F = F_;
+    static constexpr int G = (BM / TILE) * NTW / NWQ;          // activation subtiles per wavefront
+    static constexpr int U = G == 2 ? 2 : 1;                    // sub-blocks per compute group
+    static constexpr int NBUF = G == 2 ? 5 : 3;
     static constexpr int W_BYTES = BN * WROWQ;
     static constexpr int A_OFF = W_BYTES, A_BYTES = HALF * BM * SB;
     static constexpr int D_OFF = A_OFF + A_BYTES, D_BYTES = HALF * BM * 4;
@@ -78,8 +84,8 @@ struct QCfg {
     static constexpr int BUFQ = DUMP + 1024;
     static constexpr int JW = W_BYTES / 1024, JA = A_BYTES / 1024, JD = D_BYTES / 1024;
     static constexpr int SLOTS = (JW + JA + JD + NLQ - 1) / NLQ;
-    static_assert(NTW * (BM / (2 * TILE)) == NWQ, "eight wavefronts: weight subtile x activation pair");
-    static_assert(W_BYTES % 1024 == 0 && D_BYTES % 1024 == 0 && NBUFQ * BUFQ + 256 <= 160 * 1024, "LDS budget");
+    static_assert((G == 2 || G == 4) && NTW * (BM / (G * TILE)) == NWQ, "eight wavefronts: weight subtile x group");
+    static_assert(W_BYTES % 1024 == 0 && D_BYTES % 1024 == 0 && NBUF * BUFQ + 256 <= 160 * 1024, "LDS budget");
 };
 
 // Unit cursor: one half super-block of one tile per step (j counts halves,
@@ -112,7 +118,8 @@ struct FixRuns {
 
 // Partial tile slot (run g, 0 = its first tile, 1 = its last): 8 float4 per
 // thread, float4 e of thread tid at [e][tid] (coalesced stores and loads);
-// e = 4*i + r/4 for accumulator i, result register r.
+// e = 4*i + r/4 for accumulator i, result register r.  (Tiles with G = 2
+// only: the plan never gives the 256 x 128 tiles a workspace.)
 constexpr int SLOT_F4 = 8 * NTQ;
 __device__ __forceinline__ float4 *slot_at(float *ws, int g, int which)
 {
@@ -128,7 +135,8 @@ k_mmqt(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__re
     constexpr int A_OFF = C::A_OFF, D_OFF = C::D_OFF, BUFQ = C::BUFQ;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int nt = wave % C::NTW, mp = wave / C::NTW;        // weight subtile, activation pair
+    constexpr int GQ = C::G, UQ = C::U, NB = C::NBUF;
+    const int nt = wave % C::NTW, mq = wave / C::NTW;        // weight subtile, activation group
     const int col = lane & 31, h = lane >> 5;
     // Workgroups are dealt round-robin to the 8 XCDs (each with its own L2):
     // give the workgroups of one XCD consecutive runs, so that the activation
@@ -200,9 +208,9 @@ k_mmqt(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__re
         }
     };
 
-    float acc[2][16];
+    float acc[GQ][16];
 #pragma unroll
-    for (int i = 0; i < 2; i++)
+    for (int i = 0; i < GQ; i++)
 #pragma unroll
         for (int r = 0; r < 16; r++)
             acc[i][r] = 0.0f;
@@ -212,10 +220,10 @@ k_mmqt(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__re
             const int mb = t % mblocks, wb = t / mblocks;
             const int n = wb * BN + nt * TILE + col;
 #pragma unroll
-            for (int i = 0; i < 2; i++)
+            for (int i = 0; i < GQ; i++)
 #pragma unroll
                 for (int r = 0; r < 16; r++) {
-                    const int m = mb * BM + (2 * mp + i) * TILE + 8 * (r / 4) + 4 * h + (r % 4);
+                    const int m = mb * BM + (GQ * mq + i) * TILE + 8 * (r / 4) + 4 * h + (r % 4);
                     if (m < M && n < N)
                         Y[(int64_t)m * N + n] = acc[i][r];
                 }
@@ -223,14 +231,14 @@ k_mmqt(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__re
             const int mb = t % mblocks, wb = t / mblocks;
             const int n = wb * BN + nt * TILE + col;
 #pragma unroll
-            for (int i = 0; i < 2; i++)
+            for (int i = 0; i < GQ; i++)
 #pragma unroll
                 for (int r = 0; r < 16; r++) {
-                    const int m = mb * BM + (2 * mp + i) * TILE + 8 * (r / 4) + 4 * h + (r % 4);
+                    const int m = mb * BM + (GQ * mq + i) * TILE + 8 * (r / 4) + 4 * h + (r % 4);
                     if (m < M && n < N)
                         atomicAdd(Y + (int64_t)m * N + n, acc[i][r]);
                 }
-        } else {
+        } else if constexpr (GQ == 2) {
             float4 *slot = slot_at(ws, g, t == t_first ? 0 : 1);
 #pragma unroll
             for (int i = 0; i < 2; i++)
@@ -240,7 +248,7 @@ k_mmqt(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__re
                         make_float4(acc[i][4 * q], acc[i][4 * q + 1], acc[i][4 * q + 2], acc[i][4 * q + 3]);
         }
 #pragma unroll
-        for (int i = 0; i < 2; i++)
+        for (int i = 0; i < GQ; i++)
 #pragma unroll
             for (int r = 0; r < 16; r++)
                 acc[i][r] = 0.0f;
@@ -254,61 +262,75 @@ k_mmqt(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__re
         if constexpr (C::F == FMT_IQ4_XS)
             hdr = *reinterpret_cast<const uint2 *>(wrow);
         const char *unit = wrow - 64 * hf;                    // where the 144-byte unit would start
-        // Two sub-blocks at a time: all their LDS reads first, then all four
-        // products (each into registers of its own), then the epilogues, so
-        // that reads, lookups, matrix-core work and rescaling of the two
-        // overlap.
+        // U sub-blocks at a time (two with G = 2, one with G = 4): all their
+        // LDS reads first, then all U*G products (each into registers of its
+        // own), then the epilogues, so that reads, lookups, matrix-core work
+        // and rescaling overlap.
 #pragma unroll
-        for (int s0 = 0; s0 < HALF; s0 += 2) {
-            uint2 q[2];
-            v4i ax[2][2];
-            float4 dx[2][2][4];
+        for (int s0 = 0; s0 < HALF; s0 += UQ) {
+            uint2 q[UQ];
+            v4i ax[UQ][GQ];
+            float4 dx[UQ][GQ][4];
+            // this lane's activation scales of subtile i, sub-block s: rows
+            // 8*qd + 4*h .. +3
+            auto load_dx = [&](int u, int i) __attribute__((always_inline)) {
 #pragma unroll
-            for (int u = 0; u < 2; u++) {
+                for (int qd = 0; qd < 4; qd++)
+                    dx[u][i][qd] = *reinterpret_cast<const float4 *>(
+                        B + D_OFF + ((s0 + u) * BM + (GQ * mq + i) * TILE + 4 * h + 8 * qd) * 4);
+            };
+#pragma unroll
+            for (int u = 0; u < UQ; u++) {
                 const int s = s0 + u;
                 if constexpr (C::F == FMT_IQ4_XS)
                     q[u] = *reinterpret_cast<const uint2 *>(wrow + 16 + 16 * s + 8 * h);
                 else
                     q[u] = unit_qs<C::F>(unit, HALF * hf + s, h);
 #pragma unroll
-                for (int i = 0; i < 2; i++) {
-                    const int mt = 2 * mp + i;
+                for (int i = 0; i < GQ; i++) {
+                    const int mt = GQ * mq + i;
                     ax[u][i] = *reinterpret_cast<const v4i *>(B + A_OFF + (s * BM + mt * TILE + col) * SB + 16 * h);
-#pragma unroll
-                    for (int qd = 0; qd < 4; qd++)
-                        dx[u][i][qd] =
-                            *reinterpret_cast<const float4 *>(B + D_OFF + (s * BM + mt * TILE + 4 * h + 8 * qd) * 4);
+                    if constexpr (GQ == 2)
+                        load_dx(u, i);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
-            v16i D[2][2];
-            // (the two halves of the wavefront, same rows, each decode one of
-            // the two sub-blocks' scales and swap them)
-            float sw[2];
-            {
+            v16i D[UQ][GQ];
+            float sw[UQ];
+            if constexpr (UQ == 2) {
+                // (the two halves of the wavefront, same rows, each decode one
+                // of the two sub-blocks' scales and swap them)
                 const float sc = C::F == FMT_IQ4_XS ? sub_scale(hdr.x, hdr.y, HALF * hf + s0 + h)
                                                     : unit_scale<C::F>(unit, HALF * hf + s0 + h, true);
                 const uint32_t own = __builtin_bit_cast(uint32_t, sc);
                 const auto both = __builtin_amdgcn_permlane32_swap(own, own, false, false);
                 sw[0] = __builtin_bit_cast(float, (uint32_t)both[0]);
                 sw[1] = __builtin_bit_cast(float, (uint32_t)both[1]);
+            } else {
+                sw[0] = C::F == FMT_IQ4_XS ? sub_scale(hdr.x, hdr.y, HALF * hf + s0)
+                                           : unit_scale<C::F>(unit, HALF * hf + s0, true);
             }
 #pragma unroll
-            for (int u = 0; u < 2; u++) {
+            for (int u = 0; u < UQ; u++) {
                 uint32_t wf[4];
                 expand8<C::F>(q[u].x, q[u].y, wf);
                 const v4i bf = {(int)wf[0], (int)wf[1], (int)wf[2], (int)wf[3]};
 #pragma unroll
-                for (int i = 0; i < 2; i++) {
+                for (int i = 0; i < GQ; i++) {
                     const v16i zero = {0};
                     D[u][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ax[u][i], bf, zero, 0, 0, 0);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int u = 0; u < 2; u++)
+            for (int u = 0; u < UQ; u++)
 #pragma unroll
-                for (int i = 0; i < 2; i++) {
+                for (int i = 0; i < GQ; i++) {
+                    if constexpr (GQ == 4) {
+                        // (scales loaded per subtile: sixteen registers live, not 64)
+                        load_dx(u, i);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
 #pragma unroll
                     for (int r = 0; r < 16; r++) {
                         const float d = (r % 4 == 0) ? dx[u][i][r / 4].x : (r % 4 == 1) ? dx[u][i][r / 4].y
@@ -317,9 +339,9 @@ k_mmqt(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__re
                     }
                 }
 #pragma unroll
-            for (int u = 0; u < 2; u++)
+            for (int u = 0; u < UQ; u++)
 #pragma unroll
-                for (int i = 0; i < 2; i++)
+                for (int i = 0; i < GQ; i++)
                     keep_live(D[u][i]);
         }
         if (c.flags & 1)
@@ -333,20 +355,20 @@ k_mmqt(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__re
     cur.u = ua;
     cur.t = t_first;
     cur.j = ua - cur.t * 2 * nb;
-    Chunk info[NBUFQ];
-    static_for(std::make_integer_sequence<int, NBUFQ - 1>(), [&](auto bc) {
+    Chunk info[NB];
+    static_for(std::make_integer_sequence<int, NB - 1>(), [&](auto bc) {
         info[decltype(bc)::value] = cur.next();
         issue(info[decltype(bc)::value], bc);
     });
     // Step on buffer b: wait for this wavefront's loads of the unit (those of
-    // the NBUFQ-2 units issued after it stay in flight), meet the others (all
-    // loads landed; the buffer computed last is free), load the unit NBUFQ-1
+    // the NB-2 units issued after it stay in flight), meet the others (all
+    // loads landed; the buffer computed last is free), load the unit NB-1
     // ahead into that buffer, compute.
     auto step = [&](auto bc) __attribute__((always_inline)) {
-        constexpr int b = decltype(bc)::value, nxt = (b + NBUFQ - 1) % NBUFQ;
+        constexpr int b = decltype(bc)::value, nxt = (b + NB - 1) % NB;
         if (info[b].cl == 0)
             return false;
-        __builtin_amdgcn_s_waitcnt(wait_vm_lds(SLOTS * (NBUFQ - 2)));
+        __builtin_amdgcn_s_waitcnt(wait_vm_lds(SLOTS * (NB - 2)));
         raw_barrier();
         info[nxt] = cur.next();
         issue(info[nxt], std::integral_constant<int, nxt>());
@@ -355,7 +377,7 @@ k_mmqt(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__re
     };
     bool go = true;
     do
-        static_for(std::make_integer_sequence<int, NBUFQ>(), [&](auto bc) __attribute__((always_inline)) {
+        static_for(std::make_integer_sequence<int, NB>(), [&](auto bc) __attribute__((always_inline)) {
             if (go)
                 go = step(bc);
         });
@@ -402,14 +424,14 @@ k_mmqt_fix(const float *__restrict__ ws, float *__restrict__ Y, int M, int N, in
         }
     }
     const int lane = tid & 63, wave = tid >> 6;
-    const int nt = wave % C::NTW, mp = wave / C::NTW, col = lane & 31, h = lane >> 5;
+    const int nt = wave % C::NTW, mq = wave / C::NTW, col = lane & 31, h = lane >> 5;
     const int mb = t % mblocks, wb = t / mblocks;
     const int n = wb * BN + nt * TILE + col;
     const float v4[4] = {sum.x, sum.y, sum.z, sum.w};
 #pragma unroll
     for (int c = 0; c < 4; c++) {
         const int i = e / 4, r = 4 * (e % 4) + c;
-        const int m = mb * BM + (2 * mp + i) * TILE + 8 * (r / 4) + 4 * h + (r % 4);
+        const int m = mb * BM + (C::G * mq + i) * TILE + 8 * (r / 4) + 4 * h + (r % 4);
         if (m < M && n < N)
             Y[(int64_t)m * N + n] = v4[c];
     }
@@ -444,13 +466,17 @@ hipError_t launch_cfg(const void *W, const XPlanes &x, float *Y, float *ws, int6
 
 }  // namespace
 
-MmqtPlan mmqt_plan(int64_t M, int64_t N, int64_t K, int cus, int fmt)
+namespace {
+
+int64_t bn_of(int64_t bm) { return bm == 64 ? 256 : 128; }
+
+// The plan for tiles of BM x bn_of(BM) (not ok: offsets past 32 bits).
+MmqtPlan plan_tiles(int64_t M, int64_t N, int64_t K, int cus, int fmt, int64_t BM)
 {
     MmqtPlan p;
     const int64_t nb = K / QK, row_bytes = nb * sblk_bytes(fmt);
     const int64_t Mp = round_up(M, MPAD);
-    // 64 x 256 tiles up to M = 64, else 128 x 128
-    const int64_t BM = M <= 2 * TILE ? 64 : 128, BN = 16384 / BM;
+    const int64_t BN = bn_of(BM);
     const int64_t mblocks = (M + BM - 1) / BM, wblocks = (N + BN - 1) / BN;
     const int64_t T = mblocks * wblocks, U = T * 2 * nb;
     // 32-bit offsets
@@ -470,6 +496,7 @@ MmqtPlan mmqt_plan(int64_t M, int64_t N, int64_t K, int cus, int fmt)
     p.grid = (int)std::max<int64_t>(G, 1);
     p.mblocks = (int)mblocks;
     p.bm = (int)BM;
+    p.tiles = T;
     // With at least one tile's units per run a tile has two owners at most:
     // they add into a zeroed Y (0 + a + b == 0 + b + a), which costs less
     // than writing and summing partial tiles (M=512, 10240 x 5120: the
@@ -491,15 +518,31 @@ MmqtPlan mmqt_plan(int64_t M, int64_t N, int64_t K, int cus, int fmt)
     return p;
 }
 
+}  // namespace
+
+// 64 x 256 tiles up to M = 64, else 128 x 128; 256 x 128 from M = 256 when
+// every run spans at least four of them (few tiles shared, none with more
+// than two owners, so no workspace).
+MmqtPlan mmqt_plan(int64_t M, int64_t N, int64_t K, int cus, int fmt)
+{
+    if (M >= 256) {
+        const MmqtPlan big = plan_tiles(M, N, K, cus, fmt, 256);
+        if (big.ok && big.workspace_bytes == 0 && 4LL * big.grid <= big.tiles)
+            return big;
+    }
+    return plan_tiles(M, N, K, cus, fmt, M <= 2 * TILE ? 64 : 128);
+}
+
 hipError_t launch_mmqt(const void *W, const XPlanes &x, float *Y, int64_t N, const MmqtPlan &p, void *workspace,
                        hipStream_t s)
 {
-    if (!p.ok || p.grid < 1 || p.grid > MAXG || (p.workspace_bytes && workspace == nullptr))
+    if (!p.ok || p.grid < 1 || p.grid > MAXG || (p.workspace_bytes && workspace == nullptr) ||
+        (p.bm == 256 && p.workspace_bytes))
         return hipErrorInvalidValue;
     if ((const char *)x.dp != (const char *)x.qp + x.Mp * x.K)
         return hipErrorInvalidValue;
     const int nb = (int)(x.K / QK), nh = 2 * nb;
-    const int64_t BN = 16384 / p.bm;
+    const int64_t BN = bn_of(p.bm);
     const int64_t U = (int64_t)p.mblocks * ((N + BN - 1) / BN) * nh;
     Runs runs;
     for (int g = 0; g <= p.grid; g++) {
@@ -508,13 +551,16 @@ hipError_t launch_mmqt(const void *W, const XPlanes &x, float *Y, int64_t N, con
             runs.t[g] = runs.u[g] / nh;
     }
     float *ws = (float *)workspace;
-    switch (p.fmt * 2 + (p.bm == 128 ? 1 : 0)) {
-    case 2 * FMT_IQ4_XS: return launch_cfg<QCfg<64, 256, FMT_IQ4_XS>>(W, x, Y, ws, N, p, runs, s);
-    case 2 * FMT_IQ4_XS + 1: return launch_cfg<QCfg<128, 128, FMT_IQ4_XS>>(W, x, Y, ws, N, p, runs, s);
-    case 2 * FMT_IQ4_NL: return launch_cfg<QCfg<64, 256, FMT_IQ4_NL>>(W, x, Y, ws, N, p, runs, s);
-    case 2 * FMT_IQ4_NL + 1: return launch_cfg<QCfg<128, 128, FMT_IQ4_NL>>(W, x, Y, ws, N, p, runs, s);
-    case 2 * FMT_Q4_0: return launch_cfg<QCfg<64, 256, FMT_Q4_0>>(W, x, Y, ws, N, p, runs, s);
-    case 2 * FMT_Q4_0 + 1: return launch_cfg<QCfg<128, 128, FMT_Q4_0>>(W, x, Y, ws, N, p, runs, s);
+    switch (p.fmt * 3 + (p.bm == 64 ? 0 : p.bm == 128 ? 1 : 2)) {
+    case 3 * FMT_IQ4_XS: return launch_cfg<QCfg<64, 256, FMT_IQ4_XS>>(W, x, Y, ws, N, p, runs, s);
+    case 3 * FMT_IQ4_XS + 1: return launch_cfg<QCfg<128, 128, FMT_IQ4_XS>>(W, x, Y, ws, N, p, runs, s);
+    case 3 * FMT_IQ4_XS + 2: return launch_cfg<QCfg<256, 128, FMT_IQ4_XS>>(W, x, Y, ws, N, p, runs, s);
+    case 3 * FMT_IQ4_NL: return launch_cfg<QCfg<64, 256, FMT_IQ4_NL>>(W, x, Y, ws, N, p, runs, s);
+    case 3 * FMT_IQ4_NL + 1: return launch_cfg<QCfg<128, 128, FMT_IQ4_NL>>(W, x, Y, ws, N, p, runs, s);
+    case 3 * FMT_IQ4_NL + 2: return launch_cfg<QCfg<256, 128, FMT_IQ4_NL>>(W, x, Y, ws, N, p, runs, s);
+    case 3 * FMT_Q4_0: return launch_cfg<QCfg<64, 256, FMT_Q4_0>>(W, x, Y, ws, N, p, runs, s);
+    case 3 * FMT_Q4_0 + 1: return launch_cfg<QCfg<128, 128, FMT_Q4_0>>(W, x, Y, ws, N, p, runs, s);
+    case 3 * FMT_Q4_0 + 2: return launch_cfg<QCfg<256, 128, FMT_Q4_0>>(W, x, Y, ws, N, p, runs, s);
     default: return hipErrorInvalidValue;
     }
 }
