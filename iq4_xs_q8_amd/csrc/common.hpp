@@ -363,7 +363,7 @@ hipError_t launch_mmv_group(const MmvGroup &grp, const XPlanes &x, const MmvPlan
 // workgroups are summed from a workspace of partial tiles by a second kernel.
 struct MmqtPlan {
     bool ok = false, zero_y = false;    // zero_y: shared tiles add into a zeroed Y
-    int grid = 0, mblocks = 0, bm = 0;   // bm: tile rows (64, 128 or 256)
+    int grid = 0, mblocks = 0, bm = 0, bn = 0;   // tile: bm activation rows x bn weight rows
     int64_t tiles = 0;
     int fmt = FMT_IQ4_XS;
     size_t workspace_bytes = 0;         // else partial tiles in a workspace

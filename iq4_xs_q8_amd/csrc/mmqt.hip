@@ -58,12 +58,13 @@ constexpr int HALF = SUBS / 2;             // sub-blocks per step
 constexpr int WROWQ = 80;                  // LDS weight row: header, 8 unused, 64 index bytes
 constexpr int NLQ = NWQ;                   // copying wavefronts
 
-// Output tile BM activation rows x BN weight rows: 128 x 128, 64 x 256 for
-// M <= 64, or 256 x 128 for large M.  Wavefront w owns weight subtile
-// w % (BN/32) and the group of G activation subtiles w / (BN/32): G = 2, or
-// 4 for 256 x 128, where each wavefront's codebook lookup serves four
-// activation subtiles (half the lookup work per output; the rescale, three
-// VALU instructions per output, is the rest).  One LDS buffer: weights
+// Output tile BM activation rows x BN weight rows: 128 x 128 or 64 x 256
+// (M <= 64), or, where every stream-K run spans a whole tile, 256 x 128 or
+// 128 x 256.  Wavefront w owns weight
+// subtile w % (BN/32) and the group of G activation subtiles w / (BN/32):
+// G = 2, or 4 for the two large tiles, where each wavefront's codebook lookup
+// serves four activation subtiles (half the lookup work per output; the
+// rescale, three VALU instructions per output, is the rest).  One LDS buffer: weights
 // [BN][80], activations [HALF][BM][32], scales [HALF][BM], 1 KB for slots
 // without a job; NBUF buffers (5, or 3 for the larger tile).  F: the weight
 // format.  An 80-byte weight row holds, for IQ4_XS, the super-block's
@@ -468,15 +469,12 @@ hipError_t launch_cfg(const void *W, const XPlanes &x, float *Y, float *ws, int6
 
 namespace {
 
-int64_t bn_of(int64_t bm) { return bm == 64 ? 256 : 128; }
-
-// The plan for tiles of BM x bn_of(BM) (not ok: offsets past 32 bits).
-MmqtPlan plan_tiles(int64_t M, int64_t N, int64_t K, int cus, int fmt, int64_t BM)
+// The plan for tiles of BM x BN (not ok: offsets past 32 bits).
+MmqtPlan plan_tiles(int64_t M, int64_t N, int64_t K, int cus, int fmt, int64_t BM, int64_t BN)
 {
     MmqtPlan p;
     const int64_t nb = K / QK, row_bytes = nb * sblk_bytes(fmt);
     const int64_t Mp = round_up(M, MPAD);
-    const int64_t BN = bn_of(BM);
     const int64_t mblocks = (M + BM - 1) / BM, wblocks = (N + BN - 1) / BN;
     const int64_t T = mblocks * wblocks, U = T * 2 * nb;
     // 32-bit offsets
@@ -496,6 +494,7 @@ MmqtPlan plan_tiles(int64_t M, int64_t N, int64_t K, int cus, int fmt, int64_t B
     p.grid = (int)std::max<int64_t>(G, 1);
     p.mblocks = (int)mblocks;
     p.bm = (int)BM;
+    p.bn = (int)BN;
     p.tiles = T;
     // With at least one tile's units per run a tile has two owners at most:
     // they add into a zeroed Y (0 + a + b == 0 + b + a), which costs less
@@ -520,29 +519,35 @@ MmqtPlan plan_tiles(int64_t M, int64_t N, int64_t K, int cus, int fmt, int64_t B
 
 }  // namespace
 
-// 64 x 256 tiles up to M = 64, else 128 x 128; 256 x 128 from M = 256 when
-// every run spans at least four of them (few tiles shared, none with more
-// than two owners, so no workspace).
+// The tiles with four activation subtiles per wavefront (128 x 256 from
+// M = 128, 256 x 128 from 256) wherever every run spans at least one of them
+// (no tile with more than two owners, so no workspace); else 64 x 256 up to
+// M = 64 and 128 x 128 above.  (Measured with the
+// 256 x 128 tile at 512 x 17408 x 5120, where almost every tile has two
+// owners: 206 against 235 us for 128 x 128; with 128 x 256 at
+// 128 x 248320 x 5120: 674 against 753 us.)
 MmqtPlan mmqt_plan(int64_t M, int64_t N, int64_t K, int cus, int fmt)
 {
-    if (M >= 256) {
-        const MmqtPlan big = plan_tiles(M, N, K, cus, fmt, 256);
-        if (big.ok && big.workspace_bytes == 0 && 4LL * big.grid <= big.tiles)
+    if (M >= 128) {
+        const int64_t BM = M >= 256 ? 256 : 128, BN = 32768 / BM;
+        const MmqtPlan big = plan_tiles(M, N, K, cus, fmt, BM, BN);
+        if (big.ok && big.workspace_bytes == 0)
             return big;
     }
-    return plan_tiles(M, N, K, cus, fmt, M <= 2 * TILE ? 64 : 128);
+    return M <= 2 * TILE ? plan_tiles(M, N, K, cus, fmt, 64, 256) : plan_tiles(M, N, K, cus, fmt, 128, 128);
 }
 
 hipError_t launch_mmqt(const void *W, const XPlanes &x, float *Y, int64_t N, const MmqtPlan &p, void *workspace,
                        hipStream_t s)
 {
+    const int cfg = p.bm == 64 ? 0 : p.bm == 128 && p.bn == 128 ? 1 : p.bm == 256 ? 2 : 3;
     if (!p.ok || p.grid < 1 || p.grid > MAXG || (p.workspace_bytes && workspace == nullptr) ||
-        (p.bm == 256 && p.workspace_bytes))
+        (cfg >= 2 && p.workspace_bytes))
         return hipErrorInvalidValue;
     if ((const char *)x.dp != (const char *)x.qp + x.Mp * x.K)
         return hipErrorInvalidValue;
     const int nb = (int)(x.K / QK), nh = 2 * nb;
-    const int64_t BN = bn_of(p.bm);
+    const int64_t BN = p.bn;
     const int64_t U = (int64_t)p.mblocks * ((N + BN - 1) / BN) * nh;
     Runs runs;
     for (int g = 0; g <= p.grid; g++) {
@@ -551,16 +556,19 @@ hipError_t launch_mmqt(const void *W, const XPlanes &x, float *Y, int64_t N, con
             runs.t[g] = runs.u[g] / nh;
     }
     float *ws = (float *)workspace;
-    switch (p.fmt * 3 + (p.bm == 64 ? 0 : p.bm == 128 ? 1 : 2)) {
-    case 3 * FMT_IQ4_XS: return launch_cfg<QCfg<64, 256, FMT_IQ4_XS>>(W, x, Y, ws, N, p, runs, s);
-    case 3 * FMT_IQ4_XS + 1: return launch_cfg<QCfg<128, 128, FMT_IQ4_XS>>(W, x, Y, ws, N, p, runs, s);
-    case 3 * FMT_IQ4_XS + 2: return launch_cfg<QCfg<256, 128, FMT_IQ4_XS>>(W, x, Y, ws, N, p, runs, s);
-    case 3 * FMT_IQ4_NL: return launch_cfg<QCfg<64, 256, FMT_IQ4_NL>>(W, x, Y, ws, N, p, runs, s);
-    case 3 * FMT_IQ4_NL + 1: return launch_cfg<QCfg<128, 128, FMT_IQ4_NL>>(W, x, Y, ws, N, p, runs, s);
-    case 3 * FMT_IQ4_NL + 2: return launch_cfg<QCfg<256, 128, FMT_IQ4_NL>>(W, x, Y, ws, N, p, runs, s);
-    case 3 * FMT_Q4_0: return launch_cfg<QCfg<64, 256, FMT_Q4_0>>(W, x, Y, ws, N, p, runs, s);
-    case 3 * FMT_Q4_0 + 1: return launch_cfg<QCfg<128, 128, FMT_Q4_0>>(W, x, Y, ws, N, p, runs, s);
-    case 3 * FMT_Q4_0 + 2: return launch_cfg<QCfg<256, 128, FMT_Q4_0>>(W, x, Y, ws, N, p, runs, s);
+    switch (p.fmt * 4 + cfg) {
+    case 4 * FMT_IQ4_XS: return launch_cfg<QCfg<64, 256, FMT_IQ4_XS>>(W, x, Y, ws, N, p, runs, s);
+    case 4 * FMT_IQ4_XS + 1: return launch_cfg<QCfg<128, 128, FMT_IQ4_XS>>(W, x, Y, ws, N, p, runs, s);
+    case 4 * FMT_IQ4_XS + 2: return launch_cfg<QCfg<256, 128, FMT_IQ4_XS>>(W, x, Y, ws, N, p, runs, s);
+    case 4 * FMT_IQ4_XS + 3: return launch_cfg<QCfg<128, 256, FMT_IQ4_XS>>(W, x, Y, ws, N, p, runs, s);
+    case 4 * FMT_IQ4_NL: return launch_cfg<QCfg<64, 256, FMT_IQ4_NL>>(W, x, Y, ws, N, p, runs, s);
+    case 4 * FMT_IQ4_NL + 1: return launch_cfg<QCfg<128, 128, FMT_IQ4_NL>>(W, x, Y, ws, N, p, runs, s);
+    case 4 * FMT_IQ4_NL + 2: return launch_cfg<QCfg<256, 128, FMT_IQ4_NL>>(W, x, Y, ws, N, p, runs, s);
+    case 4 * FMT_IQ4_NL + 3: return launch_cfg<QCfg<128, 256, FMT_IQ4_NL>>(W, x, Y, ws, N, p, runs, s);
+    case 4 * FMT_Q4_0: return launch_cfg<QCfg<64, 256, FMT_Q4_0>>(W, x, Y, ws, N, p, runs, s);
+    case 4 * FMT_Q4_0 + 1: return launch_cfg<QCfg<128, 128, FMT_Q4_0>>(W, x, Y, ws, N, p, runs, s);
+    case 4 * FMT_Q4_0 + 2: return launch_cfg<QCfg<256, 128, FMT_Q4_0>>(W, x, Y, ws, N, p, runs, s);
+    case 4 * FMT_Q4_0 + 3: return launch_cfg<QCfg<128, 256, FMT_Q4_0>>(W, x, Y, ws, N, p, runs, s);
     default: return hipErrorInvalidValue;
     }
 }

@@ -189,8 +189,8 @@ def _check_invariants(Wd, W2d, Xd, path, what):
 
 # Every kernel and work split of the integer paths.  The tile-kernel cases
 # were chosen with the host plan's rules (grid size, run length, tile shape):
-# 64 x 256 tiles up to M = 64, 128 x 128 above, 256 x 128 from M = 256 when
-# every run spans at least four tiles; "two owners": runs longer
+# 64 x 256 tiles up to M = 64, 128 x 128 above, 128 x 256 from M = 128 and
+# 256 x 128 from M = 256 when every run spans a tile; "two owners": runs longer
 # than a tile, shared tiles added into a zeroed Y; "workspace": runs shorter
 # than a tile, 2..16 owners per tile summed in run order by the second kernel.
 INVARIANT_CASES = [
@@ -205,10 +205,11 @@ INVARIANT_CASES = [
     ("tile 128x128, workspace (16 owners)", iq.PATH_MMQ, 100, 200, 4096),
     ("tile 128x128, workspace (5 owners)", iq.PATH_MMQ, 96, 5120, 5120),
     ("tile 128x128, two owners, M=512", iq.PATH_MMQ, 512, 10240, 5120),
-    # 256 x 128 tiles (four activation subtiles per wavefront): M >= 256 and
-    # runs of at least four tiles; ragged M and N, two owners per shared tile
+    # the tiles with four activation subtiles per wavefront; ragged M and N,
+    # two owners per shared tile
     ("tile 256x128, two owners, ragged", iq.PATH_MMQ, 300, 65613, 256),
     ("tile 256x128, M=512", iq.PATH_MMQ, 512, 65536, 256),
+    ("tile 128x256, two owners, ragged", iq.PATH_MMQ, 150, 65613, 256),
 ]
 
 
