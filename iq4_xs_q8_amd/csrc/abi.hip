@@ -356,12 +356,21 @@ int run_gemm(const void *W, const float *X, const void *Xq, float *Y, int64_t M,
     if (path == IQ4XS_PATH_GEMV || path == IQ4XS_PATH_MMQ) {
         const size_t pbytes = (size_t)round_up((int64_t)xplanes_bytes(M, K), 256);
         const XPlanes xp = xplanes_at(base, M, K);
-        // a matmul that adds partial tiles into Y gets it zeroed by the quantizer
-        const bool zero = path == IQ4XS_PATH_MMQ && mmq_plan(M, N, K, fmt).zero_y;
-        float *yz = zero ? Y : nullptr;
-        const int64_t nz = zero ? M * N : 0;
-        hipError_t e = X ? launch_quantize(X, nullptr, &xp, M, K, s, yz, nz)
-                         : launch_q8_1_convert(Xq, &xp, M, K, s, yz, nz);
+        // a matmul that adds partial tiles into Y gets them zeroed by the
+        // quantizer: the shared tiles of the tile kernel, all of Y (M <= 32)
+        // for the streaming kernel
+        const MmqPlan mp = path == IQ4XS_PATH_MMQ ? mmq_plan(M, N, K, fmt) : MmqPlan();
+        const bool zero = path == IQ4XS_PATH_MMQ && mp.zero_y;
+        ZeroList zl;
+        if (zero && mp.tile) {
+            zl.tiles = mmqt_zero_tiles(mp.tp, M, N, K, Y);
+        } else if (zero) {
+            zl.p[0] = Y;
+            zl.n[0] = M * N;
+            zl.count = 1;
+        }
+        hipError_t e = X ? launch_quantize(X, nullptr, &xp, M, K, s, zl)
+                         : launch_q8_1_convert(Xq, &xp, M, K, s, zl);
         if ((st = launch_err(e, "quantize")) != IQ4XS_OK)
             return st;
         e = path == IQ4XS_PATH_GEMV ? launch_gemv(W, xp, Y, N, s, fmt)

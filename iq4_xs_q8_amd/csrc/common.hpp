@@ -319,10 +319,24 @@ __device__ __forceinline__ void bf16x2_split(float a, float b, uint32_t &hi, uin
     lo = __builtin_bit_cast(uint32_t, l);
 }
 
+// Tiles of Y that two workgroups of the tile kernel add into (a stream-K run
+// boundary falls inside each): zeroed before the matmul instead of all of Y.
+// Tile t covers rows (t % mblocks)*bm .. +bm and columns (t / mblocks)*bn .. +bn.
+constexpr int MAXZT = 256;
+struct ZeroTiles {
+    float *y = nullptr;
+    int64_t M = 0, N = 0;
+    int bm = 0, bn = 0, mblocks = 0, count = 0;
+    int t[MAXZT] = {};
+};
+
+// What a quantize launch zeroes besides its work: whole ranges (one per
+// matrix of a grouped call) and the shared tiles of one tile-kernel call.
 struct ZeroList {
     float *p[MAXGRP] = {};
     int64_t n[MAXGRP] = {};
     int count = 0;
+    ZeroTiles tiles;
 };
 
 // ---- launchers (each defined in the .hip file that holds its kernel) -----
@@ -336,7 +350,10 @@ hipError_t launch_quantize(const float *X, void *Xq, const XPlanes *planes, int6
                            const ZeroList &zl, const XSplit *xs = nullptr);
 hipError_t launch_q8_1_convert(const void *Xq, const XPlanes *planes, int64_t M, int64_t K, hipStream_t s,
                               float *yz = nullptr, int64_t nz = 0, const XSplit *xs = nullptr);
+hipError_t launch_q8_1_convert(const void *Xq, const XPlanes *planes, int64_t M, int64_t K, hipStream_t s,
+                              const ZeroList &zl, const XSplit *xs = nullptr);
 hipError_t launch_zero(float *y, int64_t n, hipStream_t s);
+hipError_t launch_zero_tiles(const ZeroTiles &zt, hipStream_t s);
 hipError_t launch_gemv(const void *W, const XPlanes &x, float *Y, int64_t N, hipStream_t s,
                        int fmt = FMT_IQ4_XS);
 // MMQ work split for a shape: TM 32-row subtiles per wavefront, KW
@@ -369,6 +386,8 @@ struct MmqtPlan {
     size_t workspace_bytes = 0;         // else partial tiles in a workspace
 };
 MmqtPlan mmqt_plan(int64_t M, int64_t N, int64_t K, int cus, int fmt = FMT_IQ4_XS);
+// The tiles of Y a plan with zero_y needs zeroed (count 0 otherwise).
+ZeroTiles mmqt_zero_tiles(const MmqtPlan &p, int64_t M, int64_t N, int64_t K, float *Y);
 hipError_t launch_mmqt(const void *W, const XPlanes &x, float *Y, int64_t N, const MmqtPlan &p, void *workspace,
                        hipStream_t s);
 struct MmqPlan {

@@ -295,7 +295,7 @@ hipError_t launch_mmq(const void *Wv, const XPlanes &x, float *Y, int64_t N, voi
         if (p.tp.workspace_bytes && workspace == nullptr)
             return hipErrorInvalidValue;
         if (p.tp.zero_y && !y_zeroed) {
-            const hipError_t e = launch_zero(Y, x.M * N, s);
+            const hipError_t e = launch_zero_tiles(mmqt_zero_tiles(p.tp, x.M, N, x.K, Y), s);
             if (e != hipSuccess)
                 return e;
         }

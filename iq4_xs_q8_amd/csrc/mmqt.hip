@@ -526,6 +526,29 @@ MmqtPlan plan_tiles(int64_t M, int64_t N, int64_t K, int cus, int fmt, int64_t B
 // 256 x 128 tile at 512 x 17408 x 5120, where almost every tile has two
 // owners: 206 against 235 us for 128 x 128; with 128 x 256 at
 // 128 x 248320 x 5120: 674 against 753 us.)
+ZeroTiles mmqt_zero_tiles(const MmqtPlan &p, int64_t M, int64_t N, int64_t K, float *Y)
+{
+    static_assert(MAXZT == MAXG, "one shared tile per run boundary at most");
+    ZeroTiles zt;
+    if (!p.ok || !p.zero_y)
+        return zt;
+    zt.y = Y;
+    zt.M = M;
+    zt.N = N;
+    zt.bm = p.bm;
+    zt.bn = p.bn;
+    zt.mblocks = p.mblocks;
+    // the run bounds of launch_mmqt: a bound inside a tile makes it shared
+    // (runs of at least a tile: one bound per shared tile)
+    const int64_t nh = 2 * (K / QK), U = p.tiles * nh;
+    for (int g = 1; g < p.grid; g++) {
+        const int64_t u = U * g / p.grid;
+        if (u % nh != 0)
+            zt.t[zt.count++] = (int)(u / nh);
+    }
+    return zt;
+}
+
 MmqtPlan mmqt_plan(int64_t M, int64_t N, int64_t K, int cus, int fmt)
 {
     if (M >= 128) {

@@ -46,17 +46,40 @@ __device__ __forceinline__ void zero_range(float *yz, int64_t nz, int64_t tid, i
         yz[4 * n4 + tid] = 0.0f;
 }
 
+// The listed tiles of zt.y = 0 over a grid of `stride` threads (elements
+// past M or N skipped; fewer than 2^31 elements in all).
+__device__ __forceinline__ void zero_tiles(const ZeroTiles &zt, int64_t tid, int64_t stride)
+{
+    if (zt.count == 0)
+        return;
+    const int per = zt.bm * zt.bn;
+    for (int64_t e = tid; e < (int64_t)zt.count * per; e += stride) {
+        const int i = (int)(e / per), w = (int)(e - (int64_t)i * per);
+        const int t = zt.t[i];
+        const int64_t m = (int64_t)(t % zt.mblocks) * zt.bm + w / zt.bn;
+        const int64_t n = (int64_t)(t / zt.mblocks) * zt.bn + w % zt.bn;
+        if (m < zt.M && n < zt.N)
+            zt.y[m * zt.N + n] = 0.0f;
+    }
+}
+
 __device__ __forceinline__ void zero_list(const ZeroList &zl, int64_t tid, int64_t stride)
 {
 #pragma unroll
     for (int i = 0; i < MAXGRP; i++)
         if (i < zl.count)
             zero_range(zl.p[i], zl.n[i], tid, stride);
+    zero_tiles(zl.tiles, tid, stride);
 }
 
 __global__ void __launch_bounds__(256) k_zero(float *__restrict__ y, int64_t n)
 {
     zero_range(y, n, (int64_t)blockIdx.x * blockDim.x + threadIdx.x, (int64_t)gridDim.x * blockDim.x);
+}
+
+__global__ void __launch_bounds__(256) k_zero_tiles(ZeroTiles zt)
+{
+    zero_tiles(zt, (int64_t)blockIdx.x * blockDim.x + threadIdx.x, (int64_t)gridDim.x * blockDim.x);
 }
 
 // Elements 4t..4t+3 of block b of row m into the compensated bf16 planes
@@ -205,18 +228,34 @@ hipError_t launch_quantize(const float *X, void *Xq, const XPlanes *planes, int6
     return launch_quantize(X, Xq, planes, M, K, s, zl, xs);
 }
 
+hipError_t launch_zero_tiles(const ZeroTiles &zt, hipStream_t s)
+{
+    if (zt.count == 0)
+        return hipSuccess;
+    const int64_t n = (int64_t)zt.count * zt.bm * zt.bn;
+    const int64_t grid = std::min<int64_t>((n + 255) / 256, 4096);
+    hipLaunchKernelGGL(k_zero_tiles, dim3((unsigned)grid), dim3(256), 0, s, zt);
+    return hipGetLastError();
+}
+
 hipError_t launch_q8_1_convert(const void *Xq, const XPlanes *planes, int64_t M, int64_t K, hipStream_t s,
                               float *yz, int64_t nz, const XSplit *xs)
 {
-    const int64_t Mrows = xs ? xs->Ms : M;
-    const int64_t threads = Mrows * (K / 4);
-    const int64_t grid = (threads + 255) / 256;
     ZeroList zl;
     if (yz != nullptr && nz > 0) {
         zl.p[0] = yz;
         zl.n[0] = nz;
         zl.count = 1;
     }
+    return launch_q8_1_convert(Xq, planes, M, K, s, zl, xs);
+}
+
+hipError_t launch_q8_1_convert(const void *Xq, const XPlanes *planes, int64_t M, int64_t K, hipStream_t s,
+                              const ZeroList &zl, const XSplit *xs)
+{
+    const int64_t Mrows = xs ? xs->Ms : M;
+    const int64_t threads = Mrows * (K / 4);
+    const int64_t grid = (threads + 255) / 256;
     hipLaunchKernelGGL(k_q8_1_convert, dim3((unsigned)grid), dim3(256), 0, s, (const uint8_t *)Xq,
                        planes ? planes->qp : nullptr, planes ? planes->dp : nullptr,
                        zl, xs ? *xs : XSplit(), M, Mrows,
