@@ -158,7 +158,7 @@ int iq4xs_gemm_ws(const void *W, const float *X, float *Y, int64_t M, int64_t N,
  * Every call on one device uses that device's array and leaves its contents
  * behind: calls that overlap in time on one device (two streams, two threads)
  * race and give undefined results, so order them on one stream. */
-#define IQ4XS_STATIC_SCRATCH_BYTES (64u << 20)
+#define IQ4XS_STATIC_SCRATCH_BYTES (128u << 20)
 int iq4xs_gemm_noalloc(const void *W, const float *X, float *Y, int64_t M, int64_t N, int64_t K,
                        int path, void *stream);
 

@@ -241,7 +241,7 @@ def gemm(W: torch.Tensor, X: torch.Tensor, path: int = PATH_AUTO,
     return out
 
 
-STATIC_SCRATCH_BYTES = 64 << 20     # IQ4XS_STATIC_SCRATCH_BYTES
+STATIC_SCRATCH_BYTES = 128 << 20    # IQ4XS_STATIC_SCRATCH_BYTES
 
 
 def gemm_noalloc(W: torch.Tensor, X: torch.Tensor, out: torch.Tensor, path: int = PATH_AUTO) -> torch.Tensor:

@@ -117,14 +117,14 @@ struct FixRuns {
     int k[MAXG];
 };
 
-// Partial tile slot (run g, 0 = its first tile, 1 = its last): 8 float4 per
-// thread, float4 e of thread tid at [e][tid] (coalesced stores and loads);
-// e = 4*i + r/4 for accumulator i, result register r.  (Tiles with G = 2
-// only: the plan never gives the 256 x 128 tiles a workspace.)
-constexpr int SLOT_F4 = 8 * NTQ;
+// Partial tile slot (run g, 0 = its first tile, 1 = its last): 4*G float4
+// per thread, float4 e of thread tid at [e][tid] (coalesced stores and
+// loads); e = 4*i + r/4 for accumulator i, result register r.
+constexpr int slot_f4(int G) { return 4 * G * NTQ; }
+template <int G>
 __device__ __forceinline__ float4 *slot_at(float *ws, int g, int which)
 {
-    return reinterpret_cast<float4 *>(ws) + (size_t)(2 * g + which) * SLOT_F4;
+    return reinterpret_cast<float4 *>(ws) + (size_t)(2 * g + which) * slot_f4(G);
 }
 
 template <class C>
@@ -239,10 +239,10 @@ k_mmqt(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__re
                     if (m < M && n < N)
                         atomicAdd(Y + (int64_t)m * N + n, acc[i][r]);
                 }
-        } else if constexpr (GQ == 2) {
-            float4 *slot = slot_at(ws, g, t == t_first ? 0 : 1);
+        } else {
+            float4 *slot = slot_at<GQ>(ws, g, t == t_first ? 0 : 1);
 #pragma unroll
-            for (int i = 0; i < 2; i++)
+            for (int i = 0; i < GQ; i++)
 #pragma unroll
                 for (int q = 0; q < 4; q++)
                     slot[(4 * i + q) * NTQ + tid] =
@@ -414,7 +414,7 @@ k_mmqt_fix(const float *__restrict__ ws, float *__restrict__ Y, int M, int N, in
             v[q] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
             if (gg <= k && runs.u[gg] != runs.u[gg + 1])          // (uniform)
                 v[q] = (reinterpret_cast<const float4 *>(ws) +
-                        (size_t)(2 * gg + (runs.t[gg] == t ? 0 : 1)) * SLOT_F4)[e * NTQ + tid];
+                        (size_t)(2 * gg + (runs.t[gg] == t ? 0 : 1)) * slot_f4(C::G))[e * NTQ + tid];
         }
 #pragma unroll
         for (int q = 0; q < 8; q++) {
@@ -448,7 +448,7 @@ hipError_t launch_cfg(const void *W, const XPlanes &x, float *Y, float *ws, int6
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.workspace_bytes == 0)
         return e;
-    // one group of 8 workgroups per shared tile: the runs that start inside
+    // one group of 4*G workgroups per shared tile: the runs that start inside
     // their first tile and reach its end
     FixRuns fix;
     int nfix = 0;
@@ -460,7 +460,7 @@ hipError_t launch_cfg(const void *W, const XPlanes &x, float *Y, float *ws, int6
     }
     if (nfix == 0)
         return hipSuccess;
-    hipLaunchKernelGGL((k_mmqt_fix<C>), dim3((unsigned)nfix, 8), dim3(NTQ), 0, s, (const float *)ws, Y,
+    hipLaunchKernelGGL((k_mmqt_fix<C>), dim3((unsigned)nfix, 4 * C::G), dim3(NTQ), 0, s, (const float *)ws, Y,
                        (int)x.M, (int)N, nh, p.mblocks, runs, fix);
     return hipGetLastError();
 }
@@ -510,7 +510,7 @@ MmqtPlan plan_tiles(int64_t M, int64_t N, int64_t K, int cus, int fmt, int64_t B
             }
         p.workspace_bytes = 0;
     } else {
-        p.workspace_bytes = (size_t)p.grid * 2 * SLOT_F4 * sizeof(float4);
+        p.workspace_bytes = (size_t)p.grid * 2 * slot_f4((int)((BM / TILE) * (BN / TILE) / NWQ)) * sizeof(float4);
     }
     p.fmt = fmt;
     p.ok = true;
@@ -519,13 +519,6 @@ MmqtPlan plan_tiles(int64_t M, int64_t N, int64_t K, int cus, int fmt, int64_t B
 
 }  // namespace
 
-// The tiles with four activation subtiles per wavefront (128 x 256 from
-// M = 128, 256 x 128 from 256) wherever every run spans at least one of them
-// (no tile with more than two owners, so no workspace); else 64 x 256 up to
-// M = 64 and 128 x 128 above.  (Measured with the
-// 256 x 128 tile at 512 x 17408 x 5120, where almost every tile has two
-// owners: 206 against 235 us for 128 x 128; with 128 x 256 at
-// 128 x 248320 x 5120: 674 against 753 us.)
 ZeroTiles mmqt_zero_tiles(const MmqtPlan &p, int64_t M, int64_t N, int64_t K, float *Y)
 {
     static_assert(MAXZT == MAXG, "one shared tile per run boundary at most");
@@ -549,23 +542,34 @@ ZeroTiles mmqt_zero_tiles(const MmqtPlan &p, int64_t M, int64_t N, int64_t K, fl
     return zt;
 }
 
+// The tiles with four activation subtiles per wavefront (128 x 256 from
+// M = 128, 256 x 128 from 256), else 64 x 256 up to M = 64 and 128 x 128
+// above.  The larger tiles lose only where they need partial tiles summed
+// from a workspace, the smaller ones do not, and the runs are shorter than
+// a super-block (8 units): the summing then outweighs the lookups saved.
+// (Measured: 512 x 10240 x 5120, 25 units per run, 137 against 157 us;
+// 512 x 5120 x 1024, 4 units per run, 37.5 against 29.7 us; 512 x 17408 x
+// 5120 without a workspace, almost every tile with two owners, 206 against
+// 235 us; 256 x 17408 x 5120 with one, 118 against 136 us.)
 MmqtPlan mmqt_plan(int64_t M, int64_t N, int64_t K, int cus, int fmt)
 {
+    const MmqtPlan small =
+        M <= 2 * TILE ? plan_tiles(M, N, K, cus, fmt, 64, 256) : plan_tiles(M, N, K, cus, fmt, 128, 128);
     if (M >= 128) {
         const int64_t BM = M >= 256 ? 256 : 128, BN = 32768 / BM;
         const MmqtPlan big = plan_tiles(M, N, K, cus, fmt, BM, BN);
-        if (big.ok && big.workspace_bytes == 0)
+        const int64_t units_per_run = big.tiles * 2 * (K / QK) / std::max(big.grid, 1);
+        if (big.ok && (big.workspace_bytes == 0 || !small.ok || small.workspace_bytes != 0 || units_per_run >= 8))
             return big;
     }
-    return M <= 2 * TILE ? plan_tiles(M, N, K, cus, fmt, 64, 256) : plan_tiles(M, N, K, cus, fmt, 128, 128);
+    return small;
 }
 
 hipError_t launch_mmqt(const void *W, const XPlanes &x, float *Y, int64_t N, const MmqtPlan &p, void *workspace,
                        hipStream_t s)
 {
     const int cfg = p.bm == 64 ? 0 : p.bm == 128 && p.bn == 128 ? 1 : p.bm == 256 ? 2 : 3;
-    if (!p.ok || p.grid < 1 || p.grid > MAXG || (p.workspace_bytes && workspace == nullptr) ||
-        (cfg >= 2 && p.workspace_bytes))
+    if (!p.ok || p.grid < 1 || p.grid > MAXG || (p.workspace_bytes && workspace == nullptr))
         return hipErrorInvalidValue;
     if ((const char *)x.dp != (const char *)x.qp + x.Mp * x.K)
         return hipErrorInvalidValue;

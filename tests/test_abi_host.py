@@ -365,16 +365,16 @@ def test_calibrate_carries_the_compute_unit_count(tmp_path):
 def test_noalloc_rejects_shapes_beyond_the_static_scratch():
     """The allocation-free entry point refuses, on the host and before any
     HIP call, a shape whose scratch would not fit the static array."""
-    assert iq.STATIC_SCRATCH_BYTES == 64 << 20
+    assert iq.STATIC_SCRATCH_BYTES == 128 << 20
     text = open(HEADER).read()
-    assert re.search(r"#define IQ4XS_STATIC_SCRATCH_BYTES \(64u << 20\)", text)
-    # activation planes of 4096 x 17408 alone are 80 MB
+    assert re.search(r"#define IQ4XS_STATIC_SCRATCH_BYTES \(128u << 20\)", text)
+    # activation planes of 8192 x 17408 alone are 160 MB
     far = 1 << 44                     # fake addresses far apart: no overlap
-    assert L.iq4xs_gemm_noalloc(A, far, 2 * far, 4096, 8, 17408, iq.PATH_MMQ, None) == iq.EINVAL
+    assert L.iq4xs_gemm_noalloc(A, far, 2 * far, 8192, 8, 17408, iq.PATH_MMQ, None) == iq.EINVAL
     assert b"static scratch" in L.iq4xs_last_error()
-    # the bf16 paths' activation planes at 4096 x 17408: 285 MB
+    # the bf16 paths' activation planes at 8192 x 17408: 570 MB
     for p in (iq.PATH_DEQ_BF16, iq.PATH_BF16X3):
-        assert L.iq4xs_gemm_noalloc(A, far, 2 * far, 4096, 8, 17408, p, None) == iq.EINVAL
+        assert L.iq4xs_gemm_noalloc(A, far, 2 * far, 8192, 8, 17408, p, None) == iq.EINVAL
     assert b"static scratch" in L.iq4xs_last_error()
     # argument checks as iq4xs_gemm_path
     assert L.iq4xs_gemm_noalloc(None, A * 2, A * 4, 4, 8, 256, 0, None) == iq.EINVAL

@@ -190,7 +190,8 @@ def _check_invariants(Wd, W2d, Xd, path, what):
 # Every kernel and work split of the integer paths.  The tile-kernel cases
 # were chosen with the host plan's rules (grid size, run length, tile shape):
 # 64 x 256 tiles up to M = 64, 128 x 128 above, 128 x 256 from M = 128 and
-# 256 x 128 from M = 256 when every run spans a tile; "two owners": runs longer
+# 256 x 128 from M = 256 (unless only they would need a workspace, with runs
+# shorter than a super-block); "two owners": runs longer
 # than a tile, shared tiles added into a zeroed Y; "workspace": runs shorter
 # than a tile, 2..16 owners per tile summed in run order by the second kernel.
 INVARIANT_CASES = [
@@ -210,6 +211,8 @@ INVARIANT_CASES = [
     ("tile 256x128, two owners, ragged", iq.PATH_MMQ, 300, 65613, 256),
     ("tile 256x128, M=512", iq.PATH_MMQ, 512, 65536, 256),
     ("tile 128x256, two owners, ragged", iq.PATH_MMQ, 150, 65613, 256),
+    ("tile 256x128, workspace (3-4 owners)", iq.PATH_MMQ, 300, 5120, 5120),
+    ("tile 128x256, workspace (8 owners)", iq.PATH_MMQ, 130, 2000, 8192),
 ]
 
 

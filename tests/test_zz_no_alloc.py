@@ -75,7 +75,7 @@ def test_noalloc_matches_allocating_entry_point(pair):
 
 
 def test_noalloc_refuses_oversized_scratch_on_the_device():
-    M, N, K = 4096, 64, 17408          # activation planes alone: 80 MB > 64 MiB
+    M, N, K = 8192, 64, 17408          # activation planes alone: 160 MB > 128 MiB
     W = torch.zeros((N, K // 256 * 136), dtype=torch.uint8, device="cuda")
     X = torch.zeros((M, K), dtype=torch.float32, device="cuda")
     Y = poisoned((M, N))
