@@ -76,6 +76,16 @@ INT8_PEAK_TOPS = 5000.0         # MI355X dense int8 MFMA, published
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
 MALL_BYTES = 256 << 20
 PROBE_BYTES = 1 << 30           # calibration read / write of the profiling runs
+# launches per shape of the profiling runs: warm-up (the first few calls on
+# rotated weights run up to 30% slower), then the measured ones; the
+# summaries keep the measured ones
+PROFILE_WARM, PROFILE_RUNS = 10, 20
+PROFILE_GROUP = PROFILE_WARM + PROFILE_RUNS
+
+
+def _measured(seq):
+    """The measured launches of one kernel's launches in a profiling run."""
+    return seq[PROFILE_WARM:] if len(seq) >= PROFILE_GROUP else seq
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_mmv_decode_n10240_k5120_traffic.txt")
 TILE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_mmqt_tile_shapes_traffic.txt")
 KERNEL_SOURCES = {"k_mmv": ["mmv.hip", "common.hpp", "stream.hpp"], "k_gemv": ["gemv.hip", "common.hpp"],
@@ -579,9 +589,9 @@ def _probe_pair():
 
 
 def profile_run():
-    """Fixed launches for rocprofv3 --pmc: per M of the decode sweep, 20
-    launches of the matmul kernel alone (rotated weights, as in the timed
-    step), then the calibration probes."""
+    """Fixed launches for rocprofv3: per M of the decode sweep, PROFILE_WARM
+    then PROFILE_RUNS launches of the matmul kernel alone (rotated weights, as
+    in the timed step), then the calibration probes."""
     wl = synth.DECODE_ATTN
     (N, K), ms = wl.shapes[0], wl.ms
     rot = Rotation(wl.w(N, K))
@@ -590,10 +600,10 @@ def profile_run():
         act = iq.prepare_act(X)
         Y = torch.zeros((M, N), dtype=torch.float32, device="cuda")
         path = iq.dispatch(M, N, K)
-        for _ in range(20):
+        for _ in range(PROFILE_GROUP):
             iq.gemm_act(rot.next(), act, M, K, path=path, out=Y, y_zeroed=True)
         torch.cuda.synchronize()
-        print(f"[profile-run] M={M} {kernel_name(M, N, K, path)} x20", flush=True)
+        print(f"[profile-run] M={M} {kernel_name(M, N, K, path)} x{PROFILE_GROUP}", flush=True)
     del rot
     torch.cuda.empty_cache()
     _probe_pair()
@@ -601,7 +611,7 @@ def profile_run():
 
 def profile_shapes(specs):
     """Fixed launches for rocprofv3 at given shapes ("MxNxK", comma
-    separated): per shape, 20 launches of the matmul kernel(s) alone
+    separated): per shape, PROFILE_WARM then PROFILE_RUNS launches of the matmul kernel(s) alone
     (gemm_act, rotated weights), inputs of the workload the shape belongs to
     (else the prefill recipe); then the calibration probes.  "MxNxK:PATH"
     forces a path and launches whole calls (for the paths gemm_act does not
@@ -616,15 +626,15 @@ def profile_shapes(specs):
         if pname:
             path = iq.PATHS[pname]
             ws = torch.empty(iq.workspace_bytes(M, N, K, path), dtype=torch.uint8, device="cuda")
-            for _ in range(20):
+            for _ in range(PROFILE_GROUP):
                 iq.gemm(rot.next(), X, path=path, out=Y, workspace=ws)
         else:
             act = iq.prepare_act(X)
             path = iq.dispatch(M, N, K)
-            for _ in range(20):
+            for _ in range(PROFILE_GROUP):
                 iq.gemm_act(rot.next(), act, M, K, path=path, out=Y)
         torch.cuda.synchronize()
-        print(f"[profile-shapes] M={M} N={N} K={K} {kernel_name(M, N, K, path)} x20", flush=True)
+        print(f"[profile-shapes] M={M} N={N} K={K} {kernel_name(M, N, K, path)} x{PROFILE_GROUP}", flush=True)
         del rot
         torch.cuda.empty_cache()
     _probe_pair()
@@ -673,9 +683,13 @@ def summarize_pmc(fetch_dir, write_dir, out, cmd_fetch, cmd_write):
             if key is None:
                 continue
             label = name.split("Cfg<")[1].split(">")[0].replace(" ", "") if "Cfg<" in name else ""
-            acc.setdefault((key, label), {}).setdefault(r["Dispatch_Id"], 0.0)
-            acc[(key, label)][r["Dispatch_Id"]] += float(r["Counter_Value"])
-        return {k: sum(v.values()) / len(v) for k, v in acc.items()}
+            acc.setdefault((key, label), {}).setdefault(int(r["Dispatch_Id"]), 0.0)
+            acc[(key, label)][int(r["Dispatch_Id"])] += float(r["Counter_Value"])
+        out = {}
+        for k, v in acc.items():
+            vals = _measured([v[i] for i in sorted(v)])
+            out[k] = sum(vals) / len(vals)
+        return out
     fk, wk, f_scale, w_scale = _probe_scales(fr, wr)
     fetch, write = per_kernel(fr, "FETCH_SIZE"), per_kernel(wr, "WRITE_SIZE")
     wl = synth.DECODE_ATTN
@@ -727,18 +741,22 @@ def summarize_fused(trace_dir, fetch_dir, write_dir, out, cmds, spec):
         acc = {}
         for r in rows:
             if r["Counter_Name"] == counter and kern in r["Kernel_Name"]:
-                acc[r["Dispatch_Id"]] = acc.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
-        return sum(acc.values()) / len(acc) if acc else float("nan")
+                i = int(r["Dispatch_Id"])
+                acc[i] = acc.get(i, 0.0) + float(r["Counter_Value"])
+        vals = _measured([acc[i] for i in sorted(acc)])
+        return sum(vals) / len(vals) if vals else float("nan")
     f_kib, w_kib = per_launch(fr, "FETCH_SIZE"), per_launch(wr, "WRITE_SIZE")
     traffic = f_kib * 1024.0 * f_scale + w_kib * 1024.0 * w_scale
     ms_rows = -(-M // 256) * 256
     act = 4.0 if x3 else 2.0
     algo = 0.53125 * N * K + act * ms_rows * K + 4.0 * M * N
     flops = (6.0 if x3 else 2.0) * M * N * K
+    durs = {k: _measured(v) for k, v in durs.items()}
     d = durs.get(kern, [float("nan")])
     avg = sum(d) / len(d)
     title = "compensated-bf16 kernel (BF16X3 path)" if x3 else "plain bf16 kernel (DEQ_BF16 path)"
-    lines = [f"# fused {title}, M={M} N={N} K={K}: kernel trace and HBM counters (20 whole calls, rotated weights)",
+    lines = [f"# fused {title}, M={M} N={N} K={K}: kernel trace and HBM counters ({PROFILE_RUNS} whole calls "
+             f"after {PROFILE_WARM} of warm-up, rotated weights)",
              *[f"# command: {c}" for c in cmds],
              f"source_hash {kern} {source_hash(kern)}",
              f"# calibration by the runs' own probes ({PROBE_BYTES} bytes read / written): fetch x{f_scale:.4f}, "
@@ -758,7 +776,8 @@ def summarize_fused(trace_dir, fetch_dir, write_dir, out, cmds, spec):
 
 
 def summarize_pmc_shapes(fetch_dir, write_dir, out, cmd_fetch, cmd_write, specs):
-    """Per shape of a --profile-shapes run (20 launches each, in order): mean
+    """Per shape of a --profile-shapes run (PROFILE_GROUP launches each, in
+    order, the first PROFILE_WARM left out): mean
     FETCH_SIZE / WRITE_SIZE per launch of the tile kernel and of its
     shared-tile kernel, calibrated by the probes of the same runs, against
     the algorithmic bytes."""
@@ -774,7 +793,8 @@ def summarize_pmc_shapes(fetch_dir, write_dir, out, cmd_fetch, cmd_write, specs)
         return acc
     fd, wd = per_dispatch(fr, "FETCH_SIZE"), per_dispatch(wr, "WRITE_SIZE")
     shapes = [tuple(int(v) for v in sp.split("x")) for sp in specs.split(",")]
-    lines = ["# HBM traffic per launch of the tile kernel from rocprofv3 counters (20 launches per shape)",
+    lines = [f"# HBM traffic per launch of the tile kernel from rocprofv3 counters ({PROFILE_RUNS} launches per "
+             f"shape after {PROFILE_WARM} of warm-up)",
              f"# fetch run: {cmd_fetch}", f"# write run: {cmd_write}",
              f"# calibration by the runs' own probes ({PROBE_BYTES} bytes read / written): "
              f"fetch x{f_scale:.4f} ({fk:.1f} KiB counted), write x{w_scale:.4f} ({wk:.1f} KiB counted)",
@@ -785,7 +805,9 @@ def summarize_pmc_shapes(fetch_dir, write_dir, out, cmd_fetch, cmd_write, specs)
     for (i, part) in sorted(set(fd) | set(wd)):
         if part == "main":
             n_main += 1
-        shape = n_main // 20
+        shape = n_main // PROFILE_GROUP
+        if n_main % PROFILE_GROUP < PROFILE_WARM:
+            continue
         acc = sums.setdefault((shape, part), [0.0, 0.0, 0])
         acc[0] += fd.get((i, part), 0.0)
         acc[1] += wd.get((i, part), 0.0)
@@ -842,10 +864,10 @@ SQ_PASSES = (("SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_
 
 def _sq_key(name, order, shapes):
     """Kernel label; the tile kernel's launches of a --profile-shapes run
-    (20 per shape, in order) also carry their shape."""
+    (PROFILE_GROUP per shape, in order) also carry their shape."""
     key = name.replace("void ", "").replace("iq4xs::(anonymous namespace)::", "").split("(")[0]
     if shapes and "k_mmqt<" in key and order is not None:
-        i = order // 20
+        i = order // PROFILE_GROUP
         if i < len(shapes):
             key += " [M=%d N=%d K=%d]" % shapes[i]
     return key
@@ -887,7 +909,9 @@ def summarize_sq(dirs, trace_dirs, out, cmds, specs=""):
         order = _tile_order(rows, "Dispatch_Id")
         for r in rows:
             key = _sq_key(r["Kernel_Name"], order.get(int(r["Dispatch_Id"])), shapes)
-            dur.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+            dur.setdefault(key, []).append((int(r["Start_Timestamp"]), (int(r["End_Timestamp"]) -
+                                                                          int(r["Start_Timestamp"])) * 1e-3))
+    dur = {k: _measured([d for _, d in sorted(v)]) for k, v in dur.items()}
     lines = ["# SQ counters per dispatch (averages), matmul and quantize kernels of the decode sweep and the tile shapes",
              *[f"# run: {c}" for c in cmds],
              "# VALU/MFMA: instructions; LDS-conflict: bank-conflict cycles per LDS instruction; VALU-issue and "
@@ -895,7 +919,10 @@ def summarize_sq(dirs, trace_dirs, out, cmds, specs=""):
              "# kernel | " + " ".join(c for p_ in SQ_PASSES for c in p_) +
              " | VALU/MFMA  LDS-conflict  trace-us  VALU-issue  MFMA-busy | clock-GHz  VALU-issue  MFMA-busy  sum"]
     for key in sorted(per):
-        v = {c: sum(d.values()) / len(d) for c, d in per[key].items()}
+        v = {}
+        for c, d in per[key].items():
+            vals = _measured([d[i] for i in sorted(d, key=int)])
+            v[c] = sum(vals) / len(vals)
         vals = " ".join(f"{v.get(c, float('nan')):.4g}" for p_ in SQ_PASSES for c in p_)
         valu, mfma = v.get("SQ_INSTS_VALU", 0.0), v.get("SQ_INSTS_MFMA", 0.0)
         lds, conf = v.get("SQ_INSTS_LDS", 0.0), v.get("SQ_LDS_BANK_CONFLICT", 0.0)
@@ -914,31 +941,40 @@ def summarize_sq(dirs, trace_dirs, out, cmds, specs=""):
 
 
 def summarize_trace(trace_dir, out, cmd, title):
-    """The kernel-trace statistics of a rocprofv3 --stats run as a short text
-    table (kernel, calls, average / min / max microseconds, share of GPU
-    time)."""
-    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    """The kernel trace of a rocprofv3 run as a short text table (kernel,
+    calls, average / min / max microseconds, share of GPU time), the
+    warm-up launches of each matmul kernel left out."""
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
     if not files:
-        raise SystemExit(f"no kernel_stats.csv under {trace_dir}")
+        raise SystemExit(f"no kernel_trace.csv under {trace_dir}")
     with open(files[0]) as fh:
-        rows = list(csv.DictReader(fh))
+        rows = sorted(csv.DictReader(fh), key=lambda r: int(r["Start_Timestamp"]))
 
     def short(name):
-        name = name.replace("iq4xs::(anonymous namespace)::", "").replace("iq4xs::", "")
+        name = name.replace("void ", "").replace("iq4xs::(anonymous namespace)::", "").replace("iq4xs::", "")
         return name.replace("(anonymous namespace)::", "").split("(")[0]
+    per = {}
+    for r in rows:
+        per.setdefault(short(r["Kernel_Name"]), []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+    per = {k: (_measured(v) if k.startswith(("k_mmv", "k_gemv", "k_mmqt", "k_mmq", "k_gemm")) else v)
+           for k, v in per.items()}
+    total = sum(sum(v) for v in per.values())
     lines = [f"# rocprofv3 kernel-trace statistics: {title}", f"# command: {cmd}",
+             f"# matmul kernels: the last {PROFILE_RUNS} of each {PROFILE_GROUP} launches (warm-up left out)",
              f"{'kernel':60s} {'calls':>6s} {'avg_us':>8s} {'min_us':>8s} {'max_us':>8s} {'pct':>6s}"]
-    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
-        lines.append(f"{short(r['Name'])[:60]:60s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:8.2f} "
-                     f"{float(r['MinNs']) / 1e3:8.2f} {float(r['MaxNs']) / 1e3:8.2f} {float(r['Percentage']):6.2f}")
+    for k, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"{k[:60]:60s} {len(v):6d} {sum(v) / len(v):8.2f} {min(v):8.2f} {max(v):8.2f} "
+                     f"{100.0 * sum(v) / total:6.2f}")
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
 def summarize_trace_shapes(trace_dir, out, cmd, specs):
-    """Per shape of a --profile-shapes kernel trace (20 launches per shape,
-    in order): the tile kernel's and its summing kernel's durations."""
+    """Per shape of a --profile-shapes kernel trace (PROFILE_GROUP launches per
+    shape, in order, the first PROFILE_WARM left out): the tile kernel's and
+    its summing kernel's durations."""
     files = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
     if not files:
         raise SystemExit(f"no kernel_trace.csv under {trace_dir}")
@@ -952,9 +988,13 @@ def summarize_trace_shapes(trace_dir, out, cmd, specs):
         part = "k_mmqt_fix" if "k_mmqt_fix" in name else "k_mmqt"
         if part == "k_mmqt":
             n_main += 1
-        per.setdefault((n_main // 20, part), []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
-    lines = ["# tile-kernel durations per shape from a rocprofv3 kernel trace (20 launches per shape, gemm_act, "
-             "rotated weights)", f"# command: {cmd}", f"source_hash k_mmqt {source_hash('k_mmqt')}",
+        if n_main % PROFILE_GROUP < PROFILE_WARM:
+            continue
+        per.setdefault((n_main // PROFILE_GROUP, part), []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+    lines = [f"# tile-kernel durations per shape from a rocprofv3 kernel trace ({PROFILE_RUNS} launches per shape "
+             f"after {PROFILE_WARM} of warm-up, gemm_act, rotated weights)", f"# command: {cmd}",
+             f"source_hash k_mmqt {source_hash('k_mmqt')}",
              "# M N K  kernel  calls  avg_us  min_us  max_us"]
     for (i, part), d in sorted(per.items()):
         if i < len(shapes):
