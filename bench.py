@@ -55,6 +55,7 @@ import argparse
 import csv
 import glob
 import hashlib
+import re
 import json
 import math
 import os
@@ -116,10 +117,15 @@ def kernel_name(M, N, K, path):
 
 
 def source_hash(kernel):
+    """Hash of a kernel's source files with comments and whitespace taken out,
+    so that a profile stays valid across edits of the comments only."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, "iq4_xs_q8_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "iq4_xs_q8_amd", "csrc", f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

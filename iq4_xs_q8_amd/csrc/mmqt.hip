@@ -1,5 +1,6 @@
 // mmqt.hip -- IQ4_XS x Q8_1 for many activation rows (M > 32) on the int8
-// matrix cores: 128 x 128 output tiles, each output owned by one wavefront.
+// matrix cores: output tiles of BM activation rows x BN weight rows, each
+// output owned by one wavefront.
 //
 // Arithmetic (batched IQ4_XS kernel section of the "V100TPS engine log",
 // agent-report.daedalus.work/V100TPS/engine.html): per 32-element sub-block
@@ -11,34 +12,35 @@
 // MFMA measured faster.)
 //
 // Work split:
-//  * Output tiles are 128 activation rows (4 MFMA subtiles) x 128 weight rows
-//    (4 subtiles), ordered with the activation block fastest.  Units are
-//    (tile, half super-block), tile-major; each workgroup gets one contiguous
-//    run of equal length (stream-K style: every compute unit gets the same
-//    work, also when there are fewer tiles than compute units).  A tile
-//    covered by one run is stored by its workgroup.  When every run covers
-//    at least a tile's units, a tile has two owners at most and they add
-//    into a Y zeroed beforehand (0 + a + b == 0 + b + a); otherwise the
-//    owners store their partial tiles (at most two per run: its first and
-//    its last) in a workspace, and a second kernel adds the partials of every
-//    shared tile in run order.  Either way the result does not depend on
-//    timing.
+//  * Tiles (see QCfg): 64 x 256 up to M = 64, 128 x 128 above, and 256 x 128
+//    (M >= 256) or 128 x 256 (M >= 128) where those larger tiles need no
+//    summing of many partial tiles.  Tiles are ordered with the activation
+//    block fastest.  Units are (tile, half super-block), tile-major; each
+//    workgroup gets one contiguous run of equal length (stream-K style:
+//    every compute unit gets the same work, also when there are fewer tiles
+//    than compute units).  A tile covered by one run is stored by its
+//    workgroup.  When every run covers at least a tile's units, a tile has
+//    two owners at most and they add into a Y whose shared tiles were zeroed
+//    beforehand (0 + a + b == 0 + b + a); otherwise the owners store their
+//    partial tiles (at most two per run: its first and its last) in a
+//    workspace, and a second kernel adds the partials of every shared tile
+//    in run order.  Either way the result does not depend on timing.
 //  * Half a super-block of a tile at a time (4 sub-blocks) goes straight
-//    from memory into one of five LDS buffers with 16-byte LDS-writing buffer
-//    loads: for each of the BN weight rows its header and the half's 64 index
-//    bytes (an 80-byte LDS row), the BM activation rows of the 4 sub-blocks
-//    (sub-block-major planes) and their scales.  The loads of a half run four
-//    halves ahead of its use, so the memory system always has about 90 KB per
-//    compute unit in flight; one barrier per half.  (A wavefront that walked
-//    the run ahead touching whole weight rows, to turn the 72-byte pieces
-//    into long contiguous reads, made every measured shape 4-9% slower: it
-//    arrived last at every barrier.)
-//  * Eight wavefronts: wavefront w owns weight subtile w%(BN/32) and the
-//    activation subtile pair w/(BN/32), i.e. 2 x 16 accumulators per lane.  Per
-//    sub-block it expands its weight subtile's index bytes once (byte
-//    permutes) and uses them for both activation subtiles, so the fp32
-//    rescale of the integer dots (three VALU operations per output and
-//    sub-block) is the bulk of the work.
+//    from memory into one of NBUF LDS buffers (5, or 3 for the larger tiles)
+//    with 16-byte LDS-writing buffer loads: for each of the BN weight rows
+//    its header and the half's 64 index bytes (an 80-byte LDS row), the BM
+//    activation rows of the 4 sub-blocks (sub-block-major planes) and their
+//    scales.  The loads of a half run NBUF-1 halves ahead of its use; one
+//    barrier per half.  (A wavefront that walked the run ahead touching
+//    whole weight rows, to turn the 72-byte pieces into long contiguous
+//    reads, made every measured shape 4-9% slower: it arrived last at every
+//    barrier.)
+//  * Eight wavefronts: wavefront w owns weight subtile w%(BN/32) and a group
+//    of G activation subtiles w/(BN/32) (G = 2, or 4 for the larger tiles),
+//    i.e. G x 16 accumulators per lane.  Per sub-block it expands its weight
+//    subtile's index bytes once (byte permutes) and uses them for all G
+//    activation subtiles, so the fp32 rescale of the integer dots (three
+//    VALU operations per output and sub-block) is the bulk of the work.
 #include "common.hpp"
 #include "stream.hpp"
 
@@ -58,20 +60,19 @@ constexpr int HALF = SUBS / 2;             // sub-blocks per step
 constexpr int WROWQ = 80;                  // LDS weight row: header, 8 unused, 64 index bytes
 constexpr int NLQ = NWQ;                   // copying wavefronts
 
-// Output tile BM activation rows x BN weight rows: 128 x 128 or 64 x 256
-// (M <= 64), or, where every stream-K run spans a whole tile, 256 x 128 or
-// 128 x 256.  Wavefront w owns weight
+// Output tile BM activation rows x BN weight rows: 64 x 256, 128 x 128,
+// 256 x 128 or 128 x 256 (mmqt_plan picks one).  Wavefront w owns weight
 // subtile w % (BN/32) and the group of G activation subtiles w / (BN/32):
 // G = 2, or 4 for the two large tiles, where each wavefront's codebook lookup
 // serves four activation subtiles (half the lookup work per output; the
-// rescale, three VALU instructions per output, is the rest).  One LDS buffer: weights
-// [BN][80], activations [HALF][BM][32], scales [HALF][BM], 1 KB for slots
-// without a job; NBUF buffers (5, or 3 for the larger tile).  F: the weight
-// format.  An 80-byte weight row holds, for IQ4_XS, the super-block's
-// 8 header bytes, 8 unused bytes and the half's 64 index bytes; for IQ4_NL
-// and Q4_0, bytes [0, 80) of the 144-byte unit for the first half and
-// [64, 144) for the second (its four 18-byte blocks at 8 + 18s), so that no
-// copy reaches past the unit.
+// rescale, three VALU instructions per output, is the rest).  One LDS
+// buffer: weights [BN][80], activations [HALF][BM][32], scales [HALF][BM],
+// 1 KB for slots without a job; NBUF buffers (5, or 3 for the large tiles).
+// F: the weight format.  An 80-byte weight row holds, for IQ4_XS, the
+// super-block's 8 header bytes, 8 unused bytes and the half's 64 index
+// bytes; for IQ4_NL and Q4_0, bytes [0, 80) of the 144-byte unit for the
+// first half and [64, 144) for the second (its four 18-byte blocks at
+// 8 + 18s), so that no copy reaches past the unit.
 template <int BM_, int BN_, int F_ = FMT_IQ4_XS>
 struct QCfg {
     static constexpr int BM = BM_, BN = BN_, NTW = BN / TILE, F = F_;
