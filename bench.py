@@ -164,6 +164,25 @@ class Rotation:
         return w
 
 
+def time_graph(fn, reps, stream):
+    """ms per call of `reps` calls of fn captured in one HIP graph and
+    replayed (no host launch gaps between short kernels)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        fn()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    g.replay()
+    t = time_events(g.replay, 3, stream) / reps
+    del g
+    return t
+
+
 def time_events(fn, reps, stream):
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
@@ -329,7 +348,8 @@ def probes(reps=10):
     stream reads of 28 MB (one decode-shape weight matrix), 95 MB and 1 GiB,
     each buffer rotated with others so that >= 768 MB lie between two reads
     of it (the Infinity Cache holds 256 MB); a 1 GiB stream write; and
-    back-to-back int8 and bf16 MFMA instructions on every SIMD."""
+    back-to-back int8 and bf16 MFMA instructions on every SIMD.  Reads and
+    writes are replayed from a HIP graph, as the matmul calls are."""
     stream = torch.cuda.current_stream()
     sink = torch.empty(65536, dtype=torch.int32, device="cuda")
     out = {"read": [], "write": None, "mfma": {}}
@@ -343,13 +363,13 @@ def probes(reps=10):
             k[0] += 1
         for _ in range(n):
             rd()
-        t = time_events(rd, reps * n if nbytes < (1 << 30) else reps, stream)
+        t = time_graph(rd, reps * n if nbytes < (1 << 30) else reps, stream)
         out["read"].append({"bytes": nbytes, "ms": t, "GBs": nbytes / (t * 1e-3) / 1e9,
                             "frac_of_8TBs": nbytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, "buffers": n})
         del bufs
     buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     iq.probe_write(buf)
-    t = time_events(lambda: iq.probe_write(buf), reps, stream)
+    t = time_graph(lambda: iq.probe_write(buf), reps, stream)
     out["write"] = {"bytes": 1 << 30, "ms": t, "GBs": (1 << 30) / (t * 1e-3) / 1e9}
     del buf
     torch.cuda.empty_cache()
