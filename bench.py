@@ -383,6 +383,21 @@ def probes(reps=10):
         rate = grid * 4 * 4 * iters * flops / (t * 1e-3) / 1e12
         out["mfma"][name] = {"T_per_s": rate, "published_peak": peak, "frac": rate / peak,
                              "instructions_per_wave": 4 * iters, "waves": grid * 4}
+    # matrix-core and vector-ALU work on the same SIMDs (one workgroup of
+    # eight wavefronts per compute unit; 2 MFMAs and 96 FMAs per iteration)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    mixo = torch.empty(cus * 512, dtype=torch.int32, device="cuda")
+    t = {}
+    for mode, name in ((iq.PROBE_MIX_MFMA, "mfma"), (iq.PROBE_MIX_VALU, "valu"), (iq.PROBE_MIX_SAME, "same"),
+                       (iq.PROBE_MIX_SPLIT, "split")):
+        iq.probe_mix(mode, 10, mixo, cus)
+        t[name] = time_events(lambda: iq.probe_mix(mode, 1000, mixo, cus), 3, stream)
+    out["mfma_beside_valu"] = {
+        "ms": t, "iterations": 1000, "per_iteration": "2 v_mfma_i32_32x32x32_i8 + 96 v_fma_f32",
+        # 1.0: the two kinds of work add up; 0.5 (same) would be full overlap
+        "same_over_sum": t["same"] / (t["mfma"] + t["valu"]),
+        # each SIMD gets half of 'same': 1.0 = adds up, max/sum = full overlap
+        "split_over_half_sum": t["split"] / (0.5 * (t["mfma"] + t["valu"]))}
     return out
 
 

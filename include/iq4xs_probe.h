@@ -39,6 +39,23 @@ int iq4xs_probe_write(void *dst, size_t nbytes, uint32_t value, int grid, void *
 #define IQ4XS_PROBE_MFMA_BF16 1
 int iq4xs_probe_mfma(int kind, int iters, void *out, int grid, void *stream);
 
+/* Matrix-core and vector-ALU work on the same SIMDs: `grid` workgroups of
+ * 512 threads (eight wavefronts, two per SIMD when one workgroup runs per
+ * compute unit).  Each iteration of `iters` holds 2 independent
+ * v_mfma_i32_32x32x32_i8 and 96 independent v_fma_f32: 48 VALU operations
+ * per MFMA, the mix of the int8 tile kernel's rescale (16 outputs of a
+ * lane per MFMA, three VALU operations each).  mode IQ4XS_PROBE_MIX_MFMA: every wavefront issues only the
+ * MFMAs; _VALU: only the FMAs; _SAME: both, in every wavefront; _SPLIT: the
+ * two wavefronts of a SIMD split them (one the MFMAs, the other the FMAs), so
+ * that each SIMD gets half of _SAME's work.  One value per thread is written
+ * to out[0..grid*512) (int32).  The ratio of _SAME to _MFMA + _VALU says
+ * whether the two kinds of work overlap on a SIMD. */
+#define IQ4XS_PROBE_MIX_MFMA 0
+#define IQ4XS_PROBE_MIX_VALU 1
+#define IQ4XS_PROBE_MIX_SAME 2
+#define IQ4XS_PROBE_MIX_SPLIT 3
+int iq4xs_probe_mix(int mode, int iters, void *out, int grid, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

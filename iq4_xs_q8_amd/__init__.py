@@ -43,8 +43,9 @@ EXPORTS = ("iq4xs_weight_bytes", "iq4xs_q8_1_bytes", "iq4xs_init", "iq4xs_quanti
 
 
 # measurement kernels (include/iq4xs_probe.h)
-PROBE_EXPORTS = ("iq4xs_probe_read", "iq4xs_probe_write", "iq4xs_probe_mfma")
+PROBE_EXPORTS = ("iq4xs_probe_read", "iq4xs_probe_write", "iq4xs_probe_mfma", "iq4xs_probe_mix")
 PROBE_MFMA_I8, PROBE_MFMA_BF16 = 0, 1
+PROBE_MIX_MFMA, PROBE_MIX_VALU, PROBE_MIX_SAME, PROBE_MIX_SPLIT = 0, 1, 2, 3
 
 
 class Iq4xsError(RuntimeError):
@@ -87,6 +88,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "iq4xs_probe_read": [p, ctypes.c_size_t, p, i32, p],
         "iq4xs_probe_write": [p, ctypes.c_size_t, ctypes.c_uint32, i32, p],
         "iq4xs_probe_mfma": [i32, i32, p, i32, p],
+        "iq4xs_probe_mix": [i32, i32, p, i32, p],
     })
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -432,3 +434,11 @@ def probe_mfma(kind: int, iters: int, out: torch.Tensor, grid: int) -> None:
     dt = torch.int32 if kind == PROBE_MFMA_I8 else torch.float32
     with _on(out):
         _probe_check(_L().iq4xs_probe_mfma(kind, iters, _dev(out, dt, "out"), grid, _stream(out)), "probe_mfma")
+
+
+def probe_mix(mode: int, iters: int, out: torch.Tensor, grid: int) -> None:
+    """Matrix-core beside vector-ALU work (PROBE_MIX_*); out: int32, grid * 512 elements."""
+    _at_least(out, "out", 4 * 512 * grid)
+    with _on(out):
+        _probe_check(_L().iq4xs_probe_mix(mode, iters, _dev(out, torch.int32, "out"), grid, _stream(out)),
+                     "probe_mix")

@@ -1,6 +1,7 @@
 // probe.hip -- measurement kernels (include/iq4xs_probe.h): what this device
-// sustains for a plain stream read, a plain stream write, and back-to-back
-// int8 and bf16 matrix-core instructions.  The matmul's rooflines are quoted
+// sustains for a plain stream read, a plain stream write, back-to-back
+// int8 and bf16 matrix-core instructions, and matrix-core beside vector-ALU
+// work on the same SIMDs.  The matmul's rooflines are quoted
 // against the published peaks; these give the achievable figures beside them
 // ("V100TPS engine log", opening section: a bytes-moved / time check against
 // the card's peak exposes a kernel that did not run).  They also calibrate
@@ -115,6 +116,55 @@ __global__ void __launch_bounds__(PT) k_probe_mfma_bf16(int iters, float *__rest
     out[(size_t)blockIdx.x * PT + threadIdx.x] = s;
 }
 
+// MODE: 0 MFMAs only, 1 FMAs only, 2 both in every wavefront, 3 split
+// between the two wavefronts of a SIMD (waves w and w+4 of the workgroup,
+// which the compute unit places on the same SIMD).
+template <int MODE>
+__global__ void __launch_bounds__(512) k_probe_mix(int iters, int *__restrict__ out)
+{
+    constexpr int NV = 96;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool dm = MODE == 0 || MODE == 2 || (MODE == 3 && ((wave >> 2) & 1) == 0);
+    const bool dv = MODE == 1 || MODE == 2 || (MODE == 3 && ((wave >> 2) & 1) == 1);
+    const v4i a = {lane, lane + 1, lane * 3, 7};
+    const v4i b = {1, lane, 2, lane ^ 5};
+    v16i c0 = {0}, c1 = {0};
+    float f[NV];
+#pragma unroll
+    for (int j = 0; j < NV; j++)
+        f[j] = 1.0f + 0.001f * (float)(lane + j);
+    const float x = 0.999f + 1e-6f * (float)lane, y = 1e-3f;
+    for (int i = 0; i < iters; i++) {
+        if (dm) {                                              // (uniform)
+            c0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c0, 0, 0, 0);
+            c1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(b, a, c1, 0, 0, 0);
+        }
+        if (dv) {
+#pragma unroll
+            for (int j = 0; j < NV; j++)
+                f[j] = __builtin_fmaf(f[j], x, y);
+        }
+    }
+    int s = 0;
+#pragma unroll
+    for (int r = 0; r < 16; r++)
+        s += c0[r] ^ c1[r];
+    // 96 KB of LDS (never used: iters >= 1) so that one workgroup runs per
+    // compute unit, two wavefronts per SIMD
+    __shared__ int hold[96 * 256];
+    if (iters < 0) {
+        hold[tid] = s;
+        __syncthreads();
+        s += hold[(tid + 1) & 511];
+    }
+    float t = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NV; j++)
+        t += f[j];
+    out[(size_t)blockIdx.x * 512 + tid] = s + (int)t;
+}
+
 int launch_status(void)
 {
     const hipError_t e = hipGetLastError();
@@ -156,6 +206,22 @@ int iq4xs_probe_mfma(int kind, int iters, void *out, int grid, void *stream)
                            (float *)out);
     else
         return -1;
+    return launch_status();
+}
+
+int iq4xs_probe_mix(int mode, int iters, void *out, int grid, void *stream)
+{
+    if (!out || iters < 1 || grid < 1 || grid > 65536 || ((uintptr_t)out % 4) || mode < IQ4XS_PROBE_MIX_MFMA ||
+        mode > IQ4XS_PROBE_MIX_SPLIT)
+        return -1;
+    const hipStream_t s = (hipStream_t)stream;
+    int *o = (int *)out;
+    switch (mode) {
+    case IQ4XS_PROBE_MIX_MFMA: hipLaunchKernelGGL(k_probe_mix<0>, dim3((unsigned)grid), dim3(512), 0, s, iters, o); break;
+    case IQ4XS_PROBE_MIX_VALU: hipLaunchKernelGGL(k_probe_mix<1>, dim3((unsigned)grid), dim3(512), 0, s, iters, o); break;
+    case IQ4XS_PROBE_MIX_SAME: hipLaunchKernelGGL(k_probe_mix<2>, dim3((unsigned)grid), dim3(512), 0, s, iters, o); break;
+    default: hipLaunchKernelGGL(k_probe_mix<3>, dim3((unsigned)grid), dim3(512), 0, s, iters, o); break;
+    }
     return launch_status();
 }
 

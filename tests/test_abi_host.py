@@ -49,6 +49,19 @@ def test_probe_arguments_checked_on_the_host():
     assert L.iq4xs_probe_write(A, 0, 1, 1, None) == -1
     assert L.iq4xs_probe_mfma(7, 1, A, 1, None) == -1
     assert L.iq4xs_probe_mfma(0, 0, A, 1, None) == -1
+    assert L.iq4xs_probe_mix(4, 1, A, 1, None) == -1
+    assert L.iq4xs_probe_mix(-1, 1, A, 1, None) == -1
+    assert L.iq4xs_probe_mix(0, 0, A, 1, None) == -1
+    assert L.iq4xs_probe_mix(0, 1, None, 1, None) == -1
+    assert L.iq4xs_probe_mix(0, 1, A, 0, None) == -1
+
+
+def test_probe_constants_match_binding():
+    text = open(os.path.join(ROOT, "include", "iq4xs_probe.h")).read()
+    consts = dict((k, int(v)) for k, v in re.findall(r"#define (IQ4XS_PROBE_\w+) (\d+)", text))
+    assert consts["IQ4XS_PROBE_MFMA_I8"] == iq.PROBE_MFMA_I8 and consts["IQ4XS_PROBE_MFMA_BF16"] == iq.PROBE_MFMA_BF16
+    assert [consts[f"IQ4XS_PROBE_MIX_{n}"] for n in ("MFMA", "VALU", "SAME", "SPLIT")] == \
+        [iq.PROBE_MIX_MFMA, iq.PROBE_MIX_VALU, iq.PROBE_MIX_SAME, iq.PROBE_MIX_SPLIT]
 
 
 def test_header_constants_match_binding():
