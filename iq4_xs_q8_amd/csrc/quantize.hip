@@ -47,19 +47,32 @@ __device__ __forceinline__ void zero_range(float *yz, int64_t nz, int64_t tid, i
 }
 
 // The listed tiles of zt.y = 0 over a grid of `stride` threads (elements
-// past M or N skipped; fewer than 2^31 elements in all).
+// past M or N skipped; fewer than 2^31 elements in all).  Four consecutive
+// columns of a tile row per step: one 16-byte store where the row is 16-byte
+// aligned (N a multiple of 4) and the four columns lie inside N, else up to
+// four single stores.
 __device__ __forceinline__ void zero_tiles(const ZeroTiles &zt, int64_t tid, int64_t stride)
 {
     if (zt.count == 0)
         return;
-    const int per = zt.bm * zt.bn;
-    for (int64_t e = tid; e < (int64_t)zt.count * per; e += stride) {
-        const int i = (int)(e / per), w = (int)(e - (int64_t)i * per);
-        const int t = zt.t[i];
-        const int64_t m = (int64_t)(t % zt.mblocks) * zt.bm + w / zt.bn;
-        const int64_t n = (int64_t)(t / zt.mblocks) * zt.bn + w % zt.bn;
-        if (m < zt.M && n < zt.N)
-            zt.y[m * zt.N + n] = 0.0f;
+    const int per4 = zt.bm * zt.bn / 4;                   // (bn a multiple of 4)
+    const bool vec = (zt.N & 3) == 0;
+    for (int e = (int)tid; e < zt.count * per4; e += (int)stride) {
+        const int i = e / per4, w = 4 * (e - i * per4);
+        const int t = zt.t[i], row = w / zt.bn, col = w - row * zt.bn;
+        const int64_t m = (int64_t)(t % zt.mblocks) * zt.bm + row;
+        const int64_t n = (int64_t)(t / zt.mblocks) * zt.bn + col;
+        if (m >= zt.M)
+            continue;
+        float *y = zt.y + m * zt.N + n;
+        if (vec && n + 4 <= zt.N) {
+            *reinterpret_cast<float4 *>(y) = make_float4(0.f, 0.f, 0.f, 0.f);
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; c++)
+                if (n + c < zt.N)
+                    y[c] = 0.0f;
+        }
     }
 }
 
@@ -232,7 +245,7 @@ hipError_t launch_zero_tiles(const ZeroTiles &zt, hipStream_t s)
 {
     if (zt.count == 0)
         return hipSuccess;
-    const int64_t n = (int64_t)zt.count * zt.bm * zt.bn;
+    const int64_t n = (int64_t)zt.count * zt.bm * zt.bn / 4;
     const int64_t grid = std::min<int64_t>((n + 255) / 256, 4096);
     hipLaunchKernelGGL(k_zero_tiles, dim3((unsigned)grid), dim3(256), 0, s, zt);
     return hipGetLastError();

@@ -261,12 +261,14 @@ def test_rows_independent_of_m_streaming_and_gemv():
 @pytest.mark.parametrize("M,N,K", [(300, 2800, 512), (97, 8200, 256), (130, 8320, 1024),
                                    (100, 200, 4096), (130, 1000, 2048), (257, 384, 8192), (200, 300, 2816),
                                    (40, 1000, 2048), (64, 600, 4096), (50, 5000, 512), (33, 300, 2816),
-                                   (65, 16768, 256), (130, 11392, 768), (700, 520, 1280), (1030, 270, 768)])
+                                   (65, 16768, 256), (130, 11392, 768), (700, 520, 1280), (1030, 270, 768),
+                                   (97, 40003, 256), (97, 40004, 256)])
 def test_tile_kernel_shapes(M, N, K):
     """Shapes the tile kernel takes (64 x 256 tiles for 32 < M <= 64, 128 x 128
     above, 128 x 256 or 256 x 128 from M = 128 or 256, also past M = 512):
     ragged M and N; K of one super-block (runs of more than a
-    tile: two owners per shared tile, adding into a zeroed Y); few tiles and
+    tile: two owners per shared tile, adding into a zeroed Y; N = 40003 and
+    40004 for the zeroing of shared tiles with and without 16-byte rows); few tiles and
     long K (runs shorter than a tile: two to eight workgroups share a tile,
     their partial tiles summed in run order by the second kernel); run bounds
     on and off tile and super-block boundaries; through gemm and gemm_act
