@@ -321,12 +321,12 @@ __device__ __forceinline__ void bf16x2_split(float a, float b, uint32_t &hi, uin
 
 // Tiles of Y that two workgroups of the tile kernel add into (a stream-K run
 // boundary falls inside each): zeroed before the matmul instead of all of Y.
-// Tile t covers rows (t % mblocks)*bm .. +bm and columns (t / mblocks)*bn .. +bn.
+// Tile t covers rows (t / wblocks)*bm .. +bm and columns (t % wblocks)*bn .. +bn.
 constexpr int MAXZT = 256;
 struct ZeroTiles {
     float *y = nullptr;
     int64_t M = 0, N = 0;
-    int bm = 0, bn = 0, mblocks = 0, count = 0;
+    int bm = 0, bn = 0, wblocks = 0, count = 0;
     int t[MAXZT] = {};
 };
 
@@ -380,7 +380,7 @@ hipError_t launch_mmv_group(const MmvGroup &grp, const XPlanes &x, const MmvPlan
 // workgroups are summed from a workspace of partial tiles by a second kernel.
 struct MmqtPlan {
     bool ok = false, zero_y = false;    // zero_y: shared tiles add into a zeroed Y
-    int grid = 0, mblocks = 0, bm = 0, bn = 0;   // tile: bm activation rows x bn weight rows
+    int grid = 0, mblocks = 0, wblocks = 0, bm = 0, bn = 0;   // tile: bm activation rows x bn weight rows
     int64_t tiles = 0;
     int fmt = FMT_IQ4_XS;
     size_t workspace_bytes = 0;         // else partial tiles in a workspace

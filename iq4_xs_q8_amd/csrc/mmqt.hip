@@ -131,7 +131,7 @@ __device__ __forceinline__ float4 *slot_at(float *ws, int g, int which)
 template <class C>
 __global__ void __launch_bounds__(NTQ, 1)
 k_mmqt(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__restrict__ Y,
-       float *__restrict__ ws, int M, int N, int K, int Mp, int nb, int mblocks, int G, int add_into_y, Runs runs)
+       float *__restrict__ ws, int M, int N, int K, int Mp, int nb, int wblocks, int G, int add_into_y, Runs runs)
 {
     constexpr int BM = C::BM, BN = C::BN, SLOTS = C::SLOTS, JW = C::JW, JA = C::JA, JD = C::JD;
     constexpr int A_OFF = C::A_OFF, D_OFF = C::D_OFF, BUFQ = C::BUFQ;
@@ -140,10 +140,20 @@ k_mmqt(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__re
     constexpr int GQ = C::G, UQ = C::U, NB = C::NBUF;
     const int nt = wave % C::NTW, mq = wave / C::NTW;        // weight subtile, activation group
     const int col = lane & 31, h = lane >> 5;
-    // Workgroups are dealt round-robin to the 8 XCDs (each with its own L2):
-    // give the workgroups of one XCD consecutive runs, so that the activation
-    // blocks that share a weight block meet in one L2.
-    const int g = G % 8 == 0 ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+    // Workgroups are dealt round-robin to the 8 XCDs (each with its own L2).
+    // Tiles are numbered weight block fastest, so runs g and g + G/mblocks
+    // cover the same weight columns and half super-blocks in consecutive
+    // activation blocks, at the same pace.  One XCD takes such a set of runs
+    // (and neighbouring sets), so the weights that one of them loads are in
+    // that XCD's L2 when the others need them.
+    const int mblocks = (M + BM - 1) / BM;
+    int g = (int)blockIdx.x;
+    if (G % (8 * mblocks) == 0) {
+        const int S = G / 8, x = g % 8, s = g / 8;
+        g = (s % mblocks) * (G / mblocks) + x * (S / mblocks) + s / mblocks;
+    } else if (G % 8 == 0) {
+        g = (g % 8) * (G / 8) + g / 8;
+    }
     const int ua = runs.u[g], ub = runs.u[g + 1], t_first = runs.t[g];
     const uint32_t row_bytes = (uint32_t)nb * sblk_bytes(C::F);
     const int dp_at = Mp * K;
@@ -192,11 +202,11 @@ k_mmqt(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__re
             p_go0[k] = p_go1[k] = OOB;
         }
     }
-    // tile t -> (activation block, weight block), the activation block fastest;
+    // tile t -> (activation block, weight block), the weight block fastest;
     // unit half j: super-block j/2, sub-blocks 4*(j%2) .. 4*(j%2)+3
     auto issue = [&](const Chunk &c, auto bc) __attribute__((always_inline)) {
         char *buf = lds_area<decltype(bc)::value, BUFQ>();
-        const int mb = c.t % mblocks, wb = c.t / mblocks, js = c.j0 >> 1, hf = c.j0 & 1;
+        const int mb = c.t / wblocks, wb = c.t - mb * wblocks, js = c.j0 >> 1, hf = c.j0 & 1;
         const bool live = c.cl > 0;
         const uint32_t wbase = (uint32_t)wb * BN * row_bytes + (uint32_t)js * sblk_bytes(C::F);
         const int sb0 = js * SUBS + HALF * hf;
@@ -219,7 +229,7 @@ k_mmqt(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__re
     // result register r of lane (col, h) holds activation row 8*(r/4) + 4*h + r%4
     auto flush = [&](int t, bool owned) __attribute__((always_inline)) {
         if (owned) {
-            const int mb = t % mblocks, wb = t / mblocks;
+            const int mb = t / wblocks, wb = t - mb * wblocks;
             const int n = wb * BN + nt * TILE + col;
 #pragma unroll
             for (int i = 0; i < GQ; i++)
@@ -230,7 +240,7 @@ k_mmqt(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__re
                         Y[(int64_t)m * N + n] = acc[i][r];
                 }
         } else if (add_into_y) {                              // (uniform) two owners at most
-            const int mb = t % mblocks, wb = t / mblocks;
+            const int mb = t / wblocks, wb = t - mb * wblocks;
             const int n = wb * BN + nt * TILE + col;
 #pragma unroll
             for (int i = 0; i < GQ; i++)
@@ -394,7 +404,7 @@ k_mmqt(const uint8_t *__restrict__ W, const int8_t *__restrict__ qp, float *__re
 // order.
 template <class C>
 __global__ void __launch_bounds__(NTQ, 1)
-k_mmqt_fix(const float *__restrict__ ws, float *__restrict__ Y, int M, int N, int nh, int mblocks, Runs runs,
+k_mmqt_fix(const float *__restrict__ ws, float *__restrict__ Y, int M, int N, int nh, int wblocks, Runs runs,
            FixRuns fix)
 {
     constexpr int BM = C::BM, BN = C::BN;
@@ -427,7 +437,7 @@ k_mmqt_fix(const float *__restrict__ ws, float *__restrict__ Y, int M, int N, in
     }
     const int lane = tid & 63, wave = tid >> 6;
     const int nt = wave % C::NTW, mq = wave / C::NTW, col = lane & 31, h = lane >> 5;
-    const int mb = t % mblocks, wb = t / mblocks;
+    const int mb = t / wblocks, wb = t - mb * wblocks;
     const int n = wb * BN + nt * TILE + col;
     const float v4[4] = {sum.x, sum.y, sum.z, sum.w};
 #pragma unroll
@@ -445,7 +455,7 @@ hipError_t launch_cfg(const void *W, const XPlanes &x, float *Y, float *ws, int6
 {
     const int nb = (int)(x.K / QK);
     hipLaunchKernelGGL((k_mmqt<C>), dim3((unsigned)p.grid), dim3(NTQ), 0, s, (const uint8_t *)W, x.qp, Y, ws,
-                       (int)x.M, (int)N, (int)x.K, (int)x.Mp, nb, p.mblocks, p.grid, p.zero_y ? 1 : 0, runs);
+                       (int)x.M, (int)N, (int)x.K, (int)x.Mp, nb, p.wblocks, p.grid, p.zero_y ? 1 : 0, runs);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.workspace_bytes == 0)
         return e;
@@ -462,7 +472,7 @@ hipError_t launch_cfg(const void *W, const XPlanes &x, float *Y, float *ws, int6
     if (nfix == 0)
         return hipSuccess;
     hipLaunchKernelGGL((k_mmqt_fix<C>), dim3((unsigned)nfix, 4 * C::G), dim3(NTQ), 0, s, (const float *)ws, Y,
-                       (int)x.M, (int)N, nh, p.mblocks, runs, fix);
+                       (int)x.M, (int)N, nh, p.wblocks, runs, fix);
     return hipGetLastError();
 }
 
@@ -494,6 +504,7 @@ MmqtPlan plan_tiles(int64_t M, int64_t N, int64_t K, int cus, int fmt, int64_t B
     G = std::min<int64_t>(G, cap);
     p.grid = (int)std::max<int64_t>(G, 1);
     p.mblocks = (int)mblocks;
+    p.wblocks = (int)wblocks;
     p.bm = (int)BM;
     p.bn = (int)BN;
     p.tiles = T;
@@ -531,7 +542,7 @@ ZeroTiles mmqt_zero_tiles(const MmqtPlan &p, int64_t M, int64_t N, int64_t K, fl
     zt.N = N;
     zt.bm = p.bm;
     zt.bn = p.bn;
-    zt.mblocks = p.mblocks;
+    zt.wblocks = p.wblocks;
     // the run bounds of launch_mmqt: a bound inside a tile makes it shared
     // (runs of at least a tile: one bound per shared tile)
     const int64_t nh = 2 * (K / QK), U = p.tiles * nh;

@@ -60,8 +60,8 @@ __device__ __forceinline__ void zero_tiles(const ZeroTiles &zt, int64_t tid, int
     for (int e = (int)tid; e < zt.count * per4; e += (int)stride) {
         const int i = e / per4, w = 4 * (e - i * per4);
         const int t = zt.t[i], row = w / zt.bn, col = w - row * zt.bn;
-        const int64_t m = (int64_t)(t % zt.mblocks) * zt.bm + row;
-        const int64_t n = (int64_t)(t / zt.mblocks) * zt.bn + col;
+        const int64_t m = (int64_t)(t / zt.wblocks) * zt.bm + row;
+        const int64_t n = (int64_t)(t % zt.wblocks) * zt.bn + col;
         if (m >= zt.M)
             continue;
         float *y = zt.y + m * zt.N + n;
