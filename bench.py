@@ -230,29 +230,27 @@ def measure_point(rot, X, N, K, path, reps=20, fmt=iq.FMT_IQ4_XS):
     if path not in (iq.PATH_DEQ_BF16, iq.PATH_BF16X3) and fmt == iq.FMT_IQ4_XS:
         act = iq.prepare_act(X)
         Y.zero_()
-        kern = lambda: iq.gemm_act(rot.next(), act, M, K, path=path, out=Y, y_zeroed=True)  # noqa: E731
+        # the partial-tile scratch from the caller: the launch allocates
+        # nothing and is replayed from a graph like the calls (no host gaps
+        # between short kernels)
+        kws = torch.empty(iq.act_workspace_bytes(M, N, K, path), dtype=torch.uint8, device="cuda")
+        kern = lambda: iq.gemm_act(rot.next(), act, M, K, path=path, out=Y, y_zeroed=True,  # noqa: E731
+                                   workspace=kws)
         for _ in range(3):
             kern()
-        # without a partial-tile workspace the launch allocates nothing and is
-        # replayed from a graph like the calls (no host gaps between short
-        # kernels); with one, it is launched eagerly
-        planes = -(-iq.act_bytes(M, K) // 256) * 256
-        if path == iq.PATH_GEMV or iq.workspace_bytes(M, N, K, path) == planes:
-            side = torch.cuda.Stream()
-            side.wait_stream(stream)
-            with torch.cuda.stream(side):
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            kern()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
                 kern()
-            stream.wait_stream(side)
-            torch.cuda.synchronize()
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for _ in range(reps):
-                    kern()
-            g.replay()
-            t_kern = time_events(g.replay, 3, stream) / reps
-            del g
-        else:
-            t_kern = time_events(kern, reps, stream)
+        g.replay()
+        t_kern = time_events(g.replay, 3, stream) / reps
+        del g
     return t_call, t_kern, t_eager
 
 

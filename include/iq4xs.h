@@ -214,6 +214,19 @@ int iq4xs_prepare_act(const float *X, void *act, int64_t M, int64_t K, void *str
 #define IQ4XS_Y_ZEROED 0x100
 int iq4xs_gemm_act(const void *W, const void *act, float *Y, int64_t M, int64_t N, int64_t K,
                    int path, void *stream);
+/* iq4xs_gemm_act with the partial-result scratch supplied by the caller, so
+ * that the launch allocates nothing and can be recorded into a HIP graph.
+ * iq4xs_gemm_act_workspace_bytes gives the bytes that the shape and path need
+ * (AUTO resolved with the dispatch table in force, IQ4XS_Y_ZEROED ignored);
+ * most shapes need 0, and then `workspace` may be NULL.  Otherwise
+ * `workspace` holds at least that many bytes, is 256-byte aligned and does
+ * not overlap W, act or Y (EINVAL for NULL, too small or overlapping; EALIGN
+ * when misaligned).  Its contents on entry do not matter and are left
+ * undefined; calls that share one workspace must be ordered on one stream.
+ * Result and other errors as iq4xs_gemm_act. */
+int iq4xs_gemm_act_workspace_bytes(int64_t M, int64_t N, int64_t K, int path, size_t *out);
+int iq4xs_gemm_act_ws(const void *W, const void *act, float *Y, int64_t M, int64_t N, int64_t K, int path,
+                      void *workspace, size_t workspace_bytes, void *stream);
 
 /* Several weight matrices that share one X ("SGLang MoE port thread",
  * decode measurements of the grouped expert call: one call per layer,

@@ -37,7 +37,8 @@ EXPORTS = ("iq4xs_weight_bytes", "iq4xs_q8_1_bytes", "iq4xs_init", "iq4xs_quanti
            "iq4xs_gemm", "iq4xs_gemm_path", "iq4xs_gemm_workspace_bytes", "iq4xs_gemm_ws",
            "iq4xs_gemm_noalloc", "iq4xs_weight_bytes_fmt", "iq4xs_gemm_fmt_workspace_bytes",
            "iq4xs_gemm_fmt", "iq4xs_gemm_q8_1", "iq4xs_act_bytes",
-           "iq4xs_prepare_act", "iq4xs_gemm_act", "iq4xs_gemm_group_workspace_bytes", "iq4xs_gemm_group",
+           "iq4xs_prepare_act", "iq4xs_gemm_act", "iq4xs_gemm_act_workspace_bytes", "iq4xs_gemm_act_ws",
+           "iq4xs_gemm_group_workspace_bytes", "iq4xs_gemm_group",
            "iq4xs_dequantize_bf16",
            "iq4xs_dispatch", "iq4xs_load_dispatch_table", "iq4xs_path_name", "iq4xs_last_error")
 
@@ -77,6 +78,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "iq4xs_act_bytes": [i64, i64, sz],
         "iq4xs_prepare_act": [p, p, i64, i64, p],
         "iq4xs_gemm_act": [p, p, p, i64, i64, i64, i32, p],
+        "iq4xs_gemm_act_workspace_bytes": [i64, i64, i64, i32, sz],
+        "iq4xs_gemm_act_ws": [p, p, p, i64, i64, i64, i32, p, ctypes.c_size_t, p],
         "iq4xs_gemm_group_workspace_bytes": [ctypes.POINTER(i64), i32, i64, i64, sz],
         "iq4xs_gemm_group": [ctypes.POINTER(p), ctypes.POINTER(p), ctypes.POINTER(i64), i32, p, i64, i64, p,
                              ctypes.c_size_t, p],
@@ -328,20 +331,37 @@ def prepare_act(X: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tenso
     return out
 
 
+def act_workspace_bytes(M: int, N: int, K: int, path: int = PATH_AUTO) -> int:
+    """Bytes of partial-result scratch gemm_act needs for this shape (often 0)."""
+    out = ctypes.c_size_t()
+    check(_L().iq4xs_gemm_act_workspace_bytes(M, N, K, path, ctypes.byref(out)))
+    return out.value
+
+
 def gemm_act(W: torch.Tensor, act: torch.Tensor, M: int, K: int, path: int = PATH_AUTO,
-             out: torch.Tensor | None = None, y_zeroed: bool = False) -> torch.Tensor:
+             out: torch.Tensor | None = None, y_zeroed: bool = False,
+             workspace: torch.Tensor | None = None) -> torch.Tensor:
     """Y[M, N] from prepared activations (the matmul kernel; y_zeroed: `out`
-    already holds zeros, so no zeroing kernel runs before it)."""
+    already holds zeros, so no zeroing kernel runs before it).  With
+    `workspace` (uint8, act_workspace_bytes(M, N, K, path) bytes) nothing is
+    allocated inside the call, so it can be captured in a graph."""
     N = _wrows(W, K)
     _at_least(act, "act", act_bytes(M, K))
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=act.device)
     _shape(out, "Y", (M, N))
-    _one_device(W, act, out)
+    _one_device(W, act, out, workspace)
+    flag = path | (Y_ZEROED if y_zeroed else 0)
     with _on(act):
-        check(_L().iq4xs_gemm_act(_dev(W, torch.uint8, "W"), _dev(act, torch.uint8, "act"),
-                                 _dev(out, torch.float32, "Y"), M, N, K,
-                                 path | (Y_ZEROED if y_zeroed else 0), _stream(act)))
+        if workspace is None:
+            check(_L().iq4xs_gemm_act(_dev(W, torch.uint8, "W"), _dev(act, torch.uint8, "act"),
+                                     _dev(out, torch.float32, "Y"), M, N, K, flag, _stream(act)))
+        else:
+            wp = _dev(workspace, torch.uint8, "workspace")
+            ws = wp if workspace.numel() else None          # an empty tensor may have no address
+            check(_L().iq4xs_gemm_act_ws(_dev(W, torch.uint8, "W"), _dev(act, torch.uint8, "act"),
+                                        _dev(out, torch.float32, "Y"), M, N, K, flag, ws,
+                                        workspace.numel(), _stream(act)))
     return out
 
 

@@ -626,8 +626,35 @@ int iq4xs_prepare_act(const float *X, void *act, int64_t M, int64_t K, void *str
     return launch_err(launch_quantize(X, nullptr, &xp, M, K, (hipStream_t)stream), "quantize");
 }
 
-int iq4xs_gemm_act(const void *W, const void *act, float *Y, int64_t M, int64_t N, int64_t K,
-                   int path, void *stream)
+// The path a prepared-activation matmul runs: GEMV or MMQ.  The table's bf16
+// bands do not apply to prepared activations: the integer kernel takes those
+// shapes.
+static int resolve_act_path(int path, int64_t M, int64_t N, int64_t K, int *out)
+{
+    const int requested = path;
+    int st = resolve_path(path, M, N, K, &path);
+    if (st != IQ4XS_OK)
+        return st;
+    if (requested == IQ4XS_PATH_AUTO && path == IQ4XS_PATH_BF16X3)
+        path = IQ4XS_PATH_MMQ;
+    if (path == IQ4XS_PATH_DEQ_BF16 || path == IQ4XS_PATH_BF16X3)
+        return fail(IQ4XS_EPATH, "prepared activations feed the GEMV and MMQ paths only");
+    *out = path;
+    return IQ4XS_OK;
+}
+
+// Partial-result scratch of a prepared-activation matmul (the tile kernel
+// with few tiles, the K-split fallback); 0 for every other shape.
+static size_t act_workspace_need(int path, int64_t M, int64_t N, int64_t K)
+{
+    return path == IQ4XS_PATH_MMQ ? mmq_plan(M, N, K).workspace_bytes : 0;
+}
+
+// Common body of iq4xs_gemm_act (caller_ws false: scratch from the device's
+// pool, stream-ordered) and iq4xs_gemm_act_ws (ws, ws_bytes from the caller;
+// nothing allocated).
+static int run_gemm_act(const void *W, const void *act, float *Y, int64_t M, int64_t N, int64_t K, int path,
+                        bool caller_ws, void *ws, size_t ws_bytes, hipStream_t s)
 {
     const bool y_zeroed = (path & IQ4XS_Y_ZEROED) != 0;
     path &= ~IQ4XS_Y_ZEROED;
@@ -638,33 +665,65 @@ int iq4xs_gemm_act(const void *W, const void *act, float *Y, int64_t M, int64_t 
         return st;
     if (!aligned(W, 16) || !aligned(Y, 16) || !aligned(act, 256))
         return fail(IQ4XS_EALIGN, "W and Y must be 16-byte and act 256-byte aligned");
-    const size_t yb = (size_t)(M * N * 4);
-    if (overlaps(Y, yb, W, (size_t)(N * (K / QK) * WBLK)) || overlaps(Y, yb, act, xplanes_bytes(M, K)))
+    const size_t yb = (size_t)(M * N * 4), wb = (size_t)(N * (K / QK) * WBLK), ab = xplanes_bytes(M, K);
+    if (overlaps(Y, yb, W, wb) || overlaps(Y, yb, act, ab))
         return fail(IQ4XS_EINVAL, "Y overlaps an input");
     const int requested = path;
-    if ((st = resolve_path(path, M, N, K, &path)) != IQ4XS_OK)
+    if ((st = resolve_act_path(path, M, N, K, &path)) != IQ4XS_OK)
         return st;
-    // the table's bf16 bands do not apply to prepared activations: the
-    // integer kernel takes those shapes
-    if (requested == IQ4XS_PATH_AUTO && path == IQ4XS_PATH_BF16X3)
-        path = IQ4XS_PATH_MMQ;
-    if (path == IQ4XS_PATH_DEQ_BF16 || path == IQ4XS_PATH_BF16X3)
-        return fail(IQ4XS_EPATH, "prepared activations feed the GEMV and MMQ paths only");
+    const size_t need = act_workspace_need(path, M, N, K);
+    if (caller_ws && need > 0) {
+        if (ws == nullptr)
+            return fail(IQ4XS_EINVAL, "null workspace, %zu bytes needed", need);
+        if (!aligned(ws, 256))
+            return fail(IQ4XS_EALIGN, "workspace must be 256-byte aligned");
+        if (ws_bytes < need)
+            return fail(IQ4XS_EINVAL, "workspace of %zu bytes, %zu needed", ws_bytes, need);
+        if (overlaps(ws, ws_bytes, Y, yb) || overlaps(ws, ws_bytes, W, wb) || overlaps(ws, ws_bytes, act, ab))
+            return fail(IQ4XS_EINVAL, "workspace overlaps W, act or Y");
+    }
     if ((st = check_device()) != IQ4XS_OK || (st = check_auto_cus(requested)) != IQ4XS_OK)
         return st;
     const XPlanes xp = xplanes_at((void *)act, M, K);
-    const hipStream_t s = (hipStream_t)stream;
     if (path == IQ4XS_PATH_GEMV)
         return launch_err(launch_gemv(W, xp, Y, N, s), path_name(path));
     Scratch scr;   // partial-sum workspace when the shape splits K over workgroups
     scr.s = s;
-    const size_t wbytes = mmq_plan(M, N, K).workspace_bytes;
-    if (wbytes && hipMallocAsync(&scr.p, wbytes, s) != hipSuccess) {
-        (void)hipGetLastError();
-        scr.p = nullptr;
-        return fail(IQ4XS_ENOMEM, "workspace of %zu bytes", wbytes);
+    void *p = need > 0 ? ws : nullptr;
+    if (!caller_ws && need > 0) {
+        if (hipMallocAsync(&scr.p, need, s) != hipSuccess) {
+            (void)hipGetLastError();
+            scr.p = nullptr;
+            return fail(IQ4XS_ENOMEM, "workspace of %zu bytes", need);
+        }
+        p = scr.p;
     }
-    return launch_err(launch_mmq(W, xp, Y, N, scr.p, y_zeroed, s), path_name(path));
+    return launch_err(launch_mmq(W, xp, Y, N, p, y_zeroed, s), path_name(path));
+}
+
+int iq4xs_gemm_act(const void *W, const void *act, float *Y, int64_t M, int64_t N, int64_t K,
+                   int path, void *stream)
+{
+    return run_gemm_act(W, act, Y, M, N, K, path, false, nullptr, 0, (hipStream_t)stream);
+}
+
+int iq4xs_gemm_act_workspace_bytes(int64_t M, int64_t N, int64_t K, int path, size_t *out)
+{
+    if (!out)
+        return fail(IQ4XS_EINVAL, "null output pointer");
+    int st = check_dims(M, N, K);
+    if (st != IQ4XS_OK)
+        return st;
+    if ((st = resolve_act_path(path & ~IQ4XS_Y_ZEROED, M, N, K, &path)) != IQ4XS_OK)
+        return st;
+    *out = act_workspace_need(path, M, N, K);
+    return IQ4XS_OK;
+}
+
+int iq4xs_gemm_act_ws(const void *W, const void *act, float *Y, int64_t M, int64_t N, int64_t K, int path,
+                      void *workspace, size_t workspace_bytes, void *stream)
+{
+    return run_gemm_act(W, act, Y, M, N, K, path, true, workspace, workspace_bytes, (hipStream_t)stream);
 }
 
 static_assert(IQ4XS_MAX_GROUP == MAXGRP, "group bound of the header and the kernels");

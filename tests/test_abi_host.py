@@ -169,6 +169,42 @@ def test_workspace_query_and_checks():
     assert L.iq4xs_gemm_ws(A, A * 2, A * 4 + 4, 4, 8, 256, iq.PATH_MMQ, WS, need, None) == iq.EALIGN
 
 
+def test_act_workspace_query_and_checks():
+    """The prepared-activation matmul's own scratch: exactly the partial-tile
+    part of iq4xs_gemm_ws's scratch (which also holds the activation planes),
+    0 where no tile has more than two owners; the caller-workspace entry point
+    checks it before anything runs."""
+    size = ctypes.c_size_t()
+    for M, N, K in ((64, 5120, 1024), (128, 5120, 17408), (100, 200, 4096), (512, 248320, 5120), (8, 300, 1024)):
+        assert L.iq4xs_gemm_act_workspace_bytes(M, N, K, iq.PATH_MMQ, ctypes.byref(size)) == iq.OK
+        planes = -(-iq.act_bytes(M, K) // 256) * 256
+        assert size.value == iq.workspace_bytes(M, N, K, iq.PATH_MMQ) - planes, (M, N, K)
+        assert iq.act_workspace_bytes(M, N, K, iq.PATH_MMQ | iq.Y_ZEROED) == size.value
+    assert iq.act_workspace_bytes(64, 5120, 1024, iq.PATH_MMQ) > 0
+    assert iq.act_workspace_bytes(512, 248320, 5120, iq.PATH_MMQ) == 0
+    assert iq.act_workspace_bytes(4, 1024, 2048, iq.PATH_GEMV) == 0
+    assert L.iq4xs_gemm_act_workspace_bytes(4, 1024, 2048, iq.PATH_MMQ, None) == iq.EINVAL
+    assert L.iq4xs_gemm_act_workspace_bytes(4, 1024, 300, iq.PATH_MMQ, ctypes.byref(size)) == iq.EINVAL
+    assert L.iq4xs_gemm_act_workspace_bytes(5, 1024, 2048, iq.PATH_GEMV, ctypes.byref(size)) == iq.EPATH
+    assert L.iq4xs_gemm_act_workspace_bytes(4, 1024, 2048, iq.PATH_DEQ_BF16, ctypes.byref(size)) == iq.EPATH
+    assert L.iq4xs_gemm_act_workspace_bytes(4, 1024, 2048, iq.PATH_BF16X3, ctypes.byref(size)) == iq.EPATH
+
+    M, N, K = 64, 5120, 1024
+    need = iq.act_workspace_bytes(M, N, K, iq.PATH_MMQ)
+    W, ACT, Y, WS = A, A * 2, A * 4, A * 8
+    f = L.iq4xs_gemm_act_ws
+    assert f(None, ACT, Y, M, N, K, iq.PATH_MMQ, WS, need, None) == iq.EINVAL
+    assert f(W, ACT, Y, M, N, K, iq.PATH_MMQ, None, need, None) == iq.EINVAL
+    assert "null workspace" in L.iq4xs_last_error().decode()
+    assert f(W, ACT, Y, M, N, K, iq.PATH_MMQ, WS, need - 1, None) == iq.EINVAL
+    assert f(W, ACT, Y, M, N, K, iq.PATH_MMQ, WS + 16, need, None) == iq.EALIGN
+    assert f(W, ACT + 16, Y, M, N, K, iq.PATH_MMQ, WS, need, None) == iq.EALIGN
+    for ws in (Y + 256, W + 256, ACT + 256, Y - 256):
+        assert f(W, ACT, Y, M, N, K, iq.PATH_MMQ, ws, need, None) == iq.EINVAL, hex(ws)
+        assert "workspace overlaps" in L.iq4xs_last_error().decode()
+    assert f(W, ACT, Y, M, N, K, iq.PATH_DEQ_BF16, WS, need, None) == iq.EPATH
+
+
 @pytest.mark.skipif(_has_gpu(), reason="checks the no-device error")
 def test_no_device_reports_edevice():
     assert L.iq4xs_gemm(A, A * 2, A * 4, 4, 8, 256, None) == iq.EDEVICE
@@ -177,6 +213,10 @@ def test_no_device_reports_edevice():
     assert "device" in L.iq4xs_last_error().decode()
     assert L.iq4xs_quantize_q8_1(A, A * 2, 4, 256, None) == iq.EDEVICE
     assert L.iq4xs_dequantize_bf16(A, A * 2, 8, 256, None) == iq.EDEVICE
+    # with nothing to check in the workspace (a shape that needs none), a NULL one
+    # passes the argument checks and the call stops at the device
+    assert iq.act_workspace_bytes(512, 248320, 5120, iq.PATH_MMQ) == 0
+    assert L.iq4xs_gemm_act_ws(1 << 40, 2 << 40, 3 << 40, 512, 248320, 5120, iq.PATH_MMQ, None, 0, None) == iq.EDEVICE
 
 
 def _group_args(ws, ys, ns):

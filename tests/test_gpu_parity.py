@@ -595,6 +595,50 @@ def test_graph_replays_match_eager(M, N, K):
         assert_rows_close(got, ref, what=f"graph replay {rep} M={M}")
 
 
+@pytest.mark.parametrize("M,N,K", [(64, 5120, 1024), (100, 200, 4096), (130, 1000, 2048), (512, 10240, 5120),
+                                   (300, 2800, 512), (3, 520, 1280), (8, 2048, 2048)])
+def test_gemm_act_caller_workspace_and_graph(M, N, K):
+    """Prepared activations with a caller workspace (iq4xs_gemm_act_ws): the
+    tile kernel with summed partial tiles (the first shapes), with two-owner
+    tiles added into Y (300 x 2800 x 512), the streaming kernel and GEMV.
+    Bit-identical to the allocating gemm_act whatever the workspace holds, and
+    recorded in a HIP graph: every replay, with new activations, garbage in
+    Y and the workspace, and eager work in between, equals the eager call."""
+    W, X = _inputs(M, N, K, seed=17)
+    Wd, Xd = dev(W), dev(X)
+    path = iq.PATH_GEMV if M <= 4 else iq.PATH_MMQ
+    act = iq.prepare_act(Xd)
+    need = iq.act_workspace_bytes(M, N, K, path)
+    if (M, N, K) in ((64, 5120, 1024), (100, 200, 4096), (512, 10240, 5120)):
+        assert need > 0, "expected a shape with summed partial tiles"
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device="cuda")
+    want = iq.gemm_act(Wd, act, M, K, path=path, out=poisoned((M, N))).cpu().numpy()
+    got = iq.gemm_act(Wd, act, M, K, path=path, out=poisoned((M, N)), workspace=ws).cpu().numpy()
+    assert np.array_equal(got, want), "gemm_act with a caller workspace differs"
+    assert_rows_close(got, O.gemm_q8_1(W, O.quantize_q8_1(X), K), what=f"gemm_act_ws M={M} N={N} K={K}")
+    Y = poisoned((M, N))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        iq.gemm_act(Wd, act, M, K, path=path, out=Y, workspace=ws)      # warm up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        iq.gemm_act(Wd, act, M, K, path=path, out=Y, workspace=ws)
+    for rep in range(3):
+        Xn = synth.activations((903, M, K, rep), M, K, sigma=1.0 + rep)
+        iq.prepare_act(dev(Xn), out=act)
+        Y.fill_(float("nan"))
+        ws.fill_(0x5A + rep)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        eager = iq.gemm_act(Wd, act, M, K, path=path).cpu().numpy()
+        assert np.array_equal(Y.cpu().numpy(), eager), f"replay {rep} differs from the eager call"
+    del g
+
+
 def test_table_for_another_compute_unit_count_is_refused(tmp_path):
     """A dispatch table measured on another number of compute units does not
     drive AUTO on this device (fail-closed: ETABLE); explicit paths still run."""
