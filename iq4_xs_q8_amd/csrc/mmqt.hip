@@ -14,8 +14,10 @@
 // Work split:
 //  * Tiles (see QCfg): 64 x 256 up to M = 64, 128 x 128 above, and 256 x 128
 //    (M >= 256) or 128 x 256 (M >= 128) where those larger tiles need no
-//    summing of many partial tiles.  Tiles are ordered with the activation
-//    block fastest.  Units are (tile, half super-block), tile-major; each
+//    summing of many partial tiles.  Tiles are ordered with the weight
+//    block fastest, so with several activation blocks the partition repeats
+//    in each of them and the runs over one weight range can share an XCD's
+//    L2.  Units are (tile, half super-block), tile-major; each
 //    workgroup gets one contiguous run of equal length (stream-K style:
 //    every compute unit gets the same work, also when there are fewer tiles
 //    than compute units).  A tile covered by one run is stored by its
