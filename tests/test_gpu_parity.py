@@ -205,11 +205,11 @@ INVARIANT_CASES = [
     ("tile 128x128, two owners", iq.PATH_MMQ, 65, 16768, 256),
     ("tile 128x128, workspace (16 owners)", iq.PATH_MMQ, 100, 200, 4096),
     ("tile 128x128, workspace (5 owners)", iq.PATH_MMQ, 96, 5120, 5120),
-    ("tile 128x128, two owners, M=512", iq.PATH_MMQ, 512, 10240, 5120),
+    ("tile 256x128, workspace (2-3 owners), M=512, paired runs", iq.PATH_MMQ, 512, 10240, 5120),
     # the tiles with four activation subtiles per wavefront; ragged M and N,
     # two owners per shared tile
     ("tile 256x128, two owners, ragged", iq.PATH_MMQ, 300, 65613, 256),
-    ("tile 256x128, M=512", iq.PATH_MMQ, 512, 65536, 256),
+    ("tile 256x128, M=512, paired runs", iq.PATH_MMQ, 512, 65536, 256),
     ("tile 128x256, two owners, ragged", iq.PATH_MMQ, 150, 65613, 256),
     ("tile 256x128, workspace (3-4 owners)", iq.PATH_MMQ, 300, 5120, 5120),
     ("tile 128x256, workspace (8 owners)", iq.PATH_MMQ, 130, 2000, 8192),
@@ -262,7 +262,8 @@ def test_rows_independent_of_m_streaming_and_gemv():
                                    (100, 200, 4096), (130, 1000, 2048), (257, 384, 8192), (200, 300, 2816),
                                    (40, 1000, 2048), (64, 600, 4096), (50, 5000, 512), (33, 300, 2816),
                                    (65, 16768, 256), (130, 11392, 768), (700, 520, 1280), (1030, 270, 768),
-                                   (97, 40003, 256), (97, 40004, 256)])
+                                   (97, 40003, 256), (97, 40004, 256), (300, 20480, 768), (512, 4096, 1024),
+                                   (512, 2048, 2560)])
 def test_tile_kernel_shapes(M, N, K):
     """Shapes the tile kernel takes (64 x 256 tiles for 32 < M <= 64, 128 x 128
     above, 128 x 256 or 256 x 128 from M = 128 or 256, also past M = 512):
@@ -271,7 +272,11 @@ def test_tile_kernel_shapes(M, N, K):
     40004 for the zeroing of shared tiles with and without 16-byte rows); few tiles and
     long K (runs shorter than a tile: two to eight workgroups share a tile,
     their partial tiles summed in run order by the second kernel); run bounds
-    on and off tile and super-block boundaries; through gemm and gemm_act
+    on and off tile and super-block boundaries; several activation blocks
+    whose runs over the same weight columns are paired on one XCD (300 x
+    20480 x 768: two 256-row blocks, the second ragged, two-owner tiles;
+    512 x 4096 x 1024: four 128-row blocks; 512 x 2048 x 2560: two blocks
+    with partial tiles summed); through gemm and gemm_act
     (with and without the Y-zeroed hint), bit-identical."""
     W, X = _inputs(M, N, K, seed=M + N)
     ref = O.gemm_q8_1(W, O.quantize_q8_1(X), K)
